@@ -1,0 +1,208 @@
+"""CPU oracle of one masked-diffusion denoising step (fp64, plain loops).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the GPU library and
+its Python binding never do.  The oracle shares no code with the GPU path.
+
+The arithmetic lives in ``dlm_oracle.c`` (plain C, fp64, OpenMP over
+independent rows); this module only marshals numpy arrays into it.  Each
+function states the passage it follows.
+
+Parity status: every function here is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` against library routines (torch SDPA, scipy),
+hand-worked fixtures under ``tests/golden/`` and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dlm_oracle.c")
+_LIB = os.path.join(_HERE, "libdlm_oracle.so")
+
+MASK_FULL, MASK_BLOCK_CAUSAL, MASK_GROUP = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
+                        "-Wall", "-Wextra", "-Wno-unused-parameter",
+                        _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I, L, Dd = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.ora_scatter.argtypes = [P, P, P, P, P, I, I, I, I, I]
+        lib.ora_scatter.restype = None
+        lib.ora_visible.argtypes = [I, I, I, I, I, P, P, I, I]
+        lib.ora_visible.restype = I
+        lib.ora_attn.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, I, I, P, P,
+                                 Dd, L, P, P, P]
+        lib.ora_attn.restype = None
+        lib.ora_colsum.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, P, P,
+                                   Dd, I, I, I, P, L, P, P]
+        lib.ora_colsum.restype = None
+        lib.ora_posterior.argtypes = [P, P, P, L, L, Dd, L, P, P, P, P, P]
+        lib.ora_posterior.restype = None
+        lib.ora_select.argtypes = [I, I, I, Dd, P, P, P, P, I, P]
+        lib.ora_select.restype = None
+        lib.ora_num_threads.argtypes = []
+        lib.ora_num_threads.restype = I
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def num_threads() -> int:
+    return _load().ora_num_threads()
+
+
+def effective_kv(case):
+    """The cache after the fresh K/V of the active rows are written at their
+    positions (SureLock, section 2: locked rows keep cached K/V, active rows
+    are recomputed).  Returns new (K, V) bf16-bit arrays; inputs untouched."""
+    lib = _load()
+    ck = case.cache_k.copy()
+    cv = case.cache_v.copy()
+    lib.ora_scatter(_p(ck), _p(cv), _p(_c(case.k, np.uint16)), _p(_c(case.v, np.uint16)),
+                    _p(_c(case.active_idx, np.int32)), case.B, case.Hkv, case.n_cap,
+                    case.D, case.M)
+    return ck, cv
+
+
+def scale_of(case) -> float:
+    return case.scale if case.scale else 1.0 / np.sqrt(case.D)
+
+
+def visible(case, b, i, n) -> bool:
+    """Key n visible to the query at position i (MBD-LM sections 2.2/2.3,
+    Bifocal dLLM section 1)."""
+    lib = _load()
+    st = _c(case.slot_state[b], np.uint8) if case.n_slots else None
+    gr = _c(case.slot_group[b], np.int32) if case.n_slots else None
+    return bool(lib.ora_visible(case.kind, case.kv_len, case.prefix_len,
+                                case.block_size, case.n_slots, _p(st), _p(gr), i, n))
+
+
+def attention(case, kv=None, rows=None, want_out=True):
+    """Attention of active rows over visible keys of the effective cache.
+
+    rows: flat indices ((b*Hq + h)*M + j) or None for all.  Returns
+    (out [n,D] fp64 or None, lse [n] fp64).  With rows=None the arrays are
+    reshaped to [B,Hq,M,D] and [B,Hq,M]."""
+    lib = _load()
+    K, Vv = effective_kv(case) if kv is None else kv
+    n = case.B * case.Hq * case.M if rows is None else len(rows)
+    rows_a = None if rows is None else _c(rows, np.int64)
+    out = np.empty((n, case.D), np.float64) if want_out else None
+    lse = np.empty(n, np.float64)
+    st = _c(case.slot_state, np.uint8) if case.n_slots else None
+    gr = _c(case.slot_group, np.int32) if case.n_slots else None
+    lib.ora_attn(_p(_c(case.q, np.uint16)), _p(K), _p(Vv), _p(_c(case.active_idx, np.int32)),
+                 case.B, case.Hq, case.Hkv, case.n_cap, case.D, case.M, case.kind,
+                 case.kv_len, case.prefix_len, case.block_size, case.n_slots,
+                 _p(st), _p(gr), scale_of(case), n, _p(rows_a), _p(out), _p(lse))
+    if rows is None:
+        lse = lse.reshape(case.B, case.Hq, case.M)
+        if out is not None:
+            out = out.reshape(case.B, case.Hq, case.M, case.D)
+    return out, lse
+
+
+def colsum(case, lse_all, kv=None, cols=None):
+    """Attention column sums (Attn-Sampler section 2B), head-summed or per
+    head, over rows whose position lies in [cs_lo, cs_hi).
+
+    lse_all: [B,Hq,M] from ``attention`` over all rows.  cols: flat
+    (b*kv_len + n) or None for all.  Returns [B,kv_len] / [B,Hq,kv_len] for
+    cols=None, else [n] / [n,Hq]."""
+    lib = _load()
+    K, _ = effective_kv(case) if kv is None else kv
+    n = case.B * case.kv_len if cols is None else len(cols)
+    cols_a = None if cols is None else _c(cols, np.int64)
+    res = np.empty((n, case.Hq) if case.colsum_per_head else (n,), np.float64)
+    st = _c(case.slot_state, np.uint8) if case.n_slots else None
+    gr = _c(case.slot_group, np.int32) if case.n_slots else None
+    lib.ora_colsum(_p(_c(case.q, np.uint16)), _p(K), _p(_c(case.active_idx, np.int32)),
+                   case.B, case.Hq, case.Hkv, case.n_cap, case.D, case.M, case.kind,
+                   case.kv_len, case.prefix_len, case.block_size, case.n_slots,
+                   _p(st), _p(gr), scale_of(case), case.cs_lo, case.cs_hi,
+                   case.colsum_per_head, _p(_c(lse_all, np.float64)), n, _p(cols_a),
+                   _p(res))
+    if cols is None:
+        if case.colsum_per_head:
+            res = res.reshape(case.B, case.kv_len, case.Hq).transpose(0, 2, 1).copy()
+        else:
+            res = res.reshape(case.B, case.kv_len)
+    return res
+
+
+def posterior(logits, prev, locked, eps, rows=None):
+    """Per-row KL(p_t || p_{t-1}), confidence, argmax token and lock flag
+    (SureLock section 2).  Returns dict of kl, conf, tok, locked (new)."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    prev = _c(prev, np.float32)
+    locked = _c(locked, np.uint8)
+    R, V = logits.shape
+    n = R if rows is None else len(rows)
+    rows_a = None if rows is None else _c(rows, np.int64)
+    kl = np.empty(n, np.float64)
+    conf = np.empty(n, np.float64)
+    tok = np.empty(n, np.int32)
+    lk = np.empty(n, np.uint8)
+    lib.ora_posterior(_p(logits), _p(prev), _p(locked), R, V, float(eps), n, _p(rows_a),
+                      _p(kl), _p(conf), _p(tok), _p(lk))
+    return {"kl": kl, "conf": conf, "tok": tok, "locked": lk}
+
+
+def select(mode, k, group_rows, tau, score, conf, tok, locked_in):
+    """Unmask selection per group of rows (confidence top-k / threshold,
+    Attn-Sampler order and dynamic threshold).  Returns sel int32 [R]."""
+    lib = _load()
+    conf = _c(conf, np.float64)
+    R = conf.shape[0]
+    score_a = _c(score, np.float64) if score is not None else np.zeros(R, np.float64)
+    sel = np.empty(R, np.int32)
+    lib.ora_select(int(mode), int(k), int(group_rows), float(tau), _p(score_a), _p(conf),
+                   _p(_c(tok, np.int32)), _p(_c(locked_in, np.uint8)), R, _p(sel))
+    return sel
+
+
+def step(workload, attn_rows=None):
+    """The whole step on the CPU: effective K/V, attention, column sums,
+    posterior, selection.  Returns a dict of fp64 results."""
+    from workloads import score_for
+    a, p = workload.attn, workload.post
+    kv = effective_kv(a)
+    out, lse = attention(a, kv=kv)
+    cs = colsum(a, lse, kv=kv)
+    post = posterior(p.logits, p.prev, p.locked, p.eps)
+    score = score_for(p, cs if not a.colsum_per_head else cs.sum(1))
+    sel = select(p.mode, p.k, p.group_rows, p.tau, score, post["conf"], post["tok"], p.locked)
+    return {"cache_k": kv[0], "cache_v": kv[1], "out": out, "lse": lse, "colsum": cs,
+            "score": score, "sel": sel, **post}

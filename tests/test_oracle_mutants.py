@@ -1,0 +1,83 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case plants one mistake (a dropped term, a wrong sign, a wrong index, a
+swapped operand, an off-by-one comparison) in a private copy of the oracle's
+C source, builds it on the CPU, and checks that at least one pin in
+test_oracle_pins.py fails against it.  The committed oracle is untouched.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "dlm_oracle.c")
+
+MUTANTS = [
+    ("kl_sign", "d += exp(logp) * (logp - logq);", "d += exp(logp) * (logq - logp);",
+     [pins.test_posterior_golden, pins.test_posterior_bernoulli_closed_form]),
+    ("lse_drops_max", "double L = mx + log(sum);", "double L = log(sum);",
+     [lambda: pins.test_attention_and_lse_vs_library(0)]),
+    ("gqa_head_map", "int g = h / G;\n            int i = active_idx",
+     "int g = h % Hkv;\n            int i = active_idx",
+     [lambda: pins.test_attention_and_lse_vs_library(2)]),
+    ("pv_uses_keys", "o[d] += p * wide(vb[(int64_t)n * D + d]);",
+     "o[d] += p * wide(kb[(int64_t)n * D + d]);",
+     [lambda: pins.test_attention_and_lse_vs_library(0)]),
+    ("scale_dropped", "s[n] = scale * dot;", "s[n] = dot;",
+     [lambda: pins.test_attention_and_lse_vs_library(1)]),
+    ("block_causal_strict", "return slot_n <= slot_i;", "return slot_n < slot_i;",
+     [pins.test_visibility_golden]),
+    ("group_equal_only", "return group[slot_n] <= group[slot_i];",
+     "return group[slot_n] == group[slot_i];", [pins.test_visibility_golden]),
+    ("dummy_visible", "if (state[slot_n] == ORA_DUMMY)\n        return 0;", "",
+     [pins.test_visibility_golden]),
+    ("lock_strict", "locked_out[t] = (uint8_t)(d <= eps);", "locked_out[t] = (uint8_t)(d < eps);",
+     [pins.test_lock_threshold_is_inclusive]),
+    ("argmax_last", "if ((double)x[v] > mx) {", "if ((double)x[v] >= mx) {",
+     [pins.test_posterior_golden]),
+    ("colsum_unnormalised", "head_sum += exp(scale * dot - L);", "head_sum += exp(scale * dot);",
+     [lambda: pins.test_colsum_vs_explicit_matrix(0, 0)]),
+    ("colsum_row_range", "if (i < cs_lo || i >= cs_hi)", "if (i < cs_lo)",
+     [lambda: pins.test_colsum_vs_explicit_matrix(0, 0)]),
+    ("scatter_wrong_row", "int64_t dst = (((int64_t)b * Hkv + g) * n_cap + pos) * D;",
+     "int64_t dst = (((int64_t)b * Hkv + g) * n_cap + j) * D;",
+     [pins.test_sparse_equals_full_recompute]),
+    ("dynamic_threshold_inclusive", "if (conf[order[t]] > tau && score[order[t]] > thr) {",
+     "if (conf[order[t]] > tau && score[order[t]] >= thr) {",
+     [pins.test_selection_golden, pins.test_selection_brute_force]),
+    ("thresh_conf_inclusive", "if (conf[order[t]] > tau) {", "if (conf[order[t]] >= tau) {",
+     [pins.test_selection_golden]),
+    ("select_ignores_locks", "if (!locked_in[r])\n                order[n++] = r;",
+     "order[n++] = r;", [pins.test_selection_golden]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,checks", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, checks, tmp_path, monkeypatch):
+    with open(SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path = tmp_path / f"mutant_{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / f"libmutant_{name}.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", str(path),
+                    "-o", str(lib), "-lm"], check=True)
+    oracle._load()                       # set argtypes on the real library first
+    real = oracle._lib
+    mutant = ctypes.CDLL(str(lib))
+    for fn in ("ora_scatter", "ora_visible", "ora_attn", "ora_colsum", "ora_posterior",
+               "ora_select", "ora_num_threads"):
+        getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
+        getattr(mutant, fn).restype = getattr(real, fn).restype
+    monkeypatch.setattr(oracle, "_lib", mutant)
+    caught = 0
+    for check in checks:
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the planted mistake {name}"
