@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of one masked-diffusion denoising step on one MI355X.
+
+A step is the whole hot path on one batch of seeded synthetic input:
+K/V scatter + sparse-query attention (pass 1) + column sums (pass 2) +
+posterior / KL lock test / unmask selection, through the two C-ABI calls.
+Inputs are resident in HBM before timing starts; the timed steps rotate over
+enough copies of the inputs that they cannot be served from the 256 MB
+Infinity Cache.  The lock flags are restored before every step (a small
+device copy inside the timed region) so every step does the same work.
+
+Prints ONE JSON line.  Default workload: the LLaDA-8B-like bidirectional
+layer (B=1, 32 heads x 128, N=1024 all active; posterior 32 x 126464).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+MALL_BYTES = 256 << 20
+
+
+def visible_pairs(a) -> int:
+    """Sum over active rows and q-heads of the number of visible keys."""
+    import numpy as np
+    if a.kind == 0:
+        return a.B * a.Hq * a.M * a.kv_len
+    tot = 0
+    n = np.arange(a.kv_len)
+    for b in range(a.B):
+        pos = a.active_idx[b]
+        if a.kind == 1:
+            kb = np.where(n < a.prefix_len, -1, (n - a.prefix_len) // a.block_size)
+            qb = (pos - a.prefix_len) // a.block_size
+            vis = (kb[None, :] <= qb[:, None])
+        else:
+            slot = np.clip((n - a.prefix_len) // a.block_size, 0, a.n_slots - 1)
+            kcode = np.where(a.slot_state[b][slot] == 0, np.iinfo(np.int64).max, a.slot_group[b][slot])
+            kcode = np.where(n < a.prefix_len, np.iinfo(np.int64).min, kcode)
+            qc = a.slot_group[b][(pos - a.prefix_len) // a.block_size]
+            vis = kcode[None, :] <= qc[:, None]
+        tot += int(vis.sum()) * a.Hq
+    return tot
+
+
+def time_loop(fn, n_sets, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i % n_sets)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(i % n_sets)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps        # ms per call
+
+
+def cpu_baseline(w, budget_heads=None):
+    """Time the oracle, as it stands, on a bounded sample of the workload and
+    scale to the metric's unit (rows/s of a whole step)."""
+    import numpy as np
+    import oracle
+    from workloads import AttnCase
+    a, p = w.attn, w.post
+    H = budget_heads or max(1, min(a.Hq, 4))
+    # keep whole GQA groups so the sample has the workload's structure
+    H = max(a.G, (H // a.G) * a.G)
+    sub = AttnCase(**{**a.__dict__, "Hq": H, "Hkv": H // a.G, "q": a.q[:, :H],
+                      "k": a.k[:, :H // a.G], "v": a.v[:, :H // a.G],
+                      "cache_k": a.cache_k[:, :H // a.G], "cache_v": a.cache_v[:, :H // a.G]})
+    t0 = time.perf_counter()
+    kv = oracle.effective_kv(sub)
+    _, lse = oracle.attention(sub, kv=kv)
+    oracle.colsum(sub, lse, kv=kv)
+    t_attn = (time.perf_counter() - t0) * (a.Hq / H)
+    rows = min(p.R, 64)
+    t0 = time.perf_counter()
+    post = oracle.posterior(p.logits[:rows], p.prev[:rows], p.locked[:rows], p.eps)
+    t_post = (time.perf_counter() - t0) * (p.R / rows)
+    t_step = t_attn + t_post
+    return {"value": a.B * a.M / t_step, "unit": "rows/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"attention + column sums on {H} of {a.Hq} q-heads (scaled x{a.Hq / H:g}), "
+                      f"posterior on {rows} of {p.R} rows (scaled x{p.R / rows:g}); "
+                      f"step time {t_step:.3f} s",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llada_bidirectional")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is a design, not a build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import denoising_step_amd as dlm
+    from denoising_step_amd.runner import DeviceStep
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = W.get(args.config, seed=args.seed)
+    a, p = w.attn, w.post
+    print(f"bench: {args.config}: {w.description}", file=sys.stderr, flush=True)
+
+    first = DeviceStep(w)
+    foot = sum(t.numel() * t.element_size() for t in
+               (first.q, first.k, first.v, first.cache_k, first.cache_v, first.logits, first.prev))
+    n_sets = max(1, math.ceil(2 * MALL_BYTES / foot))
+    sets = [first] + [DeviceStep(w) for _ in range(n_sets - 1)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        ds = sets[i]
+        ds.locked.copy_(ds.locked0)
+        ds.run(stream)
+
+    ms_step = time_loop(step, n_sets, args.steps, args.warmup)
+
+    # pass 1 alone: no fresh K/V (already in the cache), no column sums
+    def pass1(i):
+        ds = sets[i]
+        dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, None, stream)
+
+    ms_pass1 = time_loop(pass1, n_sets, args.steps, args.warmup)
+
+    def posterior(i):
+        ds = sets[i]
+        ds.locked.copy_(ds.locked0)
+        ds.run_posterior(stream)
+
+    ms_post = time_loop(posterior, n_sets, args.steps, args.warmup)
+
+    pairs = visible_pairs(a)
+    alg_flops = 4.0 * a.D * pairs                       # QK^T and PV, 2 flops per MAC
+    achieved_tflops = alg_flops / (ms_pass1 * 1e-3) / 1e12
+    unlocked = int((p.locked == 0).sum())
+    post_bytes = 8.0 * unlocked * p.V
+    post_gbs = post_bytes / (ms_post * 1e-3) / 1e9
+    plan = {"n_sets": n_sets, "footprint_mb_per_set": round(foot / 2**20, 1)}
+
+    rows = a.B * a.M
+    res = {
+        "metric": "active query-rows/s per denoising step",
+        "value": rows / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the pages' workloads, no trained weights)",
+        "config": {"workload": args.config, "B": a.B, "Hq": a.Hq, "Hkv": a.Hkv, "D": a.D,
+                   "kv_len": a.kv_len, "active_rows": a.M, "posterior_rows": p.R, "vocab": p.V,
+                   "mask": ["full", "block_causal", "group"][a.kind], "selection": p.mode},
+        "roofline": {"bound": "mfma", "kernel": "attention pass 1 (sparse-query flash attention)",
+                     "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "per_launch_flops": alg_flops, "avg_launch_us": ms_pass1 * 1e3},
+        "posterior_roofline": {"bound": "hbm", "achieved": post_gbs, "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": post_gbs / PEAK_HBM_GBS,
+                               "per_launch_bytes": post_bytes, "avg_launch_us": ms_post * 1e3},
+        "timing": plan,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

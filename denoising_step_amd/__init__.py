@@ -1,0 +1,249 @@
+"""MI355X-native denoising step: Python binding of libdlm_step.so.
+
+The binding only marshals arguments into the C ABI of include/dlm_step.h
+(``dlm_step_attn``, ``dlm_posterior`` and their workspace queries); every
+step of the computation runs in the library's HIP kernels.  Tensors are
+PyTorch device tensors, used for memory and streams only.  It checks tensor
+shapes, dtypes and contiguity against the declared sizes so that a
+mis-sized tensor can never reach a kernel.
+
+There is no fallback: if the library is not built, importing this package
+raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdlm_step.so")
+
+DLM_OK, DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_DESC, DLM_E_WORKSPACE, DLM_E_HIP = \
+    0, -1, -2, -3, -4, -5, -6
+MASK_FULL, MASK_BLOCK_CAUSAL, MASK_GROUP = 0, 1, 2
+SLOT_DUMMY, SLOT_ACTIVE, SLOT_TO_CACHE, SLOT_IN_CACHE = 0, 1, 2, 3
+SEL_NONE, SEL_TOPK_CONF, SEL_THRESH_CONF, SEL_ATTN_DYNAMIC, SEL_TOPK_SCORE = 0, 1, 2, 3, 4
+
+EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
+           "dlm_posterior_workspace_bytes", "dlm_last_error")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950)")
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class DlmError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class _KVCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("B", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("n_cap", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class _MaskDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("Hq", ctypes.c_int32), ("M", ctypes.c_int32),
+                ("kv_len", ctypes.c_int32), ("prefix_len", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("slot_state", ctypes.c_void_p), ("slot_group", ctypes.c_void_p),
+                ("cs_lo", ctypes.c_int32), ("cs_hi", ctypes.c_int32),
+                ("colsum_per_head", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class _Select(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("group_rows", ctypes.c_int32),
+                ("tau", ctypes.c_float), ("score", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_P = ctypes.c_void_p
+lib.dlm_step_attn.argtypes = [_P, _P, _P, ctypes.POINTER(_KVCache), _P, ctypes.POINTER(_MaskDesc),
+                              _P, _P, _P, _P]
+lib.dlm_step_attn.restype = ctypes.c_int
+lib.dlm_step_attn_workspace_bytes.argtypes = [ctypes.POINTER(_KVCache), ctypes.POINTER(_MaskDesc),
+                                              ctypes.POINTER(ctypes.c_size_t)]
+lib.dlm_step_attn_workspace_bytes.restype = ctypes.c_int
+lib.dlm_posterior.argtypes = [_P, _P, _P, ctypes.c_float, ctypes.POINTER(_Select), _P, _P, _P,
+                              ctypes.c_int32, ctypes.c_int32, _P]
+lib.dlm_posterior.restype = ctypes.c_int
+lib.dlm_posterior_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Select),
+                                              ctypes.POINTER(ctypes.c_size_t)]
+lib.dlm_posterior_workspace_bytes.restype = ctypes.c_int
+lib.dlm_last_error.argtypes = []
+lib.dlm_last_error.restype = ctypes.c_char_p
+
+
+def dlm_last_error() -> str:
+    return lib.dlm_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != DLM_OK:
+        raise DlmError(rc, dlm_last_error())
+
+
+# ---------------------------------------------------------------------------
+# Descriptors (Python side).  Tensor fields hold torch device tensors; plain
+# ints are accepted in their place by the raw entry points (tests of the
+# host-side checks pass dummy addresses that are never dereferenced).
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class KVCache:
+    k: object                  # bf16 [B, Hkv, n_cap, D]
+    v: object
+    B: int = 0
+    Hkv: int = 0
+    n_cap: int = 0
+    D: int = 0
+
+    def __post_init__(self):
+        if hasattr(self.k, "shape") and not self.B:
+            self.B, self.Hkv, self.n_cap, self.D = (int(x) for x in self.k.shape)
+
+
+@dataclasses.dataclass
+class MaskDesc:
+    kind: int
+    Hq: int
+    M: int
+    kv_len: int
+    prefix_len: int = 0
+    block_size: int = 0
+    n_slots: int = 0
+    slot_state: object = None  # uint8 [B, n_slots]
+    slot_group: object = None  # int32 [B, n_slots]
+    cs_lo: int = 0
+    cs_hi: int = 0
+    colsum_per_head: int = 0
+    scale: float = 0.0
+    workspace: object = None   # uint8 device buffer
+    workspace_bytes: Optional[int] = None
+
+
+@dataclasses.dataclass
+class Select:
+    mode: int
+    k: int = 0
+    group_rows: int = 1
+    tau: float = 0.0
+    score: object = None       # fp32 [R]
+    workspace: object = None
+    workspace_bytes: Optional[int] = None
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _nbytes(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return 0
+    return x.numel() * x.element_size()
+
+
+def _c_kv(kv: KVCache) -> _KVCache:
+    return _KVCache(_ptr(kv.k), _ptr(kv.v), kv.B, kv.Hkv, kv.n_cap, kv.D)
+
+
+def _c_mask(md: MaskDesc) -> _MaskDesc:
+    wb = md.workspace_bytes if md.workspace_bytes is not None else _nbytes(md.workspace)
+    return _MaskDesc(md.kind, md.Hq, md.M, md.kv_len, md.prefix_len, md.block_size, md.n_slots,
+                     _ptr(md.slot_state), _ptr(md.slot_group), md.cs_lo, md.cs_hi,
+                     md.colsum_per_head, md.scale, _ptr(md.workspace), wb)
+
+
+def _c_sel(s: Select) -> _Select:
+    wb = s.workspace_bytes if s.workspace_bytes is not None else _nbytes(s.workspace)
+    return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _expect(t, name, shape, dtype):
+    """Tensor argument check: device tensor, contiguous, exact shape/dtype."""
+    if t is None or isinstance(t, int):
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise DlmError(DLM_E_SHAPE, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if str(t.dtype) != dtype:
+        raise DlmError(DLM_E_SHAPE, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise DlmError(DLM_E_SHAPE, f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise DlmError(DLM_E_SHAPE, f"{name} must be a device tensor")
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def dlm_step_attn_workspace_bytes(kv_cache: KVCache, mask_desc: MaskDesc) -> int:
+    n = ctypes.c_size_t(0)
+    kv, md = _c_kv(kv_cache), _c_mask(mask_desc)
+    _check(lib.dlm_step_attn_workspace_bytes(ctypes.byref(kv), ctypes.byref(md), ctypes.byref(n)))
+    return n.value
+
+
+def dlm_step_attn(q, k, v, kv_cache: KVCache, active_idx, mask_desc: MaskDesc, out, lse,
+                  colsum=None, stream=None) -> None:
+    B, Hkv, n_cap, D = kv_cache.B, kv_cache.Hkv, kv_cache.n_cap, kv_cache.D
+    Hq, M = mask_desc.Hq, mask_desc.M
+    _expect(q, "q", (B, Hq, M, D), "torch.bfloat16")
+    _expect(k, "k", (B, Hkv, M, D), "torch.bfloat16")
+    _expect(v, "v", (B, Hkv, M, D), "torch.bfloat16")
+    _expect(kv_cache.k, "kv_cache.k", (B, Hkv, n_cap, D), "torch.bfloat16")
+    _expect(kv_cache.v, "kv_cache.v", (B, Hkv, n_cap, D), "torch.bfloat16")
+    _expect(active_idx, "active_idx", (B, M), "torch.int32")
+    _expect(out, "out", (B, Hq, M, D), "torch.bfloat16")
+    _expect(lse, "lse", (B, Hq, M), "torch.float32")
+    if colsum is not None:
+        shape = (B, Hq, mask_desc.kv_len) if mask_desc.colsum_per_head else (B, mask_desc.kv_len)
+        _expect(colsum, "colsum", shape, "torch.float32")
+    if mask_desc.kind == MASK_GROUP:
+        _expect(mask_desc.slot_state, "slot_state", (B, mask_desc.n_slots), "torch.uint8")
+        _expect(mask_desc.slot_group, "slot_group", (B, mask_desc.n_slots), "torch.int32")
+    kv, md = _c_kv(kv_cache), _c_mask(mask_desc)
+    _check(lib.dlm_step_attn(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(kv), _ptr(active_idx),
+                             ctypes.byref(md), _ptr(out), _ptr(lse), _ptr(colsum), _stream(stream)))
+
+
+def dlm_posterior_workspace_bytes(R: int, V: int, select: Select) -> int:
+    n = ctypes.c_size_t(0)
+    s = _c_sel(select)
+    _check(lib.dlm_posterior_workspace_bytes(R, V, ctypes.byref(s), ctypes.byref(n)))
+    return n.value
+
+
+def dlm_posterior(logits, prev_logits, locked, eps: float, select: Select, sel, kl, conf,
+                  R: int, V: int, stream=None) -> None:
+    _expect(logits, "logits", (R, V), "torch.float32")
+    _expect(prev_logits, "prev_logits", (R, V), "torch.float32")
+    _expect(locked, "locked", (R,), "torch.uint8")
+    _expect(sel, "sel", (R,), "torch.int32")
+    _expect(kl, "kl", (R,), "torch.float32")
+    _expect(conf, "conf", (R,), "torch.float32")
+    if select.score is not None:
+        _expect(select.score, "select.score", (R,), "torch.float32")
+    s = _c_sel(select)
+    _check(lib.dlm_posterior(_ptr(logits), _ptr(prev_logits), _ptr(locked), eps, ctypes.byref(s),
+                             _ptr(sel), _ptr(kl), _ptr(conf), R, V, _stream(stream)))

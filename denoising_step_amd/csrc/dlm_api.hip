@@ -1,0 +1,250 @@
+// dlm_api.hip -- host side of the C ABI declared in include/dlm_step.h:
+// argument validation (before anything is enqueued), workspace sizing,
+// launch plans, and the optional DLM_VALIDATE content check.
+#include "dlm_step.h"
+#include "dlm_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool validate_env()
+{
+    const char *e = getenv("DLM_VALIDATE");
+    return e && e[0] == '1';
+}
+
+// Scalar checks shared by dlm_step_attn and its workspace query.
+int check_attn_scalars(const dlm_kv_cache *kc, const dlm_mask_desc *md)
+{
+    if (!kc) return fail(DLM_E_NULL, "kv_cache is NULL");
+    if (!md) return fail(DLM_E_NULL, "mask_desc is NULL");
+    if (kc->B < 1 || kc->Hkv < 1 || md->Hq < 1)
+        return fail(DLM_E_SHAPE, "B=%d Hkv=%d Hq=%d must be >= 1", kc->B, kc->Hkv, md->Hq);
+    if (kc->D != 32 && kc->D != 64 && kc->D != 128)
+        return fail(DLM_E_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", kc->D);
+    if (md->Hq % kc->Hkv != 0)
+        return fail(DLM_E_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", md->Hq, kc->Hkv);
+    if (md->kv_len < 1 || md->kv_len > kc->n_cap)
+        return fail(DLM_E_SHAPE, "kv_len=%d must be in [1, n_cap=%d]", md->kv_len, kc->n_cap);
+    if (md->prefix_len < 0 || md->prefix_len > md->kv_len)
+        return fail(DLM_E_SHAPE, "prefix_len=%d must be in [0, kv_len=%d]", md->prefix_len, md->kv_len);
+    if (md->M < 0 || md->M > md->kv_len - md->prefix_len)
+        return fail(DLM_E_SHAPE, "M=%d must be in [0, kv_len - prefix_len = %d]", md->M,
+                    md->kv_len - md->prefix_len);
+    if ((long)kc->B * md->Hq * md->M > (1L << 31) - 1 ||
+        (long)kc->B * kc->Hkv * kc->n_cap > (1L << 31) - 1)
+        return fail(DLM_E_SHAPE, "problem too large for 32-bit row indices");
+    if (md->kind < DLM_MASK_FULL || md->kind > DLM_MASK_GROUP)
+        return fail(DLM_E_DESC, "unknown mask kind %d", md->kind);
+    if (md->kind != DLM_MASK_FULL && md->block_size < 1)
+        return fail(DLM_E_DESC, "block_size=%d must be >= 1 for block-causal / group masks",
+                    md->block_size);
+    if (md->kind == DLM_MASK_GROUP) {
+        if (md->n_slots < 1 || md->n_slots > dlm::kMaxSlots)
+            return fail(DLM_E_DESC, "n_slots=%d must be in [1, %d]", md->n_slots, dlm::kMaxSlots);
+        if (!md->slot_state || !md->slot_group)
+            return fail(DLM_E_NULL, "group mask needs slot_state and slot_group");
+        if ((long)md->prefix_len + (long)md->n_slots * md->block_size < md->kv_len)
+            return fail(DLM_E_DESC, "kv_len=%d exceeds prefix_len + n_slots * block_size = %ld",
+                        md->kv_len, (long)md->prefix_len + (long)md->n_slots * md->block_size);
+    }
+    if (md->cs_lo > md->cs_hi)
+        return fail(DLM_E_DESC, "cs_lo=%d > cs_hi=%d", md->cs_lo, md->cs_hi);
+    if (md->colsum_per_head != 0 && md->colsum_per_head != 1)
+        return fail(DLM_E_DESC, "colsum_per_head must be 0 or 1");
+    if (!(md->scale >= 0.f) || isinf(md->scale))
+        return fail(DLM_E_DESC, "scale must be finite and >= 0 (0 selects 1/sqrt(D))");
+    return DLM_OK;
+}
+
+// DLM_VALIDATE=1: check the contents of active_idx and the slot tables on a
+// host copy (synchronises the stream).
+int validate_contents(const dlm_kv_cache *kc, const dlm_mask_desc *md, const int32_t *active_idx,
+                      hipStream_t stream)
+{
+    const int B = kc->B, M = md->M;
+    std::vector<int32_t> act((size_t)B * M);
+    std::vector<uint8_t> st;
+    std::vector<int32_t> gr;
+    if (M > 0 && hipMemcpyAsync(act.data(), active_idx, act.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return fail(DLM_E_HIP, "DLM_VALIDATE: copy of active_idx failed");
+    if (md->kind == DLM_MASK_GROUP) {
+        st.resize((size_t)B * md->n_slots);
+        gr.resize((size_t)B * md->n_slots);
+        if (hipMemcpyAsync(st.data(), md->slot_state, st.size(), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipMemcpyAsync(gr.data(), md->slot_group, gr.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess)
+            return fail(DLM_E_HIP, "DLM_VALIDATE: copy of slot tables failed");
+    }
+    if (hipStreamSynchronize(stream) != hipSuccess) return fail(DLM_E_HIP, "DLM_VALIDATE: sync failed");
+    for (int b = 0; b < B; ++b)
+        for (int j = 0; j < M; ++j) {
+            int p = act[(size_t)b * M + j];
+            if (p < md->prefix_len || p >= md->kv_len)
+                return fail(DLM_E_DESC, "active_idx[%d,%d]=%d outside [prefix_len=%d, kv_len=%d)", b, j, p,
+                            md->prefix_len, md->kv_len);
+            if (j > 0 && p <= act[(size_t)b * M + j - 1])
+                return fail(DLM_E_DESC, "active_idx[%d] not strictly ascending at %d", b, j);
+        }
+    for (size_t i = 0; i < st.size(); ++i) {
+        if (st[i] > DLM_SLOT_IN_CACHE) return fail(DLM_E_DESC, "slot_state[%zu]=%d unknown", i, st[i]);
+        if (gr[i] < 0 || gr[i] == 0x7fffffff) return fail(DLM_E_DESC, "slot_group[%zu]=%d out of range", i, gr[i]);
+    }
+    return DLM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char *dlm_last_error(void) { return g_err; }
+
+int dlm_step_attn_workspace_bytes(const dlm_kv_cache *kv_cache, const dlm_mask_desc *mask_desc,
+                                  size_t *bytes)
+{
+    g_err[0] = 0;
+    if (!bytes) return fail(DLM_E_NULL, "bytes is NULL");
+    int rc = check_attn_scalars(kv_cache, mask_desc);
+    if (rc != DLM_OK) return rc;
+    dlm::AttnPlan p = dlm::plan_attn(kv_cache->B, mask_desc->Hq, kv_cache->Hkv, kv_cache->D,
+                                     mask_desc->M, mask_desc->kv_len, kv_cache->n_cap);
+    *bytes = p.ws_total;
+    return DLM_OK;
+}
+
+int dlm_step_attn(const void *q, const void *k, const void *v, const dlm_kv_cache *kv_cache,
+                  const int32_t *active_idx, const dlm_mask_desc *mask_desc, void *out, float *lse,
+                  float *colsum, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_attn_scalars(kv_cache, mask_desc);
+    if (rc != DLM_OK) return rc;
+    const dlm_kv_cache *kc = kv_cache;
+    const dlm_mask_desc *md = mask_desc;
+    if (!kc->k || !kc->v) return fail(DLM_E_NULL, "the cache k/v must be non-NULL");
+    if (md->M > 0 && (!q || !active_idx || !out || !lse))
+        return fail(DLM_E_NULL, "q, active_idx, out and lse must be non-NULL when M > 0");
+    if (md->M > 0 && (k == nullptr) != (v == nullptr))
+        return fail(DLM_E_NULL, "fresh k and v must both be given or both be NULL");
+    if ((md->M > 0 && (!aligned16(q) || !aligned16(out))) || !aligned16(kc->k) || !aligned16(kc->v) ||
+        (k && !aligned16(k)) || (v && !aligned16(v)))
+        return fail(DLM_E_SHAPE, "bf16 tensors must be 16-byte aligned");
+    dlm::AttnPlan p = dlm::plan_attn(kc->B, md->Hq, kc->Hkv, kc->D, md->M, md->kv_len, kc->n_cap);
+    const size_t need = p.ws_total;
+    if (need > 0 && (md->workspace == nullptr || md->workspace_bytes < need))
+        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    md->workspace ? md->workspace_bytes : (size_t)0);
+    if (validate_env()) {
+        rc = validate_contents(kc, md, active_idx, stream);
+        if (rc != DLM_OK) return rc;
+    }
+
+    dlm::AttnArgs a{};
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.ck = static_cast<uint16_t *>(kc->k);
+    a.cv = static_cast<uint16_t *>(kc->v);
+    a.active_idx = active_idx;
+    a.slot_state = md->slot_state;
+    a.slot_group = md->slot_group;
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.colsum = colsum;
+    char *ws = static_cast<char *>(md->workspace);
+    a.ws_o = p.ws_split_o ? reinterpret_cast<float *>(ws) : nullptr;
+    a.ws_l = p.ws_split_l ? reinterpret_cast<float *>(ws + align256(p.ws_split_o)) : nullptr;
+    a.ws_cs = reinterpret_cast<float *>(ws + align256(p.ws_split_o) + align256(p.ws_split_l));
+    a.B = kc->B; a.Hq = md->Hq; a.Hkv = kc->Hkv; a.G = md->Hq / kc->Hkv; a.D = kc->D; a.M = md->M;
+    a.n_cap = kc->n_cap; a.kv_len = md->kv_len; a.P = md->prefix_len; a.bs = md->block_size;
+    a.n_slots = md->kind == DLM_MASK_GROUP ? md->n_slots : 0;
+    a.kind = md->kind;
+    a.cs_lo = md->cs_lo; a.cs_hi = md->cs_hi; a.per_head = md->colsum_per_head;
+    const float scale = md->scale > 0.f ? md->scale : 1.f / sqrtf((float)kc->D);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.n_qtiles = p.n_qtiles; a.n_split = p.n_split; a.split_keys = p.split_keys;
+    a.n_kblocks = p.n_kblocks; a.n_rsplit = p.n_rsplit;
+
+    hipError_t e = dlm::launch_step_attn(a, stream);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return DLM_OK;
+}
+
+static int check_post_scalars(int32_t R, int32_t V, const dlm_select *s)
+{
+    if (!s) return fail(DLM_E_NULL, "select is NULL");
+    if (R < 0) return fail(DLM_E_SHAPE, "R=%d must be >= 0", R);
+    if (V < 1) return fail(DLM_E_SHAPE, "V=%d must be >= 1", V);
+    if ((long)R * V > (1L << 40)) return fail(DLM_E_SHAPE, "R*V too large");
+    if (s->mode < DLM_SEL_NONE || s->mode > DLM_SEL_TOPK_SCORE)
+        return fail(DLM_E_DESC, "unknown selection mode %d", s->mode);
+    if (s->mode != DLM_SEL_NONE && (s->group_rows < 1 || s->group_rows > dlm::kMaxGroupRows))
+        return fail(DLM_E_DESC, "group_rows=%d must be in [1, %d]", s->group_rows, dlm::kMaxGroupRows);
+    if ((s->mode == DLM_SEL_TOPK_CONF || s->mode == DLM_SEL_TOPK_SCORE) && s->k < 0)
+        return fail(DLM_E_DESC, "k=%d must be >= 0", s->k);
+    if ((s->mode == DLM_SEL_THRESH_CONF || s->mode == DLM_SEL_ATTN_DYNAMIC) && !isfinite(s->tau))
+        return fail(DLM_E_DESC, "tau must be finite");
+    return DLM_OK;
+}
+
+int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select, size_t *bytes)
+{
+    g_err[0] = 0;
+    if (!bytes) return fail(DLM_E_NULL, "bytes is NULL");
+    int rc = check_post_scalars(R, V, select);
+    if (rc != DLM_OK) return rc;
+    *bytes = dlm::plan_post(R, V, select->mode, select->group_rows).ws_total;
+    return DLM_OK;
+}
+
+int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked, float eps,
+                  const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R, int32_t V,
+                  hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_post_scalars(R, V, select);
+    if (rc != DLM_OK) return rc;
+    if (!logits || !prev_logits || !locked || !sel || !kl || !conf)
+        return fail(DLM_E_NULL, "logits, prev_logits, locked, sel, kl and conf must be non-NULL");
+    if ((select->mode == DLM_SEL_ATTN_DYNAMIC || select->mode == DLM_SEL_TOPK_SCORE) && !select->score)
+        return fail(DLM_E_NULL, "selection by score needs select->score");
+    if (isnan(eps)) return fail(DLM_E_DESC, "eps is NaN");
+    if ((V & 3) == 0 && (!aligned16(logits) || !aligned16(prev_logits)))
+        return fail(DLM_E_SHAPE, "logits must be 16-byte aligned");
+    dlm::PostPlan p = dlm::plan_post(R, V, select->mode, select->group_rows);
+    if (p.ws_total > 0 && (select->workspace == nullptr || select->workspace_bytes < p.ws_total))
+        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_total,
+                    select->workspace ? select->workspace_bytes : (size_t)0);
+    dlm::PostArgs a{};
+    a.x = logits; a.y = prev_logits; a.locked = locked; a.score = select->score;
+    a.sel = sel; a.kl = kl; a.conf = conf;
+    a.part = static_cast<dlm::PostPartial *>(select->workspace);
+    a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
+    a.eps = eps; a.tau = select->tau; a.n_chunks = p.n_chunks; a.chunk = p.chunk;
+    hipError_t e = dlm::launch_posterior(a, stream);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return DLM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// dlm_internal.h -- types, tile constants, launch plans and kernel-launch
+// declarations shared by the HIP sources of libdlm_step.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dlm {
+
+// MFMA operand / accumulator types (gfx950 v_mfma_f32_32x32x16_bf16).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kNumCU = 256;          // MI355X: 256 CUs in 8 XCDs
+constexpr int kNumXCD = 8;
+constexpr int kAttnRows = 128;       // query rows per attention workgroup (4 waves x 32)
+constexpr int kKeyTile = 64;         // keys per LDS tile in pass 1
+constexpr int kCsKeys = 256;         // keys per column-sum workgroup (4 waves x 64)
+constexpr int kCsRows = 32;          // query rows per column-sum tile
+constexpr int kMaxSlots = 1024;      // GROUP: slots per batch entry
+constexpr int kMaxGroupRows = 1024;  // posterior selection group
+constexpr int kPostThreads = 256;
+constexpr int kPostVec = 4 * 4;      // floats per thread per streaming step (4 x float4)
+
+// Launch plan of dlm_step_attn, a pure function of the shapes.
+struct AttnPlan {
+    int B, Hq, Hkv, G, D, M, kv_len, n_cap;
+    int n_qtiles;       // query tiles of kAttnRows packed rows per (b, kv-head)
+    int n_split;        // key splits of pass 1
+    int split_keys;     // keys per split (multiple of kKeyTile)
+    int n_kblocks;      // column-sum key blocks of kCsKeys
+    int n_rsplit;       // column-sum row splits
+    size_t ws_split_o;  // bytes of split partial outputs (fp32)
+    size_t ws_split_l;  // bytes of split partial lse (fp32)
+    size_t ws_colsum;   // bytes of column-sum partials (fp32)
+    size_t ws_total;
+};
+AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap);
+
+// Per-row partial state of the posterior stream over one vocabulary chunk.
+struct PostPartial {
+    float mx;   // running max of logits x
+    float sx;   // sum exp(x - mx)
+    float tx;   // sum exp(x - mx) * (x - y)
+    float my;   // running max of previous logits y
+    float sy;   // sum exp(y - my)
+    float av;   // largest x seen
+    int ai;     // lowest index attaining av
+    int pad;
+};
+
+struct PostPlan {
+    int n_chunks;       // vocabulary chunks per row
+    int chunk;          // elements per chunk (multiple of 4)
+    int group_rows;     // rows per finishing workgroup
+    size_t ws_total;
+};
+PostPlan plan_post(int R, int V, int mode, int group_rows);
+
+struct AttnArgs {
+    const uint16_t *q, *k, *v;      // bf16 bit patterns
+    uint16_t *ck, *cv;
+    const int32_t *active_idx;
+    const uint8_t *slot_state;
+    const int32_t *slot_group;
+    uint16_t *out;
+    float *lse, *colsum;
+    float *ws_o, *ws_l, *ws_cs;
+    int B, Hq, Hkv, G, D, M, n_cap, kv_len, P, bs, n_slots, kind;
+    int cs_lo, cs_hi, per_head;
+    float scale_log2;               // softmax scale * log2(e)
+    int n_qtiles, n_split, split_keys, n_kblocks, n_rsplit;
+};
+
+struct PostArgs {
+    const float *x, *y;
+    uint8_t *locked;
+    const float *score;
+    int32_t *sel;
+    float *kl, *conf;
+    PostPartial *part;
+    int R, V, mode, k, group_rows;
+    float eps, tau;
+    int n_chunks, chunk;
+};
+
+// Enqueue the kernels of one call (arguments already validated).
+hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_posterior(const PostArgs &a, hipStream_t stream);
+
+// Map a hardware workgroup id to a logical one so that logically
+// consecutive workgroups (which share K/V) run on the same XCD: the
+// dispatcher deals workgroups round-robin over the 8 XCDs.
+__device__ __forceinline__ int xcd_remap(int hw, int n)
+{
+    int per = n / kNumXCD, rem = n % kNumXCD;
+    int x = hw % kNumXCD, kth = hw / kNumXCD;
+    return x * per + (x < rem ? x : rem) + kth;
+}
+
+}  // namespace dlm

@@ -1,0 +1,218 @@
+/*
+ * dlm_step.h -- C ABI of one masked-diffusion LM denoising step on MI355X
+ * (gfx950).
+ *
+ * One step has two calls:
+ *   dlm_step_attn  -- sparse-query attention of the active rows over the K/V
+ *                     cache under a bidirectional, block-causal or
+ *                     group-aware mask, plus attention column sums;
+ *   dlm_posterior  -- per-row softmax posterior, confidence, the step-wise
+ *                     KL(p_t || p_{t-1}) lock test and unmask selection.
+ *
+ * Conventions for every entry point:
+ *  - Pointers to tensors are DEVICE pointers (HIP global memory) and every
+ *    tensor is dense and row-major in the layout stated.  The descriptor
+ *    structs themselves (dlm_kv_cache, dlm_mask_desc, dlm_select) live in
+ *    HOST memory and are read during the call only.
+ *  - bf16 is IEEE bfloat16 stored as 16-bit words; fp32 is IEEE binary32.
+ *  - The caller owns every buffer, the workspace included.  The library
+ *    allocates nothing, frees nothing, keeps no state between calls and does
+ *    not synchronise: all work is enqueued on `stream` and outputs are valid
+ *    once that stream reaches the point of the call.
+ *  - Every function returns DLM_OK (0) or a negative DLM_E_* code; the
+ *    message of the last failure on the calling thread is dlm_last_error().
+ *    Scalar and descriptor checks run on the host before anything is
+ *    enqueued, so a failed call has enqueued no work.  The CONTENTS of device
+ *    arrays (order of active_idx, slot tables) are not checked unless the
+ *    environment variable DLM_VALIDATE=1 is set, in which case a host copy is
+ *    checked first (this synchronises the stream); otherwise contents that
+ *    break the stated rules give undefined results.
+ *  - Calls on one stream are ordered; calls on different streams that share
+ *    a workspace or an output race.
+ */
+#ifndef DLM_STEP_H
+#define DLM_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DLM_OK = 0,
+    DLM_E_NULL = -1,        /* a required pointer is NULL */
+    DLM_E_SHAPE = -2,       /* a size is out of range or sizes disagree */
+    DLM_E_UNSUPPORTED = -3, /* valid, but not built: D not in {32,64,128}, Hq % Hkv != 0, ... */
+    DLM_E_DESC = -4,        /* bad mask / selection descriptor (or DLM_VALIDATE content check) */
+    DLM_E_WORKSPACE = -5,   /* workspace missing or too small */
+    DLM_E_HIP = -6          /* a HIP runtime call or kernel launch failed */
+};
+
+/* Mask kinds.  Query position i (an active row), key position n:
+ *  FULL          n < kv_len: bidirectional attention, every token sees the
+ *                whole context ("Bifocal Diffusion Language Models", sec. 1).
+ *  BLOCK_CAUSAL  n < prefix_len, or block(n) <= block(i), where
+ *                block(x) = (x - prefix_len) / block_size: one noisy block
+ *                sees the clean prefix and the blocks before it and itself
+ *                ("Multi-Block Diffusion LMs", sec. 1, SingleBD).
+ *  GROUP         n < prefix_len, or slot(n) is not DUMMY and
+ *                group(slot(n)) <= group(slot(i)), slot(x) = block(x):
+ *                blocks of one noise group see each other, earlier groups
+ *                and completed slots are clean context, the prefix never sees
+ *                the noisy blocks because it is never a query
+ *                ("Multi-Block Diffusion LMs", sec. 2.2 group-aware mask,
+ *                sec. 2.3 block-buffer slot states).
+ * Keys at or beyond kv_len are never visible. */
+enum { DLM_MASK_FULL = 0, DLM_MASK_BLOCK_CAUSAL = 1, DLM_MASK_GROUP = 2 };
+
+/* Block-buffer slot states ("Multi-Block Diffusion LMs", sec. 2.3). */
+enum { DLM_SLOT_DUMMY = 0, DLM_SLOT_ACTIVE = 1, DLM_SLOT_TO_CACHE = 2, DLM_SLOT_IN_CACHE = 3 };
+
+/* The K/V cache of one attention layer: k and v are bf16 [B, Hkv, n_cap, D]
+ * each (device).  Rows [0, kv_len) of each (b, kv-head) are meaningful. */
+typedef struct {
+    void *k;
+    void *v;
+    int32_t B, Hkv, n_cap, D;
+} dlm_kv_cache;
+
+/* Problem and mask descriptor of dlm_step_attn. */
+typedef struct {
+    int32_t kind;            /* DLM_MASK_* */
+    int32_t Hq;              /* query heads; Hq % Hkv == 0; q-head h reads kv-head h / (Hq/Hkv) */
+    int32_t M;               /* active query rows per batch entry */
+    int32_t kv_len;          /* key positions [0, kv_len), kv_len <= n_cap */
+    int32_t prefix_len;      /* clean prefix [0, prefix_len): never written, never a query */
+    int32_t block_size;      /* BLOCK_CAUSAL / GROUP: positions per block (slot) */
+    int32_t n_slots;         /* GROUP: slots per batch entry, <= 1024, and
+                                kv_len <= prefix_len + n_slots * block_size */
+    const uint8_t *slot_state;   /* GROUP: device uint8 [B, n_slots], DLM_SLOT_* */
+    const int32_t *slot_group;   /* GROUP: device int32 [B, n_slots], noise-group id */
+    int32_t cs_lo, cs_hi;    /* active rows whose POSITION lies in [cs_lo, cs_hi) feed colsum */
+    int32_t colsum_per_head; /* 0: colsum is [B, kv_len] summed over q-heads; 1: [B, Hq, kv_len] */
+    float scale;             /* softmax scale; 0 means 1/sqrt(D) */
+    void *workspace;         /* device scratch, >= dlm_step_attn_workspace_bytes() */
+    size_t workspace_bytes;
+} dlm_mask_desc;
+
+/*
+ * dlm_step_attn -- one denoising step's attention for the active rows.
+ *
+ * Defines ("Stopping Computation for Converged Tokens in Masked Diffusion-LM
+ * Decoding" (SureLock), sec. 2 core mechanism; "Bifocal Diffusion Language
+ * Models", sec. 2 inference; "Attention-Based Sampler for Diffusion
+ * Language Models", sec. 2B):
+ *   1. the fresh K/V of the active rows are written into the cache at their
+ *      positions: cache[b, g, active_idx[b, j], :] = k[b, g, j, :] (same for
+ *      v).  Locked rows and the prefix keep their cached K/V.
+ *   2. for each active row j of batch b and q-head h (kv-head g = h/(Hq/Hkv)),
+ *      at position i = active_idx[b, j], over the keys n visible to i:
+ *        s_n   = scale * q[b,h,j,:] . Kcache[b,g,n,:]
+ *        lse   = log sum_n exp(s_n)                (natural log)
+ *        out   = sum_n exp(s_n - lse) * Vcache[b,g,n,:]
+ *      A row with no visible key gets out = 0 and lse = -inf.
+ *   3. if colsum != NULL, the attention column sums
+ *        colsum[b, n] = sum_h sum_{j : cs_lo <= active_idx[b,j] < cs_hi}
+ *                       exp(s^{(b,h,j)}_n - lse_{b,h,j})   (0 where not visible)
+ *      ([B, Hq, kv_len] without the sum over h if colsum_per_head).  Columns
+ *      are exact (each row normalised by its full log-sum-exp), computed in a
+ *      fixed order: bitwise reproducible for equal inputs.
+ *
+ * Arguments (device unless stated):
+ *   q          bf16 [B, Hq, M, D]       queries of the active rows
+ *   k, v       bf16 [B, Hkv, M, D]      fresh K/V of the active rows; both
+ *                                       NULL means "already in the cache"
+ *   kv_cache   host struct; cache k/v are written at active positions only
+ *   active_idx int32 [B, M]             positions, strictly ascending per b,
+ *                                       each in [prefix_len, kv_len)
+ *   mask_desc  host struct (above)
+ *   out        bf16 [B, Hq, M, D]       attention output (round to nearest even)
+ *   lse        fp32 [B, Hq, M]          natural-log log-sum-exp of each row
+ *   colsum     fp32 [B, kv_len] or [B, Hq, kv_len], or NULL
+ *   stream     HIP stream all work is enqueued on
+ * Supported: D in {32, 64, 128}; Hq % Hkv == 0.
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_DESC,
+ *         DLM_E_WORKSPACE, DLM_E_HIP.
+ */
+int dlm_step_attn(const void *q, const void *k, const void *v,
+                  const dlm_kv_cache *kv_cache, const int32_t *active_idx,
+                  const dlm_mask_desc *mask_desc, void *out, float *lse,
+                  float *colsum, hipStream_t stream);
+
+/* Workspace bytes dlm_step_attn needs for this problem (with colsum).
+ * Writes *bytes; returns DLM_OK or the error dlm_step_attn would return
+ * for the scalar arguments. */
+int dlm_step_attn_workspace_bytes(const dlm_kv_cache *kv_cache,
+                                  const dlm_mask_desc *mask_desc, size_t *bytes);
+
+/* Unmask selection modes:
+ *  NONE          lock test only.
+ *  TOPK_CONF     the k most confident eligible rows of each group
+ *                (confidence sampler; "Attention-Based Sampler ...", sec. 1).
+ *  THRESH_CONF   eligible rows with conf > tau; if none, the most confident.
+ *  ATTN_DYNAMIC  Attn-Sampler dynamic attention threshold (sec. 2B):
+ *                candidates = eligible rows with conf > tau; threshold =
+ *                largest score among eligible non-candidates (-inf if none);
+ *                decode candidates whose score exceeds it; if none, the
+ *                eligible row of highest score.
+ *  TOPK_SCORE    the k eligible rows of highest score (column-sum order).
+ * Eligible = not locked on entry.  Order: larger key first, then lower row
+ * index.  If fewer than k rows are eligible, all are taken. */
+enum { DLM_SEL_NONE = 0, DLM_SEL_TOPK_CONF = 1, DLM_SEL_THRESH_CONF = 2,
+       DLM_SEL_ATTN_DYNAMIC = 3, DLM_SEL_TOPK_SCORE = 4 };
+
+typedef struct {
+    int32_t mode;            /* DLM_SEL_* */
+    int32_t k;               /* TOPK_*: rows per group, >= 0 */
+    int32_t group_rows;      /* rows per selection group (consecutive rows), 1..1024 */
+    float tau;               /* THRESH_CONF / ATTN_DYNAMIC confidence threshold */
+    const float *score;      /* device fp32 [R]: ATTN_DYNAMIC / TOPK_SCORE ranking key */
+    void *workspace;         /* device scratch, >= dlm_posterior_workspace_bytes() */
+    size_t workspace_bytes;
+} dlm_select;
+
+/*
+ * dlm_posterior -- posterior, lock test and unmask selection for R rows.
+ *
+ * Defines (SureLock page, sec. 2 core mechanism; Attn-Sampler page,
+ * sec. 1 and 2B), per row r that arrives with locked[r] == 0:
+ *   p_t = softmax(logits[r]), p_{t-1} = softmax(prev_logits[r])
+ *   kl[r]   = KL(p_t || p_{t-1}) = sum_v p_t(v) (log p_t(v) - log p_{t-1}(v))
+ *   conf[r] = max_v p_t(v);  tok = lowest v with the largest logit
+ *   locked[r] = 1 if kl[r] <= eps (a lock is never undone)
+ *   sel[r]  = tok if the row is selected (mode above), else -1.
+ * A row that arrives locked is not read: kl = conf = 0, sel = -1, stays locked.
+ * kl and conf are fp32; KL is computed in one pass as
+ * E_p[x - y] - (logsumexp x - logsumexp y).
+ *
+ * Arguments (device unless stated):
+ *   logits       fp32 [R, V]   step-t logits
+ *   prev_logits  fp32 [R, V]   step-(t-1) logits of the same rows
+ *   locked       uint8 [R]     in/out lock flags
+ *   eps          lock threshold
+ *   select       host struct (above)
+ *   sel          int32 [R]     out
+ *   kl, conf     fp32 [R]      out
+ *   R, V         rows (>= 0) and vocabulary size (>= 1)
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_DESC, DLM_E_WORKSPACE, DLM_E_HIP.
+ */
+int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked,
+                  float eps, const dlm_select *select, int32_t *sel, float *kl,
+                  float *conf, int32_t R, int32_t V, hipStream_t stream);
+
+/* Workspace bytes dlm_posterior needs for R x V.  Writes *bytes. */
+int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select,
+                                  size_t *bytes);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *dlm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLM_STEP_H */

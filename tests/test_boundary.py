@@ -1,0 +1,176 @@
+"""The C-ABI library: loads, exports every declared entry point, sizes its
+workspaces, and rejects bad arguments on the host before enqueuing work.
+
+No GPU is needed: every call here fails validation (or is a workspace query)
+before any HIP call, so the dummy device addresses are never dereferenced.
+"""
+import os
+import re
+
+import pytest
+
+import denoising_step_amd as dlm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000          # a 16-byte aligned dummy device address, never dereferenced
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            with open(os.path.join(ROOT, "include", fn)) as f:
+                text = f.read()
+            names |= set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(dlm_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared()
+    assert declared == set(dlm.EXPORTS), declared
+    for name in declared:
+        assert hasattr(dlm.lib, name), name
+
+
+def _kv(B=2, Hkv=2, n_cap=128, D=64):
+    return dlm.KVCache(FAKE, FAKE, B, Hkv, n_cap, D)
+
+
+def _md(**kw):
+    base = dict(kind=dlm.MASK_FULL, Hq=4, M=16, kv_len=100, prefix_len=10, cs_lo=0, cs_hi=100)
+    base.update(kw)
+    return dlm.MaskDesc(**base)
+
+
+def _attn(kv=None, md=None, q=FAKE, k=FAKE, v=FAKE, active=FAKE, out=FAKE, lse=FAKE, colsum=FAKE):
+    kv = kv or _kv()
+    md = md or _md()
+    if md.workspace is None:
+        md.workspace = FAKE
+        try:
+            md.workspace_bytes = dlm.dlm_step_attn_workspace_bytes(kv, md)
+        except dlm.DlmError:
+            md.workspace_bytes = 1 << 40
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_step_attn(q, k, v, kv, active, md, out, lse, colsum, stream=0)
+    return e.value.code
+
+
+def test_workspace_queries():
+    n = dlm.dlm_step_attn_workspace_bytes(_kv(), _md())
+    assert n > 0 and n % 256 == 0
+    # the long-prefix shape uses key splits: partial outputs need room
+    long_kv = dlm.KVCache(FAKE, FAKE, 1, 32, 16640, 128)
+    n_long = dlm.dlm_step_attn_workspace_bytes(long_kv, _md(Hq=32, M=256, kv_len=16640, prefix_len=16384))
+    assert n_long >= 32 * 256 * 128 * 4 * 2
+    s = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=4, group_rows=16)
+    assert dlm.dlm_posterior_workspace_bytes(16, 512, s) >= 16 * 32
+    assert dlm.dlm_posterior_workspace_bytes(0, 512, s) == 0
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(kv=_kv(D=48)), dlm.DLM_E_UNSUPPORTED),
+    (dict(md=_md(Hq=3)), dlm.DLM_E_UNSUPPORTED),
+    (dict(kv=_kv(B=0)), dlm.DLM_E_SHAPE),
+    (dict(md=_md(kv_len=129)), dlm.DLM_E_SHAPE),
+    (dict(md=_md(kv_len=0)), dlm.DLM_E_SHAPE),
+    (dict(md=_md(prefix_len=101)), dlm.DLM_E_SHAPE),
+    (dict(md=_md(prefix_len=-1)), dlm.DLM_E_SHAPE),
+    (dict(md=_md(M=91)), dlm.DLM_E_SHAPE),
+    (dict(md=_md(M=-1)), dlm.DLM_E_SHAPE),
+    (dict(md=_md(kind=7)), dlm.DLM_E_DESC),
+    (dict(md=_md(kind=dlm.MASK_BLOCK_CAUSAL, block_size=0)), dlm.DLM_E_DESC),
+    (dict(md=_md(kind=dlm.MASK_GROUP, block_size=16, n_slots=0, slot_state=FAKE, slot_group=FAKE)), dlm.DLM_E_DESC),
+    (dict(md=_md(kind=dlm.MASK_GROUP, block_size=16, n_slots=2000, slot_state=FAKE, slot_group=FAKE)), dlm.DLM_E_DESC),
+    (dict(md=_md(kind=dlm.MASK_GROUP, block_size=16, n_slots=6)), dlm.DLM_E_NULL),
+    (dict(md=_md(kind=dlm.MASK_GROUP, block_size=16, n_slots=5, slot_state=FAKE, slot_group=FAKE)), dlm.DLM_E_DESC),
+    (dict(md=_md(cs_lo=50, cs_hi=40)), dlm.DLM_E_DESC),
+    (dict(md=_md(colsum_per_head=2)), dlm.DLM_E_DESC),
+    (dict(md=_md(scale=-1.0)), dlm.DLM_E_DESC),
+    (dict(md=_md(scale=float("nan"))), dlm.DLM_E_DESC),
+    (dict(q=None), dlm.DLM_E_NULL),
+    (dict(active=None), dlm.DLM_E_NULL),
+    (dict(out=None), dlm.DLM_E_NULL),
+    (dict(lse=None), dlm.DLM_E_NULL),
+    (dict(kv=dlm.KVCache(None, FAKE, 2, 2, 128, 64)), dlm.DLM_E_NULL),
+    (dict(v=None), dlm.DLM_E_NULL),
+    (dict(q=FAKE + 2), dlm.DLM_E_SHAPE),
+    (dict(out=FAKE + 8), dlm.DLM_E_SHAPE),
+])
+def test_step_attn_rejects(case, code):
+    assert _attn(**case) == code
+    assert dlm.dlm_last_error() != ""
+
+
+def test_step_attn_workspace_checked():
+    md = _md()
+    md.workspace = None
+    md.workspace_bytes = 0
+    md2 = _md()
+    md2.workspace = FAKE
+    md2.workspace_bytes = dlm.dlm_step_attn_workspace_bytes(_kv(), md2) - 1
+    for m in (md, md2):
+        with pytest.raises(dlm.DlmError) as e:
+            dlm.dlm_step_attn(FAKE, FAKE, FAKE, _kv(), FAKE, m, FAKE, FAKE, FAKE, stream=0)
+        assert e.value.code == dlm.DLM_E_WORKSPACE
+
+
+def test_null_descriptors():
+    import ctypes
+    rc = dlm.lib.dlm_step_attn(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, None)
+    assert rc == dlm.DLM_E_NULL
+    n = ctypes.c_size_t(0)
+    assert dlm.lib.dlm_posterior_workspace_bytes(4, 4, None, ctypes.byref(n)) == dlm.DLM_E_NULL
+    assert dlm.lib.dlm_posterior(FAKE, FAKE, FAKE, 1e-3, None, FAKE, FAKE, FAKE, 4, 4, None) == dlm.DLM_E_NULL
+
+
+def _post(R=16, V=512, sel=None, logits=FAKE, prev=FAKE, locked=FAKE, out=FAKE, eps=1e-3, ws=True):
+    sel = sel or dlm.Select(mode=dlm.SEL_TOPK_CONF, k=4, group_rows=16)
+    if ws and sel.workspace is None and R >= 0 and V >= 1:
+        try:
+            sel.workspace_bytes = dlm.dlm_posterior_workspace_bytes(R, V, sel)
+            sel.workspace = FAKE
+        except dlm.DlmError:
+            pass
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_posterior(logits, prev, locked, eps, sel, out, FAKE, FAKE, R, V, stream=0)
+    return e.value.code
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(R=-1), dlm.DLM_E_SHAPE),
+    (dict(V=0), dlm.DLM_E_SHAPE),
+    (dict(sel=dlm.Select(mode=9)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=2, group_rows=0)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=2, group_rows=1025)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=-1, group_rows=16)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_THRESH_CONF, group_rows=16, tau=float("nan"))), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_ATTN_DYNAMIC, group_rows=16, tau=0.9)), dlm.DLM_E_NULL),
+    (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_SCORE, k=3, group_rows=16)), dlm.DLM_E_NULL),
+    (dict(logits=None), dlm.DLM_E_NULL),
+    (dict(prev=None), dlm.DLM_E_NULL),
+    (dict(locked=None), dlm.DLM_E_NULL),
+    (dict(out=None), dlm.DLM_E_NULL),
+    (dict(eps=float("nan")), dlm.DLM_E_DESC),
+    (dict(logits=FAKE + 4), dlm.DLM_E_SHAPE),
+    (dict(ws=False), dlm.DLM_E_WORKSPACE),
+])
+def test_posterior_rejects(case, code):
+    assert _post(**case) == code
+
+
+def test_oracle_and_library_share_no_code():
+    """The GPU sources and the oracle neither include nor import each other."""
+    csrc = os.path.join(ROOT, "denoising_step_amd", "csrc")
+    for fn in os.listdir(csrc):
+        with open(os.path.join(csrc, fn)) as f:
+            assert "oracle" not in f.read().lower(), fn
+    pkg = os.path.join(ROOT, "denoising_step_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            with open(os.path.join(pkg, fn)) as f:
+                text = f.read()
+            assert "import oracle" not in text and "from oracle" not in text, fn
+    with open(os.path.join(ROOT, "oracle", "dlm_oracle.c")) as f:
+        src = f.read()
+    assert "dlm_step.h" not in src and "dlm_internal.h" not in src

@@ -1,0 +1,364 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element on the same seeded inputs.
+
+Reduced shapes (several tiles plus a ragged tail, every mask kind, GQA, key
+splits, every selection mode, edge cases) are compared in full; the full
+workloads are compared on sampled rows and columns the oracle computes one
+by one, plus invariants that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import (check_attention, check_colsum, check_posterior, check_selection)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the GPU tests need an MI355X")
+    import denoising_step_amd  # noqa: F401  (raises if the library is not built)
+    yield
+
+
+def _device_step(w, **kw):
+    from denoising_step_amd.runner import DeviceStep
+    return DeviceStep(w, **kw)
+
+
+# --------------------------------------------------------------------------
+# reduced workloads
+# --------------------------------------------------------------------------
+
+def small_llada(spread=False, seed=0):
+    N = 300
+    std = 1.0 if spread else 1.0 / np.sqrt(128)
+    a = W.make_attn("small_llada", B=1, Hq=4, Hkv=4, D=128, kv_len=N, prefix_len=0,
+                    active_idx=np.arange(N, dtype=np.int32)[None], kind=W.MASK_FULL,
+                    cs_lo=150, cs_hi=N, q_std=std, kv_std=std, cache_std=std, seed=seed)
+    p = W.make_post("small_llada", R=32, V=5000, logit_std=3.0, noise_std=0.1, eps=1e-3,
+                    mode=W.SEL_ATTN_DYNAMIC, tau=0.9, group_rows=32,
+                    spike_frac=0.25 if spread else 0.0, score_cols=(0, 150), seed=seed)
+    return W.Workload(a, p, "small llada")
+
+
+def small_mbd(variant="group", D=128, per_head=0, V=8192, seed=0):
+    B, Hq, Hkv, P, bs = 2, 8, 2, 333, 32
+    n_slots = 6 if variant == "dummy" else 4
+    kv_len = P + n_slots * bs
+    M = 4 * bs
+    act = np.tile(np.arange(P, P + M, dtype=np.int32), (B, 1))
+    state = np.full((B, n_slots), W.SLOT_ACTIVE, np.uint8)
+    state[:, 4:] = W.SLOT_DUMMY
+    state[1, 1] = W.SLOT_IN_CACHE
+    group = np.zeros((B, n_slots), np.int32)
+    kind = W.MASK_GROUP
+    garbage = None
+    if variant == "two_groups":
+        group[:, :4] = [0, 0, 1, 1]
+    elif variant == "block_causal":
+        kind = W.MASK_BLOCK_CAUSAL
+    elif variant == "dummy":
+        garbage = np.zeros((B, kv_len), bool)
+        garbage[:, P + M:] = True
+    a = W.make_attn("small_mbd_" + variant, B=B, Hq=Hq, Hkv=Hkv, D=D, kv_len=kv_len, prefix_len=P,
+                    active_idx=act, kind=kind, block_size=bs, n_slots=n_slots, slot_state=state,
+                    slot_group=group, cs_lo=P, cs_hi=P + M, colsum_per_head=per_head,
+                    garbage_rows=garbage, seed=seed)
+    p = W.make_post(a.name, R=B * M, V=V, logit_std=3.0, noise_std=0.1, eps=1e-3,
+                    mode=W.SEL_TOPK_CONF, k=8, group_rows=bs, locked_frac=0.1, seed=seed)
+    return W.Workload(a, p, "small mbd " + variant)
+
+
+def small_surelock(D=128, Hq=4, Hkv=4, seed=0):
+    rng = np.random.default_rng(100 + seed)
+    B, N, M = 2, 1000, 250
+    std = 1.0 / np.sqrt(D)
+    a = W.make_attn("small_surelock", B=B, Hq=Hq, Hkv=Hkv, D=D, kv_len=N, prefix_len=0,
+                    active_idx=W.sorted_subset(rng, B, 0, N, M), kind=W.MASK_FULL,
+                    q_std=std, kv_std=std, cache_std=std, n_cap=N + 24, seed=seed)
+    p = W.make_post("small_surelock", R=B * M, V=10000, logit_std=3.0, noise_std=0.0,
+                    mixture=(0.4, 0.02, 0.1), eps=1e-3, mode=W.SEL_NONE, locked_frac=0.1,
+                    seed=seed)
+    return W.Workload(a, p, "small surelock")
+
+
+def small_long(seed=0):
+    P, gen = 3000, 256
+    a = W.make_attn("small_long", B=1, Hq=4, Hkv=4, D=128, kv_len=P + gen, prefix_len=P,
+                    active_idx=np.arange(P, P + gen, dtype=np.int32)[None], kind=W.MASK_FULL,
+                    cs_lo=P, cs_hi=P + gen, seed=seed)
+    p = W.make_post("small_long", R=gen, V=20000, logit_std=3.0, noise_std=0.1, eps=1e-3,
+                    mode=W.SEL_TOPK_SCORE, k=16, group_rows=gen, score_cols=(0, P), seed=seed)
+    return W.Workload(a, p, "small long prefix (key splits)")
+
+
+def full_check(w, check_cache=True):
+    _say(f"case: {w.attn.name} / {w.post.name}")
+    ora = oracle.step(w)
+    ds = _device_step(w)
+    ds.run()
+    g = ds.results()
+    if check_cache:
+        assert np.array_equal(g["cache_k"], ora["cache_k"]), "cache K after scatter differs"
+        assert np.array_equal(g["cache_v"], ora["cache_v"]), "cache V after scatter differs"
+    check_attention(g["out"], g["lse"], ora["out"], ora["lse"])
+    check_colsum(g["colsum"], ora["colsum"])
+    p = w.post
+    lk_exc = check_posterior(g["kl"], g["conf"], g["locked"], ora["kl"], ora["conf"], ora["locked"],
+                             p.eps, p.locked)
+    sel_exc = check_selection(g["sel"], ora["sel"], p.mode, p.group_rows, p.tau, ora["conf"],
+                              ora["score"], p.locked, p.logits)
+    _say(f"  excused: locks {lk_exc}, selections {sel_exc}")
+    return ds, g, ora
+
+
+def test_tiny():
+    full_check(W.tiny())
+
+
+@pytest.mark.parametrize("spread", [False, True])
+def test_small_llada(spread):
+    full_check(small_llada(spread))
+
+
+@pytest.mark.parametrize("variant", ["group", "dummy", "block_causal", "two_groups"])
+def test_small_mbd(variant):
+    full_check(small_mbd(variant))
+
+
+def test_small_mbd_per_head_colsum_scalar_vocab():
+    full_check(small_mbd("two_groups", per_head=1, V=4099))
+
+
+def test_small_surelock():
+    full_check(small_surelock())
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 4, 2), (32, 6, 3), (128, 8, 1)])
+def test_head_dims_and_gqa(D, Hq, Hkv):
+    full_check(small_surelock(D=D, Hq=Hq, Hkv=Hkv))
+
+
+def test_small_long_prefix_key_splits():
+    full_check(small_long())
+
+
+def test_deterministic():
+    w = small_long(seed=1)
+    ds = _device_step(w)
+    ds.run()
+    r1 = ds.results()
+    ds.reset()
+    ds.run()
+    r2 = ds.results()
+    for k in ("out", "lse", "colsum", "kl", "conf", "sel", "locked"):
+        assert np.array_equal(r1[k], r2[k]), k
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def test_single_active_row_short_cache():
+    a = W.make_attn("one_row", B=1, Hq=2, Hkv=1, D=128, kv_len=37, prefix_len=5,
+                    active_idx=np.array([[20]], np.int32), kind=W.MASK_FULL, cs_lo=0, cs_hi=37)
+    p = W.make_post("one_row", R=1, V=3, logit_std=1.0, noise_std=0.1, eps=1e-3,
+                    mode=W.SEL_THRESH_CONF, tau=0.99, group_rows=1)
+    full_check(W.Workload(a, p, "one row"))
+
+
+def test_row_without_visible_key():
+    """GROUP, no prefix: a query in a DUMMY slot of group 0 sees nothing
+    (its own slot is dummy, the other slot is in a later group)."""
+    bs = 16
+    act = np.array([list(range(0, 8)) + list(range(bs, bs + 8))], np.int32)
+    a = W.make_attn("no_key", B=1, Hq=2, Hkv=2, D=64, kv_len=2 * bs, prefix_len=0,
+                    active_idx=act, kind=W.MASK_GROUP, block_size=bs, n_slots=2,
+                    slot_state=np.array([[W.SLOT_DUMMY, W.SLOT_ACTIVE]], np.uint8),
+                    slot_group=np.array([[0, 1]], np.int32), cs_lo=0, cs_hi=2 * bs)
+    p = W.make_post("no_key", R=16, V=64, logit_std=2.0, noise_std=0.05, eps=1e-3,
+                    mode=W.SEL_TOPK_CONF, k=3, group_rows=5)
+    _, g, ora = full_check(W.Workload(a, p, "rows without keys"), check_cache=True)
+    assert np.isneginf(ora["lse"][0, :, :8]).all()
+    assert np.all(g["out"][0, :, :8] == 0)
+
+
+def test_zero_active_rows():
+    import denoising_step_amd as dlm
+    dev = torch.device("cuda")
+    B, Hkv, N, D = 2, 2, 100, 64
+    ck = torch.zeros((B, Hkv, N, D), dtype=torch.bfloat16, device=dev)
+    cv = torch.zeros_like(ck)
+    kv = dlm.KVCache(ck, cv)
+    md = dlm.MaskDesc(kind=dlm.MASK_FULL, Hq=4, M=0, kv_len=N, cs_lo=0, cs_hi=N)
+    md.workspace = torch.empty(max(1, dlm.dlm_step_attn_workspace_bytes(kv, md)), dtype=torch.uint8, device=dev)
+    colsum = torch.full((B, N), 7.0, device=dev)
+    empty_q = torch.empty((B, 4, 0, D), dtype=torch.bfloat16, device=dev)
+    dlm.dlm_step_attn(empty_q, None, None, kv, torch.empty((B, 0), dtype=torch.int32, device=dev), md,
+                      torch.empty((B, 4, 0, D), dtype=torch.bfloat16, device=dev),
+                      torch.empty((B, 4, 0), dtype=torch.float32, device=dev), colsum)
+    torch.cuda.synchronize()
+    assert torch.all(colsum == 0)
+
+
+def test_posterior_edge_cases():
+    """Ragged last group, arrived-locked rows holding NaN (never read), argmax
+    ties, every selection mode, a vocabulary that is not a multiple of 4."""
+    import denoising_step_amd as dlm
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(21)
+    R, V = 37, 1003
+    x = (rng.standard_normal((R, V)) * 2).astype(np.float32)
+    x[3, [10, 500]] = 9.0          # tie for the argmax: lowest index wins
+    y = (x + rng.standard_normal((R, V)) * np.where(rng.random(R) < 0.5, 0.01, 0.2)[:, None]).astype(np.float32)
+    y[5] = x[5]                    # KL exactly 0
+    locked = (rng.random(R) < 0.2).astype(np.uint8)
+    x[locked == 1] = np.nan        # a locked row is never read
+    y[locked == 1] = np.nan
+    score = rng.random(R).astype(np.float32)
+    ora = oracle.posterior(x, y, locked, 1e-3)
+    for mode, k, tau, g in [(W.SEL_TOPK_CONF, 3, 0.0, 8), (W.SEL_THRESH_CONF, 0, 0.05, 6),
+                            (W.SEL_ATTN_DYNAMIC, 0, 0.05, 10), (W.SEL_TOPK_SCORE, 4, 0.0, 37),
+                            (W.SEL_NONE, 0, 0.0, 1)]:
+        _say(f"case: posterior edges mode={mode}")
+        s = dlm.Select(mode=mode, k=k, group_rows=g, tau=tau,
+                       score=torch.from_numpy(score).to(dev))
+        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device=dev)
+        lk = torch.from_numpy(locked.copy()).to(dev)
+        sel = torch.empty(R, dtype=torch.int32, device=dev)
+        kl = torch.empty(R, dtype=torch.float32, device=dev)
+        conf = torch.empty(R, dtype=torch.float32, device=dev)
+        dlm.dlm_posterior(torch.from_numpy(x).to(dev), torch.from_numpy(y).to(dev), lk, 1e-3, s,
+                          sel, kl, conf, R, V)
+        torch.cuda.synchronize()
+        check_posterior(kl.cpu().numpy(), conf.cpu().numpy(), lk.cpu().numpy(), ora["kl"], ora["conf"],
+                        ora["locked"], 1e-3, locked)
+        sel_o = oracle.select(mode, k, g, tau, score.astype(np.float64), ora["conf"], ora["tok"], locked)
+        check_selection(sel.cpu().numpy(), sel_o, mode, g, tau, ora["conf"], score.astype(np.float64),
+                        locked, np.nan_to_num(x))
+        assert kl.cpu().numpy()[5] == 0.0 or abs(kl.cpu().numpy()[5]) < 1e-6
+        assert np.all(sel.cpu().numpy()[locked == 1] == -1)
+
+
+# --------------------------------------------------------------------------
+# full workloads: sampled outputs and invariants
+# --------------------------------------------------------------------------
+
+def _sub_batch(case, b):
+    return W.AttnCase(**{**case.__dict__, "B": 1, "q": case.q[b:b + 1], "k": case.k[b:b + 1],
+                         "v": case.v[b:b + 1], "cache_k": case.cache_k[b:b + 1],
+                         "cache_v": case.cache_v[b:b + 1], "active_idx": case.active_idx[b:b + 1],
+                         "slot_state": case.slot_state[b:b + 1], "slot_group": case.slot_group[b:b + 1]})
+
+
+def _check_attn_sampled(a, g, n_rows=256, colsum_batch=0, extra_cols=None, seed=0):
+    """Sampled out/lse rows for the whole batch; every row's lse and sampled
+    columns of one batch entry; the column-total invariant for every entry."""
+    rng = np.random.default_rng(seed)
+    kv = oracle.effective_kv(a)
+    assert np.array_equal(g["cache_k"], kv[0]) and np.array_equal(g["cache_v"], kv[1])
+    rows = np.sort(rng.choice(a.B * a.Hq * a.M, size=min(n_rows, a.B * a.Hq * a.M), replace=False))
+    out_o, lse_o = oracle.attention(a, kv=kv, rows=rows)
+    out_g = g["out"].reshape(-1, a.D)[rows]
+    lse_g = g["lse"].reshape(-1)[rows]
+    check_attention(out_g, lse_g, out_o, lse_o)
+    # one batch entry in full for the column sums
+    sb = _sub_batch(a, colsum_batch)
+    kvb = (kv[0][colsum_batch:colsum_batch + 1], kv[1][colsum_batch:colsum_batch + 1])
+    _, lse_b = oracle.attention(sb, kv=kvb, want_out=False)
+    check_attention(np.zeros((1, 1), np.uint16), g["lse"][colsum_batch].reshape(-1),
+                    np.zeros((1, 1)), lse_b.reshape(-1))
+    cols = rng.choice(a.kv_len, size=min(256, a.kv_len), replace=False)
+    if extra_cols is not None:
+        cols = np.union1d(cols, extra_cols)
+    cs_o = oracle.colsum(sb, lse_b, kv=kvb, cols=cols)
+    cs_g = g["colsum"][colsum_batch][cols] if not a.colsum_per_head else g["colsum"][colsum_batch][:, cols].T
+    check_colsum(cs_g, cs_o)
+    # invariant: each counted row's weights sum to 1
+    counted = ((a.active_idx >= a.cs_lo) & (a.active_idx < a.cs_hi)).sum(axis=1)
+    tot = g["colsum"].reshape(a.B, -1).astype(np.float64).sum(axis=1)
+    assert np.allclose(tot, a.Hq * counted, rtol=1e-4), (tot, a.Hq * counted)
+    return cs_o, cols
+
+
+def _check_post_sampled(p, g, rows, score_o=None):
+    ora = oracle.posterior(p.logits, p.prev, p.locked, p.eps, rows=rows)
+    check_posterior(g["kl"][rows], g["conf"][rows], g["locked"][rows], ora["kl"], ora["conf"],
+                    ora["locked"], p.eps, p.locked[rows])
+    return ora
+
+
+def test_full_llada_bidirectional():
+    full_check(W.llada_bidirectional())
+
+
+def test_full_llada_bidirectional_spread():
+    full_check(W.llada_bidirectional(spread=True))
+
+
+@pytest.mark.parametrize("variant", ["group", "dummy", "block_causal", "two_groups"])
+def test_full_mbd_multiblock(variant):
+    w = W.mbd_multiblock(variant=variant)
+    _say(f"case: {w.attn.name} (sampled)")
+    with_post = variant == "group"
+    ds = _device_step(w, with_posterior=with_post)
+    ds.run()
+    g = ds.results()
+    a = w.attn
+    _check_attn_sampled(a, g, extra_cols=np.arange(a.prefix_len - 64, a.kv_len))
+    if with_post:
+        p = w.post
+        groups = [0, 5, 17, 31]
+        rows = np.concatenate([np.arange(q * p.group_rows, (q + 1) * p.group_rows) for q in groups])
+        ora = _check_post_sampled(p, g, rows)
+        for q in range(len(groups)):
+            sl = slice(q * p.group_rows, (q + 1) * p.group_rows)
+            rr = rows[sl]
+            sel_o = oracle.select(p.mode, p.k, p.group_rows, p.tau, None, ora["conf"][sl], ora["tok"][sl],
+                                  p.locked[rr])
+            check_selection(g["sel"][rr], sel_o, p.mode, p.group_rows, p.tau, ora["conf"][sl], None,
+                            p.locked[rr], p.logits[rr])
+
+
+def test_full_surelock_sparse():
+    w = W.surelock_sparse()
+    _say("case: surelock_sparse (sampled)")
+    ds = _device_step(w)
+    ds.run()
+    g = ds.results()
+    _check_attn_sampled(w.attn, g, colsum_batch=1)
+    p = w.post
+    rows = np.sort(np.random.default_rng(3).choice(p.R, size=256, replace=False))
+    _check_post_sampled(p, g, rows)
+    assert np.all(g["sel"] == -1)
+    frac = g["locked"].mean()
+    _say(f"  locked fraction after the step: {frac:.3f}")
+    assert 0.3 < frac < 0.5
+
+
+def test_full_long_prefix_sampler():
+    w = W.long_prefix_sampler()
+    _say("case: long_prefix_sampler (sampled, exact top-16)")
+    ds = _device_step(w)
+    ds.run()
+    g = ds.results()
+    a, p = w.attn, w.post
+    gen_cols = np.arange(a.prefix_len, a.kv_len)
+    cs_o, cols = _check_attn_sampled(a, g, extra_cols=gen_cols)
+    score_o = cs_o[np.searchsorted(cols, gen_cols)]
+    ora = oracle.posterior(p.logits, p.prev, p.locked, p.eps)
+    check_posterior(g["kl"], g["conf"], g["locked"], ora["kl"], ora["conf"], ora["locked"], p.eps, p.locked)
+    sel_o = oracle.select(p.mode, p.k, p.group_rows, p.tau, score_o, ora["conf"], ora["tok"], p.locked)
+    exc = check_selection(g["sel"], sel_o, p.mode, p.group_rows, p.tau, ora["conf"], score_o, p.locked,
+                          p.logits)
+    assert (g["sel"] >= 0).sum() == 16
+    _say(f"  excused selections: {exc}")

@@ -21,6 +21,7 @@ standard deviation ("N(0, s)" is read as standard deviation s).
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -51,9 +52,35 @@ def bf16_bits_to_f32(b) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def _streams(config_id: int, seed: int):
+def _seqs(config_id: int, seed: int):
     children = np.random.SeedSequence([config_id, seed]).spawn(len(_STREAMS))
-    return {name: np.random.default_rng(s) for name, s in zip(_STREAMS, children)}
+    return dict(zip(_STREAMS, children))
+
+
+def _streams(config_id: int, seed: int):
+    return {name: np.random.default_rng(s) for name, s in _seqs(config_id, seed).items()}
+
+
+def _par_normal(seq, shape, std, block_rows=256) -> np.ndarray:
+    """float32 N(0, std) of the given 2-D shape, filled in row blocks by
+    worker threads; block i draws from the i-th child of ``seq``, so the
+    result does not depend on the number of threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    R, V = shape
+    out = np.empty((R, V), np.float32)
+    n_blocks = max(1, (R + block_rows - 1) // block_rows)
+    kids = seq.spawn(n_blocks)
+
+    def fill(i):
+        r0, r1 = i * block_rows, min(R, (i + 1) * block_rows)
+        np.random.default_rng(kids[i]).standard_normal(size=(r1 - r0, V), dtype=np.float32,
+                                                       out=out[r0:r1])
+        out[r0:r1] *= np.float32(std)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, range(n_blocks)))
+    return out
 
 
 def _normal_bf16(rng, shape, std) -> np.ndarray:
@@ -180,11 +207,10 @@ def make_post(name, *, R, V, logit_std, noise_std, eps, mode, k=0,
     ``spike_value`` in both arrays.  ``locked_frac`` of rows arrive locked.
     ``score_std`` draws an explicit per-row score (for posterior-only cases).
     """
-    rs = _streams(config_id, seed)
-    logits = rs["logits"].standard_normal(size=(R, V), dtype=np.float32)
-    logits *= np.float32(logit_std)
-    noise = rs["noise"].standard_normal(size=(R, V), dtype=np.float32)
-    mx = rs["mixture"]
+    seqs = _seqs(config_id, seed)
+    logits = _par_normal(seqs["logits"], (R, V), logit_std)
+    noise = _par_normal(seqs["noise"], (R, V), 1.0)
+    mx = np.random.default_rng(seqs["mixture"])
     if mixture is not None:
         frac, std_a, std_b = mixture
         pick = mx.random(R) < frac
