@@ -32,7 +32,28 @@ EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                       "(hipcc --offload-arch=gfx950)")
+
+# PyTorch ships its own HIP runtime.  The library must bind to that same
+# runtime (it is linked against the soname libamdhip64.so.7, which torch's
+# copy carries), so torch is imported first; loading the library first would
+# map a second HIP runtime into the process and torch's streams would be
+# handed to the wrong one.
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are mapped into this process "
+                      f"({_hip_runtimes()}); import torch before loading libdlm_step")
 
 
 class DlmError(RuntimeError):

@@ -174,3 +174,14 @@ def test_oracle_and_library_share_no_code():
     with open(os.path.join(ROOT, "oracle", "dlm_oracle.c")) as f:
         src = f.read()
     assert "dlm_step.h" not in src and "dlm_internal.h" not in src
+
+
+def test_single_hip_runtime():
+    """The library binds to the HIP runtime that PyTorch loaded: one runtime
+    in the process, whatever was imported first."""
+    import subprocess
+    import sys
+    code = ("import denoising_step_amd as d; print(len(d._hip_runtimes()))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.strip()
+    assert out == "1", out
