@@ -52,6 +52,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Raw buffer view of [base, base + bytes): 16-byte loads at or past `bytes`
+// return zeros (hardware range check), so tails need no branches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    return uint4{v[0], v[1], v[2], v[3]};
+}
+
 // Key code: a key is visible to a query iff key_code <= query_code.
 //   FULL:          in-range keys INT_MIN; query code 0.
 //   BLOCK_CAUSAL:  prefix INT_MIN; block index; query code = its block.
@@ -78,13 +91,14 @@ __device__ __forceinline__ int query_code(const AttnArgs &a, const int32_t *gr, 
 }
 
 // ---------------------------------------------------------------------------
-// Scatter: cache[b, g, active_idx[b, j], :] = fresh[b, g, j, :], 16 B/thread.
+// Scatter: cache[b, g, active_idx[b, j], :] = fresh[b, g, j, :], 16 B per
+// thread.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a, long total)
+__global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a, long scatter_total)
 {
     const int ch = a.D / 8;
-    long t = (long)blockIdx.x * 256 + threadIdx.x;
-    if (t >= total) return;
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= scatter_total) return;
     int c = (int)(t % ch);
     long row = t / ch;                  // (b*Hkv + g)*M + j
     int j = (int)(row % a.M);
@@ -99,8 +113,21 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a, long total)
 // ---------------------------------------------------------------------------
 // Pass 1.  Workgroup = 4 waves = 128 packed query rows of one (b, kv-head):
 // packed row r = (q-head within the GQA group) * M + j, so the G q-heads that
-// share a kv-head share every K/V tile staged in LDS.  Optional key split.
+// share a kv-head share every K/V tile staged in LDS.  Two workgroups share
+// a CU, so one can run its softmax while the other keeps the matrix cores
+// busy.
+//
+// K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
+// t+1 are issued before tile t is computed and stored to the other buffer
+// afterwards, so one barrier per tile suffices.  The running max is only
+// moved when it grows by more than kRescaleLog2 (log2 units): exp2 arguments
+// stay <= kRescaleLog2, and the O/l rescale is skipped on most tiles.
+//
+// With a key split, each workgroup writes its normalised partial (out, lse)
+// to the workspace and a separate kernel merges the splits in split order.
 // ---------------------------------------------------------------------------
+constexpr float kRescaleLog2 = 8.f;
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
 {
@@ -114,9 +141,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     constexpr int VGROUPS = (KT / 4) * CH;       // (4-key group, chunk) pairs per tile
     constexpr int VLOADS = (VGROUPS + 255) / 256;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
-    __shared__ int kcode_s[KT];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+    __shared__ int kcode_s[2][KT];
     __shared__ int scode_s[kMaxSlots];
 
     const int tid = threadIdx.x;
@@ -159,6 +186,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     const int k1 = min(a.kv_len, k0 + a.split_keys);
     const uint16_t *kbase = a.ck + (long)bg * a.n_cap * D;
     const uint16_t *vbase = a.cv + (long)bg * a.n_cap * D;
+    const float c2 = a.scale_log2;
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 o[DT];
@@ -166,45 +194,52 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
 
     uint4 kreg[KLOADS], vreg[VLOADS][4];
 
-    // A key row is loaded when it is below kv_len and not in a DUMMY slot
-    // (DUMMY rows may hold anything; their weight is 0, their values must
-    // not poison 0 * V).
-    auto row_ok = [&](int n) -> bool {
-        if (n >= a.kv_len) return false;
-        if (a.kind != 2 || n < a.P) return true;
-        int s = (n - a.P) / a.bs;
-        return s < a.n_slots && scode_s[s] != INT_MAX;
+    // K/V rows at or past kv_len read as zeros (buffer range check).  Rows
+    // in a DUMMY slot of a GROUP mask are zeroed after loading: they may hold
+    // anything, their weight is 0, and their values must not poison 0 * V.
+    const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = buffer_view(vbase, a.kv_len * D * 2);
+    auto dummy_row = [&](int n) -> bool {
+        if (n < a.P || n >= a.kv_len) return false;
+        const int s = (n - a.P) / a.bs;
+        return s >= a.n_slots || scode_s[s] == INT_MAX;
     };
     auto load_tile = [&](int t0) {
         for (int u = 0; u < KLOADS; ++u) {
-            int idx = tid + 256 * u;
-            int n = idx / CH, c = idx % CH;
-            kreg[u] = row_ok(t0 + n) ? *reinterpret_cast<const uint4 *>(kbase + (long)(t0 + n) * D + c * 8)
-                                     : uint4{0, 0, 0, 0};
+            const int idx = tid + 256 * u;
+            kreg[u] = buffer_load16(krs, ((t0 + idx / CH) * D + (idx % CH) * 8) * 2);
         }
         for (int u = 0; u < VLOADS; ++u) {
-            int idx = tid + 256 * u;
+            const int idx = tid + 256 * u;
             if (idx < VGROUPS) {
-                int kg = idx % (KT / 4), c = idx / (KT / 4);
-                for (int e = 0; e < 4; ++e) {
-                    int n = t0 + kg * 4 + e;
-                    vreg[u][e] = row_ok(n) ? *reinterpret_cast<const uint4 *>(vbase + (long)n * D + c * 8)
-                                           : uint4{0, 0, 0, 0};
-                }
+                const int kg = idx % (KT / 4), c = idx / (KT / 4);
+                for (int e = 0; e < 4; ++e) vreg[u][e] = buffer_load16(vrs, ((t0 + kg * 4 + e) * D + c * 8) * 2);
+            }
+        }
+        if (a.kind == 2 && t0 + KT > a.P) {
+            for (int u = 0; u < KLOADS; ++u)
+                if (dummy_row(t0 + (tid + 256 * u) / CH)) kreg[u] = uint4{0, 0, 0, 0};
+            for (int u = 0; u < VLOADS; ++u) {
+                const int idx = tid + 256 * u;
+                if (idx < VGROUPS)
+                    for (int e = 0; e < 4; ++e)
+                        if (dummy_row(t0 + (idx % (KT / 4)) * 4 + e)) vreg[u][e] = uint4{0, 0, 0, 0};
             }
         }
     };
-    auto store_tile = [&](int t0) {
+    auto store_tile = [&](int buf, int t0) {
+        uint16_t *ks = Ks[buf];
+        uint16_t *vt = Vt[buf];
         for (int u = 0; u < KLOADS; ++u) {
-            int idx = tid + 256 * u;
-            int n = idx / CH, c = idx % CH;
-            int nr = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);   // sigma(n)
-            *reinterpret_cast<uint4 *>(&Ks[nr * KSTR + c * 8]) = kreg[u];
+            const int idx = tid + 256 * u;
+            const int n = idx / CH, c = idx % CH;
+            const int nr = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);   // sigma(n)
+            *reinterpret_cast<uint4 *>(&ks[nr * KSTR + c * 8]) = kreg[u];
         }
         for (int u = 0; u < VLOADS; ++u) {
-            int idx = tid + 256 * u;
+            const int idx = tid + 256 * u;
             if (idx < VGROUPS) {
-                int kg = idx % (KT / 4), c = idx / (KT / 4);
+                const int kg = idx % (KT / 4), c = idx / (KT / 4);
                 const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&vreg[u][0]);
                 const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&vreg[u][1]);
                 const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&vreg[u][2]);
@@ -216,129 +251,152 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
                     ev.y = (w2[w] & 0xFFFFu) | (w3[w] << 16);
                     od.x = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
                     od.y = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
-                    *reinterpret_cast<uint2 *>(&Vt[(c * 8 + 2 * w) * VSTR + kg * 4]) = ev;
-                    *reinterpret_cast<uint2 *>(&Vt[(c * 8 + 2 * w + 1) * VSTR + kg * 4]) = od;
+                    *reinterpret_cast<uint2 *>(&vt[(c * 8 + 2 * w) * VSTR + kg * 4]) = ev;
+                    *reinterpret_cast<uint2 *>(&vt[(c * 8 + 2 * w + 1) * VSTR + kg * 4]) = od;
                 }
             }
         }
-        if (tid < KT) kcode_s[tid] = key_code(a, st, gr, t0 + tid);
+        if (tid < KT) kcode_s[buf][tid] = key_code(a, st, gr, t0 + tid);
     };
 
     __syncthreads();   // slot codes visible
-    if (k0 < k1) load_tile(k0);
-    for (int t0 = k0; t0 < k1; t0 += KT) {
-        __syncthreads();
-        store_tile(t0);
-        __syncthreads();
-        if (t0 + KT < k1) load_tile(t0 + KT);
+    if (k0 < k1) {
+        load_tile(k0);
+        store_tile(0, k0);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int t0 = k0; t0 < k1; t0 += KT, buf ^= 1) {
+        const bool more = t0 + KT < k1;
+        if (more) load_tile(t0 + KT);
 
         // S^T for two 32-key sub-tiles.
         f32x16 s[2];
         for (int sub = 0; sub < 2; ++sub) {
             s[sub] = f32x16{};
-            const uint16_t *kr = &Ks[(sub * 32 + l32) * KSTR + hh * 8];
+            const uint16_t *kr = &Ks[buf][(sub * 32 + l32) * KSTR + hh * 8];
             for (int kk = 0; kk < DK; ++kk) s[sub] = mfma32(lds_frag(kr + kk * 16), qf[kk], s[sub]);
         }
         const bool all_vis = (a.kind == 0 && t0 + KT <= a.kv_len) || (t0 + KT <= a.P);
-        float tmax = -INFINITY;
-        for (int sub = 0; sub < 2; ++sub) {
-            for (int i = 0; i < 16; ++i) {
-                float v = s[sub][i] * a.scale_log2;
-                if (!all_vis) {
-                    int key = sub * 32 + 16 * (i >> 3) + 8 * hh + (i & 7);
-                    if (kcode_s[key] > qcode) v = -INFINITY;
+        if (!all_vis) {
+            for (int sub = 0; sub < 2; ++sub)
+                for (int i = 0; i < 16; ++i) {
+                    const int key = sub * 32 + 16 * (i >> 3) + 8 * hh + (i & 7);
+                    if (kcode_s[buf][key] > qcode) s[sub][i] = -INFINITY;
                 }
-                s[sub][i] = v;
-                tmax = fmaxf(tmax, v);
-            }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
+        // Raw-score max (scale > 0, so the max commutes with scaling).
+        float tmax = s[0][0];
+        for (int sub = 0; sub < 2; ++sub)
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[sub][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;
+        const bool grow = tmax > m_run + kRescaleLog2;
+        if (__any(grow)) {
+            // lanes that do not grow keep their max (alpha = 1; this also
+            // keeps a lane that has seen no key at m = -inf without NaN)
+            const float alpha = grow ? fast_exp2(m_run - tmax) : 1.f;   // 0 when m_run = -inf
+            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+            l_run *= alpha;
+            if (grow) m_run = tmax;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float psum = 0.f;
         bf16x8 pf[2][2];
         for (int sub = 0; sub < 2; ++sub)
             for (int t = 0; t < 2; ++t)
                 for (int e = 0; e < 8; ++e) {
-                    float p = fast_exp2(s[sub][t * 8 + e] - m_use);
+                    const float p = fast_exp2(fmaf(s[sub][t * 8 + e], c2, -m_use));
                     psum += p;
                     pf[sub][t][e] = (__bf16)p;
                 }
-        l_run = l_run * alpha + psum;
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        l_run += psum;
         for (int sub = 0; sub < 2; ++sub)
             for (int t = 0; t < 2; ++t)
                 for (int dt = 0; dt < DT; ++dt) {
-                    bf16x8 vf = lds_frag(&Vt[(dt * 32 + l32) * VSTR + sub * 32 + t * 16 + hh * 8]);
+                    const bf16x8 vf = lds_frag(&Vt[buf][(dt * 32 + l32) * VSTR + sub * 32 + t * 16 + hh * 8]);
                     o[dt] = mfma32(vf, pf[sub][t], o[dt]);
                 }
+        if (more) store_tile(buf ^ 1, t0 + KT);
+        __syncthreads();
     }
 
+    // Epilogue: normalise; write out/lse, or the split partial.
+    const long rows_total = (long)a.B * a.Hq * a.M;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (!rv) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float row_lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    const long row_flat = (long)(b * a.Hq + h) * a.M + j;
-    if (a.n_split == 1) {
-        uint16_t *orow = a.out + row_flat * D;
-        for (int dt = 0; dt < DT; ++dt)
-            for (int q4 = 0; q4 < 4; ++q4) {
-                __bf16 v4[4];
-                for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[dt][q4 * 4 + c] * inv);
-                *reinterpret_cast<uint2 *>(orow + dt * 32 + q4 * 8 + hh * 4) =
-                    *reinterpret_cast<const uint2 *>(v4);
-            }
-        if (hh == 0) a.lse[row_flat] = row_lse;
-    } else {
-        const long rows_total = (long)a.B * a.Hq * a.M;
-        float *orow = a.ws_o + ((long)split * rows_total + row_flat) * D;
-        for (int dt = 0; dt < DT; ++dt)
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float4 v;
-                v.x = o[dt][q4 * 4 + 0] * inv;
-                v.y = o[dt][q4 * 4 + 1] * inv;
-                v.z = o[dt][q4 * 4 + 2] * inv;
-                v.w = o[dt][q4 * 4 + 3] * inv;
-                *reinterpret_cast<float4 *>(orow + dt * 32 + q4 * 8 + hh * 4) = v;
-            }
-        if (hh == 0) a.ws_l[(long)split * rows_total + row_flat] = row_lse;
+    if (rv) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float row_lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        const long row_flat = (long)(b * a.Hq + h) * a.M + j;
+        if (a.n_split == 1) {
+            uint16_t *orow = a.out + row_flat * D;
+            for (int dt = 0; dt < DT; ++dt)
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    __bf16 v4[4];
+                    for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[dt][q4 * 4 + c] * inv);
+                    *reinterpret_cast<uint2 *>(orow + dt * 32 + q4 * 8 + hh * 4) =
+                        *reinterpret_cast<const uint2 *>(v4);
+                }
+            if (hh == 0) a.lse[row_flat] = row_lse;
+        } else {
+            float *orow = a.ws_o + ((long)split * rows_total + row_flat) * D;
+            for (int dt = 0; dt < DT; ++dt)
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    float4 v;
+                    v.x = o[dt][q4 * 4 + 0] * inv;
+                    v.y = o[dt][q4 * 4 + 1] * inv;
+                    v.z = o[dt][q4 * 4 + 2] * inv;
+                    v.w = o[dt][q4 * 4 + 3] * inv;
+                    *reinterpret_cast<float4 *>(orow + dt * 32 + q4 * 8 + hh * 4) = v;
+                }
+            if (hh == 0) a.ws_l[(long)split * rows_total + row_flat] = row_lse;
+        }
     }
 }
 
 // Merge the key splits of each row in split order:
 // lse = logsumexp_s lse_s, out = sum_s exp(lse_s - lse) out_s.
+// One thread per 4 consecutive output elements of a row.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
-    constexpr int RPB = 256 / D;        // rows per block
+    constexpr int PER_ROW = D / 4;
+    constexpr int RPB = 256 / PER_ROW;  // rows per block
     const long rows_total = (long)a.B * a.Hq * a.M;
-    const long row = (long)blockIdx.x * RPB + threadIdx.x / D;
-    const int d = threadIdx.x % D;
+    const long row = (long)blockIdx.x * RPB + threadIdx.x / PER_ROW;
+    const int d4 = threadIdx.x % PER_ROW;
     if (row >= rows_total) return;
+    const float *ls = a.ws_l + row;
     float m = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, a.ws_l[s * rows_total + row]);
-    float res = 0.f, L = -INFINITY;
+    for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, ls[s * rows_total]);
+    float4 res = {0.f, 0.f, 0.f, 0.f};
+    float L = -INFINITY;
     if (m != -INFINITY) {
         float sum = 0.f;
-        for (int s = 0; s < a.n_split; ++s) sum += expf(a.ws_l[s * rows_total + row] - m);
+        for (int s = 0; s < a.n_split; ++s) sum += fast_exp2((ls[s * rows_total] - m) * kLog2e);
         L = m + logf(sum);
         for (int s = 0; s < a.n_split; ++s) {
-            float w = expf(a.ws_l[s * rows_total + row] - L);
-            res += w * a.ws_o[(s * rows_total + row) * D + d];
+            const float w = fast_exp2((ls[s * rows_total] - L) * kLog2e);
+            const float4 v = reinterpret_cast<const float4 *>(a.ws_o + (s * rows_total + row) * D)[d4];
+            res.x = fmaf(w, v.x, res.x);
+            res.y = fmaf(w, v.y, res.y);
+            res.z = fmaf(w, v.z, res.z);
+            res.w = fmaf(w, v.w, res.w);
         }
     }
-    __bf16 bv = (__bf16)res;
-    a.out[row * D + d] = *reinterpret_cast<uint16_t *>(&bv);
-    if (d == 0) a.lse[row] = L;
+    __bf16 bv[4] = {(__bf16)res.x, (__bf16)res.y, (__bf16)res.z, (__bf16)res.w};
+    reinterpret_cast<uint2 *>(a.out + row * D)[d4] = *reinterpret_cast<const uint2 *>(bv);
+    if (d4 == 0) a.lse[row] = L;
 }
 
 // ---------------------------------------------------------------------------
 // Pass 2.  Workgroup = (b, kv-head g, row split, 256-key block); wave w owns
-// keys [64w, 64w+64) of the block in registers for the whole pass.  It loops
-// over the G q-heads of g and over 32-row query tiles of its slice of the
-// counted rows, writing one partial column sum per (q-head, row split).
+// keys [64w, 64w+64) of the block in registers for the whole pass.  It walks
+// the (q-head of g, 32-row query tile) pairs of its slice of the counted rows
+// as one sequence, double-buffered in LDS (tile t+1 is loaded while tile t
+// is used), and writes one partial column sum per (q-head, row split).
+// Rows past the slice or with lse = -inf get lse = +inf (weight 0).  The
+// visibility test is only evaluated when the mask can hide a key of the
+// block from a counted row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
@@ -348,9 +406,9 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     constexpr int CH = D / 8;
     constexpr int QLOADS = (kCsRows * CH + 255) / 256;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[kCsRows * QSTR];
-    __shared__ float lse2_s[kCsRows];
-    __shared__ int qcode_s[kCsRows];
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[2][kCsRows * QSTR];
+    __shared__ __attribute__((aligned(16))) float lse2_s[2][kCsRows];
+    __shared__ int qcode_s[2][kCsRows];
     __shared__ int range_s[2];
 
     const int tid = threadIdx.x;
@@ -382,100 +440,152 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
         range_s[tid] = lo;
     }
 
-    // This lane's two keys and their K fragments.
+    // This lane's two keys and their K fragments (zeros past kv_len).
     int key[2], kc[2];
     bf16x8 kf[2][DK];
     const uint16_t *kbase = a.ck + ((long)b * a.Hkv + g) * a.n_cap * D;
+    const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * D * 2);
     for (int ct = 0; ct < 2; ++ct) {
         key[ct] = kb * kCsKeys + wid * 64 + ct * 32 + l32;
         kc[ct] = key_code(a, st, gr, key[ct]);
-        const bool ok = key[ct] < a.kv_len;
         for (int kk = 0; kk < DK; ++kk) {
-            if (ok) kf[ct][kk] = *reinterpret_cast<const bf16x8 *>(kbase + (long)key[ct] * D + kk * 16 + hh * 8);
-            else kf[ct][kk] = bf16x8{};
+            const uint4 v = buffer_load16(krs, (key[ct] * D + kk * 16 + hh * 8) * 2);
+            kf[ct][kk] = *reinterpret_cast<const bf16x8 *>(&v);
         }
     }
+    const bool need_mask = a.kind != 0 && (kb + 1) * kCsKeys > a.P;
     __syncthreads();
     const int j_lo = range_s[0], j_hi = range_s[1];
     const int cnt = max(0, j_hi - j_lo);
     const int per = ((cnt + a.n_rsplit - 1) / a.n_rsplit + kCsRows - 1) / kCsRows * kCsRows;
     const int r0 = min(j_hi, j_lo + rs * per);
     const int r1 = min(j_hi, r0 + per);
+    const int tiles_h = (r1 - r0 + kCsRows - 1) / kCsRows;     // query tiles per q-head
+    const int n_tiles = tiles_h * a.G;
 
-    for (int hl = 0; hl < a.G; ++hl) {
-        const int h = g * a.G + hl;
-        const uint16_t *qhead = a.q + ((long)b * a.Hq + h) * a.M * D;
-        const float *lhead = a.lse + ((long)b * a.Hq + h) * a.M;
-        float acc[2] = {0.f, 0.f};
-        for (int rb = r0; rb < r1; rb += kCsRows) {
-            __syncthreads();
-            for (int u = 0; u < QLOADS; ++u) {
-                int idx = tid + 256 * u;
-                if (idx < kCsRows * CH) {
-                    int rr = idx / CH, c = idx % CH;
-                    uint4 v = {0, 0, 0, 0};
-                    if (rb + rr < r1) v = *reinterpret_cast<const uint4 *>(qhead + (long)(rb + rr) * D + c * 8);
-                    *reinterpret_cast<uint4 *>(&Qs[rr * QSTR + c * 8]) = v;
+    uint4 qreg[QLOADS];
+    float lreg = INFINITY;
+    int creg = INT_MIN;
+    auto load_tile = [&](int t) {
+        const int hl = t / tiles_h, rb = r0 + (t - hl * tiles_h) * kCsRows;
+        const long hrow = ((long)b * a.Hq + g * a.G + hl) * a.M;
+        // rows at or past r1 read as zeros
+        const __amdgpu_buffer_rsrc_t qrs = buffer_view(a.q + hrow * D, r1 * D * 2);
+        for (int u = 0; u < QLOADS; ++u) {
+            const int idx = tid + 256 * u;
+            if (idx < kCsRows * CH) qreg[u] = buffer_load16(qrs, ((rb + idx / CH) * D + (idx % CH) * 8) * 2);
+        }
+        if (tid < kCsRows) {
+            const int jr = rb + tid;
+            lreg = INFINITY;
+            creg = INT_MIN;
+            if (jr < r1) {
+                const float lv = a.lse[hrow + jr];
+                if (lv != -INFINITY) {
+                    lreg = lv * kLog2e;
+                    creg = need_mask ? query_code(a, gr, act[jr]) : 0;
                 }
             }
-            if (tid < kCsRows) {
-                int jr = rb + tid;
-                float l2 = INFINITY;
-                int qc = INT_MIN;
-                if (jr < r1) {
-                    float lv = lhead[jr];
-                    if (lv != -INFINITY) {
-                        l2 = lv * kLog2e;
-                        qc = query_code(a, gr, act[jr]);
-                    }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        for (int u = 0; u < QLOADS; ++u) {
+            const int idx = tid + 256 * u;
+            if (idx < kCsRows * CH) *reinterpret_cast<uint4 *>(&Qs[buf][(idx / CH) * QSTR + (idx % CH) * 8]) = qreg[u];
+        }
+        if (tid < kCsRows) {
+            lse2_s[buf][tid] = lreg;
+            qcode_s[buf][tid] = creg;
+        }
+    };
+
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    float acc[2] = {0.f, 0.f};
+    for (int t = 0; t < n_tiles; ++t) {
+        const int buf = t & 1;
+        const bool more = t + 1 < n_tiles;
+        if (more) load_tile(t + 1);
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        const uint16_t *qr = &Qs[buf][l32 * QSTR + hh * 8];
+        for (int kk = 0; kk < DK; ++kk) {
+            const bf16x8 qa = lds_frag(qr + kk * 16);
+            s0 = mfma32(qa, kf[0][kk], s0);
+            s1 = mfma32(qa, kf[1][kk], s1);
+        }
+        // element i of this lane is query row 8*(i/4) + 4*hh + i%4 of the tile
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 l2 = *reinterpret_cast<const float4 *>(&lse2_s[buf][8 * q4 + 4 * hh]);
+            const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+            if (!need_mask) {
+                for (int e = 0; e < 4; ++e) {
+                    acc[0] += fast_exp2(fmaf(s0[q4 * 4 + e], a.scale_log2, -lv[e]));
+                    acc[1] += fast_exp2(fmaf(s1[q4 * 4 + e], a.scale_log2, -lv[e]));
                 }
-                lse2_s[tid] = l2;
-                qcode_s[tid] = qc;
-            }
-            __syncthreads();
-            f32x16 s0 = f32x16{}, s1 = f32x16{};
-            const uint16_t *qr = &Qs[l32 * QSTR + hh * 8];
-            for (int kk = 0; kk < DK; ++kk) {
-                bf16x8 qa = lds_frag(qr + kk * 16);
-                s0 = mfma32(qa, kf[0][kk], s0);
-                s1 = mfma32(qa, kf[1][kk], s1);
-            }
-            for (int i = 0; i < 16; ++i) {
-                int ri = 8 * (i >> 2) + 4 * hh + (i & 3);
-                float l2 = lse2_s[ri];
-                int qc = qcode_s[ri];
-                float p0 = fast_exp2(s0[i] * a.scale_log2 - l2);
-                float p1 = fast_exp2(s1[i] * a.scale_log2 - l2);
-                if (kc[0] <= qc) acc[0] += p0;
-                if (kc[1] <= qc) acc[1] += p1;
+            } else {
+                for (int e = 0; e < 4; ++e) {
+                    const int qc = qcode_s[buf][8 * q4 + 4 * hh + e];
+                    const float p0 = fast_exp2(fmaf(s0[q4 * 4 + e], a.scale_log2, -lv[e]));
+                    const float p1 = fast_exp2(fmaf(s1[q4 * 4 + e], a.scale_log2, -lv[e]));
+                    acc[0] += kc[0] <= qc ? p0 : 0.f;
+                    acc[1] += kc[1] <= qc ? p1 : 0.f;
+                }
             }
         }
-        for (int ct = 0; ct < 2; ++ct) {
-            float tot = acc[ct] + __shfl_xor(acc[ct], 32);
-            if (hh == 0 && key[ct] < a.kv_len)
-                a.ws_cs[(((long)b * a.Hq + h) * a.n_rsplit + rs) * a.kv_len + key[ct]] = tot;
+        if (more) store_tile(buf ^ 1);
+        if (t % tiles_h == tiles_h - 1) {
+            // last tile of a q-head: write its partial column sums
+            const int h = g * a.G + t / tiles_h;
+            for (int ct = 0; ct < 2; ++ct) {
+                const float tot = acc[ct] + __shfl_xor(acc[ct], 32);
+                if (hh == 0 && key[ct] < a.kv_len)
+                    a.ws_cs[(((long)b * a.Hq + h) * a.n_rsplit + rs) * a.kv_len + key[ct]] = tot;
+                acc[ct] = 0.f;
+            }
         }
+        __syncthreads();
+    }
+    if (n_tiles == 0) {
+        // no counted rows in this slice: zero partials for every q-head
+        for (int hl = 0; hl < a.G; ++hl)
+            for (int ct = 0; ct < 2; ++ct)
+                if (hh == 0 && key[ct] < a.kv_len)
+                    a.ws_cs[(((long)b * a.Hq + g * a.G + hl) * a.n_rsplit + rs) * a.kv_len + key[ct]] = 0.f;
     }
 }
 
-// colsum[b, n] = sum_h sum_rs part[b, h, rs, n] (or per head: sum_rs), fixed order.
+// colsum[b, n] = sum_h sum_rs part[b, h, rs, n] (or per head: sum_rs).
+// Block = 64 columns x 4 slices; slice q sums partials s = q, q+4, ... with
+// four independent accumulators, then the slices are added in slice order:
+// a fixed order, so the result is bitwise reproducible.
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(AttnArgs a)
 {
+    __shared__ float part_s[4][64];
     const int nh = a.per_head ? a.Hq : 1;
     const long total = (long)a.B * nh * a.kv_len;
-    const long t = (long)blockIdx.x * 256 + threadIdx.x;
-    if (t >= total) return;
-    const int n = (int)(t % a.kv_len);
-    const long bh = t / a.kv_len;
-    float sum = 0.f;
-    if (a.per_head) {
-        const float *p = a.ws_cs + bh * a.n_rsplit * a.kv_len + n;
-        for (int s = 0; s < a.n_rsplit; ++s) sum += p[(long)s * a.kv_len];
-    } else {
-        const float *p = a.ws_cs + bh * a.Hq * a.n_rsplit * a.kv_len + n;
-        for (int s = 0; s < a.Hq * a.n_rsplit; ++s) sum += p[(long)s * a.kv_len];
+    const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const long t = (long)blockIdx.x * 64 + c;
+    const int S = a.per_head ? a.n_rsplit : a.Hq * a.n_rsplit;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < total) {
+        const int n = (int)(t % a.kv_len);
+        const long bh = t / a.kv_len;
+        const float *p = a.ws_cs + bh * S * a.kv_len + n;
+        int s = q;
+        for (; s + 12 < S; s += 16) {
+            acc[0] += p[(long)s * a.kv_len];
+            acc[1] += p[(long)(s + 4) * a.kv_len];
+            acc[2] += p[(long)(s + 8) * a.kv_len];
+            acc[3] += p[(long)(s + 12) * a.kv_len];
+        }
+        for (int u = 0; s < S; s += 4, ++u) acc[u] += p[(long)s * a.kv_len];
     }
-    a.colsum[t] = sum;
+    part_s[q][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    __syncthreads();
+    if (q == 0 && t < total) a.colsum[t] = (part_s[0][c] + part_s[1][c]) + (part_s[2][c] + part_s[3][c]);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, long n)
@@ -487,10 +597,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, long n)
 template <int D>
 hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
 {
-    if (a.M > 0 && a.k != nullptr) {
-        long total = (long)a.B * a.Hkv * a.M * (D / 8);
-        kv_scatter_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(a, total);
-    }
+    const long scatter_total = (a.M > 0 && a.k != nullptr) ? (long)a.B * a.Hkv * a.M * (D / 8) : 0;
+    if (scatter_total > 0)
+        kv_scatter_kernel<<<dim3((unsigned)((scatter_total + 255) / 256)), dim3(256), 0, stream>>>(a, scatter_total);
     if (a.M == 0) {
         if (a.colsum) {
             long n = (long)a.B * (a.per_head ? a.Hq : 1) * a.kv_len;
@@ -503,15 +612,15 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
         attn_fwd_kernel<D><<<dim3((unsigned)nwg), dim3(256), 0, stream>>>(a);
     }
     if (a.n_split > 1) {
-        long rows = (long)a.B * a.Hq * a.M;
-        constexpr int RPB = 256 / D;
+        const long rows = (long)a.B * a.Hq * a.M;
+        constexpr int RPB = 256 / (D / 4);
         attn_combine_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(a);
     }
     if (a.colsum) {
         long nwg = (long)a.B * a.Hkv * a.n_rsplit * a.n_kblocks;
         colsum_kernel<D><<<dim3((unsigned)nwg), dim3(256), 0, stream>>>(a);
         long n = (long)a.B * (a.per_head ? a.Hq : 1) * a.kv_len;
-        colsum_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(a);
+        colsum_reduce_kernel<<<dim3((unsigned)((n + 63) / 64)), dim3(256), 0, stream>>>(a);
     }
     return hipGetLastError();
 }
@@ -536,12 +645,13 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap)
     p.n_qtiles = (p.G * M + kAttnRows - 1) / kAttnRows;
     const long base = (long)B * Hkv * p.n_qtiles;
     const int key_tiles = (kv_len + kKeyTile - 1) / kKeyTile;
-    // Split the keys until about two workgroups per CU are resident, keeping
-    // at least four key tiles per split.
+    // Split the keys until there are kAttnWgTarget workgroups, keeping at
+    // least 16 key tiles per split: shorter splits lose more to the split
+    // merge than they gain in parallelism (measured on MI355X).
     int split = 1;
-    if (base > 0 && base < 2L * kNumCU) {
-        split = (int)((2L * kNumCU + base - 1) / base);
-        split = min(split, max(1, key_tiles / 4));
+    if (base > 0 && base < kAttnWgTarget) {
+        split = (int)((kAttnWgTarget + base - 1) / base);
+        split = min(split, max(1, key_tiles / 16));
     }
     int tiles_per = (key_tiles + split - 1) / split;
     p.split_keys = max(1, tiles_per) * kKeyTile;

@@ -16,6 +16,10 @@ constexpr int kNumCU = 256;          // MI355X: 256 CUs in 8 XCDs
 constexpr int kNumXCD = 8;
 constexpr int kAttnRows = 128;       // query rows per attention workgroup (4 waves x 32)
 constexpr int kKeyTile = 64;         // keys per LDS tile in pass 1
+#ifndef DLM_ATTN_WG_TARGET
+#define DLM_ATTN_WG_TARGET 512
+#endif
+constexpr long kAttnWgTarget = DLM_ATTN_WG_TARGET;  // pass-1 workgroups wanted (2 per CU)
 constexpr int kCsKeys = 256;         // keys per column-sum workgroup (4 waves x 64)
 constexpr int kCsRows = 32;          // query rows per column-sum tile
 constexpr int kMaxSlots = 1024;      // GROUP: slots per batch entry

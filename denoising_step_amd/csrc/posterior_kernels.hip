@@ -162,79 +162,155 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
 
 // One workgroup per selection group of rows: merge each row's chunk
 // partials, finish KL / conf / tok / lock, then select within the group.
+//
+// All global loads of the group (lock flags, scores, chunk partials) are
+// issued before anything waits on them: the partials are staged into LDS.
+// For a group of at most 32 rows, eight threads merge one row: thread k
+// takes chunks k, k+8, ... in order, and a fixed three-step butterfly over
+// the eight combines them; larger groups merge one row per thread.
+// The selection uses block-wide reductions, not a serial scan.
+constexpr int kStageBytes = 32768;
+constexpr int kMergeLanes = 8;
+
+__device__ __forceinline__ float block_max(float v, float *red)
+{
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    const int wid = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[wid] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ RowState rs_load(const PostPartial &p)
+{
+    RowState s;
+    s.mx = p.mx; s.sx = p.sx; s.tx = p.tx; s.my = p.my; s.sy = p.sy; s.av = p.av; s.ai = p.ai;
+    return s;
+}
+
 __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
 {
-    __shared__ float key_s[kMaxGroupRows];
+    __shared__ __attribute__((aligned(16))) float key_s[kMaxGroupRows];
     __shared__ float conf_s[kMaxGroupRows];
     __shared__ int tok_s[kMaxGroupRows];
     __shared__ uint8_t elig_s[kMaxGroupRows];
-    __shared__ float thr_s;
-    __shared__ int any_s;
+    __shared__ __attribute__((aligned(16))) PostPartial stage_s[kStageBytes / sizeof(PostPartial)];
+    __shared__ float red_s[4];
 
     const int tid = threadIdx.x;
     const int g0 = blockIdx.x * a.group_rows;
     const int n = min(a.R - g0, a.group_rows);
     const bool by_score = a.mode == 3 || a.mode == 4;
+    constexpr int kStageParts = kStageBytes / (int)sizeof(PostPartial);
+    const int rows_per_round = max(1, min(n, kStageParts / a.n_chunks));
+    // Threads per row in the merge: up to kMergeLanes when the group has
+    // few rows (so one pass covers it), one per row otherwise.
+    const bool wide = a.n_chunks > 1 && n * kMergeLanes <= 256;
+    const int lanes = wide ? kMergeLanes : 1;
 
-    for (int t = tid; t < n; t += 256) {
-        const int r = g0 + t;
-        const bool was_locked = a.locked[r] != 0;
-        float klv = 0.f, cf = 0.f;
-        int tok = -1;
-        if (!was_locked) {
-            const PostPartial *pp = a.part + (long)r * a.n_chunks;
-            RowState s;
-            s.mx = pp[0].mx; s.sx = pp[0].sx; s.tx = pp[0].tx; s.my = pp[0].my; s.sy = pp[0].sy;
-            s.av = pp[0].av; s.ai = pp[0].ai;
-            for (int c = 1; c < a.n_chunks; ++c) {
-                RowState o;
-                o.mx = pp[c].mx; o.sx = pp[c].sx; o.tx = pp[c].tx; o.my = pp[c].my; o.sy = pp[c].sy;
-                o.av = pp[c].av; o.ai = pp[c].ai;
-                rs_merge(s, o);
+    // Issue the lock-flag and score loads together with the first staging
+    // round; nothing waits until the barrier.
+    uint8_t lk[4];
+    float sc[4];
+    for (int k = 0; k < 4; ++k) {
+        const int t = tid + 256 * k;
+        lk[k] = t < n ? a.locked[g0 + t] : 1;
+        sc[k] = (by_score && t < n) ? a.score[g0 + t] : 0.f;
+    }
+    for (int r0 = 0; r0 < n; r0 += rows_per_round) {
+        const int nr = min(rows_per_round, n - r0);
+        // Stage: partials of rows [g0+r0, g0+r0+nr) are contiguous.
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.part + (long)(g0 + r0) * a.n_chunks);
+        uint4 *dst = reinterpret_cast<uint4 *>(stage_s);
+        const int n16 = nr * a.n_chunks * (int)(sizeof(PostPartial) / 16);
+        if (r0 > 0) __syncthreads();
+        for (int i = tid; i < n16; i += 256) dst[i] = src[i];
+        if (r0 == 0) {
+            for (int k = 0; k < 4; ++k) {
+                const int t = tid + 256 * k;
+                if (t < n) {
+                    elig_s[t] = lk[k] == 0 ? 1 : 0;
+                    if (by_score) key_s[t] = sc[k];
+                }
             }
-            // KL = t/sx - (mx + ln sx) + (my + ln sy)
-            klv = s.tx / s.sx - (s.mx - s.my) - (logf(s.sx) - logf(s.sy));
-            cf = 1.f / s.sx;
-            tok = s.ai;
-            a.locked[r] = klv <= a.eps ? 1 : 0;
         }
-        a.kl[r] = klv;
-        a.conf[r] = cf;
-        conf_s[t] = cf;
-        tok_s[t] = tok;
-        elig_s[t] = was_locked ? 0 : 1;
-        key_s[t] = by_score ? a.score[r] : cf;
+        __syncthreads();
+        for (int t0 = 0; t0 < nr; t0 += 256 / lanes) {
+            const int t = t0 + tid / lanes;
+            const int sub = tid % lanes;
+            const bool row_ok = t < nr;
+            const int gt = r0 + t;
+            const bool was_locked = !row_ok || elig_s[gt] == 0;
+            RowState s;
+            rs_init(s);
+            if (!was_locked) {
+                const PostPartial *pp = stage_s + t * a.n_chunks;
+                for (int c = sub; c < a.n_chunks; c += lanes) rs_merge(s, rs_load(pp[c]));
+            }
+            if (wide)
+                for (int m = kMergeLanes / 2; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
+            if (row_ok && sub == 0) {
+                const int r = g0 + gt;
+                float klv = 0.f, cf = 0.f;
+                int tok = -1;
+                if (!was_locked) {
+                    // KL = t/sx - (mx + ln sx) + (my + ln sy)
+                    klv = s.tx / s.sx - (s.mx - s.my) - (logf(s.sx) - logf(s.sy));
+                    cf = 1.f / s.sx;
+                    tok = s.ai;
+                    a.locked[r] = klv <= a.eps ? 1 : 0;
+                }
+                a.kl[r] = klv;
+                a.conf[r] = cf;
+                conf_s[gt] = cf;
+                tok_s[gt] = tok;
+                if (!by_score) key_s[gt] = cf;
+            }
+        }
     }
     if (a.mode == 0) {
         for (int t = tid; t < n; t += 256) a.sel[g0 + t] = -1;
         return;
     }
-    __syncthreads();
-    if (tid == 0) {
-        // Dynamic threshold: the largest score of an eligible non-candidate.
-        float thr = -INFINITY;
-        if (a.mode == 3)
-            for (int t = 0; t < n; ++t)
-                if (elig_s[t] && !(conf_s[t] > a.tau)) thr = fmaxf(thr, key_s[t]);
-        int any = 0;
-        for (int t = 0; t < n; ++t) {
-            if (!elig_s[t]) continue;
-            if (a.mode == 2 && conf_s[t] > a.tau) any = 1;
-            if (a.mode == 3 && conf_s[t] > a.tau && key_s[t] > thr) any = 1;
-        }
-        thr_s = thr;
-        any_s = any;
+    __syncthreads();   // row results visible
+    // Dynamic threshold: the largest score of an eligible non-candidate.
+    float thr = -INFINITY;
+    if (a.mode == 3) {
+        float v = -INFINITY;
+        for (int t = tid; t < n; t += 256)
+            if (elig_s[t] && !(conf_s[t] > a.tau)) v = fmaxf(v, key_s[t]);
+        thr = block_max(v, red_s);
     }
+    int mine = 0;
+    for (int t = tid; t < n; t += 256) {
+        if (!elig_s[t]) continue;
+        if (a.mode == 2 && conf_s[t] > a.tau) mine = 1;
+        if (a.mode == 3 && conf_s[t] > a.tau && key_s[t] > thr) mine = 1;
+    }
+    const int any = __syncthreads_or(mine);
+    // rank(t) = number of eligible rows ordered before t: (key desc, row
+    // asc).  Ineligible rows take key -inf (eligible keys are finite: a
+    // confidence or a column sum), so they never count; the count is
+    // branch-free over float4 reads of the keys.
     __syncthreads();
-    const float thr = thr_s;
-    const int any = any_s;
+    for (int t = tid; t < n; t += 256)
+        if (!elig_s[t]) key_s[t] = -INFINITY;
+    for (int t = n; t < ((n + 3) & ~3); ++t)
+        if (tid == 0) key_s[t] = -INFINITY;
+    __syncthreads();
     for (int t = tid; t < n; t += 256) {
         int out = -1;
         if (elig_s[t]) {
             const float kt = key_s[t];
             int rank = 0;
-            for (int u = 0; u < n; ++u)
-                if (elig_s[u] && (key_s[u] > kt || (key_s[u] == kt && u < t))) ++rank;
+            for (int u = 0; u < n; u += 4) {
+                const float4 k4 = *reinterpret_cast<const float4 *>(&key_s[u]);
+                rank += (k4.x > kt || (k4.x == kt && u + 0 < t)) ? 1 : 0;
+                rank += (k4.y > kt || (k4.y == kt && u + 1 < t)) ? 1 : 0;
+                rank += (k4.z > kt || (k4.z == kt && u + 2 < t)) ? 1 : 0;
+                rank += (k4.w > kt || (k4.w == kt && u + 3 < t)) ? 1 : 0;
+            }
             bool pick = false;
             if (a.mode == 1 || a.mode == 4) pick = rank < a.k;
             else if (a.mode == 2) pick = any ? conf_s[t] > a.tau : rank == 0;
@@ -263,12 +339,13 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream)
 PostPlan plan_post(int R, int V, int mode, int group_rows)
 {
     PostPlan p{};
-    // Enough workgroups for ~8 per CU, chunks of at least 16K elements.
+    // About four streaming workgroups per CU, chunks of at least 4096 elements
+    // (one 16-byte load per array per thread per 1024 elements).
     int chunks = 1;
     if (R > 0) {
-        const long target = 8L * kNumCU;
+        const long target = 4L * kNumCU;
         if (R < target) chunks = (int)((target + R - 1) / R);
-        const int max_chunks = max(1, V / 16384);
+        const int max_chunks = max(1, V / 4096);
         chunks = min(chunks, max_chunks);
     }
     int chunk = (V + chunks - 1) / chunks;

@@ -88,15 +88,16 @@ class DeviceStep:
         dlm_step_attn(self.q, self.k if fresh else None, self.v if fresh else None, self.kv,
                       self.active_idx, self.md, self.out, self.lse, self.colsum, stream)
 
-    def run_posterior(self, stream=None):
+    def run_posterior(self, stream=None, locked=None):
+        """``locked`` replaces the lock-flag buffer for this call (in/out)."""
         p = self.workload.post
-        dlm_posterior(self.logits, self.prev, self.locked, p.eps, self.select, self.sel, self.kl,
-                      self.conf, p.R, p.V, stream)
+        dlm_posterior(self.logits, self.prev, self.locked if locked is None else locked, p.eps,
+                      self.select, self.sel, self.kl, self.conf, p.R, p.V, stream)
 
-    def run(self, stream=None):
+    def run(self, stream=None, locked=None):
         self.run_attn(stream)
         if self.with_posterior:
-            self.run_posterior(stream)
+            self.run_posterior(stream, locked)
 
     def results(self) -> dict:
         torch.cuda.synchronize()

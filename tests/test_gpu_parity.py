@@ -362,3 +362,32 @@ def test_full_long_prefix_sampler():
                           p.logits)
     assert (g["sel"] >= 0).sum() == 16
     _say(f"  excused selections: {exc}")
+
+
+def test_validate_env_rejects_bad_contents(monkeypatch):
+    """DLM_VALIDATE=1 checks device-array contents on a host copy and
+    returns DLM_E_DESC before any launch."""
+    import denoising_step_amd as dlm
+    w = small_mbd("group")
+    ds = _device_step(w, with_posterior=False)
+    monkeypatch.setenv("DLM_VALIDATE", "1")
+    ds.run_attn()                                   # valid contents pass
+    torch.cuda.synchronize()
+    good = ds.active_idx.clone()
+    for mutate in ("duplicate", "past_kv_len", "in_prefix"):
+        bad = good.clone()
+        if mutate == "duplicate":
+            bad[1, 7] = bad[1, 6]
+        elif mutate == "past_kv_len":
+            bad[0, -1] = w.attn.kv_len
+        else:
+            bad[0, 0] = w.attn.prefix_len - 1
+        with pytest.raises(dlm.DlmError) as e:
+            dlm.dlm_step_attn(ds.q, ds.k, ds.v, ds.kv, bad, ds.md, ds.out, ds.lse, ds.colsum)
+        assert e.value.code == dlm.DLM_E_DESC, mutate
+    bad_state = ds.md.slot_state.clone()
+    bad_state[0, 0] = 7
+    md = dlm.MaskDesc(**{**ds.md.__dict__, "slot_state": bad_state})
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_step_attn(ds.q, ds.k, ds.v, ds.kv, good, md, ds.out, ds.lse, ds.colsum)
+    assert e.value.code == dlm.DLM_E_DESC
