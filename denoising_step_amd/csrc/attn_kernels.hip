@@ -245,12 +245,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
                 const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&vreg[u][2]);
                 const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&vreg[u][3]);
                 for (int w = 0; w < 4; ++w) {
-                    // d = 8c + 2w (low halves) and 8c + 2w + 1 (high halves)
+                    // d = 8c + 2w (low halves) and 8c + 2w + 1 (high halves),
+                    // one byte permute per packed pair of keys
                     uint2 ev, od;
-                    ev.x = (w0[w] & 0xFFFFu) | (w1[w] << 16);
-                    ev.y = (w2[w] & 0xFFFFu) | (w3[w] << 16);
-                    od.x = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
-                    od.y = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
+                    ev.x = __builtin_amdgcn_perm(w1[w], w0[w], 0x05040100u);
+                    ev.y = __builtin_amdgcn_perm(w3[w], w2[w], 0x05040100u);
+                    od.x = __builtin_amdgcn_perm(w1[w], w0[w], 0x07060302u);
+                    od.y = __builtin_amdgcn_perm(w3[w], w2[w], 0x07060302u);
                     *reinterpret_cast<uint2 *>(&vt[(c * 8 + 2 * w) * VSTR + kg * 4]) = ev;
                     *reinterpret_cast<uint2 *>(&vt[(c * 8 + 2 * w + 1) * VSTR + kg * 4]) = od;
                 }
