@@ -33,6 +33,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace dlm {
 
 namespace {
@@ -117,32 +119,58 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a, long scatte
 // a CU, so one can run its softmax while the other keeps the matrix cores
 // busy.
 //
-// K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
-// t+1 are issued before tile t is computed and stored to the other buffer
-// afterwards, so one barrier per tile suffices.  The running max is only
-// moved when it grows by more than kRescaleLog2 (log2 units): exp2 arguments
-// stay <= kRescaleLog2, and the O/l rescale is skipped on most tiles.
+// K/V tiles of 64 keys go from global memory straight into LDS (buffer
+// loads with the LDS destination: no registers, no LDS store instructions),
+// double-buffered: the loads of tile t+1 are issued before tile t is
+// computed, and one barrier per tile publishes them.  Rows at or past
+// kv_len and rows of DUMMY slots are given an out-of-range offset and read
+// as zeros.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so every 8 lanes of a read hit
+// distinct banks):
+//   K: row r holds key sigma(r) (bits 2 and 3 of r swapped within each
+//      32-key sub-tile), chunk c of that key at position c ^ (r mod 8).
+//      The S^T accumulator then holds, in element i of half-wave h, key
+//      16*(i/8) + 8*h + i%8: exactly the operand-B order of V^T P^T.
+//   V: row r holds key r, chunk c at position c ^ (2r mod 8).  Operand A of
+//      V^T P^T (8 consecutive keys of one column per lane) is two
+//      ds_read_b64_tr_b16: within each 16-lane group, source lane s points
+//      at key 4e0 + s/4, column d0 + 4*(s%4), and lane j receives keys
+//      4e0..4e0+3 of column d0 + j.
+// The running max is only moved when it grows by more than kRescaleLog2
+// (log2 units): exp2 arguments stay <= kRescaleLog2, and the O/l rescale is
+// skipped on most tiles.
 //
 // With a key split, each workgroup writes its normalised partial (out, lse)
 // to the workspace and a separate kernel merges the splits in split order.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.f;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
 {
     constexpr int KT = kKeyTile;
-    constexpr int KSTR = D + 8;          // bf16 per LDS K row (16 B pad: conflict-free reads)
-    constexpr int VSTR = KT + 8;         // bf16 per LDS Vt row
+    constexpr int CH = D / 8;            // 16-byte chunks per K/V row
+    constexpr int ROWB = D * 2;          // bytes per K/V row
+    constexpr int NLD = KT * ROWB / (256 * 16);  // 16-byte direct loads per thread per tile, per tensor
+    constexpr int SWZ = CH < 8 ? CH : 8; // swizzle period (chunks)
     constexpr int DK = D / 16;           // MFMA k-steps over the head dim
     constexpr int DT = D / 32;           // 32-row tiles of O^T
-    constexpr int CH = D / 8;            // 16-byte chunks per K/V row
-    constexpr int KLOADS = KT * CH / 256;        // K chunks per thread per tile
-    constexpr int VGROUPS = (KT / 4) * CH;       // (4-key group, chunk) pairs per tile
-    constexpr int VLOADS = (VGROUPS + 255) / 256;
+    constexpr int OOB = 0x7ffffff0;      // an offset past any buffer view
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[KT * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KT * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[KT * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KT * D];
     __shared__ int kcode_s[2][KT];
     __shared__ int scode_s[kMaxSlots];
 
@@ -161,6 +189,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     const int32_t *gr = a.kind == 2 ? a.slot_group + (long)b * a.n_slots : nullptr;
     if (a.kind == 2) {
         for (int s = tid; s < a.n_slots; s += 256) scode_s[s] = st[s] == 0 ? INT_MAX : gr[s];
+    }
+    // Zero the tiles once, so no LDS byte a tile does not overwrite can
+    // ever be a non-finite value times a zero weight.
+    for (int i = tid; i < KT * D / 8; i += 256) {
+        reinterpret_cast<uint4 *>(Ks0)[i] = uint4{0, 0, 0, 0};
+        reinterpret_cast<uint4 *>(Ks1)[i] = uint4{0, 0, 0, 0};
+        reinterpret_cast<uint4 *>(Vs0)[i] = uint4{0, 0, 0, 0};
+        reinterpret_cast<uint4 *>(Vs1)[i] = uint4{0, 0, 0, 0};
     }
 
     // This lane's query.
@@ -186,104 +222,83 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     const int k1 = min(a.kv_len, k0 + a.split_keys);
     const uint16_t *kbase = a.ck + (long)bg * a.n_cap * D;
     const uint16_t *vbase = a.cv + (long)bg * a.n_cap * D;
+    const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * ROWB);
+    const __amdgpu_buffer_rsrc_t vrs = buffer_view(vbase, a.kv_len * ROWB);
     const float c2 = a.scale_log2;
 
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 o[DT];
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-
-    uint4 kreg[KLOADS], vreg[VLOADS][4];
-
-    // K/V rows at or past kv_len read as zeros (buffer range check).  Rows
-    // in a DUMMY slot of a GROUP mask are zeroed after loading: they may hold
-    // anything, their weight is 0, and their values must not poison 0 * V.
-    const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = buffer_view(vbase, a.kv_len * D * 2);
+    // Direct-load geometry of this thread: load u writes 16 bytes at LDS
+    // byte (wid*NLD + u)*1024 + lane*16 of a tile, i.e. row lr, position lp.
+    int ld_row[NLD], k_goff[NLD], v_goff[NLD];
+    for (int u = 0; u < NLD; ++u) {
+        const int byte = (wid * NLD + u) * 1024 + lane * 16;
+        const int lr = byte / ROWB, lp = (byte % ROWB) / 16;
+        ld_row[u] = lr;
+        const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));   // sigma(lr)
+        k_goff[u] = (kkey * D + ((lp ^ (lr & (SWZ - 1))) * 8)) * 2;
+        v_goff[u] = (lr * D + ((lp ^ ((2 * lr) & (SWZ - 1))) * 8)) * 2;
+    }
     auto dummy_row = [&](int n) -> bool {
         if (n < a.P || n >= a.kv_len) return false;
         const int s = (n - a.P) / a.bs;
         return s >= a.n_slots || scode_s[s] == INT_MAX;
     };
-    auto load_tile = [&](int t0) {
-        for (int u = 0; u < KLOADS; ++u) {
-            const int idx = tid + 256 * u;
-            kreg[u] = buffer_load16(krs, ((t0 + idx / CH) * D + (idx % CH) * 8) * 2);
-        }
-        for (int u = 0; u < VLOADS; ++u) {
-            const int idx = tid + 256 * u;
-            if (idx < VGROUPS) {
-                const int kg = idx % (KT / 4), c = idx / (KT / 4);
-                for (int e = 0; e < 4; ++e) vreg[u][e] = buffer_load16(vrs, ((t0 + kg * 4 + e) * D + c * 8) * 2);
+    auto issue_tile = [&](int t0, int buf) {
+        uint16_t *ks = buf ? Ks1 : Ks0;
+        uint16_t *vs = buf ? Vs1 : Vs0;
+        const bool group_tail = a.kind == 2 && t0 + KT > a.P;
+        for (int u = 0; u < NLD; ++u) {
+            int ko = k_goff[u] + t0 * ROWB, vo = v_goff[u] + t0 * ROWB;
+            if (group_tail) {
+                const int lr = ld_row[u];
+                const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));
+                if (dummy_row(t0 + kkey)) ko = OOB;
+                if (dummy_row(t0 + lr)) vo = OOB;
             }
-        }
-        if (a.kind == 2 && t0 + KT > a.P) {
-            for (int u = 0; u < KLOADS; ++u)
-                if (dummy_row(t0 + (tid + 256 * u) / CH)) kreg[u] = uint4{0, 0, 0, 0};
-            for (int u = 0; u < VLOADS; ++u) {
-                const int idx = tid + 256 * u;
-                if (idx < VGROUPS)
-                    for (int e = 0; e < 4; ++e)
-                        if (dummy_row(t0 + (idx % (KT / 4)) * 4 + e)) vreg[u][e] = uint4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int buf, int t0) {
-        uint16_t *ks = Ks[buf];
-        uint16_t *vt = Vt[buf];
-        for (int u = 0; u < KLOADS; ++u) {
-            const int idx = tid + 256 * u;
-            const int n = idx / CH, c = idx % CH;
-            const int nr = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);   // sigma(n)
-            *reinterpret_cast<uint4 *>(&ks[nr * KSTR + c * 8]) = kreg[u];
-        }
-        for (int u = 0; u < VLOADS; ++u) {
-            const int idx = tid + 256 * u;
-            if (idx < VGROUPS) {
-                const int kg = idx % (KT / 4), c = idx / (KT / 4);
-                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&vreg[u][0]);
-                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&vreg[u][1]);
-                const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&vreg[u][2]);
-                const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&vreg[u][3]);
-                for (int w = 0; w < 4; ++w) {
-                    // d = 8c + 2w (low halves) and 8c + 2w + 1 (high halves),
-                    // one byte permute per packed pair of keys
-                    uint2 ev, od;
-                    ev.x = __builtin_amdgcn_perm(w1[w], w0[w], 0x05040100u);
-                    ev.y = __builtin_amdgcn_perm(w3[w], w2[w], 0x05040100u);
-                    od.x = __builtin_amdgcn_perm(w1[w], w0[w], 0x07060302u);
-                    od.y = __builtin_amdgcn_perm(w3[w], w2[w], 0x07060302u);
-                    *reinterpret_cast<uint2 *>(&vt[(c * 8 + 2 * w) * VSTR + kg * 4]) = ev;
-                    *reinterpret_cast<uint2 *>(&vt[(c * 8 + 2 * w + 1) * VSTR + kg * 4]) = od;
-                }
-            }
+            lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
+            lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
         }
         if (tid < KT) kcode_s[buf][tid] = key_code(a, st, gr, t0 + tid);
     };
 
-    __syncthreads();   // slot codes visible
-    if (k0 < k1) {
-        load_tile(k0);
-        store_tile(0, k0);
+    // Loop-invariant LDS read offsets (elements) of this lane.
+    int k_rd[DK];                                          // K chunk 2kk+hh of row l32
+    for (int kk = 0; kk < DK; ++kk) k_rd[kk] = l32 * D + (((2 * kk + hh) ^ (l32 & (SWZ - 1))) * 8);
+    const int s16 = lane & 15, g16 = lane >> 4;
+    int v_rd[DT];                                          // column tile dt, first row of the group
+    for (int dt = 0; dt < DT; ++dt) {
+        const int chunk = 4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+        const int row = 8 * (g16 >> 1) + (s16 >> 2);      // row mod 4 = s16 / 4
+        v_rd[dt] = row * D + ((chunk ^ ((2 * row) & (SWZ - 1))) * 8) + (s16 & 1) * 4;
     }
-    __syncthreads();
-    int buf = 0;
-    for (int t0 = k0; t0 < k1; t0 += KT, buf ^= 1) {
-        const bool more = t0 + KT < k1;
-        if (more) load_tile(t0 + KT);
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o[DT];
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+
+    // One tile: compute on LDS buffer BUF while tile t0 + KT streams into
+    // the other one.  BUF is a compile-time constant, so the compiler sees
+    // that the reads and the in-flight LDS loads touch different arrays and
+    // does not wait for the loads before reading.
+    auto tile_step = [&](auto bufc, int t0) {
+        constexpr int BUF = decltype(bufc)::value;
+        if (t0 + KT < k1) issue_tile(t0 + KT, BUF ^ 1);
+        const uint16_t *ks = BUF ? Ks1 : Ks0;
+        const uint16_t *vs = BUF ? Vs1 : Vs0;
 
         // S^T for two 32-key sub-tiles.
         f32x16 s[2];
         for (int sub = 0; sub < 2; ++sub) {
             s[sub] = f32x16{};
-            const uint16_t *kr = &Ks[buf][(sub * 32 + l32) * KSTR + hh * 8];
-            for (int kk = 0; kk < DK; ++kk) s[sub] = mfma32(lds_frag(kr + kk * 16), qf[kk], s[sub]);
+            for (int kk = 0; kk < DK; ++kk) s[sub] = mfma32(lds_frag(ks + sub * 32 * D + k_rd[kk]), qf[kk], s[sub]);
         }
         const bool all_vis = (a.kind == 0 && t0 + KT <= a.kv_len) || (t0 + KT <= a.P);
         if (!all_vis) {
             for (int sub = 0; sub < 2; ++sub)
                 for (int i = 0; i < 16; ++i) {
                     const int key = sub * 32 + 16 * (i >> 3) + 8 * hh + (i & 7);
-                    if (kcode_s[buf][key] > qcode) s[sub][i] = -INFINITY;
+                    if (kcode_s[BUF][key] > qcode) s[sub][i] = -INFINITY;
                 }
         }
         // Raw-score max (scale > 0, so the max commutes with scaling).
@@ -314,11 +329,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
         for (int sub = 0; sub < 2; ++sub)
             for (int t = 0; t < 2; ++t)
                 for (int dt = 0; dt < DT; ++dt) {
-                    const bf16x8 vf = lds_frag(&Vt[buf][(dt * 32 + l32) * VSTR + sub * 32 + t * 16 + hh * 8]);
-                    o[dt] = mfma32(vf, pf[sub][t], o[dt]);
+                    // keys 32sub + 16t + 8hh + (0..3 | 4..7) of column 32dt + l32
+                    const uint16_t *vp = vs + (32 * sub + 16 * t) * D + v_rd[dt];
+                    const s16x4 lo = lds_read_tr(vp);
+                    const s16x4 hi = lds_read_tr(vp + 4 * D);
+                    const s16x4 v8[2] = {lo, hi};
+                    o[dt] = mfma32(*reinterpret_cast<const bf16x8 *>(v8), pf[sub][t], o[dt]);
                 }
-        if (more) store_tile(buf ^ 1, t0 + KT);
+        __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile landed
         __syncthreads();
+    };
+
+    __syncthreads();   // slot codes and zeroed tiles visible
+    if (k0 < k1) issue_tile(k0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t0 = k0; t0 < k1; t0 += 2 * KT) {
+        tile_step(std::integral_constant<int, 0>{}, t0);
+        if (t0 + KT < k1) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
     }
 
     // Epilogue: normalise; write out/lse, or the split partial.
