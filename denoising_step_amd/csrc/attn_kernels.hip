@@ -93,23 +93,30 @@ __device__ __forceinline__ int query_code(const AttnArgs &a, const int32_t *gr, 
 }
 
 // ---------------------------------------------------------------------------
-// Scatter: cache[b, g, active_idx[b, j], :] = fresh[b, g, j, :], 16 B per
-// thread.
+// Scatter: cache[b, g, active_idx[b, j], :] = fresh[b, g, j, :].
+// Workgroup w covers row block w % per_bg of (b, kv-head) w / per_bg (both
+// wave-uniform, so scalar), and a thread moves one 16-byte chunk of K and of
+// V: the per-lane index math is shifts.  The fresh tensors are read once
+// (non-temporal).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a, long scatter_total)
+template <int D>
+__global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 {
-    const int ch = a.D / 8;
-    const long t = (long)blockIdx.x * 256 + threadIdx.x;
-    if (t >= scatter_total) return;
-    int c = (int)(t % ch);
-    long row = t / ch;                  // (b*Hkv + g)*M + j
-    int j = (int)(row % a.M);
-    long bg = row / a.M;
-    int b = (int)(bg / a.Hkv);
-    int pos = a.active_idx[(long)b * a.M + j];
-    long dst = (bg * a.n_cap + pos) * ch + c;
-    reinterpret_cast<uint4 *>(a.ck)[dst] = reinterpret_cast<const uint4 *>(a.k)[t];
-    reinterpret_cast<uint4 *>(a.cv)[dst] = reinterpret_cast<const uint4 *>(a.v)[t];
+    constexpr int CH = D / 8;                     // chunks per row (power of 2)
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const int per_bg = (a.M * CH + 255) / 256;
+    const int bg = blockIdx.x / per_bg;
+    const int b = bg / a.Hkv;
+    const int t = (blockIdx.x - bg * per_bg) * 256 + threadIdx.x;
+    const int j = t / CH, c = t % CH;
+    if (j >= a.M) return;
+    const int pos = a.active_idx[(long)b * a.M + j];
+    const long src = ((long)bg * a.M + j) * CH + c;
+    const long dst = ((long)bg * a.n_cap + pos) * CH + c;
+    const v4u kv = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(a.k) + src);
+    const v4u vv = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(a.v) + src);
+    reinterpret_cast<v4u *>(a.ck)[dst] = kv;
+    reinterpret_cast<v4u *>(a.cv)[dst] = vv;
 }
 
 // ---------------------------------------------------------------------------
@@ -126,13 +133,13 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a, long scatte
 // kv_len and rows of DUMMY slots are given an out-of-range offset and read
 // as zeros.
 //
-// LDS layouts (16-byte chunks, XOR-swizzled so every 8 lanes of a read hit
-// distinct banks):
+// LDS layouts (16-byte chunks, XOR-swizzled so that every lane group the
+// LDS serves in one cycle hits distinct banks):
 //   K: row r holds key sigma(r) (bits 2 and 3 of r swapped within each
-//      32-key sub-tile), chunk c of that key at position c ^ (r mod 8).
+//      32-key sub-tile), chunk c of that key at position c ^ k_swz(r).
 //      The S^T accumulator then holds, in element i of half-wave h, key
 //      16*(i/8) + 8*h + i%8: exactly the operand-B order of V^T P^T.
-//   V: row r holds key r, chunk c at position c ^ (2r mod 8).  Operand A of
+//   V: row r holds key r, chunk c at position c ^ v_swz(r).  Operand A of
 //      V^T P^T (8 consecutive keys of one column per lane) is two
 //      ds_read_b64_tr_b16: within each 16-lane group, source lane s points
 //      at key 4e0 + s/4, column d0 + 4*(s%4), and lane j receives keys
@@ -155,6 +162,27 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
+// XOR swizzles of the pass-1 LDS tiles (16-byte chunk index of row r).
+// gfx950 serves a 16-byte LDS read 16 lanes per cycle and an 8-byte one 32
+// lanes per cycle over 64 banks (8 and 16 lanes over 32 banks on older
+// parts); these keep every such lane group on distinct banks under both
+// models.  K: the 16 rows a lane group reads at one chunk land on 16
+// distinct chunk slots.  V: the 4 rows x 4 chunks of a transposed read land
+// on 16 distinct slots.  Both depend on r mod 16 only.
+template <int D>
+__device__ __forceinline__ int k_swz(int r)
+{
+    constexpr int SH = D == 128 ? 4 : D == 64 ? 3 : 2;   // log2(chunks per row)
+    const int r4 = r & 15;
+    return (r4 ^ (r4 >> SH)) & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r)
+{
+    const int i = r & 3, par = (i ^ (i >> 1)) & 1;
+    return D == 128 ? (4 * i) ^ (2 * par) : D == 64 ? 2 * i : 2 * par;
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
 {
@@ -162,7 +190,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     constexpr int CH = D / 8;            // 16-byte chunks per K/V row
     constexpr int ROWB = D * 2;          // bytes per K/V row
     constexpr int NLD = KT * ROWB / (256 * 16);  // 16-byte direct loads per thread per tile, per tensor
-    constexpr int SWZ = CH < 8 ? CH : 8; // swizzle period (chunks)
     constexpr int DK = D / 16;           // MFMA k-steps over the head dim
     constexpr int DT = D / 32;           // 32-row tiles of O^T
     constexpr int OOB = 0x7ffffff0;      // an offset past any buffer view
@@ -234,8 +261,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
         const int lr = byte / ROWB, lp = (byte % ROWB) / 16;
         ld_row[u] = lr;
         const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));   // sigma(lr)
-        k_goff[u] = (kkey * D + ((lp ^ (lr & (SWZ - 1))) * 8)) * 2;
-        v_goff[u] = (lr * D + ((lp ^ ((2 * lr) & (SWZ - 1))) * 8)) * 2;
+        k_goff[u] = (kkey * D + ((lp ^ k_swz<D>(lr)) * 8)) * 2;
+        v_goff[u] = (lr * D + ((lp ^ v_swz<D>(lr)) * 8)) * 2;
     }
     auto dummy_row = [&](int n) -> bool {
         if (n < a.P || n >= a.kv_len) return false;
@@ -264,13 +291,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
 
     // Loop-invariant LDS read offsets (elements) of this lane.
     int k_rd[DK];                                          // K chunk 2kk+hh of row l32
-    for (int kk = 0; kk < DK; ++kk) k_rd[kk] = l32 * D + (((2 * kk + hh) ^ (l32 & (SWZ - 1))) * 8);
+    for (int kk = 0; kk < DK; ++kk) k_rd[kk] = l32 * D + (((2 * kk + hh) ^ k_swz<D>(l32)) * 8);
     const int s16 = lane & 15, g16 = lane >> 4;
     int v_rd[DT];                                          // column tile dt, first row of the group
     for (int dt = 0; dt < DT; ++dt) {
         const int chunk = 4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1);
         const int row = 8 * (g16 >> 1) + (s16 >> 2);      // row mod 4 = s16 / 4
-        v_rd[dt] = row * D + ((chunk ^ ((2 * row) & (SWZ - 1))) * 8) + (s16 & 1) * 4;
+        v_rd[dt] = row * D + ((chunk ^ v_swz<D>(row)) * 8) + (s16 & 1) * 4;
     }
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -587,34 +614,50 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
 }
 
 // colsum[b, n] = sum_h sum_rs part[b, h, rs, n] (or per head: sum_rs).
-// Block = 64 columns x 4 slices; slice q sums partials s = q, q+4, ... with
-// four independent accumulators, then the slices are added in slice order:
-// a fixed order, so the result is bitwise reproducible.
+// Workgroup = (256 / SL) consecutive columns of one (b, h-or-all) x SL
+// slices; slice q sums partials s = q, q + SL, ... with eight independent
+// accumulators (eight loads in flight per thread), and the slices are then
+// added in a fixed tree order: the result depends on the shape only, so it
+// is bitwise reproducible.  SL = 16 when there are many partials per column
+// (all heads), 1 when there are few (per head).
+template <int SL>
 __global__ __launch_bounds__(256) void colsum_reduce_kernel(AttnArgs a)
 {
-    __shared__ float part_s[4][64];
-    const int nh = a.per_head ? a.Hq : 1;
-    const long total = (long)a.B * nh * a.kv_len;
-    const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const long t = (long)blockIdx.x * 64 + c;
+    constexpr int CW = 256 / SL;             // columns per workgroup
+    constexpr int U = 8;
+    __shared__ float part_s[SL][CW];
+    const int nblk = (a.kv_len + CW - 1) / CW;
+    const int bh = blockIdx.x / nblk;        // (b, h) or b
+    const int c = threadIdx.x % CW, q = threadIdx.x / CW;
+    const int n = (blockIdx.x - bh * nblk) * CW + c;
     const int S = a.per_head ? a.n_rsplit : a.Hq * a.n_rsplit;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < total) {
-        const int n = (int)(t % a.kv_len);
-        const long bh = t / a.kv_len;
-        const float *p = a.ws_cs + bh * S * a.kv_len + n;
-        int s = q;
-        for (; s + 12 < S; s += 16) {
-            acc[0] += p[(long)s * a.kv_len];
-            acc[1] += p[(long)(s + 4) * a.kv_len];
-            acc[2] += p[(long)(s + 8) * a.kv_len];
-            acc[3] += p[(long)(s + 12) * a.kv_len];
+    float acc[U];
+    for (int u = 0; u < U; ++u) acc[u] = 0.f;
+    if (n < a.kv_len) {
+        const float *p = a.ws_cs + (long)bh * S * a.kv_len + n;
+        for (int s0 = q; s0 < S; s0 += U * SL) {
+            float v[U];
+            for (int u = 0; u < U; ++u) {
+                const int s = s0 + u * SL;
+                v[u] = s < S ? p[(long)s * a.kv_len] : 0.f;
+            }
+            for (int u = 0; u < U; ++u) acc[u] += v[u];
         }
-        for (int u = 0; s < S; s += 4, ++u) acc[u] += p[(long)s * a.kv_len];
     }
-    part_s[q][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float mine = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    if (SL == 1) {
+        if (n < a.kv_len) a.colsum[(long)bh * a.kv_len + n] = mine;
+        return;
+    }
+    part_s[q][c] = mine;
     __syncthreads();
-    if (q == 0 && t < total) a.colsum[t] = (part_s[0][c] + part_s[1][c]) + (part_s[2][c] + part_s[3][c]);
+    if (q == 0 && n < a.kv_len) {
+        float t[SL];
+        for (int k = 0; k < SL; ++k) t[k] = part_s[k][c];
+        for (int w = SL / 2; w >= 1; w >>= 1)
+            for (int k = 0; k < w; ++k) t[k] = t[k] + t[k + w];
+        a.colsum[(long)bh * a.kv_len + n] = t[0];
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, long n)
@@ -626,9 +669,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, long n)
 template <int D>
 hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
 {
-    const long scatter_total = (a.M > 0 && a.k != nullptr) ? (long)a.B * a.Hkv * a.M * (D / 8) : 0;
-    if (scatter_total > 0)
-        kv_scatter_kernel<<<dim3((unsigned)((scatter_total + 255) / 256)), dim3(256), 0, stream>>>(a, scatter_total);
+    if (a.M > 0 && a.k != nullptr) {
+        const long per_bg = ((long)a.M * (D / 8) + 255) / 256;
+        kv_scatter_kernel<D><<<dim3((unsigned)(per_bg * a.B * a.Hkv)), dim3(256), 0, stream>>>(a);
+    }
     if (a.M == 0) {
         if (a.colsum) {
             long n = (long)a.B * (a.per_head ? a.Hq : 1) * a.kv_len;
@@ -648,8 +692,12 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
     if (a.colsum) {
         long nwg = (long)a.B * a.Hkv * a.n_rsplit * a.n_kblocks;
         colsum_kernel<D><<<dim3((unsigned)nwg), dim3(256), 0, stream>>>(a);
-        long n = (long)a.B * (a.per_head ? a.Hq : 1) * a.kv_len;
-        colsum_reduce_kernel<<<dim3((unsigned)((n + 63) / 64)), dim3(256), 0, stream>>>(a);
+        const long nbh = (long)a.B * (a.per_head ? a.Hq : 1);
+        const int S = a.per_head ? a.n_rsplit : a.Hq * a.n_rsplit;
+        if (S >= 32)
+            colsum_reduce_kernel<16><<<dim3((unsigned)(nbh * ((a.kv_len + 15) / 16))), dim3(256), 0, stream>>>(a);
+        else
+            colsum_reduce_kernel<1><<<dim3((unsigned)(nbh * ((a.kv_len + 255) / 256))), dim3(256), 0, stream>>>(a);
     }
     return hipGetLastError();
 }

@@ -93,6 +93,31 @@ __device__ __forceinline__ void rs_fold(RowState &s, const float (&x)[N], const 
     s.mx = mx; s.my = my; s.sx = sx; s.tx = tx; s.sy = sy;
 }
 
+// As rs_fold, over the elements with ok[i] set (at least one may be unset;
+// all may be).  A state that stays empty keeps mx = -inf without NaNs.
+template <int N>
+__device__ __forceinline__ void rs_fold_masked(RowState &s, const float (&x)[N], const float (&y)[N],
+                                               const int (&idx)[N], const bool (&ok)[N])
+{
+    float bx = -INFINITY, by = -INFINITY;
+    for (int i = 0; i < N; ++i)
+        if (ok[i]) { bx = fmaxf(bx, x[i]); by = fmaxf(by, y[i]); }
+    const float mx = fmaxf(s.mx, bx), my = fmaxf(s.my, by);
+    const float cx = s.mx == mx ? 1.f : fast_exp2((s.mx - mx) * kLog2e);
+    const float cy = s.my == my ? 1.f : fast_exp2((s.my - my) * kLog2e);
+    float sx = s.sx * cx, tx = s.tx * cx, sy = s.sy * cy;
+    const float mxl = mx * kLog2e, myl = my * kLog2e;
+    for (int i = 0; i < N; ++i) {
+        if (!ok[i]) continue;
+        float ex = fast_exp2(fmaf(x[i], kLog2e, -mxl));
+        sx += ex;
+        tx = fmaf(ex, x[i] - y[i], tx);
+        sy += fast_exp2(fmaf(y[i], kLog2e, -myl));
+        if (x[i] > s.av) { s.av = x[i]; s.ai = idx[i]; }
+    }
+    s.mx = mx; s.my = my; s.sx = sx; s.tx = tx; s.sy = sy;
+}
+
 template <bool VEC4>
 __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs a)
 {
@@ -108,33 +133,42 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
     RowState s;
     rs_init(s);
     if (VEC4) {
-        // e0 and e1 are multiples of 4; 4 float4 per array per thread per step.
+        // e0 and e1 are multiples of 4; 4 float4 per array per thread per
+        // step.  A partial last step issues all of its loads together too
+        // (chunks are whole steps except at the end of a row).
         constexpr int U = 4;
         const int step = kPostThreads * 4 * U;
-        int e = e0;
-        for (; e + step <= e1; e += step) {
+        for (int e = e0; e < e1; e += step) {
             v4f xv[U], yv[U];
+            const bool full = e + step <= e1;
             for (int u = 0; u < U; ++u) {
-                int off = e + (u * kPostThreads + tid) * 4;
-                xv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(x + off));
-                yv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(y + off));
+                const int off = e + (u * kPostThreads + tid) * 4;
+                if (full || off < e1) {
+                    xv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(x + off));
+                    yv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(y + off));
+                } else {
+                    xv[u] = v4f{0.f, 0.f, 0.f, 0.f};
+                    yv[u] = v4f{0.f, 0.f, 0.f, 0.f};
+                }
             }
             float xs[4 * U], ys[4 * U];
             int is[4 * U];
             for (int u = 0; u < U; ++u) {
-                int off = e + (u * kPostThreads + tid) * 4;
+                const int off = e + (u * kPostThreads + tid) * 4;
                 xs[4 * u + 0] = xv[u].x; xs[4 * u + 1] = xv[u].y; xs[4 * u + 2] = xv[u].z; xs[4 * u + 3] = xv[u].w;
                 ys[4 * u + 0] = yv[u].x; ys[4 * u + 1] = yv[u].y; ys[4 * u + 2] = yv[u].z; ys[4 * u + 3] = yv[u].w;
                 is[4 * u + 0] = off; is[4 * u + 1] = off + 1; is[4 * u + 2] = off + 2; is[4 * u + 3] = off + 3;
             }
-            rs_fold(s, xs, ys, is);
-        }
-        for (int off = e + tid * 4; off < e1; off += kPostThreads * 4) {
-            v4f xv = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(x + off));
-            v4f yv = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(y + off));
-            float xs[4] = {xv.x, xv.y, xv.z, xv.w}, ys[4] = {yv.x, yv.y, yv.z, yv.w};
-            int is[4] = {off, off + 1, off + 2, off + 3};
-            rs_fold(s, xs, ys, is);
+            if (full) {
+                rs_fold(s, xs, ys, is);
+            } else {
+                bool ok[4 * U];
+                for (int u = 0; u < U; ++u) {
+                    const bool in = e + (u * kPostThreads + tid) * 4 < e1;   // e1 is a multiple of 4
+                    ok[4 * u + 0] = in; ok[4 * u + 1] = in; ok[4 * u + 2] = in; ok[4 * u + 3] = in;
+                }
+                rs_fold_masked(s, xs, ys, is, ok);
+            }
         }
     } else {
         for (int off = e0 + tid; off < e1; off += kPostThreads) {
@@ -213,6 +247,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     // round; nothing waits until the barrier.
     uint8_t lk[4];
     float sc[4];
+#pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int t = tid + 256 * k;
         lk[k] = t < n ? a.locked[g0 + t] : 1;
@@ -221,12 +256,27 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     for (int r0 = 0; r0 < n; r0 += rows_per_round) {
         const int nr = min(rows_per_round, n - r0);
         // Stage: partials of rows [g0+r0, g0+r0+nr) are contiguous.
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.part + (long)(g0 + r0) * a.n_chunks);
-        uint4 *dst = reinterpret_cast<uint4 *>(stage_s);
+        typedef unsigned v4u __attribute__((ext_vector_type(4)));
+        const v4u *src = reinterpret_cast<const v4u *>(a.part + (long)(g0 + r0) * a.n_chunks);
+        v4u *dst = reinterpret_cast<v4u *>(stage_s);
         const int n16 = nr * a.n_chunks * (int)(sizeof(PostPartial) / 16);
         if (r0 > 0) __syncthreads();
-        for (int i = tid; i < n16; i += 256) dst[i] = src[i];
+        // up to eight 16-byte loads in flight per thread (the stage is 2048)
+        for (int i0 = 0; i0 < n16; i0 += 256 * 8) {
+            v4u v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 256 + tid;
+                v[u] = i < n16 ? src[i] : v4u{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 256 + tid;
+                if (i < n16) dst[i] = v[u];
+            }
+        }
         if (r0 == 0) {
+#pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int t = tid + 256 * k;
                 if (t < n) {
@@ -339,17 +389,20 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream)
 PostPlan plan_post(int R, int V, int mode, int group_rows)
 {
     PostPlan p{};
-    // About four streaming workgroups per CU, chunks of at least 4096 elements
-    // (one 16-byte load per array per thread per 1024 elements).
+    // About four streaming workgroups per CU, chunks of at least one
+    // streaming step (4096 elements).
     int chunks = 1;
     if (R > 0) {
         const long target = 4L * kNumCU;
         if (R < target) chunks = (int)((target + R - 1) / R);
-        const int max_chunks = max(1, V / 4096);
+        const int max_chunks = max(1, (V + kPostThreads * kPostVec - 1) / (kPostThreads * kPostVec));
         chunks = min(chunks, max_chunks);
     }
     int chunk = (V + chunks - 1) / chunks;
-    chunk = (chunk + 3) / 4 * 4;
+    // A split row gets chunks of whole streaming steps (4 float4 per array
+    // per thread), so a chunk is one round of loads per step.
+    constexpr int kStep = kPostThreads * kPostVec;
+    chunk = chunks > 1 ? (chunk + kStep - 1) / kStep * kStep : (chunk + 3) / 4 * 4;
     p.chunk = max(4, chunk);
     p.n_chunks = max(1, (V + p.chunk - 1) / p.chunk);
     p.group_rows = mode == 0 ? 256 : group_rows;
