@@ -120,13 +120,17 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1.  Workgroup = 4 waves = 128 packed query rows of one (b, kv-head):
-// packed row r = (q-head within the GQA group) * M + j, so the G q-heads that
-// share a kv-head share every K/V tile staged in LDS.  Two workgroups share
-// a CU, so one can run its softmax while the other keeps the matrix cores
-// busy.
+// Pass 1.  Workgroup = 8 waves = 128 packed query rows of one (b, kv-head)
+// x 2 key groups: packed row r = (q-head within the GQA group) * M + j, so
+// the G q-heads that share a kv-head share every K/V tile staged in LDS.
+// Waves w and w + 4 own the same 32 rows; in each 128-key tile, key group
+// 0 (waves 0-3) takes keys 0-63 and key group 1 (waves 4-7) keys 64-127.
+// That puts two waves on every SIMD even when the rows alone give one wave
+// per SIMD, so one wave's softmax can run beside the other's MFMAs.  At the
+// end group 1 hands its (max, sum, O) to group 0 through LDS, which merges
+// them and writes the rows.
 //
-// K/V tiles of 64 keys go from global memory straight into LDS (buffer
+// K/V tiles of 128 keys go from global memory straight into LDS (buffer
 // loads with the LDS destination: no registers, no LDS store instructions),
 // double-buffered: the loads of tile t+1 are issued before tile t is
 // computed, and one barrier per tile publishes them.  Rows at or past
@@ -183,13 +187,21 @@ __device__ __forceinline__ int v_swz(int r)
     return D == 128 ? (4 * i) ^ (2 * par) : D == 64 ? 2 * i : 2 * par;
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
+// Max over the two half-waves (lanes l and l ^ 32 hold the same query):
+// v_permlane32_swap hands each half the other's values without LDS.
+__device__ __forceinline__ float half_swap_max(float v)
 {
-    constexpr int KT = kKeyTile;
-    constexpr int CH = D / 8;            // 16-byte chunks per K/V row
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int D, int NG>
+__global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
+{
+    constexpr int KT = 64 * NG;          // keys per LDS tile; key group kg takes [64kg, 64kg + 64)
+    constexpr int NT = 256 * NG;         // threads
     constexpr int ROWB = D * 2;          // bytes per K/V row
-    constexpr int NLD = KT * ROWB / (256 * 16);  // 16-byte direct loads per thread per tile, per tensor
+    constexpr int NLD = KT * ROWB / (NT * 16);   // 16-byte direct loads per thread per tile, per tensor
     constexpr int DK = D / 16;           // MFMA k-steps over the head dim
     constexpr int DT = D / 32;           // 32-row tiles of O^T
     constexpr int OOB = 0x7ffffff0;      // an offset past any buffer view
@@ -200,10 +212,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KT * D];
     __shared__ int kcode_s[2][KT];
     __shared__ int scode_s[kMaxSlots];
+    __shared__ float ml_s[NG == 2 ? 2 * 4 * 64 : 1];   // key group 1's running max and sum
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
+    const int kg = NG == 2 ? wid >> 2 : 0;   // key group
+    const int wq = wid & 3;                  // query wave
+    const int kofs = 64 * kg;                // this group's first key in a tile
 
     int L = xcd_remap(blockIdx.x, gridDim.x);
     const int qt = L % a.n_qtiles;
@@ -215,11 +231,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     const uint8_t *st = a.kind == 2 ? a.slot_state + (long)b * a.n_slots : nullptr;
     const int32_t *gr = a.kind == 2 ? a.slot_group + (long)b * a.n_slots : nullptr;
     if (a.kind == 2) {
-        for (int s = tid; s < a.n_slots; s += 256) scode_s[s] = st[s] == 0 ? INT_MAX : gr[s];
+        for (int s = tid; s < a.n_slots; s += NT) scode_s[s] = st[s] == 0 ? INT_MAX : gr[s];
     }
     // Zero the tiles once, so no LDS byte a tile does not overwrite can
     // ever be a non-finite value times a zero weight.
-    for (int i = tid; i < KT * D / 8; i += 256) {
+    for (int i = tid; i < KT * D / 8; i += NT) {
         reinterpret_cast<uint4 *>(Ks0)[i] = uint4{0, 0, 0, 0};
         reinterpret_cast<uint4 *>(Ks1)[i] = uint4{0, 0, 0, 0};
         reinterpret_cast<uint4 *>(Vs0)[i] = uint4{0, 0, 0, 0};
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
 
     // This lane's query.
     const int rows_bg = a.G * a.M;
-    const int r = qt * kAttnRows + wid * 32 + l32;
+    const int r = qt * kAttnRows + wq * 32 + l32;
     const bool rv = r < rows_bg;
     const int hl = rv ? r / a.M : 0;
     const int j = rv ? r - hl * a.M : 0;
@@ -304,65 +320,110 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
     f32x16 o[DT];
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
+    // O^T += V^T P^T over one 32-key sub-tile at vt: two transposed reads
+    // give keys 16t + 8hh + (0..7) of column 32dt + l32 (operand A).
+    auto pv_mfma = [&](const uint16_t *vt, int t, int dt, const bf16x8 &p) {
+        const uint16_t *vp = vt + 16 * t * D + v_rd[dt];
+        const s16x4 lo = lds_read_tr(vp);
+        const s16x4 hi = lds_read_tr(vp + 4 * D);
+        const s16x4 v8[2] = {lo, hi};
+        o[dt] = mfma32(*reinterpret_cast<const bf16x8 *>(v8), p, o[dt]);
+    };
+
     // One tile: compute on LDS buffer BUF while tile t0 + KT streams into
     // the other one.  BUF is a compile-time constant, so the compiler sees
     // that the reads and the in-flight LDS loads touch different arrays and
-    // does not wait for the loads before reading.
+    // does not wait for the loads before reading.  This wave's 64 keys are
+    // two 32-key sub-tiles: after the shared max, the PV products of
+    // sub-tile 0 are interleaved with the exponentials of sub-tile 1, so the
+    // matrix core and the vector ALU work at the same time.
     auto tile_step = [&](auto bufc, int t0) {
         constexpr int BUF = decltype(bufc)::value;
         if (t0 + KT < k1) issue_tile(t0 + KT, BUF ^ 1);
-        const uint16_t *ks = BUF ? Ks1 : Ks0;
-        const uint16_t *vs = BUF ? Vs1 : Vs0;
+        const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
+        const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
 
-        // S^T for two 32-key sub-tiles.
-        f32x16 s[2];
-        for (int sub = 0; sub < 2; ++sub) {
-            s[sub] = f32x16{};
-            for (int kk = 0; kk < DK; ++kk) s[sub] = mfma32(lds_frag(ks + sub * 32 * D + k_rd[kk]), qf[kk], s[sub]);
+        // S^T of both sub-tiles, the two MFMA chains interleaved and the K
+        // fragments read two k-steps ahead of their MFMAs.
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        {
+            bf16x8 r0[2], r1[2];
+            for (int kk = 0; kk < 2 && kk < DK; ++kk) {
+                r0[kk] = lds_frag(ks + k_rd[kk]);
+                r1[kk] = lds_frag(ks + 32 * D + k_rd[kk]);
+            }
+            for (int kk = 0; kk < DK; ++kk) {
+                const bf16x8 a0 = r0[kk & 1], a1 = r1[kk & 1];
+                if (kk + 2 < DK) {
+                    r0[kk & 1] = lds_frag(ks + k_rd[kk + 2]);
+                    r1[kk & 1] = lds_frag(ks + 32 * D + k_rd[kk + 2]);
+                }
+                s0 = mfma32(a0, qf[kk], s0);
+                s1 = mfma32(a1, qf[kk], s1);
+            }
+            // keep that order: 4 reads, then (2 MFMAs, 2 reads) ..., 4 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, DK >= 2 ? 4 : 2, 0);
+            for (int kk = 0; kk + 2 < DK; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, DK >= 2 ? 4 : 2, 0);
         }
         const bool all_vis = (a.kind == 0 && t0 + KT <= a.kv_len) || (t0 + KT <= a.P);
         if (!all_vis) {
-            for (int sub = 0; sub < 2; ++sub)
-                for (int i = 0; i < 16; ++i) {
-                    const int key = sub * 32 + 16 * (i >> 3) + 8 * hh + (i & 7);
-                    if (kcode_s[BUF][key] > qcode) s[sub][i] = -INFINITY;
-                }
+            const int *kc = kcode_s[BUF] + kofs;
+            for (int i = 0; i < 16; ++i) {
+                const int key = 16 * (i >> 3) + 8 * hh + (i & 7);
+                if (kc[key] > qcode) s0[i] = -INFINITY;
+                if (kc[32 + key] > qcode) s1[i] = -INFINITY;
+            }
         }
-        // Raw-score max (scale > 0, so the max commutes with scaling).
-        float tmax = s[0][0];
-        for (int sub = 0; sub < 2; ++sub)
-            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[sub][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c2;
-        const bool grow = tmax > m_run + kRescaleLog2;
+        // Exponent arguments u = s * scale * log2(e) - m_use (the running
+        // max, 0 before the first visible key), and their max: taking the
+        // max of FMA results rather than raw MFMA outputs spares the NaN
+        // canonicalisation of every input.
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float u0[16], u1[16];
+        for (int i = 0; i < 16; ++i) {
+            u0[i] = fmaf(s0[i], c2, -m_use);
+            u1[i] = fmaf(s1[i], c2, -m_use);
+        }
+        float tmax = fmaxf(u0[0], u1[0]);
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(u0[i], u1[i]));
+        tmax = half_swap_max(tmax);
+        // Move the running max only when the tile's max exceeds it by more
+        // than kRescaleLog2, or when it is the lane's first visible key.
+        const bool grow = m_run == -INFINITY ? tmax != -INFINITY : tmax > kRescaleLog2;
         if (__any(grow)) {
-            // lanes that do not grow keep their max (alpha = 1; this also
-            // keeps a lane that has seen no key at m = -inf without NaN)
-            const float alpha = grow ? fast_exp2(m_run - tmax) : 1.f;   // 0 when m_run = -inf
+            const float d = grow ? tmax : 0.f;                 // new max - m_use
+            const float alpha = grow ? fast_exp2(m_run - (m_use + d)) : 1.f;   // 0 when m_run = -inf
             for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
             l_run *= alpha;
-            if (grow) m_run = tmax;
+            if (grow) m_run = m_use + d;
+            for (int i = 0; i < 16; ++i) {
+                u0[i] -= d;
+                u1[i] -= d;
+            }
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float psum = 0.f;
-        bf16x8 pf[2][2];
-        for (int sub = 0; sub < 2; ++sub)
-            for (int t = 0; t < 2; ++t)
-                for (int e = 0; e < 8; ++e) {
-                    const float p = fast_exp2(fmaf(s[sub][t * 8 + e], c2, -m_use));
-                    psum += p;
-                    pf[sub][t][e] = (__bf16)p;
-                }
+        bf16x8 p0[2], p1[2];
+        for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(u0[i]);
+            psum += p;
+            p0[i >> 3][i & 7] = (__bf16)p;
+        }
+        constexpr int PER = 16 / (2 * DT);   // exps of sub-tile 1 per PV product
+        for (int q = 0; q < 2 * DT; ++q) {
+            pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
+            for (int e = 0; e < PER; ++e) {
+                const int i = q * PER + e;
+                const float p = fast_exp2(u1[i]);
+                psum += p;
+                p1[i >> 3][i & 7] = (__bf16)p;
+            }
+        }
         l_run += psum;
-        for (int sub = 0; sub < 2; ++sub)
-            for (int t = 0; t < 2; ++t)
-                for (int dt = 0; dt < DT; ++dt) {
-                    // keys 32sub + 16t + 8hh + (0..3 | 4..7) of column 32dt + l32
-                    const uint16_t *vp = vs + (32 * sub + 16 * t) * D + v_rd[dt];
-                    const s16x4 lo = lds_read_tr(vp);
-                    const s16x4 hi = lds_read_tr(vp + 4 * D);
-                    const s16x4 v8[2] = {lo, hi};
-                    o[dt] = mfma32(*reinterpret_cast<const bf16x8 *>(v8), pf[sub][t], o[dt]);
-                }
+        for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
         __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile landed
         __syncthreads();
     };
@@ -376,6 +437,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a)
         if (t0 + KT < k1) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
     }
 
+    if (NG == 2) {
+        // Key group 1 hands its state to group 0 through LDS (the last tile
+        // step ended with a barrier and issued no loads, so the tiles are
+        // free): wave 4 + w writes O in the accumulator layout,
+        // lane-contiguous.
+        constexpr int OW = DT * 16 * 64;                    // floats of O per wave
+        float *ox = reinterpret_cast<float *>(wq < 2 ? Ks0 : Ks1) + (wq & 1) * OW;
+        if (kg == 1) {
+            for (int dt = 0; dt < DT; ++dt)
+                for (int i = 0; i < 16; ++i) ox[(dt * 16 + i) * 64 + lane] = o[dt][i];
+            ml_s[(0 * 4 + wq) * 64 + lane] = m_run;
+            ml_s[(1 * 4 + wq) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (kg == 1) return;
+        const float m1 = ml_s[(0 * 4 + wq) * 64 + lane], l1 = ml_s[(1 * 4 + wq) * 64 + lane];
+        const float m = fmaxf(m_run, m1);
+        // a side whose max is the merged one (also both -inf) keeps scale 1
+        const float a0 = m_run == m ? 1.f : fast_exp2(m_run - m);
+        const float a1 = m1 == m ? 1.f : fast_exp2(m1 - m);
+        for (int dt = 0; dt < DT; ++dt)
+            for (int i = 0; i < 16; ++i) o[dt][i] = fmaf(o[dt][i], a0, ox[(dt * 16 + i) * 64 + lane] * a1);
+        l_run = fmaf(l_run, a0, l1 * a1);
+        m_run = m;
+    }
     // Epilogue: normalise; write out/lse, or the split partial.
     const long rows_total = (long)a.B * a.Hq * a.M;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -682,7 +768,10 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
     }
     {
         long nwg = (long)a.B * a.Hkv * a.n_split * a.n_qtiles;
-        attn_fwd_kernel<D><<<dim3((unsigned)nwg), dim3(256), 0, stream>>>(a);
+        if (a.n_kgroups == 2)
+            attn_fwd_kernel<D, 2><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
+        else
+            attn_fwd_kernel<D, 1><<<dim3((unsigned)nwg), dim3(256), 0, stream>>>(a);
     }
     if (a.n_split > 1) {
         const long rows = (long)a.B * a.Hq * a.M;
@@ -721,17 +810,23 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap)
     p.kv_len = kv_len; p.n_cap = n_cap;
     p.n_qtiles = (p.G * M + kAttnRows - 1) / kAttnRows;
     const long base = (long)B * Hkv * p.n_qtiles;
-    const int key_tiles = (kv_len + kKeyTile - 1) / kKeyTile;
-    // Split the keys until there are kAttnWgTarget workgroups, keeping at
-    // least 16 key tiles per split: shorter splits lose more to the split
-    // merge than they gain in parallelism (measured on MI355X).
+    // Enough query tiles for two 4-wave workgroups per CU: one key group,
+    // and the two workgroups on a CU keep their own barriers (one can run
+    // its softmax while the other runs MFMAs).  Fewer: two key groups per
+    // workgroup (8 waves), and split the keys until there are
+    // kAttnWgTarget workgroups, keeping at least 1024 keys per split:
+    // shorter splits lose more to the split merge than they gain in
+    // parallelism (measured on MI355X).
+    p.n_kgroups = base >= 2L * kNumCU ? 1 : 2;
+    const int tile = 64 * p.n_kgroups;
+    const int key_tiles = (kv_len + tile - 1) / tile;
     int split = 1;
-    if (base > 0 && base < kAttnWgTarget) {
+    if (p.n_kgroups == 2 && base > 0 && base < kAttnWgTarget) {
         split = (int)((kAttnWgTarget + base - 1) / base);
-        split = min(split, max(1, key_tiles / 16));
+        split = min(split, max(1, key_tiles / (1024 / tile)));
     }
     int tiles_per = (key_tiles + split - 1) / split;
-    p.split_keys = max(1, tiles_per) * kKeyTile;
+    p.split_keys = max(1, tiles_per) * tile;
     p.n_split = max(1, (kv_len + p.split_keys - 1) / p.split_keys);
     p.n_kblocks = (kv_len + kCsKeys - 1) / kCsKeys;
     const long cs_base = (long)B * Hkv * p.n_kblocks;

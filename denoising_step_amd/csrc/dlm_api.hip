@@ -183,7 +183,7 @@ int dlm_step_attn(const void *q, const void *k, const void *v, const dlm_kv_cach
     a.cs_lo = md->cs_lo; a.cs_hi = md->cs_hi; a.per_head = md->colsum_per_head;
     const float scale = md->scale > 0.f ? md->scale : 1.f / sqrtf((float)kc->D);
     a.scale_log2 = scale * 1.4426950408889634f;
-    a.n_qtiles = p.n_qtiles; a.n_split = p.n_split; a.split_keys = p.split_keys;
+    a.n_qtiles = p.n_qtiles; a.n_kgroups = p.n_kgroups; a.n_split = p.n_split; a.split_keys = p.split_keys;
     a.n_kblocks = p.n_kblocks; a.n_rsplit = p.n_rsplit;
 
     hipError_t e = dlm::launch_step_attn(a, stream);

@@ -14,12 +14,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kNumCU = 256;          // MI355X: 256 CUs in 8 XCDs
 constexpr int kNumXCD = 8;
-constexpr int kAttnRows = 128;       // query rows per attention workgroup (4 waves x 32)
-constexpr int kKeyTile = 64;         // keys per LDS tile in pass 1
+constexpr int kAttnRows = 128;       // query rows per pass-1 workgroup (4 query waves x 32)
 #ifndef DLM_ATTN_WG_TARGET
-#define DLM_ATTN_WG_TARGET 512
+#define DLM_ATTN_WG_TARGET 256
 #endif
-constexpr long kAttnWgTarget = DLM_ATTN_WG_TARGET;  // pass-1 workgroups wanted (2 per CU)
+constexpr long kAttnWgTarget = DLM_ATTN_WG_TARGET;  // 8-wave pass-1 workgroups wanted (1 per CU)
 constexpr int kCsKeys = 256;         // keys per column-sum workgroup (4 waves x 64)
 constexpr int kCsRows = 32;          // query rows per column-sum tile
 constexpr int kMaxSlots = 1024;      // GROUP: slots per batch entry
@@ -31,8 +30,9 @@ constexpr int kPostVec = 4 * 4;      // floats per thread per streaming step (4 
 struct AttnPlan {
     int B, Hq, Hkv, G, D, M, kv_len, n_cap;
     int n_qtiles;       // query tiles of kAttnRows packed rows per (b, kv-head)
+    int n_kgroups;      // key groups per pass-1 workgroup (1: 4 waves, 2: 8 waves)
     int n_split;        // key splits of pass 1
-    int split_keys;     // keys per split (multiple of kKeyTile)
+    int split_keys;     // keys per split (multiple of the 64 * n_kgroups key tile)
     int n_kblocks;      // column-sum key blocks of kCsKeys
     int n_rsplit;       // column-sum row splits
     size_t ws_split_o;  // bytes of split partial outputs (fp32)
@@ -74,7 +74,7 @@ struct AttnArgs {
     int B, Hq, Hkv, G, D, M, n_cap, kv_len, P, bs, n_slots, kind;
     int cs_lo, cs_hi, per_head;
     float scale_log2;               // softmax scale * log2(e)
-    int n_qtiles, n_split, split_keys, n_kblocks, n_rsplit;
+    int n_qtiles, n_kgroups, n_split, split_keys, n_kblocks, n_rsplit;
 };
 
 struct PostArgs {
