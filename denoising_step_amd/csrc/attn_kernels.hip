@@ -32,6 +32,7 @@
 
 #include <limits.h>
 #include <math.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -94,29 +95,60 @@ __device__ __forceinline__ int query_code(const AttnArgs &a, const int32_t *gr, 
 
 // ---------------------------------------------------------------------------
 // Scatter: cache[b, g, active_idx[b, j], :] = fresh[b, g, j, :].
-// Workgroup w covers row block w % per_bg of (b, kv-head) w / per_bg (both
-// wave-uniform, so scalar), and a thread moves one 16-byte chunk of K and of
-// V: the per-lane index math is shifts.  The fresh tensors are read once
+// The copy is cut into row blocks of 256 16-byte chunks, each inside one
+// (b, kv-head): block r is (b, kv-head) r / per_bg, rows (r % per_bg) * 256 /
+// (D/8) onward (wave-uniform, so scalar).  Each workgroup walks blocks
+// blockIdx.x, blockIdx.x + gridDim.x, ... U at a time: a thread issues the
+// loads of U chunks of K and V, then their stores, so the stores of one
+// round overlap the loads of the next.  The fresh tensors are read once
 // (non-temporal).
 // ---------------------------------------------------------------------------
+#ifndef DLM_SCATTER_UNROLL
+#define DLM_SCATTER_UNROLL 2
+#endif
+#ifndef DLM_SCATTER_WGS
+#define DLM_SCATTER_WGS 1024
+#endif
+constexpr int kScatterUnroll = DLM_SCATTER_UNROLL;
+constexpr int kScatterWgs = DLM_SCATTER_WGS;
+
 template <int D>
 __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 {
     constexpr int CH = D / 8;                     // chunks per row (power of 2)
+    constexpr int U = kScatterUnroll;
     typedef unsigned v4u __attribute__((ext_vector_type(4)));
     const int per_bg = (a.M * CH + 255) / 256;
-    const int bg = blockIdx.x / per_bg;
-    const int b = bg / a.Hkv;
-    const int t = (blockIdx.x - bg * per_bg) * 256 + threadIdx.x;
-    const int j = t / CH, c = t % CH;
-    if (j >= a.M) return;
-    const int pos = a.active_idx[(long)b * a.M + j];
-    const long src = ((long)bg * a.M + j) * CH + c;
-    const long dst = ((long)bg * a.n_cap + pos) * CH + c;
-    const v4u kv = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(a.k) + src);
-    const v4u vv = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(a.v) + src);
-    reinterpret_cast<v4u *>(a.ck)[dst] = kv;
-    reinterpret_cast<v4u *>(a.cv)[dst] = vv;
+    const int nblk = per_bg * a.B * a.Hkv;
+    for (int r0 = blockIdx.x; r0 < nblk; r0 += U * gridDim.x) {
+        v4u kv[U], vv[U];
+        long dst[U];
+        bool ok[U];
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + u * gridDim.x;
+            const int bg = r / per_bg;
+            const int t = (r - bg * per_bg) * 256 + threadIdx.x;
+            const int j = t / CH, c = t % CH;
+            ok[u] = r < nblk && j < a.M;
+            dst[u] = 0;
+            kv[u] = v4u{0u, 0u, 0u, 0u};
+            vv[u] = v4u{0u, 0u, 0u, 0u};
+            if (ok[u]) {
+                const int b = bg / a.Hkv;
+                const long src = ((long)bg * a.M + j) * CH + c;
+                kv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(a.k) + src);
+                vv[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(a.v) + src);
+                const int pos = a.active_idx[(long)b * a.M + j];
+                dst[u] = ((long)bg * a.n_cap + pos) * CH + c;
+            }
+        }
+        for (int u = 0; u < U; ++u) {
+            if (ok[u]) {
+                reinterpret_cast<v4u *>(a.ck)[dst[u]] = kv[u];
+                reinterpret_cast<v4u *>(a.cv)[dst[u]] = vv[u];
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -756,8 +788,9 @@ template <int D>
 hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
 {
     if (a.M > 0 && a.k != nullptr) {
-        const long per_bg = ((long)a.M * (D / 8) + 255) / 256;
-        kv_scatter_kernel<D><<<dim3((unsigned)(per_bg * a.B * a.Hkv)), dim3(256), 0, stream>>>(a);
+        const long nblk = ((long)a.M * (D / 8) + 255) / 256 * a.B * a.Hkv;
+        const long grid = nblk < kScatterWgs ? nblk : kScatterWgs;
+        kv_scatter_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
     }
     if (a.M == 0) {
         if (a.colsum) {
@@ -818,6 +851,12 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap)
     // shorter splits lose more to the split merge than they gain in
     // parallelism (measured on MI355X).
     p.n_kgroups = base >= 2L * kNumCU ? 1 : 2;
+    // DLM_ATTN_KGROUPS=1 or 2 forces the workgroup shape (tests and tuning;
+    // the workspace query must see the same setting as the call).
+    if (const char *e = getenv("DLM_ATTN_KGROUPS")) {
+        if (e[0] == '1' && e[1] == 0) p.n_kgroups = 1;
+        if (e[0] == '2' && e[1] == 0) p.n_kgroups = 2;
+    }
     const int tile = 64 * p.n_kgroups;
     const int key_tiles = (kv_len + tile - 1) / tile;
     int split = 1;

@@ -29,6 +29,11 @@
  *    break the stated rules give undefined results.
  *  - Calls on one stream are ordered; calls on different streams that share
  *    a workspace or an output race.
+ *  - DLM_ATTN_KGROUPS=1 or 2 in the environment forces the shape of the
+ *    pass-1 workgroups (one key group of 4 waves, or two of 4); by default
+ *    it follows from the shapes.  It changes the workspace size, so
+ *    dlm_step_attn_workspace_bytes and dlm_step_attn must see the same
+ *    setting.  Results agree to rounding either way.
  */
 #ifndef DLM_STEP_H
 #define DLM_STEP_H

@@ -152,6 +152,23 @@ def test_small_long_prefix_key_splits():
     full_check(small_long())
 
 
+@pytest.mark.parametrize("kgroups", ["1", "2"])
+@pytest.mark.parametrize("case", ["mbd_dummy", "surelock_d64_gqa", "surelock_d32_gqa", "long_splits",
+                                  "llada_spread"])
+def test_both_pass1_workgroup_shapes(kgroups, case, monkeypatch):
+    """Pass 1 has two workgroup shapes (one key group of 4 waves with 64-key
+    tiles, two key groups of 4 waves with 128-key tiles merged through LDS);
+    the plan picks one by problem size.  Force each on the same cases."""
+    monkeypatch.setenv("DLM_ATTN_KGROUPS", kgroups)
+    w = {"mbd_dummy": lambda: small_mbd("dummy"),
+         "surelock_d64_gqa": lambda: small_surelock(D=64, Hq=4, Hkv=2),
+         "surelock_d32_gqa": lambda: small_surelock(D=32, Hq=6, Hkv=3),
+         "long_splits": lambda: small_long(seed=2),
+         "llada_spread": lambda: small_llada(spread=True, seed=3)}[case]()
+    _say(f"DLM_ATTN_KGROUPS={kgroups}")
+    full_check(w)
+
+
 def test_deterministic():
     w = small_long(seed=1)
     ds = _device_step(w)
