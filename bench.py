@@ -29,15 +29,19 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MALL_BYTES = 256 << 20
 
 
-def visible_pairs(a) -> int:
-    """Sum over active rows and q-heads of the number of visible keys."""
+def visible_pairs(a, counted_only=False) -> int:
+    """Sum over active rows (only those feeding the column sums when
+    counted_only) and q-heads of the number of visible keys."""
     import numpy as np
-    if a.kind == 0:
-        return a.B * a.Hq * a.M * a.kv_len
-    tot = 0
     n = np.arange(a.kv_len)
+    tot = 0
     for b in range(a.B):
         pos = a.active_idx[b]
+        if counted_only:
+            pos = pos[(pos >= a.cs_lo) & (pos < a.cs_hi)]
+        if a.kind == 0:
+            tot += len(pos) * a.kv_len * a.Hq
+            continue
         if a.kind == 1:
             kb = np.where(n < a.prefix_len, -1, (n - a.prefix_len) // a.block_size)
             qb = (pos - a.prefix_len) // a.block_size
@@ -102,18 +106,26 @@ def copy_probe(n_bytes: int = 256 << 20, reps: int = 5):
     print(json.dumps({"copy_probe_bytes": n_bytes, "reps": reps}), flush=True)
 
 
-def time_loop(fn, n_sets, steps, warmup):
+def time_loop(fn, n_sets, steps, warmup, per_step=False):
+    """ms per call over `steps` timed calls after `warmup` untimed ones,
+    bracketed by synchronisations; with per_step, also every call's own
+    duration (an event between consecutive calls)."""
     import torch
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
+    ev[0].record()
     for i in range(steps):
         fn(i % n_sets)
-    e.record()
+        if per_step:
+            ev[i + 1].record()
+    ev[-1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps        # ms per call
+    mean = ev[0].elapsed_time(ev[-1]) / steps        # ms per call
+    if not per_step:
+        return mean
+    return mean, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
 def cpu_baseline(w, budget_heads=None):
@@ -201,7 +213,7 @@ def main():
     # One fresh copy of the entry lock flags per call, made before timing
     # (the flags are in/out; every timed step must see the same entry state).
     n_calls = args.steps + args.warmup
-    lock_bufs = [sets[i % n_sets].locked0.clone() for i in range(3 * n_calls)]
+    lock_bufs = [sets[i % n_sets].locked0.clone() for i in range(4 * n_calls)]
     calls = [0]
 
     def fresh_lock():
@@ -212,6 +224,9 @@ def main():
         sets[i].run(stream, locked=fresh_lock())
 
     ms_step = time_loop(step, n_sets, args.steps, args.warmup)
+    # the spread of single steps, from a separate loop: an event after every
+    # step adds a small gap, so the figure above comes from a loop without them
+    _, step_ms = time_loop(step, n_sets, args.steps, 0, per_step=True)
 
     # pass 1 alone: no fresh K/V (already in the cache), no column sums
     def pass1(i):
@@ -219,6 +234,13 @@ def main():
         dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, None, stream)
 
     ms_pass1 = time_loop(pass1, n_sets, args.steps, args.warmup)
+
+    # both attention passes (no fresh K/V): the attention MFMA figure
+    def passes12(i):
+        ds = sets[i]
+        dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, ds.colsum, stream)
+
+    ms_p12 = time_loop(passes12, n_sets, args.steps, args.warmup)
 
     def posterior(i):
         sets[i].run_posterior(stream, locked=fresh_lock())
@@ -228,6 +250,9 @@ def main():
     pairs = visible_pairs(a)
     alg_flops = 4.0 * a.D * pairs                       # QK^T and PV, 2 flops per MAC
     achieved_tflops = alg_flops / (ms_pass1 * 1e-3) / 1e12
+    cs_flops = 2.0 * a.D * visible_pairs(a, counted_only=True)   # pass 2 recomputes QK^T
+    p12_tflops = (alg_flops + cs_flops) / (ms_p12 * 1e-3) / 1e12
+    q = np.percentile(np.array(step_ms), [10, 50, 90])
     unlocked = int((p.locked == 0).sum())
     post_bytes = 8.0 * unlocked * p.V
     post_gbs = post_bytes / (ms_post * 1e-3) / 1e9
@@ -254,6 +279,10 @@ def main():
                      "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": stored_traffic(args.config),
                      "per_launch_flops": alg_flops, "avg_launch_us": ms_pass1 * 1e3},
+        "step_ms_p10_p50_p90": [float(x) for x in q],
+        "attention_passes_1_2": {"achieved": p12_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": p12_tflops / PEAK_BF16_TFLOPS, "flops": alg_flops + cs_flops,
+                                 "avg_call_us": ms_p12 * 1e3},
         "posterior_roofline": {"bound": "hbm", "achieved": post_gbs, "peak": PEAK_HBM_GBS,
                                "unit": "GB/s", "frac": post_gbs / PEAK_HBM_GBS,
                                "per_launch_bytes": post_bytes, "avg_launch_us": ms_post * 1e3},

@@ -266,8 +266,12 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
         for (int s = tid; s < a.n_slots; s += NT) scode_s[s] = st[s] == 0 ? INT_MAX : gr[s];
     }
     // Zero the tiles once, so no LDS byte a tile does not overwrite can
-    // ever be a non-finite value times a zero weight.
-    for (int i = tid; i < KT * D / 8; i += NT) {
+    // ever be a non-finite value times a zero weight.  Only a ragged last
+    // tile (rows past kv_len) or DUMMY rows (GROUP) take the out-of-range
+    // path; split boundaries are whole tiles, so otherwise every row of
+    // every tile is loaded.
+    const bool ragged = a.kv_len % KT != 0 || a.kind == 2;
+    for (int i = tid; ragged && i < KT * D / 8; i += NT) {
         reinterpret_cast<uint4 *>(Ks0)[i] = uint4{0, 0, 0, 0};
         reinterpret_cast<uint4 *>(Ks1)[i] = uint4{0, 0, 0, 0};
         reinterpret_cast<uint4 *>(Vs0)[i] = uint4{0, 0, 0, 0};
@@ -603,15 +607,27 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
 
     // Counted rows: active rows whose position lies in [cs_lo, cs_hi);
     // active_idx is ascending, so they are the index range [j_lo, j_hi).
-    if (tid < 2) {
-        int target = tid == 0 ? a.cs_lo : a.cs_hi;
-        int lo = 0, hi = a.M;
-        while (lo < hi) {
-            int mid = (lo + hi) >> 1;
-            if (act[mid] < target) lo = mid + 1;
-            else hi = mid;
+    // Waves 0 and 1 find j_lo and j_hi with a 64-way search: each round
+    // probes 64 evenly spaced entries of the remaining range at once, so
+    // M <= 4096 takes two rounds of loads instead of log2(M) dependent ones.
+    if (wid < 2) {
+        const int target = wid == 0 ? a.cs_lo : a.cs_hi;
+        int lo = 0, len = a.M;                       // answer in [lo, lo + len]
+        while (len > 0) {
+            const int step = (len + 63) / 64;
+            const int p = lo + lane * step;
+            const bool below = p < lo + len && act[p] < target;
+            const int c = __popcll(__ballot(below));   // probes below target: a prefix
+            if (c == 0) {
+                len = 0;
+            } else {
+                const int nlo = lo + (c - 1) * step + 1;
+                const int nhi = min(lo + c * step, lo + len);
+                lo = nlo;
+                len = nhi - nlo;
+            }
         }
-        range_s[tid] = lo;
+        if (lane == 0) range_s[wid] = lo;
     }
 
     // This lane's two keys and their K fragments (zeros past kv_len).

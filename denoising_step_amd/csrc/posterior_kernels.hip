@@ -199,9 +199,10 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
 //
 // All global loads of the group (lock flags, scores, chunk partials) are
 // issued before anything waits on them: the partials are staged into LDS.
-// For a group of at most 32 rows, eight threads merge one row: thread k
-// takes chunks k, k+8, ... in order, and a fixed three-step butterfly over
-// the eight combines them; larger groups merge one row per thread.
+// For a group of at most 128 rows, 2, 4 or 8 threads merge one row (as many
+// as one pass allows): thread k takes chunks k, k+lanes, ... in order, and
+// a fixed butterfly over the lanes combines them; larger groups merge one
+// row per thread.
 // The selection uses block-wide reductions, not a serial scan.
 constexpr int kStageBytes = 32768;
 constexpr int kMergeLanes = 8;
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     __shared__ int tok_s[kMaxGroupRows];
     __shared__ uint8_t elig_s[kMaxGroupRows];
     __shared__ __attribute__((aligned(16))) PostPartial stage_s[kStageBytes / sizeof(PostPartial)];
+    __shared__ __attribute__((aligned(16))) unsigned long long ord_s[kMaxGroupRows];
     __shared__ float red_s[4];
 
     const int tid = threadIdx.x;
@@ -238,10 +240,14 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     const bool by_score = a.mode == 3 || a.mode == 4;
     constexpr int kStageParts = kStageBytes / (int)sizeof(PostPartial);
     const int rows_per_round = max(1, min(n, kStageParts / a.n_chunks));
-    // Threads per row in the merge: up to kMergeLanes when the group has
-    // few rows (so one pass covers it), one per row otherwise.
-    const bool wide = a.n_chunks > 1 && n * kMergeLanes <= 256;
-    const int lanes = wide ? kMergeLanes : 1;
+    // Threads per row in the merge: the largest power of two up to
+    // kMergeLanes with which one pass covers the group (1 for more than 128
+    // rows, or for unsplit rows).  It depends on the shapes only, so the
+    // merge order is fixed.
+    int lanes = 1;
+    if (a.n_chunks > 1)
+        while (lanes < kMergeLanes && n * lanes * 2 <= 256) lanes *= 2;
+    const bool wide = lanes > 1;
 
     // Issue the lock-flag and score loads together with the first staging
     // round; nothing waits until the barrier.
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                 for (int c = sub; c < a.n_chunks; c += lanes) rs_merge(s, rs_load(pp[c]));
             }
             if (wide)
-                for (int m = kMergeLanes / 2; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
+                for (int m = lanes / 2; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
             if (row_ok && sub == 0) {
                 const int r = g0 + gt;
                 float klv = 0.f, cf = 0.f;
@@ -340,26 +346,31 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     }
     const int any = __syncthreads_or(mine);
     // rank(t) = number of eligible rows ordered before t: (key desc, row
-    // asc).  Ineligible rows take key -inf (eligible keys are finite: a
-    // confidence or a column sum), so they never count; the count is
-    // branch-free over float4 reads of the keys.
+    // asc).  Each row's (key, row) is packed into one 64-bit integer whose
+    // unsigned order is exactly that order: the key's bits made
+    // order-preserving (all bits flipped for a negative key, the sign bit
+    // for a positive one) above the complemented row index.  Ineligible
+    // rows take key -inf and sort last (eligible keys are finite: a
+    // confidence or a column sum).  The rank is then a count of larger
+    // packed values: one 64-bit compare and one add per row.
+    typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
     __syncthreads();
-    for (int t = tid; t < n; t += 256)
-        if (!elig_s[t]) key_s[t] = -INFINITY;
-    for (int t = n; t < ((n + 3) & ~3); ++t)
-        if (tid == 0) key_s[t] = -INFINITY;
+    for (int t = tid; t < n; t += 256) {
+        const unsigned bits = __float_as_uint(elig_s[t] ? key_s[t] : -INFINITY);
+        const unsigned ord = bits ^ ((unsigned)((int)bits >> 31) | 0x80000000u);
+        ord_s[t] = ((unsigned long long)ord << 32) | (0xffffffffu - (unsigned)t);
+    }
+    for (int t = n + tid; t < ((n + 1) & ~1); t += 256) ord_s[t] = 0;   // even count
     __syncthreads();
     for (int t = tid; t < n; t += 256) {
         int out = -1;
         if (elig_s[t]) {
             const float kt = key_s[t];
+            const unsigned long long mine = ord_s[t];
             int rank = 0;
-            for (int u = 0; u < n; u += 4) {
-                const float4 k4 = *reinterpret_cast<const float4 *>(&key_s[u]);
-                rank += (k4.x > kt || (k4.x == kt && u + 0 < t)) ? 1 : 0;
-                rank += (k4.y > kt || (k4.y == kt && u + 1 < t)) ? 1 : 0;
-                rank += (k4.z > kt || (k4.z == kt && u + 2 < t)) ? 1 : 0;
-                rank += (k4.w > kt || (k4.w == kt && u + 3 < t)) ? 1 : 0;
+            for (int u = 0; u < n; u += 2) {
+                const u64x2 p = *reinterpret_cast<const u64x2 *>(&ord_s[u]);
+                rank += (p.x > mine ? 1 : 0) + (p.y > mine ? 1 : 0);
             }
             bool pick = false;
             if (a.mode == 1 || a.mode == 4) pick = rank < a.k;
