@@ -3,7 +3,10 @@
 
 A step is the whole hot path on one batch of seeded synthetic input:
 K/V scatter + sparse-query attention (pass 1) + column sums (pass 2) +
-posterior / KL lock test / unmask selection, through the two C-ABI calls.
+posterior / KL lock test / unmask selection, through the two C-ABI calls
+on one stream.  The same step with dlm_posterior on a second stream (its
+selection waiting for the column sums through select.score_ready) is
+reported for reference ("ms_per_step_two_streams").
 Inputs are resident in HBM before timing starts; the timed steps rotate over
 enough copies of the inputs that they cannot be served from the 256 MB
 Infinity Cache.  The lock flags are in/out, so every call gets its own copy
@@ -213,17 +216,26 @@ def main():
     # One fresh copy of the entry lock flags per call, made before timing
     # (the flags are in/out; every timed step must see the same entry state).
     n_calls = args.steps + args.warmup
-    lock_bufs = [sets[i % n_sets].locked0.clone() for i in range(4 * n_calls)]
+    lock_bufs = [sets[i % n_sets].locked0.clone() for i in range(5 * n_calls)]
     calls = [0]
 
     def fresh_lock():
         calls[0] += 1
         return lock_bufs[calls[0] - 1]
 
+    # A step: both C-ABI calls on the timed stream.
     def step(i):
         sets[i].run(stream, locked=fresh_lock())
 
     ms_step = time_loop(step, n_sets, args.steps, args.warmup)
+
+    # The same step with dlm_posterior on a second stream (its selection
+    # waiting for the column sums through select.score_ready), for reference:
+    # the cross-stream waits cost more than the overlap gains here.
+    def step_two_streams(i):
+        sets[i].run(stream, locked=fresh_lock(), overlap=True)
+
+    ms_step_2s = time_loop(step_two_streams, n_sets, args.steps, args.warmup)
     # the spread of single steps, from a separate loop: an event after every
     # step adds a small gap, so the figure above comes from a loop without them
     _, step_ms = time_loop(step, n_sets, args.steps, 0, per_step=True)
@@ -280,6 +292,7 @@ def main():
                      "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": stored_traffic(args.config),
                      "per_launch_flops": alg_flops, "avg_launch_us": ms_pass1 * 1e3},
         "step_ms_p10_p50_p90": [float(x) for x in q],
+        "ms_per_step_two_streams": ms_step_2s,
         "attention_passes_1_2": {"achieved": p12_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                  "frac": p12_tflops / PEAK_BF16_TFLOPS, "flops": alg_flops + cs_flops,
                                  "avg_call_us": ms_p12 * 1e3},

@@ -80,7 +80,8 @@ class _MaskDesc(ctypes.Structure):
 class _Select(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("group_rows", ctypes.c_int32),
                 ("tau", ctypes.c_float), ("score", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("score_ready", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -157,6 +158,7 @@ class Select:
     score: object = None       # fp32 [R]
     workspace: object = None
     workspace_bytes: Optional[int] = None
+    score_ready: object = None  # torch.cuda.Event (recorded) or a raw hipEvent_t, or None
 
 
 def _ptr(x) -> Optional[int]:
@@ -188,7 +190,12 @@ def _c_mask(md: MaskDesc) -> _MaskDesc:
 
 def _c_sel(s: Select) -> _Select:
     wb = s.workspace_bytes if s.workspace_bytes is not None else _nbytes(s.workspace)
-    return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb)
+    ev = s.score_ready
+    if ev is not None and not isinstance(ev, int):
+        ev = ev.cuda_event
+        if not ev:
+            raise DlmError(-1, "select.score_ready: the event has not been recorded")
+    return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb, ev or None)
 
 
 def _stream(stream) -> Optional[int]:

@@ -242,8 +242,8 @@ int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked
     a.part = static_cast<dlm::PostPartial *>(select->workspace);
     a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
     a.eps = eps; a.tau = select->tau; a.n_chunks = p.n_chunks; a.chunk = p.chunk;
-    hipError_t e = dlm::launch_posterior(a, stream);
-    if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    hipError_t e = dlm::launch_posterior(a, stream, select->score_ready);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "launch or event wait failed: %s", hipGetErrorString(e));
     return DLM_OK;
 }
 

@@ -91,7 +91,7 @@ struct PostArgs {
 
 // Enqueue the kernels of one call (arguments already validated).
 hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream);
-hipError_t launch_posterior(const PostArgs &a, hipStream_t stream);
+hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after);
 
 // Map a hardware workgroup id to a logical one so that logically
 // consecutive workgroups (which share K/V) run on the same XCD: the

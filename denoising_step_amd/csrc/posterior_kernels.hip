@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
 
 }  // namespace
 
-hipError_t launch_posterior(const PostArgs &a, hipStream_t stream)
+hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after)
 {
     if (a.R == 0) return hipSuccess;
     const long nwg = (long)a.R * a.n_chunks;
@@ -392,6 +392,10 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream)
         posterior_stream_kernel<true><<<dim3((unsigned)nwg), dim3(kPostThreads), 0, stream>>>(a);
     else
         posterior_stream_kernel<false><<<dim3((unsigned)nwg), dim3(kPostThreads), 0, stream>>>(a);
+    if (finish_after) {
+        const hipError_t e = hipStreamWaitEvent(stream, finish_after, 0);
+        if (e != hipSuccess) return e;
+    }
     const int groups = (a.R + a.group_rows - 1) / a.group_rows;
     posterior_finish_kernel<<<dim3((unsigned)groups), dim3(256), 0, stream>>>(a);
     return hipGetLastError();

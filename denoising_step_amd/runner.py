@@ -94,10 +94,31 @@ class DeviceStep:
         dlm_posterior(self.logits, self.prev, self.locked if locked is None else locked, p.eps,
                       self.select, self.sel, self.kl, self.conf, p.R, p.V, stream)
 
-    def run(self, stream=None, locked=None):
-        self.run_attn(stream)
-        if self.with_posterior:
-            self.run_posterior(stream, locked)
+    def run(self, stream=None, locked=None, overlap=False):
+        """One step.  With overlap, the posterior runs on a second stream:
+        its logit stream starts with the attention passes, and only its
+        selection waits for the column sums (select.score_ready); the
+        calling stream then waits for the posterior."""
+        if not (overlap and self.with_posterior):
+            self.run_attn(stream)
+            if self.with_posterior:
+                self.run_posterior(stream, locked)
+            return
+        main = stream if stream is not None else torch.cuda.current_stream()
+        if not hasattr(self, "_side"):
+            self._side = torch.cuda.Stream()
+            self._ev_start, self._ev_cs, self._ev_post = (torch.cuda.Event() for _ in range(3))
+        self._ev_start.record(main)
+        self._side.wait_event(self._ev_start)      # prior work on the calling stream first
+        self.run_attn(main)
+        self._ev_cs.record(main)                   # column sums ready
+        self.select.score_ready = self._ev_cs
+        try:
+            self.run_posterior(self._side, locked)
+        finally:
+            self.select.score_ready = None
+        self._ev_post.record(self._side)
+        main.wait_event(self._ev_post)
 
     def results(self) -> dict:
         torch.cuda.synchronize()

@@ -178,6 +178,13 @@ typedef struct {
     const float *score;      /* device fp32 [R]: ATTN_DYNAMIC / TOPK_SCORE ranking key */
     void *workspace;         /* device scratch, >= dlm_posterior_workspace_bytes() */
     size_t workspace_bytes;
+    hipEvent_t score_ready;  /* optional (NULL: none).  The selection stage, the only
+                                part that reads `score`, first waits for this event on
+                                `stream` (hipStreamWaitEvent); the KL / confidence
+                                stream over the logits does not.  A caller that records
+                                an event after the dlm_step_attn producing the column
+                                sums and calls dlm_posterior on a second stream thus
+                                overlaps the logit stream with the attention passes. */
 } dlm_select;
 
 /*

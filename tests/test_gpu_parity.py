@@ -169,6 +169,25 @@ def test_both_pass1_workgroup_shapes(kgroups, case, monkeypatch):
     full_check(w)
 
 
+@pytest.mark.parametrize("case", ["llada_dynamic", "long_topk_score"])
+def test_overlapped_step_equals_serial(case):
+    """The overlapped schedule (posterior on a second stream, its selection
+    waiting for the column sums through select.score_ready) gives the same
+    bits as the serial one, for both selection modes that read the score."""
+    w = small_llada(spread=True, seed=4) if case == "llada_dynamic" else small_long(seed=5)
+    _say(f"case: overlap {case}")
+    ds = _device_step(w)
+    ds.run()
+    r1 = ds.results()
+    for rep in range(3):
+        ds.reset()
+        ds.colsum.fill_(float("nan"))      # a read before the sums are ready would show
+        ds.run(overlap=True)
+        r2 = ds.results()
+        for k in ("out", "lse", "colsum", "kl", "conf", "sel", "locked", "cache_k", "cache_v"):
+            assert np.array_equal(r1[k], r2[k], equal_nan=False), (rep, k)
+
+
 def test_deterministic():
     w = small_long(seed=1)
     ds = _device_step(w)
