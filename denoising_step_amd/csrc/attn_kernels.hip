@@ -152,19 +152,23 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1.  Workgroup = 8 waves = 128 packed query rows of one (b, kv-head)
-// x 2 key groups: packed row r = (q-head within the GQA group) * M + j, so
-// the G q-heads that share a kv-head share every K/V tile staged in LDS.
-// Waves w and w + 4 own the same 32 rows; in each 128-key tile, key group
-// 0 (waves 0-3) takes keys 0-63 and key group 1 (waves 4-7) keys 64-127.
-// That puts two waves on every SIMD even when the rows alone give one wave
-// per SIMD, so one wave's softmax can run beside the other's MFMAs.  At the
-// end group 1 hands its (max, sum, O) to group 0 through LDS, which merges
-// them and writes the rows.
+// Pass 1.  A workgroup owns packed query rows of one (b, kv-head): packed
+// row r = (q-head within the GQA group) * M + j, so the G q-heads that share
+// a kv-head share every K/V tile staged in LDS.  Two shapes:
+//   one key group (NG = 1): QW query waves of 32 rows (8 at D >= 64: 256
+//     rows share each 64-key tile, halving the tile traffic per FLOP), for
+//     problems with enough query tiles to fill the chip;
+//   two key groups (NG = 2): 4 query waves x 2 = 8 waves on 128 rows.
+//     Waves w and w + 4 own the same 32 rows; in each 128-key tile, group 0
+//     takes keys 0-63 and group 1 keys 64-127.  That puts two waves on every
+//     SIMD when the rows alone give one wave per SIMD.  At the end group 1
+//     hands its (max, sum, O) to group 0 through LDS, which merges them and
+//     writes the rows.
 //
-// K/V tiles of 128 keys go from global memory straight into LDS (buffer
-// loads with the LDS destination: no registers, no LDS store instructions),
-// double-buffered: the loads of tile t+1 are issued before tile t is
+// K/V tiles (64 keys per key group) go from global memory straight into
+// LDS (buffer loads with the LDS destination: no registers, no LDS store
+// instructions), double-buffered: the loads of tile t+1 are issued before
+// tile t is
 // computed, and one barrier per tile publishes them.  Rows at or past
 // kv_len and rows of DUMMY slots are given an out-of-range offset and read
 // as zeros.
@@ -188,6 +192,12 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 // to the workspace and a separate kernel merges the splits in split order.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.f;
+
+// Query waves of a one-key-group pass-1 workgroup (32 rows each).
+#ifndef DLM_ATTN_QW1
+#define DLM_ATTN_QW1 8
+#endif
+constexpr int qwaves1(int D) { return D >= 64 ? DLM_ATTN_QW1 : 4; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -227,13 +237,15 @@ __device__ __forceinline__ float half_swap_max(float v)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, int NG>
-__global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
+template <int D, int NG, int QW>
+__global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
 {
     constexpr int KT = 64 * NG;          // keys per LDS tile; key group kg takes [64kg, 64kg + 64)
-    constexpr int NT = 256 * NG;         // threads
+    constexpr int NT = 64 * QW * NG;     // threads: QW query waves per key group
+    static_assert(NG == 1 || QW == 4, "two key groups run four query waves each");
     constexpr int ROWB = D * 2;          // bytes per K/V row
     constexpr int NLD = KT * ROWB / (NT * 16);   // 16-byte direct loads per thread per tile, per tensor
+    static_assert(NLD >= 1 && NLD * NT * 16 == KT * ROWB, "tile loads must cover the tile exactly");
     constexpr int DK = D / 16;           // MFMA k-steps over the head dim
     constexpr int DT = D / 32;           // 32-row tiles of O^T
     constexpr int OOB = 0x7ffffff0;      // an offset past any buffer view
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
     const int wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
     const int kg = NG == 2 ? wid >> 2 : 0;   // key group
-    const int wq = wid & 3;                  // query wave
+    const int wq = NG == 2 ? wid & 3 : wid;  // query wave
     const int kofs = 64 * kg;                // this group's first key in a tile
 
     int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
 
     // This lane's query.
     const int rows_bg = a.G * a.M;
-    const int r = qt * kAttnRows + wq * 32 + l32;
+    const int r = qt * (32 * QW) + wq * 32 + l32;
     const bool rv = r < rows_bg;
     const int hl = rv ? r / a.M : 0;
     const int j = rv ? r - hl * a.M : 0;
@@ -321,24 +333,41 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
         const int s = (n - a.P) / a.bs;
         return s >= a.n_slots || scode_s[s] == INT_MAX;
     };
-    auto issue_tile = [&](int t0, int buf) {
+    // key_code from the slot codes staged in LDS: no global load, so the
+    // only loads in flight in the tile loop are the tile loads themselves.
+    auto key_code_lds = [&](int n) -> int {
+        if (n >= a.kv_len) return INT_MAX;
+        if (a.kind == 0 || n < a.P) return INT_MIN;
+        const int sl = (n - a.P) / a.bs;
+        if (a.kind == 1) return sl;
+        return sl < a.n_slots ? scode_s[sl] : INT_MAX;
+    };
+    // Direct loads of the K (with its key codes) or V half of the tile at t0
+    // into LDS buffer buf.
+    auto issue_k = [&](int t0, int buf) {
         uint16_t *ks = buf ? Ks1 : Ks0;
-        uint16_t *vs = buf ? Vs1 : Vs0;
         const bool group_tail = a.kind == 2 && t0 + KT > a.P;
         for (int u = 0; u < NLD; ++u) {
-            int ko = k_goff[u] + t0 * ROWB, vo = v_goff[u] + t0 * ROWB;
+            int ko = k_goff[u] + t0 * ROWB;
             if (group_tail) {
                 const int lr = ld_row[u];
                 const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));
                 if (dummy_row(t0 + kkey)) ko = OOB;
-                if (dummy_row(t0 + lr)) vo = OOB;
             }
             lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
-            lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
+        }
+        if (tid < KT) kcode_s[buf][tid] = key_code_lds(t0 + tid);
+    };
+    auto issue_v = [&](int t0, int buf) {
+        uint16_t *vs = buf ? Vs1 : Vs0;
+        const bool group_tail = a.kind == 2 && t0 + KT > a.P;
+        for (int u = 0; u < NLD; ++u) {
+            int vo = v_goff[u] + t0 * ROWB;
+            if (group_tail && dummy_row(t0 + ld_row[u])) vo = OOB;
+            lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
         }
-        if (tid < KT) kcode_s[buf][tid] = key_code(a, st, gr, t0 + tid);
     };
 
     // Loop-invariant LDS read offsets (elements) of this lane.
@@ -366,60 +395,50 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
         o[dt] = mfma32(*reinterpret_cast<const bf16x8 *>(v8), p, o[dt]);
     };
 
-    // One tile: compute on LDS buffer BUF while tile t0 + KT streams into
-    // the other one.  BUF is a compile-time constant, so the compiler sees
-    // that the reads and the in-flight LDS loads touch different arrays and
-    // does not wait for the loads before reading.  This wave's 64 keys are
-    // two 32-key sub-tiles: after the shared max, the PV products of
-    // sub-tile 0 are interleaved with the exponentials of sub-tile 1, so the
-    // matrix core and the vector ALU work at the same time.
-    auto tile_step = [&](auto bufc, int t0) {
-        constexpr int BUF = decltype(bufc)::value;
-        if (t0 + KT < k1) issue_tile(t0 + KT, BUF ^ 1);
-        const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
-        const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
-
-        // S^T of both sub-tiles, the two MFMA chains interleaved and the K
-        // fragments read two k-steps ahead of their MFMAs.
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
-        {
-            bf16x8 r0[2], r1[2];
-            for (int kk = 0; kk < 2 && kk < DK; ++kk) {
-                r0[kk] = lds_frag(ks + k_rd[kk]);
-                r1[kk] = lds_frag(ks + 32 * D + k_rd[kk]);
-            }
-            for (int kk = 0; kk < DK; ++kk) {
-                const bf16x8 a0 = r0[kk & 1], a1 = r1[kk & 1];
-                if (kk + 2 < DK) {
-                    r0[kk & 1] = lds_frag(ks + k_rd[kk + 2]);
-                    r1[kk & 1] = lds_frag(ks + 32 * D + k_rd[kk + 2]);
-                }
-                s0 = mfma32(a0, qf[kk], s0);
-                s1 = mfma32(a1, qf[kk], s1);
-            }
-            // keep that order: 4 reads, then (2 MFMAs, 2 reads) ..., 4 MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, DK >= 2 ? 4 : 2, 0);
-            for (int kk = 0; kk + 2 < DK; ++kk) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, DK >= 2 ? 4 : 2, 0);
+    // S^T of this group's two 32-key sub-tiles of a tile (K at ks), the two
+    // MFMA chains interleaved and the K fragments read two k-steps ahead.
+    auto qk = [&](const uint16_t *ks, f32x16 &s0, f32x16 &s1) {
+        s0 = f32x16{};
+        s1 = f32x16{};
+        bf16x8 r0[2], r1[2];
+        for (int kk = 0; kk < 2 && kk < DK; ++kk) {
+            r0[kk] = lds_frag(ks + k_rd[kk]);
+            r1[kk] = lds_frag(ks + 32 * D + k_rd[kk]);
         }
-        const bool all_vis = (a.kind == 0 && t0 + KT <= a.kv_len) || (t0 + KT <= a.P);
+        for (int kk = 0; kk < DK; ++kk) {
+            const bf16x8 a0 = r0[kk & 1], a1 = r1[kk & 1];
+            if (kk + 2 < DK) {
+                r0[kk & 1] = lds_frag(ks + k_rd[kk + 2]);
+                r1[kk & 1] = lds_frag(ks + 32 * D + k_rd[kk + 2]);
+            }
+            s0 = mfma32(a0, qf[kk], s0);
+            s1 = mfma32(a1, qf[kk], s1);
+        }
+        // keep that order: 4 reads, then (2 MFMAs, 2 reads) ..., 4 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, DK >= 2 ? 4 : 2, 0);
+        for (int kk = 0; kk + 2 < DK; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, DK >= 2 ? 4 : 2, 0);
+    };
+
+    // Mask, then the exponent arguments u = s * scale * log2(e) - m_use (the
+    // running max, 0 before the first visible key) and their max: taking
+    // the max of FMA results rather than raw MFMA outputs spares the NaN
+    // canonicalisation of every input.  The running max moves only when
+    // the tile's max exceeds it by more than kRescaleLog2, or at the lane's
+    // first visible key; then O and l are rescaled and u shifted.
+    auto prep = [&](f32x16 &s0, f32x16 &s1, const int *kc, bool all_vis, float (&u0)[16],
+                    float (&u1)[16]) {
         if (!all_vis) {
-            const int *kc = kcode_s[BUF] + kofs;
             for (int i = 0; i < 16; ++i) {
                 const int key = 16 * (i >> 3) + 8 * hh + (i & 7);
                 if (kc[key] > qcode) s0[i] = -INFINITY;
                 if (kc[32 + key] > qcode) s1[i] = -INFINITY;
             }
         }
-        // Exponent arguments u = s * scale * log2(e) - m_use (the running
-        // max, 0 before the first visible key), and their max: taking the
-        // max of FMA results rather than raw MFMA outputs spares the NaN
-        // canonicalisation of every input.
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float u0[16], u1[16];
         for (int i = 0; i < 16; ++i) {
             u0[i] = fmaf(s0[i], c2, -m_use);
             u1[i] = fmaf(s1[i], c2, -m_use);
@@ -427,8 +446,6 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
         float tmax = fmaxf(u0[0], u1[0]);
         for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(u0[i], u1[i]));
         tmax = half_swap_max(tmax);
-        // Move the running max only when the tile's max exceeds it by more
-        // than kRescaleLog2, or when it is the lane's first visible key.
         const bool grow = m_run == -INFINITY ? tmax != -INFINITY : tmax > kRescaleLog2;
         if (__any(grow)) {
             const float d = grow ? tmax : 0.f;                 // new max - m_use
@@ -441,6 +458,27 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
                 u1[i] -= d;
             }
         }
+    };
+    auto all_visible = [&](int t0) { return (a.kind == 0 && t0 + KT <= a.kv_len) || (t0 + KT <= a.P); };
+
+    // One tile: compute on LDS buffer BUF while tile t0 + KT streams
+    // into the other one.  BUF is a compile-time constant, so the
+    // compiler sees that the reads and the in-flight LDS loads touch
+    // different arrays and does not wait for the loads before reading.
+    // The PV products of sub-tile 0 are interleaved with the
+    // exponentials of sub-tile 1.
+    auto tile_step = [&](auto bufc, int t0) {
+        constexpr int BUF = decltype(bufc)::value;
+        if (t0 + KT < k1) {
+            issue_k(t0 + KT, BUF ^ 1);
+            issue_v(t0 + KT, BUF ^ 1);
+        }
+        const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
+        const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
+        f32x16 s0, s1;
+        qk(ks, s0, s1);
+        float u0[16], u1[16];
+        prep(s0, s1, kcode_s[BUF] + kofs, all_visible(t0), u0, u1);
         float psum = 0.f;
         bf16x8 p0[2], p1[2];
         for (int i = 0; i < 16; ++i) {
@@ -465,7 +503,10 @@ __global__ __launch_bounds__(256 * NG, 2) void attn_fwd_kernel(AttnArgs a)
     };
 
     __syncthreads();   // slot codes and zeroed tiles visible
-    if (k0 < k1) issue_tile(k0, 0);
+    if (k0 < k1) {
+        issue_k(k0, 0);
+        issue_v(k0, 0);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t0 = k0; t0 < k1; t0 += 2 * KT) {
@@ -818,9 +859,9 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
     {
         long nwg = (long)a.B * a.Hkv * a.n_split * a.n_qtiles;
         if (a.n_kgroups == 2)
-            attn_fwd_kernel<D, 2><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
+            attn_fwd_kernel<D, 2, 4><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
         else
-            attn_fwd_kernel<D, 1><<<dim3((unsigned)nwg), dim3(256), 0, stream>>>(a);
+            attn_fwd_kernel<D, 1, qwaves1(D)><<<dim3((unsigned)nwg), dim3(64 * qwaves1(D)), 0, stream>>>(a);
     }
     if (a.n_split > 1) {
         const long rows = (long)a.B * a.Hq * a.M;
@@ -858,7 +899,7 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap)
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.D = D; p.M = M;
     p.kv_len = kv_len; p.n_cap = n_cap;
     p.n_qtiles = (p.G * M + kAttnRows - 1) / kAttnRows;
-    const long base = (long)B * Hkv * p.n_qtiles;
+    long base = (long)B * Hkv * p.n_qtiles;
     // Enough query tiles for two 4-wave workgroups per CU: one key group,
     // and the two workgroups on a CU keep their own barriers (one can run
     // its softmax while the other runs MFMAs).  Fewer: two key groups per
@@ -872,6 +913,10 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap)
     if (const char *e = getenv("DLM_ATTN_KGROUPS")) {
         if (e[0] == '1' && e[1] == 0) p.n_kgroups = 1;
         if (e[0] == '2' && e[1] == 0) p.n_kgroups = 2;
+    }
+    if (p.n_kgroups == 1 && qwaves1(D) != 4) {   // one key group: query tiles of 32 * qwaves1 rows
+        p.n_qtiles = (p.G * M + 32 * qwaves1(D) - 1) / (32 * qwaves1(D));
+        base = (long)B * Hkv * p.n_qtiles;
     }
     const int tile = 64 * p.n_kgroups;
     const int key_tiles = (kv_len + tile - 1) / tile;
