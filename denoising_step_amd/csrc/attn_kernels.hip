@@ -611,8 +611,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 // Pass 2.  Workgroup = (b, kv-head g, row split, 256-key block); wave w owns
 // keys [64w, 64w+64) of the block in registers for the whole pass.  It walks
 // the (q-head of g, 32-row query tile) pairs of its slice of the counted rows
-// as one sequence, double-buffered in LDS (tile t+1 is loaded while tile t
-// is used), and writes one partial column sum per (q-head, row split).
+// as one sequence, double-buffered in LDS (tile t+1 is loaded straight into
+// LDS while tile t is used), and writes one partial column sum per (q-head,
+// row split).
 // Rows past the slice or with lse = -inf get lse = +inf (weight 0).  The
 // visibility test is only evaluated when the mask can hide a key of the
 // block from a counted row.
@@ -621,14 +622,16 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
 {
     constexpr int DK = D / 16;
-    constexpr int QSTR = D + 8;
-    constexpr int CH = D / 8;
-    constexpr int QLOADS = (kCsRows * CH + 255) / 256;
+    constexpr int ROWB = D * 2;                    // bytes per Q row
+    constexpr int NQL = kCsRows * ROWB / 1024;     // 1-KB direct loads per Q tile
+    constexpr int OOB = 0x7ffffff0;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[2][kCsRows * QSTR];
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs0[kCsRows * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs1[kCsRows * D];
     __shared__ __attribute__((aligned(16))) float lse2_s[2][kCsRows];
     __shared__ int qcode_s[2][kCsRows];
     __shared__ int range_s[2];
+    __shared__ int grp_s[kMaxSlots];               // GROUP: slot -> group id
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6, lane = tid & 63;
@@ -645,6 +648,8 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     const uint8_t *st = a.kind == 2 ? a.slot_state + (long)b * a.n_slots : nullptr;
     const int32_t *gr = a.kind == 2 ? a.slot_group + (long)b * a.n_slots : nullptr;
     const int32_t *act = a.active_idx + (long)b * a.M;
+    if (a.kind == 2)
+        for (int sl = tid; sl < a.n_slots; sl += 256) grp_s[sl] = gr[sl];
 
     // Counted rows: active rows whose position lies in [cs_lo, cs_hi);
     // active_idx is ascending, so they are the index range [j_lo, j_hi).
@@ -694,62 +699,74 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     const int tiles_h = (r1 - r0 + kCsRows - 1) / kCsRows;     // query tiles per q-head
     const int n_tiles = tiles_h * a.G;
 
-    uint4 qreg[QLOADS];
-    float lreg = INFINITY;
-    int creg = INT_MIN;
-    auto load_tile = [&](int t) {
-        const int hl = t / tiles_h, rb = r0 + (t - hl * tiles_h) * kCsRows;
-        const long hrow = ((long)b * a.Hq + g * a.G + hl) * a.M;
-        // rows at or past r1 read as zeros
-        const __amdgpu_buffer_rsrc_t qrs = buffer_view(a.q + hrow * D, r1 * D * 2);
-        for (int u = 0; u < QLOADS; ++u) {
-            const int idx = tid + 256 * u;
-            if (idx < kCsRows * CH) qreg[u] = buffer_load16(qrs, ((rb + idx / CH) * D + (idx % CH) * 8) * 2);
+    // Q tiles go straight into LDS (1-KB buffer loads with the LDS
+    // destination; wave w issues loads w, w + 4, ...), with the chunk
+    // swizzle of pass 1's K tiles so that the fragment reads are
+    // conflict-free; rows at or past r1 read as zeros.  The per-row lse and
+    // query code take the register path (threads 0-31).
+    // Raw per-row values of the tile in flight (loaded when the tile is
+    // issued, turned into LDS entries only after the tile's compute, so no
+    // wait sits at the start of a tile).
+    float lraw = -INFINITY;
+    int praw = 0;
+    auto tile_rows = [&](int t, int &rb, long &hrow) {
+        const int hl = t / tiles_h;
+        rb = r0 + (t - hl * tiles_h) * kCsRows;
+        hrow = ((long)b * a.Hq + g * a.G + hl) * a.M;
+    };
+    auto issue_q = [&](int t, int buf) {
+        int rb;
+        long hrow;
+        tile_rows(t, rb, hrow);
+        const __amdgpu_buffer_rsrc_t qrs = buffer_view(a.q + hrow * D, r1 * ROWB);
+        uint16_t *qs = buf ? Qs1 : Qs0;
+        for (int u = wid; u < NQL; u += 4) {
+            const int byte = u * 1024 + lane * 16;
+            const int lr = byte / ROWB, lp = (byte % ROWB) / 16;
+            const int off = rb + lr < r1 ? ((rb + lr) * D + ((lp ^ k_swz<D>(lr)) * 8)) * 2 : OOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)(qs + u * 512), 16, off, 0, 0, 0);
         }
         if (tid < kCsRows) {
             const int jr = rb + tid;
-            lreg = INFINITY;
-            creg = INT_MIN;
-            if (jr < r1) {
-                const float lv = a.lse[hrow + jr];
-                if (lv != -INFINITY) {
-                    lreg = lv * kLog2e;
-                    creg = need_mask ? query_code(a, gr, act[jr]) : 0;
-                }
-            }
+            lraw = jr < r1 ? a.lse[hrow + jr] : -INFINITY;
+            praw = (jr < r1 && need_mask) ? act[jr] : 0;
         }
     };
-    auto store_tile = [&](int buf) {
-        for (int u = 0; u < QLOADS; ++u) {
-            const int idx = tid + 256 * u;
-            if (idx < kCsRows * CH) *reinterpret_cast<uint4 *>(&Qs[buf][(idx / CH) * QSTR + (idx % CH) * 8]) = qreg[u];
-        }
+    // lse in log2 units, +inf (weight 0) for a row past the slice or
+    // without a visible key; the row's mask code from the staged slot table.
+    auto store_rows = [&](int buf) {
         if (tid < kCsRows) {
-            lse2_s[buf][tid] = lreg;
-            qcode_s[buf][tid] = creg;
+            const bool ok = lraw != -INFINITY;
+            int qc = 0;
+            if (need_mask) {
+                const int sl = (praw - a.P) / a.bs;
+                qc = a.kind == 1 ? sl : (sl >= 0 && sl < a.n_slots ? grp_s[sl] : INT_MIN);
+            }
+            lse2_s[buf][tid] = ok ? lraw * kLog2e : INFINITY;
+            qcode_s[buf][tid] = ok ? qc : INT_MIN;
         }
     };
+    int q_rd[DK];                                        // Q chunk 2kk+hh of row l32
+    for (int kk = 0; kk < DK; ++kk) q_rd[kk] = l32 * D + (((2 * kk + hh) ^ k_swz<D>(l32)) * 8);
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
     float acc[2] = {0.f, 0.f};
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
+    // One query tile on LDS buffer BUF while tile t + 1 streams into the
+    // other (BUF a compile-time constant: the compiler sees the reads and
+    // the in-flight loads touch different arrays).
+    auto tile = [&](auto bufc, int t) {
+        constexpr int BUF = decltype(bufc)::value;
         const bool more = t + 1 < n_tiles;
-        if (more) load_tile(t + 1);
+        if (more) issue_q(t + 1, BUF ^ 1);
+        const uint16_t *qs = BUF ? Qs1 : Qs0;
         f32x16 s0 = f32x16{}, s1 = f32x16{};
-        const uint16_t *qr = &Qs[buf][l32 * QSTR + hh * 8];
         for (int kk = 0; kk < DK; ++kk) {
-            const bf16x8 qa = lds_frag(qr + kk * 16);
+            const bf16x8 qa = lds_frag(qs + q_rd[kk]);
             s0 = mfma32(qa, kf[0][kk], s0);
             s1 = mfma32(qa, kf[1][kk], s1);
         }
         // element i of this lane is query row 8*(i/4) + 4*hh + i%4 of the tile
         for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 l2 = *reinterpret_cast<const float4 *>(&lse2_s[buf][8 * q4 + 4 * hh]);
+            const float4 l2 = *reinterpret_cast<const float4 *>(&lse2_s[BUF][8 * q4 + 4 * hh]);
             const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
             if (!need_mask) {
                 for (int e = 0; e < 4; ++e) {
@@ -758,7 +775,7 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
                 }
             } else {
                 for (int e = 0; e < 4; ++e) {
-                    const int qc = qcode_s[buf][8 * q4 + 4 * hh + e];
+                    const int qc = qcode_s[BUF][8 * q4 + 4 * hh + e];
                     const float p0 = fast_exp2(fmaf(s0[q4 * 4 + e], a.scale_log2, -lv[e]));
                     const float p1 = fast_exp2(fmaf(s1[q4 * 4 + e], a.scale_log2, -lv[e]));
                     acc[0] += kc[0] <= qc ? p0 : 0.f;
@@ -766,7 +783,7 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
                 }
             }
         }
-        if (more) store_tile(buf ^ 1);
+        if (more) store_rows(BUF ^ 1);
         if (t % tiles_h == tiles_h - 1) {
             // last tile of a q-head: write its partial column sums
             const int h = g * a.G + t / tiles_h;
@@ -777,7 +794,19 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
                 acc[ct] = 0.f;
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile landed
         __syncthreads();
+    };
+
+    if (n_tiles > 0) {
+        issue_q(0, 0);
+        store_rows(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; t += 2) {
+        tile(std::integral_constant<int, 0>{}, t);
+        if (t + 1 < n_tiles) tile(std::integral_constant<int, 1>{}, t + 1);
     }
     if (n_tiles == 0) {
         // no counted rows in this slice: zero partials for every q-head
