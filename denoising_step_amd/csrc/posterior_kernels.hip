@@ -401,17 +401,25 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t fi
     return hipGetLastError();
 }
 
+#ifndef DLM_POST_WGS_PER_CU
+#define DLM_POST_WGS_PER_CU 16
+#endif
+
 PostPlan plan_post(int R, int V, int mode, int group_rows)
 {
     PostPlan p{};
-    // About four streaming workgroups per CU, chunks of at least one
-    // streaming step (4096 elements).
+    // About sixteen streaming workgroups per CU (measured: shorter chunks
+    // balance the end of the stream better than four long ones per CU),
+    // chunks of at least one streaming step (4096 elements).
     int chunks = 1;
     if (R > 0) {
-        const long target = 4L * kNumCU;
+        const long target = (long)DLM_POST_WGS_PER_CU * kNumCU;
         if (R < target) chunks = (int)((target + R - 1) / R);
         const int max_chunks = max(1, (V + kPostThreads * kPostVec - 1) / (kPostThreads * kPostVec));
         chunks = min(chunks, max_chunks);
+        // and a finishing group's partials fit one LDS staging round
+        const int g = min(R, mode == 0 ? 256 : group_rows);
+        chunks = min(chunks, max(1, (kStageBytes / (int)sizeof(PostPartial)) / max(1, g)));
     }
     int chunk = (V + chunks - 1) / chunks;
     // A split row gets chunks of whole streaming steps (4 float4 per array
