@@ -59,9 +59,9 @@ def _load():
         lib.ora_colsum.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, P, P,
                                    Dd, I, I, I, P, L, P, P]
         lib.ora_colsum.restype = None
-        lib.ora_posterior.argtypes = [P, P, P, L, L, Dd, L, P, P, P, P, P]
+        lib.ora_posterior.argtypes = [P, P, P, L, L, Dd, L, P, P, P, P, P, P, P]
         lib.ora_posterior.restype = None
-        lib.ora_select.argtypes = [I, I, I, Dd, P, P, P, P, I, P]
+        lib.ora_select.argtypes = [I, I, I, Dd, P, P, P, P, I, P, P, P]
         lib.ora_select.restype = None
         lib.ora_num_threads.argtypes = []
         lib.ora_num_threads.restype = I
@@ -163,7 +163,9 @@ def colsum(case, lse_all, kv=None, cols=None):
 
 def posterior(logits, prev, locked, eps, rows=None):
     """Per-row KL(p_t || p_{t-1}), confidence, argmax token and lock flag
-    (SureLock section 2).  Returns dict of kl, conf, tok, locked (new)."""
+    (SureLock section 2), and the margin p(top-1) - p(top-2) and entropy of
+    p_t (the token-level scores named on the Attn-Sampler page, section 1).
+    Returns dict of kl, conf, tok, locked (new), margin, entropy."""
     lib = _load()
     logits = _c(logits, np.float32)
     prev = _c(prev, np.float32)
@@ -175,21 +177,28 @@ def posterior(logits, prev, locked, eps, rows=None):
     conf = np.empty(n, np.float64)
     tok = np.empty(n, np.int32)
     lk = np.empty(n, np.uint8)
+    margin = np.empty(n, np.float64)
+    entropy = np.empty(n, np.float64)
     lib.ora_posterior(_p(logits), _p(prev), _p(locked), R, V, float(eps), n, _p(rows_a),
-                      _p(kl), _p(conf), _p(tok), _p(lk))
-    return {"kl": kl, "conf": conf, "tok": tok, "locked": lk}
+                      _p(kl), _p(conf), _p(tok), _p(lk), _p(margin), _p(entropy))
+    return {"kl": kl, "conf": conf, "tok": tok, "locked": lk, "margin": margin, "entropy": entropy}
 
 
-def select(mode, k, group_rows, tau, score, conf, tok, locked_in):
+def select(mode, k, group_rows, tau, score, conf, tok, locked_in, margin=None, entropy=None):
     """Unmask selection per group of rows (confidence top-k / threshold,
-    Attn-Sampler order and dynamic threshold).  Returns sel int32 [R]."""
+    Attn-Sampler order and dynamic threshold, margin and entropy samplers).
+    Returns sel int32 [R]."""
     lib = _load()
     conf = _c(conf, np.float64)
     R = conf.shape[0]
-    score_a = _c(score, np.float64) if score is not None else np.zeros(R, np.float64)
+    zeros = np.zeros(R, np.float64)
+    score_a = _c(score, np.float64) if score is not None else zeros
+    margin_a = _c(margin, np.float64) if margin is not None else zeros
+    entropy_a = _c(entropy, np.float64) if entropy is not None else zeros
     sel = np.empty(R, np.int32)
     lib.ora_select(int(mode), int(k), int(group_rows), float(tau), _p(score_a), _p(conf),
-                   _p(_c(tok, np.int32)), _p(_c(locked_in, np.uint8)), R, _p(sel))
+                   _p(_c(tok, np.int32)), _p(_c(locked_in, np.uint8)), R, _p(sel),
+                   _p(margin_a), _p(entropy_a))
     return sel
 
 
@@ -203,6 +212,7 @@ def step(workload, attn_rows=None):
     cs = colsum(a, lse, kv=kv)
     post = posterior(p.logits, p.prev, p.locked, p.eps)
     score = score_for(p, cs if not a.colsum_per_head else cs.sum(1))
-    sel = select(p.mode, p.k, p.group_rows, p.tau, score, post["conf"], post["tok"], p.locked)
+    sel = select(p.mode, p.k, p.group_rows, p.tau, score, post["conf"], post["tok"], p.locked,
+                 post["margin"], post["entropy"])
     return {"cache_k": kv[0], "cache_v": kv[1], "out": out, "lse": lse, "colsum": cs,
             "score": score, "sel": sel, **post}

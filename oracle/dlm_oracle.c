@@ -36,7 +36,8 @@
 enum { ORA_FULL = 0, ORA_BLOCK_CAUSAL = 1, ORA_GROUP = 2 };
 enum { ORA_DUMMY = 0 };
 enum { ORA_SEL_NONE = 0, ORA_SEL_TOPK_CONF = 1, ORA_SEL_THRESH_CONF = 2,
-       ORA_SEL_ATTN_DYNAMIC = 3, ORA_SEL_TOPK_SCORE = 4 };
+       ORA_SEL_ATTN_DYNAMIC = 3, ORA_SEL_TOPK_SCORE = 4, ORA_SEL_TOPK_MARGIN = 5,
+       ORA_SEL_TOPK_LOW_ENTROPY = 6 };
 
 /* Exact bf16 -> fp64 widening: a bf16 value is the top half of an fp32. */
 static double wide(uint16_t bits)
@@ -250,7 +251,7 @@ void ora_colsum(const uint16_t *q, const uint16_t *Kc, const int32_t *active_idx
 void ora_posterior(const float *logits, const float *prev, const uint8_t *locked_in,
                    int64_t R, int64_t V, double eps, int64_t n_rows,
                    const int64_t *rows, double *kl, double *conf, int32_t *tok,
-                   uint8_t *locked_out)
+                   uint8_t *locked_out, double *margin, double *entropy)
 {
     if (rows == NULL)
         n_rows = R;
@@ -262,6 +263,8 @@ void ora_posterior(const float *logits, const float *prev, const uint8_t *locked
             conf[t] = 0.0;
             tok[t] = -1;
             locked_out[t] = 1;
+            margin[t] = 0.0;
+            entropy[t] = 0.0;
             continue;
         }
         const float *x = logits + r * V;
@@ -293,6 +296,22 @@ void ora_posterior(const float *logits, const float *prev, const uint8_t *locked
         conf[t] = exp(mx - Lx);
         tok[t] = (int32_t)arg;
         locked_out[t] = (uint8_t)(d <= eps);
+        /* Token-level scores of the confidence family (Attn-Sampler page,
+         * section 1: confidence, margin, entropy).  margin = p(top-1) -
+         * p(top-2), the runner-up being the largest logit at any other
+         * index (equal to the top one on a tie; no runner-up when V = 1);
+         * entropy = -sum_v p_v ln p_v of p_t. */
+        double x2 = -INFINITY;
+        for (int64_t v = 0; v < V; ++v)
+            if (v != arg && (double)x[v] > x2)
+                x2 = (double)x[v];
+        margin[t] = exp(mx - Lx) - (x2 == -INFINITY ? 0.0 : exp(x2 - Lx));
+        double h = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            double logp = (double)x[v] - Lx;
+            h -= exp(logp) * logp;
+        }
+        entropy[t] = h;
     }
 }
 
@@ -308,6 +327,8 @@ void ora_posterior(const float *logits, const float *prev, const uint8_t *locked
  *                none); select candidates whose score exceeds it; if none,
  *                the eligible row of highest score (Attn-Sampler section 2B).
  *  TOPK_SCORE:   the k eligible rows of highest score.
+ *  TOPK_MARGIN:  the k eligible rows of largest margin (margin sampler).
+ *  TOPK_LOW_ENTROPY: the k eligible rows of lowest entropy (entropy sampler).
  * sel[r] = tok[r] if selected, else -1.
  * ---------------------------------------------------------------------- */
 static const double *g_key;
@@ -323,13 +344,18 @@ static int cmp_desc(const void *a, const void *b)
 
 void ora_select(int mode, int k, int group_rows, double tau, const double *score,
                 const double *conf, const int32_t *tok, const uint8_t *locked_in,
-                int R, int32_t *sel)
+                int R, int32_t *sel, const double *margin, const double *entropy)
 {
     int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)(group_rows > 0 ? group_rows : 1));
+    /* lowest entropy first: rank by the negated entropy */
+    double *neg_entropy = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    for (int r = 0; r < R; ++r)
+        neg_entropy[r] = mode == ORA_SEL_TOPK_LOW_ENTROPY ? -entropy[r] : 0.0;
     for (int r = 0; r < R; ++r)
         sel[r] = -1;
     if (mode == ORA_SEL_NONE) {
         free(order);
+        free(neg_entropy);
         return;
     }
     for (int g0 = 0; g0 < R; g0 += group_rows) {
@@ -340,10 +366,14 @@ void ora_select(int mode, int k, int group_rows, double tau, const double *score
                 order[n++] = r;
         if (n == 0)
             continue;
-        const double *key = (mode == ORA_SEL_TOPK_SCORE || mode == ORA_SEL_ATTN_DYNAMIC) ? score : conf;
+        const double *key = (mode == ORA_SEL_TOPK_SCORE || mode == ORA_SEL_ATTN_DYNAMIC) ? score
+                            : mode == ORA_SEL_TOPK_MARGIN                         ? margin
+                            : mode == ORA_SEL_TOPK_LOW_ENTROPY                    ? neg_entropy
+                                                                                  : conf;
         g_key = key;
         qsort(order, (size_t)n, sizeof(int32_t), cmp_desc);
-        if (mode == ORA_SEL_TOPK_CONF || mode == ORA_SEL_TOPK_SCORE) {
+        if (mode == ORA_SEL_TOPK_CONF || mode == ORA_SEL_TOPK_SCORE || mode == ORA_SEL_TOPK_MARGIN ||
+            mode == ORA_SEL_TOPK_LOW_ENTROPY) {
             for (int t = 0; t < n && t < k; ++t)
                 sel[order[t]] = tok[order[t]];
         } else if (mode == ORA_SEL_THRESH_CONF) {
@@ -371,6 +401,7 @@ void ora_select(int mode, int k, int group_rows, double tau, const double *score
         }
     }
     free(order);
+    free(neg_entropy);
 }
 
 int ora_num_threads(void)

@@ -53,6 +53,15 @@ MUTANTS = [
      [pins.test_selection_golden]),
     ("select_ignores_locks", "if (!locked_in[r])\n                order[n++] = r;",
      "order[n++] = r;", [pins.test_selection_golden]),
+    ("entropy_in_bits", "h -= exp(logp) * logp;", "h -= exp(logp) * logp / log(2.0);",
+     [pins.test_margin_entropy_vs_library, pins.test_margin_entropy_closed_forms]),
+    ("margin_drops_runner_up", "margin[t] = exp(mx - Lx) - (x2 == -INFINITY ? 0.0 : exp(x2 - Lx));",
+     "margin[t] = exp(mx - Lx);", [pins.test_margin_entropy_vs_library]),
+    ("runner_up_may_be_argmax", "if (v != arg && (double)x[v] > x2)", "if ((double)x[v] > x2)",
+     [pins.test_margin_entropy_vs_library]),
+    ("entropy_sampler_highest", "neg_entropy[r] = mode == ORA_SEL_TOPK_LOW_ENTROPY ? -entropy[r] : 0.0;",
+     "neg_entropy[r] = mode == ORA_SEL_TOPK_LOW_ENTROPY ? entropy[r] : 0.0;",
+     [pins.test_selection_golden, pins.test_selection_brute_force]),
 ]
 
 

@@ -288,6 +288,46 @@ def test_posterior_vs_scipy():
     assert np.allclose(r["kl"][small], 0.5 * var[small], rtol=0.05)
 
 
+def test_margin_entropy_vs_library():
+    """entropy against scipy.stats.entropy of the softmax (natural log);
+    margin against the two largest softmax probabilities from a sort."""
+    import scipy.stats as st
+    rng = np.random.default_rng(31)
+    R, V = 20, 2049
+    x = (rng.standard_normal((R, V)) * np.linspace(0.1, 8.0, R)[:, None]).astype(np.float32)
+    x[3, 7] = 40.0                                   # one near-certain row
+    r = oracle.posterior(x, x + np.float32(0.01), np.zeros(R, np.uint8), 1e-3)
+    p = sps.softmax(x.astype(np.float64), axis=1)
+    assert np.abs(r["entropy"] - st.entropy(p, axis=1)).max() <= 1e-11
+    ps = np.sort(p, axis=1)
+    assert np.abs(r["margin"] - (ps[:, -1] - ps[:, -2])).max() <= 1e-13
+    assert np.all(r["margin"] >= 0) and np.all(r["entropy"] >= 0)
+
+
+def test_margin_entropy_closed_forms():
+    # two tokens: H = -p ln p - (1-p) ln(1-p), margin = |2p - 1|
+    for a in (2.0, -1.5, 0.0, 6.0):
+        x = np.array([[a, 0.0]], np.float32)
+        p = 1.0 / (1.0 + math.exp(-float(np.float32(a))))
+        r = oracle.posterior(x, x.copy(), np.zeros(1, np.uint8), 1e-3)
+        h = -p * math.log(p) - (1 - p) * math.log(1 - p)
+        assert abs(r["entropy"][0] - h) <= 1e-14
+        assert abs(r["margin"][0] - abs(2 * p - 1)) <= 1e-14
+    # uniform over V: H = ln V, margin 0 (every logit ties with the maximum)
+    for V in (1, 2, 7, 1000):
+        x = np.full((1, V), 1.25, np.float32)
+        r = oracle.posterior(x, x.copy(), np.zeros(1, np.uint8), 1e-3)
+        assert abs(r["entropy"][0] - math.log(V)) <= 1e-12
+        assert r["margin"][0] == (1.0 if V == 1 else 0.0)   # V = 1: no runner-up
+    # a repeated maximum elsewhere: margin exactly 0
+    x = np.array([[0.5, 3.0, -1.0, 3.0]], np.float32)
+    r = oracle.posterior(x, x.copy(), np.zeros(1, np.uint8), 1e-3)
+    assert r["margin"][0] == 0.0 and r["tok"][0] == 1
+    # locked rows report zeros
+    r = oracle.posterior(x, x.copy(), np.ones(1, np.uint8), 1e-3)
+    assert r["margin"][0] == 0.0 and r["entropy"][0] == 0.0
+
+
 def test_posterior_identical_rows_kl_zero_and_lock():
     rng = np.random.default_rng(4)
     x = (rng.standard_normal((5, 777)) * 3).astype(np.float32)
@@ -330,11 +370,13 @@ def test_selection_golden():
     for c in cases:
         sel = oracle.select(c["mode"], c["k"], c["group_rows"], c["tau"],
                             np.array(c["score"], np.float64), np.array(c["conf"], np.float64),
-                            tok, np.array(c["locked"], np.uint8))
+                            tok, np.array(c["locked"], np.uint8),
+                            np.array(c.get("margin", [0.0] * 6), np.float64),
+                            np.array(c.get("entropy", [0.0] * 6), np.float64))
         assert sel.tolist() == c["sel"], c["cite"]
 
 
-def _brute_select(mode, k, g, tau, score, conf, tok, locked):
+def _brute_select(mode, k, g, tau, score, conf, tok, locked, margin=None, entropy=None):
     """Brute force: sort each group with numpy.lexsort; the dynamic threshold
     uses its equivalent walk (descending score, longest run of candidates)."""
     R = len(conf)
@@ -345,9 +387,11 @@ def _brute_select(mode, k, g, tau, score, conf, tok, locked):
         rows = np.array([r for r in range(g0, min(R, g0 + g)) if not locked[r]], np.int64)
         if rows.size == 0:
             continue
-        key = score if mode in (W.SEL_TOPK_SCORE, W.SEL_ATTN_DYNAMIC) else conf
+        key = (score if mode in (W.SEL_TOPK_SCORE, W.SEL_ATTN_DYNAMIC) else
+               margin if mode == W.SEL_TOPK_MARGIN else
+               -entropy if mode == W.SEL_TOPK_LOW_ENTROPY else conf)
         order = rows[np.lexsort((rows, -key[rows]))]
-        if mode in (W.SEL_TOPK_CONF, W.SEL_TOPK_SCORE):
+        if mode in (W.SEL_TOPK_CONF, W.SEL_TOPK_SCORE, W.SEL_TOPK_MARGIN, W.SEL_TOPK_LOW_ENTROPY):
             pick = order[:k]
         elif mode == W.SEL_THRESH_CONF:
             pick = [r for r in order if conf[r] > tau] or [order[0]]
@@ -373,15 +417,17 @@ def test_selection_brute_force():
     for trial in range(300):
         R = int(rng.integers(1, 40))
         g = int(rng.integers(1, R + 1))
-        mode = int(rng.integers(0, 5))
+        mode = int(rng.integers(0, 7))
         k = int(rng.integers(0, 8))
         tau = float(rng.choice([0.3, 0.5, 0.9]))
         conf = np.round(rng.random(R), 1)            # many exact ties
         score = np.round(rng.random(R) * 4, 0)
+        margin = np.round(rng.random(R), 1)
+        entropy = np.round(rng.random(R) * 3, 1)
         tok = rng.integers(0, 1000, R).astype(np.int32)
         locked = (rng.random(R) < 0.3).astype(np.uint8)
-        got = oracle.select(mode, k, g, tau, score, conf, tok, locked)
-        ref = _brute_select(mode, k, g, tau, score, conf, tok, locked)
+        got = oracle.select(mode, k, g, tau, score, conf, tok, locked, margin, entropy)
+        ref = _brute_select(mode, k, g, tau, score, conf, tok, locked, margin, entropy)
         assert np.array_equal(got, ref), (trial, mode)
 
 

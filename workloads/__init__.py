@@ -30,6 +30,7 @@ import numpy as np
 MASK_FULL, MASK_BLOCK_CAUSAL, MASK_GROUP = 0, 1, 2
 SLOT_DUMMY, SLOT_ACTIVE, SLOT_TO_CACHE, SLOT_IN_CACHE = 0, 1, 2, 3
 SEL_NONE, SEL_TOPK_CONF, SEL_THRESH_CONF, SEL_ATTN_DYNAMIC, SEL_TOPK_SCORE = 0, 1, 2, 3, 4
+SEL_TOPK_MARGIN, SEL_TOPK_LOW_ENTROPY = 5, 6
 
 _STREAMS = ("q", "k", "v", "cache_k", "cache_v", "active", "logits", "noise",
             "mixture")
