@@ -25,6 +25,7 @@ DLM_OK, DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_DESC, DLM_E_WORKSPACE,
 MASK_FULL, MASK_BLOCK_CAUSAL, MASK_GROUP = 0, 1, 2
 SLOT_DUMMY, SLOT_ACTIVE, SLOT_TO_CACHE, SLOT_IN_CACHE = 0, 1, 2, 3
 SEL_NONE, SEL_TOPK_CONF, SEL_THRESH_CONF, SEL_ATTN_DYNAMIC, SEL_TOPK_SCORE = 0, 1, 2, 3, 4
+SEL_TOPK_MARGIN, SEL_TOPK_LOW_ENTROPY = 5, 6
 
 EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
            "dlm_posterior_workspace_bytes", "dlm_last_error")
@@ -74,14 +75,16 @@ class _MaskDesc(ctypes.Structure):
                 ("slot_state", ctypes.c_void_p), ("slot_group", ctypes.c_void_p),
                 ("cs_lo", ctypes.c_int32), ("cs_hi", ctypes.c_int32),
                 ("colsum_per_head", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("colsum_accumulate", ctypes.c_int32)]
 
 
 class _Select(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("group_rows", ctypes.c_int32),
                 ("tau", ctypes.c_float), ("score", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("score_ready", ctypes.c_void_p)]
+                ("score_ready", ctypes.c_void_p), ("margin", ctypes.c_void_p),
+                ("entropy", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -147,6 +150,7 @@ class MaskDesc:
     scale: float = 0.0
     workspace: object = None   # uint8 device buffer
     workspace_bytes: Optional[int] = None
+    colsum_accumulate: int = 0  # 1: colsum += this call's sums (e.g. over layers)
 
 
 @dataclasses.dataclass
@@ -159,6 +163,8 @@ class Select:
     workspace: object = None
     workspace_bytes: Optional[int] = None
     score_ready: object = None  # torch.cuda.Event (recorded) or a raw hipEvent_t, or None
+    margin: object = None       # optional fp32 [R] output
+    entropy: object = None      # optional fp32 [R] output
 
 
 def _ptr(x) -> Optional[int]:
@@ -185,7 +191,7 @@ def _c_mask(md: MaskDesc) -> _MaskDesc:
     wb = md.workspace_bytes if md.workspace_bytes is not None else _nbytes(md.workspace)
     return _MaskDesc(md.kind, md.Hq, md.M, md.kv_len, md.prefix_len, md.block_size, md.n_slots,
                      _ptr(md.slot_state), _ptr(md.slot_group), md.cs_lo, md.cs_hi,
-                     md.colsum_per_head, md.scale, _ptr(md.workspace), wb)
+                     md.colsum_per_head, md.scale, _ptr(md.workspace), wb, md.colsum_accumulate)
 
 
 def _c_sel(s: Select) -> _Select:
@@ -195,7 +201,8 @@ def _c_sel(s: Select) -> _Select:
         ev = ev.cuda_event
         if not ev:
             raise DlmError(-1, "select.score_ready: the event has not been recorded")
-    return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb, ev or None)
+    return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb, ev or None,
+                   _ptr(s.margin), _ptr(s.entropy))
 
 
 def _stream(stream) -> Optional[int]:
@@ -272,6 +279,10 @@ def dlm_posterior(logits, prev_logits, locked, eps: float, select: Select, sel, 
     _expect(conf, "conf", (R,), "torch.float32")
     if select.score is not None:
         _expect(select.score, "select.score", (R,), "torch.float32")
+    if select.margin is not None:
+        _expect(select.margin, "select.margin", (R,), "torch.float32")
+    if select.entropy is not None:
+        _expect(select.entropy, "select.entropy", (R,), "torch.float32")
     s = _c_sel(select)
     _check(lib.dlm_posterior(_ptr(logits), _ptr(prev_logits), _ptr(locked), eps, ctypes.byref(s),
                              _ptr(sel), _ptr(kl), _ptr(conf), R, V, _stream(stream)))

@@ -817,7 +817,8 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     }
 }
 
-// colsum[b, n] = sum_h sum_rs part[b, h, rs, n] (or per head: sum_rs).
+// colsum[b, n] = sum_h sum_rs part[b, h, rs, n] (or per head: sum_rs); with
+// accumulate, added to what colsum holds.
 // Workgroup = (256 / SL) consecutive columns of one (b, h-or-all) x SL
 // slices; slice q sums partials s = q, q + SL, ... with eight independent
 // accumulators (eight loads in flight per thread), and the slices are then
@@ -850,7 +851,10 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(AttnArgs a)
     }
     const float mine = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     if (SL == 1) {
-        if (n < a.kv_len) a.colsum[(long)bh * a.kv_len + n] = mine;
+        if (n < a.kv_len) {
+            float *c = a.colsum + (long)bh * a.kv_len + n;
+            *c = a.accumulate ? *c + mine : mine;
+        }
         return;
     }
     part_s[q][c] = mine;
@@ -860,7 +864,8 @@ __global__ __launch_bounds__(256) void colsum_reduce_kernel(AttnArgs a)
         for (int k = 0; k < SL; ++k) t[k] = part_s[k][c];
         for (int w = SL / 2; w >= 1; w >>= 1)
             for (int k = 0; k < w; ++k) t[k] = t[k] + t[k + w];
-        a.colsum[(long)bh * a.kv_len + n] = t[0];
+        float *c = a.colsum + (long)bh * a.kv_len + n;
+        *c = a.accumulate ? *c + t[0] : t[0];
     }
 }
 
@@ -879,7 +884,7 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
         kv_scatter_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
     }
     if (a.M == 0) {
-        if (a.colsum) {
+        if (a.colsum && !a.accumulate) {
             long n = (long)a.B * (a.per_head ? a.Hq : 1) * a.kv_len;
             fill_zero_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(a.colsum, n);
         }

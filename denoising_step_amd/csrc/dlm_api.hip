@@ -72,6 +72,8 @@ int check_attn_scalars(const dlm_kv_cache *kc, const dlm_mask_desc *md)
         return fail(DLM_E_DESC, "cs_lo=%d > cs_hi=%d", md->cs_lo, md->cs_hi);
     if (md->colsum_per_head != 0 && md->colsum_per_head != 1)
         return fail(DLM_E_DESC, "colsum_per_head must be 0 or 1");
+    if (md->colsum_accumulate != 0 && md->colsum_accumulate != 1)
+        return fail(DLM_E_DESC, "colsum_accumulate must be 0 or 1");
     if (!(md->scale >= 0.f) || isinf(md->scale))
         return fail(DLM_E_DESC, "scale must be finite and >= 0 (0 selects 1/sqrt(D))");
     return DLM_OK;
@@ -181,6 +183,7 @@ int dlm_step_attn(const void *q, const void *k, const void *v, const dlm_kv_cach
     a.n_slots = md->kind == DLM_MASK_GROUP ? md->n_slots : 0;
     a.kind = md->kind;
     a.cs_lo = md->cs_lo; a.cs_hi = md->cs_hi; a.per_head = md->colsum_per_head;
+    a.accumulate = md->colsum_accumulate;
     const float scale = md->scale > 0.f ? md->scale : 1.f / sqrtf((float)kc->D);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.n_qtiles = p.n_qtiles; a.n_kgroups = p.n_kgroups; a.n_split = p.n_split; a.split_keys = p.split_keys;
@@ -197,11 +200,12 @@ static int check_post_scalars(int32_t R, int32_t V, const dlm_select *s)
     if (R < 0) return fail(DLM_E_SHAPE, "R=%d must be >= 0", R);
     if (V < 1) return fail(DLM_E_SHAPE, "V=%d must be >= 1", V);
     if ((long)R * V > (1L << 40)) return fail(DLM_E_SHAPE, "R*V too large");
-    if (s->mode < DLM_SEL_NONE || s->mode > DLM_SEL_TOPK_SCORE)
+    if (s->mode < DLM_SEL_NONE || s->mode > DLM_SEL_TOPK_LOW_ENTROPY)
         return fail(DLM_E_DESC, "unknown selection mode %d", s->mode);
     if (s->mode != DLM_SEL_NONE && (s->group_rows < 1 || s->group_rows > dlm::kMaxGroupRows))
         return fail(DLM_E_DESC, "group_rows=%d must be in [1, %d]", s->group_rows, dlm::kMaxGroupRows);
-    if ((s->mode == DLM_SEL_TOPK_CONF || s->mode == DLM_SEL_TOPK_SCORE) && s->k < 0)
+    if ((s->mode == DLM_SEL_TOPK_CONF || s->mode == DLM_SEL_TOPK_SCORE || s->mode == DLM_SEL_TOPK_MARGIN ||
+         s->mode == DLM_SEL_TOPK_LOW_ENTROPY) && s->k < 0)
         return fail(DLM_E_DESC, "k=%d must be >= 0", s->k);
     if ((s->mode == DLM_SEL_THRESH_CONF || s->mode == DLM_SEL_ATTN_DYNAMIC) && !isfinite(s->tau))
         return fail(DLM_E_DESC, "tau must be finite");
@@ -238,7 +242,7 @@ int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked
                     select->workspace ? select->workspace_bytes : (size_t)0);
     dlm::PostArgs a{};
     a.x = logits; a.y = prev_logits; a.locked = locked; a.score = select->score;
-    a.sel = sel; a.kl = kl; a.conf = conf;
+    a.sel = sel; a.kl = kl; a.conf = conf; a.margin = select->margin; a.entropy = select->entropy;
     a.part = static_cast<dlm::PostPartial *>(select->workspace);
     a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
     a.eps = eps; a.tau = select->tau; a.n_chunks = p.n_chunks; a.chunk = p.chunk;

@@ -42,7 +42,8 @@ struct AttnPlan {
 };
 AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap);
 
-// Per-row partial state of the posterior stream over one vocabulary chunk.
+// Per-row partial state of the posterior stream over one vocabulary chunk
+// (48 bytes: staged through LDS in 16-byte pieces).
 struct PostPartial {
     float mx;   // running max of logits x
     float sx;   // sum exp(x - mx)
@@ -50,9 +51,12 @@ struct PostPartial {
     float my;   // running max of previous logits y
     float sy;   // sum exp(y - my)
     float av;   // largest x seen
+    float a2;   // runner-up: largest x at any other index (= av on a tie)
+    float ex;   // sum exp(x - mx) * (x - mx)
     int ai;     // lowest index attaining av
-    int pad;
+    int pad[3];
 };
+static_assert(sizeof(PostPartial) % 16 == 0, "partials are staged in 16-byte pieces");
 
 struct PostPlan {
     int n_chunks;       // vocabulary chunks per row
@@ -72,7 +76,7 @@ struct AttnArgs {
     float *lse, *colsum;
     float *ws_o, *ws_l, *ws_cs;
     int B, Hq, Hkv, G, D, M, n_cap, kv_len, P, bs, n_slots, kind;
-    int cs_lo, cs_hi, per_head;
+    int cs_lo, cs_hi, per_head, accumulate;
     float scale_log2;               // softmax scale * log2(e)
     int n_qtiles, n_kgroups, n_split, split_keys, n_kblocks, n_rsplit;
 };
@@ -83,6 +87,7 @@ struct PostArgs {
     const float *score;
     int32_t *sel;
     float *kl, *conf;
+    float *margin, *entropy;        // optional outputs (nullptr: not written)
     PostPartial *part;
     int R, V, mode, k, group_rows;
     float eps, tau;

@@ -30,7 +30,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct RowState {
-    float mx, sx, tx, my, sy, av;
+    float mx, sx, tx, my, sy, av, a2, ex;
     int ai;
 };
 
@@ -38,15 +38,23 @@ __device__ __forceinline__ void rs_init(RowState &s)
 {
     s.mx = -INFINITY; s.sx = 0.f; s.tx = 0.f;
     s.my = -INFINITY; s.sy = 0.f;
-    s.av = -INFINITY; s.ai = INT_MAX;
+    s.av = -INFINITY; s.a2 = -INFINITY; s.ex = 0.f; s.ai = INT_MAX;
 }
 
-// Merge state b into a.  Both describe disjoint element sets.
+// Merge state b into a.  Both describe disjoint element sets.  SC: also
+// the runner-up and the entropy sum (margin / entropy requested).
+template <bool SC = true>
 __device__ __forceinline__ void rs_merge(RowState &a, const RowState &b)
 {
     float m = fmaxf(a.mx, b.mx);
     if (m != -INFINITY) {
         float ca = fast_exp2((a.mx - m) * kLog2e), cb = fast_exp2((b.mx - m) * kLog2e);
+        // ex is relative to each side's own max: shift it to m (a side with
+        // no element has sx = ex = 0)
+        if constexpr (SC) {
+            const float da = a.mx == -INFINITY ? 0.f : a.mx - m, db = b.mx == -INFINITY ? 0.f : b.mx - m;
+            a.ex = (a.ex + a.sx * da) * ca + (b.ex + b.sx * db) * cb;
+        }
         a.sx = a.sx * ca + b.sx * cb;
         a.tx = a.tx * ca + b.tx * cb;
     }
@@ -57,23 +65,30 @@ __device__ __forceinline__ void rs_merge(RowState &a, const RowState &b)
         a.sy = a.sy * ca + b.sy * cb;
     }
     a.my = my;
+    // runner-up of the union: the smaller of the two tops or either runner-up
+    if constexpr (SC) a.a2 = fmaxf(fminf(a.av, b.av), fmaxf(a.a2, b.a2));
     if (b.av > a.av || (b.av == a.av && b.ai < a.ai)) {
         a.av = b.av;
         a.ai = b.ai;
     }
 }
 
+template <bool SC = true>
 __device__ __forceinline__ RowState rs_shfl_xor(const RowState &s, int m)
 {
-    RowState o;
+    RowState o = s;
     o.mx = __shfl_xor(s.mx, m); o.sx = __shfl_xor(s.sx, m); o.tx = __shfl_xor(s.tx, m);
     o.my = __shfl_xor(s.my, m); o.sy = __shfl_xor(s.sy, m);
     o.av = __shfl_xor(s.av, m); o.ai = __shfl_xor(s.ai, m);
+    if constexpr (SC) {
+        o.a2 = __shfl_xor(s.a2, m);
+        o.ex = __shfl_xor(s.ex, m);
+    }
     return o;
 }
 
 // Fold a batch of n values (x[i], y[i]) at indices idx0 + stride*i into s.
-template <int N>
+template <bool SC, int N>
 __device__ __forceinline__ void rs_fold(RowState &s, const float (&x)[N], const float (&y)[N],
                                         const int (&idx)[N])
 {
@@ -81,21 +96,29 @@ __device__ __forceinline__ void rs_fold(RowState &s, const float (&x)[N], const 
     for (int i = 1; i < N; ++i) { bx = fmaxf(bx, x[i]); by = fmaxf(by, y[i]); }
     const float mx = fmaxf(s.mx, bx), my = fmaxf(s.my, by);
     const float cx = fast_exp2((s.mx - mx) * kLog2e), cy = fast_exp2((s.my - my) * kLog2e);
-    float sx = s.sx * cx, tx = s.tx * cx, sy = s.sy * cy;
+    const float dx = s.mx == -INFINITY ? 0.f : s.mx - mx;      // shift of ex to the new max
+    float sx = s.sx * cx, tx = s.tx * cx, sy = s.sy * cy, eh = (s.ex + s.sx * dx) * cx;
     const float mxl = mx * kLog2e, myl = my * kLog2e;
     for (int i = 0; i < N; ++i) {
         float ex = fast_exp2(fmaf(x[i], kLog2e, -mxl));
         sx += ex;
         tx = fmaf(ex, x[i] - y[i], tx);
         sy += fast_exp2(fmaf(y[i], kLog2e, -myl));
-        if (x[i] > s.av) { s.av = x[i]; s.ai = idx[i]; }
+        if constexpr (SC) {
+            eh = fmaf(ex, x[i] - mx, eh);
+            if (x[i] > s.av) { s.a2 = s.av; s.av = x[i]; s.ai = idx[i]; }
+            else s.a2 = fmaxf(s.a2, x[i]);
+        } else {
+            if (x[i] > s.av) { s.av = x[i]; s.ai = idx[i]; }
+        }
     }
     s.mx = mx; s.my = my; s.sx = sx; s.tx = tx; s.sy = sy;
+    if constexpr (SC) s.ex = eh;
 }
 
 // As rs_fold, over the elements with ok[i] set (at least one may be unset;
 // all may be).  A state that stays empty keeps mx = -inf without NaNs.
-template <int N>
+template <bool SC, int N>
 __device__ __forceinline__ void rs_fold_masked(RowState &s, const float (&x)[N], const float (&y)[N],
                                                const int (&idx)[N], const bool (&ok)[N])
 {
@@ -105,7 +128,8 @@ __device__ __forceinline__ void rs_fold_masked(RowState &s, const float (&x)[N],
     const float mx = fmaxf(s.mx, bx), my = fmaxf(s.my, by);
     const float cx = s.mx == mx ? 1.f : fast_exp2((s.mx - mx) * kLog2e);
     const float cy = s.my == my ? 1.f : fast_exp2((s.my - my) * kLog2e);
-    float sx = s.sx * cx, tx = s.tx * cx, sy = s.sy * cy;
+    const float dx = (s.mx == -INFINITY || s.mx == mx) ? 0.f : s.mx - mx;
+    float sx = s.sx * cx, tx = s.tx * cx, sy = s.sy * cy, eh = (s.ex + s.sx * dx) * cx;
     const float mxl = mx * kLog2e, myl = my * kLog2e;
     for (int i = 0; i < N; ++i) {
         if (!ok[i]) continue;
@@ -113,12 +137,19 @@ __device__ __forceinline__ void rs_fold_masked(RowState &s, const float (&x)[N],
         sx += ex;
         tx = fmaf(ex, x[i] - y[i], tx);
         sy += fast_exp2(fmaf(y[i], kLog2e, -myl));
-        if (x[i] > s.av) { s.av = x[i]; s.ai = idx[i]; }
+        if constexpr (SC) {
+            eh = fmaf(ex, x[i] - mx, eh);
+            if (x[i] > s.av) { s.a2 = s.av; s.av = x[i]; s.ai = idx[i]; }
+            else s.a2 = fmaxf(s.a2, x[i]);
+        } else {
+            if (x[i] > s.av) { s.av = x[i]; s.ai = idx[i]; }
+        }
     }
     s.mx = mx; s.my = my; s.sx = sx; s.tx = tx; s.sy = sy;
+    if constexpr (SC) s.ex = eh;
 }
 
-template <bool VEC4>
+template <bool VEC4, bool SC>
 __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs a)
 {
     const int row = blockIdx.x / a.n_chunks;
@@ -160,36 +191,37 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
                 is[4 * u + 0] = off; is[4 * u + 1] = off + 1; is[4 * u + 2] = off + 2; is[4 * u + 3] = off + 3;
             }
             if (full) {
-                rs_fold(s, xs, ys, is);
+                rs_fold<SC>(s, xs, ys, is);
             } else {
                 bool ok[4 * U];
                 for (int u = 0; u < U; ++u) {
                     const bool in = e + (u * kPostThreads + tid) * 4 < e1;   // e1 is a multiple of 4
                     ok[4 * u + 0] = in; ok[4 * u + 1] = in; ok[4 * u + 2] = in; ok[4 * u + 3] = in;
                 }
-                rs_fold_masked(s, xs, ys, is, ok);
+                rs_fold_masked<SC>(s, xs, ys, is, ok);
             }
         }
     } else {
         for (int off = e0 + tid; off < e1; off += kPostThreads) {
             float xs[1] = {x[off]}, ys[1] = {y[off]};
             int is[1] = {off};
-            rs_fold(s, xs, ys, is);
+            rs_fold<SC>(s, xs, ys, is);
         }
     }
 
     // Wave, then workgroup reduction (fixed shape: deterministic).
-    for (int m = 32; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
+    for (int m = 32; m >= 1; m >>= 1) rs_merge<SC>(s, rs_shfl_xor<SC>(s, m));
     __shared__ RowState red[kPostThreads / 64];
     const int wid = tid >> 6;
     if ((tid & 63) == 0) red[wid] = s;
     __syncthreads();
     if (tid == 0) {
         RowState t = red[0];
-        for (int w = 1; w < kPostThreads / 64; ++w) rs_merge(t, red[w]);
+        for (int w = 1; w < kPostThreads / 64; ++w) rs_merge<SC>(t, red[w]);
         PostPartial p;
         p.mx = t.mx; p.sx = t.sx; p.tx = t.tx; p.my = t.my; p.sy = t.sy;
-        p.av = t.av; p.ai = t.ai; p.pad = 0;
+        p.av = t.av; p.a2 = t.a2; p.ex = t.ex; p.ai = t.ai;
+        p.pad[0] = p.pad[1] = p.pad[2] = 0;
         a.part[(long)row * a.n_chunks + ch] = p;
     }
 }
@@ -204,7 +236,7 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
 // a fixed butterfly over the lanes combines them; larger groups merge one
 // row per thread.
 // The selection uses block-wide reductions, not a serial scan.
-constexpr int kStageBytes = 32768;
+constexpr int kStageBytes = 48 * 1024;   // 1024 partials of 48 bytes
 constexpr int kMergeLanes = 8;
 
 __device__ __forceinline__ float block_max(float v, float *red)
@@ -221,6 +253,7 @@ __device__ __forceinline__ RowState rs_load(const PostPartial &p)
 {
     RowState s;
     s.mx = p.mx; s.sx = p.sx; s.tx = p.tx; s.my = p.my; s.sy = p.sy; s.av = p.av; s.ai = p.ai;
+    s.a2 = p.a2; s.ex = p.ex;
     return s;
 }
 
@@ -267,16 +300,16 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         v4u *dst = reinterpret_cast<v4u *>(stage_s);
         const int n16 = nr * a.n_chunks * (int)(sizeof(PostPartial) / 16);
         if (r0 > 0) __syncthreads();
-        // up to eight 16-byte loads in flight per thread (the stage is 2048)
-        for (int i0 = 0; i0 < n16; i0 += 256 * 8) {
-            v4u v[8];
+        // up to twelve 16-byte loads in flight per thread (one round: the stage is 3072)
+        for (int i0 = 0; i0 < n16; i0 += 256 * 12) {
+            v4u v[12];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 12; ++u) {
                 const int i = i0 + u * 256 + tid;
                 v[u] = i < n16 ? src[i] : v4u{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < 12; ++u) {
                 const int i = i0 + u * 256 + tid;
                 if (i < n16) dst[i] = v[u];
             }
@@ -308,7 +341,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                 for (int m = lanes / 2; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
             if (row_ok && sub == 0) {
                 const int r = g0 + gt;
-                float klv = 0.f, cf = 0.f;
+                float klv = 0.f, cf = 0.f, mg = 0.f, en = 0.f;
                 int tok = -1;
                 if (!was_locked) {
                     // KL = t/sx - (mx + ln sx) + (my + ln sy)
@@ -316,12 +349,18 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                     cf = 1.f / s.sx;
                     tok = s.ai;
                     a.locked[r] = klv <= a.eps ? 1 : 0;
+                    // margin = p(top-1) - p(top-2) = conf * (1 - exp(a2 - mx)): exactly
+                    // 0 on a tie, conf without a runner-up; entropy = ln sx - ex / sx
+                    mg = cf * (1.f - fast_exp2((s.a2 - s.mx) * kLog2e));
+                    en = logf(s.sx) - s.ex / s.sx;
                 }
                 a.kl[r] = klv;
                 a.conf[r] = cf;
+                if (a.margin) a.margin[r] = mg;
+                if (a.entropy) a.entropy[r] = en;
                 conf_s[gt] = cf;
                 tok_s[gt] = tok;
-                if (!by_score) key_s[gt] = cf;
+                if (!by_score) key_s[gt] = a.mode == 5 ? mg : a.mode == 6 ? -en : cf;
             }
         }
     }
@@ -373,7 +412,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                 rank += (p.x > mine ? 1 : 0) + (p.y > mine ? 1 : 0);
             }
             bool pick = false;
-            if (a.mode == 1 || a.mode == 4) pick = rank < a.k;
+            if (a.mode == 1 || a.mode == 4 || a.mode == 5 || a.mode == 6) pick = rank < a.k;
             else if (a.mode == 2) pick = any ? conf_s[t] > a.tau : rank == 0;
             else if (a.mode == 3) pick = any ? (conf_s[t] > a.tau && kt > thr) : rank == 0;
             if (pick) out = tok_s[t];
@@ -388,10 +427,16 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t fi
 {
     if (a.R == 0) return hipSuccess;
     const long nwg = (long)a.R * a.n_chunks;
-    if ((a.V & 3) == 0)
-        posterior_stream_kernel<true><<<dim3((unsigned)nwg), dim3(kPostThreads), 0, stream>>>(a);
-    else
-        posterior_stream_kernel<false><<<dim3((unsigned)nwg), dim3(kPostThreads), 0, stream>>>(a);
+    // margin / entropy: only when an output or the selection needs them
+    const bool sc = a.margin || a.entropy || a.mode == 5 || a.mode == 6;
+    const dim3 grid((unsigned)nwg), block(kPostThreads);
+    if ((a.V & 3) == 0) {
+        if (sc) posterior_stream_kernel<true, true><<<grid, block, 0, stream>>>(a);
+        else posterior_stream_kernel<true, false><<<grid, block, 0, stream>>>(a);
+    } else {
+        if (sc) posterior_stream_kernel<false, true><<<grid, block, 0, stream>>>(a);
+        else posterior_stream_kernel<false, false><<<grid, block, 0, stream>>>(a);
+    }
     if (finish_after) {
         const hipError_t e = hipStreamWaitEvent(stream, finish_after, 0);
         if (e != hipSuccess) return e;

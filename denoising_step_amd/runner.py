@@ -25,7 +25,9 @@ def bf16_to_host(t: torch.Tensor) -> np.ndarray:
 
 
 class DeviceStep:
-    def __init__(self, workload, device="cuda", with_colsum=True, with_posterior=True):
+    def __init__(self, workload, device="cuda", with_colsum=True, with_posterior=True, with_scores=False):
+        """with_scores: also compute margin and entropy of p_t (always when the
+        selection mode ranks by them)."""
         a, p = workload.attn, workload.post
         self.workload = workload
         self.device = device
@@ -66,6 +68,8 @@ class DeviceStep:
             self.sel = torch.empty(p.R, dtype=torch.int32, device=dev)
             self.kl = torch.empty(p.R, dtype=torch.float32, device=dev)
             self.conf = torch.empty(p.R, dtype=torch.float32, device=dev)
+            self.margin = torch.empty(p.R, dtype=torch.float32, device=dev)
+            self.entropy = torch.empty(p.R, dtype=torch.float32, device=dev)
             score = None
             if p.score is not None:
                 score = torch.from_numpy(p.score).to(dev)
@@ -73,7 +77,11 @@ class DeviceStep:
                 b, first = p.score_cols
                 score = self.colsum[b, first:first + p.R]
             self.score = score
-            self.select = Select(mode=p.mode, k=p.k, group_rows=p.group_rows, tau=p.tau, score=score)
+            scores = with_scores or p.mode in (5, 6)
+            self.with_scores = scores
+            self.select = Select(mode=p.mode, k=p.k, group_rows=p.group_rows, tau=p.tau, score=score,
+                                 margin=self.margin if scores else None,
+                                 entropy=self.entropy if scores else None)
             ws = dlm_posterior_workspace_bytes(p.R, p.V, self.select)
             self.post_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
             self.select.workspace = self.post_ws
@@ -129,6 +137,8 @@ class DeviceStep:
         if self.with_posterior:
             r.update(sel=self.sel.cpu().numpy(), kl=self.kl.cpu().numpy(),
                      conf=self.conf.cpu().numpy(), locked=self.locked.cpu().numpy())
+            if self.with_scores:
+                r.update(margin=self.margin.cpu().numpy(), entropy=self.entropy.cpu().numpy())
             if self.score is not None:
                 r["score"] = self.score.cpu().numpy()
         return r

@@ -102,6 +102,10 @@ typedef struct {
     float scale;             /* softmax scale; 0 means 1/sqrt(D) */
     void *workspace;         /* device scratch, >= dlm_step_attn_workspace_bytes() */
     size_t workspace_bytes;
+    int32_t colsum_accumulate;   /* 0: colsum = the sums of this call; 1: colsum += them,
+                                    e.g. summed over the layers of a model (the
+                                    Attention-Based Sampler page, sec. 4, averages the
+                                    scores of all layers and heads; a sum ranks the same) */
 } dlm_mask_desc;
 
 /*
@@ -165,10 +169,16 @@ int dlm_step_attn_workspace_bytes(const dlm_kv_cache *kv_cache,
  *                decode candidates whose score exceeds it; if none, the
  *                eligible row of highest score.
  *  TOPK_SCORE    the k eligible rows of highest score (column-sum order).
+ *  TOPK_MARGIN   the k eligible rows of largest margin p(top-1) - p(top-2)
+ *                (margin sampler; sec. 1 names margin among the token-level
+ *                scores of the greedy samplers).
+ *  TOPK_LOW_ENTROPY  the k eligible rows of lowest entropy -sum p ln p
+ *                (entropy sampler; likewise sec. 1).
  * Eligible = not locked on entry.  Order: larger key first, then lower row
  * index.  If fewer than k rows are eligible, all are taken. */
 enum { DLM_SEL_NONE = 0, DLM_SEL_TOPK_CONF = 1, DLM_SEL_THRESH_CONF = 2,
-       DLM_SEL_ATTN_DYNAMIC = 3, DLM_SEL_TOPK_SCORE = 4 };
+       DLM_SEL_ATTN_DYNAMIC = 3, DLM_SEL_TOPK_SCORE = 4, DLM_SEL_TOPK_MARGIN = 5,
+       DLM_SEL_TOPK_LOW_ENTROPY = 6 };
 
 typedef struct {
     int32_t mode;            /* DLM_SEL_* */
@@ -185,6 +195,11 @@ typedef struct {
                                 an event after the dlm_step_attn producing the column
                                 sums and calls dlm_posterior on a second stream thus
                                 overlaps the logit stream with the attention passes. */
+    float *margin;           /* optional device fp32 [R] out (NULL: not written):
+                                p_t(top-1) - p_t(top-2); 0 on a tie and for rows locked
+                                on entry; p_t(top-1) when V == 1 */
+    float *entropy;          /* optional device fp32 [R] out (NULL: not written):
+                                -sum_v p_t(v) ln p_t(v); 0 for rows locked on entry */
 } dlm_select;
 
 /*

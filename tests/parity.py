@@ -21,6 +21,8 @@ LSE_TOL = 1e-3
 CS_REL, CS_ABS = 1e-3, 1e-6
 KL_TOL = 1e-4
 CONF_TOL = 1e-5
+MARGIN_TOL = 1e-5       # like conf: a difference of two fp32 probabilities
+ENTROPY_TOL = 1e-4      # like KL: ln sx - ex / sx from fp32 sums over the vocabulary
 TIE = 1e-4
 
 
@@ -65,7 +67,18 @@ def _tol(v, relative):
     return TIE * abs(v) if relative else TIE * max(1.0, abs(v))
 
 
-def check_selection(sel_g, sel_o, mode, group_rows, tau, conf_o, score_o, locked_in, logits):
+def check_scores(margin_g, entropy_g, margin_o, entropy_o, locked_in):
+    """Margin and entropy per row; rows locked on entry report zeros."""
+    lk = locked_in.astype(bool)
+    assert np.all(margin_g[lk] == 0) and np.all(entropy_g[lk] == 0), "locked rows must report 0"
+    dm = np.abs(margin_g.astype(np.float64) - margin_o)
+    de = np.abs(entropy_g.astype(np.float64) - entropy_o)
+    assert dm.max(initial=0) <= MARGIN_TOL, f"margin max-abs {dm.max()}"
+    assert de.max(initial=0) <= ENTROPY_TOL, f"entropy max-abs {de.max()}"
+
+
+def check_selection(sel_g, sel_o, mode, group_rows, tau, conf_o, score_o, locked_in, logits,
+                    margin_o=None, entropy_o=None):
     """Exact match of selected rows and tokens up to oracle ties.
     Returns the number of excused disagreements."""
     if mode == W.SEL_NONE:
@@ -73,7 +86,8 @@ def check_selection(sel_g, sel_o, mode, group_rows, tau, conf_o, score_o, locked
         return 0
     R = len(sel_o)
     by_score = mode in (W.SEL_ATTN_DYNAMIC, W.SEL_TOPK_SCORE)
-    key = score_o if by_score else conf_o
+    key = (score_o if by_score else margin_o if mode == W.SEL_TOPK_MARGIN else
+           -entropy_o if mode == W.SEL_TOPK_LOW_ENTROPY else conf_o)
     excused = 0
     for g0 in range(0, R, group_rows):
         rows = np.arange(g0, min(R, g0 + group_rows))

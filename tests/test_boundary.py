@@ -86,6 +86,7 @@ def test_workspace_queries():
     (dict(md=_md(kind=dlm.MASK_GROUP, block_size=16, n_slots=5, slot_state=FAKE, slot_group=FAKE)), dlm.DLM_E_DESC),
     (dict(md=_md(cs_lo=50, cs_hi=40)), dlm.DLM_E_DESC),
     (dict(md=_md(colsum_per_head=2)), dlm.DLM_E_DESC),
+    (dict(md=_md(colsum_accumulate=2)), dlm.DLM_E_DESC),
     (dict(md=_md(scale=-1.0)), dlm.DLM_E_DESC),
     (dict(md=_md(scale=float("nan"))), dlm.DLM_E_DESC),
     (dict(q=None), dlm.DLM_E_NULL),
@@ -141,6 +142,9 @@ def _post(R=16, V=512, sel=None, logits=FAKE, prev=FAKE, locked=FAKE, out=FAKE, 
     (dict(R=-1), dlm.DLM_E_SHAPE),
     (dict(V=0), dlm.DLM_E_SHAPE),
     (dict(sel=dlm.Select(mode=9)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=7)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_MARGIN, k=-1, group_rows=16)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_LOW_ENTROPY, k=-3, group_rows=16)), dlm.DLM_E_DESC),
     (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=2, group_rows=0)), dlm.DLM_E_DESC),
     (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=2, group_rows=1025)), dlm.DLM_E_DESC),
     (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=-1, group_rows=16)), dlm.DLM_E_DESC),

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import (check_attention, check_colsum, check_posterior, check_selection)
+from parity import (check_attention, check_colsum, check_posterior, check_scores, check_selection)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,9 +102,11 @@ def small_long(seed=0):
 
 
 def full_check(w, check_cache=True):
+    """Everything against the oracle, margin and entropy included (the
+    score-tracking variant of the posterior stream)."""
     _say(f"case: {w.attn.name} / {w.post.name}")
     ora = oracle.step(w)
-    ds = _device_step(w)
+    ds = _device_step(w, with_scores=True)
     ds.run()
     g = ds.results()
     if check_cache:
@@ -115,8 +117,9 @@ def full_check(w, check_cache=True):
     p = w.post
     lk_exc = check_posterior(g["kl"], g["conf"], g["locked"], ora["kl"], ora["conf"], ora["locked"],
                              p.eps, p.locked)
+    check_scores(g["margin"], g["entropy"], ora["margin"], ora["entropy"], p.locked)
     sel_exc = check_selection(g["sel"], ora["sel"], p.mode, p.group_rows, p.tau, ora["conf"],
-                              ora["score"], p.locked, p.logits)
+                              ora["score"], p.locked, p.logits, ora["margin"], ora["entropy"])
     _say(f"  excused: locks {lk_exc}, selections {sel_exc}")
     return ds, g, ora
 
@@ -186,6 +189,20 @@ def test_overlapped_step_equals_serial(case):
         r2 = ds.results()
         for k in ("out", "lse", "colsum", "kl", "conf", "sel", "locked", "cache_k", "cache_v"):
             assert np.array_equal(r1[k], r2[k], equal_nan=False), (rep, k)
+
+
+def test_posterior_stream_variants_agree():
+    """The stream kernel without margin / entropy tracking gives the same
+    KL, confidence, tokens, locks and selection, bit for bit."""
+    w = small_llada(spread=True, seed=8)
+    _say("case: posterior variants")
+    r = []
+    for scores in (True, False):
+        ds = _device_step(w, with_scores=scores)
+        ds.run()
+        r.append(ds.results())
+    for k in ("kl", "conf", "sel", "locked"):
+        assert np.array_equal(r[0][k], r[1][k]), k
 
 
 def test_deterministic():
@@ -283,6 +300,85 @@ def test_posterior_edge_cases():
                         locked, np.nan_to_num(x))
         assert kl.cpu().numpy()[5] == 0.0 or abs(kl.cpu().numpy()[5]) < 1e-6
         assert np.all(sel.cpu().numpy()[locked == 1] == -1)
+
+
+@pytest.mark.parametrize("V", [1, 1003, 6000])
+def test_margin_entropy_samplers(V):
+    """Margin and entropy of p_t and the two token-level samplers that rank
+    by them (top-k by largest margin, top-k by lowest entropy), with rows
+    whose maximum repeats (margin 0), near-certain rows and locked rows."""
+    import denoising_step_amd as dlm
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(40 + V)
+    R = 70
+    x = (rng.standard_normal((R, V)) * np.linspace(0.2, 6.0, R)[:, None]).astype(np.float32)
+    if V > 3:
+        x[5, [3, V - 2]] = x[5].max() + 1.0      # repeated maximum: margin 0
+        x[9, 0] = 40.0                            # near-certain row
+    y = (x + rng.standard_normal((R, V)) * 0.05).astype(np.float32)
+    locked = (rng.random(R) < 0.15).astype(np.uint8)
+    x[locked == 1] = np.nan                       # never read
+    y[locked == 1] = np.nan
+    ora = oracle.posterior(x, y, locked, 1e-3)
+    for mode, k, g in [(W.SEL_TOPK_MARGIN, 3, 10), (W.SEL_TOPK_LOW_ENTROPY, 2, 7),
+                       (W.SEL_TOPK_MARGIN, 100, 70), (W.SEL_TOPK_LOW_ENTROPY, 1, 1)]:
+        _say(f"case: samplers V={V} mode={mode} k={k} group={g}")
+        mg = torch.full((R,), float("nan"), device=dev)
+        en = torch.full((R,), float("nan"), device=dev)
+        s = dlm.Select(mode=mode, k=k, group_rows=g, margin=mg, entropy=en)
+        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device=dev)
+        lk = torch.from_numpy(locked.copy()).to(dev)
+        sel = torch.empty(R, dtype=torch.int32, device=dev)
+        kl = torch.empty(R, dtype=torch.float32, device=dev)
+        conf = torch.empty(R, dtype=torch.float32, device=dev)
+        dlm.dlm_posterior(torch.from_numpy(x).to(dev), torch.from_numpy(y).to(dev), lk, 1e-3, s,
+                          sel, kl, conf, R, V)
+        torch.cuda.synchronize()
+        check_scores(mg.cpu().numpy(), en.cpu().numpy(), ora["margin"], ora["entropy"], locked)
+        if V > 3:
+            assert mg.cpu().numpy()[5] == 0.0 and ora["margin"][5] == 0.0
+        sel_o = oracle.select(mode, k, g, 0.0, None, ora["conf"], ora["tok"], locked,
+                              ora["margin"], ora["entropy"])
+        exc = check_selection(sel.cpu().numpy(), sel_o, mode, g, 0.0, ora["conf"], None, locked,
+                              np.nan_to_num(x), ora["margin"], ora["entropy"])
+        _say(f"  excused {exc}")
+
+
+def test_colsum_accumulates_over_layers():
+    """colsum_accumulate = 1 adds a call's column sums to the buffer: three
+    layers (different queries over the same cache) against the sum of the
+    oracle's per-layer sums; a call with no active rows leaves it as is."""
+    import denoising_step_amd as dlm
+    base = small_mbd("two_groups", seed=7)
+    a = base.attn
+    rng = np.random.default_rng(77)
+    layers = []
+    for l in range(3):
+        q = W.to_bf16_bits(rng.standard_normal(a.q.shape) * (0.5 + 0.5 * l))
+        layers.append(W.AttnCase(**{**a.__dict__, "q": q}))
+    want = sum(oracle.colsum(c, oracle.attention(c)[1]) for c in layers)
+    ds = _device_step(W.Workload(layers[0], base.post, "layer 0"), with_posterior=False)
+    for l, c in enumerate(layers):
+        _say(f"case: accumulate layer {l}")
+        from denoising_step_amd.runner import bf16_to_device
+        ds.q = bf16_to_device(c.q, torch.device("cuda"))
+        ds.md.colsum_accumulate = 0 if l == 0 else 1
+        ds.run_attn()
+    torch.cuda.synchronize()
+    check_colsum(ds.colsum.cpu().numpy(), want)
+    before = ds.colsum.clone()
+    md0 = dlm.MaskDesc(kind=a.kind, Hq=a.Hq, M=0, kv_len=a.kv_len, prefix_len=a.prefix_len,
+                       block_size=a.block_size, n_slots=a.n_slots, slot_state=ds.md.slot_state,
+                       slot_group=ds.md.slot_group, cs_lo=a.cs_lo, cs_hi=a.cs_hi, colsum_accumulate=1)
+    md0.workspace = torch.empty(max(1, dlm.dlm_step_attn_workspace_bytes(ds.kv, md0)), dtype=torch.uint8,
+                                device="cuda")
+    D = a.D
+    dlm.dlm_step_attn(torch.empty((a.B, a.Hq, 0, D), dtype=torch.bfloat16, device="cuda"), None, None, ds.kv,
+                      torch.empty((a.B, 0), dtype=torch.int32, device="cuda"), md0,
+                      torch.empty((a.B, a.Hq, 0, D), dtype=torch.bfloat16, device="cuda"),
+                      torch.empty((a.B, a.Hq, 0), dtype=torch.float32, device="cuda"), ds.colsum)
+    torch.cuda.synchronize()
+    assert torch.equal(ds.colsum, before)
 
 
 # --------------------------------------------------------------------------
