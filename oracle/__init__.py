@@ -4,13 +4,16 @@ TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package; the GPU library and
 its Python binding never do.  The oracle shares no code with the GPU path.
 
-The arithmetic lives in ``dlm_oracle.c`` (plain C, fp64, OpenMP over
-independent rows); this module only marshals numpy arrays into it.  Each
-function states the passage it follows.
+The arithmetic of one step lives in ``dlm_oracle.c`` (plain C, fp64, OpenMP
+over independent rows); this module only marshals numpy arrays into it.
+``block_buffer`` (the Block Buffer state machine and the compaction of the
+rows to compute) and ``loop`` (the multi-step run that composes them with
+the step) are plain Python.  Each function states the passage it follows.
 
 Parity status: every function here is pinned by the CPU tests in
-``tests/test_oracle_pins.py`` against library routines (torch SDPA, scipy),
-hand-worked fixtures under ``tests/golden/`` and invariants.
+``tests/test_oracle_pins.py`` and ``tests/test_oracle_loop_pins.py`` against
+library routines (torch SDPA, scipy, numpy), hand-worked fixtures under
+``tests/golden/`` and invariants.
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ _SRC = os.path.join(_HERE, "dlm_oracle.c")
 _LIB = os.path.join(_HERE, "libdlm_oracle.so")
 
 MASK_FULL, MASK_BLOCK_CAUSAL, MASK_GROUP = 0, 1, 2
+ROW_SELECT, ROW_LOCK = 1, 2      # per-row flags of posterior() / select()
 
 
 def build(force: bool = True) -> str:
@@ -59,9 +63,9 @@ def _load():
         lib.ora_colsum.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, P, P,
                                    Dd, I, I, I, P, L, P, P]
         lib.ora_colsum.restype = None
-        lib.ora_posterior.argtypes = [P, P, P, L, L, Dd, L, P, P, P, P, P, P, P]
+        lib.ora_posterior.argtypes = [P, P, P, L, L, Dd, L, P, P, P, P, P, P, P, P]
         lib.ora_posterior.restype = None
-        lib.ora_select.argtypes = [I, I, I, Dd, P, P, P, P, I, P, P, P]
+        lib.ora_select.argtypes = [I, I, I, Dd, P, P, P, P, I, P, P, P, P]
         lib.ora_select.restype = None
         lib.ora_num_threads.argtypes = []
         lib.ora_num_threads.restype = I
@@ -161,10 +165,11 @@ def colsum(case, lse_all, kv=None, cols=None):
     return res
 
 
-def posterior(logits, prev, locked, eps, rows=None):
+def posterior(logits, prev, locked, eps, rows=None, flags=None):
     """Per-row KL(p_t || p_{t-1}), confidence, argmax token and lock flag
     (SureLock section 2), and the margin p(top-1) - p(top-2) and entropy of
     p_t (the token-level scores named on the Attn-Sampler page, section 1).
+    flags (uint8 [R] or None): only rows with bit ROW_LOCK may lock.
     Returns dict of kl, conf, tok, locked (new), margin, entropy."""
     lib = _load()
     logits = _c(logits, np.float32)
@@ -179,14 +184,17 @@ def posterior(logits, prev, locked, eps, rows=None):
     lk = np.empty(n, np.uint8)
     margin = np.empty(n, np.float64)
     entropy = np.empty(n, np.float64)
+    flags_a = None if flags is None else _c(flags, np.uint8)
     lib.ora_posterior(_p(logits), _p(prev), _p(locked), R, V, float(eps), n, _p(rows_a),
-                      _p(kl), _p(conf), _p(tok), _p(lk), _p(margin), _p(entropy))
+                      _p(kl), _p(conf), _p(tok), _p(lk), _p(margin), _p(entropy), _p(flags_a))
     return {"kl": kl, "conf": conf, "tok": tok, "locked": lk, "margin": margin, "entropy": entropy}
 
 
-def select(mode, k, group_rows, tau, score, conf, tok, locked_in, margin=None, entropy=None):
+def select(mode, k, group_rows, tau, score, conf, tok, locked_in, margin=None, entropy=None,
+           flags=None):
     """Unmask selection per group of rows (confidence top-k / threshold,
     Attn-Sampler order and dynamic threshold, margin and entropy samplers).
+    flags (uint8 [R] or None): only rows with bit ROW_SELECT are eligible.
     Returns sel int32 [R]."""
     lib = _load()
     conf = _c(conf, np.float64)
@@ -198,7 +206,7 @@ def select(mode, k, group_rows, tau, score, conf, tok, locked_in, margin=None, e
     sel = np.empty(R, np.int32)
     lib.ora_select(int(mode), int(k), int(group_rows), float(tau), _p(score_a), _p(conf),
                    _p(_c(tok, np.int32)), _p(_c(locked_in, np.uint8)), R, _p(sel),
-                   _p(margin_a), _p(entropy_a))
+                   _p(margin_a), _p(entropy_a), _p(None if flags is None else _c(flags, np.uint8)))
     return sel
 
 

@@ -35,6 +35,7 @@
 
 enum { ORA_FULL = 0, ORA_BLOCK_CAUSAL = 1, ORA_GROUP = 2 };
 enum { ORA_DUMMY = 0 };
+enum { ORA_ROW_SELECT = 1, ORA_ROW_LOCK = 2 };
 enum { ORA_SEL_NONE = 0, ORA_SEL_TOPK_CONF = 1, ORA_SEL_THRESH_CONF = 2,
        ORA_SEL_ATTN_DYNAMIC = 3, ORA_SEL_TOPK_SCORE = 4, ORA_SEL_TOPK_MARGIN = 5,
        ORA_SEL_TOPK_LOW_ENTROPY = 6 };
@@ -251,7 +252,8 @@ void ora_colsum(const uint16_t *q, const uint16_t *Kc, const int32_t *active_idx
 void ora_posterior(const float *logits, const float *prev, const uint8_t *locked_in,
                    int64_t R, int64_t V, double eps, int64_t n_rows,
                    const int64_t *rows, double *kl, double *conf, int32_t *tok,
-                   uint8_t *locked_out, double *margin, double *entropy)
+                   uint8_t *locked_out, double *margin, double *entropy,
+                   const uint8_t *flags)
 {
     if (rows == NULL)
         n_rows = R;
@@ -295,7 +297,11 @@ void ora_posterior(const float *logits, const float *prev, const uint8_t *locked
         kl[t] = d;
         conf[t] = exp(mx - Lx);
         tok[t] = (int32_t)arg;
-        locked_out[t] = (uint8_t)(d <= eps);
+        /* The lock test (KL <= eps) applies to rows the caller marks
+         * lockable (flags bit 1; every row when flags is NULL).  SureLock
+         * section 2: converged, already unmasked tokens are the ones whose
+         * computation stops. */
+        locked_out[t] = (uint8_t)(d <= eps && (flags == NULL || (flags[r] & ORA_ROW_LOCK)));
         /* Token-level scores of the confidence family (Attn-Sampler page,
          * section 1: confidence, margin, entropy).  margin = p(top-1) -
          * p(top-2), the runner-up being the largest logit at any other
@@ -317,8 +323,9 @@ void ora_posterior(const float *logits, const float *prev, const uint8_t *locked
 
 /* ------------------------------------------------------------------------
  * Unmask selection over consecutive groups of group_rows rows.  Only rows
- * that arrived unlocked are eligible.  Order: higher key first, then lower
- * row index.
+ * that arrived unlocked, and that the caller marks selectable (flags bit 0;
+ * every row when flags is NULL: a still-masked token), are eligible.
+ * Order: higher key first, then lower row index.
  *  TOPK_CONF:    the k most confident eligible rows (all if fewer).
  *  THRESH_CONF:  eligible rows with conf > tau; if none, the most
  *                confident eligible row.
@@ -344,7 +351,8 @@ static int cmp_desc(const void *a, const void *b)
 
 void ora_select(int mode, int k, int group_rows, double tau, const double *score,
                 const double *conf, const int32_t *tok, const uint8_t *locked_in,
-                int R, int32_t *sel, const double *margin, const double *entropy)
+                int R, int32_t *sel, const double *margin, const double *entropy,
+                const uint8_t *flags)
 {
     int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)(group_rows > 0 ? group_rows : 1));
     /* lowest entropy first: rank by the negated entropy */
@@ -362,7 +370,7 @@ void ora_select(int mode, int k, int group_rows, double tau, const double *score
         int g1 = g0 + group_rows < R ? g0 + group_rows : R;
         int n = 0;
         for (int r = g0; r < g1; ++r)
-            if (!locked_in[r])
+            if (!locked_in[r] && (flags == NULL || (flags[r] & ORA_ROW_SELECT)))
                 order[n++] = r;
         if (n == 0)
             continue;

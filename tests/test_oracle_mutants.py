@@ -35,8 +35,10 @@ MUTANTS = [
      "return group[slot_n] == group[slot_i];", [pins.test_visibility_golden]),
     ("dummy_visible", "if (state[slot_n] == ORA_DUMMY)\n        return 0;", "",
      [pins.test_visibility_golden]),
-    ("lock_strict", "locked_out[t] = (uint8_t)(d <= eps);", "locked_out[t] = (uint8_t)(d < eps);",
+    ("lock_strict", "locked_out[t] = (uint8_t)(d <= eps &&", "locked_out[t] = (uint8_t)(d < eps &&",
      [pins.test_lock_threshold_is_inclusive]),
+    ("lock_ignores_row_flags", "(d <= eps && (flags == NULL || (flags[r] & ORA_ROW_LOCK)))",
+     "(d <= eps)", [pins.test_lock_respects_row_flags]),
     ("argmax_last", "if ((double)x[v] > mx) {", "if ((double)x[v] >= mx) {",
      [pins.test_posterior_golden]),
     ("colsum_unnormalised", "head_sum += exp(scale * dot - L);", "head_sum += exp(scale * dot);",
@@ -51,8 +53,10 @@ MUTANTS = [
      [pins.test_selection_golden, pins.test_selection_brute_force]),
     ("thresh_conf_inclusive", "if (conf[order[t]] > tau) {", "if (conf[order[t]] >= tau) {",
      [pins.test_selection_golden]),
-    ("select_ignores_locks", "if (!locked_in[r])\n                order[n++] = r;",
-     "order[n++] = r;", [pins.test_selection_golden]),
+    ("select_ignores_locks", "if (!locked_in[r] && (flags == NULL",
+     "if ((flags == NULL", [pins.test_selection_golden]),
+    ("select_ignores_row_flags", "(flags == NULL || (flags[r] & ORA_ROW_SELECT))", "1",
+     [pins.test_selection_brute_force]),
     ("entropy_in_bits", "h -= exp(logp) * logp;", "h -= exp(logp) * logp / log(2.0);",
      [pins.test_margin_entropy_vs_library, pins.test_margin_entropy_closed_forms]),
     ("margin_drops_runner_up", "margin[t] = exp(mx - Lx) - (x2 == -INFINITY ? 0.0 : exp(x2 - Lx));",

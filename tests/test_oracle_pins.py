@@ -348,6 +348,25 @@ def test_lock_threshold_is_inclusive():
         assert at["locked"][0] == 1 and below["locked"][0] == 0
 
 
+def test_lock_respects_row_flags():
+    """Only rows marked lockable may lock (SureLock section 2: converged,
+    already unmasked tokens stop); KL itself is unchanged by the flags."""
+    from scipy.special import rel_entr, softmax
+    rng = np.random.default_rng(15)
+    R, V = 24, 300
+    x = (rng.standard_normal((R, V)) * 2).astype(np.float32)
+    noise = np.where(np.arange(R)[:, None] % 2 == 0, 0.01, 0.5)
+    y = (x + rng.standard_normal((R, V)) * noise).astype(np.float32)
+    flags = rng.integers(0, 4, R).astype(np.uint8)
+    r = oracle.posterior(x, y, np.zeros(R, np.uint8), 1e-3, flags=flags)
+    kl = np.array([rel_entr(softmax(x[i].astype(np.float64)),
+                            softmax(y[i].astype(np.float64))).sum() for i in range(R)])
+    assert np.allclose(r["kl"], kl, rtol=1e-9, atol=1e-12)
+    want = (kl <= 1e-3) & ((flags & oracle.ROW_LOCK) != 0)
+    assert np.array_equal(r["locked"].astype(bool), want)
+    assert want.any() and ((kl <= 1e-3) & ~want).any()     # both branches exercised
+
+
 def test_locked_rows_not_recomputed():
     rng = np.random.default_rng(6)
     x = (rng.standard_normal((8, 300))).astype(np.float32)
@@ -376,15 +395,19 @@ def test_selection_golden():
         assert sel.tolist() == c["sel"], c["cite"]
 
 
-def _brute_select(mode, k, g, tau, score, conf, tok, locked, margin=None, entropy=None):
+def _brute_select(mode, k, g, tau, score, conf, tok, locked, margin=None, entropy=None,
+                  flags=None):
     """Brute force: sort each group with numpy.lexsort; the dynamic threshold
-    uses its equivalent walk (descending score, longest run of candidates)."""
+    uses its equivalent walk (descending score, longest run of candidates).
+    Rows without the selectable flag are left out like locked rows."""
     R = len(conf)
     sel = np.full(R, -1, np.int32)
     if mode == W.SEL_NONE:
         return sel
     for g0 in range(0, R, g):
-        rows = np.array([r for r in range(g0, min(R, g0 + g)) if not locked[r]], np.int64)
+        rows = np.array([r for r in range(g0, min(R, g0 + g))
+                         if not locked[r] and (flags is None or flags[r] & oracle.ROW_SELECT)],
+                        np.int64)
         if rows.size == 0:
             continue
         key = (score if mode in (W.SEL_TOPK_SCORE, W.SEL_ATTN_DYNAMIC) else
@@ -426,8 +449,9 @@ def test_selection_brute_force():
         entropy = np.round(rng.random(R) * 3, 1)
         tok = rng.integers(0, 1000, R).astype(np.int32)
         locked = (rng.random(R) < 0.3).astype(np.uint8)
-        got = oracle.select(mode, k, g, tau, score, conf, tok, locked, margin, entropy)
-        ref = _brute_select(mode, k, g, tau, score, conf, tok, locked, margin, entropy)
+        flags = rng.integers(0, 4, R).astype(np.uint8) if trial % 2 else None
+        got = oracle.select(mode, k, g, tau, score, conf, tok, locked, margin, entropy, flags)
+        ref = _brute_select(mode, k, g, tau, score, conf, tok, locked, margin, entropy, flags)
         assert np.array_equal(got, ref), (trial, mode)
 
 

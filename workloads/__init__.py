@@ -370,6 +370,127 @@ def long_prefix_sampler(seed=0, P=16384, gen=256, H=32, D=128, V=151936) -> Work
     return Workload(a, p, "long-prefix Attn-Sampler, P=16384 + 256-token block")
 
 
+# --------------------------------------------------------------------------
+# Multi-step runs (Block Buffer loop)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LoopCase:
+    """Inputs of a multi-step denoising run over a Block Buffer.  The model
+    that would produce each step's queries, fresh K/V and logits is not part
+    of the path: these stand in for it, for every generation position and
+    step (a step reads the entries of the rows it computes)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    prefix_len: int             # clean prompt rows in the cache
+    block_size: int
+    n_slots: int                # generation region = n_slots * block_size positions
+    max_active: int             # running-set size (most active slots at once)
+    T: int                      # steps drawn
+    V: int
+    eps: float
+    mode: int
+    k: int
+    tau: float
+    cache_k: np.ndarray         # bf16 bits [B, Hkv, kv_len, D]
+    cache_v: np.ndarray
+    q: np.ndarray               # bf16 bits [T, B, Hq, n_gen, D]
+    k_new: np.ndarray           # bf16 bits [T, B, Hkv, n_gen, D]
+    v_new: np.ndarray
+    logits: np.ndarray          # float32 [T, B, n_gen, V]
+    decoded0: np.ndarray        # uint8 [B, n_gen]: positions unmasked at the start
+    tokens0: np.ndarray         # int32 [B, n_gen]
+
+    @property
+    def n_gen(self) -> int:
+        return self.n_slots * self.block_size
+
+    @property
+    def kv_len(self) -> int:
+        return self.prefix_len + self.n_gen
+
+
+def make_loop(name, *, B, Hq, Hkv, D, P, block_size, n_slots, max_active, T, V,
+              eps=1e-3, mode=SEL_TOPK_CONF, k=2, tau=0.9, logit_std=3.0,
+              noise_std=1.0, decay=(0.5, 0.75), qkv_std=None, n_decoded0=0,
+              config_id=90, seed=0) -> LoopCase:
+    """Draw a run.  Queries and fresh K/V are N(0, qkv_std) per step and
+    position (default 1/sqrt(D)); the clean prompt's cache rows likewise,
+    and the generation rows of the cache hold garbage N(0, 50) until a step
+    writes them.  Logits of position p at step t are
+        base[p] + noise_std * decay[p]**t * xi[t, p],
+    base ~ N(0, logit_std), xi ~ N(0, 1) fresh each step and decay[p]
+    uniform in ``decay``: each position's posterior settles geometrically at
+    its own rate, so rows lock at different steps.  The first ``n_decoded0``
+    positions of each sequence start unmasked (a prompt recomputed each
+    step) with their base argmax as token."""
+    rs = _streams(config_id, seed)
+    n_gen = n_slots * block_size
+    kv_len = P + n_gen
+    std = (1.0 / np.sqrt(D)) if qkv_std is None else qkv_std
+    q = _normal_bf16(rs["q"], (T, B, Hq, n_gen, D), std)
+    kn = _normal_bf16(rs["k"], (T, B, Hkv, n_gen, D), std)
+    vn = _normal_bf16(rs["v"], (T, B, Hkv, n_gen, D), std)
+    ck = rs["cache_k"].standard_normal(size=(B, Hkv, kv_len, D), dtype=np.float32) * np.float32(std)
+    cv = rs["cache_v"].standard_normal(size=(B, Hkv, kv_len, D), dtype=np.float32) * np.float32(std)
+    ck[:, :, P:] *= np.float32(50.0 / std)
+    cv[:, :, P:] *= np.float32(50.0 / std)
+    lg = rs["logits"]
+    base = lg.standard_normal(size=(B, n_gen, V), dtype=np.float32) * np.float32(logit_std)
+    rate = rs["mixture"].uniform(decay[0], decay[1], size=(B, n_gen))
+    nz = rs["noise"]
+    logits = np.empty((T, B, n_gen, V), np.float32)
+    for t in range(T):
+        amp = (noise_std * rate ** t).astype(np.float32)
+        logits[t] = base + amp[:, :, None] * nz.standard_normal(size=(B, n_gen, V), dtype=np.float32)
+    dec0 = np.zeros((B, n_gen), np.uint8)
+    tok0 = np.full((B, n_gen), -1, np.int32)
+    dec0[:, :n_decoded0] = 1
+    tok0[:, :n_decoded0] = np.argmax(base[:, :n_decoded0], axis=-1)
+    return LoopCase(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, prefix_len=P, block_size=block_size,
+                    n_slots=n_slots, max_active=max_active, T=T, V=V, eps=eps, mode=mode,
+                    k=k, tau=tau, cache_k=to_bf16_bits(ck), cache_v=to_bf16_bits(cv),
+                    q=q, k_new=kn, v_new=vn, logits=logits, decoded0=dec0, tokens0=tok0)
+
+
+def loop_multiblock(seed=0) -> LoopCase:
+    """Multi-block run: B=2, GQA 4/2 heads of width 64, a 48-row prompt in
+    the cache, four 16-token blocks with a running set of two, vocab 1000,
+    the top-2 by confidence unmasked per block and step, eps 1e-3."""
+    return make_loop("loop_multiblock", B=2, Hq=4, Hkv=2, D=64, P=48, block_size=16,
+                     n_slots=4, max_active=2, T=24, V=1000, mode=SEL_TOPK_CONF, k=2,
+                     config_id=91, seed=seed)
+
+
+def loop_surelock(seed=0) -> LoopCase:
+    """SureLock-style run: B=1, 2 heads of width 128, no cached prefix, one
+    80-position block of which the first 32 are an unmasked prompt that is
+    recomputed until it locks; Attn-Sampler dynamic threshold (tau 0.5,
+    scored by column sums), vocab 1003 (not a multiple of 4)."""
+    return make_loop("loop_surelock", B=1, Hq=2, Hkv=2, D=128, P=0, block_size=80,
+                     n_slots=1, max_active=1, T=64, V=1003, mode=SEL_ATTN_DYNAMIC, tau=0.5,
+                     n_decoded0=32, config_id=92, seed=seed)
+
+
+def loop_threshold(seed=0) -> LoopCase:
+    """Six 8-token blocks, three running, GQA 8/2 heads of width 32, a
+    40-row prompt, confidence threshold 0.3 (the single most confident row
+    when none passes), vocab 512."""
+    return make_loop("loop_threshold", B=1, Hq=8, Hkv=2, D=32, P=40, block_size=8,
+                     n_slots=6, max_active=3, T=40, V=512, mode=SEL_THRESH_CONF, tau=0.3,
+                     config_id=93, seed=seed)
+
+
+LOOPS = {
+    "loop_multiblock": loop_multiblock,
+    "loop_surelock": loop_surelock,
+    "loop_threshold": loop_threshold,
+}
+
+
 CONFIGS = {
     "tiny": tiny,
     "llada_bidirectional": llada_bidirectional,
