@@ -1,7 +1,8 @@
 """MI355X-native denoising step: Python binding of libdlm_step.so.
 
 The binding only marshals arguments into the C ABI of include/dlm_step.h
-(``dlm_step_attn``, ``dlm_posterior`` and their workspace queries); every
+(``dlm_step_attn``, ``dlm_posterior``, their workspace queries and the Block
+Buffer calls ``dlm_block_buffer_init`` / ``dlm_block_buffer_advance``); every
 step of the computation runs in the library's HIP kernels.  Tensors are
 PyTorch device tensors, used for memory and streams only.  It checks tensor
 shapes, dtypes and contiguity against the declared sizes so that a
@@ -26,9 +27,11 @@ MASK_FULL, MASK_BLOCK_CAUSAL, MASK_GROUP = 0, 1, 2
 SLOT_DUMMY, SLOT_ACTIVE, SLOT_TO_CACHE, SLOT_IN_CACHE = 0, 1, 2, 3
 SEL_NONE, SEL_TOPK_CONF, SEL_THRESH_CONF, SEL_ATTN_DYNAMIC, SEL_TOPK_SCORE = 0, 1, 2, 3, 4
 SEL_TOPK_MARGIN, SEL_TOPK_LOW_ENTROPY = 5, 6
+ROW_SELECT, ROW_LOCK = 1, 2
 
 EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
-           "dlm_posterior_workspace_bytes", "dlm_last_error")
+           "dlm_posterior_workspace_bytes", "dlm_block_buffer_init", "dlm_block_buffer_advance",
+           "dlm_last_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -76,7 +79,7 @@ class _MaskDesc(ctypes.Structure):
                 ("cs_lo", ctypes.c_int32), ("cs_hi", ctypes.c_int32),
                 ("colsum_per_head", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("colsum_accumulate", ctypes.c_int32)]
+                ("colsum_accumulate", ctypes.c_int32), ("m_active", ctypes.c_void_p)]
 
 
 class _Select(ctypes.Structure):
@@ -84,7 +87,17 @@ class _Select(ctypes.Structure):
                 ("tau", ctypes.c_float), ("score", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("score_ready", ctypes.c_void_p), ("margin", ctypes.c_void_p),
-                ("entropy", ctypes.c_void_p)]
+                ("entropy", ctypes.c_void_p), ("row_flags", ctypes.c_void_p)]
+
+
+class _BlockBuffer(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_active", ctypes.c_int32), ("prefix_len", ctypes.c_int32),
+                ("slot_state", ctypes.c_void_p), ("slot_group", ctypes.c_void_p),
+                ("decoded", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
+                ("locked", ctypes.c_void_p), ("skip", ctypes.c_void_p),
+                ("row_flags", ctypes.c_void_p), ("active_idx", ctypes.c_void_p),
+                ("m_active", ctypes.c_void_p), ("n_open", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -100,6 +113,10 @@ lib.dlm_posterior.restype = ctypes.c_int
 lib.dlm_posterior_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Select),
                                               ctypes.POINTER(ctypes.c_size_t)]
 lib.dlm_posterior_workspace_bytes.restype = ctypes.c_int
+lib.dlm_block_buffer_init.argtypes = [ctypes.POINTER(_BlockBuffer), _P]
+lib.dlm_block_buffer_init.restype = ctypes.c_int
+lib.dlm_block_buffer_advance.argtypes = [ctypes.POINTER(_BlockBuffer), _P, _P]
+lib.dlm_block_buffer_advance.restype = ctypes.c_int
 lib.dlm_last_error.argtypes = []
 lib.dlm_last_error.restype = ctypes.c_char_p
 
@@ -151,6 +168,7 @@ class MaskDesc:
     workspace: object = None   # uint8 device buffer
     workspace_bytes: Optional[int] = None
     colsum_accumulate: int = 0  # 1: colsum += this call's sums (e.g. over layers)
+    m_active: object = None     # optional int32 [B] device row counts
 
 
 @dataclasses.dataclass
@@ -165,6 +183,31 @@ class Select:
     score_ready: object = None  # torch.cuda.Event (recorded) or a raw hipEvent_t, or None
     margin: object = None       # optional fp32 [R] output
     entropy: object = None      # optional fp32 [R] output
+    row_flags: object = None    # optional uint8 [R]: ROW_SELECT | ROW_LOCK per row
+
+
+@dataclasses.dataclass
+class BlockBuffer:
+    """Device arrays of a multi-step run's Block Buffer (see dlm_step.h)."""
+    B: int
+    n_slots: int
+    block_size: int
+    max_active: int
+    prefix_len: int
+    slot_state: object = None  # uint8 [B, n_slots]
+    slot_group: object = None  # int32 [B, n_slots]
+    decoded: object = None     # uint8 [B, n_gen]
+    tokens: object = None      # int32 [B, n_gen]
+    locked: object = None      # uint8 [B, n_gen]
+    skip: object = None        # uint8 [B, n_gen]
+    row_flags: object = None   # uint8 [B, n_gen]
+    active_idx: object = None  # int32 [B, n_gen]
+    m_active: object = None    # int32 [B]
+    n_open: object = None      # int32 [B]
+
+    @property
+    def n_gen(self) -> int:
+        return self.n_slots * self.block_size
 
 
 def _ptr(x) -> Optional[int]:
@@ -191,7 +234,8 @@ def _c_mask(md: MaskDesc) -> _MaskDesc:
     wb = md.workspace_bytes if md.workspace_bytes is not None else _nbytes(md.workspace)
     return _MaskDesc(md.kind, md.Hq, md.M, md.kv_len, md.prefix_len, md.block_size, md.n_slots,
                      _ptr(md.slot_state), _ptr(md.slot_group), md.cs_lo, md.cs_hi,
-                     md.colsum_per_head, md.scale, _ptr(md.workspace), wb, md.colsum_accumulate)
+                     md.colsum_per_head, md.scale, _ptr(md.workspace), wb, md.colsum_accumulate,
+                     _ptr(md.m_active))
 
 
 def _c_sel(s: Select) -> _Select:
@@ -202,7 +246,14 @@ def _c_sel(s: Select) -> _Select:
         if not ev:
             raise DlmError(-1, "select.score_ready: the event has not been recorded")
     return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb, ev or None,
-                   _ptr(s.margin), _ptr(s.entropy))
+                   _ptr(s.margin), _ptr(s.entropy), _ptr(s.row_flags))
+
+
+def _c_bb(bb: BlockBuffer) -> _BlockBuffer:
+    return _BlockBuffer(bb.B, bb.n_slots, bb.block_size, bb.max_active, bb.prefix_len,
+                        _ptr(bb.slot_state), _ptr(bb.slot_group), _ptr(bb.decoded), _ptr(bb.tokens),
+                        _ptr(bb.locked), _ptr(bb.skip), _ptr(bb.row_flags), _ptr(bb.active_idx),
+                        _ptr(bb.m_active), _ptr(bb.n_open))
 
 
 def _stream(stream) -> Optional[int]:
@@ -254,6 +305,8 @@ def dlm_step_attn(q, k, v, kv_cache: KVCache, active_idx, mask_desc: MaskDesc, o
     if colsum is not None:
         shape = (B, Hq, mask_desc.kv_len) if mask_desc.colsum_per_head else (B, mask_desc.kv_len)
         _expect(colsum, "colsum", shape, "torch.float32")
+    if mask_desc.m_active is not None:
+        _expect(mask_desc.m_active, "m_active", (B,), "torch.int32")
     if mask_desc.kind == MASK_GROUP:
         _expect(mask_desc.slot_state, "slot_state", (B, mask_desc.n_slots), "torch.uint8")
         _expect(mask_desc.slot_group, "slot_group", (B, mask_desc.n_slots), "torch.int32")
@@ -283,6 +336,31 @@ def dlm_posterior(logits, prev_logits, locked, eps: float, select: Select, sel, 
         _expect(select.margin, "select.margin", (R,), "torch.float32")
     if select.entropy is not None:
         _expect(select.entropy, "select.entropy", (R,), "torch.float32")
+    if select.row_flags is not None:
+        _expect(select.row_flags, "select.row_flags", (R,), "torch.uint8")
     s = _c_sel(select)
     _check(lib.dlm_posterior(_ptr(logits), _ptr(prev_logits), _ptr(locked), eps, ctypes.byref(s),
                              _ptr(sel), _ptr(kl), _ptr(conf), R, V, _stream(stream)))
+
+
+def _expect_bb(bb: BlockBuffer):
+    B, S, n = bb.B, bb.n_slots, bb.n_gen
+    for name, shape, dt in (("slot_state", (B, S), "torch.uint8"), ("slot_group", (B, S), "torch.int32"),
+                            ("decoded", (B, n), "torch.uint8"), ("tokens", (B, n), "torch.int32"),
+                            ("locked", (B, n), "torch.uint8"), ("skip", (B, n), "torch.uint8"),
+                            ("row_flags", (B, n), "torch.uint8"), ("active_idx", (B, n), "torch.int32"),
+                            ("m_active", (B,), "torch.int32"), ("n_open", (B,), "torch.int32")):
+        _expect(getattr(bb, name), name, shape, dt)
+
+
+def dlm_block_buffer_init(bb: BlockBuffer, stream=None) -> None:
+    _expect_bb(bb)
+    c = _c_bb(bb)
+    _check(lib.dlm_block_buffer_init(ctypes.byref(c), _stream(stream)))
+
+
+def dlm_block_buffer_advance(bb: BlockBuffer, sel, stream=None) -> None:
+    _expect_bb(bb)
+    _expect(sel, "sel", (bb.B, bb.n_gen), "torch.int32")
+    c = _c_bb(bb)
+    _check(lib.dlm_block_buffer_advance(ctypes.byref(c), _ptr(sel), _stream(stream)))

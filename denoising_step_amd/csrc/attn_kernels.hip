@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
             const int bg = r / per_bg;
             const int t = (r - bg * per_bg) * 256 + threadIdx.x;
             const int j = t / CH, c = t % CH;
-            ok[u] = r < nblk && j < a.M;
+            ok[u] = r < nblk && j < a.M && j < valid_rows(a, bg / a.Hkv);
             dst[u] = 0;
             kv[u] = v4u{0u, 0u, 0u, 0u};
             vv[u] = v4u{0u, 0u, 0u, 0u};
@@ -271,6 +271,10 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     const int split = L % a.n_split;
     const int bg = L / a.n_split;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
+    // With a device row count, a tile past the valid rows has nothing to do
+    // (the whole workgroup leaves before its first barrier).
+    const int Mv = valid_rows(a, b);
+    if (qt * (32 * QW) >= a.G * Mv) return;
 
     const uint8_t *st = a.kind == 2 ? a.slot_state + (long)b * a.n_slots : nullptr;
     const int32_t *gr = a.kind == 2 ? a.slot_group + (long)b * a.n_slots : nullptr;
@@ -290,12 +294,13 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         reinterpret_cast<uint4 *>(Vs1)[i] = uint4{0, 0, 0, 0};
     }
 
-    // This lane's query.
-    const int rows_bg = a.G * a.M;
+    // This lane's query: packed row r = hl * Mv + j over the Mv valid rows
+    // (the row stride in memory stays M).
+    const int rows_bg = a.G * Mv;
     const int r = qt * (32 * QW) + wq * 32 + l32;
     const bool rv = r < rows_bg;
-    const int hl = rv ? r / a.M : 0;
-    const int j = rv ? r - hl * a.M : 0;
+    const int hl = rv ? r / Mv : 0;
+    const int j = rv ? r - hl * Mv : 0;
     const int h = g * a.G + hl;
     const int pos = a.active_idx[(long)b * a.M + j];
     const int qcode = rv ? query_code(a, gr, pos) : INT_MIN;
@@ -584,6 +589,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     const long row = (long)blockIdx.x * RPB + threadIdx.x / PER_ROW;
     const int d4 = threadIdx.x % PER_ROW;
     if (row >= rows_total) return;
+    if (a.m_valid && (int)(row % a.M) >= valid_rows(a, (int)(row / ((long)a.Hq * a.M)))) return;
     const float *ls = a.ws_l + row;
     float m = -INFINITY;
     for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, ls[s * rows_total]);
@@ -658,7 +664,7 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     // M <= 4096 takes two rounds of loads instead of log2(M) dependent ones.
     if (wid < 2) {
         const int target = wid == 0 ? a.cs_lo : a.cs_hi;
-        int lo = 0, len = a.M;                       // answer in [lo, lo + len]
+        int lo = 0, len = valid_rows(a, b);          // answer in [lo, lo + len]
         while (len > 0) {
             const int step = (len + 63) / 64;
             const int p = lo + lane * step;

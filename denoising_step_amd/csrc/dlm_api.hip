@@ -86,10 +86,13 @@ int validate_contents(const dlm_kv_cache *kc, const dlm_mask_desc *md, const int
 {
     const int B = kc->B, M = md->M;
     std::vector<int32_t> act((size_t)B * M);
+    std::vector<int32_t> mv((size_t)B, M);
     std::vector<uint8_t> st;
     std::vector<int32_t> gr;
     if (M > 0 && hipMemcpyAsync(act.data(), active_idx, act.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess)
         return fail(DLM_E_HIP, "DLM_VALIDATE: copy of active_idx failed");
+    if (md->m_active && hipMemcpyAsync(mv.data(), md->m_active, mv.size() * 4, hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return fail(DLM_E_HIP, "DLM_VALIDATE: copy of m_active failed");
     if (md->kind == DLM_MASK_GROUP) {
         st.resize((size_t)B * md->n_slots);
         gr.resize((size_t)B * md->n_slots);
@@ -99,7 +102,10 @@ int validate_contents(const dlm_kv_cache *kc, const dlm_mask_desc *md, const int
     }
     if (hipStreamSynchronize(stream) != hipSuccess) return fail(DLM_E_HIP, "DLM_VALIDATE: sync failed");
     for (int b = 0; b < B; ++b)
-        for (int j = 0; j < M; ++j) {
+        if (mv[b] < 0 || mv[b] > M)
+            return fail(DLM_E_DESC, "m_active[%d]=%d outside [0, M=%d]", b, mv[b], M);
+    for (int b = 0; b < B; ++b)
+        for (int j = 0; j < mv[b]; ++j) {
             int p = act[(size_t)b * M + j];
             if (p < md->prefix_len || p >= md->kv_len)
                 return fail(DLM_E_DESC, "active_idx[%d,%d]=%d outside [prefix_len=%d, kv_len=%d)", b, j, p,
@@ -182,6 +188,7 @@ int dlm_step_attn(const void *q, const void *k, const void *v, const dlm_kv_cach
     a.n_cap = kc->n_cap; a.kv_len = md->kv_len; a.P = md->prefix_len; a.bs = md->block_size;
     a.n_slots = md->kind == DLM_MASK_GROUP ? md->n_slots : 0;
     a.kind = md->kind;
+    a.m_valid = md->m_active;
     a.cs_lo = md->cs_lo; a.cs_hi = md->cs_hi; a.per_head = md->colsum_per_head;
     a.accumulate = md->colsum_accumulate;
     const float scale = md->scale > 0.f ? md->scale : 1.f / sqrtf((float)kc->D);
@@ -243,12 +250,61 @@ int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked
     dlm::PostArgs a{};
     a.x = logits; a.y = prev_logits; a.locked = locked; a.score = select->score;
     a.sel = sel; a.kl = kl; a.conf = conf; a.margin = select->margin; a.entropy = select->entropy;
+    a.flags = select->row_flags;
     a.part = static_cast<dlm::PostPartial *>(select->workspace);
     a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
     a.eps = eps; a.tau = select->tau; a.n_chunks = p.n_chunks; a.chunk = p.chunk;
     hipError_t e = dlm::launch_posterior(a, stream, select->score_ready);
     if (e != hipSuccess) return fail(DLM_E_HIP, "launch or event wait failed: %s", hipGetErrorString(e));
     return DLM_OK;
+}
+
+static int check_bb(const dlm_block_buffer *bb)
+{
+    if (!bb) return fail(DLM_E_NULL, "block buffer is NULL");
+    if (bb->B < 1) return fail(DLM_E_SHAPE, "B=%d must be >= 1", bb->B);
+    if (bb->n_slots < 1 || bb->n_slots > dlm::kMaxSlots)
+        return fail(DLM_E_SHAPE, "n_slots=%d must be in [1, %d]", bb->n_slots, dlm::kMaxSlots);
+    if (bb->block_size < 1) return fail(DLM_E_SHAPE, "block_size=%d must be >= 1", bb->block_size);
+    if (bb->max_active < 1) return fail(DLM_E_SHAPE, "max_active=%d must be >= 1", bb->max_active);
+    if (bb->prefix_len < 0) return fail(DLM_E_SHAPE, "prefix_len=%d must be >= 0", bb->prefix_len);
+    const long n_gen = (long)bb->n_slots * bb->block_size;
+    if (n_gen > (1L << 24) || (long)bb->prefix_len + n_gen > (1L << 31) - 1 || bb->B * n_gen > (1L << 31) - 1)
+        return fail(DLM_E_SHAPE, "generation region too large (%ld positions)", n_gen);
+    if (!bb->slot_state || !bb->slot_group || !bb->decoded || !bb->tokens || !bb->locked || !bb->skip ||
+        !bb->row_flags || !bb->active_idx || !bb->m_active || !bb->n_open)
+        return fail(DLM_E_NULL, "every array of the block buffer must be non-NULL");
+    return DLM_OK;
+}
+
+static int run_bb(const dlm_block_buffer *bb, const int32_t *sel, hipStream_t stream)
+{
+    dlm::BBArgs a{};
+    a.state = bb->slot_state; a.group = bb->slot_group; a.decoded = bb->decoded; a.tokens = bb->tokens;
+    a.locked = bb->locked; a.skip = bb->skip; a.flags = bb->row_flags; a.active_idx = bb->active_idx;
+    a.m_active = bb->m_active; a.n_open = bb->n_open; a.sel = sel;
+    a.B = bb->B; a.n_slots = bb->n_slots; a.bs = bb->block_size; a.max_active = bb->max_active;
+    a.P = bb->prefix_len; a.n_gen = bb->n_slots * bb->block_size;
+    hipError_t e = dlm::launch_block_buffer(a, stream);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return DLM_OK;
+}
+
+int dlm_block_buffer_init(const dlm_block_buffer *bb, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_bb(bb);
+    if (rc != DLM_OK) return rc;
+    return run_bb(bb, nullptr, stream);
+}
+
+int dlm_block_buffer_advance(const dlm_block_buffer *bb, const int32_t *sel, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_bb(bb);
+    if (rc != DLM_OK) return rc;
+    if (!sel) return fail(DLM_E_NULL, "sel is NULL");
+    return run_bb(bb, sel, stream);
 }
 
 }  // extern "C"

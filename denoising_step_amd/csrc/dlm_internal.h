@@ -75,6 +75,7 @@ struct AttnArgs {
     uint16_t *out;
     float *lse, *colsum;
     float *ws_o, *ws_l, *ws_cs;
+    const int32_t *m_valid;         // optional device [B]: rows of batch b that are valid
     int B, Hq, Hkv, G, D, M, n_cap, kv_len, P, bs, n_slots, kind;
     int cs_lo, cs_hi, per_head, accumulate;
     float scale_log2;               // softmax scale * log2(e)
@@ -88,15 +89,35 @@ struct PostArgs {
     int32_t *sel;
     float *kl, *conf;
     float *margin, *entropy;        // optional outputs (nullptr: not written)
+    const uint8_t *flags;           // optional [R]: bit 0 selectable, bit 1 lockable
     PostPartial *part;
     int R, V, mode, k, group_rows;
     float eps, tau;
     int n_chunks, chunk;
 };
 
+// Block Buffer state of a multi-step run (device arrays, see dlm_step.h).
+struct BBArgs {
+    uint8_t *state;
+    int32_t *group;
+    uint8_t *decoded;
+    int32_t *tokens;
+    uint8_t *locked, *skip, *flags;
+    int32_t *active_idx, *m_active, *n_open;
+    const int32_t *sel;             // nullptr: initialise instead of advancing
+    int B, n_slots, bs, max_active, P, n_gen;
+};
+
+// Valid rows of batch entry b: all M unless a device count is given.
+__device__ __forceinline__ int valid_rows(const AttnArgs &a, int b)
+{
+    return a.m_valid ? min(max(a.m_valid[b], 0), a.M) : a.M;
+}
+
 // Enqueue the kernels of one call (arguments already validated).
 hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after);
+hipError_t launch_block_buffer(const BBArgs &a, hipStream_t stream);
 
 // Map a hardware workgroup id to a logical one so that logically
 // consecutive workgroups (which share K/V) run on the same XCD: the

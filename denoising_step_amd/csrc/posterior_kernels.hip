@@ -5,8 +5,9 @@
 //   p = softmax(x), q = softmax(y) for step-t logits x and step-(t-1) y
 //   KL(p || q) = E_p[x - y] - (logsumexp x - logsumexp y)    (one pass)
 //   conf = max p = 1 / sum exp(x - max x),  tok = lowest argmax x
-//   lock if KL <= eps;  then a per-group selection (top-k / threshold /
-//   Attn-Sampler dynamic threshold / top-k by score).
+//   lock if KL <= eps (rows the caller marks lockable: all by default);
+//   then a per-group selection among rows it marks selectable (top-k /
+//   threshold / Attn-Sampler dynamic threshold / top-k by score).
 //
 // The stream kernel is HBM-bound: every logit of both steps is read exactly
 // once with 16-byte non-temporal loads, 4 per array in flight per thread,
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     __shared__ __attribute__((aligned(16))) float key_s[kMaxGroupRows];
     __shared__ float conf_s[kMaxGroupRows];
     __shared__ int tok_s[kMaxGroupRows];
-    __shared__ uint8_t elig_s[kMaxGroupRows];
+    __shared__ uint8_t elig_s[kMaxGroupRows];   // may be selected: unlocked and selectable
+    __shared__ uint8_t rowf_s[kMaxGroupRows];   // bit 0 unlocked on entry, bit 2 lockable
     __shared__ __attribute__((aligned(16))) PostPartial stage_s[kStageBytes / sizeof(PostPartial)];
     __shared__ __attribute__((aligned(16))) unsigned long long ord_s[kMaxGroupRows];
     __shared__ float red_s[4];
@@ -284,12 +286,13 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
 
     // Issue the lock-flag and score loads together with the first staging
     // round; nothing waits until the barrier.
-    uint8_t lk[4];
+    uint8_t lk[4], fl[4];
     float sc[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int t = tid + 256 * k;
         lk[k] = t < n ? a.locked[g0 + t] : 1;
+        fl[k] = (a.flags && t < n) ? a.flags[g0 + t] : 3;
         sc[k] = (by_score && t < n) ? a.score[g0 + t] : 0.f;
     }
     for (int r0 = 0; r0 < n; r0 += rows_per_round) {
@@ -319,7 +322,8 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
             for (int k = 0; k < 4; ++k) {
                 const int t = tid + 256 * k;
                 if (t < n) {
-                    elig_s[t] = lk[k] == 0 ? 1 : 0;
+                    elig_s[t] = (lk[k] == 0 && (fl[k] & 1)) ? 1 : 0;
+                    rowf_s[t] = (lk[k] == 0 ? 1 : 0) | ((fl[k] & 2) << 1);
                     if (by_score) key_s[t] = sc[k];
                 }
             }
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
             const int sub = tid % lanes;
             const bool row_ok = t < nr;
             const int gt = r0 + t;
-            const bool was_locked = !row_ok || elig_s[gt] == 0;
+            const bool was_locked = !row_ok || (rowf_s[gt] & 1) == 0;
             RowState s;
             rs_init(s);
             if (!was_locked) {
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                     klv = s.tx / s.sx - (s.mx - s.my) - (logf(s.sx) - logf(s.sy));
                     cf = 1.f / s.sx;
                     tok = s.ai;
-                    a.locked[r] = klv <= a.eps ? 1 : 0;
+                    a.locked[r] = (klv <= a.eps && (rowf_s[gt] & 4)) ? 1 : 0;
                     // margin = p(top-1) - p(top-2) = conf * (1 - exp(a2 - mx)): exactly
                     // 0 on a tie, conf without a runner-up; entropy = ln sx - ex / sx
                     mg = cf * (1.f - fast_exp2((s.a2 - s.mx) * kLog2e));

@@ -8,12 +8,19 @@
  *                     group-aware mask, plus attention column sums;
  *   dlm_posterior  -- per-row softmax posterior, confidence, the step-wise
  *                     KL(p_t || p_{t-1}) lock test and unmask selection.
+ * A multi-step run adds one call between steps:
+ *   dlm_block_buffer_advance -- the Block Buffer slot state machine, the
+ *                     unmasking and locking of rows, and the compaction of
+ *                     the rows the next step computes, all on the device
+ *                     (dlm_block_buffer_init starts a run).
  *
  * Conventions for every entry point:
  *  - Pointers to tensors are DEVICE pointers (HIP global memory) and every
  *    tensor is dense and row-major in the layout stated.  The descriptor
- *    structs themselves (dlm_kv_cache, dlm_mask_desc, dlm_select) live in
- *    HOST memory and are read during the call only.
+ *    structs themselves (dlm_kv_cache, dlm_mask_desc, dlm_select,
+ *    dlm_block_buffer) live in HOST memory and are read during the call
+ *    only.  A run's Block Buffer state lives in device arrays the caller
+ *    owns; the library itself keeps none.
  *  - bf16 is IEEE bfloat16 stored as 16-bit words; fp32 is IEEE binary32.
  *  - The caller owns every buffer, the workspace included.  The library
  *    allocates nothing, frees nothing, keeps no state between calls and does
@@ -106,6 +113,15 @@ typedef struct {
                                     e.g. summed over the layers of a model (the
                                     Attention-Based Sampler page, sec. 4, averages the
                                     scores of all layers and heads; a sum ranks the same) */
+    const int32_t *m_active;     /* optional device int32 [B] (NULL: every row is valid).
+                                    Only rows j < m_active[b] (clamped to [0, M]) of batch
+                                    entry b are valid: the others are not read (q, k, v,
+                                    active_idx) nor written (out, lse, the cache) and add
+                                    nothing to colsum.  M stays the row stride and the
+                                    capacity.  With it a step whose row count is decided
+                                    on the device (dlm_block_buffer_advance) keeps the
+                                    same launch shapes, e.g. inside a captured HIP graph
+                                    (SureLock page, sec. 2: M_t rows are computed). */
 } dlm_mask_desc;
 
 /*
@@ -174,8 +190,9 @@ int dlm_step_attn_workspace_bytes(const dlm_kv_cache *kv_cache,
  *                scores of the greedy samplers).
  *  TOPK_LOW_ENTROPY  the k eligible rows of lowest entropy -sum p ln p
  *                (entropy sampler; likewise sec. 1).
- * Eligible = not locked on entry.  Order: larger key first, then lower row
- * index.  If fewer than k rows are eligible, all are taken. */
+ * Eligible = not locked on entry and selectable (dlm_select.row_flags).
+ * Order: larger key first, then lower row index.  If fewer than k rows are
+ * eligible, all are taken. */
 enum { DLM_SEL_NONE = 0, DLM_SEL_TOPK_CONF = 1, DLM_SEL_THRESH_CONF = 2,
        DLM_SEL_ATTN_DYNAMIC = 3, DLM_SEL_TOPK_SCORE = 4, DLM_SEL_TOPK_MARGIN = 5,
        DLM_SEL_TOPK_LOW_ENTROPY = 6 };
@@ -200,7 +217,16 @@ typedef struct {
                                 on entry; p_t(top-1) when V == 1 */
     float *entropy;          /* optional device fp32 [R] out (NULL: not written):
                                 -sum_v p_t(v) ln p_t(v); 0 for rows locked on entry */
+    const uint8_t *row_flags;    /* optional device uint8 [R] (NULL: every row both):
+                                DLM_ROW_SELECT -- the row may be selected (a masked token);
+                                DLM_ROW_LOCK   -- the row may lock (SureLock page, sec. 2:
+                                a converged, already unmasked token stops).  A row
+                                without DLM_ROW_LOCK keeps locked[r] = 0 whatever its
+                                KL; its kl, conf and scores are still written. */
 } dlm_select;
+
+/* Bits of dlm_select.row_flags. */
+enum { DLM_ROW_SELECT = 1, DLM_ROW_LOCK = 2 };
 
 /*
  * dlm_posterior -- posterior, lock test and unmask selection for R rows.
@@ -210,7 +236,8 @@ typedef struct {
  *   p_t = softmax(logits[r]), p_{t-1} = softmax(prev_logits[r])
  *   kl[r]   = KL(p_t || p_{t-1}) = sum_v p_t(v) (log p_t(v) - log p_{t-1}(v))
  *   conf[r] = max_v p_t(v);  tok = lowest v with the largest logit
- *   locked[r] = 1 if kl[r] <= eps (a lock is never undone)
+ *   locked[r] = 1 if kl[r] <= eps and the row may lock (row_flags; a lock
+ *               is never undone)
  *   sel[r]  = tok if the row is selected (mode above), else -1.
  * A row that arrives locked is not read: kl = conf = 0, sel = -1, stays locked.
  * kl and conf are fp32; KL is computed in one pass as
@@ -234,6 +261,78 @@ int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked
 /* Workspace bytes dlm_posterior needs for R x V.  Writes *bytes. */
 int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select,
                                   size_t *bytes);
+
+/*
+ * Block Buffer of a multi-step run ("Multi-Block Diffusion Language Models"
+ * page, sec. 2.3; SureLock page, sec. 2).  The generation region of each
+ * batch entry is n_slots blocks of block_size positions starting at
+ * absolute position prefix_len; position p (0-based in the region) is in
+ * slot p / block_size.  All arrays are device memory owned by the caller;
+ * n_gen = n_slots * block_size.
+ *   slot_state  uint8 [B, n_slots]   DLM_SLOT_*            (written)
+ *   slot_group  int32 [B, n_slots]   noise group of a slot (written): a
+ *               to-cache or in-cache slot s is group s (clean, block-causal
+ *               context), every active slot is group n_slots (the running
+ *               noise group, mutually visible); use both as the GROUP mask's
+ *               slot tables
+ *   decoded     uint8 [B, n_gen]     1 once unmasked        (read, updated)
+ *   tokens      int32 [B, n_gen]     token of an unmasked position (updated)
+ *   locked      uint8 [B, n_gen]     1 once locked (its query stops)
+ *   skip        uint8 [B, n_gen]     the next step's dlm_posterior `locked`
+ *               argument: 1 for locked rows and rows outside active slots;
+ *               the posterior then sets it for rows that lock
+ *   row_flags   uint8 [B, n_gen]     the next step's dlm_select.row_flags:
+ *               DLM_ROW_SELECT for masked rows, DLM_ROW_LOCK for unmasked
+ *               rows whose slot was active in the step just taken (they
+ *               have a previous-step posterior)
+ *   active_idx  int32 [B, n_gen]     the next step's rows to compute: the
+ *               absolute positions of unlocked rows of active and to-cache
+ *               slots, ascending, then -1 (dlm_step_attn's active_idx with
+ *               M = n_gen)
+ *   m_active    int32 [B]            how many (dlm_mask_desc.m_active)
+ *   n_open      int32 [B]            slots not yet in-cache (0: finished)
+ */
+typedef struct {
+    int32_t B;              /* batch entries, >= 1 */
+    int32_t n_slots;        /* slots per batch entry, 1..1024 */
+    int32_t block_size;     /* positions per slot, >= 1 */
+    int32_t max_active;     /* running-set size: most slots active at once, >= 1 */
+    int32_t prefix_len;     /* absolute position of the region's first row, >= 0 */
+    uint8_t *slot_state;
+    int32_t *slot_group;
+    uint8_t *decoded;
+    int32_t *tokens;
+    uint8_t *locked;
+    uint8_t *skip;
+    uint8_t *row_flags;
+    int32_t *active_idx;
+    int32_t *m_active;
+    int32_t *n_open;
+} dlm_block_buffer;
+
+/* Start a run: slots 0 .. max_active-1 active, the rest dummy; locked
+ * cleared; decoded and tokens kept as the caller set them (e.g. a prompt
+ * inside the region starts unmasked); no row may lock in the first step.
+ * Writes slot_state, slot_group, locked, skip, row_flags, active_idx,
+ * m_active, n_open.  One kernel on `stream`.
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_HIP. */
+int dlm_block_buffer_init(const dlm_block_buffer *bb, hipStream_t stream);
+
+/* Between two steps: apply the step's results to rows of active slots (a
+ * row with sel >= 0 becomes unmasked with that token; a row the posterior
+ * locked in `skip` becomes locked), then move the slots in this order:
+ * to-cache -> in-cache (the step just taken recomputed those blocks and
+ * wrote their K/V into the cache); the leading run of fully unmasked active
+ * slots -> to-cache (a block is committed only after every earlier one, so
+ * the cached prefix stays contiguous); the lowest dummy slots -> active
+ * until max_active are active.  Then derives skip, row_flags, active_idx,
+ * m_active and n_open for the next step.  The next step's forward computes
+ * the to-cache rows (their commit) together with the active rows (their
+ * decoding), so decoding and cache writes overlap in one launch.
+ *   sel  int32 [B, n_gen]  (device) the step's dlm_posterior selections
+ * One kernel on `stream`.  Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_HIP. */
+int dlm_block_buffer_advance(const dlm_block_buffer *bb, const int32_t *sel,
+                             hipStream_t stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *dlm_last_error(void);

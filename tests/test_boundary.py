@@ -189,3 +189,46 @@ def test_single_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout.strip()
     assert out == "1", out
+
+
+def _bb(**kw):
+    base = dict(B=2, n_slots=4, block_size=16, max_active=2, prefix_len=32)
+    base.update(kw)
+    arrays = {f: FAKE for f in ("slot_state", "slot_group", "decoded", "tokens", "locked", "skip",
+                                "row_flags", "active_idx", "m_active", "n_open")}
+    for f in list(arrays):
+        if f in kw:
+            arrays[f] = kw.pop(f)
+            base.pop(f, None)
+    return dlm.BlockBuffer(**base, **arrays)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(B=0), dlm.DLM_E_SHAPE),
+    (dict(n_slots=0), dlm.DLM_E_SHAPE),
+    (dict(n_slots=1025), dlm.DLM_E_SHAPE),
+    (dict(block_size=0), dlm.DLM_E_SHAPE),
+    (dict(max_active=0), dlm.DLM_E_SHAPE),
+    (dict(prefix_len=-1), dlm.DLM_E_SHAPE),
+    (dict(n_slots=1024, block_size=1 << 15), dlm.DLM_E_SHAPE),
+    (dict(slot_state=None), dlm.DLM_E_NULL),
+    (dict(active_idx=None), dlm.DLM_E_NULL),
+    (dict(n_open=None), dlm.DLM_E_NULL),
+])
+def test_block_buffer_rejects(case, code):
+    bb = _bb(**case)
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_block_buffer_init(bb, stream=0)
+    assert e.value.code == code
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_block_buffer_advance(bb, FAKE, stream=0)
+    assert e.value.code == code
+
+
+def test_block_buffer_advance_needs_sel():
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_block_buffer_advance(_bb(), None, stream=0)
+    assert e.value.code == dlm.DLM_E_NULL
+    import ctypes
+    assert dlm.lib.dlm_block_buffer_init(None, None) == dlm.DLM_E_NULL
+    assert dlm.lib.dlm_block_buffer_advance(None, FAKE, None) == dlm.DLM_E_NULL
