@@ -173,6 +173,126 @@ def _cpu_model():
     return "unknown"
 
 
+def loop_bench(args):
+    """A whole SureLock-style run at the LLaDA-8B layer shape: one 1024-
+    position block of which the first 512 are an unmasked prompt (recomputed
+    until it locks) and 512 are masked, 32 heads of width 128, vocabulary
+    126464, the 16 most confident rows unmasked per step, eps 1e-3.  Each
+    step is the hot path (attention over the M_t computed rows, the
+    posterior of the unlocked rows, the Block Buffer advance), timed per
+    step eagerly and as replays of one captured HIP graph; the stand-in for
+    the model (q / k / v rows, logits that settle geometrically per
+    position) runs between the timed regions.  Prints one JSON line."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from denoising_step_amd.loop import DeviceLoop
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    B, H, D, n, V = 1, 32, 128, 1024, 126464
+    n_prompt, k_step = 512, 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    std = 1.0 / math.sqrt(D)
+
+    def randn(shape, scale):
+        return torch.randn(shape, generator=gen, device=dev).mul_(scale)
+
+    base = randn((B, n, V), 3.0)
+    dec0 = torch.zeros((B, n), dtype=torch.uint8, device=dev)
+    dec0[:, :n_prompt] = 1
+    tok0 = torch.where(dec0 == 1, base.argmax(-1).to(torch.int32), torch.full_like(dec0, -1, dtype=torch.int32))
+    case = types.SimpleNamespace(
+        name="llada_surelock_run", B=B, Hq=H, Hkv=H, D=D, prefix_len=0, block_size=n, n_slots=1,
+        max_active=1, T=n, V=V, eps=1e-3, mode=W.SEL_TOPK_CONF, k=k_step, tau=0.9,
+        cache_k=randn((B, H, n, D), std).to(torch.bfloat16), cache_v=randn((B, H, n, D), std).to(torch.bfloat16),
+        q=None, k_new=None, v_new=None, logits=None, decoded0=dec0, tokens0=tok0)
+
+    class Run(DeviceLoop):
+        def __init__(self):
+            super().__init__(case)
+            self.qb = randn((B, H, n, D), std).to(torch.bfloat16)
+            self.kb = randn((B, H, n, D), std).to(torch.bfloat16)
+            self.vb = randn((B, H, n, D), std).to(torch.bfloat16)
+            self.rate = torch.empty((B, n), device=dev).uniform_(0.5, 0.75, generator=gen)
+            self.noise_seed = args.seed + 1
+
+        def feed(self, t, stream=None):
+            with torch.cuda.stream(stream):
+                idx = (self.bb.active_idx - self.P).clamp_(min=0).long()
+                for src, dst in ((self.qb, self.q), (self.kb, self.k), (self.vb, self.v)):
+                    torch.gather(src, 2, idx[:, None, :, None].expand(B, H, n, D), out=dst)
+                if t > 0:
+                    self.y.copy_(self.x)
+                g = torch.Generator(device=dev)
+                g.manual_seed(self.noise_seed * 100003 + t)
+                torch.randn(self.x.shape, generator=g, device=dev, out=self.x)
+                self.x.mul_((self.rate ** t)[..., None]).add_(base)
+                if t == 0:
+                    self.y.copy_(self.x)
+
+    run = Run()
+    s = torch.cuda.Stream()
+
+    # 1. the row counts of the run (host reads between steps: not timed)
+    run.start(s)
+    m_t, n_steps = [], 0
+    while True:
+        st = run.state()
+        if int(st["n_open"].sum()) == 0 or n_steps >= n:
+            break
+        m_t.append(int(st["m_active"].sum()))
+        run.feed(n_steps, s)
+        run.step(s)
+        n_steps += 1
+    torch.cuda.synchronize()
+    tokens_ref = run.bb.tokens.cpu()
+
+    def timed(replay):
+        run.start(s)
+        torch.cuda.synchronize()
+        g = run.capture(s) if replay else None
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_steps)]
+        for t in range(n_steps):
+            run.feed(t, s)
+            ev[t][0].record(s)
+            if replay:
+                with torch.cuda.stream(s):
+                    g.replay()
+            else:
+                run.step(s)
+            ev[t][1].record(s)
+        torch.cuda.synchronize()
+        assert torch.equal(run.bb.tokens.cpu(), tokens_ref), "the timed run diverged"
+        return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+    timed(False)                       # warm-up
+    eager = timed(False)
+    graph = timed(True)
+    full = n_steps * eager[0]          # every step at the first step's cost (nothing locked)
+    line = {
+        "metric": "hot-path time of a whole SureLock run (per denoising step)",
+        "unit": "us", "n_gpus": 1, "steps": n_steps, "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": case.name, "B": B, "Hq": H, "Hkv": H, "D": D, "positions": n,
+                   "prompt_unmasked": n_prompt, "vocab": V, "selection": "top-16 confidence per step",
+                   "eps": case.eps},
+        "M_t": m_t,
+        "step_us_eager": [round(x, 1) for x in eager],
+        "step_us_graph": [round(x, 1) for x in graph],
+        "total_ms_eager": round(sum(eager) / 1e3, 3),
+        "total_ms_graph": round(sum(graph) / 1e3, 3),
+        "full_recompute_ms": round(full / 1e3, 3),
+        "rows_computed_frac": round(sum(m_t) / (n_steps * n), 4),
+        "time_frac_of_full": round(sum(graph) / full, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +303,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--loop", action="store_true",
+                    help="time a whole multi-step SureLock run instead (its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -190,6 +312,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.loop:
+        loop_bench(args)
         return
 
     import numpy as np

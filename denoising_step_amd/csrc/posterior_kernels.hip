@@ -267,6 +267,8 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     __shared__ uint8_t rowf_s[kMaxGroupRows];   // bit 0 unlocked on entry, bit 2 lockable
     __shared__ __attribute__((aligned(16))) PostPartial stage_s[kStageBytes / sizeof(PostPartial)];
     __shared__ __attribute__((aligned(16))) unsigned long long ord_s[kMaxGroupRows];
+    __shared__ int hist_s[256];
+    __shared__ int pick_s[2];                   // radix select: digit found, count still to go
     __shared__ float red_s[4];
 
     const int tid = threadIdx.x;
@@ -394,9 +396,17 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     // order-preserving (all bits flipped for a negative key, the sign bit
     // for a positive one) above the complemented row index.  Ineligible
     // rows take key -inf and sort last (eligible keys are finite: a
-    // confidence or a column sum).  The rank is then a count of larger
-    // packed values: one 64-bit compare and one add per row.
+    // confidence or a column sum).  The packed values are distinct, so
+    // rank(t) < k exactly when t's packed value is at least the k-th
+    // largest.  A small group counts larger values per row (one 64-bit
+    // compare and one add per pair); a larger one finds the k-th largest
+    // value by radix selection over its eight bytes, most significant
+    // first: a 256-bin histogram in LDS of the values that share the bytes
+    // found so far, then one wave scans the bins from the top for the one
+    // that holds the k-th value.  Same cost for any k.
     typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+    constexpr int kCountMax = 256;
+    const bool counted = n <= kCountMax;
     __syncthreads();
     for (int t = tid; t < n; t += 256) {
         const unsigned bits = __float_as_uint(elig_s[t] ? key_s[t] : -INFINITY);
@@ -405,20 +415,78 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     }
     for (int t = n + tid; t < ((n + 1) & ~1); t += 256) ord_s[t] = 0;   // even count
     __syncthreads();
+    // the kk-th largest packed value (kk in [1, n]); block-uniform call
+    auto kth_largest = [&](int kk) -> unsigned long long {
+        unsigned long long prefix = 0;
+        int krem = kk;
+        for (int pass = 7; pass >= 0; --pass) {
+            const int shift = pass * 8;
+            hist_s[tid] = 0;
+            __syncthreads();
+            for (int i = tid; i < n; i += 256) {
+                const unsigned long long v = ord_s[i];
+                if (pass == 7 || (v >> (shift + 8)) == prefix) atomicAdd(&hist_s[(v >> shift) & 255], 1);
+            }
+            __syncthreads();
+            if (tid < 64) {
+                // lane l holds bins 255 - 4l - j, j = 0..3 (descending)
+                int c[4], sum = 0;
+                for (int j = 0; j < 4; ++j) {
+                    c[j] = hist_s[255 - 4 * tid - j];
+                    sum += c[j];
+                }
+                int incl = sum;
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int o = __shfl_up(incl, off);
+                    if (tid >= off) incl += o;
+                }
+                int cum = incl - sum;
+                if (cum < krem && krem <= incl) {
+                    for (int j = 0; j < 4; ++j) {
+                        if (cum + c[j] >= krem) {
+                            pick_s[0] = 255 - 4 * tid - j;
+                            pick_s[1] = krem - cum;
+                            break;
+                        }
+                        cum += c[j];
+                    }
+                }
+            }
+            __syncthreads();
+            prefix = (prefix << 8) | (unsigned)pick_s[0];
+            krem = pick_s[1];
+            __syncthreads();
+        }
+        return prefix;
+    };
+    const bool topk = a.mode == 1 || a.mode == 4 || a.mode == 5 || a.mode == 6;
+    unsigned long long kth = 0;                 // picked iff eligible and value >= kth
+    if (!counted) {
+        if (topk) kth = a.k <= 0 ? ~0ull : a.k >= n ? 0ull : kth_largest(a.k);
+        else if (!any) kth = kth_largest(1);
+    }
     for (int t = tid; t < n; t += 256) {
         int out = -1;
         if (elig_s[t]) {
             const float kt = key_s[t];
             const unsigned long long mine = ord_s[t];
-            int rank = 0;
-            for (int u = 0; u < n; u += 2) {
-                const u64x2 p = *reinterpret_cast<const u64x2 *>(&ord_s[u]);
-                rank += (p.x > mine ? 1 : 0) + (p.y > mine ? 1 : 0);
+            bool first = false, in_topk = false;
+            if (counted) {
+                int rank = 0;
+                for (int u = 0; u < n; u += 2) {
+                    const u64x2 p = *reinterpret_cast<const u64x2 *>(&ord_s[u]);
+                    rank += (p.x > mine ? 1 : 0) + (p.y > mine ? 1 : 0);
+                }
+                first = rank == 0;
+                in_topk = rank < a.k;
+            } else {
+                first = mine >= kth;            // kth = the largest when a fallback is needed
+                in_topk = a.k > 0 && mine >= kth;
             }
             bool pick = false;
-            if (a.mode == 1 || a.mode == 4 || a.mode == 5 || a.mode == 6) pick = rank < a.k;
-            else if (a.mode == 2) pick = any ? conf_s[t] > a.tau : rank == 0;
-            else if (a.mode == 3) pick = any ? (conf_s[t] > a.tau && kt > thr) : rank == 0;
+            if (topk) pick = in_topk;
+            else if (a.mode == 2) pick = any ? conf_s[t] > a.tau : first;
+            else if (a.mode == 3) pick = any ? (conf_s[t] > a.tau && kt > thr) : first;
             if (pick) out = tok_s[t];
         }
         a.sel[g0 + t] = out;

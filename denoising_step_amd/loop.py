@@ -33,12 +33,24 @@ from . import (MASK_GROUP, BlockBuffer, KVCache, MaskDesc, Select, dlm_block_buf
 from .runner import bf16_to_device
 
 
+def _on(x, dev, dtype=None, bf16=False):
+    """A device tensor from a numpy array (bf16 as bit patterns) or a tensor."""
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.to(dev)
+    if bf16:
+        return bf16_to_device(x, dev)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype)).to(dev)
+
+
 class DeviceLoop:
     def __init__(self, case, device="cuda"):
         """case: a run's inputs (``workloads.LoopCase`` fields: shapes, the
         selection rule, per-step bf16 q / k_new / v_new bit patterns and fp32
         logits for every generation position, the cache, the positions that
-        start unmasked)."""
+        start unmasked), as numpy arrays or device tensors.  The per-step
+        inputs may be None when a subclass's ``feed`` makes them."""
         dev = torch.device(device)
         self.case = case
         B, Hq, Hkv, D = case.B, case.Hq, case.Hkv, case.D
@@ -46,12 +58,12 @@ class DeviceLoop:
         n_gen, kv_len, V = S * bs, P + S * bs, case.V
         self.B, self.n_gen, self.kv_len, self.V, self.P = B, n_gen, kv_len, V, P
         # stand-in inputs of every step
-        self.q_all = bf16_to_device(case.q, dev)
-        self.k_all = bf16_to_device(case.k_new, dev)
-        self.v_all = bf16_to_device(case.v_new, dev)
-        self.logits_all = torch.from_numpy(np.ascontiguousarray(case.logits)).to(dev)
-        self.cache_k0 = bf16_to_device(case.cache_k, dev)
-        self.cache_v0 = bf16_to_device(case.cache_v, dev)
+        self.q_all = _on(case.q, dev, bf16=True)
+        self.k_all = _on(case.k_new, dev, bf16=True)
+        self.v_all = _on(case.v_new, dev, bf16=True)
+        self.logits_all = _on(case.logits, dev, np.float32)
+        self.cache_k0 = _on(case.cache_k, dev, bf16=True)
+        self.cache_v0 = _on(case.cache_v, dev, bf16=True)
         self.cache_k = self.cache_k0.clone()
         self.cache_v = self.cache_v0.clone()
         self.kv = KVCache(self.cache_k, self.cache_v)
@@ -59,8 +71,8 @@ class DeviceLoop:
         def z(shape, dt):
             return torch.zeros(shape, dtype=dt, device=dev)
 
-        self.decoded0 = torch.from_numpy(np.ascontiguousarray(case.decoded0, np.uint8)).to(dev)
-        self.tokens0 = torch.from_numpy(np.ascontiguousarray(case.tokens0, np.int32)).to(dev)
+        self.decoded0 = _on(case.decoded0, dev, np.uint8)
+        self.tokens0 = _on(case.tokens0, dev, np.int32)
         self.bb = BlockBuffer(B=B, n_slots=S, block_size=bs, max_active=case.max_active, prefix_len=P,
                               slot_state=z((B, S), torch.uint8), slot_group=z((B, S), torch.int32),
                               decoded=self.decoded0.clone(), tokens=self.tokens0.clone(),

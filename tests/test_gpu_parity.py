@@ -302,6 +302,49 @@ def test_posterior_edge_cases():
         assert np.all(sel.cpu().numpy()[locked == 1] == -1)
 
 
+@pytest.mark.parametrize("g", [200, 257, 700, 1024])
+def test_large_selection_groups(g):
+    """Groups of more than 256 rows pick by radix selection of the k-th
+    largest packed key (up to 1024 rows), smaller ones by counting: every
+    ranking mode on both sides of the boundary, a ragged last group, locked
+    rows and rows that may not be selected."""
+    import denoising_step_amd as dlm
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(60 + g)
+    R, V = 2 * g + 77, 600
+    x = (rng.standard_normal((R, V)) * rng.uniform(0.5, 4.0, R)[:, None]).astype(np.float32)
+    y = (x + rng.standard_normal((R, V)) * 0.1).astype(np.float32)
+    locked = (rng.random(R) < 0.2).astype(np.uint8)
+    flags = np.where(rng.random(R) < 0.1, 2, 3).astype(np.uint8)
+    score = rng.random(R).astype(np.float32)
+    ora = oracle.posterior(x, y, locked, 1e-3, flags=flags)
+    for mode, k, tau in [(W.SEL_TOPK_CONF, 37, 0.0), (W.SEL_TOPK_SCORE, g // 3, 0.0),
+                         (W.SEL_TOPK_MARGIN, 5, 0.0), (W.SEL_TOPK_LOW_ENTROPY, 1, 0.0),
+                         (W.SEL_THRESH_CONF, 0, 0.999), (W.SEL_ATTN_DYNAMIC, 0, 0.3)]:
+        _say(f"case: large groups g={g} mode={mode}")
+        mg = torch.empty(R, device=dev)
+        en = torch.empty(R, device=dev)
+        s = dlm.Select(mode=mode, k=k, group_rows=g, tau=tau, score=torch.from_numpy(score).to(dev),
+                       margin=mg, entropy=en, row_flags=torch.from_numpy(flags).to(dev))
+        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
+                                  device=dev)
+        lk = torch.from_numpy(locked.copy()).to(dev)
+        sel = torch.empty(R, dtype=torch.int32, device=dev)
+        kl = torch.empty(R, dtype=torch.float32, device=dev)
+        conf = torch.empty(R, dtype=torch.float32, device=dev)
+        dlm.dlm_posterior(torch.from_numpy(x).to(dev), torch.from_numpy(y).to(dev), lk, 1e-3, s,
+                          sel, kl, conf, R, V)
+        torch.cuda.synchronize()
+        check_posterior(kl.cpu().numpy(), conf.cpu().numpy(), lk.cpu().numpy(), ora["kl"], ora["conf"],
+                        ora["locked"], 1e-3, locked)
+        sel_o = oracle.select(mode, k, g, tau, score.astype(np.float64), ora["conf"], ora["tok"], locked,
+                              ora["margin"], ora["entropy"], flags=flags)
+        inelig = ((locked != 0) | ((flags & 1) == 0)).astype(np.uint8)
+        check_selection(sel.cpu().numpy(), sel_o, mode, g, tau, ora["conf"], score.astype(np.float64),
+                        inelig, x, ora["margin"], ora["entropy"])
+        assert (sel_o >= 0).sum() > 0
+
+
 @pytest.mark.parametrize("V", [1, 1003, 6000])
 def test_margin_entropy_samplers(V):
     """Margin and entropy of p_t and the two token-level samplers that rank
