@@ -63,7 +63,7 @@ def _load():
         lib.ora_colsum.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I, I, I, P, P,
                                    Dd, I, I, I, P, L, P, P]
         lib.ora_colsum.restype = None
-        lib.ora_posterior.argtypes = [P, P, P, L, L, Dd, L, P, P, P, P, P, P, P, P]
+        lib.ora_posterior.argtypes = [P, P, P, L, L, Dd, L, P, P, P, P, P, P, P, P, Dd]
         lib.ora_posterior.restype = None
         lib.ora_select.argtypes = [I, I, I, Dd, P, P, P, P, I, P, P, P, P]
         lib.ora_select.restype = None
@@ -165,11 +165,13 @@ def colsum(case, lse_all, kv=None, cols=None):
     return res
 
 
-def posterior(logits, prev, locked, eps, rows=None, flags=None):
+def posterior(logits, prev, locked, eps, rows=None, flags=None, conf_gate=0.0):
     """Per-row KL(p_t || p_{t-1}), confidence, argmax token and lock flag
     (SureLock section 2), and the margin p(top-1) - p(top-2) and entropy of
     p_t (the token-level scores named on the Attn-Sampler page, section 1).
     flags (uint8 [R] or None): only rows with bit ROW_LOCK may lock.
+    conf_gate: the optional confidence gate (SureLock section 2): a row
+    locks only if also conf >= conf_gate (0: no gate).
     Returns dict of kl, conf, tok, locked (new), margin, entropy."""
     lib = _load()
     logits = _c(logits, np.float32)
@@ -186,7 +188,8 @@ def posterior(logits, prev, locked, eps, rows=None, flags=None):
     entropy = np.empty(n, np.float64)
     flags_a = None if flags is None else _c(flags, np.uint8)
     lib.ora_posterior(_p(logits), _p(prev), _p(locked), R, V, float(eps), n, _p(rows_a),
-                      _p(kl), _p(conf), _p(tok), _p(lk), _p(margin), _p(entropy), _p(flags_a))
+                      _p(kl), _p(conf), _p(tok), _p(lk), _p(margin), _p(entropy), _p(flags_a),
+                      float(conf_gate))
     return {"kl": kl, "conf": conf, "tok": tok, "locked": lk, "margin": margin, "entropy": entropy}
 
 

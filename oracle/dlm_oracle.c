@@ -253,7 +253,7 @@ void ora_posterior(const float *logits, const float *prev, const uint8_t *locked
                    int64_t R, int64_t V, double eps, int64_t n_rows,
                    const int64_t *rows, double *kl, double *conf, int32_t *tok,
                    uint8_t *locked_out, double *margin, double *entropy,
-                   const uint8_t *flags)
+                   const uint8_t *flags, double conf_gate)
 {
     if (rows == NULL)
         n_rows = R;
@@ -300,8 +300,10 @@ void ora_posterior(const float *logits, const float *prev, const uint8_t *locked
         /* The lock test (KL <= eps) applies to rows the caller marks
          * lockable (flags bit 1; every row when flags is NULL).  SureLock
          * section 2: converged, already unmasked tokens are the ones whose
-         * computation stops. */
-        locked_out[t] = (uint8_t)(d <= eps && (flags == NULL || (flags[r] & ORA_ROW_LOCK)));
+         * computation stops.  The optional confidence gate of that section
+         * (a peaked posterior) adds conf >= conf_gate; 0 leaves it off. */
+        locked_out[t] = (uint8_t)(d <= eps && (flags == NULL || (flags[r] & ORA_ROW_LOCK)) &&
+                                  exp(mx - Lx) >= conf_gate);
         /* Token-level scores of the confidence family (Attn-Sampler page,
          * section 1: confidence, margin, entropy).  margin = p(top-1) -
          * p(top-2), the runner-up being the largest logit at any other

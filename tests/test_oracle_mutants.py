@@ -37,8 +37,9 @@ MUTANTS = [
      [pins.test_visibility_golden]),
     ("lock_strict", "locked_out[t] = (uint8_t)(d <= eps &&", "locked_out[t] = (uint8_t)(d < eps &&",
      [pins.test_lock_threshold_is_inclusive]),
-    ("lock_ignores_row_flags", "(d <= eps && (flags == NULL || (flags[r] & ORA_ROW_LOCK)))",
-     "(d <= eps)", [pins.test_lock_respects_row_flags]),
+    ("lock_ignores_row_flags", "(d <= eps && (flags == NULL || (flags[r] & ORA_ROW_LOCK)) &&",
+     "(d <= eps &&", [pins.test_lock_respects_row_flags]),
+    ("confidence_gate_ignored", "exp(mx - Lx) >= conf_gate);", "1);", [pins.test_confidence_gate]),
     ("argmax_last", "if ((double)x[v] > mx) {", "if ((double)x[v] >= mx) {",
      [pins.test_posterior_golden]),
     ("colsum_unnormalised", "head_sum += exp(scale * dot - L);", "head_sum += exp(scale * dot);",

@@ -367,6 +367,27 @@ def test_lock_respects_row_flags():
     assert want.any() and ((kl <= 1e-3) & ~want).any()     # both branches exercised
 
 
+def test_confidence_gate():
+    """With the gate, a row locks only if KL <= eps and conf >= gate
+    (SureLock section 2, the optional confidence criterion); KL and conf
+    come from scipy / numpy here."""
+    from scipy.special import rel_entr, softmax
+    rng = np.random.default_rng(16)
+    R, V = 40, 200
+    x = (rng.standard_normal((R, V)) * np.linspace(0.5, 6.0, R)[:, None]).astype(np.float32)
+    y = (x + rng.standard_normal((R, V)) * 0.005).astype(np.float32)
+    p = np.array([softmax(x[i].astype(np.float64)) for i in range(R)])
+    kl = np.array([rel_entr(p[i], softmax(y[i].astype(np.float64))).sum() for i in range(R)])
+    conf = p.max(1)
+    gate = float(np.median(conf))
+    r = oracle.posterior(x, y, np.zeros(R, np.uint8), 1e-3, conf_gate=gate)
+    want = (kl <= 1e-3) & (conf >= gate)
+    assert np.array_equal(r["locked"].astype(bool), want)
+    assert want.any() and ((kl <= 1e-3) & ~want).any()
+    assert np.array_equal(oracle.posterior(x, y, np.zeros(R, np.uint8), 1e-3, conf_gate=0.0)["locked"],
+                          (kl <= 1e-3).astype(np.uint8))
+
+
 def test_locked_rows_not_recomputed():
     rng = np.random.default_rng(6)
     x = (rng.standard_normal((8, 300))).astype(np.float32)

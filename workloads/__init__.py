@@ -491,6 +491,63 @@ LOOPS = {
 }
 
 
+# --------------------------------------------------------------------------
+# A layer's active-row projections and feed-forward
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LayerCase:
+    """Inputs of one layer's active-row projections and SwiGLU feed-forward:
+    hidden states, the active rows, synthetic weights [out, in] and the
+    attention output / residual rows that the later calls take."""
+    name: str
+    B: int
+    n_pos: int
+    d: int
+    Hq: int
+    Hkv: int
+    D: int
+    F: int
+    M: int
+    x: np.ndarray               # bf16 bits [B, n_pos, d]
+    active_idx: np.ndarray      # int32 [B, M], ascending
+    m: np.ndarray               # int32 [B]: valid rows per batch entry
+    w_qkv: np.ndarray           # bf16 bits [(Hq + 2 Hkv) D, d]
+    w_o: np.ndarray             # bf16 bits [d, Hq D]
+    w_gate: np.ndarray          # bf16 bits [F, d]
+    w_up: np.ndarray            # bf16 bits [F, d]
+    w_down: np.ndarray          # bf16 bits [d, F]
+    attn_out: np.ndarray        # bf16 bits [B, Hq, M, D]
+    h: np.ndarray               # bf16 bits [B, M, d]
+
+
+def make_layer(name, *, B, n_pos, d, Hq, Hkv, D, F, M, m=None, config_id=95, seed=0) -> LayerCase:
+    """Hidden states and residual rows N(0, 1); weights N(0, 1/sqrt(fan_in))
+    (activations stay of order one); attention output N(0, 0.5).  The M
+    active positions of each sequence are a seeded ascending subset."""
+    rs = _streams(config_id, seed)
+    act = sorted_subset(rs["active"], B, 0, n_pos, M)
+    m = np.full(B, M, np.int32) if m is None else np.asarray(m, np.int32)
+    wq = rs["k"]
+    return LayerCase(
+        name=name, B=B, n_pos=n_pos, d=d, Hq=Hq, Hkv=Hkv, D=D, F=F, M=M,
+        x=_normal_bf16(rs["cache_k"], (B, n_pos, d), 1.0), active_idx=act, m=m,
+        w_qkv=_normal_bf16(wq, ((Hq + 2 * Hkv) * D, d), 1.0 / np.sqrt(d)),
+        w_o=_normal_bf16(wq, (d, Hq * D), 1.0 / np.sqrt(Hq * D)),
+        w_gate=_normal_bf16(rs["v"], (F, d), 1.0 / np.sqrt(d)),
+        w_up=_normal_bf16(rs["v"], (F, d), 1.0 / np.sqrt(d)),
+        w_down=_normal_bf16(rs["v"], (d, F), 1.0 / np.sqrt(F)),
+        attn_out=_normal_bf16(rs["q"], (B, Hq, M, D), 0.5),
+        h=_normal_bf16(rs["cache_v"], (B, M, d), 1.0))
+
+
+def layer_llada(seed=0, M=1024, n_pos=1024) -> LayerCase:
+    """LLaDA-8B-shaped layer: width 4096, 32 heads of 128, feed-forward
+    width 12288 (SwiGLU), B=1; M active rows of n_pos positions."""
+    return make_layer("layer_llada", B=1, n_pos=n_pos, d=4096, Hq=32, Hkv=32, D=128, F=12288, M=M,
+                      config_id=96, seed=seed)
+
+
 CONFIGS = {
     "tiny": tiny,
     "llada_bidirectional": llada_bidirectional,
