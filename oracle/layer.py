@@ -55,7 +55,7 @@ def proj_out(x_bits, act, m, attn_out_bits, w_o_bits):
     ao = _f64(attn_out_bits)                           # [B, Hq, M, D]
     res = []
     for b, xr in enumerate(rows(x_bits, act, m)):
-        a = ao[b, :, :m[b], :].transpose(1, 0, 2).reshape(m[b], -1)   # [m, Hq D]
+        a = ao[b, :, :m[b], :].transpose(1, 0, 2).reshape(m[b], ao.shape[1] * ao.shape[3])   # [m, Hq D]
         res.append(xr + a @ w.T)
     return res
 

@@ -137,8 +137,8 @@ MUTANTS = [
     ("residual_dropped", "res.append(xr + a @ w.T)", "res.append(a @ w.T)"),
     ("gather_by_index", "return [x[b, act[b, :m[b]]] for b", "return [x[b, :m[b]] for b"),
     ("k_v_swapped", "k = y[:, Hq * D:(Hq + Hkv) * D]", "k = y[:, (Hq + Hkv) * D:]"),
-    ("heads_not_concatenated", "a = ao[b, :, :m[b], :].transpose(1, 0, 2).reshape(m[b], -1)",
-     "a = ao[b, :, :m[b], :].reshape(m[b], -1)"),
+    ("heads_not_concatenated", "a = ao[b, :, :m[b], :].transpose(1, 0, 2).reshape(",
+     "a = ao[b, :, :m[b], :].reshape("),
     ("down_residual_dropped", "return [h[b, :m[b]] + g[b] @ wd.T", "return [g[b] @ wd.T"),
     ("up_ignored", "silu(h[b, :m[b]] @ wg.T) * (h[b, :m[b]] @ wu.T)", "silu(h[b, :m[b]] @ wg.T)"),
 ]
