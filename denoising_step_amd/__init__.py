@@ -31,7 +31,7 @@ ROW_SELECT, ROW_LOCK = 1, 2
 
 EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
            "dlm_posterior_workspace_bytes", "dlm_block_buffer_init", "dlm_block_buffer_advance",
-           "dlm_last_error")
+           "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_ffn_workspace_bytes", "dlm_last_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -87,7 +87,15 @@ class _Select(ctypes.Structure):
                 ("tau", ctypes.c_float), ("score", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("score_ready", ctypes.c_void_p), ("margin", ctypes.c_void_p),
-                ("entropy", ctypes.c_void_p), ("row_flags", ctypes.c_void_p)]
+                ("entropy", ctypes.c_void_p), ("row_flags", ctypes.c_void_p),
+                ("conf_gate", ctypes.c_float)]
+
+
+class _LayerDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("n_pos", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("M", ctypes.c_int32), ("active_idx", ctypes.c_void_p), ("m_active", ctypes.c_void_p),
+                ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("F", ctypes.c_int32)]
 
 
 class _BlockBuffer(ctypes.Structure):
@@ -117,6 +125,15 @@ lib.dlm_block_buffer_init.argtypes = [ctypes.POINTER(_BlockBuffer), _P]
 lib.dlm_block_buffer_init.restype = ctypes.c_int
 lib.dlm_block_buffer_advance.argtypes = [ctypes.POINTER(_BlockBuffer), _P, _P]
 lib.dlm_block_buffer_advance.restype = ctypes.c_int
+_LP = ctypes.POINTER(_LayerDesc)
+lib.dlm_proj_qkv.argtypes = [_LP, _P, _P, _P, _P, _P, _P]
+lib.dlm_proj_qkv.restype = ctypes.c_int
+lib.dlm_proj_out.argtypes = [_LP, _P, _P, _P, _P, _P]
+lib.dlm_proj_out.restype = ctypes.c_int
+lib.dlm_ffn.argtypes = [_LP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+lib.dlm_ffn.restype = ctypes.c_int
+lib.dlm_ffn_workspace_bytes.argtypes = [_LP, ctypes.POINTER(ctypes.c_size_t)]
+lib.dlm_ffn_workspace_bytes.restype = ctypes.c_int
 lib.dlm_last_error.argtypes = []
 lib.dlm_last_error.restype = ctypes.c_char_p
 
@@ -184,6 +201,22 @@ class Select:
     margin: object = None       # optional fp32 [R] output
     entropy: object = None      # optional fp32 [R] output
     row_flags: object = None    # optional uint8 [R]: ROW_SELECT | ROW_LOCK per row
+    conf_gate: float = 0.0      # lock only if also conf >= conf_gate (0: no gate)
+
+
+@dataclasses.dataclass
+class LayerDesc:
+    """Shapes and active rows of one layer's projections and feed-forward."""
+    B: int
+    n_pos: int
+    d: int
+    M: int
+    active_idx: object = None  # int32 [B, M]
+    m_active: object = None    # optional int32 [B]
+    Hq: int = 1
+    Hkv: int = 1
+    D: int = 64
+    F: int = 64
 
 
 @dataclasses.dataclass
@@ -246,7 +279,11 @@ def _c_sel(s: Select) -> _Select:
         if not ev:
             raise DlmError(-1, "select.score_ready: the event has not been recorded")
     return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb, ev or None,
-                   _ptr(s.margin), _ptr(s.entropy), _ptr(s.row_flags))
+                   _ptr(s.margin), _ptr(s.entropy), _ptr(s.row_flags), s.conf_gate)
+
+
+def _c_layer(L: LayerDesc) -> _LayerDesc:
+    return _LayerDesc(L.B, L.n_pos, L.d, L.M, _ptr(L.active_idx), _ptr(L.m_active), L.Hq, L.Hkv, L.D, L.F)
 
 
 def _c_bb(bb: BlockBuffer) -> _BlockBuffer:
@@ -364,3 +401,52 @@ def dlm_block_buffer_advance(bb: BlockBuffer, sel, stream=None) -> None:
     _expect(sel, "sel", (bb.B, bb.n_gen), "torch.int32")
     c = _c_bb(bb)
     _check(lib.dlm_block_buffer_advance(ctypes.byref(c), _ptr(sel), _stream(stream)))
+
+
+def _expect_layer(L: LayerDesc):
+    _expect(L.active_idx, "active_idx", (L.B, L.M), "torch.int32")
+    if L.m_active is not None:
+        _expect(L.m_active, "m_active", (L.B,), "torch.int32")
+
+
+def dlm_proj_qkv(layer: LayerDesc, x, w_qkv, q, k, v, stream=None) -> None:
+    L = layer
+    _expect_layer(L)
+    _expect(x, "x", (L.B, L.n_pos, L.d), "torch.bfloat16")
+    _expect(w_qkv, "w_qkv", ((L.Hq + 2 * L.Hkv) * L.D, L.d), "torch.bfloat16")
+    _expect(q, "q", (L.B, L.Hq, L.M, L.D), "torch.bfloat16")
+    _expect(k, "k", (L.B, L.Hkv, L.M, L.D), "torch.bfloat16")
+    _expect(v, "v", (L.B, L.Hkv, L.M, L.D), "torch.bfloat16")
+    c = _c_layer(L)
+    _check(lib.dlm_proj_qkv(ctypes.byref(c), _ptr(x), _ptr(w_qkv), _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+
+
+def dlm_proj_out(layer: LayerDesc, x, attn_out, w_o, h, stream=None) -> None:
+    L = layer
+    _expect_layer(L)
+    _expect(x, "x", (L.B, L.n_pos, L.d), "torch.bfloat16")
+    _expect(attn_out, "attn_out", (L.B, L.Hq, L.M, L.D), "torch.bfloat16")
+    _expect(w_o, "w_o", (L.d, L.Hq * L.D), "torch.bfloat16")
+    _expect(h, "h", (L.B, L.M, L.d), "torch.bfloat16")
+    c = _c_layer(L)
+    _check(lib.dlm_proj_out(ctypes.byref(c), _ptr(x), _ptr(attn_out), _ptr(w_o), _ptr(h), _stream(stream)))
+
+
+def dlm_ffn_workspace_bytes(layer: LayerDesc) -> int:
+    n = ctypes.c_size_t(0)
+    c = _c_layer(layer)
+    _check(lib.dlm_ffn_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
+    return n.value
+
+
+def dlm_ffn(layer: LayerDesc, h, w_gate, w_up, w_down, x, workspace, stream=None) -> None:
+    L = layer
+    _expect_layer(L)
+    _expect(h, "h", (L.B, L.M, L.d), "torch.bfloat16")
+    _expect(w_gate, "w_gate", (L.F, L.d), "torch.bfloat16")
+    _expect(w_up, "w_up", (L.F, L.d), "torch.bfloat16")
+    _expect(w_down, "w_down", (L.d, L.F), "torch.bfloat16")
+    _expect(x, "x", (L.B, L.n_pos, L.d), "torch.bfloat16")
+    c = _c_layer(L)
+    _check(lib.dlm_ffn(ctypes.byref(c), _ptr(h), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x),
+                       _ptr(workspace), _nbytes(workspace), _stream(stream)))

@@ -216,6 +216,7 @@ static int check_post_scalars(int32_t R, int32_t V, const dlm_select *s)
         return fail(DLM_E_DESC, "k=%d must be >= 0", s->k);
     if ((s->mode == DLM_SEL_THRESH_CONF || s->mode == DLM_SEL_ATTN_DYNAMIC) && !isfinite(s->tau))
         return fail(DLM_E_DESC, "tau must be finite");
+    if (!isfinite(s->conf_gate)) return fail(DLM_E_DESC, "conf_gate must be finite");
     return DLM_OK;
 }
 
@@ -253,9 +254,44 @@ int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked
     a.flags = select->row_flags;
     a.part = static_cast<dlm::PostPartial *>(select->workspace);
     a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
-    a.eps = eps; a.tau = select->tau; a.n_chunks = p.n_chunks; a.chunk = p.chunk;
+    a.eps = eps; a.tau = select->tau; a.conf_gate = select->conf_gate;
+    a.n_chunks = p.n_chunks; a.chunk = p.chunk;
     hipError_t e = dlm::launch_posterior(a, stream, select->score_ready);
     if (e != hipSuccess) return fail(DLM_E_HIP, "launch or event wait failed: %s", hipGetErrorString(e));
+    return DLM_OK;
+}
+
+static int check_layer(const dlm_layer_desc *L)
+{
+    if (!L) return fail(DLM_E_NULL, "layer descriptor is NULL");
+    if (L->B < 1 || L->n_pos < 1 || L->M < 0 || L->d < 1 || L->F < 1 || L->Hq < 1 || L->Hkv < 1 || L->D < 1)
+        return fail(DLM_E_SHAPE, "B=%d n_pos=%d M=%d d=%d F=%d Hq=%d Hkv=%d D=%d out of range", L->B, L->n_pos,
+                    L->M, L->d, L->F, L->Hq, L->Hkv, L->D);
+    if (L->d % 64 != 0 || L->F % 64 != 0)
+        return fail(DLM_E_UNSUPPORTED, "d=%d and F=%d must be multiples of 64", L->d, L->F);
+    if (L->Hq % L->Hkv != 0) return fail(DLM_E_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", L->Hq, L->Hkv);
+    const long big = (1L << 31) - 1;
+    const long rows = (long)L->B * L->M;
+    const long wq = (long)(L->Hq + 2 * L->Hkv) * L->D;
+    if ((long)L->B * L->n_pos * L->d * 2 > big || rows * L->F * 2 > big || rows * L->d * 2 > big ||
+        rows * wq * 2 > big || wq * L->d * 2 > big || (long)L->F * L->d * 2 > big || (long)L->Hq * L->D * L->d * 2 > big)
+        return fail(DLM_E_SHAPE, "a tensor of the layer exceeds 2 GiB");
+    if (L->M > 0 && !L->active_idx) return fail(DLM_E_NULL, "active_idx is NULL");
+    return DLM_OK;
+}
+
+static dlm::GemmArgs gemm_base(const dlm_layer_desc *L)
+{
+    dlm::GemmArgs a{};
+    a.act = L->active_idx; a.m_valid = L->m_active;
+    a.B = L->B; a.M = L->M; a.n_pos = L->n_pos; a.Hq = L->Hq; a.Hkv = L->Hkv; a.D = L->D;
+    return a;
+}
+
+static int run_gemm(const dlm::GemmArgs &a, hipStream_t stream)
+{
+    hipError_t e = dlm::launch_gemm(a, stream);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return DLM_OK;
 }
 
@@ -288,6 +324,86 @@ static int run_bb(const dlm_block_buffer *bb, const int32_t *sel, hipStream_t st
     hipError_t e = dlm::launch_block_buffer(a, stream);
     if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return DLM_OK;
+}
+
+int dlm_proj_qkv(const dlm_layer_desc *L, const void *x, const void *w_qkv, void *q, void *k, void *v,
+                 hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_layer(L);
+    if (rc != DLM_OK) return rc;
+    if (!x || !w_qkv || (L->M > 0 && (!q || !k || !v))) return fail(DLM_E_NULL, "x, w_qkv, q, k and v must be non-NULL");
+    if (L->M == 0) return DLM_OK;
+    dlm::GemmArgs a = gemm_base(L);
+    a.a = static_cast<const uint16_t *>(x);
+    a.a_bytes = (long)L->B * L->n_pos * L->d * 2;
+    a.a_mode = 1; a.ep_mode = 1;
+    a.K = L->d; a.N = (L->Hq + 2 * L->Hkv) * L->D;
+    a.w0 = static_cast<const uint16_t *>(w_qkv);
+    a.out = static_cast<uint16_t *>(q); a.out_k = static_cast<uint16_t *>(k); a.out_v = static_cast<uint16_t *>(v);
+    return run_gemm(a, stream);
+}
+
+int dlm_proj_out(const dlm_layer_desc *L, const void *x, const void *attn_out, const void *w_o, void *h,
+                 hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_layer(L);
+    if (rc != DLM_OK) return rc;
+    if (L->D % 64 != 0) return fail(DLM_E_UNSUPPORTED, "dlm_proj_out needs D a multiple of 64 (D=%d)", L->D);
+    if (!x || !w_o || (L->M > 0 && (!attn_out || !h))) return fail(DLM_E_NULL, "x, attn_out, w_o and h must be non-NULL");
+    if (L->M == 0) return DLM_OK;
+    dlm::GemmArgs a = gemm_base(L);
+    a.a = static_cast<const uint16_t *>(attn_out);
+    a.a_bytes = (long)L->B * L->Hq * L->M * L->D * 2;
+    a.a_mode = 2; a.ep_mode = 2; a.resid_gather = 1;
+    a.K = L->Hq * L->D; a.N = L->d;
+    a.w0 = static_cast<const uint16_t *>(w_o);
+    a.resid = static_cast<const uint16_t *>(x);
+    a.out = static_cast<uint16_t *>(h);
+    return run_gemm(a, stream);
+}
+
+int dlm_ffn_workspace_bytes(const dlm_layer_desc *L, size_t *bytes)
+{
+    g_err[0] = 0;
+    if (!bytes) return fail(DLM_E_NULL, "bytes is NULL");
+    int rc = check_layer(L);
+    if (rc != DLM_OK) return rc;
+    *bytes = (size_t)L->B * L->M * L->F * 2;
+    return DLM_OK;
+}
+
+int dlm_ffn(const dlm_layer_desc *L, const void *h, const void *w_gate, const void *w_up, const void *w_down,
+            void *x, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_layer(L);
+    if (rc != DLM_OK) return rc;
+    if (!w_gate || !w_up || !w_down || !x || (L->M > 0 && !h))
+        return fail(DLM_E_NULL, "h, w_gate, w_up, w_down and x must be non-NULL");
+    if (L->M == 0) return DLM_OK;
+    const size_t need = (size_t)L->B * L->M * L->F * 2;
+    if (!workspace || workspace_bytes < need)
+        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    dlm::GemmArgs g = gemm_base(L);      // gated hidden rows: silu(h Wg^T) * (h Wu^T)
+    g.a = static_cast<const uint16_t *>(h);
+    g.a_bytes = (long)L->B * L->M * L->d * 2;
+    g.a_mode = 0; g.ep_mode = 0;
+    g.K = L->d; g.N = L->F;
+    g.w0 = static_cast<const uint16_t *>(w_gate); g.w1 = static_cast<const uint16_t *>(w_up);
+    g.out = static_cast<uint16_t *>(workspace);
+    rc = run_gemm(g, stream);
+    if (rc != DLM_OK) return rc;
+    dlm::GemmArgs d = gemm_base(L);      // down projection + residual, back to x's active rows
+    d.a = static_cast<const uint16_t *>(workspace);
+    d.a_bytes = (long)need;
+    d.a_mode = 0; d.ep_mode = 3; d.resid_gather = 0;
+    d.K = L->F; d.N = L->d;
+    d.w0 = static_cast<const uint16_t *>(w_down);
+    d.resid = static_cast<const uint16_t *>(h);
+    d.out = static_cast<uint16_t *>(x);
+    return run_gemm(d, stream);
 }
 
 int dlm_block_buffer_init(const dlm_block_buffer *bb, hipStream_t stream)

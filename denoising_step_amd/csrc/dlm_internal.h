@@ -92,7 +92,7 @@ struct PostArgs {
     const uint8_t *flags;           // optional [R]: bit 0 selectable, bit 1 lockable
     PostPartial *part;
     int R, V, mode, k, group_rows;
-    float eps, tau;
+    float eps, tau, conf_gate;
     int n_chunks, chunk;
 };
 
@@ -108,6 +108,21 @@ struct BBArgs {
     int B, n_slots, bs, max_active, P, n_gen;
 };
 
+// One active-row product C = A W^T with its epilogue (gemm_kernels.hip).
+struct GemmArgs {
+    const uint16_t *a;              // A rows: see a_mode
+    long a_bytes;                   // size of the A tensor (loads past it read zero)
+    const int32_t *act;             // active_idx [B, M] (gather modes)
+    const int32_t *m_valid;         // optional device [B] row counts
+    const uint16_t *w0, *w1;        // W [N, K]; w1: the up matrix of SwiGLU (else nullptr)
+    uint16_t *out, *out_k, *out_v;  // outputs (QKV: q, k, v)
+    const uint16_t *resid;          // residual rows (EP_RESID, EP_SCATTER)
+    int a_mode;                     // 0 plain [B*M, K], 1 gather x[b, act, :], 2 heads out[b, h, j, d]
+    int ep_mode;                    // 0 plain / SwiGLU, 1 QKV, 2 residual to compact rows, 3 residual scattered to x
+    int resid_gather;               // residual row: 1 x[b, act[b, j]], 0 resid[b * M + j]
+    int B, M, K, N, n_pos, Hq, Hkv, D;
+};
+
 // Valid rows of batch entry b: all M unless a device count is given.
 __device__ __forceinline__ int valid_rows(const AttnArgs &a, int b)
 {
@@ -118,6 +133,7 @@ __device__ __forceinline__ int valid_rows(const AttnArgs &a, int b)
 hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after);
 hipError_t launch_block_buffer(const BBArgs &a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
 
 // Map a hardware workgroup id to a logical one so that logically
 // consecutive workgroups (which share K/V) run on the same XCD: the

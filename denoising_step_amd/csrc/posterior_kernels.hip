@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                     klv = s.tx / s.sx - (s.mx - s.my) - (logf(s.sx) - logf(s.sy));
                     cf = 1.f / s.sx;
                     tok = s.ai;
-                    a.locked[r] = (klv <= a.eps && (rowf_s[gt] & 4)) ? 1 : 0;
+                    a.locked[r] = (klv <= a.eps && (rowf_s[gt] & 4) && cf >= a.conf_gate) ? 1 : 0;
                     // margin = p(top-1) - p(top-2) = conf * (1 - exp(a2 - mx)): exactly
                     // 0 on a tie, conf without a runner-up; entropy = ln sx - ex / sx
                     mg = cf * (1.f - fast_exp2((s.a2 - s.mx) * kLog2e));

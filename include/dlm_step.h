@@ -223,6 +223,9 @@ typedef struct {
                                 a converged, already unmasked token stops).  A row
                                 without DLM_ROW_LOCK keeps locked[r] = 0 whatever its
                                 KL; its kl, conf and scores are still written. */
+    float conf_gate;         /* the optional confidence gate of the lock test (SureLock
+                                page, sec. 2: a peaked posterior): a row locks only if
+                                also conf >= conf_gate.  0 (no gate) or any finite value. */
 } dlm_select;
 
 /* Bits of dlm_select.row_flags. */
@@ -236,8 +239,8 @@ enum { DLM_ROW_SELECT = 1, DLM_ROW_LOCK = 2 };
  *   p_t = softmax(logits[r]), p_{t-1} = softmax(prev_logits[r])
  *   kl[r]   = KL(p_t || p_{t-1}) = sum_v p_t(v) (log p_t(v) - log p_{t-1}(v))
  *   conf[r] = max_v p_t(v);  tok = lowest v with the largest logit
- *   locked[r] = 1 if kl[r] <= eps and the row may lock (row_flags; a lock
- *               is never undone)
+ *   locked[r] = 1 if kl[r] <= eps, the row may lock (row_flags) and
+ *               conf[r] >= conf_gate (a lock is never undone)
  *   sel[r]  = tok if the row is selected (mode above), else -1.
  * A row that arrives locked is not read: kl = conf = 0, sel = -1, stays locked.
  * kl and conf are fp32; KL is computed in one pass as
@@ -333,6 +336,62 @@ int dlm_block_buffer_init(const dlm_block_buffer *bb, hipStream_t stream);
  * One kernel on `stream`.  Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_HIP. */
 int dlm_block_buffer_advance(const dlm_block_buffer *bb, const int32_t *sel,
                              hipStream_t stream);
+
+/*
+ * Active-row projections and feed-forward of one layer (SureLock page,
+ * sec. 2: a locked position skips its query projection and its feed-forward
+ * sub-layer, so a step's dense work is O(M_t d^2) over the active rows).
+ *
+ * The rows are those of dlm_step_attn: row j of batch entry b is the position
+ * active_idx[b, j], j < M (j < m_active[b] when m_active is given).  Weights
+ * are bf16, row-major [out_features, in_features]; products accumulate in
+ * fp32 and results are rounded to bf16 (nearest even).  The layer is
+ *   q | k | v = x[act] W_qkv^T                       (dlm_proj_qkv)
+ *   h         = x[act] + attn_out W_o^T              (dlm_proj_out)
+ *   x[act]    = h + (silu(h W_gate^T) * (h W_up^T)) W_down^T   (dlm_ffn)
+ * silu(z) = z / (1 + exp(-z)).  The layer's normalisations are not part of
+ * these calls.  Rows of locked positions are neither read nor written.
+ */
+typedef struct {
+    int32_t B;                  /* batch entries, >= 1 */
+    int32_t n_pos;              /* positions of the hidden states x: bf16 [B, n_pos, d] */
+    int32_t d;                  /* model width, a multiple of 64 */
+    int32_t M;                  /* active rows per batch entry (row capacity), >= 0 */
+    const int32_t *active_idx;  /* device int32 [B, M], positions in [0, n_pos) */
+    const int32_t *m_active;    /* optional device int32 [B] (NULL: all M rows) */
+    int32_t Hq, Hkv, D;         /* attention heads (Hq % Hkv == 0) and head width */
+    int32_t F;                  /* feed-forward width, a multiple of 64 */
+} dlm_layer_desc;
+
+/* q | k | v projection of the active rows.
+ *   x      bf16 [B, n_pos, d]
+ *   w_qkv  bf16 [(Hq + 2 Hkv) * D, d]: the q rows (head-major), then k, then v
+ *   q      bf16 [B, Hq, M, D] out;  k, v  bf16 [B, Hkv, M, D] out
+ * (the layouts dlm_step_attn reads).  Errors: DLM_E_NULL, DLM_E_SHAPE,
+ * DLM_E_UNSUPPORTED, DLM_E_HIP. */
+int dlm_proj_qkv(const dlm_layer_desc *layer, const void *x, const void *w_qkv, void *q, void *k,
+                 void *v, hipStream_t stream);
+
+/* Output projection with the residual: h = x[act] + attn_out W_o^T.
+ *   attn_out  bf16 [B, Hq, M, D] (dlm_step_attn's out); D a multiple of 64
+ *   w_o       bf16 [d, Hq * D]
+ *   h         bf16 [B, M, d] out
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_HIP. */
+int dlm_proj_out(const dlm_layer_desc *layer, const void *x, const void *attn_out, const void *w_o,
+                 void *h, hipStream_t stream);
+
+/* SwiGLU feed-forward with the residual, written back to the active rows of
+ * x: x[b, active_idx[b, j], :] = h + (silu(h W_gate^T) * (h W_up^T)) W_down^T.
+ *   h               bf16 [B, M, d]
+ *   w_gate, w_up    bf16 [F, d];  w_down  bf16 [d, F]
+ *   x               bf16 [B, n_pos, d] in/out (only active rows written)
+ *   workspace       the gated hidden rows, bf16 [B * M, F] (rounded there)
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_WORKSPACE, DLM_E_HIP. */
+int dlm_ffn(const dlm_layer_desc *layer, const void *h, const void *w_gate, const void *w_up,
+            const void *w_down, void *x, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of dlm_ffn.  Writes *bytes. */
+int dlm_ffn_workspace_bytes(const dlm_layer_desc *layer, size_t *bytes);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *dlm_last_error(void);

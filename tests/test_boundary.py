@@ -232,3 +232,52 @@ def test_block_buffer_advance_needs_sel():
     import ctypes
     assert dlm.lib.dlm_block_buffer_init(None, None) == dlm.DLM_E_NULL
     assert dlm.lib.dlm_block_buffer_advance(None, FAKE, None) == dlm.DLM_E_NULL
+
+
+def _layer(**kw):
+    base = dict(B=2, n_pos=100, d=256, M=40, active_idx=FAKE, Hq=4, Hkv=2, D=64, F=384)
+    base.update(kw)
+    return dlm.LayerDesc(**base)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(B=0), dlm.DLM_E_SHAPE),
+    (dict(d=0), dlm.DLM_E_SHAPE),
+    (dict(M=-1), dlm.DLM_E_SHAPE),
+    (dict(d=100), dlm.DLM_E_UNSUPPORTED),
+    (dict(F=100), dlm.DLM_E_UNSUPPORTED),
+    (dict(Hq=3), dlm.DLM_E_UNSUPPORTED),
+    (dict(n_pos=1 << 20, d=4096), dlm.DLM_E_SHAPE),
+    (dict(active_idx=None), dlm.DLM_E_NULL),
+])
+def test_layer_calls_reject(case, code):
+    L = _layer(**case)
+    for call in (lambda: dlm.dlm_proj_qkv(L, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
+                 lambda: dlm.dlm_proj_out(L, FAKE, FAKE, FAKE, FAKE, stream=0),
+                 lambda: dlm.dlm_ffn(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
+                 lambda: dlm.dlm_ffn_workspace_bytes(L)):
+        with pytest.raises(dlm.DlmError) as e:
+            call()
+        assert e.value.code == code
+
+
+def test_layer_call_specific_checks():
+    with pytest.raises(dlm.DlmError) as e:          # heads of 32 do not tile the K steps of 64
+        dlm.dlm_proj_out(_layer(D=32), FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == dlm.DLM_E_UNSUPPORTED
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_proj_qkv(_layer(), FAKE, None, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.code == dlm.DLM_E_NULL
+    L = _layer()
+    need = dlm.dlm_ffn_workspace_bytes(L)
+    assert need == 2 * 40 * 384 * 2
+    import ctypes
+    c = dlm._c_layer(L)
+    rc = dlm.lib.dlm_ffn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
+    assert rc == dlm.DLM_E_WORKSPACE
+    assert dlm.lib.dlm_proj_qkv(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == dlm.DLM_E_NULL
+
+
+def test_posterior_rejects_nan_gate():
+    assert _post(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=2, group_rows=16, conf_gate=float("nan"))) \
+        == dlm.DLM_E_DESC
