@@ -293,6 +293,70 @@ def loop_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def layer_bench(args):
+    """The active-row projections and feed-forward of one LLaDA-8B-shaped
+    layer (width 4096, 32 heads of 128, SwiGLU width 12288, B=1, 2048
+    positions) for a range of active-row counts M_t: each call timed alone
+    with HIP events, against the bf16 MFMA peak (2 M N K flops) and the
+    weight bytes read (the bound at small M_t).  Two sets of weights rotate
+    so their footprint exceeds the 256 MB MALL.  Prints one JSON line."""
+    import torch
+
+    import denoising_step_amd as dlm
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    d, Hq, Hkv, D, F, n_pos = 4096, 32, 32, 128, 12288, 2048
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def w(shape, fan_in):
+        return (torch.randn(shape, generator=gen, device=dev) / math.sqrt(fan_in)).to(torch.bfloat16)
+
+    sets = [dict(qkv=w(((Hq + 2 * Hkv) * D, d), d), o=w((d, Hq * D), Hq * D), g=w((F, d), d),
+                 u=w((F, d), d), dn=w((d, F), F)) for _ in range(2)]
+    x = torch.randn((1, n_pos, d), generator=gen, device=dev).to(torch.bfloat16)
+    res = []
+    for M in (1024, 512, 256, 128, 64, 16):
+        act = torch.sort(torch.randperm(n_pos, generator=gen, device=dev)[:M])[0].to(torch.int32)[None]
+        L = dlm.LayerDesc(B=1, n_pos=n_pos, d=d, M=M, active_idx=act, Hq=Hq, Hkv=Hkv, D=D, F=F)
+        q = torch.empty((1, Hq, M, D), dtype=torch.bfloat16, device=dev)
+        k = torch.empty((1, Hkv, M, D), dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        ao = torch.randn((1, Hq, M, D), generator=gen, device=dev).to(torch.bfloat16)
+        h = torch.empty((1, M, d), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(1, dlm.dlm_layer_workspace_bytes(L)), dtype=torch.uint8, device=dev)
+        calls = {
+            "qkv": (lambda i: dlm.dlm_proj_qkv(L, x, sets[i]["qkv"], q, k, v, ws),
+                    (Hq + 2 * Hkv) * D, d),
+            "out": (lambda i: dlm.dlm_proj_out(L, x, ao, sets[i]["o"], h, ws), d, Hq * D),
+            "ffn": (lambda i: dlm.dlm_ffn(L, h, sets[i]["g"], sets[i]["u"], sets[i]["dn"], x, ws),
+                    None, None),
+        }
+        row = {"M_t": M}
+        for name, (fn, N, K) in calls.items():
+            ms = time_loop(fn, 2, args.steps, args.warmup)
+            if name == "ffn":
+                flops = 2.0 * M * (2 * F * d + d * F)
+                wbytes = 3.0 * F * d * 2
+            else:
+                flops = 2.0 * M * N * K
+                wbytes = 2.0 * N * K
+            row[name] = {"us": round(ms * 1e3, 2), "tflops": round(flops / ms / 1e9, 1),
+                         "mfma_frac": round(flops / ms / 1e9 / 2500.0, 3),
+                         "weight_gbs": round(wbytes / ms / 1e6, 0),
+                         "hbm_frac": round(wbytes / ms / 1e6 / 8000.0, 3)}
+        res.append(row)
+        print(f"layer M_t={M}: " + " ".join(f"{n}={row[n]['us']}us/{row[n]['tflops']}TF"
+                                           for n in calls), file=sys.stderr, flush=True)
+    line = {"metric": "active-row projections and feed-forward of one layer", "unit": "us",
+            "n_gpus": 1, "dtype": "bf16", "data": "synthetic (random weights drawn on the device)",
+            "config": {"workload": "layer_llada", "d": d, "Hq": Hq, "Hkv": Hkv, "D": D, "F": F,
+                       "positions": n_pos},
+            "peak": {"mfma_bf16_tflops": 2500.0, "hbm_gbs": 8000.0}, "rows": res}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,6 +369,8 @@ def main():
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
     ap.add_argument("--loop", action="store_true",
                     help="time a whole multi-step SureLock run instead (its own JSON line)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time a layer's active-row projections and feed-forward instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -315,6 +381,9 @@ def main():
         return
     if args.loop:
         loop_bench(args)
+        return
+    if args.layer:
+        layer_bench(args)
         return
 
     import numpy as np

@@ -31,7 +31,7 @@ ROW_SELECT, ROW_LOCK = 1, 2
 
 EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
            "dlm_posterior_workspace_bytes", "dlm_block_buffer_init", "dlm_block_buffer_advance",
-           "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_ffn_workspace_bytes", "dlm_last_error")
+           "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_layer_workspace_bytes", "dlm_last_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -126,14 +126,14 @@ lib.dlm_block_buffer_init.restype = ctypes.c_int
 lib.dlm_block_buffer_advance.argtypes = [ctypes.POINTER(_BlockBuffer), _P, _P]
 lib.dlm_block_buffer_advance.restype = ctypes.c_int
 _LP = ctypes.POINTER(_LayerDesc)
-lib.dlm_proj_qkv.argtypes = [_LP, _P, _P, _P, _P, _P, _P]
+lib.dlm_proj_qkv.argtypes = [_LP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.dlm_proj_qkv.restype = ctypes.c_int
-lib.dlm_proj_out.argtypes = [_LP, _P, _P, _P, _P, _P]
+lib.dlm_proj_out.argtypes = [_LP, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.dlm_proj_out.restype = ctypes.c_int
 lib.dlm_ffn.argtypes = [_LP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.dlm_ffn.restype = ctypes.c_int
-lib.dlm_ffn_workspace_bytes.argtypes = [_LP, ctypes.POINTER(ctypes.c_size_t)]
-lib.dlm_ffn_workspace_bytes.restype = ctypes.c_int
+lib.dlm_layer_workspace_bytes.argtypes = [_LP, ctypes.POINTER(ctypes.c_size_t)]
+lib.dlm_layer_workspace_bytes.restype = ctypes.c_int
 lib.dlm_last_error.argtypes = []
 lib.dlm_last_error.restype = ctypes.c_char_p
 
@@ -409,7 +409,7 @@ def _expect_layer(L: LayerDesc):
         _expect(L.m_active, "m_active", (L.B,), "torch.int32")
 
 
-def dlm_proj_qkv(layer: LayerDesc, x, w_qkv, q, k, v, stream=None) -> None:
+def dlm_proj_qkv(layer: LayerDesc, x, w_qkv, q, k, v, workspace, stream=None) -> None:
     L = layer
     _expect_layer(L)
     _expect(x, "x", (L.B, L.n_pos, L.d), "torch.bfloat16")
@@ -418,10 +418,11 @@ def dlm_proj_qkv(layer: LayerDesc, x, w_qkv, q, k, v, stream=None) -> None:
     _expect(k, "k", (L.B, L.Hkv, L.M, L.D), "torch.bfloat16")
     _expect(v, "v", (L.B, L.Hkv, L.M, L.D), "torch.bfloat16")
     c = _c_layer(L)
-    _check(lib.dlm_proj_qkv(ctypes.byref(c), _ptr(x), _ptr(w_qkv), _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+    _check(lib.dlm_proj_qkv(ctypes.byref(c), _ptr(x), _ptr(w_qkv), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def dlm_proj_out(layer: LayerDesc, x, attn_out, w_o, h, stream=None) -> None:
+def dlm_proj_out(layer: LayerDesc, x, attn_out, w_o, h, workspace, stream=None) -> None:
     L = layer
     _expect_layer(L)
     _expect(x, "x", (L.B, L.n_pos, L.d), "torch.bfloat16")
@@ -429,13 +430,14 @@ def dlm_proj_out(layer: LayerDesc, x, attn_out, w_o, h, stream=None) -> None:
     _expect(w_o, "w_o", (L.d, L.Hq * L.D), "torch.bfloat16")
     _expect(h, "h", (L.B, L.M, L.d), "torch.bfloat16")
     c = _c_layer(L)
-    _check(lib.dlm_proj_out(ctypes.byref(c), _ptr(x), _ptr(attn_out), _ptr(w_o), _ptr(h), _stream(stream)))
+    _check(lib.dlm_proj_out(ctypes.byref(c), _ptr(x), _ptr(attn_out), _ptr(w_o), _ptr(h),
+                            _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def dlm_ffn_workspace_bytes(layer: LayerDesc) -> int:
+def dlm_layer_workspace_bytes(layer: LayerDesc) -> int:
     n = ctypes.c_size_t(0)
     c = _c_layer(layer)
-    _check(lib.dlm_ffn_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
+    _check(lib.dlm_layer_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
     return n.value
 
 

@@ -326,14 +326,64 @@ static int run_bb(const dlm_block_buffer *bb, const int32_t *sel, hipStream_t st
     return DLM_OK;
 }
 
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The products of the layer's calls and their K splits.
+struct LayerPlans {
+    dlm::GemmPlan qkv, out, gu, down;
+    size_t g_bytes;        // gated hidden rows (bf16)
+    size_t total;
+};
+static LayerPlans plan_layer(const dlm_layer_desc *L)
+{
+    LayerPlans p{};
+    const int rows = L->B * L->M;
+    p.qkv = dlm::plan_gemm(rows, (L->Hq + 2 * L->Hkv) * L->D, L->d, false);
+    p.out = dlm::plan_gemm(rows, L->d, L->Hq * L->D, false);
+    p.gu = dlm::plan_gemm(rows, L->F, L->d, true);
+    p.down = dlm::plan_gemm(rows, L->d, L->F, false);
+    p.g_bytes = al256((size_t)rows * L->F * 2);
+    size_t t = p.qkv.part_bytes > p.out.part_bytes ? p.qkv.part_bytes : p.out.part_bytes;
+    const size_t f = p.g_bytes + (p.gu.part_bytes > p.down.part_bytes ? p.gu.part_bytes : p.down.part_bytes);
+    p.total = t > f ? t : f;
+    return p;
+}
+
+static int check_ws(void *ws, size_t have, size_t need)
+{
+    if (need > 0 && (!ws || have < need))
+        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? have : (size_t)0);
+    return DLM_OK;
+}
+
+static void set_plan(dlm::GemmArgs &a, const dlm::GemmPlan &p, void *part)
+{
+    a.splits = p.splits;
+    a.kc = p.kc;
+    a.part = p.splits > 1 ? static_cast<float *>(part) : nullptr;
+}
+
+int dlm_layer_workspace_bytes(const dlm_layer_desc *L, size_t *bytes)
+{
+    g_err[0] = 0;
+    if (!bytes) return fail(DLM_E_NULL, "bytes is NULL");
+    int rc = check_layer(L);
+    if (rc != DLM_OK) return rc;
+    *bytes = plan_layer(L).total;
+    return DLM_OK;
+}
+
 int dlm_proj_qkv(const dlm_layer_desc *L, const void *x, const void *w_qkv, void *q, void *k, void *v,
-                 hipStream_t stream)
+                 void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     g_err[0] = 0;
     int rc = check_layer(L);
     if (rc != DLM_OK) return rc;
     if (!x || !w_qkv || (L->M > 0 && (!q || !k || !v))) return fail(DLM_E_NULL, "x, w_qkv, q, k and v must be non-NULL");
     if (L->M == 0) return DLM_OK;
+    const LayerPlans P = plan_layer(L);
+    rc = check_ws(workspace, workspace_bytes, P.qkv.part_bytes);
+    if (rc != DLM_OK) return rc;
     dlm::GemmArgs a = gemm_base(L);
     a.a = static_cast<const uint16_t *>(x);
     a.a_bytes = (long)L->B * L->n_pos * L->d * 2;
@@ -341,11 +391,12 @@ int dlm_proj_qkv(const dlm_layer_desc *L, const void *x, const void *w_qkv, void
     a.K = L->d; a.N = (L->Hq + 2 * L->Hkv) * L->D;
     a.w0 = static_cast<const uint16_t *>(w_qkv);
     a.out = static_cast<uint16_t *>(q); a.out_k = static_cast<uint16_t *>(k); a.out_v = static_cast<uint16_t *>(v);
+    set_plan(a, P.qkv, workspace);
     return run_gemm(a, stream);
 }
 
 int dlm_proj_out(const dlm_layer_desc *L, const void *x, const void *attn_out, const void *w_o, void *h,
-                 hipStream_t stream)
+                 void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     g_err[0] = 0;
     int rc = check_layer(L);
@@ -353,6 +404,9 @@ int dlm_proj_out(const dlm_layer_desc *L, const void *x, const void *attn_out, c
     if (L->D % 64 != 0) return fail(DLM_E_UNSUPPORTED, "dlm_proj_out needs D a multiple of 64 (D=%d)", L->D);
     if (!x || !w_o || (L->M > 0 && (!attn_out || !h))) return fail(DLM_E_NULL, "x, attn_out, w_o and h must be non-NULL");
     if (L->M == 0) return DLM_OK;
+    const LayerPlans P = plan_layer(L);
+    rc = check_ws(workspace, workspace_bytes, P.out.part_bytes);
+    if (rc != DLM_OK) return rc;
     dlm::GemmArgs a = gemm_base(L);
     a.a = static_cast<const uint16_t *>(attn_out);
     a.a_bytes = (long)L->B * L->Hq * L->M * L->D * 2;
@@ -361,17 +415,8 @@ int dlm_proj_out(const dlm_layer_desc *L, const void *x, const void *attn_out, c
     a.w0 = static_cast<const uint16_t *>(w_o);
     a.resid = static_cast<const uint16_t *>(x);
     a.out = static_cast<uint16_t *>(h);
+    set_plan(a, P.out, workspace);
     return run_gemm(a, stream);
-}
-
-int dlm_ffn_workspace_bytes(const dlm_layer_desc *L, size_t *bytes)
-{
-    g_err[0] = 0;
-    if (!bytes) return fail(DLM_E_NULL, "bytes is NULL");
-    int rc = check_layer(L);
-    if (rc != DLM_OK) return rc;
-    *bytes = (size_t)L->B * L->M * L->F * 2;
-    return DLM_OK;
 }
 
 int dlm_ffn(const dlm_layer_desc *L, const void *h, const void *w_gate, const void *w_up, const void *w_down,
@@ -383,26 +428,30 @@ int dlm_ffn(const dlm_layer_desc *L, const void *h, const void *w_gate, const vo
     if (!w_gate || !w_up || !w_down || !x || (L->M > 0 && !h))
         return fail(DLM_E_NULL, "h, w_gate, w_up, w_down and x must be non-NULL");
     if (L->M == 0) return DLM_OK;
-    const size_t need = (size_t)L->B * L->M * L->F * 2;
-    if (!workspace || workspace_bytes < need)
-        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    const LayerPlans P = plan_layer(L);
+    const size_t need = P.g_bytes + (P.gu.part_bytes > P.down.part_bytes ? P.gu.part_bytes : P.down.part_bytes);
+    rc = check_ws(workspace, workspace_bytes, need);
+    if (rc != DLM_OK) return rc;
+    char *ws = static_cast<char *>(workspace);
     dlm::GemmArgs g = gemm_base(L);      // gated hidden rows: silu(h Wg^T) * (h Wu^T)
     g.a = static_cast<const uint16_t *>(h);
     g.a_bytes = (long)L->B * L->M * L->d * 2;
     g.a_mode = 0; g.ep_mode = 0;
     g.K = L->d; g.N = L->F;
     g.w0 = static_cast<const uint16_t *>(w_gate); g.w1 = static_cast<const uint16_t *>(w_up);
-    g.out = static_cast<uint16_t *>(workspace);
+    g.out = reinterpret_cast<uint16_t *>(ws);
+    set_plan(g, P.gu, ws + P.g_bytes);
     rc = run_gemm(g, stream);
     if (rc != DLM_OK) return rc;
     dlm::GemmArgs d = gemm_base(L);      // down projection + residual, back to x's active rows
-    d.a = static_cast<const uint16_t *>(workspace);
-    d.a_bytes = (long)need;
+    d.a = reinterpret_cast<const uint16_t *>(ws);
+    d.a_bytes = (long)L->B * L->M * L->F * 2;
     d.a_mode = 0; d.ep_mode = 3; d.resid_gather = 0;
     d.K = L->F; d.N = L->d;
     d.w0 = static_cast<const uint16_t *>(w_down);
     d.resid = static_cast<const uint16_t *>(h);
     d.out = static_cast<uint16_t *>(x);
+    set_plan(d, P.down, ws + P.g_bytes);
     return run_gemm(d, stream);
 }
 

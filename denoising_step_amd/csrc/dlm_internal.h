@@ -121,7 +121,14 @@ struct GemmArgs {
     int ep_mode;                    // 0 plain / SwiGLU, 1 QKV, 2 residual to compact rows, 3 residual scattered to x
     int resid_gather;               // residual row: 1 x[b, act[b, j]], 0 resid[b * M + j]
     int B, M, K, N, n_pos, Hq, Hkv, D;
+    int splits, kc;                 // K splits of kc columns each (1: one pass, fused epilogue)
+    float *part;                    // splits > 1: fp32 partial sums [splits, B*M, N (2N for SwiGLU)]
 };
+struct GemmPlan {
+    int splits, kc;
+    size_t part_bytes;
+};
+GemmPlan plan_gemm(int rows, int N, int K, bool swiglu);
 
 // Valid rows of batch entry b: all M unless a device count is given.
 __device__ __forceinline__ int valid_rows(const AttnArgs &a, int b)

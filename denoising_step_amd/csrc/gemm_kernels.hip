@@ -65,6 +65,33 @@ __device__ __forceinline__ uint16_t to_bf16(float f)
 
 __device__ __forceinline__ float from_bf16(uint16_t u) { return __uint_as_float((unsigned)u << 16); }
 
+// The epilogue of element (r, n): v = C[r, n] (the gate product for
+// SwiGLU), up = the up product (SwiGLU only).
+__device__ __forceinline__ void store_out(const GemmArgs &a, bool swiglu, int r, int n, float v, float up)
+{
+    const int b = r / a.M, j = r - b * a.M;
+    if (swiglu) {
+        a.out[(long)r * a.N + n] = to_bf16(v / (1.f + __expf(-v)) * up);
+    } else if (a.ep_mode == 1) {
+        // q | k | v columns, head-major
+        const int qn = a.Hq * a.D, kn = a.Hkv * a.D;
+        if (n < qn)
+            a.out[(((long)b * a.Hq + n / a.D) * a.M + j) * a.D + n % a.D] = to_bf16(v);
+        else if (n < qn + kn)
+            a.out_k[(((long)b * a.Hkv + (n - qn) / a.D) * a.M + j) * a.D + (n - qn) % a.D] = to_bf16(v);
+        else
+            a.out_v[(((long)b * a.Hkv + (n - qn - kn) / a.D) * a.M + j) * a.D + (n - qn - kn) % a.D] = to_bf16(v);
+    } else if (a.ep_mode == 0) {
+        a.out[(long)r * a.N + n] = to_bf16(v);
+    } else {
+        // residual: the row's own hidden state (gathered or compact)
+        const long src = a.resid_gather ? ((long)b * a.n_pos + a.act[b * a.M + j]) * a.N + n : (long)r * a.N + n;
+        v += from_bf16(a.resid[src]);
+        const long dst = a.ep_mode == 3 ? ((long)b * a.n_pos + a.act[b * a.M + j]) * a.N + n : (long)r * a.N + n;
+        a.out[dst] = to_bf16(v);
+    }
+}
+
 template <bool SWIGLU>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
 {
@@ -79,8 +106,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     const int wm = wid >> 1, wn = wid & 1;
     const int tiles_m = (a.B * a.M + kBM - 1) / kBM;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int mt = L % tiles_m, nt = L / tiles_m;
+    const int mt = L % tiles_m, rest = L / tiles_m;
+    const int ks = rest % a.splits, nt = rest / a.splits;
     const int m0 = mt * kBM, n0 = nt * kBN;
+    const int kbeg = ks * a.kc, kend = min(a.K, kbeg + a.kc);
 
     // A tile geometry of this thread: load u writes LDS bytes
     // (4u + wid) * 1024 + lane * 16: tile row ar[u], slot sl; the global
@@ -170,17 +199,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         }
     };
 
-    const int nk = a.K / kBK;
-    issue(0, As0, Ws0);
+    const int nk = (kend - kbeg) / kBK;
+    issue(kbeg, As0, Ws0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < nk; t += 2) {
-        if (t + 1 < nk) issue((t + 1) * kBK, As1, Ws1);
+        if (t + 1 < nk) issue(kbeg + (t + 1) * kBK, As1, Ws1);
         compute(As0, Ws0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 1 < nk) {
-            if (t + 2 < nk) issue((t + 2) * kBK, As0, Ws0);
+            if (t + 2 < nk) issue(kbeg + (t + 2) * kBK, As0, Ws0);
             compute(As1, Ws1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -188,54 +217,82 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     }
 
     // Epilogue.  Accumulator element e of lane (l32, hh) in tile (i, j) is
-    // row wm*64 + 32i + 8(e/4) + 4hh + e%4, column wn*64 + 32j + l32.
+    // row wm*64 + 32i + 8(e/4) + 4hh + e%4, column wn*64 + 32j + l32.  With
+    // K splits the fp32 sums go to this split's slice of the partials.
+    const long rows = (long)a.B * a.M;
+    const int np = SWIGLU ? 2 * a.N : a.N;
     for (int i = 0; i < 2; ++i)
         for (int e = 0; e < 16; ++e) {
             const int r = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
             if (!row_valid(a, r)) continue;
-            const int b = r / a.M, j = r - b * a.M;
             for (int jj = 0; jj < 2; ++jj) {
                 const int n = n0 + wn * 64 + 32 * jj + l32;
                 if (n >= a.N) continue;
-                float v = acc[0][i][jj][e];
-                if (SWIGLU) {
-                    const float g = v, up = acc[NW - 1][i][jj][e];
-                    v = g / (1.f + __expf(-g)) * up;
-                    a.out[(long)r * a.N + n] = to_bf16(v);
-                } else if (a.ep_mode == 1) {
-                    // q | k | v columns, head-major
-                    const int qn = a.Hq * a.D, kn = a.Hkv * a.D;
-                    if (n < qn)
-                        a.out[(((long)b * a.Hq + n / a.D) * a.M + j) * a.D + n % a.D] = to_bf16(v);
-                    else if (n < qn + kn)
-                        a.out_k[(((long)b * a.Hkv + (n - qn) / a.D) * a.M + j) * a.D + (n - qn) % a.D] =
-                            to_bf16(v);
-                    else
-                        a.out_v[(((long)b * a.Hkv + (n - qn - kn) / a.D) * a.M + j) * a.D + (n - qn - kn) % a.D] =
-                            to_bf16(v);
+                const float v = acc[0][i][jj][e], up = acc[NW - 1][i][jj][e];
+                if (a.splits > 1) {
+                    float *p = a.part + ((long)ks * rows + r) * np + n;
+                    p[0] = v;
+                    if (SWIGLU) p[a.N] = up;
                 } else {
-                    // residual: the row's own hidden state (gathered or compact)
-                    const long src = a.resid_gather ? ((long)b * a.n_pos + a.act[b * a.M + j]) * a.N + n
-                                                    : (long)r * a.N + n;
-                    v += from_bf16(a.resid[src]);
-                    const long dst = a.ep_mode == 3 ? ((long)b * a.n_pos + a.act[b * a.M + j]) * a.N + n
-                                                    : (long)r * a.N + n;
-                    a.out[dst] = to_bf16(v);
+                    store_out(a, SWIGLU, r, n, v, up);
                 }
             }
         }
 }
 
+// Sum the K splits of each valid element in split order (deterministic)
+// and apply the epilogue.  One thread per element.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, int swiglu)
+{
+    const long rows = (long)a.B * a.M;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * a.N) return;
+    const int r = (int)(idx / a.N), n = (int)(idx - (long)r * a.N);
+    if (!row_valid(a, r)) return;
+    const int np = swiglu ? 2 * a.N : a.N;
+    float v = 0.f, up = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+        const float *p = a.part + ((long)s * rows + r) * np + n;
+        v += p[0];
+        if (swiglu) up += p[a.N];
+    }
+    store_out(a, swiglu != 0, r, n, v, up);
+}
+
 }  // namespace
+
+GemmPlan plan_gemm(int rows, int N, int K, bool swiglu)
+{
+    GemmPlan p{};
+    const long tiles = (long)((rows + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    // Too few output tiles to fill the chip: split K (at least four K steps
+    // per split), the partial sums then reduced by a second kernel.  From
+    // 1.5 tiles per CU on, the partial-sum traffic costs more than the
+    // extra parallelism gains (measured on MI355X).
+    int s = 1;
+    if (tiles > 0 && tiles < 3L * kNumCU / 2) {
+        s = (int)((2L * kNumCU + tiles - 1) / tiles);
+        s = max(1, min(s, min(16, K / (4 * kBK))));
+    }
+    const int steps = (K / kBK + s - 1) / s;
+    p.kc = steps * kBK;
+    p.splits = (K + p.kc - 1) / p.kc;
+    p.part_bytes = p.splits > 1 ? (size_t)p.splits * rows * N * (swiglu ? 2 : 1) * sizeof(float) : 0;
+    return p;
+}
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 {
-    const long tiles = (long)((a.B * a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+    const long tiles = (long)((a.B * a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN) * a.splits;
     if (tiles == 0) return hipSuccess;
     if (a.w1)
         gemm_kernel<true><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
     else
         gemm_kernel<false><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
+    if (a.splits > 1) {
+        const long n = (long)a.B * a.M * a.N;
+        gemm_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(a, a.w1 ? 1 : 0);
+    }
     return hipGetLastError();
 }
 

@@ -363,35 +363,39 @@ typedef struct {
     int32_t F;                  /* feed-forward width, a multiple of 64 */
 } dlm_layer_desc;
 
+/* Every call takes a device workspace of at least dlm_layer_workspace_bytes()
+ * (fp32 partial sums when a product has too few output tiles to fill the chip
+ * and its K dimension is split; the gated hidden rows of dlm_ffn).  Calls that
+ * share a workspace must be ordered (one stream). */
+int dlm_layer_workspace_bytes(const dlm_layer_desc *layer, size_t *bytes);
+
 /* q | k | v projection of the active rows.
  *   x      bf16 [B, n_pos, d]
  *   w_qkv  bf16 [(Hq + 2 Hkv) * D, d]: the q rows (head-major), then k, then v
  *   q      bf16 [B, Hq, M, D] out;  k, v  bf16 [B, Hkv, M, D] out
  * (the layouts dlm_step_attn reads).  Errors: DLM_E_NULL, DLM_E_SHAPE,
- * DLM_E_UNSUPPORTED, DLM_E_HIP. */
+ * DLM_E_UNSUPPORTED, DLM_E_WORKSPACE, DLM_E_HIP. */
 int dlm_proj_qkv(const dlm_layer_desc *layer, const void *x, const void *w_qkv, void *q, void *k,
-                 void *v, hipStream_t stream);
+                 void *v, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Output projection with the residual: h = x[act] + attn_out W_o^T.
  *   attn_out  bf16 [B, Hq, M, D] (dlm_step_attn's out); D a multiple of 64
  *   w_o       bf16 [d, Hq * D]
  *   h         bf16 [B, M, d] out
- * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_HIP. */
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_WORKSPACE, DLM_E_HIP. */
 int dlm_proj_out(const dlm_layer_desc *layer, const void *x, const void *attn_out, const void *w_o,
-                 void *h, hipStream_t stream);
+                 void *h, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* SwiGLU feed-forward with the residual, written back to the active rows of
  * x: x[b, active_idx[b, j], :] = h + (silu(h W_gate^T) * (h W_up^T)) W_down^T.
  *   h               bf16 [B, M, d]
  *   w_gate, w_up    bf16 [F, d];  w_down  bf16 [d, F]
  *   x               bf16 [B, n_pos, d] in/out (only active rows written)
- *   workspace       the gated hidden rows, bf16 [B * M, F] (rounded there)
+ *   the gated hidden rows are rounded to bf16 (in the workspace) before the
+ *   down projection
  * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_WORKSPACE, DLM_E_HIP. */
 int dlm_ffn(const dlm_layer_desc *layer, const void *h, const void *w_gate, const void *w_up,
             const void *w_down, void *x, void *workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* Workspace bytes of dlm_ffn.  Writes *bytes. */
-int dlm_ffn_workspace_bytes(const dlm_layer_desc *layer, size_t *bytes);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *dlm_last_error(void);

@@ -252,10 +252,10 @@ def _layer(**kw):
 ])
 def test_layer_calls_reject(case, code):
     L = _layer(**case)
-    for call in (lambda: dlm.dlm_proj_qkv(L, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
-                 lambda: dlm.dlm_proj_out(L, FAKE, FAKE, FAKE, FAKE, stream=0),
+    for call in (lambda: dlm.dlm_proj_qkv(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
+                 lambda: dlm.dlm_proj_out(L, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
                  lambda: dlm.dlm_ffn(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0),
-                 lambda: dlm.dlm_ffn_workspace_bytes(L)):
+                 lambda: dlm.dlm_layer_workspace_bytes(L)):
         with pytest.raises(dlm.DlmError) as e:
             call()
         assert e.value.code == code
@@ -263,19 +263,26 @@ def test_layer_calls_reject(case, code):
 
 def test_layer_call_specific_checks():
     with pytest.raises(dlm.DlmError) as e:          # heads of 32 do not tile the K steps of 64
-        dlm.dlm_proj_out(_layer(D=32), FAKE, FAKE, FAKE, FAKE, stream=0)
+        dlm.dlm_proj_out(_layer(D=32), FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert e.value.code == dlm.DLM_E_UNSUPPORTED
     with pytest.raises(dlm.DlmError) as e:
-        dlm.dlm_proj_qkv(_layer(), FAKE, None, FAKE, FAKE, FAKE, stream=0)
+        dlm.dlm_proj_qkv(_layer(), FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert e.value.code == dlm.DLM_E_NULL
     L = _layer()
-    need = dlm.dlm_ffn_workspace_bytes(L)
-    assert need == 2 * 40 * 384 * 2
+    need = dlm.dlm_layer_workspace_bytes(L)
+    assert need >= 2 * 40 * 384 * 2           # at least the gated hidden rows
     import ctypes
     c = dlm._c_layer(L)
     rc = dlm.lib.dlm_ffn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
     assert rc == dlm.DLM_E_WORKSPACE
-    assert dlm.lib.dlm_proj_qkv(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == dlm.DLM_E_NULL
+    # few output tiles and a long K: K is split and the projections need partial sums too
+    c = dlm._c_layer(_layer(d=1024, M=8))
+    assert dlm.lib.dlm_proj_qkv(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
+        dlm.DLM_E_WORKSPACE
+    c = dlm._c_layer(_layer(Hq=16, Hkv=2, M=8))          # K = Hq D = 1024
+    assert dlm.lib.dlm_proj_out(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == \
+        dlm.DLM_E_WORKSPACE
+    assert dlm.lib.dlm_proj_qkv(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == dlm.DLM_E_NULL
 
 
 def test_posterior_rejects_nan_gate():

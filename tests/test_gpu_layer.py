@@ -66,6 +66,8 @@ CASES = {
     "d192_head128": dict(B=1, n_pos=200, d=192, Hq=2, Hkv=1, D=128, F=128, M=130, m=[130]),
     "all_rows": dict(B=3, n_pos=90, d=128, Hq=2, Hkv=2, D=64, F=256, M=90, m=None),
     "rows_cut": dict(B=2, n_pos=260, d=320, Hq=4, Hkv=4, D=64, F=192, M=257, m=[0, 129]),
+    # few rows, long K: every product splits K (partial sums and the reduction)
+    "split_k": dict(B=2, n_pos=64, d=1024, Hq=16, Hkv=4, D=64, F=1024, M=40, m=[33, 40]),
 }
 
 
@@ -115,9 +117,9 @@ def _run_layer(c, m_dev, sentinel=5.0):
     k = torch.full((c.B, c.Hkv, c.M, c.D), sentinel, dtype=torch.bfloat16, device="cuda")
     v = torch.full_like(k, sentinel)
     h = torch.full((c.B, c.M, c.d), sentinel, dtype=torch.bfloat16, device="cuda")
-    dlm.dlm_proj_qkv(L, x, _dev(c.w_qkv), q, k, v)
-    dlm.dlm_proj_out(L, x, _dev(c.attn_out), _dev(c.w_o), h)
-    ws = torch.empty(max(1, dlm.dlm_ffn_workspace_bytes(L)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, dlm.dlm_layer_workspace_bytes(L)), dtype=torch.uint8, device="cuda")
+    dlm.dlm_proj_qkv(L, x, _dev(c.w_qkv), q, k, v, ws)
+    dlm.dlm_proj_out(L, x, _dev(c.attn_out), _dev(c.w_o), h, ws)
     x2 = x.clone()
     dlm.dlm_ffn(L, _dev(c.h), _dev(c.w_gate), _dev(c.w_up), _dev(c.w_down), x2, ws)
     torch.cuda.synchronize()
