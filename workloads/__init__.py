@@ -548,6 +548,51 @@ def layer_llada(seed=0, M=1024, n_pos=1024) -> LayerCase:
                       config_id=96, seed=seed)
 
 
+# --------------------------------------------------------------------------
+# R2LM right-to-left selective scan over the generation block
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class R2LCase:
+    """Inputs of the right-to-left scan of one step: the generation block's
+    hidden states and the scan's parameters (synthetic: the projections that
+    produce delta, B and C are not part of the path)."""
+    name: str
+    B: int
+    L: int
+    E: int
+    N: int
+    u: np.ndarray               # bf16 bits [B, L, E]
+    delta: np.ndarray           # bf16 bits [B, L, E], positive step sizes
+    A: np.ndarray               # float32 [E, N], negative
+    Bm: np.ndarray              # bf16 bits [B, L, N]
+    Cm: np.ndarray              # bf16 bits [B, L, N]
+    Dv: np.ndarray              # float32 [E]
+    gate: float                 # the scalar s
+    x: np.ndarray               # bf16 bits [B, L, E]: the hidden stream the correction joins
+
+
+def make_r2l(name, *, B, L, E, N, gate=0.5, config_id=97, seed=0) -> R2LCase:
+    """u, x ~ N(0, 1); delta = softplus of N(-2, 1) draws (Mamba's step-size
+    parameterisation, mostly in (0.01, 1)); A[e, n] = -(n + 1) (the usual
+    initialisation); B, C ~ N(0, 1); D ~ N(0, 1)."""
+    rs = _streams(config_id, seed)
+    d = rs["k"].standard_normal(size=(B, L, E)).astype(np.float32) - np.float32(2.0)
+    delta = np.log1p(np.exp(d)).astype(np.float32)
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float32), (E, 1))
+    return R2LCase(name=name, B=B, L=L, E=E, N=N,
+                   u=_normal_bf16(rs["q"], (B, L, E), 1.0), delta=to_bf16_bits(delta), A=A,
+                   Bm=_normal_bf16(rs["v"], (B, L, N), 1.0), Cm=_normal_bf16(rs["cache_k"], (B, L, N), 1.0),
+                   Dv=rs["cache_v"].standard_normal(size=E).astype(np.float32), gate=gate,
+                   x=_normal_bf16(rs["logits"], (B, L, E), 1.0))
+
+
+def r2l_bifocal(seed=0) -> R2LCase:
+    """The Bifocal page's serving setting: batch 8, a 256-token generation
+    block, the width 2048 of its 1.7B backbone, 16 scan states."""
+    return make_r2l("r2l_bifocal", B=8, L=256, E=2048, N=16, config_id=98, seed=seed)
+
+
 CONFIGS = {
     "tiny": tiny,
     "llada_bidirectional": llada_bidirectional,
