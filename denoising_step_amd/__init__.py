@@ -31,7 +31,8 @@ ROW_SELECT, ROW_LOCK = 1, 2
 
 EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
            "dlm_posterior_workspace_bytes", "dlm_block_buffer_init", "dlm_block_buffer_advance",
-           "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_layer_workspace_bytes", "dlm_last_error")
+           "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_layer_workspace_bytes", "dlm_r2l_scan",
+           "dlm_last_error")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -125,6 +126,14 @@ lib.dlm_block_buffer_init.argtypes = [ctypes.POINTER(_BlockBuffer), _P]
 lib.dlm_block_buffer_init.restype = ctypes.c_int
 lib.dlm_block_buffer_advance.argtypes = [ctypes.POINTER(_BlockBuffer), _P, _P]
 lib.dlm_block_buffer_advance.restype = ctypes.c_int
+class _R2LDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("L", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("gate", ctypes.c_float)]
+
+
+lib.dlm_r2l_scan.argtypes = [ctypes.POINTER(_R2LDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P]
+lib.dlm_r2l_scan.restype = ctypes.c_int
+
 _LP = ctypes.POINTER(_LayerDesc)
 lib.dlm_proj_qkv.argtypes = [_LP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.dlm_proj_qkv.restype = ctypes.c_int
@@ -452,3 +461,21 @@ def dlm_ffn(layer: LayerDesc, h, w_gate, w_up, w_down, x, workspace, stream=None
     c = _c_layer(L)
     _check(lib.dlm_ffn(ctypes.byref(c), _ptr(h), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(x),
                        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def dlm_r2l_scan(B: int, L: int, E: int, N: int, gate: float, u, delta, A, Bm, Cm, D, y=None, x=None,
+                 stream=None) -> None:
+    """The right-to-left selective scan (see dlm_step.h)."""
+    _expect(u, "u", (B, L, E), "torch.bfloat16")
+    _expect(delta, "delta", (B, L, E), "torch.bfloat16")
+    _expect(A, "A", (E, N), "torch.float32")
+    _expect(Bm, "Bm", (B, L, N), "torch.bfloat16")
+    _expect(Cm, "Cm", (B, L, N), "torch.bfloat16")
+    _expect(D, "D", (E,), "torch.float32")
+    if y is not None:
+        _expect(y, "y", (B, L, E), "torch.float32")
+    if x is not None:
+        _expect(x, "x", (B, L, E), "torch.bfloat16")
+    c = _R2LDesc(B, L, E, N, gate)
+    _check(lib.dlm_r2l_scan(ctypes.byref(c), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D),
+                            _ptr(y), _ptr(x), _stream(stream)))

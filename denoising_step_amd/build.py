@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["dlm_api.hip", "attn_kernels.hip", "posterior_kernels.hip", "loop_kernels.hip",
-           "gemm_kernels.hip"]
+           "gemm_kernels.hip", "r2l_kernels.hip"]
 LIB = os.path.join(HERE, "libdlm_step.so")
 
 HIPCC_FLAGS = [

@@ -455,6 +455,32 @@ int dlm_ffn(const dlm_layer_desc *L, const void *h, const void *w_gate, const vo
     return run_gemm(d, stream);
 }
 
+int dlm_r2l_scan(const dlm_r2l_desc *desc, const void *u, const void *delta, const float *A, const void *Bm,
+                 const void *Cm, const float *D, float *y, void *x, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (!desc) return fail(DLM_E_NULL, "descriptor is NULL");
+    const dlm_r2l_desc *d = desc;
+    if (d->B < 1 || d->L < 0 || d->E < 1 || d->N < 1)
+        return fail(DLM_E_SHAPE, "B=%d L=%d E=%d N=%d out of range", d->B, d->L, d->E, d->N);
+    if (d->N != 4 && d->N != 8 && d->N != 16 && d->N != 32 && d->N != 64)
+        return fail(DLM_E_UNSUPPORTED, "N=%d not in {4, 8, 16, 32, 64}", d->N);
+    if ((long)d->B * d->L * d->E > (1L << 31) - 1) return fail(DLM_E_SHAPE, "B*L*E too large");
+    if (!isfinite(d->gate)) return fail(DLM_E_DESC, "gate must be finite");
+    if (!u || !delta || !A || !Bm || !Cm || !D) return fail(DLM_E_NULL, "u, delta, A, Bm, Cm and D must be non-NULL");
+    if (!y && !x) return fail(DLM_E_NULL, "at least one of y and x must be given");
+    if (!aligned16(Bm) || !aligned16(Cm)) return fail(DLM_E_SHAPE, "Bm and Cm must be 16-byte aligned");
+    if (d->L == 0) return DLM_OK;
+    dlm::R2LArgs a{};
+    a.u = static_cast<const uint16_t *>(u); a.delta = static_cast<const uint16_t *>(delta);
+    a.Bm = static_cast<const uint16_t *>(Bm); a.Cm = static_cast<const uint16_t *>(Cm);
+    a.A = A; a.D = D; a.y = y; a.x = static_cast<uint16_t *>(x);
+    a.B = d->B; a.L = d->L; a.E = d->E; a.N = d->N; a.gate = d->gate;
+    hipError_t e = dlm::launch_r2l(a, stream);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return DLM_OK;
+}
+
 int dlm_block_buffer_init(const dlm_block_buffer *bb, hipStream_t stream)
 {
     g_err[0] = 0;

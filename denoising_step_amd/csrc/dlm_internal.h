@@ -130,6 +130,16 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int rows, int N, int K, bool swiglu);
 
+// The right-to-left selective scan of one step (r2l_kernels.hip).
+struct R2LArgs {
+    const uint16_t *u, *delta, *Bm, *Cm;   // bf16 [B, L, E], [B, L, E], [B, L, N], [B, L, N]
+    const float *A, *D;                    // [E, N], [E]
+    float *y;                              // optional fp32 [B, L, E] out
+    uint16_t *x;                           // optional bf16 [B, L, E] in/out (x += y)
+    int B, L, E, N;
+    float gate;
+};
+
 // Valid rows of batch entry b: all M unless a device count is given.
 __device__ __forceinline__ int valid_rows(const AttnArgs &a, int b)
 {
@@ -141,6 +151,7 @@ hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after);
 hipError_t launch_block_buffer(const BBArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
+hipError_t launch_r2l(const R2LArgs &a, hipStream_t stream);
 
 // Map a hardware workgroup id to a logical one so that logically
 // consecutive workgroups (which share K/V) run on the same XCD: the

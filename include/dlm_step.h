@@ -397,6 +397,34 @@ int dlm_proj_out(const dlm_layer_desc *layer, const void *x, const void *attn_ou
 int dlm_ffn(const dlm_layer_desc *layer, const void *h, const void *w_gate, const void *w_up,
             const void *w_down, void *x, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * R2LM right-to-left selective scan over the generation block ("Bifocal
+ * Diffusion Language Models" page, sec. 2: the right-to-left stream flips
+ * the hidden states, applies a selective scan (Mamba) and flips them back; a
+ * learnable scalar gate s, 0 at initialisation, scales the correction).  Per
+ * batch entry b and channel e, from a zero state at the block's last token,
+ * for t = L-1 down to 0:
+ *   h[e, n] = exp(delta[b,t,e] * A[e,n]) * h[e, n] + delta[b,t,e] * Bm[b,t,n] * u[b,t,e]
+ *   y[b,t,e] = s * (sum_n Cm[b,t,n] * h[e, n] + D[e] * u[b,t,e])
+ * in fp32 (exp as exp2 of delta * A * log2 e).
+ *   u, delta  bf16 [B, L, E] (delta > 0 in use; not checked)
+ *   A         fp32 [E, N];  D  fp32 [E]
+ *   Bm, Cm    bf16 [B, L, N]
+ *   y         fp32 [B, L, E] out, or NULL
+ *   x         bf16 [B, L, E] in/out, or NULL: x = bf16(x + y), the correction
+ *             joining the hidden stream
+ * At least one of y and x.  Bm and Cm 16-byte aligned.
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED (N not in {4, 8, 16, 32, 64}),
+ * DLM_E_DESC (gate not finite), DLM_E_HIP.
+ */
+typedef struct {
+    int32_t B, L, E, N;     /* batch, tokens of the block, channels, states per channel */
+    float gate;             /* s */
+} dlm_r2l_desc;
+
+int dlm_r2l_scan(const dlm_r2l_desc *desc, const void *u, const void *delta, const float *A,
+                 const void *Bm, const void *Cm, const float *D, float *y, void *x, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *dlm_last_error(void);
 

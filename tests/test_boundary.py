@@ -288,3 +288,22 @@ def test_layer_call_specific_checks():
 def test_posterior_rejects_nan_gate():
     assert _post(sel=dlm.Select(mode=dlm.SEL_TOPK_CONF, k=2, group_rows=16, conf_gate=float("nan"))) \
         == dlm.DLM_E_DESC
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(B=0), dlm.DLM_E_SHAPE),
+    (dict(E=0), dlm.DLM_E_SHAPE),
+    (dict(L=-1), dlm.DLM_E_SHAPE),
+    (dict(N=12), dlm.DLM_E_UNSUPPORTED),
+    (dict(gate=float("inf")), dlm.DLM_E_DESC),
+    (dict(u=None), dlm.DLM_E_NULL),
+    (dict(y=None, x=None), dlm.DLM_E_NULL),
+    (dict(Bm=FAKE + 8), dlm.DLM_E_SHAPE),
+])
+def test_r2l_scan_rejects(case, code):
+    args = dict(B=2, L=16, E=64, N=16, gate=0.5, u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, D=FAKE,
+                y=FAKE, x=None)
+    args.update(case)
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_r2l_scan(stream=0, **args)
+    assert e.value.code == code
