@@ -357,6 +357,50 @@ def layer_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def r2l_bench(args):
+    """The R2LM right-to-left scan at the Bifocal page's serving shape (batch
+    8, a 256-token generation block, width 2048, 16 states), the correction
+    added to the hidden stream: timed with HIP events; bound by the
+    exponentials (one per state update: B L E N of them) on the
+    transcendental unit, and reported against HBM bytes too.  Prints one
+    JSON line."""
+    import torch
+
+    import denoising_step_amd as dlm
+    import workloads as W
+    from denoising_step_amd.runner import bf16_to_device
+
+    torch.cuda.set_device(0)
+    c = W.r2l_bifocal(seed=args.seed)
+    dev = torch.device("cuda")
+    bf = lambda a: bf16_to_device(a, dev)
+    n_sets = 8                      # rotate inputs past the MALL
+    sets = [dict(u=bf(c.u), dl=bf(c.delta), Bm=bf(c.Bm), Cm=bf(c.Cm), x=bf(c.x)) for _ in range(n_sets)]
+    A = torch.from_numpy(c.A).to(dev)
+    D = torch.from_numpy(c.Dv).to(dev)
+
+    def call(i):
+        s_ = sets[i]
+        dlm.dlm_r2l_scan(c.B, c.L, c.E, c.N, c.gate, s_["u"], s_["dl"], A, s_["Bm"], s_["Cm"], D, x=s_["x"])
+
+    ms = time_loop(call, n_sets, args.steps, args.warmup)
+    updates = float(c.B) * c.L * c.E * c.N
+    # one state update: at least 4 full-rate fp32 VALU ops (delta*A, delta*u*B, the state FMA,
+    # the output FMA) and one quarter-rate exp: 4/16 + 1/4 = 0.5 SIMD clocks per lane;
+    # 256 CUs x 4 SIMDs at 2.4 GHz
+    peak = 256 * 4 * 2.4e9 / 0.5
+    nbytes = float(c.B) * c.L * c.E * 2 * 4 + 2.0 * c.B * c.L * c.N * 2   # u, delta, x read + x write; B, C
+    line = {"metric": "R2LM right-to-left scan per denoising step", "unit": "us", "n_gpus": 1,
+            "value_us": round(ms * 1e3, 2), "dtype": "bf16 in, fp32 scan",
+            "data": "synthetic (seeded)",
+            "config": {"workload": c.name, "B": c.B, "L": c.L, "E": c.E, "N": c.N},
+            "roofline": {"bound": "alu", "achieved": round(updates / ms / 1e9, 3),
+                         "peak": round(peak / 1e12, 3), "unit": "T state updates/s",
+                         "frac": round(updates / ms * 1e3 / peak, 3),
+                         "hbm_gbs": round(nbytes / ms / 1e6, 0), "hbm_frac": round(nbytes / ms / 1e6 / 8000.0, 3)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,6 +415,8 @@ def main():
                     help="time a whole multi-step SureLock run instead (its own JSON line)")
     ap.add_argument("--layer", action="store_true",
                     help="time a layer's active-row projections and feed-forward instead")
+    ap.add_argument("--r2l", action="store_true",
+                    help="time the R2LM right-to-left scan instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -384,6 +430,9 @@ def main():
         return
     if args.layer:
         layer_bench(args)
+        return
+    if args.r2l:
+        r2l_bench(args)
         return
 
     import numpy as np

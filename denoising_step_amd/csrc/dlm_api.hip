@@ -463,13 +463,15 @@ int dlm_r2l_scan(const dlm_r2l_desc *desc, const void *u, const void *delta, con
     const dlm_r2l_desc *d = desc;
     if (d->B < 1 || d->L < 0 || d->E < 1 || d->N < 1)
         return fail(DLM_E_SHAPE, "B=%d L=%d E=%d N=%d out of range", d->B, d->L, d->E, d->N);
-    if (d->N != 4 && d->N != 8 && d->N != 16 && d->N != 32 && d->N != 64)
-        return fail(DLM_E_UNSUPPORTED, "N=%d not in {4, 8, 16, 32, 64}", d->N);
+    if (d->N != 8 && d->N != 16 && d->N != 32)
+        return fail(DLM_E_UNSUPPORTED, "N=%d not in {8, 16, 32}", d->N);
+    if (d->E % 8 != 0) return fail(DLM_E_UNSUPPORTED, "E=%d is not a multiple of 8", d->E);
     if ((long)d->B * d->L * d->E > (1L << 31) - 1) return fail(DLM_E_SHAPE, "B*L*E too large");
     if (!isfinite(d->gate)) return fail(DLM_E_DESC, "gate must be finite");
     if (!u || !delta || !A || !Bm || !Cm || !D) return fail(DLM_E_NULL, "u, delta, A, Bm, Cm and D must be non-NULL");
     if (!y && !x) return fail(DLM_E_NULL, "at least one of y and x must be given");
-    if (!aligned16(Bm) || !aligned16(Cm)) return fail(DLM_E_SHAPE, "Bm and Cm must be 16-byte aligned");
+    if (!aligned16(u) || !aligned16(delta) || !aligned16(Bm) || !aligned16(Cm) || (x && !aligned16(x)))
+        return fail(DLM_E_SHAPE, "u, delta, Bm, Cm and x must be 16-byte aligned");
     if (d->L == 0) return DLM_OK;
     dlm::R2LArgs a{};
     a.u = static_cast<const uint16_t *>(u); a.delta = static_cast<const uint16_t *>(delta);

@@ -10,20 +10,29 @@
 //     y_t[e]  = s (sum_n C_t[n] h[e, n] + D[e] u_t[e])
 // from a zero state at the block's right end.
 //
-// A thread keeps 4 states of one channel in registers; the N/4 threads of a
-// channel are consecutive lanes and add their partial outputs with xor
-// shuffles.  A workgroup of 256 threads covers 256 / (N/4) channels of one
-// batch entry.  The inputs of the next U tokens are loaded before the
-// current U are computed, so the loads of the dependent chain are in flight
-// while it runs.  exp is the hardware exp2 of delta * A * log2(e).
+// N is 8, 16 or 32 (a token's B row is then a whole number of 16-byte
+// loads).  A thread keeps S = 4 states of one channel in registers (S = 2
+// doubles the waves but measured slower: the per-token work is shared by
+// fewer states); the NL = N/S threads of a channel are consecutive lanes
+// and add their partial outputs with DPP (quad permutes, a row half-mirror,
+// a row mirror), no LDS traffic.  A workgroup of 256 threads covers
+// CW = 256/NL channels of one batch entry.
+//
+// The recurrence never waits on global memory: the tokens are taken in
+// chunks of LC = 4096/CW (u, delta and x of a chunk are 8 KB each, B and C
+// of its tokens follow), loaded straight into LDS, double-buffered so the
+// next chunk is in flight while this one is scanned out of LDS.  Each
+// chunk's y goes to LDS and is then written out, with x += y, coalesced.
 #include "dlm_internal.h"
 
 namespace dlm {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int kR2LThreads = 256;
-constexpr int kR2LU = 4;     // tokens per prefetch group
+constexpr int kR2LOOB = 0x7ffffff0;
 
 __device__ __forceinline__ float bf(uint16_t v) { return __uint_as_float((unsigned)v << 16); }
 
@@ -33,69 +42,173 @@ __device__ __forceinline__ uint16_t to_bf(float f)
     return *reinterpret_cast<const uint16_t *>(&h);
 }
 
+// lane value from the lane given by a DPP control (full rows and banks)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the NL consecutive lanes of a channel (NL a power of two <= 16).
+template <int NL>
+__device__ __forceinline__ float channel_sum(float v)
+{
+    if (NL >= 2) v += dpp<0xB1>(v);      // quad_perm [1,0,3,2]: lane ^ 1
+    if (NL >= 4) v += dpp<0x4E>(v);      // quad_perm [2,3,0,1]: lane ^ 2
+    if (NL >= 8) v += dpp<0x141>(v);     // row_half_mirror: pairs the two quads of 8 lanes
+    if (NL >= 16) v += dpp<0x140>(v);    // row_mirror: pairs the two halves of 16 lanes
+    return v;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t view(const void *p, long bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+#ifndef DLM_R2L_S
+#define DLM_R2L_S 4
+#endif
+constexpr int kR2LS = DLM_R2L_S;   // states per thread (2 or 4)
+
+// S consecutive bf16 values (4 or 8 bytes, aligned) widened to fp32
+template <int S>
+__device__ __forceinline__ void load_bf16s(const uint16_t *p, float (&v)[S])
+{
+    if constexpr (S == 2) {
+        const unsigned q = *reinterpret_cast<const unsigned *>(p);
+        v[0] = __uint_as_float(q << 16);
+        v[1] = __uint_as_float(q & 0xffff0000u);
+    } else {
+        const uint2 q = *reinterpret_cast<const uint2 *>(p);
+        v[0] = __uint_as_float(q.x << 16);
+        v[1] = __uint_as_float(q.x & 0xffff0000u);
+        v[2] = __uint_as_float(q.y << 16);
+        v[3] = __uint_as_float(q.y & 0xffff0000u);
+    }
+}
+
 template <int NL>
 __global__ __launch_bounds__(kR2LThreads) void r2l_scan_kernel(R2LArgs a)
 {
+    constexpr int S = kR2LS;
+    constexpr int N = S * NL;
     constexpr int CW = kR2LThreads / NL;           // channels per workgroup
-    constexpr int U = kR2LU;
-    const int tid = threadIdx.x;
-    const int g = tid % NL;                        // states 4g .. 4g+3
+    constexpr int LC = 4096 / CW;                  // tokens per chunk (8 KB per bf16 array)
+    static_assert(LC % 4 == 0 && (S == 2 || S == 4), "groups of four tokens, two or four states per thread");
+    constexpr int ROW = CW * 2;                    // bytes of one token's channels
+    constexpr int BC = LC * N * 2;                 // bytes of a chunk's B (or C)
+    constexpr int BCE = BC / 2 < 512 ? 512 : BC / 2;   // its LDS array: at least one 1-KB load
+    __shared__ __attribute__((aligned(16))) uint16_t us[2][LC * CW];
+    __shared__ __attribute__((aligned(16))) uint16_t ds[2][LC * CW];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][LC * CW];
+    __shared__ __attribute__((aligned(16))) uint16_t bs[2][BCE];
+    __shared__ __attribute__((aligned(16))) uint16_t cs[2][BCE];
+    __shared__ float ys[LC * CW];
+
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int g = tid % NL, c = tid / NL;          // states S g .. S g + S-1 of local channel c
     const int cblocks = (a.E + CW - 1) / CW;
     const int b = blockIdx.x / cblocks;
-    const int e = (blockIdx.x % cblocks) * CW + tid / NL;
-    const bool ok = e < a.E;
-    const int ec = ok ? e : a.E - 1;               // a valid channel for the loads
+    const int e0 = (blockIdx.x % cblocks) * CW;
+    const int e = e0 + c;
+    const int ec = e < a.E ? e : a.E - 1;
 
-    float A2[4], h[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < 4; ++i) A2[i] = a.A[(long)ec * a.N + 4 * g + i] * 1.4426950408889634f;
+    const long tok_bytes = (long)a.B * a.L * a.E * 2;
+    const __amdgpu_buffer_rsrc_t ur = view(a.u, tok_bytes), dr = view(a.delta, tok_bytes);
+    const __amdgpu_buffer_rsrc_t xr = view(a.x ? (const void *)a.x : (const void *)a.u, tok_bytes);
+    const __amdgpu_buffer_rsrc_t br = view(a.Bm, (long)a.B * a.L * N * 2), cr = view(a.Cm, (long)a.B * a.L * N * 2);
+
+    // Chunk k holds tokens [hi - LC + 1, hi], hi = L - 1 - k LC; LDS row i of
+    // the chunk is token lo + i.  A token before 0 reads as zeros.
+    const int nch = (a.L + LC - 1) / LC;
+    auto issue = [&](int k, int buf) {
+        const int lo = a.L - (k + 1) * LC;
+        for (int j = wid; j < 8; j += 4) {          // 8 KB per array: 8 loads of 1 KB
+            const int byte = j * 1024 + lane * 16;
+            const int t = lo + byte / ROW;
+            const int off = t >= 0 ? (int)(((long)(b * a.L + t) * a.E + e0) * 2 + byte % ROW) : kR2LOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (lds_void *)(us[buf] + j * 512), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(dr, (lds_void *)(ds[buf] + j * 512), 16, off, 0, 0, 0);
+            if (a.x) __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(xs[buf] + j * 512), 16, off, 0, 0, 0);
+        }
+        for (int j = wid; j * 1024 < BC; j += 4) {  // B and C rows of the chunk's tokens
+            const int byte = j * 1024 + lane * 16;
+            const int t = lo + byte / (N * 2);
+            const int off = (t >= 0 && byte < BC) ? (int)((long)(b * a.L + t) * N * 2 + byte % (N * 2)) : kR2LOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void *)(bs[buf] + j * 512), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_void *)(cs[buf] + j * 512), 16, off, 0, 0, 0);
+        }
+    };
+
+    float A2[S], h[S];
+    for (int i = 0; i < S; ++i) {
+        A2[i] = a.A[(long)ec * N + S * g + i] * 1.4426950408889634f;
+        h[i] = 0.f;
+    }
     const float Dv = a.D[ec];
-    const long ue = (long)b * a.L * a.E + ec;      // u / delta / y / x at token t: ue + t * E
-    const long bn = (long)b * a.L * a.N + 4 * g;   // B / C at token t: bn + t * N
 
-    struct Tok {
-        float u, dl;
-        uint2 Bq, Cq;                              // 4 bf16 each
-    };
-    auto load = [&](int t, Tok &k) {
-        k.u = bf(a.u[ue + (long)t * a.E]);
-        k.dl = bf(a.delta[ue + (long)t * a.E]);
-        k.Bq = *reinterpret_cast<const uint2 *>(a.Bm + bn + (long)t * a.N);
-        k.Cq = *reinterpret_cast<const uint2 *>(a.Cm + bn + (long)t * a.N);
-    };
-    auto step = [&](int t, const Tok &k) {
-        const float du = k.dl * k.u;
-        const float Bv[4] = {__uint_as_float(k.Bq.x << 16), __uint_as_float(k.Bq.x & 0xffff0000u),
-                             __uint_as_float(k.Bq.y << 16), __uint_as_float(k.Bq.y & 0xffff0000u)};
-        const float Cv[4] = {__uint_as_float(k.Cq.x << 16), __uint_as_float(k.Cq.x & 0xffff0000u),
-                             __uint_as_float(k.Cq.y << 16), __uint_as_float(k.Cq.y & 0xffff0000u)};
-        float yp = 0.f;
-        for (int i = 0; i < 4; ++i) {
-            const float dA = __builtin_amdgcn_exp2f(k.dl * A2[i]);
-            h[i] = fmaf(dA, h[i], du * Bv[i]);
-            yp = fmaf(Cv[i], h[i], yp);
+    // Tokens of a chunk in groups of four, last first: the group's inputs
+    // are read from LDS and its decays exponentiated up front, so only the
+    // state update is serial; the four outputs reduce as independent DPP
+    // chains.  Padding rows (tokens before 0) are zeros: decay 1, input 0,
+    // the state passes unchanged, and their outputs are never written.
+    auto scan_chunk = [&](auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        for (int i0 = LC - 4; i0 >= 0; i0 -= 4) {
+            float u[4], du[4], dA[4][S], Bv[4][S], Cv[4][S], yp[4];
+            for (int j = 0; j < 4; ++j) {
+                const int i = i0 + j;
+                u[j] = bf(us[BUF][i * CW + c]);
+                const float dl = bf(ds[BUF][i * CW + c]);
+                load_bf16s<S>(&bs[BUF][i * N + S * g], Bv[j]);
+                load_bf16s<S>(&cs[BUF][i * N + S * g], Cv[j]);
+                du[j] = dl * u[j];
+                for (int q = 0; q < S; ++q) dA[j][q] = __builtin_amdgcn_exp2f(dl * A2[q]);
+            }
+            for (int j = 3; j >= 0; --j) {
+                yp[j] = 0.f;
+                for (int q = 0; q < S; ++q) {
+                    h[q] = fmaf(dA[j][q], h[q], du[j] * Bv[j][q]);
+                    yp[j] = fmaf(Cv[j][q], h[q], yp[j]);
+                }
+            }
+            for (int j = 0; j < 4; ++j) yp[j] = channel_sum<NL>(yp[j]);
+            if (g == 0)
+                for (int j = 0; j < 4; ++j) ys[(i0 + j) * CW + c] = a.gate * fmaf(Dv, u[j], yp[j]);
         }
-        for (int m = 1; m < NL; m <<= 1) yp += __shfl_xor(yp, m);
-        if (ok && g == 0) {
-            const float y = a.gate * fmaf(Dv, k.u, yp);
-            const long o = ue + (long)t * a.E;
+    };
+
+    // write the chunk's y (and x + y) back, coalesced: thread = (row, channel)
+    auto write_chunk = [&](auto bufc, int k) {
+        constexpr int BUF = decltype(bufc)::value;
+        const int lo = a.L - (k + 1) * LC;
+        for (int idx = tid; idx < LC * CW; idx += kR2LThreads) {
+            const int i = idx / CW, cc = idx % CW;
+            const int t = lo + i, ee = e0 + cc;
+            if (t < 0 || ee >= a.E) continue;
+            const long o = (long)(b * a.L + t) * a.E + ee;
+            const float y = ys[idx];
             if (a.y) a.y[o] = y;
-            if (a.x) a.x[o] = to_bf(bf(a.x[o]) + y);
+            if (a.x) a.x[o] = to_bf(bf(xs[BUF][idx]) + y);
         }
     };
 
-    // tokens L-1 down to 0 in groups of U, the next group loaded first
-    Tok cur[U], nxt[U];
-    int t0 = a.L - 1;
-    for (int u = 0; u < U; ++u)
-        if (t0 - u >= 0) load(t0 - u, cur[u]);
-    while (t0 >= 0) {
-        const int t1 = t0 - U;
-        for (int u = 0; u < U; ++u)
-            if (t1 - u >= 0) load(t1 - u, nxt[u]);
-        for (int u = 0; u < U; ++u)
-            if (t0 - u >= 0) step(t0 - u, cur[u]);
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        t0 = t1;
+    issue(0, 0);
+    for (int k = 0; k < nch; k += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                            // chunk k in LDS; last chunk's writes done
+        if (k + 1 < nch) issue(k + 1, 1);
+        scan_chunk(std::integral_constant<int, 0>{});
+        __syncthreads();
+        write_chunk(std::integral_constant<int, 0>{}, k);
+        if (k + 1 < nch) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (k + 2 < nch) issue(k + 2, 0);
+            scan_chunk(std::integral_constant<int, 1>{});
+            __syncthreads();
+            write_chunk(std::integral_constant<int, 1>{}, k + 1);
+        }
     }
 }
 
@@ -103,16 +216,14 @@ __global__ __launch_bounds__(kR2LThreads) void r2l_scan_kernel(R2LArgs a)
 
 hipError_t launch_r2l(const R2LArgs &a, hipStream_t stream)
 {
-    const int NL = a.N / 4;
+    const int NL = a.N / kR2LS;
     const int CW = kR2LThreads / NL;
     const long grid = (long)a.B * ((a.E + CW - 1) / CW);
     if (grid == 0 || a.L == 0) return hipSuccess;
-    switch (NL) {
-    case 1: r2l_scan_kernel<1><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
-    case 2: r2l_scan_kernel<2><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
-    case 4: r2l_scan_kernel<4><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
-    case 8: r2l_scan_kernel<8><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
-    case 16: r2l_scan_kernel<16><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
+    switch (a.N) {
+    case 8: r2l_scan_kernel<8 / kR2LS><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
+    case 16: r2l_scan_kernel<16 / kR2LS><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
+    case 32: r2l_scan_kernel<32 / kR2LS><<<dim3((unsigned)grid), dim3(kR2LThreads), 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

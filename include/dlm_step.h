@@ -413,8 +413,9 @@ int dlm_ffn(const dlm_layer_desc *layer, const void *h, const void *w_gate, cons
  *   y         fp32 [B, L, E] out, or NULL
  *   x         bf16 [B, L, E] in/out, or NULL: x = bf16(x + y), the correction
  *             joining the hidden stream
- * At least one of y and x.  Bm and Cm 16-byte aligned.
- * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED (N not in {4, 8, 16, 32, 64}),
+ * At least one of y and x.  u, delta, Bm, Cm and x 16-byte aligned.
+ * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED (N not in {8, 16, 32}, or E
+ * not a multiple of 8),
  * DLM_E_DESC (gate not finite), DLM_E_HIP.
  */
 typedef struct {

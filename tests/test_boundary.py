@@ -295,6 +295,8 @@ def test_posterior_rejects_nan_gate():
     (dict(E=0), dlm.DLM_E_SHAPE),
     (dict(L=-1), dlm.DLM_E_SHAPE),
     (dict(N=12), dlm.DLM_E_UNSUPPORTED),
+    (dict(N=4), dlm.DLM_E_UNSUPPORTED),
+    (dict(E=60), dlm.DLM_E_UNSUPPORTED),
     (dict(gate=float("inf")), dlm.DLM_E_DESC),
     (dict(u=None), dlm.DLM_E_NULL),
     (dict(y=None, x=None), dlm.DLM_E_NULL),

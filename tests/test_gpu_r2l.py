@@ -59,8 +59,8 @@ def run_and_check(c):
     return ratio
 
 
-@pytest.mark.parametrize("B,L,E,N", [(2, 37, 100, 16), (1, 64, 300, 4), (3, 9, 65, 8), (1, 50, 40, 32),
-                                     (2, 33, 20, 64), (1, 1, 7, 16)])
+@pytest.mark.parametrize("B,L,E,N", [(2, 37, 104, 16), (1, 64, 296, 8), (3, 9, 72, 8), (1, 50, 40, 32),
+                                     (2, 300, 24, 32), (1, 1, 8, 16), (2, 129, 200, 16)])
 def test_r2l_matches_oracle(B, L, E, N):
     _say(f"r2l B={B} L={L} E={E} N={N}")
     c = W.make_r2l("r2l_small", B=B, L=L, E=E, N=N, gate=0.8, seed=B * 100 + N)
