@@ -153,6 +153,46 @@ hipError_t launch_block_buffer(const BBArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_r2l(const R2LArgs &a, hipStream_t stream);
 
+// ---- direct global-to-LDS loads ------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of a byte range: base address, stride 0, size in bytes
+// (16-byte loads at offsets at or past it return zeros), raw 32-bit format.
+__device__ __forceinline__ i32x4 dma_view(const void *base, long bytes)
+{
+    const unsigned long long p = (unsigned long long)base;
+    return i32x4{(int)(unsigned)p, (int)((unsigned)(p >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// Each lane loads 16 bytes at byte offset voff of the view into LDS at
+// lds + 16 * lane (lds the same for the whole wave).  The load is issued
+// from inline assembly and has no register result: the compiler neither
+// tracks it nor adds waits for it, so every wait for these loads is the
+// caller's (dma_wait_barrier, or a final vmcnt(0)), and the "memory"
+// clobber keeps the compiler from moving LDS accesses across the issue.
+// The compiler's hazard checks do not see inside the block, so it starts
+// with the wait states the hardware needs between a write of M0 (one) or a
+// VALU write of an SGPR (five) and a vector memory instruction reading it.
+__device__ __forceinline__ void dma16(i32x4 view, int voff, const void *lds)
+{
+    typedef __attribute__((address_space(3))) const void lds_cvoid;
+    const int m0 = __builtin_amdgcn_readfirstlane((int)(size_t)(lds_cvoid *)lds);
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(view), "{m0}"(m0)
+                 : "memory");
+}
+
+// Stage boundary of a ring of LDS tiles filled by dma16: wait until at
+// most N vector-memory operations of this wave are outstanding (they
+// complete in issue order, so the loads of the tile about to be read have
+// landed) and all its LDS operations are done, then the workgroup barrier.
+// The "memory" clobber keeps the compiler from moving LDS accesses across.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Map a hardware workgroup id to a logical one so that logically
 // consecutive workgroups (which share K/V) run on the same XCD: the
 // dispatcher deals workgroups round-robin over the 8 XCDs.

@@ -15,13 +15,17 @@
 //   EP_SWIGLU   bf16(silu(C_gate) * C_up), two weight matrices, one A tile.
 // Row r = b * M + j is valid when j < m_active[b] (all M rows without it).
 //
-// Workgroup: 256 threads, a 128 x 128 output tile, K in steps of 64.  Each
-// wave owns a 64 x 64 quarter as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.
-// The A and W tiles of the next K step go straight from global memory into
-// LDS (buffer loads with an LDS destination; rows past the end read as zero)
-// while the current ones are multiplied.  A tile row is 128 bytes; its
-// 16-byte chunks are stored at slot chunk ^ ((row >> 1) & 7), so the 16-byte
-// fragment reads of 16 consecutive rows hit 16 different bank groups.
+// Workgroup: 256 threads, a 128 x 128 output tile.  Each wave owns a
+// 64 x 64 quarter as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  The A and W
+// tiles of the next K steps go straight from global memory into LDS (buffer
+// loads with an LDS destination; rows past the end read as zero) while the
+// current ones are multiplied, through a ring of LDS stages: K steps of 64
+// in two stages for the plain products, of 32 in three stages for SwiGLU
+// (its stage holds two weight tiles); either way 64-72 KB of LDS, so two
+// workgroups share a CU (measured on MI355X against 32 x 4, 64 x 3 and
+// 64 x 2 / 32 x 2 for SwiGLU).  Tile rows are stored with their 16-byte
+// chunks permuted per row (gswz) so that fragment reads are free of bank
+// conflicts.
 // Workgroups are ordered weight-tile major and dealt so that the row tiles
 // sharing a weight tile run on one XCD (one L2).
 #include "dlm_internal.h"
@@ -32,22 +36,39 @@ namespace dlm {
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t gemm_view(const void *base, long bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBM = 128, kBN = 128;
+constexpr int kKQ = 64;   // split-K chunks are multiples of this many columns
+
+// K step and LDS stages of the plain products and of the SwiGLU product
+// (two weight tiles per step).  A stage holds (128 + 128 NW) x BK bf16; two
+// workgroups share a CU while 2 x ST stages fit in LDS.
+#ifndef DLM_GEMM_BK
+#define DLM_GEMM_BK 64
+#endif
+#ifndef DLM_GEMM_ST
+#define DLM_GEMM_ST 2
+#endif
+#ifndef DLM_GEMM_SW_BK
+#define DLM_GEMM_SW_BK 32
+#endif
+#ifndef DLM_GEMM_SW_ST
+#define DLM_GEMM_SW_ST 3
+#endif
 constexpr int kOOB = 0x7ffffff0;   // an offset past any view: the load returns zeros
 
-__device__ __forceinline__ int gswz(int row) { return (row >> 1) & 7; }
+// 16-byte chunk swizzle of a tile row of BK bf16: 256 bytes hold 128 / BK
+// rows, and rows that share a bank offset get distinct chunk permutations,
+// so the 16-byte reads of 16 consecutive rows hit 16 different bank groups.
+template <int BK>
+__device__ __forceinline__ int gswz(int row)
+{
+    return (row / (128 / BK)) % (BK / 8);
+}
 
 __device__ __forceinline__ bool row_valid(const GemmArgs &a, int r)
 {
@@ -92,14 +113,19 @@ __device__ __forceinline__ void store_out(const GemmArgs &a, bool swiglu, int r,
     }
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+template <bool SWIGLU, int BK, int ST>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a)
 {
-    constexpr int NW = SWIGLU ? 2 : 1;     // weight matrices sharing the A tile
-    __shared__ __attribute__((aligned(1024))) uint16_t As0[kBM * kBK];
-    __shared__ __attribute__((aligned(1024))) uint16_t As1[kBM * kBK];
-    __shared__ __attribute__((aligned(1024))) uint16_t Ws0[NW * kBN * kBK];
-    __shared__ __attribute__((aligned(1024))) uint16_t Ws1[NW * kBN * kBK];
+    constexpr int NW = SWIGLU ? 2 : 1;          // weight matrices sharing the A tile
+    constexpr int CH = BK / 8;                  // 16-byte chunks per tile row
+    constexpr int NA = kBM * BK / (256 * 8);    // direct 16-byte loads per thread, A tile
+    constexpr int NB = kBN * BK / (256 * 8);    // the same per weight tile
+    constexpr int LPS = NA + NW * NB;           // loads per thread per stage
+    constexpr int KK = BK / 16;                 // MFMA K steps per stage
+    static_assert(ST >= 2 && (BK == 32 || BK == 64), "tile shape");
+    // stage s: the A tile, then the weight tile(s)
+    constexpr int kSlot = (kBM + NW * kBN) * BK;
+    __shared__ __attribute__((aligned(1024))) uint16_t Sm[ST][kSlot];
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -111,15 +137,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     const int m0 = mt * kBM, n0 = nt * kBN;
     const int kbeg = ks * a.kc, kend = min(a.K, kbeg + a.kc);
 
-    // A tile geometry of this thread: load u writes LDS bytes
-    // (4u + wid) * 1024 + lane * 16: tile row ar[u], slot sl; the global
-    // chunk it fetches is sl ^ gswz(row).
-    int arow_off[4], achunk[4];
+    // Tile geometry of this thread: load u writes LDS bytes
+    // (4u + wid) * 1024 + lane * 16, i.e. tile row byte / (2 BK) and 16-byte
+    // slot (byte / 16) % CH; the global chunk it fetches is slot ^ gswz(row).
+    int arow_off[NA], achunk[NA];
     bool any = false;
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NA; ++u) {
         const int byte = (4 * u + wid) * 1024 + lane * 16;
-        const int row = byte >> 7, sl = (byte >> 4) & 7;
-        achunk[u] = sl ^ gswz(row);
+        const int row = byte / (2 * BK), sl = (byte >> 4) % CH;
+        achunk[u] = sl ^ gswz<BK>(row);
         const int r = m0 + row;
         const bool ok = row_valid(a, r);
         any |= ok;
@@ -137,45 +163,45 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     }
     if (!__syncthreads_or(any)) return;     // no valid row in this tile
 
-    const __amdgpu_buffer_rsrc_t ars = gemm_view(a.a, a.a_bytes);
-    const __amdgpu_buffer_rsrc_t w0 = gemm_view(a.w0, (long)a.N * a.K * 2);
-    const __amdgpu_buffer_rsrc_t w1 = gemm_view(SWIGLU ? a.w1 : a.w0, (long)a.N * a.K * 2);
-    int woff[4];
-    for (int u = 0; u < 4; ++u) {
+    const i32x4 ars = dma_view(a.a, a.a_bytes);
+    const i32x4 w0 = dma_view(a.w0, (long)a.N * a.K * 2);
+    const i32x4 w1 = dma_view(SWIGLU ? a.w1 : a.w0, (long)a.N * a.K * 2);
+    int woff[NB];
+    for (int u = 0; u < NB; ++u) {
         const int byte = (4 * u + wid) * 1024 + lane * 16;
-        const int row = byte >> 7, sl = (byte >> 4) & 7;
+        const int row = byte / (2 * BK), sl = (byte >> 4) % CH;
         const int n = n0 + row;
-        woff[u] = n < a.N ? (n * a.K + (sl ^ gswz(row)) * 8) * 2 : -1;
+        woff[u] = n < a.N ? (n * a.K + (sl ^ gswz<BK>(row)) * 8) * 2 : -1;
     }
 
-    auto issue = [&](int k0, uint16_t *as, uint16_t *ws) {
+    // Load the K step at k0 into a slot; a step past this split's end
+    // (k0 >= kend) loads zeros, so every stage issues the same loads.
+    auto issue = [&](int k0, uint16_t *slot) {
+        const bool live = k0 < kend;
         int koff;                            // byte offset of column k0 within a row
         if (a.a_mode == 2)
             koff = ((k0 / a.D) * a.M * a.D + k0 % a.D) * 2;
         else
             koff = k0 * 2;
-        for (int u = 0; u < 4; ++u) {
-            const int off = arow_off[u] < 0 ? kOOB : arow_off[u] + koff + achunk[u] * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void *)(as + (4 * u + wid) * 512), 16, off, 0, 0,
-                                                     0);
+        for (int u = 0; u < NA; ++u) {
+            const int off = (arow_off[u] < 0 || !live) ? kOOB : arow_off[u] + koff + achunk[u] * 16;
+            dma16(ars, off, slot + (4 * u + wid) * 512);
         }
-        for (int u = 0; u < 4; ++u) {
-            const int off = woff[u] < 0 ? kOOB : woff[u] + k0 * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(w0, (lds_void *)(ws + (4 * u + wid) * 512), 16, off, 0, 0,
-                                                     0);
-            if (SWIGLU)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(w1, (lds_void *)(ws + kBN * kBK + (4 * u + wid) * 512),
-                                                         16, off, 0, 0, 0);
+        uint16_t *ws = slot + kBM * BK;
+        for (int u = 0; u < NB; ++u) {
+            const int off = (woff[u] < 0 || !live) ? kOOB : woff[u] + k0 * 2;
+            dma16(w0, off, ws + (4 * u + wid) * 512);
+            if (SWIGLU) dma16(w1, off, ws + kBN * BK + (4 * u + wid) * 512);
         }
     };
 
     // fragment read offsets (elements): row (wm*64 + 32i + l32), chunk 2kk + hh
-    int ard[2][4], wrd[2][4];
+    int ard[2][KK], wrd[2][KK];
     for (int i = 0; i < 2; ++i)
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KK; ++kk) {
             const int ra = wm * 64 + 32 * i + l32, rw = wn * 64 + 32 * i + l32;
-            ard[i][kk] = ra * kBK + (((2 * kk + hh) ^ gswz(ra)) * 8);
-            wrd[i][kk] = rw * kBK + (((2 * kk + hh) ^ gswz(rw)) * 8);
+            ard[i][kk] = ra * BK + (((2 * kk + hh) ^ gswz<BK>(ra)) * 8);
+            wrd[i][kk] = kBM * BK + rw * BK + (((2 * kk + hh) ^ gswz<BK>(rw)) * 8);
         }
 
     f32x16 acc[NW][2][2];
@@ -183,38 +209,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         for (int i = 0; i < 2; ++i)
             for (int j = 0; j < 2; ++j) acc[w][i][j] = f32x16{};
 
-    auto compute = [&](const uint16_t *as, const uint16_t *ws) {
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(as + ard[0][kk]);
-            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(as + ard[1][kk]);
-            for (int w = 0; w < NW; ++w) {
-                const uint16_t *wt = ws + w * kBN * kBK;
-                const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(wt + wrd[0][kk]);
-                const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(wt + wrd[1][kk]);
-                acc[w][0][0] = mma(a0, b0, acc[w][0][0]);
-                acc[w][0][1] = mma(a0, b1, acc[w][0][1]);
-                acc[w][1][0] = mma(a1, b0, acc[w][1][0]);
-                acc[w][1][1] = mma(a1, b1, acc[w][1][1]);
+    auto compute = [&](const uint16_t *slot) {
+        for (int kk = 0; kk < KK; ++kk) {
+            bf16x8 af[2], bf[NW][2];
+            for (int i = 0; i < 2; ++i) {
+                af[i] = *reinterpret_cast<const bf16x8 *>(slot + ard[i][kk]);
+                for (int w = 0; w < NW; ++w)
+                    bf[w][i] = *reinterpret_cast<const bf16x8 *>(slot + w * kBN * BK + wrd[i][kk]);
             }
+            for (int w = 0; w < NW; ++w)
+                for (int i = 0; i < 2; ++i)
+                    for (int j = 0; j < 2; ++j) acc[w][i][j] = mma(af[i], bf[w][j], acc[w][i][j]);
         }
     };
 
-    const int nk = (kend - kbeg) / kBK;
-    issue(kbeg, As0, Ws0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t = 0; t < nk; t += 2) {
-        if (t + 1 < nk) issue(kbeg + (t + 1) * kBK, As1, Ws1);
-        compute(As0, Ws0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (t + 1 < nk) {
-            if (t + 2 < nk) issue(kbeg + (t + 2) * kBK, As0, Ws0);
-            compute(As1, Ws1);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
+    // ST-stage pipeline: at step t the loads of steps t .. t+ST-2 are in
+    // flight; wait for step t alone, one barrier (step t visible to every
+    // wave; the slot of step t-1 free), load step t+ST-1 into that slot,
+    // multiply step t.  Steps past the end load zeros and are not
+    // multiplied, so the wait count is the same at every step.
+    const int nk = (kend - kbeg) / BK;
+    for (int q = 0; q < ST - 1; ++q) issue(kbeg + q * BK, Sm[q]);
+    int rd = 0, wr = ST - 1;                 // slots of steps t and t+ST-1
+    for (int t = 0; t < nk; ++t) {
+        dma_wait_barrier<(ST - 2) * LPS>();
+        issue(kbeg + (t + ST - 1) * BK, Sm[wr]);
+        compute(Sm[rd]);
+        rd = rd + 1 == ST ? 0 : rd + 1;
+        wr = wr + 1 == ST ? 0 : wr + 1;
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the trailing loads of zeros
 
     // Epilogue.  Accumulator element e of lane (l32, hh) in tile (i, j) is
     // row wm*64 + 32i + 8(e/4) + 4hh + e%4, column wn*64 + 32j + l32.  With
@@ -265,17 +289,17 @@ GemmPlan plan_gemm(int rows, int N, int K, bool swiglu)
 {
     GemmPlan p{};
     const long tiles = (long)((rows + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    // Too few output tiles to fill the chip: split K (at least four K steps
+    // Too few output tiles to fill the chip: split K (at least 256 columns
     // per split), the partial sums then reduced by a second kernel.  From
     // 1.5 tiles per CU on, the partial-sum traffic costs more than the
     // extra parallelism gains (measured on MI355X).
     int s = 1;
     if (tiles > 0 && tiles < 3L * kNumCU / 2) {
         s = (int)((2L * kNumCU + tiles - 1) / tiles);
-        s = max(1, min(s, min(16, K / (4 * kBK))));
+        s = max(1, min(s, min(16, K / 256)));
     }
-    const int steps = (K / kBK + s - 1) / s;
-    p.kc = steps * kBK;
+    const int steps = (K / kKQ + s - 1) / s;
+    p.kc = steps * kKQ;
     p.splits = (K + p.kc - 1) / p.kc;
     p.part_bytes = p.splits > 1 ? (size_t)p.splits * rows * N * (swiglu ? 2 : 1) * sizeof(float) : 0;
     return p;
@@ -286,9 +310,9 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
     const long tiles = (long)((a.B * a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN) * a.splits;
     if (tiles == 0) return hipSuccess;
     if (a.w1)
-        gemm_kernel<true><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
+        gemm_kernel<true, DLM_GEMM_SW_BK, DLM_GEMM_SW_ST><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
     else
-        gemm_kernel<false><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
+        gemm_kernel<false, DLM_GEMM_BK, DLM_GEMM_ST><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
     if (a.splits > 1) {
         const long n = (long)a.B * a.M * a.N;
         gemm_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(a, a.w1 ? 1 : 0);
