@@ -240,13 +240,23 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
 constexpr int kStageBytes = 48 * 1024;   // 1024 partials of 48 bytes
 constexpr int kMergeLanes = 8;
 
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS
+// operations are complete, then s_barrier.  Unlike __syncthreads() it does
+// not wait for the wave's global stores (the kernel's outputs, which no
+// other wave reads back), so those drain while the kernel goes on.  The
+// "memory" clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float block_max(float v, float *red)
 {
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
     const int wid = threadIdx.x >> 6;
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) red[wid] = v;
-    __syncthreads();
+    lds_barrier();
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         const v4u *src = reinterpret_cast<const v4u *>(a.part + (long)(g0 + r0) * a.n_chunks);
         v4u *dst = reinterpret_cast<v4u *>(stage_s);
         const int n16 = nr * a.n_chunks * (int)(sizeof(PostPartial) / 16);
-        if (r0 > 0) __syncthreads();
+        if (r0 > 0) lds_barrier();
         // up to twelve 16-byte loads in flight per thread (one round: the stage is 3072)
         for (int i0 = 0; i0 < n16; i0 += 256 * 12) {
             v4u v[12];
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int t0 = 0; t0 < nr; t0 += 256 / lanes) {
             const int t = t0 + tid / lanes;
             const int sub = tid % lanes;
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         for (int t = tid; t < n; t += 256) a.sel[g0 + t] = -1;
         return;
     }
-    __syncthreads();   // row results visible
+    lds_barrier();   // row results (LDS) visible
     // Dynamic threshold: the largest score of an eligible non-candidate.
     float thr = -INFINITY;
     if (a.mode == 3) {
@@ -389,7 +399,12 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         if (a.mode == 2 && conf_s[t] > a.tau) mine = 1;
         if (a.mode == 3 && conf_s[t] > a.tau && key_s[t] > thr) mine = 1;
     }
-    const int any = __syncthreads_or(mine);
+    __shared__ int any_s;
+    if (tid == 0) any_s = 0;
+    lds_barrier();
+    if (mine) any_s = 1;                    // benign race: every writer stores 1
+    lds_barrier();
+    const int any = any_s;
     // rank(t) = number of eligible rows ordered before t: (key desc, row
     // asc).  Each row's (key, row) is packed into one 64-bit integer whose
     // unsigned order is exactly that order: the key's bits made
@@ -407,14 +422,14 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
     constexpr int kCountMax = 256;
     const bool counted = n <= kCountMax;
-    __syncthreads();
+    lds_barrier();
     for (int t = tid; t < n; t += 256) {
         const unsigned bits = __float_as_uint(elig_s[t] ? key_s[t] : -INFINITY);
         const unsigned ord = bits ^ ((unsigned)((int)bits >> 31) | 0x80000000u);
         ord_s[t] = ((unsigned long long)ord << 32) | (0xffffffffu - (unsigned)t);
     }
     for (int t = n + tid; t < ((n + 1) & ~1); t += 256) ord_s[t] = 0;   // even count
-    __syncthreads();
+    lds_barrier();
     // the kk-th largest packed value (kk in [1, n]); block-uniform call
     auto kth_largest = [&](int kk) -> unsigned long long {
         unsigned long long prefix = 0;
@@ -422,12 +437,12 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         for (int pass = 7; pass >= 0; --pass) {
             const int shift = pass * 8;
             hist_s[tid] = 0;
-            __syncthreads();
+            lds_barrier();
             for (int i = tid; i < n; i += 256) {
                 const unsigned long long v = ord_s[i];
                 if (pass == 7 || (v >> (shift + 8)) == prefix) atomicAdd(&hist_s[(v >> shift) & 255], 1);
             }
-            __syncthreads();
+            lds_barrier();
             if (tid < 64) {
                 // lane l holds bins 255 - 4l - j, j = 0..3 (descending)
                 int c[4], sum = 0;
@@ -452,10 +467,10 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             prefix = (prefix << 8) | (unsigned)pick_s[0];
             krem = pick_s[1];
-            __syncthreads();
+            lds_barrier();
         }
         return prefix;
     };
@@ -473,6 +488,9 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
             bool first = false, in_topk = false;
             if (counted) {
                 int rank = 0;
+                // sixteen 16-byte LDS reads in flight (one wave per SIMD:
+                // nothing else hides their latency)
+#pragma unroll 16
                 for (int u = 0; u < n; u += 2) {
                     const u64x2 p = *reinterpret_cast<const u64x2 *>(&ord_s[u]);
                     rank += (p.x > mine ? 1 : 0) + (p.y > mine ? 1 : 0);

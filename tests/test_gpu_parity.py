@@ -302,16 +302,18 @@ def test_posterior_edge_cases():
         assert np.all(sel.cpu().numpy()[locked == 1] == -1)
 
 
-@pytest.mark.parametrize("g", [200, 257, 700, 1024])
-def test_large_selection_groups(g):
+@pytest.mark.parametrize("g,V", [(200, 600), (257, 600), (700, 600), (1024, 600), (129, 33000), (300, 40000)])
+def test_large_selection_groups(g, V):
     """Groups of more than 256 rows pick by radix selection of the k-th
     largest packed key (up to 1024 rows), smaller ones by counting: every
     ranking mode on both sides of the boundary, a ragged last group, locked
-    rows and rows that may not be selected."""
+    rows and rows that may not be selected.  With the larger vocabularies
+    each row is also split into vocabulary chunks, so the finishing kernel
+    merges several partials per row before it selects."""
     import denoising_step_amd as dlm
     dev = torch.device("cuda")
     rng = np.random.default_rng(60 + g)
-    R, V = 2 * g + 77, 600
+    R = 2 * g + 77
     x = (rng.standard_normal((R, V)) * rng.uniform(0.5, 4.0, R)[:, None]).astype(np.float32)
     y = (x + rng.standard_normal((R, V)) * 0.1).astype(np.float32)
     locked = (rng.random(R) < 0.2).astype(np.uint8)
