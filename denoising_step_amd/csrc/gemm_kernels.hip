@@ -41,7 +41,7 @@ __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kBM = 128, kBN = 128;
+constexpr int kBN = 128;
 constexpr int kKQ = 64;   // split-K chunks are multiples of this many columns
 
 // K step and LDS stages of the plain products and of the SwiGLU product
@@ -60,6 +60,24 @@ constexpr int kKQ = 64;   // split-K chunks are multiples of this many columns
 #define DLM_GEMM_SW_ST 3
 #endif
 constexpr int kOOB = 0x7ffffff0;   // an offset past any view: the load returns zeros
+
+// Row-tile height for a product over `rows` rows.  Up to 256 rows (two row
+// tiles) the work is streaming the weights: one workgroup per CU with a
+// deep ring of 64-wide K steps (as many stages as about 150 KB of LDS
+// holds), so that 120-150 KB of weights are in flight per CU, and a 32-,
+// 64- or 128-row tile (up to 64 rows the four waves sit side by side over
+// the 128 columns).  More rows: 128-row tiles, two workgroups per CU, a
+// shallower ring (measured on MI355X: the deep ring wins up to 256 rows
+// and loses at 512).
+__host__ __device__ constexpr int gemm_bm(int rows) { return rows <= 32 ? 32 : rows <= 64 ? 64 : 128; }
+#ifndef DLM_GEMM_DEEP_MAX
+#define DLM_GEMM_DEEP_MAX 256
+#endif
+__host__ __device__ constexpr bool gemm_deep(int rows) { return rows <= DLM_GEMM_DEEP_MAX; }
+__host__ __device__ constexpr int skinny_stages(int bm, int nw)
+{
+    return (150 * 1024) / ((bm + nw * kBN) * 64 * 2) < 8 ? (150 * 1024) / ((bm + nw * kBN) * 64 * 2) : 8;
+}
 
 // 16-byte chunk swizzle of a tile row of BK bf16: 256 bytes hold 128 / BK
 // rows, and rows that share a bank offset get distinct chunk permutations,
@@ -113,23 +131,29 @@ __device__ __forceinline__ void store_out(const GemmArgs &a, bool swiglu, int r,
     }
 }
 
-template <bool SWIGLU, int BK, int ST>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a)
+template <bool SWIGLU, int BM, int BK, int ST>
+__global__ __launch_bounds__(256, 2 * 2 * (BM + (SWIGLU ? 2 : 1) * kBN) * BK * ST <= 160 * 1024 ? 2 : 1) void
+gemm_kernel(GemmArgs a)
 {
+    constexpr int kBM = BM;
     constexpr int NW = SWIGLU ? 2 : 1;          // weight matrices sharing the A tile
+    constexpr int WM = BM == 128 ? 2 : 1;       // wave grid WM x WN over the tile
+    constexpr int WN = 4 / WM;
+    constexpr int TI = BM / (32 * WM);          // 32 x 32 MFMA tiles per wave: TI x TJ
+    constexpr int TJ = kBN / (32 * WN);
     constexpr int CH = BK / 8;                  // 16-byte chunks per tile row
     constexpr int NA = kBM * BK / (256 * 8);    // direct 16-byte loads per thread, A tile
     constexpr int NB = kBN * BK / (256 * 8);    // the same per weight tile
     constexpr int LPS = NA + NW * NB;           // loads per thread per stage
     constexpr int KK = BK / 16;                 // MFMA K steps per stage
-    static_assert(ST >= 2 && (BK == 32 || BK == 64), "tile shape");
+    static_assert(ST >= 2 && (BK == 32 || BK == 64) && NA >= 1, "tile shape");
     // stage s: the A tile, then the weight tile(s)
     constexpr int kSlot = (kBM + NW * kBN) * BK;
     __shared__ __attribute__((aligned(1024))) uint16_t Sm[ST][kSlot];
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int wm = wid >> 1, wn = wid & 1;
+    const int wm = wid / WN, wn = wid % WN;
     const int tiles_m = (a.B * a.M + kBM - 1) / kBM;
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int mt = L % tiles_m, rest = L / tiles_m;
@@ -195,31 +219,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a)
         }
     };
 
-    // fragment read offsets (elements): row (wm*64 + 32i + l32), chunk 2kk + hh
-    int ard[2][KK], wrd[2][KK];
-    for (int i = 0; i < 2; ++i)
-        for (int kk = 0; kk < KK; ++kk) {
-            const int ra = wm * 64 + 32 * i + l32, rw = wn * 64 + 32 * i + l32;
+    // fragment read offsets (elements): A row wm*32TI + 32i + l32, W row
+    // wn*32TJ + 32j + l32, chunk 2kk + hh
+    int ard[TI][KK], wrd[TJ][KK];
+    for (int kk = 0; kk < KK; ++kk) {
+        for (int i = 0; i < TI; ++i) {
+            const int ra = wm * 32 * TI + 32 * i + l32;
             ard[i][kk] = ra * BK + (((2 * kk + hh) ^ gswz<BK>(ra)) * 8);
-            wrd[i][kk] = kBM * BK + rw * BK + (((2 * kk + hh) ^ gswz<BK>(rw)) * 8);
         }
+        for (int j = 0; j < TJ; ++j) {
+            const int rw = wn * 32 * TJ + 32 * j + l32;
+            wrd[j][kk] = kBM * BK + rw * BK + (((2 * kk + hh) ^ gswz<BK>(rw)) * 8);
+        }
+    }
 
-    f32x16 acc[NW][2][2];
+    f32x16 acc[NW][TI][TJ];
     for (int w = 0; w < NW; ++w)
-        for (int i = 0; i < 2; ++i)
-            for (int j = 0; j < 2; ++j) acc[w][i][j] = f32x16{};
+        for (int i = 0; i < TI; ++i)
+            for (int j = 0; j < TJ; ++j) acc[w][i][j] = f32x16{};
 
     auto compute = [&](const uint16_t *slot) {
         for (int kk = 0; kk < KK; ++kk) {
-            bf16x8 af[2], bf[NW][2];
-            for (int i = 0; i < 2; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8 *>(slot + ard[i][kk]);
-                for (int w = 0; w < NW; ++w)
-                    bf[w][i] = *reinterpret_cast<const bf16x8 *>(slot + w * kBN * BK + wrd[i][kk]);
-            }
+            bf16x8 af[TI], bf[NW][TJ];
+            for (int i = 0; i < TI; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(slot + ard[i][kk]);
             for (int w = 0; w < NW; ++w)
-                for (int i = 0; i < 2; ++i)
-                    for (int j = 0; j < 2; ++j) acc[w][i][j] = mma(af[i], bf[w][j], acc[w][i][j]);
+                for (int j = 0; j < TJ; ++j)
+                    bf[w][j] = *reinterpret_cast<const bf16x8 *>(slot + w * kBN * BK + wrd[j][kk]);
+            for (int w = 0; w < NW; ++w)
+                for (int i = 0; i < TI; ++i)
+                    for (int j = 0; j < TJ; ++j) acc[w][i][j] = mma(af[i], bf[w][j], acc[w][i][j]);
         }
     };
 
@@ -241,16 +269,16 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the trailing loads of zeros
 
     // Epilogue.  Accumulator element e of lane (l32, hh) in tile (i, j) is
-    // row wm*64 + 32i + 8(e/4) + 4hh + e%4, column wn*64 + 32j + l32.  With
-    // K splits the fp32 sums go to this split's slice of the partials.
+    // row wm*32TI + 32i + 8(e/4) + 4hh + e%4, column wn*32TJ + 32j + l32.
+    // With K splits the fp32 sums go to this split's slice of the partials.
     const long rows = (long)a.B * a.M;
     const int np = SWIGLU ? 2 * a.N : a.N;
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
         for (int e = 0; e < 16; ++e) {
-            const int r = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const int r = m0 + wm * 32 * TI + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
             if (!row_valid(a, r)) continue;
-            for (int jj = 0; jj < 2; ++jj) {
-                const int n = n0 + wn * 64 + 32 * jj + l32;
+            for (int jj = 0; jj < TJ; ++jj) {
+                const int n = n0 + wn * 32 * TJ + 32 * jj + l32;
                 if (n >= a.N) continue;
                 const float v = acc[0][i][jj][e], up = acc[NW - 1][i][jj][e];
                 if (a.splits > 1) {
@@ -288,13 +316,19 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, int swiglu
 GemmPlan plan_gemm(int rows, int N, int K, bool swiglu)
 {
     GemmPlan p{};
-    const long tiles = (long)((rows + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int bm = gemm_bm(rows);
+    const long tiles = (long)((rows + bm - 1) / bm) * ((N + kBN - 1) / kBN);
     // Too few output tiles to fill the chip: split K (at least 256 columns
     // per split), the partial sums then reduced by a second kernel.  From
     // 1.5 tiles per CU on, the partial-sum traffic costs more than the
     // extra parallelism gains (measured on MI355X).
     int s = 1;
-    if (tiles > 0 && tiles < 3L * kNumCU / 2) {
+    if (gemm_deep(rows) && tiles > 0) {
+        // deep-ring tiles run one workgroup per CU: one round of
+        // workgroups, each streaming as many K steps as the split allows
+        // (a workgroup pays one ring fill)
+        s = max(1, min((int)(kNumCU / tiles), min(16, K / 256)));
+    } else if (tiles > 0 && tiles < 3L * kNumCU / 2) {
         s = (int)((2L * kNumCU + tiles - 1) / tiles);
         s = max(1, min(s, min(16, K / 256)));
     }
@@ -307,12 +341,30 @@ GemmPlan plan_gemm(int rows, int N, int K, bool swiglu)
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 {
-    const long tiles = (long)((a.B * a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN) * a.splits;
+    const int bm = gemm_bm(a.B * a.M);
+    const long tiles = (long)((a.B * a.M + bm - 1) / bm) * ((a.N + kBN - 1) / kBN) * a.splits;
     if (tiles == 0) return hipSuccess;
-    if (a.w1)
-        gemm_kernel<true, DLM_GEMM_SW_BK, DLM_GEMM_SW_ST><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
-    else
-        gemm_kernel<false, DLM_GEMM_BK, DLM_GEMM_ST><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(a);
+    const dim3 grid((unsigned)tiles), block(256);
+    const bool deep = gemm_deep(a.B * a.M);
+    if (a.w1) {
+        if (bm == 32)
+            gemm_kernel<true, 32, 64, skinny_stages(32, 2)><<<grid, block, 0, stream>>>(a);
+        else if (bm == 64)
+            gemm_kernel<true, 64, 64, skinny_stages(64, 2)><<<grid, block, 0, stream>>>(a);
+        else if (deep)
+            gemm_kernel<true, 128, 64, skinny_stages(128, 2)><<<grid, block, 0, stream>>>(a);
+        else
+            gemm_kernel<true, 128, DLM_GEMM_SW_BK, DLM_GEMM_SW_ST><<<grid, block, 0, stream>>>(a);
+    } else {
+        if (bm == 32)
+            gemm_kernel<false, 32, 64, skinny_stages(32, 1)><<<grid, block, 0, stream>>>(a);
+        else if (bm == 64)
+            gemm_kernel<false, 64, 64, skinny_stages(64, 1)><<<grid, block, 0, stream>>>(a);
+        else if (deep)
+            gemm_kernel<false, 128, 64, skinny_stages(128, 1)><<<grid, block, 0, stream>>>(a);
+        else
+            gemm_kernel<false, 128, DLM_GEMM_BK, DLM_GEMM_ST><<<grid, block, 0, stream>>>(a);
+    }
     if (a.splits > 1) {
         const long n = (long)a.B * a.M * a.N;
         gemm_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(a, a.w1 ? 1 : 0);

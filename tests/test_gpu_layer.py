@@ -68,6 +68,12 @@ CASES = {
     "rows_cut": dict(B=2, n_pos=260, d=320, Hq=4, Hkv=4, D=64, F=192, M=257, m=[0, 129]),
     # few rows, long K: every product splits K (partial sums and the reduction)
     "split_k": dict(B=2, n_pos=64, d=1024, Hq=16, Hkv=4, D=64, F=1024, M=40, m=[33, 40]),
+    # up to 64 rows in all: the 32- and 64-row tiles with their deep stage
+    # rings; K splits, ragged column tiles, several batch entries sharing
+    # one row tile, an entry with no rows
+    "skinny32_split_k": dict(B=1, n_pos=100, d=1024, Hq=16, Hkv=4, D=64, F=1024, M=24, m=[17]),
+    "skinny32_batches": dict(B=4, n_pos=40, d=256, Hq=4, Hkv=2, D=64, F=384, M=8, m=[8, 0, 5, 8]),
+    "skinny64_ragged": dict(B=2, n_pos=70, d=320, Hq=4, Hkv=4, D=64, F=192, M=30, m=[30, 11]),
 }
 
 
@@ -148,14 +154,17 @@ def test_layer_calls_match_oracle(name):
     _say(f"  worst error / bound = {worst:.3f}")
 
 
-def test_layer_full_size_sampled():
+@pytest.mark.parametrize("M", [1024, 200, 100, 48, 16])
+def test_layer_full_size_sampled(M):
     """The LLaDA-8B-shaped layer (width 4096, 32 heads of 128, feed-forward
-    12288) with 1024 of 2048 positions active: sampled rows against the
-    oracle, each element against the same bound."""
-    c = W.layer_llada(M=1024, n_pos=2048)
-    _say("layer llada full size")
+    12288) with M of 2048 positions active (128-row tiles two to a CU; up
+    to 256 rows, the one-per-CU deep-ring tiles of 128, 64 and 32 rows with
+    K splits): sampled rows against the oracle, each element against the
+    same bound."""
+    c = W.layer_llada(M=M, n_pos=2048)
+    _say(f"layer llada full size M={M}")
     qg, kg, vg, hg, xg = _run_layer(c, None)
-    rows = np.array([0, 1, 127, 128, 511, 640, 1000, 1023])
+    rows = np.array([0, 1, 127, 128, 511, 640, 1000, 1023]) if M == 1024 else np.array([0, 1, M // 2, M - 2, M - 1])
     sub = W.LayerCase(**{**c.__dict__, "M": len(rows), "active_idx": c.active_idx[:, rows],
                          "m": np.array([len(rows)], np.int32), "attn_out": c.attn_out[:, :, rows],
                          "h": c.h[:, rows]})
