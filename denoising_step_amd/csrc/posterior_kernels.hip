@@ -296,8 +296,9 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         while (lanes < kMergeLanes && n * lanes * 2 <= 256) lanes *= 2;
     const bool wide = lanes > 1;
 
-    // Issue the lock-flag and score loads together with the first staging
-    // round; nothing waits until the barrier.
+    // Issue the lock-flag and score loads together with the staging loads
+    // of the partials (when they fit one round); nothing waits until the
+    // barrier.
     uint8_t lk[4], fl[4];
     float sc[4];
 #pragma unroll
@@ -307,14 +308,100 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         fl[k] = (a.flags && t < n) ? a.flags[g0 + t] : 3;
         sc[k] = (by_score && t < n) ? a.score[g0 + t] : 0.f;
     }
-    for (int r0 = 0; r0 < n; r0 += rows_per_round) {
+    // Finish row gt of the group from its merged state s.
+    auto finish_row = [&](int gt, const RowState &s, bool was_locked) {
+        const int r = g0 + gt;
+        float klv = 0.f, cf = 0.f, mg = 0.f, en = 0.f;
+        int tok = -1;
+        if (!was_locked) {
+            // KL = t/sx - (mx + ln sx) + (my + ln sy)
+            klv = s.tx / s.sx - (s.mx - s.my) - (logf(s.sx) - logf(s.sy));
+            cf = 1.f / s.sx;
+            tok = s.ai;
+            a.locked[r] = (klv <= a.eps && (rowf_s[gt] & 4) && cf >= a.conf_gate) ? 1 : 0;
+            // margin = p(top-1) - p(top-2) = conf * (1 - exp(a2 - mx)): exactly
+            // 0 on a tie, conf without a runner-up; entropy = ln sx - ex / sx
+            mg = cf * (1.f - fast_exp2((s.a2 - s.mx) * kLog2e));
+            en = logf(s.sx) - s.ex / s.sx;
+        }
+        a.kl[r] = klv;
+        a.conf[r] = cf;
+        if (a.margin) a.margin[r] = mg;
+        if (a.entropy) a.entropy[r] = en;
+        conf_s[gt] = cf;
+        tok_s[gt] = tok;
+        if (!by_score) key_s[gt] = a.mode == 5 ? mg : a.mode == 6 ? -en : cf;
+    };
+    auto set_flags = [&]() {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = tid + 256 * k;
+            if (t < n) {
+                elig_s[t] = (lk[k] == 0 && (fl[k] & 1)) ? 1 : 0;
+                rowf_s[t] = (lk[k] == 0 ? 1 : 0) | ((fl[k] & 2) << 1);
+                if (by_score) key_s[t] = sc[k];
+            }
+        }
+    };
+    if (rows_per_round < n) {
+        // A group of more than 256 rows with split rows: its partials would
+        // take several staging rounds, so each thread merges its rows
+        // (gt = tid, tid + 256, ...) straight from global memory, issuing
+        // the loads of up to kDirect partials (several rows when a row has
+        // fewer chunks) before merging any, each row in chunk order.  Rows
+        // locked on entry load nothing, which is what makes this path
+        // cheap late in a run, when most rows of the group are locked.
+        constexpr int kDirect = 16;
+        set_flags();
+        lds_barrier();
+        const int nc = a.n_chunks;
+        if (nc <= kDirect) {
+            const int rpb = kDirect / nc;           // rows per batch
+            for (int gt0 = tid; gt0 < n; gt0 += 256 * rpb) {
+                PostPartial q[kDirect];
+#pragma unroll
+                for (int u = 0; u < kDirect; ++u) {
+                    const int i = u / nc, c = u - i * nc, gt = gt0 + 256 * i;
+                    if (i < rpb && gt < n && (rowf_s[gt] & 1)) q[u] = a.part[(long)(g0 + gt) * nc + c];
+                }
+                RowState s;
+                rs_init(s);
+#pragma unroll
+                for (int u = 0; u < kDirect; ++u) {
+                    const int i = u / nc, c = u - i * nc, gt = gt0 + 256 * i;
+                    if (i < rpb && gt < n) {
+                        const bool live = rowf_s[gt] & 1;
+                        if (c == 0) rs_init(s);
+                        if (live) rs_merge(s, rs_load(q[u]));
+                        if (c == nc - 1) finish_row(gt, s, !live);
+                    }
+                }
+            }
+        } else {
+            for (int gt = tid; gt < n; gt += 256) {
+                const bool live = rowf_s[gt] & 1;
+                RowState s;
+                rs_init(s);
+                for (int c0 = 0; live && c0 < nc; c0 += kDirect) {
+                    PostPartial q[kDirect];
+#pragma unroll
+                    for (int u = 0; u < kDirect; ++u)
+                        if (c0 + u < nc) q[u] = a.part[(long)(g0 + gt) * nc + c0 + u];
+#pragma unroll
+                    for (int u = 0; u < kDirect; ++u)
+                        if (c0 + u < nc) rs_merge(s, rs_load(q[u]));
+                }
+                finish_row(gt, s, !live);
+            }
+        }
+    }
+    for (int r0 = 0; rows_per_round >= n && r0 < n; r0 += rows_per_round) {
         const int nr = min(rows_per_round, n - r0);
         // Stage: partials of rows [g0+r0, g0+r0+nr) are contiguous.
         typedef unsigned v4u __attribute__((ext_vector_type(4)));
         const v4u *src = reinterpret_cast<const v4u *>(a.part + (long)(g0 + r0) * a.n_chunks);
         v4u *dst = reinterpret_cast<v4u *>(stage_s);
         const int n16 = nr * a.n_chunks * (int)(sizeof(PostPartial) / 16);
-        if (r0 > 0) lds_barrier();
         // up to twelve 16-byte loads in flight per thread (one round: the stage is 3072)
         for (int i0 = 0; i0 < n16; i0 += 256 * 12) {
             v4u v[12];
@@ -329,17 +416,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                 if (i < n16) dst[i] = v[u];
             }
         }
-        if (r0 == 0) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int t = tid + 256 * k;
-                if (t < n) {
-                    elig_s[t] = (lk[k] == 0 && (fl[k] & 1)) ? 1 : 0;
-                    rowf_s[t] = (lk[k] == 0 ? 1 : 0) | ((fl[k] & 2) << 1);
-                    if (by_score) key_s[t] = sc[k];
-                }
-            }
-        }
+        set_flags();
         lds_barrier();
         for (int t0 = 0; t0 < nr; t0 += 256 / lanes) {
             const int t = t0 + tid / lanes;
@@ -355,29 +432,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
             }
             if (wide)
                 for (int m = lanes / 2; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
-            if (row_ok && sub == 0) {
-                const int r = g0 + gt;
-                float klv = 0.f, cf = 0.f, mg = 0.f, en = 0.f;
-                int tok = -1;
-                if (!was_locked) {
-                    // KL = t/sx - (mx + ln sx) + (my + ln sy)
-                    klv = s.tx / s.sx - (s.mx - s.my) - (logf(s.sx) - logf(s.sy));
-                    cf = 1.f / s.sx;
-                    tok = s.ai;
-                    a.locked[r] = (klv <= a.eps && (rowf_s[gt] & 4) && cf >= a.conf_gate) ? 1 : 0;
-                    // margin = p(top-1) - p(top-2) = conf * (1 - exp(a2 - mx)): exactly
-                    // 0 on a tie, conf without a runner-up; entropy = ln sx - ex / sx
-                    mg = cf * (1.f - fast_exp2((s.a2 - s.mx) * kLog2e));
-                    en = logf(s.sx) - s.ex / s.sx;
-                }
-                a.kl[r] = klv;
-                a.conf[r] = cf;
-                if (a.margin) a.margin[r] = mg;
-                if (a.entropy) a.entropy[r] = en;
-                conf_s[gt] = cf;
-                tok_s[gt] = tok;
-                if (!by_score) key_s[gt] = a.mode == 5 ? mg : a.mode == 6 ? -en : cf;
-            }
+            if (row_ok && sub == 0) finish_row(gt, s, was_locked);
         }
     }
     if (a.mode == 0) {
@@ -539,6 +594,10 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t fi
 #ifndef DLM_POST_WGS_PER_CU
 #define DLM_POST_WGS_PER_CU 16
 #endif
+// Least chunks per row for a selection group of more than 256 rows.
+#ifndef DLM_POST_BIG_CHUNKS
+#define DLM_POST_BIG_CHUNKS 4
+#endif
 
 PostPlan plan_post(int R, int V, int mode, int group_rows)
 {
@@ -552,9 +611,14 @@ PostPlan plan_post(int R, int V, int mode, int group_rows)
         if (R < target) chunks = (int)((target + R - 1) / R);
         const int max_chunks = max(1, (V + kPostThreads * kPostVec - 1) / (kPostThreads * kPostVec));
         chunks = min(chunks, max_chunks);
-        // and a finishing group's partials fit one LDS staging round
+        // A finishing group of up to 256 rows stages its partials in LDS in
+        // one round (measured best: its rows are all live), which caps the
+        // chunks; a larger group (the radix-selection regime of a whole
+        // block, most of whose rows are locked late in a run) merges from
+        // global memory, so its live rows keep several chunks each.
         const int g = min(R, mode == 0 ? 256 : group_rows);
-        chunks = min(chunks, max(1, (kStageBytes / (int)sizeof(PostPartial)) / max(1, g)));
+        if (g <= 256) chunks = min(chunks, max(1, (kStageBytes / (int)sizeof(PostPartial)) / max(1, g)));
+        else chunks = min(max_chunks, max(chunks, DLM_POST_BIG_CHUNKS));
     }
     int chunk = (V + chunks - 1) / chunks;
     // A split row gets chunks of whole streaming steps (4 float4 per array

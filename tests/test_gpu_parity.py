@@ -309,7 +309,8 @@ def test_large_selection_groups(g, V):
     ranking mode on both sides of the boundary, a ragged last group, locked
     rows and rows that may not be selected.  With the larger vocabularies
     each row is also split into vocabulary chunks, so the finishing kernel
-    merges several partials per row before it selects."""
+    merges several partials per row before it selects: through LDS for the
+    129-row groups, straight from global memory for the 300-row ones."""
     import denoising_step_amd as dlm
     dev = torch.device("cuda")
     rng = np.random.default_rng(60 + g)
