@@ -150,6 +150,24 @@ __device__ __forceinline__ void rs_fold_masked(RowState &s, const float (&x)[N],
     if constexpr (SC) s.ex = eh;
 }
 
+constexpr int kStageBytes = 48 * 1024;   // 1024 partials of 48 bytes
+
+// Where partial (row, chunk) lives.  The partials of selection group
+// [g0, g0 + n) fill the block [g0 nc, (g0 + n) nc) of the array.  A group
+// whose partials fit one LDS staging round keeps its block row-major; a
+// larger one, merged straight from global memory one row per thread, keeps
+// it chunk-major, so that consecutive rows of one chunk are contiguous.
+// Both kernels use this one function.
+__device__ __forceinline__ long part_index(const PostArgs &a, int row, int ch)
+{
+    const int gr = a.group_rows;        // as the finishing kernel groups rows
+    const int g0 = row / gr * gr;
+    const int n = min(a.R - g0, gr);
+    const int nc = a.n_chunks;
+    const int per_round = max(1, min(n, (kStageBytes / (int)sizeof(PostPartial)) / nc));
+    return per_round < n ? (long)g0 * nc + (long)ch * n + (row - g0) : (long)row * nc + ch;
+}
+
 template <bool VEC4, bool SC>
 __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs a)
 {
@@ -223,7 +241,7 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
         p.mx = t.mx; p.sx = t.sx; p.tx = t.tx; p.my = t.my; p.sy = t.sy;
         p.av = t.av; p.a2 = t.a2; p.ex = t.ex; p.ai = t.ai;
         p.pad[0] = p.pad[1] = p.pad[2] = 0;
-        a.part[(long)row * a.n_chunks + ch] = p;
+        a.part[part_index(a, row, ch)] = p;
     }
 }
 
@@ -237,7 +255,6 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
 // a fixed butterfly over the lanes combines them; larger groups merge one
 // row per thread.
 // The selection uses block-wide reductions, not a serial scan.
-constexpr int kStageBytes = 48 * 1024;   // 1024 partials of 48 bytes
 constexpr int kMergeLanes = 8;
 
 // Workgroup barrier for data exchanged through LDS only: this wave's LDS
@@ -248,6 +265,37 @@ constexpr int kMergeLanes = 8;
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One step of a 64-bit max across lanes: combine (hi, lo) with the lane
+// the DPP control C names, in the rows of row mask RM (the other rows
+// combine with themselves); all lanes active.
+template <int C, int RM>
+__device__ __forceinline__ void dpp_max_u64(unsigned &lo, unsigned &hi)
+{
+    const unsigned olo = __builtin_amdgcn_update_dpp(lo, lo, C, RM, 0xf, false);
+    const unsigned ohi = __builtin_amdgcn_update_dpp(hi, hi, C, RM, 0xf, false);
+    const bool gt = ohi > hi || (ohi == hi && olo > lo);
+    lo = gt ? olo : lo;
+    hi = gt ? ohi : hi;
+}
+
+// The maximum of a 64-bit value over the wave (every lane active), all in
+// DPP: within each 16-lane row (quad swaps, half-row and row mirrors), then
+// row 15 broadcast into rows 1 and 3 and lane 31 into rows 2 and 3 (GFX9
+// row broadcasts), so lane 63 holds the maximum; one read out.
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
+{
+    unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+    dpp_max_u64<0xB1, 0xf>(lo, hi);   // quad_perm [1,0,3,2]
+    dpp_max_u64<0x4E, 0xf>(lo, hi);   // quad_perm [2,3,0,1]
+    dpp_max_u64<0x141, 0xf>(lo, hi);  // row_half_mirror
+    dpp_max_u64<0x140, 0xf>(lo, hi);  // row_mirror
+    dpp_max_u64<0x142, 0xa>(lo, hi);  // row_bcast:15
+    dpp_max_u64<0x143, 0xc>(lo, hi);  // row_bcast:31
+    // readlane returns int: widen through unsigned (no sign extension)
+    return ((unsigned long long)(unsigned)__builtin_amdgcn_readlane(hi, 63) << 32) |
+           (unsigned long long)(unsigned)__builtin_amdgcn_readlane(lo, 63);
 }
 
 __device__ __forceinline__ float block_max(float v, float *red)
@@ -279,6 +327,8 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     __shared__ __attribute__((aligned(16))) unsigned long long ord_s[kMaxGroupRows];
     __shared__ int hist_s[256];
     __shared__ int pick_s[2];                   // radix select: digit found, count still to go
+    constexpr int kSmallK = 32;                 // up to this k, a tournament instead of radix select
+    __shared__ unsigned long long cand_s[4 * kSmallK + 1];
     __shared__ float red_s[4];
 
     const int tid = threadIdx.x;
@@ -348,36 +398,47 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         // take several staging rounds, so each thread merges its rows
         // (gt = tid, tid + 256, ...) straight from global memory, issuing
         // the loads of up to kDirect partials (several rows when a row has
-        // fewer chunks) before merging any, each row in chunk order.  Rows
-        // locked on entry load nothing, which is what makes this path
-        // cheap late in a run, when most rows of the group are locked.
+        // fewer chunks) before merging any, each row in chunk order.  The
+        // first batch is issued together with the lock-flag loads (one
+        // round trip); a row locked on entry is not merged.
         constexpr int kDirect = 16;
-        set_flags();
-        lds_barrier();
         const int nc = a.n_chunks;
         if (nc <= kDirect) {
             const int rpb = kDirect / nc;           // rows per batch
-            for (int gt0 = tid; gt0 < n; gt0 += 256 * rpb) {
-                PostPartial q[kDirect];
+            PostPartial q[kDirect];
+            auto load_batch = [&](int gt0) {
 #pragma unroll
                 for (int u = 0; u < kDirect; ++u) {
                     const int i = u / nc, c = u - i * nc, gt = gt0 + 256 * i;
-                    if (i < rpb && gt < n && (rowf_s[gt] & 1)) q[u] = a.part[(long)(g0 + gt) * nc + c];
+                    if (i < rpb && gt < n) q[u] = a.part[(long)g0 * nc + (long)c * n + gt];
                 }
+            };
+            auto merge_batch = [&](int gt0) {
                 RowState s;
                 rs_init(s);
 #pragma unroll
                 for (int u = 0; u < kDirect; ++u) {
                     const int i = u / nc, c = u - i * nc, gt = gt0 + 256 * i;
                     if (i < rpb && gt < n) {
-                        const bool live = rowf_s[gt] & 1;
+                        const bool live = rowf_s[gt] & 1;   // a locked row's slots are never read
                         if (c == 0) rs_init(s);
                         if (live) rs_merge(s, rs_load(q[u]));
                         if (c == nc - 1) finish_row(gt, s, !live);
                     }
                 }
+            };
+            // the first batch's loads go out with the lock-flag loads
+            load_batch(tid);
+            set_flags();
+            lds_barrier();
+            merge_batch(tid);
+            for (int gt0 = tid + 256 * rpb; gt0 < n; gt0 += 256 * rpb) {
+                load_batch(gt0);
+                merge_batch(gt0);
             }
         } else {
+            set_flags();
+            lds_barrier();
             for (int gt = tid; gt < n; gt += 256) {
                 const bool live = rowf_s[gt] & 1;
                 RowState s;
@@ -386,7 +447,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
                     PostPartial q[kDirect];
 #pragma unroll
                     for (int u = 0; u < kDirect; ++u)
-                        if (c0 + u < nc) q[u] = a.part[(long)(g0 + gt) * nc + c0 + u];
+                        if (c0 + u < nc) q[u] = a.part[(long)g0 * nc + (long)(c0 + u) * n + gt];
 #pragma unroll
                     for (int u = 0; u < kDirect; ++u)
                         if (c0 + u < nc) rs_merge(s, rs_load(q[u]));
@@ -397,7 +458,8 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     }
     for (int r0 = 0; rows_per_round >= n && r0 < n; r0 += rows_per_round) {
         const int nr = min(rows_per_round, n - r0);
-        // Stage: partials of rows [g0+r0, g0+r0+nr) are contiguous.
+        // Stage: the partials of rows [g0+r0, g0+r0+nr) are one contiguous
+        // row-major block (part_index).
         typedef unsigned v4u __attribute__((ext_vector_type(4)));
         const v4u *src = reinterpret_cast<const v4u *>(a.part + (long)(g0 + r0) * a.n_chunks);
         v4u *dst = reinterpret_cast<v4u *>(stage_s);
@@ -529,11 +591,42 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
         }
         return prefix;
     };
+    // The kk-th largest packed value for kk <= kSmallK (block-uniform
+    // call): each wave takes the kk largest of its rows (up to four per
+    // lane) by repeated 64-bit wave maxima (DPP steps), the one lane that
+    // holds a maximum dropping it (the values are distinct; padding is 0,
+    // below any packed value); the global kk largest are among these 4 kk
+    // candidates, and the one with exactly kk - 1 candidates above it is
+    // the answer.  No atomics, three barriers.
+    auto kth_small = [&](int kk) -> unsigned long long {
+        const int lane = tid & 63, wid = tid >> 6;
+        unsigned long long v[4];
+        for (int j = 0; j < 4; ++j) {
+            const int t = wid * 64 + lane + 256 * j;
+            v[j] = t < n ? ord_s[t] : 0ull;
+        }
+        for (int it = 0; it < kk; ++it) {
+            const unsigned long long m = wave_max_u64(max(max(v[0], v[1]), max(v[2], v[3])));
+            for (int j = 0; j < 4; ++j)
+                if (v[j] == m) v[j] = 0ull;
+            if (lane == 0) cand_s[wid * kk + it] = m;    // the 4 kk candidates, packed
+        }
+        lds_barrier();
+        if (tid < 4 * kk) {
+            const unsigned long long mine = cand_s[tid];
+            int above = 0;
+#pragma unroll 8
+            for (int u = 0; u < 4 * kk; ++u) above += cand_s[u] > mine ? 1 : 0;
+            if (above == kk - 1) cand_s[4 * kSmallK] = mine;
+        }
+        lds_barrier();
+        return cand_s[4 * kSmallK];
+    };
     const bool topk = a.mode == 1 || a.mode == 4 || a.mode == 5 || a.mode == 6;
     unsigned long long kth = 0;                 // picked iff eligible and value >= kth
     if (!counted) {
-        if (topk) kth = a.k <= 0 ? ~0ull : a.k >= n ? 0ull : kth_largest(a.k);
-        else if (!any) kth = kth_largest(1);
+        if (topk) kth = a.k <= 0 ? ~0ull : a.k >= n ? 0ull : a.k <= kSmallK ? kth_small(a.k) : kth_largest(a.k);
+        else if (!any) kth = kth_small(1);
     }
     for (int t = tid; t < n; t += 256) {
         int out = -1;
