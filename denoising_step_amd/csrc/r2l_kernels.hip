@@ -21,8 +21,10 @@
 // The recurrence never waits on global memory: the tokens are taken in
 // chunks of LC = 4096/CW (u, delta and x of a chunk are 8 KB each, B and C
 // of its tokens follow), loaded straight into LDS, double-buffered so the
-// next chunk is in flight while this one is scanned out of LDS.  Each
-// chunk's y goes to LDS and is then written out, with x += y, coalesced.
+// next chunk is in flight while this one is scanned out of LDS.  B and C,
+// shared by every channel, are widened to fp32 in LDS once per chunk.
+// Each chunk's y goes to LDS and is then written out, with x += y,
+// coalesced.
 #include "dlm_internal.h"
 
 namespace dlm {
@@ -103,6 +105,8 @@ __global__ __launch_bounds__(kR2LThreads) void r2l_scan_kernel(R2LArgs a)
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][LC * CW];
     __shared__ __attribute__((aligned(16))) uint16_t bs[2][BCE];
     __shared__ __attribute__((aligned(16))) uint16_t cs[2][BCE];
+    __shared__ __attribute__((aligned(16))) float bf32[LC * N];   // the chunk's B and C widened once
+    __shared__ __attribute__((aligned(16))) float cf32[LC * N];
     __shared__ float ys[LC * CW];
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -147,6 +151,18 @@ __global__ __launch_bounds__(kR2LThreads) void r2l_scan_kernel(R2LArgs a)
     }
     const float Dv = a.D[ec];
 
+    // The chunk's B and C rows, shared by every channel of the batch entry,
+    // are widened to fp32 once per chunk (by the whole workgroup) rather
+    // than once per channel; a barrier follows.
+    auto widen_bc = [&](auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        for (int i = tid; i < LC * N; i += kR2LThreads) {
+            bf32[i] = bf(bs[BUF][i]);
+            cf32[i] = bf(cs[BUF][i]);
+        }
+        __syncthreads();
+    };
+
     // Tokens of a chunk in groups of four, last first: the group's inputs
     // are read from LDS and its decays exponentiated up front, so only the
     // state update is serial; the four outputs reduce as independent DPP
@@ -160,8 +176,10 @@ __global__ __launch_bounds__(kR2LThreads) void r2l_scan_kernel(R2LArgs a)
                 const int i = i0 + j;
                 u[j] = bf(us[BUF][i * CW + c]);
                 const float dl = bf(ds[BUF][i * CW + c]);
-                load_bf16s<S>(&bs[BUF][i * N + S * g], Bv[j]);
-                load_bf16s<S>(&cs[BUF][i * N + S * g], Cv[j]);
+                for (int q = 0; q < S; ++q) {
+                    Bv[j][q] = bf32[i * N + S * g + q];
+                    Cv[j][q] = cf32[i * N + S * g + q];
+                }
                 du[j] = dl * u[j];
                 for (int q = 0; q < S; ++q) dA[j][q] = __builtin_amdgcn_exp2f(dl * A2[q]);
             }
@@ -198,6 +216,7 @@ __global__ __launch_bounds__(kR2LThreads) void r2l_scan_kernel(R2LArgs a)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                            // chunk k in LDS; last chunk's writes done
         if (k + 1 < nch) issue(k + 1, 1);
+        widen_bc(std::integral_constant<int, 0>{});
         scan_chunk(std::integral_constant<int, 0>{});
         __syncthreads();
         write_chunk(std::integral_constant<int, 0>{}, k);
@@ -205,6 +224,7 @@ __global__ __launch_bounds__(kR2LThreads) void r2l_scan_kernel(R2LArgs a)
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (k + 2 < nch) issue(k + 2, 0);
+            widen_bc(std::integral_constant<int, 1>{});
             scan_chunk(std::integral_constant<int, 1>{});
             __syncthreads();
             write_chunk(std::integral_constant<int, 1>{}, k + 1);
