@@ -238,16 +238,32 @@ gemm_kernel(GemmArgs a)
         for (int i = 0; i < TI; ++i)
             for (int j = 0; j < TJ; ++j) acc[w][i][j] = f32x16{};
 
+    // The fragments of MFMA step kk + 1 are read before the products of
+    // step kk are issued (two register buffers), so the LDS latency runs
+    // under the MFMAs.
+    constexpr int NRD = TI + NW * TJ;           // fragment reads per MFMA step
     auto compute = [&](const uint16_t *slot) {
-        for (int kk = 0; kk < KK; ++kk) {
-            bf16x8 af[TI], bf[NW][TJ];
-            for (int i = 0; i < TI; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(slot + ard[i][kk]);
+        bf16x8 af[2][TI], bf[2][NW][TJ];
+        auto read = [&](int kk, int p) {
+            for (int i = 0; i < TI; ++i) af[p][i] = *reinterpret_cast<const bf16x8 *>(slot + ard[i][kk]);
             for (int w = 0; w < NW; ++w)
                 for (int j = 0; j < TJ; ++j)
-                    bf[w][j] = *reinterpret_cast<const bf16x8 *>(slot + w * kBN * BK + wrd[j][kk]);
+                    bf[p][w][j] = *reinterpret_cast<const bf16x8 *>(slot + w * kBN * BK + wrd[j][kk]);
+        };
+        read(0, 0);
+        for (int kk = 0; kk < KK; ++kk) {
+            const int p = kk & 1;
+            if (kk + 1 < KK) read(kk + 1, p ^ 1);
             for (int w = 0; w < NW; ++w)
                 for (int i = 0; i < TI; ++i)
-                    for (int j = 0; j < TJ; ++j) acc[w][i][j] = mma(af[i], bf[w][j], acc[w][i][j]);
+                    for (int j = 0; j < TJ; ++j) acc[w][i][j] = mma(af[p][i], bf[p][w][j], acc[w][i][j]);
+        }
+        // order: the first step's reads, then per step the next step's
+        // reads ahead of this step's products
+        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+        for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NW * TI * TJ, 0);
         }
     };
 
