@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KT * D];
     __shared__ int kcode_s[2][KT];
     __shared__ int scode_s[kMaxSlots];
-    __shared__ float ml_s[NG == 2 ? 2 * 4 * 64 : 1];   // key group 1's running max and sum
+    __shared__ float ml_s[NG == 2 ? 4 * 4 * 64 : 1];   // each key group's running max and sum
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6, lane = tid & 63;
@@ -519,35 +519,58 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         if (t0 + KT < k1) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
     }
 
-    if (NG == 2) {
-        // Key group 1 hands its state to group 0 through LDS (the last tile
-        // step ended with a barrier and issued no loads, so the tiles are
-        // free): wave 4 + w writes O in the accumulator layout,
-        // lane-contiguous.
-        constexpr int OW = DT * 16 * 64;                    // floats of O per wave
-        float *ox = reinterpret_cast<float *>(wq < 2 ? Ks0 : Ks1) + (wq & 1) * OW;
-        if (kg == 1) {
-            for (int dt = 0; dt < DT; ++dt)
-                for (int i = 0; i < 16; ++i) ox[(dt * 16 + i) * 64 + lane] = o[dt][i];
-            ml_s[(0 * 4 + wq) * 64 + lane] = m_run;
-            ml_s[(1 * 4 + wq) * 64 + lane] = l_run;
-        }
-        __syncthreads();
-        if (kg == 1) return;
-        const float m1 = ml_s[(0 * 4 + wq) * 64 + lane], l1 = ml_s[(1 * 4 + wq) * 64 + lane];
-        const float m = fmaxf(m_run, m1);
-        // a side whose max is the merged one (also both -inf) keeps scale 1
-        const float a0 = m_run == m ? 1.f : fast_exp2(m_run - m);
-        const float a1 = m1 == m ? 1.f : fast_exp2(m1 - m);
-        for (int dt = 0; dt < DT; ++dt)
-            for (int i = 0; i < 16; ++i) o[dt][i] = fmaf(o[dt][i], a0, ox[(dt * 16 + i) * 64 + lane] * a1);
-        l_run = fmaf(l_run, a0, l1 * a1);
-        m_run = m;
-    }
-    // Epilogue: normalise; write out/lse, or the split partial.
+    // Finish the rows: with two key groups, the groups first merge their
+    // (max, sum, O) through LDS, each then finishing half of every row's
+    // columns -- group KG takes the lane's accumulator elements [KG H,
+    // (KG + 1) H), H = 8 DT (whole groups of four: output column blocks)
+    // and hands its other half to its partner.  Both evaluate the merge in
+    // one operand order (group 0's term first), so their halves agree with
+    // each other bitwise.  (The last tile step ended with a barrier and
+    // issued no loads, so the tiles are free for the exchange.)  Then
+    // normalise and write out/lse, or the split partial.
     const long rows_total = (long)a.B * a.Hq * a.M;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (rv) {
+    constexpr int H = NG == 2 ? DT * 8 : DT * 16;     // elements a group finishes
+    constexpr int Q4 = H / 4;                          // float4 per lane per half
+    // Group KG hands the partner's half of O, and its (max, sum), to LDS.
+    auto give = [&](auto kgc) {
+        constexpr int KG = decltype(kgc)::value;
+        constexpr int G0 = (1 - KG) * H;               // the partner's half
+        float4 *dst = reinterpret_cast<float4 *>(KG == 0 ? Ks1 : Ks0) + wq * Q4 * 64;
+        for (int e4 = 0; e4 < Q4; ++e4) {
+            const int f = G0 + 4 * e4;
+            const f32x16 &od = o[f / 16];
+            dst[e4 * 64 + lane] = float4{od[f % 16], od[f % 16 + 1], od[f % 16 + 2], od[f % 16 + 3]};
+        }
+        ml_s[((KG * 2 + 0) * 4 + wq) * 64 + lane] = m_run;
+        ml_s[((KG * 2 + 1) * 4 + wq) * 64 + lane] = l_run;
+    };
+    auto finish = [&](auto kgc) {
+        constexpr int KG = decltype(kgc)::value;
+        constexpr int E0 = KG * H, E1 = E0 + H;
+        if constexpr (NG == 2) {
+            const float4 *src = reinterpret_cast<const float4 *>(KG == 0 ? Ks0 : Ks1) + wq * Q4 * 64;
+            const float mo = ml_s[(((1 - KG) * 2 + 0) * 4 + wq) * 64 + lane];
+            const float lo = ml_s[(((1 - KG) * 2 + 1) * 4 + wq) * 64 + lane];
+            const float mg0 = KG == 0 ? m_run : mo, mg1 = KG == 0 ? mo : m_run;   // group 0's, group 1's
+            const float lg0 = KG == 0 ? l_run : lo, lg1 = KG == 0 ? lo : l_run;
+            const float m = fmaxf(mg0, mg1);
+            // a side whose max is the merged one (also both -inf) keeps scale 1
+            const float a0 = mg0 == m ? 1.f : fast_exp2(mg0 - m);
+            const float a1 = mg1 == m ? 1.f : fast_exp2(mg1 - m);
+            for (int e4 = 0; e4 < Q4; ++e4) {
+                const float4 t = src[e4 * 64 + lane];
+                const float tv[4] = {t.x, t.y, t.z, t.w};
+                for (int c = 0; c < 4; ++c) {
+                    const int f = E0 + 4 * e4 + c;
+                    const float x = o[f / 16][f % 16];
+                    o[f / 16][f % 16] = KG == 0 ? fmaf(x, a0, tv[c] * a1) : fmaf(tv[c], a0, x * a1);
+                }
+            }
+            l_run = fmaf(lg0, a0, lg1 * a1);
+            m_run = m;
+        }
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (!rv) return;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         const float row_lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
         const long row_flat = (long)(b * a.Hq + h) * a.M + j;
@@ -555,16 +578,18 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
             uint16_t *orow = a.out + row_flat * D;
             for (int dt = 0; dt < DT; ++dt)
                 for (int q4 = 0; q4 < 4; ++q4) {
+                    if (dt * 16 + q4 * 4 < E0 || dt * 16 + q4 * 4 >= E1) continue;
                     __bf16 v4[4];
                     for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[dt][q4 * 4 + c] * inv);
                     *reinterpret_cast<uint2 *>(orow + dt * 32 + q4 * 8 + hh * 4) =
                         *reinterpret_cast<const uint2 *>(v4);
                 }
-            if (hh == 0) a.lse[row_flat] = row_lse;
+            if (KG == 0 && hh == 0) a.lse[row_flat] = row_lse;
         } else {
             float *orow = a.ws_o + ((long)split * rows_total + row_flat) * D;
             for (int dt = 0; dt < DT; ++dt)
                 for (int q4 = 0; q4 < 4; ++q4) {
+                    if (dt * 16 + q4 * 4 < E0 || dt * 16 + q4 * 4 >= E1) continue;
                     float4 v;
                     v.x = o[dt][q4 * 4 + 0] * inv;
                     v.y = o[dt][q4 * 4 + 1] * inv;
@@ -572,9 +597,16 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
                     v.w = o[dt][q4 * 4 + 3] * inv;
                     *reinterpret_cast<float4 *>(orow + dt * 32 + q4 * 8 + hh * 4) = v;
                 }
-            if (hh == 0) a.ws_l[(long)split * rows_total + row_flat] = row_lse;
+            if (KG == 0 && hh == 0) a.ws_l[(long)split * rows_total + row_flat] = row_lse;
         }
+    };
+    if constexpr (NG == 2) {
+        if (kg == 0) give(std::integral_constant<int, 0>{});
+        else give(std::integral_constant<int, 1>{});
+        __syncthreads();
     }
+    if (kg == 0) finish(std::integral_constant<int, 0>{});
+    else if constexpr (NG == 2) finish(std::integral_constant<int, 1>{});
 }
 
 // Merge the key splits of each row in split order:
