@@ -161,9 +161,9 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 //   two key groups (NG = 2): 4 query waves x 2 = 8 waves on 128 rows.
 //     Waves w and w + 4 own the same 32 rows; in each 128-key tile, group 0
 //     takes keys 0-63 and group 1 keys 64-127.  That puts two waves on every
-//     SIMD when the rows alone give one wave per SIMD.  At the end group 1
-//     hands its (max, sum, O) to group 0 through LDS, which merges them and
-//     writes the rows.
+//     SIMD when the rows alone give one wave per SIMD.  At the end the two
+//     groups exchange their (max, sum) and half of O through LDS, and each
+//     merges and writes half of every row's columns.
 //
 // K/V tiles (64 keys per key group) go from global memory straight into
 // LDS (buffer loads with the LDS destination: no registers, no LDS store
