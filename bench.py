@@ -50,10 +50,13 @@ def visible_pairs(a, counted_only=False) -> int:
             qb = (pos - a.prefix_len) // a.block_size
             vis = (kb[None, :] <= qb[:, None])
         else:
+            # int64 throughout: a DUMMY slot's key code must stay above every
+            # group id and the prefix's below (no narrowing to the int32 ids)
             slot = np.clip((n - a.prefix_len) // a.block_size, 0, a.n_slots - 1)
-            kcode = np.where(a.slot_state[b][slot] == 0, np.iinfo(np.int64).max, a.slot_group[b][slot])
-            kcode = np.where(n < a.prefix_len, np.iinfo(np.int64).min, kcode)
-            qc = a.slot_group[b][(pos - a.prefix_len) // a.block_size]
+            grp = a.slot_group[b].astype(np.int64)
+            kcode = np.where(a.slot_state[b][slot] == 0, np.int64(np.iinfo(np.int64).max), grp[slot])
+            kcode = np.where(n < a.prefix_len, np.int64(np.iinfo(np.int64).min), kcode)
+            qc = grp[(pos - a.prefix_len) // a.block_size]
             vis = kcode[None, :] <= qc[:, None]
         tot += int(vis.sum()) * a.Hq
     return tot

@@ -1,0 +1,75 @@
+"""Host-side checks of bench.py (no GPU).
+
+- The one-GPU contract: any --gpus other than 1 exits with a message and
+  status 2 before anything touches a GPU.
+- The algorithmic work bench.py reports (the numerator of the pass-1 and
+  pass-2 rooflines) counts exactly the (query, key) pairs the mask makes
+  visible: checked against the oracle's own visibility predicate pair by
+  pair, for every mask kind, DUMMY slots, row subsets that feed the column
+  sums and several batches with different active sets.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def _brute_pairs(a, counted_only=False):
+    tot = 0
+    for b in range(a.B):
+        for pos in a.active_idx[b]:
+            if counted_only and not (a.cs_lo <= pos < a.cs_hi):
+                continue
+            tot += sum(oracle.visible(a, b, int(pos), n) for n in range(a.kv_len))
+    return tot * a.Hq
+
+
+def _case(kind, slots, groups, act_blocks, B=2, P=40, block=8, cs=None):
+    """kind with n_slots slot states ``slots`` and groups ``groups`` (per
+    batch rows); active rows: the positions of the slots in act_blocks[b]."""
+    n_slots = slots.shape[1]
+    kv_len = P + n_slots * block
+    act = [np.concatenate([np.arange(P + s * block, P + (s + 1) * block) for s in act_blocks[b]])
+           for b in range(B)]
+    m = max(len(x) for x in act)
+    assert all(len(x) == m for x in act)
+    lo, hi = cs if cs is not None else (0, kv_len)
+    return W.make_attn("bench_pairs", B=B, Hq=3, Hkv=1, D=32, kv_len=kv_len, prefix_len=P,
+                       active_idx=np.stack(act).astype(np.int32), kind=kind, block_size=block,
+                       n_slots=n_slots, slot_state=slots, slot_group=groups, cs_lo=lo, cs_hi=hi)
+
+
+CASES = {
+    "full": lambda: W.tiny().attn,
+    "block_causal": lambda: _case(W.MASK_BLOCK_CAUSAL,
+                                  np.full((2, 4), W.SLOT_ACTIVE, np.uint8),
+                                  np.zeros((2, 4), np.int32), [[0, 1, 3], [1, 2, 3]],
+                                  cs=(48, 72)),
+    "group_dummy": lambda: _case(W.MASK_GROUP,
+                                 np.array([[1, 1, 1, 0], [1, 0, 1, 1]], np.uint8),
+                                 np.array([[0, 0, 1, 0], [2, 0, 1, 2]], np.int32),
+                                 [[0, 1, 2], [0, 2, 3]], cs=(40, 64)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("counted_only", [False, True])
+def test_visible_pairs_match_the_oracle_mask(name, counted_only):
+    a = CASES[name]()
+    assert bench.visible_pairs(a, counted_only=counted_only) == _brute_pairs(a, counted_only)
