@@ -73,3 +73,22 @@ CASES = {
 def test_visible_pairs_match_the_oracle_mask(name, counted_only):
     a = CASES[name]()
     assert bench.visible_pairs(a, counted_only=counted_only) == _brute_pairs(a, counted_only)
+
+
+def test_stored_traffic_is_dropped_when_the_pass1_sources_change(tmp_path, monkeypatch):
+    """roofline.traffic comes from a committed counter summary only while the
+    digest of the pass-1 sources it records matches the sources."""
+    for rel in bench.TRAFFIC_SOURCES:
+        f = tmp_path / rel
+        f.parent.mkdir(parents=True, exist_ok=True)
+        f.write_text("source " + rel + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    summary = tmp_path / "profiles" / "attn_fwd_w_hbm_traffic.md"
+    summary.write_text("# counters\n\n- kernel: `k`\n- workload: `w`\n"
+                       f"- source_sha256: `{bench.source_digest()}`\n"
+                       "- traffic_bytes_per_launch: 12345\n")
+    assert bench.stored_traffic("w") == 12345
+    assert bench.stored_traffic("other") is None           # no summary for it
+    (tmp_path / bench.TRAFFIC_SOURCES[0]).write_text("changed\n")
+    assert bench.stored_traffic("w") is None                # kernel changed since
