@@ -611,34 +611,57 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
 
 // Merge the key splits of each row in split order:
 // lse = logsumexp_s lse_s, out = sum_s exp(lse_s - lse) out_s.
-// One thread per 4 consecutive output elements of a row.
+// One thread per 4 consecutive output elements of a row.  The lse and the
+// partial outputs of the first kCombineBatch splits are loaded together
+// into registers (one round trip); any further splits are read as they are
+// used.  The arithmetic runs in split order either way.
+constexpr int kCombineBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 {
     constexpr int PER_ROW = D / 4;
     constexpr int RPB = 256 / PER_ROW;  // rows per block
+    constexpr int NB = kCombineBatch;
     const long rows_total = (long)a.B * a.Hq * a.M;
     const long row = (long)blockIdx.x * RPB + threadIdx.x / PER_ROW;
     const int d4 = threadIdx.x % PER_ROW;
     if (row >= rows_total) return;
     if (a.m_valid && (int)(row % a.M) >= valid_rows(a, (int)(row / ((long)a.Hq * a.M)))) return;
+    const int ns = a.n_split;
     const float *ls = a.ws_l + row;
+    const float4 *os = reinterpret_cast<const float4 *>(a.ws_o + row * D) + d4;
+    const long ostride = rows_total * PER_ROW;     // float4 between splits
+    float lv[NB];
+    float4 ov[NB];
+    for (int s = 0; s < NB; ++s) {
+        if (s < ns) {
+            lv[s] = ls[s * rows_total];
+            ov[s] = os[s * ostride];
+        }
+    }
     float m = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) m = fmaxf(m, ls[s * rows_total]);
+    for (int s = 0; s < NB; ++s)
+        if (s < ns) m = fmaxf(m, lv[s]);
+    for (int s = NB; s < ns; ++s) m = fmaxf(m, ls[s * rows_total]);
     float4 res = {0.f, 0.f, 0.f, 0.f};
     float L = -INFINITY;
     if (m != -INFINITY) {
         float sum = 0.f;
-        for (int s = 0; s < a.n_split; ++s) sum += fast_exp2((ls[s * rows_total] - m) * kLog2e);
+        for (int s = 0; s < NB; ++s)
+            if (s < ns) sum += fast_exp2((lv[s] - m) * kLog2e);
+        for (int s = NB; s < ns; ++s) sum += fast_exp2((ls[s * rows_total] - m) * kLog2e);
         L = m + logf(sum);
-        for (int s = 0; s < a.n_split; ++s) {
-            const float w = fast_exp2((ls[s * rows_total] - L) * kLog2e);
-            const float4 v = reinterpret_cast<const float4 *>(a.ws_o + (s * rows_total + row) * D)[d4];
+        auto add = [&](float l, const float4 &v) {
+            const float w = fast_exp2((l - L) * kLog2e);
             res.x = fmaf(w, v.x, res.x);
             res.y = fmaf(w, v.y, res.y);
             res.z = fmaf(w, v.z, res.z);
             res.w = fmaf(w, v.w, res.w);
-        }
+        };
+        for (int s = 0; s < NB; ++s)
+            if (s < ns) add(lv[s], ov[s]);
+        for (int s = NB; s < ns; ++s) add(ls[s * rows_total], os[s * ostride]);
     }
     __bf16 bv[4] = {(__bf16)res.x, (__bf16)res.y, (__bf16)res.z, (__bf16)res.w};
     reinterpret_cast<uint2 *>(a.out + row * D)[d4] = *reinterpret_cast<const uint2 *>(bv);
