@@ -73,18 +73,8 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
 //   BLOCK_CAUSAL:  prefix INT_MIN; block index; query code = its block.
 //   GROUP:         prefix INT_MIN; group id of the slot (INT_MAX if the slot is
 //                  DUMMY); query code = group id of its slot.
-// Keys at or beyond kv_len are INT_MAX.
-__device__ __forceinline__ int key_code(const AttnArgs &a, const uint8_t *st, const int32_t *gr,
-                                        int n)
-{
-    if (n >= a.kv_len) return INT_MAX;
-    if (a.kind == 0 || n < a.P) return INT_MIN;
-    int s = (n - a.P) / a.bs;
-    if (a.kind == 1) return s;
-    if (s >= a.n_slots || st[s] == 0) return INT_MAX;
-    return gr[s];
-}
-
+// Keys at or beyond kv_len are INT_MAX.  Both passes evaluate the key code
+// from a slot table staged in LDS.
 __device__ __forceinline__ int query_code(const AttnArgs &a, const int32_t *gr, int pos)
 {
     if (a.kind == 0) return 0;
@@ -693,6 +683,7 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     __shared__ int qcode_s[2][kCsRows];
     __shared__ int range_s[2];
     __shared__ int grp_s[kMaxSlots];               // GROUP: slot -> group id
+    __shared__ int kcs_s[kMaxSlots];               // GROUP: slot -> key code (INT_MAX: DUMMY)
 
     const int tid = threadIdx.x;
     const int wid = tid >> 6, lane = tid & 63;
@@ -710,7 +701,12 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     const int32_t *gr = a.kind == 2 ? a.slot_group + (long)b * a.n_slots : nullptr;
     const int32_t *act = a.active_idx + (long)b * a.M;
     if (a.kind == 2)
-        for (int sl = tid; sl < a.n_slots; sl += 256) grp_s[sl] = gr[sl];
+        for (int sl = tid; sl < a.n_slots; sl += 256) {
+            const int gv = gr[sl];
+            const bool dummy = st[sl] == 0;
+            grp_s[sl] = gv;
+            kcs_s[sl] = dummy ? INT_MAX : gv;
+        }
 
     // Counted rows: active rows whose position lies in [cs_lo, cs_hi);
     // active_idx is ascending, so they are the index range [j_lo, j_hi).
@@ -744,7 +740,6 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * D * 2);
     for (int ct = 0; ct < 2; ++ct) {
         key[ct] = kb * kCsKeys + wid * 64 + ct * 32 + l32;
-        kc[ct] = key_code(a, st, gr, key[ct]);
         for (int kk = 0; kk < DK; ++kk) {
             const uint4 v = buffer_load16(krs, (key[ct] * D + kk * 16 + hh * 8) * 2);
             kf[ct][kk] = *reinterpret_cast<const bf16x8 *>(&v);
@@ -752,6 +747,18 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     }
     const bool need_mask = a.kind != 0 && (kb + 1) * kCsKeys > a.P;
     __syncthreads();
+    // the key codes from the slot table staged in LDS (no dependent global
+    // loads between the K fragment loads)
+    for (int ct = 0; ct < 2; ++ct) {
+        const int n = key[ct];
+        int c = INT_MIN;
+        if (n >= a.kv_len) c = INT_MAX;
+        else if (a.kind != 0 && n >= a.P) {
+            const int sl = (n - a.P) / a.bs;
+            c = a.kind == 1 ? sl : (sl < a.n_slots ? kcs_s[sl] : INT_MAX);
+        }
+        kc[ct] = c;
+    }
     const int j_lo = range_s[0], j_hi = range_s[1];
     const int cnt = max(0, j_hi - j_lo);
     const int per = ((cnt + a.n_rsplit - 1) / a.n_rsplit + kCsRows - 1) / kCsRows * kCsRows;
