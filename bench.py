@@ -7,13 +7,19 @@ posterior / KL lock test / unmask selection, through the two C-ABI calls
 on one stream.  The same step with dlm_posterior on a second stream (its
 selection waiting for the column sums through select.score_ready) is
 reported for reference ("ms_per_step_two_streams").
-Inputs are resident in HBM before timing starts; the timed steps rotate over
-enough copies of the inputs that they cannot be served from the 256 MB
-Infinity Cache.  The lock flags are in/out, so every call gets its own copy
-of the entry flags, made before timing: every step does the same work.
+Inputs are resident in HBM before timing starts.  Each timed loop (the
+whole step, pass 1 alone, both attention passes, the posterior alone)
+rotates over enough copies of its inputs that the bytes it touches total at
+least twice the 256 MB Infinity Cache.  The lock flags are in/out, so every
+call gets its own copy of the entry flags, made before timing: every step
+does the same work.
 
-Prints ONE JSON line.  Default workload: the LLaDA-8B-like bidirectional
-layer (B=1, 32 heads x 128, N=1024 all active; posterior 32 x 126464).
+Prints ONE JSON line.  Headline workload: the SureLock sparse-query step
+(B=4, 32 heads x 128, N=8192 with 2048 active rows per batch entry;
+posterior 8192 x 126464), the largest single-GPU configuration.  The other
+three workloads (LLaDA-like bidirectional layer, multi-block group mask,
+long-prefix Attn-Sampler) are timed the same way and reported under
+"workloads" in the same line.
 """
 from __future__ import annotations
 
@@ -62,41 +68,117 @@ def visible_pairs(a, counted_only=False) -> int:
     return tot
 
 
-# Sources whose change invalidates a stored counter measurement of pass 1.
-TRAFFIC_SOURCES = ("denoising_step_amd/csrc/attn_kernels.hip", "denoising_step_amd/csrc/dlm_internal.h",
-                   "denoising_step_amd/build.py")
+# Sources whose change invalidates a stored counter measurement, per kernel
+# tag (the summaries under profiles/ record a SHA-256 of these).
+COUNTER_SOURCES = {
+    "attn_fwd": ("denoising_step_amd/csrc/attn_kernels.hip", "denoising_step_amd/csrc/dlm_internal.h",
+                 "denoising_step_amd/build.py"),
+    "colsum": ("denoising_step_amd/csrc/attn_kernels.hip", "denoising_step_amd/csrc/dlm_internal.h",
+               "denoising_step_amd/build.py"),
+    "posterior": ("denoising_step_amd/csrc/posterior_kernels.hip", "denoising_step_amd/csrc/dlm_internal.h",
+                  "denoising_step_amd/build.py"),
+}
+TRAFFIC_SOURCES = COUNTER_SOURCES["attn_fwd"]
 
 
-def source_digest() -> str:
+def source_digest(tag: str = "attn_fwd") -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in COUNTER_SOURCES[tag]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def _summary_fields(path: str) -> dict:
+    """The machine-read "- key: value" lines of a profiles/ summary."""
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return {}
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    return fields
 
 
 def stored_traffic(workload: str):
     """HBM bytes per pass-1 launch from the committed counter summary
     (profiles/attn_fwd_<workload>_hbm_traffic.md), or None when there is
     none or the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.md")
-    try:
-        with open(path) as f:
-            text = f.read()
-    except OSError:
-        return None
-    fields = {}
-    for line in text.splitlines():
-        if line.startswith("- ") and ":" in line:
-            k, v = line[2:].split(":", 1)
-            fields[k.strip()] = v.strip().strip("`")
-    if fields.get("source_sha256") != source_digest():
+    fields = _summary_fields(os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.md"))
+    if fields.get("source_sha256") != source_digest("attn_fwd"):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def stored_counters(tag: str, workload: str):
+    """Per-launch counter figures of kernel `tag` on `workload` from the
+    committed summary profiles/<tag>_<workload>_counters.md (numeric
+    fields only), or None when there is none or the kernel sources changed
+    since the counters were taken."""
+    fields = _summary_fields(os.path.join(ROOT, "profiles", f"{tag}_{workload}_counters.md"))
+    if not fields or fields.get("source_sha256") != source_digest(tag):
+        return None
+    out = {}
+    for k, v in fields.items():
+        try:
+            out[k] = int(v)
+        except ValueError:
+            try:
+                out[k] = float(v)
+            except ValueError:
+                pass
+    out["summary"] = f"profiles/{tag}_{workload}_counters.md"
+    return out
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(path: str) -> str:
+    """Markdown table of a rocprofv3 kernel_trace.csv: per kernel, the
+    dispatch count and the mean, median, min and max duration in us."""
+    import statistics
+    by = {}
+    for r in _read_csv(path):
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        by.setdefault(r["Kernel_Name"], []).append(d)
+    lines = ["| kernel | calls | mean us | median us | min us | max us | total us |",
+             "|---|---|---|---|---|---|---|"]
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v)} | {statistics.fmean(v):.2f} | {statistics.median(v):.2f} | "
+                     f"{min(v):.2f} | {max(v):.2f} | {sum(v):.1f} |")
+    return "\n".join(lines)
+
+
+def summarize_pmc(path: str) -> str:
+    """Markdown table of a rocprofv3 counter_collection.csv: per kernel and
+    counter, the per-dispatch value (summed over the counter's instances)
+    as mean, median, min and max over the dispatches."""
+    import statistics
+    per = {}
+    for r in _read_csv(path):
+        key = (r["Kernel_Name"], r["Counter_Name"], r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by = {}
+    for (k, c, _), v in per.items():
+        by.setdefault((k, c), []).append(v)
+    lines = ["| kernel | counter | dispatches | mean | median | min | max |",
+             "|---|---|---|---|---|---|---|"]
+    for (k, c), v in sorted(by.items()):
+        lines.append(f"| `{k}` | {c} | {len(v)} | {statistics.fmean(v):.6g} | {statistics.median(v):.6g} | "
+                     f"{min(v):.6g} | {max(v):.6g} |")
+    return "\n".join(lines)
 
 
 def copy_probe(n_bytes: int = 256 << 20, reps: int = 5):
@@ -134,10 +216,11 @@ def time_loop(fn, n_sets, steps, warmup, per_step=False):
     return mean, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
-def cpu_baseline(w, budget_heads=None):
+def cpu_baseline(w, budget_heads=None, budget_rows=512):
     """Time the oracle, as it stands, on a bounded sample of the workload and
-    scale to the metric's unit (rows/s of a whole step)."""
-    import numpy as np
+    scale to the metric's unit (rows/s of a whole step): attention and
+    column sums on a few whole GQA groups of q-heads (the per-head work is
+    identical across heads), the posterior on the first rows."""
     import oracle
     from workloads import AttnCase
     a, p = w.attn, w.post
@@ -151,17 +234,22 @@ def cpu_baseline(w, budget_heads=None):
     kv = oracle.effective_kv(sub)
     _, lse = oracle.attention(sub, kv=kv)
     oracle.colsum(sub, lse, kv=kv)
-    t_attn = (time.perf_counter() - t0) * (a.Hq / H)
-    rows = min(p.R, 64)
+    t_attn_sample = time.perf_counter() - t0
+    t_attn = t_attn_sample * (a.Hq / H)
+    rows = min(p.R, budget_rows)
     t0 = time.perf_counter()
-    post = oracle.posterior(p.logits[:rows], p.prev[:rows], p.locked[:rows], p.eps)
-    t_post = (time.perf_counter() - t0) * (p.R / rows)
+    oracle.posterior(p.logits[:rows], p.prev[:rows], p.locked[:rows], p.eps)
+    t_post_sample = time.perf_counter() - t0
+    t_post = t_post_sample * (p.R / rows)
     t_step = t_attn + t_post
-    return {"value": a.B * a.M / t_step, "unit": "rows/s", "cores": oracle.num_threads(),
+    threads = oracle.num_threads()
+    return {"value": a.B * a.M / t_step, "unit": "rows/s", "cores": threads,
             "kind": "oracle",
             "sample": f"attention + column sums on {H} of {a.Hq} q-heads (scaled x{a.Hq / H:g}), "
                       f"posterior on {rows} of {p.R} rows (scaled x{p.R / rows:g}); "
-                      f"step time {t_step:.3f} s",
+                      f"{t_attn_sample + t_post_sample:.1f} s of CPU wall time sampled, "
+                      f"estimated step time {t_step:.2f} s",
+            "omp_threads": threads, "affinity_cpus": len(os.sched_getaffinity(0)),
             "cpu_model": _cpu_model()}
 
 
@@ -404,16 +492,179 @@ def r2l_bench(args):
     print(json.dumps(line), flush=True)
 
 
+HEADLINE = "surelock_sparse"
+EXTRAS = ("llada_bidirectional", "mbd_multiblock", "long_prefix_sampler")
+ATTN_TARGET, POST_TARGET = 0.5, 0.7
+LOOPS = ("step", "step_two_streams", "pass1", "passes12", "posterior")
+
+
+def _nbytes(*ts) -> int:
+    return sum(t.numel() * t.element_size() for t in ts if t is not None)
+
+
+def loop_footprints(ds) -> dict:
+    """Bytes of device memory one timed call of each loop touches in one
+    input set (what rotation must keep out of the 256 MB MALL)."""
+    attn_ws = _nbytes(ds.attn_ws)
+    pass1 = _nbytes(ds.q, ds.cache_k, ds.cache_v, ds.out, ds.lse)
+    post = _nbytes(ds.logits, ds.prev, ds.locked, ds.sel, ds.kl, ds.conf, ds.post_ws)
+    step = pass1 + _nbytes(ds.k, ds.v, ds.colsum) + attn_ws + post
+    return {"step": step, "step_two_streams": step, "pass1": pass1,
+            "passes12": pass1 + _nbytes(ds.colsum) + attn_ws, "posterior": post}
+
+
+def measure_workload(name, args, loops=LOOPS, with_cpu=False, spread=True):
+    """Time the loops of one workload; returns the per-workload record."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import denoising_step_amd as dlm
+    from denoising_step_amd.runner import DeviceStep
+
+    w = W.get(name, seed=args.seed)
+    a, p = w.attn, w.post
+    print(f"bench: {name}: {w.description}", file=sys.stderr, flush=True)
+    first = DeviceStep(w)
+    fp = loop_footprints(first)
+    # every timed loop cycles >= 2x the MALL with the bytes that loop touches
+    need = {k: max(1, math.ceil(2 * MALL_BYTES / fp[k])) for k in loops}
+    n_sets = max(need.values())
+    sets = [first] + [DeviceStep(w) for _ in range(n_sets - 1)]
+    stream = torch.cuda.current_stream()
+    # one fresh copy of the entry lock flags per call, made before timing
+    # (the flags are in/out; every timed call must see the same entry state)
+    n_calls = (args.steps + args.warmup) * (len(loops) + (1 if spread else 0))
+    lock_bufs = [sets[i % n_sets].locked0.clone() for i in range(n_calls)]
+    calls = [0]
+
+    def fresh_lock():
+        calls[0] += 1
+        return lock_bufs[(calls[0] - 1) % len(lock_bufs)]
+
+    def step(i):
+        sets[i].run(stream, locked=fresh_lock())
+
+    def step_two_streams(i):
+        sets[i].run(stream, locked=fresh_lock(), overlap=True)
+
+    def pass1(i):              # no fresh K/V (already in the cache), no column sums
+        ds = sets[i]
+        dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, None, stream)
+
+    def passes12(i):           # both attention passes, no fresh K/V
+        ds = sets[i]
+        dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, ds.colsum, stream)
+
+    def posterior(i):
+        sets[i].run_posterior(stream, locked=fresh_lock())
+
+    fns = {"step": step, "step_two_streams": step_two_streams, "pass1": pass1,
+           "passes12": passes12, "posterior": posterior}
+    ms = {}
+    for k in loops:
+        ms[k] = time_loop(fns[k], n_sets, args.steps, args.warmup)
+        print(f"bench: {name}: {k}: {ms[k] * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+
+    pairs = visible_pairs(a)
+    alg_flops = 4.0 * a.D * pairs                       # QK^T and PV, 2 flops per MAC
+    cs_flops = 2.0 * a.D * visible_pairs(a, counted_only=True)   # pass 2 recomputes QK^T
+    unlocked = int((p.locked == 0).sum())
+    post_bytes = 8.0 * unlocked * p.V
+    rec = {"config": {"workload": name, "B": a.B, "Hq": a.Hq, "Hkv": a.Hkv, "D": a.D,
+                      "kv_len": a.kv_len, "active_rows": a.M, "posterior_rows": p.R, "vocab": p.V,
+                      "mask": ["full", "block_causal", "group"][a.kind], "selection": p.mode},
+           "rows_per_step": a.B * a.M,
+           "timing": {"n_sets": n_sets, "warmup": args.warmup, "steps": args.steps,
+                      "loops": {k: {"footprint_mb_per_set": round(fp[k] / 2**20, 1),
+                                    "mb_cycled": round(n_sets * fp[k] / 2**20, 1),
+                                    "mall_multiple": round(n_sets * fp[k] / MALL_BYTES, 2)}
+                                for k in loops}}}
+    if "step" in ms:
+        rec["ms_per_step"] = ms["step"]
+        rec["rows_per_s"] = a.B * a.M / (ms["step"] * 1e-3)
+        if spread:
+            # single-step spread from its own loop: an event after every step
+            # adds a small gap, so ms_per_step comes from the loop without
+            _, step_ms = time_loop(step, n_sets, args.steps, 0, per_step=True)
+            rec["step_ms_p10_p50_p90"] = [float(x) for x in np.percentile(np.array(step_ms), [10, 50, 90])]
+    if "step_two_streams" in ms:
+        rec["ms_per_step_two_streams"] = ms["step_two_streams"]
+    if "pass1" in ms:
+        t = alg_flops / (ms["pass1"] * 1e-3) / 1e12
+        rec["attention_pass1"] = {
+            "bound": "mfma",
+            "kernel": "attention pass 1 (sparse-query flash attention; with the key-split merge "
+                      "when the launch plan splits keys)",
+            "achieved": t, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": t / PEAK_BF16_TFLOPS,
+            "target": ATTN_TARGET, "target_met": t / PEAK_BF16_TFLOPS >= ATTN_TARGET,
+            "per_launch_flops": alg_flops, "avg_launch_us": ms["pass1"] * 1e3,
+            "traffic": stored_traffic(name),
+            "counters": stored_counters("attn_fwd", name)}
+    if "passes12" in ms:
+        t = (alg_flops + cs_flops) / (ms["passes12"] * 1e-3) / 1e12
+        rec["attention_passes_1_2"] = {
+            "achieved": t, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": t / PEAK_BF16_TFLOPS,
+            "target": ATTN_TARGET, "target_met": t / PEAK_BF16_TFLOPS >= ATTN_TARGET,
+            "flops": alg_flops + cs_flops, "avg_call_us": ms["passes12"] * 1e3,
+            "counters": stored_counters("colsum", name)}
+    if "posterior" in ms:
+        g = post_bytes / (ms["posterior"] * 1e-3) / 1e9
+        rec["posterior_roofline"] = {
+            "bound": "hbm", "achieved": g, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": g / PEAK_HBM_GBS,
+            "target": POST_TARGET, "target_met": g / PEAK_HBM_GBS >= POST_TARGET,
+            "per_launch_bytes": post_bytes, "avg_launch_us": ms["posterior"] * 1e3,
+            "counters": stored_counters("posterior", name)}
+    # executed MFMA FLOPs per launch (profiler counter) over the live time
+    for key, ms_key in (("attention_pass1", "pass1"), ("attention_passes_1_2", "passes12")):
+        c = (rec.get(key) or {}).get("counters")
+        if c and "executed_mfma_flops_per_launch" in c:
+            t = c["executed_mfma_flops_per_launch"] / (ms[ms_key] * 1e-3) / 1e12
+            rec[key]["executed_tflops"] = t
+            rec[key]["executed_frac"] = t / PEAK_BF16_TFLOPS
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    del sets, lock_bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def dominant_roofline(rec) -> dict:
+    """The roofline object of the kernel that takes the largest share of
+    the step: attention pass 1 or the posterior stream (their own loops)."""
+    p1, po = rec["attention_pass1"], rec["posterior_roofline"]
+    if po["avg_launch_us"] > p1["avg_launch_us"]:
+        r = {k: po[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+        r.update(kernel="posterior stream (KL, confidence, lock) + selection",
+                 per_launch_bytes=po["per_launch_bytes"], avg_launch_us=po["avg_launch_us"],
+                 traffic=(po.get("counters") or {}).get("traffic_bytes_per_launch"),
+                 counters=po.get("counters"))
+    else:
+        r = {k: p1[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel", "per_launch_flops",
+                                "avg_launch_us", "traffic", "counters")}
+    r["chosen_as"] = "largest single-kernel share of the step time, from the loops below"
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llada_bidirectional")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the headline workload only (no per-workload extras)")
+    ap.add_argument("--only", choices=LOOPS,
+                    help="run only this loop on --config (profiler runs) and print its record")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="summarise a rocprofv3 kernel_trace.csv (per-kernel mean / median) and exit")
+    ap.add_argument("--summarize-pmc", metavar="CSV",
+                    help="summarise a rocprofv3 counter_collection.csv (per kernel and counter) and exit")
     ap.add_argument("--loop", action="store_true",
                     help="time a whole multi-step SureLock run instead (its own JSON line)")
     ap.add_argument("--layer", action="store_true",
@@ -425,6 +676,12 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design, not a build", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.copy_probe:
         copy_probe()
         return
@@ -438,117 +695,51 @@ def main():
         r2l_bench(args)
         return
 
-    import numpy as np
     import torch
-
-    import workloads as W
-    import denoising_step_amd as dlm
-    from denoising_step_amd.runner import DeviceStep
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    w = W.get(args.config, seed=args.seed)
-    a, p = w.attn, w.post
-    print(f"bench: {args.config}: {w.description}", file=sys.stderr, flush=True)
+    if args.only:
+        rec = measure_workload(args.config, args, loops=(args.only,), spread=False)
+        print(json.dumps(rec), flush=True)
+        return
 
-    first = DeviceStep(w)
-    foot = sum(t.numel() * t.element_size() for t in
-               (first.q, first.k, first.v, first.cache_k, first.cache_v, first.logits, first.prev))
-    n_sets = max(1, math.ceil(2 * MALL_BYTES / foot))
-    sets = [first] + [DeviceStep(w) for _ in range(n_sets - 1)]
-    stream = torch.cuda.current_stream()
-    # One fresh copy of the entry lock flags per call, made before timing
-    # (the flags are in/out; every timed step must see the same entry state).
-    n_calls = args.steps + args.warmup
-    lock_bufs = [sets[i % n_sets].locked0.clone() for i in range(5 * n_calls)]
-    calls = [0]
-
-    def fresh_lock():
-        calls[0] += 1
-        return lock_bufs[calls[0] - 1]
-
-    # A step: both C-ABI calls on the timed stream.
-    def step(i):
-        sets[i].run(stream, locked=fresh_lock())
-
-    ms_step = time_loop(step, n_sets, args.steps, args.warmup)
-
-    # The same step with dlm_posterior on a second stream (its selection
-    # waiting for the column sums through select.score_ready), for reference:
-    # the cross-stream waits cost more than the overlap gains here.
-    def step_two_streams(i):
-        sets[i].run(stream, locked=fresh_lock(), overlap=True)
-
-    ms_step_2s = time_loop(step_two_streams, n_sets, args.steps, args.warmup)
-    # the spread of single steps, from a separate loop: an event after every
-    # step adds a small gap, so the figure above comes from a loop without them
-    _, step_ms = time_loop(step, n_sets, args.steps, 0, per_step=True)
-
-    # pass 1 alone: no fresh K/V (already in the cache), no column sums
-    def pass1(i):
-        ds = sets[i]
-        dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, None, stream)
-
-    ms_pass1 = time_loop(pass1, n_sets, args.steps, args.warmup)
-
-    # both attention passes (no fresh K/V): the attention MFMA figure
-    def passes12(i):
-        ds = sets[i]
-        dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, ds.colsum, stream)
-
-    ms_p12 = time_loop(passes12, n_sets, args.steps, args.warmup)
-
-    def posterior(i):
-        sets[i].run_posterior(stream, locked=fresh_lock())
-
-    ms_post = time_loop(posterior, n_sets, args.steps, args.warmup)
-
-    pairs = visible_pairs(a)
-    alg_flops = 4.0 * a.D * pairs                       # QK^T and PV, 2 flops per MAC
-    achieved_tflops = alg_flops / (ms_pass1 * 1e-3) / 1e12
-    cs_flops = 2.0 * a.D * visible_pairs(a, counted_only=True)   # pass 2 recomputes QK^T
-    p12_tflops = (alg_flops + cs_flops) / (ms_p12 * 1e-3) / 1e12
-    q = np.percentile(np.array(step_ms), [10, 50, 90])
-    unlocked = int((p.locked == 0).sum())
-    post_bytes = 8.0 * unlocked * p.V
-    post_gbs = post_bytes / (ms_post * 1e-3) / 1e9
-    plan = {"n_sets": n_sets, "footprint_mb_per_set": round(foot / 2**20, 1)}
-
-    rows = a.B * a.M
+    head = measure_workload(args.config, args, with_cpu=not args.no_cpu_baseline)
     res = {
         "metric": "active query-rows/s per denoising step",
-        "value": rows / (ms_step * 1e-3),
+        "value": head["rows_per_s"],
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the pages' workloads, no trained weights)",
-        "config": {"workload": args.config, "B": a.B, "Hq": a.Hq, "Hkv": a.Hkv, "D": a.D,
-                   "kv_len": a.kv_len, "active_rows": a.M, "posterior_rows": p.R, "vocab": p.V,
-                   "mask": ["full", "block_causal", "group"][a.kind], "selection": p.mode},
-        "roofline": {"bound": "mfma", "kernel": "attention pass 1 (sparse-query flash attention)",
-                     "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": stored_traffic(args.config),
-                     "per_launch_flops": alg_flops, "avg_launch_us": ms_pass1 * 1e3},
-        "step_ms_p10_p50_p90": [float(x) for x in q],
-        "ms_per_step_two_streams": ms_step_2s,
-        "attention_passes_1_2": {"achieved": p12_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": p12_tflops / PEAK_BF16_TFLOPS, "flops": alg_flops + cs_flops,
-                                 "avg_call_us": ms_p12 * 1e3},
-        "posterior_roofline": {"bound": "hbm", "achieved": post_gbs, "peak": PEAK_HBM_GBS,
-                               "unit": "GB/s", "frac": post_gbs / PEAK_HBM_GBS,
-                               "per_launch_bytes": post_bytes, "avg_launch_us": ms_post * 1e3},
-        "timing": plan,
+        "config": head["config"],
+        "roofline": dominant_roofline(head),
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w)
+    for k in ("attention_pass1", "attention_passes_1_2", "posterior_roofline", "step_ms_p10_p50_p90",
+              "ms_per_step_two_streams", "timing"):
+        res[k] = head[k]
+    if "cpu_baseline" in head:
+        res["cpu_baseline"] = head["cpu_baseline"]
+    if not args.no_extras:
+        res["workloads"] = {}
+        for name in EXTRAS:
+            if name == args.config:
+                continue
+            rec = measure_workload(name, args)
+            res["workloads"][name] = {
+                "config": rec["config"], "rows_per_s": rec["rows_per_s"], "ms_per_step": rec["ms_per_step"],
+                "step_ms_p10_p50_p90": rec["step_ms_p10_p50_p90"],
+                "ms_per_step_two_streams": rec["ms_per_step_two_streams"],
+                "attention_pass1": rec["attention_pass1"], "attention_passes_1_2": rec["attention_passes_1_2"],
+                "posterior_roofline": rec["posterior_roofline"], "timing": rec["timing"]}
     print(json.dumps(res), flush=True)
 
 

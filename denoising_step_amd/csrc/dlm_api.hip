@@ -4,6 +4,7 @@
 #include "dlm_step.h"
 #include "dlm_internal.h"
 
+#include <limits.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -54,6 +55,11 @@ int check_attn_scalars(const dlm_kv_cache *kc, const dlm_mask_desc *md)
     if ((long)kc->B * md->Hq * md->M > (1L << 31) - 1 ||
         (long)kc->B * kc->Hkv * kc->n_cap > (1L << 31) - 1)
         return fail(DLM_E_SHAPE, "problem too large for 32-bit row indices");
+    // the kernels address one (batch, head) slice of q / K / V through
+    // 32-bit byte offsets and buffer views of kv_len * D * 2 bytes
+    if ((long)md->kv_len * kc->D * 2 > (long)INT_MAX - 4096)
+        return fail(DLM_E_SHAPE, "kv_len=%d x D=%d bf16 is past the 2 GiB per (batch, head) slice the "
+                    "kernels address with 32-bit offsets", md->kv_len, kc->D);
     if (md->kind < DLM_MASK_FULL || md->kind > DLM_MASK_GROUP)
         return fail(DLM_E_DESC, "unknown mask kind %d", md->kind);
     if (md->kind != DLM_MASK_FULL && md->block_size < 1)

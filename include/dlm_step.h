@@ -159,7 +159,9 @@ typedef struct {
  *   lse        fp32 [B, Hq, M]          natural-log log-sum-exp of each row
  *   colsum     fp32 [B, kv_len] or [B, Hq, kv_len], or NULL
  *   stream     HIP stream all work is enqueued on
- * Supported: D in {32, 64, 128}; Hq % Hkv == 0.
+ * Supported: D in {32, 64, 128}; Hq % Hkv == 0; kv_len * D * 2 bytes
+ * (one (batch, head) slice of K or V) below 2 GiB - 4 KiB, since the
+ * kernels address a slice with 32-bit byte offsets (DLM_E_SHAPE otherwise).
  * Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED, DLM_E_DESC,
  *         DLM_E_WORKSPACE, DLM_E_HIP.
  */

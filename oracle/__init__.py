@@ -31,26 +31,42 @@ MASK_FULL, MASK_BLOCK_CAUSAL, MASK_GROUP = 0, 1, 2
 ROW_SELECT, ROW_LOCK = 1, 2      # per-row flags of posterior() / select()
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
+# gcc flags of the sanitizer build (host code only): address and undefined-
+# behaviour checks, every finding fatal.
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math); with
+    sanitize, an AddressSanitizer + UBSan build at `out` (a process that
+    loads it must preload the sanitizer runtimes)."""
+    lib = out or _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp"
         subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
                         "-Wall", "-Wextra", "-Wno-unused-parameter",
+                        *(SANITIZE_FLAGS if sanitize else []),
                         _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 _lib = None
 
 
+def library_path() -> str:
+    """The oracle library this process loads: DLM_ORACLE_LIB when set (a
+    sanitizer build, used as it is), else the in-tree build."""
+    return os.environ.get("DLM_ORACLE_LIB") or _LIB
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        path = library_path()
+        if path == _LIB and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I, L, Dd = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.ora_scatter.argtypes = [P, P, P, P, P, I, I, I, I, I]

@@ -92,3 +92,41 @@ def test_stored_traffic_is_dropped_when_the_pass1_sources_change(tmp_path, monke
     assert bench.stored_traffic("other") is None           # no summary for it
     (tmp_path / bench.TRAFFIC_SOURCES[0]).write_text("changed\n")
     assert bench.stored_traffic("w") is None                # kernel changed since
+
+
+def test_trace_and_counter_summaries(tmp_path):
+    """The rocprofv3 CSV summarisers: per-kernel mean / median durations, and
+    per-dispatch counter values summed over a counter's instances."""
+    trace = tmp_path / "kernel_trace.csv"
+    trace.write_text("Kind,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+                     "KERNEL_DISPATCH,kA,1000,3000\nKERNEL_DISPATCH,kA,5000,6000\n"
+                     "KERNEL_DISPATCH,kA,7000,17000\nKERNEL_DISPATCH,kB,0,500\n")
+    t = bench.summarize_trace(str(trace))
+    assert "| `kA` | 3 | 4.33 | 2.00 | 1.00 | 10.00 | 13.0 |" in t
+    assert "| `kB` | 1 | 0.50 | 0.50 |" in t
+    pmc = tmp_path / "counter_collection.csv"
+    pmc.write_text("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+                   "1,kA,FETCH_SIZE,10\n1,kA,FETCH_SIZE,5\n2,kA,FETCH_SIZE,20\n2,kA,FETCH_SIZE,5\n"
+                   "3,kB,FETCH_SIZE,7\n")
+    s = bench.summarize_pmc(str(pmc))
+    assert "| `kA` | FETCH_SIZE | 2 | 20 | 20 | 15 | 25 |" in s
+    assert "| `kB` | FETCH_SIZE | 1 | 7 |" in s
+
+
+def test_stored_counters_follow_the_kernel_sources(tmp_path, monkeypatch):
+    for tag in bench.COUNTER_SOURCES:
+        for rel in bench.COUNTER_SOURCES[tag]:
+            f = tmp_path / rel
+            f.parent.mkdir(parents=True, exist_ok=True)
+            f.write_text("source " + rel + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "posterior_w_counters.md").write_text(
+        "# counters\n\n- kernel: `k`\n"
+        f"- source_sha256: `{bench.source_digest('posterior')}`\n"
+        "- traffic_bytes_per_launch: 4096\n- fetch_scale: 1.9998\n")
+    c = bench.stored_counters("posterior", "w")
+    assert c["traffic_bytes_per_launch"] == 4096 and c["fetch_scale"] == 1.9998
+    assert bench.stored_counters("attn_fwd", "w") is None
+    (tmp_path / bench.COUNTER_SOURCES["posterior"][0]).write_text("changed\n")
+    assert bench.stored_counters("posterior", "w") is None

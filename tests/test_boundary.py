@@ -78,6 +78,9 @@ def test_workspace_queries():
     (dict(md=_md(prefix_len=-1)), dlm.DLM_E_SHAPE),
     (dict(md=_md(M=91)), dlm.DLM_E_SHAPE),
     (dict(md=_md(M=-1)), dlm.DLM_E_SHAPE),
+    # 32-bit byte offsets per (batch, kv-head) slice: kv_len * D * 2 must stay below 2 GiB
+    (dict(kv=_kv(B=1, Hkv=1, n_cap=1 << 24, D=128), md=_md(Hq=1, kv_len=(1 << 23) + 64, prefix_len=0)),
+     dlm.DLM_E_SHAPE),
     (dict(md=_md(kind=7)), dlm.DLM_E_DESC),
     (dict(md=_md(kind=dlm.MASK_BLOCK_CAUSAL, block_size=0)), dlm.DLM_E_DESC),
     (dict(md=_md(kind=dlm.MASK_GROUP, block_size=16, n_slots=0, slot_state=FAKE, slot_group=FAKE)), dlm.DLM_E_DESC),

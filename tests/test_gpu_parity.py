@@ -438,7 +438,7 @@ def _sub_batch(case, b):
                          "slot_state": case.slot_state[b:b + 1], "slot_group": case.slot_group[b:b + 1]})
 
 
-def _check_attn_sampled(a, g, n_rows=256, colsum_batch=0, extra_cols=None, seed=0):
+def _check_attn_sampled(a, g, n_rows=1024, colsum_batch=0, extra_cols=None, seed=0):
     """Sampled out/lse rows for the whole batch; every row's lse and sampled
     columns of one batch entry; the column-total invariant for every entry."""
     rng = np.random.default_rng(seed)
@@ -468,13 +468,6 @@ def _check_attn_sampled(a, g, n_rows=256, colsum_batch=0, extra_cols=None, seed=
     return cs_o, cols
 
 
-def _check_post_sampled(p, g, rows, score_o=None):
-    ora = oracle.posterior(p.logits, p.prev, p.locked, p.eps, rows=rows)
-    check_posterior(g["kl"][rows], g["conf"][rows], g["locked"][rows], ora["kl"], ora["conf"],
-                    ora["locked"], p.eps, p.locked[rows])
-    return ora
-
-
 def test_full_llada_bidirectional():
     full_check(W.llada_bidirectional())
 
@@ -494,17 +487,16 @@ def test_full_mbd_multiblock(variant):
     a = w.attn
     _check_attn_sampled(a, g, extra_cols=np.arange(a.prefix_len - 64, a.kv_len))
     if with_post:
+        # every row and every selection group of the posterior
         p = w.post
-        groups = [0, 5, 17, 31]
-        rows = np.concatenate([np.arange(q * p.group_rows, (q + 1) * p.group_rows) for q in groups])
-        ora = _check_post_sampled(p, g, rows)
-        for q in range(len(groups)):
-            sl = slice(q * p.group_rows, (q + 1) * p.group_rows)
-            rr = rows[sl]
-            sel_o = oracle.select(p.mode, p.k, p.group_rows, p.tau, None, ora["conf"][sl], ora["tok"][sl],
-                                  p.locked[rr])
-            check_selection(g["sel"][rr], sel_o, p.mode, p.group_rows, p.tau, ora["conf"][sl], None,
-                            p.locked[rr], p.logits[rr])
+        ora = oracle.posterior(p.logits, p.prev, p.locked, p.eps)
+        check_posterior(g["kl"], g["conf"], g["locked"], ora["kl"], ora["conf"], ora["locked"], p.eps,
+                        p.locked)
+        sel_o = oracle.select(p.mode, p.k, p.group_rows, p.tau, None, ora["conf"], ora["tok"], p.locked)
+        exc = check_selection(g["sel"], sel_o, p.mode, p.group_rows, p.tau, ora["conf"], None, p.locked,
+                              p.logits)
+        assert (g["sel"] >= 0).sum() == p.k * (p.R // p.group_rows)
+        _say(f"  all {p.R // p.group_rows} groups checked; excused selections: {exc}")
 
 
 def test_full_surelock_sparse():
@@ -514,9 +506,10 @@ def test_full_surelock_sparse():
     ds.run()
     g = ds.results()
     _check_attn_sampled(w.attn, g, colsum_batch=1)
+    # every row of the posterior: KL, confidence and the lock decision
     p = w.post
-    rows = np.sort(np.random.default_rng(3).choice(p.R, size=256, replace=False))
-    _check_post_sampled(p, g, rows)
+    ora = oracle.posterior(p.logits, p.prev, p.locked, p.eps)
+    check_posterior(g["kl"], g["conf"], g["locked"], ora["kl"], ora["conf"], ora["locked"], p.eps, p.locked)
     assert np.all(g["sel"] == -1)
     frac = g["locked"].mean()
     _say(f"  locked fraction after the step: {frac:.3f}")
