@@ -30,7 +30,7 @@ SEL_TOPK_MARGIN, SEL_TOPK_LOW_ENTROPY = 5, 6
 ROW_SELECT, ROW_LOCK = 1, 2
 
 EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
-           "dlm_posterior_workspace_bytes", "dlm_block_buffer_init", "dlm_block_buffer_advance",
+           "dlm_posterior_workspace_bytes", "dlm_posterior_noalloc", "dlm_block_buffer_init", "dlm_block_buffer_advance",
            "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_layer_workspace_bytes", "dlm_r2l_scan",
            "dlm_last_error")
 
@@ -119,6 +119,8 @@ lib.dlm_step_attn_workspace_bytes.restype = ctypes.c_int
 lib.dlm_posterior.argtypes = [_P, _P, _P, ctypes.c_float, ctypes.POINTER(_Select), _P, _P, _P,
                               ctypes.c_int32, ctypes.c_int32, _P]
 lib.dlm_posterior.restype = ctypes.c_int
+lib.dlm_posterior_noalloc.argtypes = lib.dlm_posterior.argtypes
+lib.dlm_posterior_noalloc.restype = ctypes.c_int
 lib.dlm_posterior_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Select),
                                               ctypes.POINTER(ctypes.c_size_t)]
 lib.dlm_posterior_workspace_bytes.restype = ctypes.c_int
@@ -368,8 +370,7 @@ def dlm_posterior_workspace_bytes(R: int, V: int, select: Select) -> int:
     return n.value
 
 
-def dlm_posterior(logits, prev_logits, locked, eps: float, select: Select, sel, kl, conf,
-                  R: int, V: int, stream=None) -> None:
+def _post_args(logits, prev_logits, locked, select, sel, kl, conf, R, V):
     _expect(logits, "logits", (R, V), "torch.float32")
     _expect(prev_logits, "prev_logits", (R, V), "torch.float32")
     _expect(locked, "locked", (R,), "torch.uint8")
@@ -384,9 +385,27 @@ def dlm_posterior(logits, prev_logits, locked, eps: float, select: Select, sel, 
         _expect(select.entropy, "select.entropy", (R,), "torch.float32")
     if select.row_flags is not None:
         _expect(select.row_flags, "select.row_flags", (R,), "torch.uint8")
+
+
+def dlm_posterior(logits, prev_logits, locked, eps: float, select: Select, sel, kl, conf,
+                  R: int, V: int, stream=None) -> None:
+    _post_args(logits, prev_logits, locked, select, sel, kl, conf, R, V)
     s = _c_sel(select)
     _check(lib.dlm_posterior(_ptr(logits), _ptr(prev_logits), _ptr(locked), eps, ctypes.byref(s),
                              _ptr(sel), _ptr(kl), _ptr(conf), R, V, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # DLM_NOALLOC_SCRATCH_BYTES
+
+
+def dlm_posterior_noalloc(logits, prev_logits, locked, eps: float, select: Select, sel, kl, conf,
+                          R: int, V: int, stream=None) -> None:
+    """dlm_posterior with its partials in the library's own device array
+    (no workspace; select.workspace is ignored)."""
+    _post_args(logits, prev_logits, locked, select, sel, kl, conf, R, V)
+    s = _c_sel(select)
+    _check(lib.dlm_posterior_noalloc(_ptr(logits), _ptr(prev_logits), _ptr(locked), eps, ctypes.byref(s),
+                                     _ptr(sel), _ptr(kl), _ptr(conf), R, V, _stream(stream)))
 
 
 def _expect_bb(bb: BlockBuffer):

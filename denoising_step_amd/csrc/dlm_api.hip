@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -236,11 +237,33 @@ int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select
     return DLM_OK;
 }
 
-int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked, float eps,
-                  const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R, int32_t V,
-                  hipStream_t stream)
+// The posterior with its per-(row, chunk) partials at `ws` (ws_bytes of
+// device memory, or NULL when none is given).
+static int posterior_with(const float *logits, const float *prev_logits, uint8_t *locked, float eps,
+                          const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R,
+                          int32_t V, hipStream_t stream, void *ws, size_t ws_bytes)
 {
-    g_err[0] = 0;
+    dlm::PostPlan p = dlm::plan_post(R, V, select->mode, select->group_rows);
+    if (p.ws_total > 0 && (ws == nullptr || ws_bytes < p.ws_total))
+        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_total,
+                    ws ? ws_bytes : (size_t)0);
+    dlm::PostArgs a{};
+    a.x = logits; a.y = prev_logits; a.locked = locked; a.score = select->score;
+    a.sel = sel; a.kl = kl; a.conf = conf; a.margin = select->margin; a.entropy = select->entropy;
+    a.flags = select->row_flags;
+    a.part = static_cast<dlm::PostPartial *>(ws);
+    a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
+    a.eps = eps; a.tau = select->tau; a.conf_gate = select->conf_gate;
+    a.n_chunks = p.n_chunks; a.chunk = p.chunk;
+    hipError_t e = dlm::launch_posterior(a, stream, select->score_ready);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "launch or event wait failed: %s", hipGetErrorString(e));
+    return DLM_OK;
+}
+
+static int check_post_call(const float *logits, const float *prev_logits, uint8_t *locked, float eps,
+                           const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R,
+                           int32_t V)
+{
     int rc = check_post_scalars(R, V, select);
     if (rc != DLM_OK) return rc;
     if (!logits || !prev_logits || !locked || !sel || !kl || !conf)
@@ -250,21 +273,78 @@ int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked
     if (isnan(eps)) return fail(DLM_E_DESC, "eps is NaN");
     if ((V & 3) == 0 && (!aligned16(logits) || !aligned16(prev_logits)))
         return fail(DLM_E_SHAPE, "logits must be 16-byte aligned");
-    dlm::PostPlan p = dlm::plan_post(R, V, select->mode, select->group_rows);
-    if (p.ws_total > 0 && (select->workspace == nullptr || select->workspace_bytes < p.ws_total))
-        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_total,
-                    select->workspace ? select->workspace_bytes : (size_t)0);
-    dlm::PostArgs a{};
-    a.x = logits; a.y = prev_logits; a.locked = locked; a.score = select->score;
-    a.sel = sel; a.kl = kl; a.conf = conf; a.margin = select->margin; a.entropy = select->entropy;
-    a.flags = select->row_flags;
-    a.part = static_cast<dlm::PostPartial *>(select->workspace);
-    a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
-    a.eps = eps; a.tau = select->tau; a.conf_gate = select->conf_gate;
-    a.n_chunks = p.n_chunks; a.chunk = p.chunk;
-    hipError_t e = dlm::launch_posterior(a, stream, select->score_ready);
-    if (e != hipSuccess) return fail(DLM_E_HIP, "launch or event wait failed: %s", hipGetErrorString(e));
     return DLM_OK;
+}
+
+int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked, float eps,
+                  const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R, int32_t V,
+                  hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_post_call(logits, prev_logits, locked, eps, select, sel, kl, conf, R, V);
+    if (rc != DLM_OK) return rc;
+    return posterior_with(logits, prev_logits, locked, eps, select, sel, kl, conf, R, V, stream,
+                          select->workspace, select->workspace_bytes);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free posterior.  The partials live in `scratch`, a file-scope
+// device array: every GPU the library runs on holds its own copy from the
+// first call on that device until the process ends.  In host code the
+// array's name is only a host-side stand-in, so its device address is
+// fetched once per device (with that device current) by
+// hipGetSymbolAddress and kept; kernels get that address, never the name.
+// Every call on a GPU shares that GPU's array: calls that overlap on one
+// GPU (two streams, two threads) race on it.  Nothing in it has to start
+// at zero: the stream kernel writes every partial the finish kernel reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[DLM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];   // device address of `scratch`, per device
+}  // namespace
+
+static int scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DLM_E_UNSUPPORTED, "device %d is past the %d devices the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(DLM_E_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return DLM_OK;
+}
+
+int dlm_posterior_noalloc(const float *logits, const float *prev_logits, uint8_t *locked, float eps,
+                          const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R,
+                          int32_t V, hipStream_t stream)
+{
+    g_err[0] = 0;
+    int rc = check_post_call(logits, prev_logits, locked, eps, select, sel, kl, conf, R, V);
+    if (rc != DLM_OK) return rc;
+    const size_t need = dlm::plan_post(R, V, select->mode, select->group_rows).ws_total;
+    if (need > (size_t)DLM_NOALLOC_SCRATCH_BYTES)
+        return fail(DLM_E_WORKSPACE, "R=%d V=%d needs %zu bytes of partials; the allocation-free entry "
+                    "point holds %zu (use dlm_posterior with a workspace)", R, V, need,
+                    (size_t)DLM_NOALLOC_SCRATCH_BYTES);
+    if (R == 0) return DLM_OK;
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != DLM_OK) return rc;
+    return posterior_with(logits, prev_logits, locked, eps, select, sel, kl, conf, R, V, stream, ws,
+                          (size_t)DLM_NOALLOC_SCRATCH_BYTES);
 }
 
 static int check_layer(const dlm_layer_desc *L)

@@ -267,6 +267,28 @@ int dlm_posterior(const float *logits, const float *prev_logits, uint8_t *locked
 int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select,
                                   size_t *bytes);
 
+/* Largest partials area the allocation-free posterior holds (bytes). */
+#define DLM_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* dlm_posterior without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, outputs and errors as
+ * dlm_posterior; select->workspace and workspace_bytes are ignored.  The
+ * per-(row, vocabulary chunk) partials go to a file-scope device array of
+ * DLM_NOALLOC_SCRATCH_BYTES, which each GPU the library runs on holds from
+ * the first call on it until the process ends; its device address is
+ * fetched on that first call (the only call that may load the module's
+ * globals), after which no call allocates or frees anything.
+ * Limit: a problem whose partials (dlm_posterior_workspace_bytes) exceed
+ * DLM_NOALLOC_SCRATCH_BYTES returns DLM_E_WORKSPACE before any work is
+ * enqueued.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and give
+ * undefined results; calls ordered on one stream are safe. */
+int dlm_posterior_noalloc(const float *logits, const float *prev_logits,
+                          uint8_t *locked, float eps, const dlm_select *select,
+                          int32_t *sel, float *kl, float *conf, int32_t R,
+                          int32_t V, hipStream_t stream);
+
 /*
  * Block Buffer of a multi-step run ("Multi-Block Diffusion Language Models"
  * page, sec. 2.3; SureLock page, sec. 2).  The generation region of each

@@ -166,6 +166,41 @@ def test_posterior_rejects(case, code):
     assert _post(**case) == code
 
 
+def _post_noalloc(R=16, V=512, sel=None, logits=FAKE, prev=FAKE, locked=FAKE, out=FAKE, eps=1e-3):
+    sel = sel or dlm.Select(mode=dlm.SEL_TOPK_CONF, k=4, group_rows=16)
+    with pytest.raises(dlm.DlmError) as e:
+        dlm.dlm_posterior_noalloc(logits, prev, locked, eps, sel, out, FAKE, FAKE, R, V, stream=0)
+    return e.value.code
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(R=-1), dlm.DLM_E_SHAPE),
+    (dict(V=0), dlm.DLM_E_SHAPE),
+    (dict(sel=dlm.Select(mode=9)), dlm.DLM_E_DESC),
+    (dict(sel=dlm.Select(mode=dlm.SEL_TOPK_SCORE, k=3, group_rows=16)), dlm.DLM_E_NULL),
+    (dict(logits=None), dlm.DLM_E_NULL),
+    (dict(out=None), dlm.DLM_E_NULL),
+    (dict(eps=float("nan")), dlm.DLM_E_DESC),
+    (dict(logits=FAKE + 4), dlm.DLM_E_SHAPE),
+    # partials past the scratch array: 200000 rows of one chunk, 48 B each
+    (dict(R=200000, V=4096, sel=dlm.Select(mode=dlm.SEL_NONE)), dlm.DLM_E_WORKSPACE),
+])
+def test_posterior_noalloc_rejects(case, code):
+    """The allocation-free posterior checks what dlm_posterior checks, and
+    rejects a problem whose partials do not fit its array, before any HIP
+    call (the workspace fields are ignored)."""
+    assert _post_noalloc(**case) == code
+    assert dlm.dlm_last_error() != ""
+    big = dlm.dlm_posterior_workspace_bytes(200000, 4096, dlm.Select(mode=dlm.SEL_NONE))
+    assert big > dlm.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    with open(os.path.join(ROOT, "include", "dlm_step.h")) as f:
+        m = re.search(r"#define DLM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == dlm.NOALLOC_SCRATCH_BYTES
+
+
 def test_oracle_and_library_share_no_code():
     """The GPU sources and the oracle neither include nor import each other."""
     csrc = os.path.join(ROOT, "denoising_step_amd", "csrc")
