@@ -160,8 +160,16 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 // instructions), double-buffered: the loads of tile t+1 are issued before
 // tile t is
 // computed, and one barrier per tile publishes them.  Rows at or past
-// kv_len and rows of DUMMY slots are given an out-of-range offset and read
-// as zeros.
+// kv_len and rows hidden from every query of the workgroup (DUMMY slots,
+// later blocks or groups) are given an out-of-range offset and read as
+// zeros.
+//
+// Mask tiles (block-causal and group masks): the workgroup's query codes
+// span [qmin, qmax] and each key tile's codes [kmin, kmax], from the slot
+// table staged in LDS.  kmin > qmax: hidden from every row, skipped (no
+// MFMAs; none of its rows is fetched, and leading or trailing runs of such
+// tiles are not visited at all); kmax <= qmin: visible to every row, no
+// predicate; otherwise partial, the per-key predicate runs.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so that every lane group the
 // LDS serves in one cycle hits distinct banks):
@@ -246,10 +254,11 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KT * D];
     __shared__ int kcode_s[2][KT];
     __shared__ int scode_s[kMaxSlots];
+    __shared__ int qrange_s[2][QW];                    // each query wave's smallest / largest code
     __shared__ float ml_s[NG == 2 ? 4 * 4 * 64 : 1];   // each key group's running max and sum
 
     const int tid = threadIdx.x;
-    const int wid = tid >> 6, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
     const int kg = NG == 2 ? wid >> 2 : 0;   // key group
     const int wq = NG == 2 ? wid & 3 : wid;  // query wave
@@ -273,10 +282,11 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     }
     // Zero the tiles once, so no LDS byte a tile does not overwrite can
     // ever be a non-finite value times a zero weight.  Only a ragged last
-    // tile (rows past kv_len) or DUMMY rows (GROUP) take the out-of-range
-    // path; split boundaries are whole tiles, so otherwise every row of
-    // every tile is loaded.
-    const bool ragged = a.kv_len % KT != 0 || a.kind == 2;
+    // tile (rows past kv_len) or rows hidden from the whole workgroup
+    // (block-causal and group masks) take the out-of-range path; split
+    // boundaries are whole tiles, so otherwise every row of every tile is
+    // loaded.
+    const bool ragged = a.kv_len % KT != 0 || a.kind != 0;
     for (int i = tid; ragged && i < KT * D / 8; i += NT) {
         reinterpret_cast<uint4 *>(Ks0)[i] = uint4{0, 0, 0, 0};
         reinterpret_cast<uint4 *>(Ks1)[i] = uint4{0, 0, 0, 0};
@@ -294,6 +304,24 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     const int h = g * a.G + hl;
     const int pos = a.active_idx[(long)b * a.M + j];
     const int qcode = rv ? query_code(a, gr, pos) : INT_MIN;
+    // The workgroup's query-code range over its valid rows: a key tile
+    // whose smallest code exceeds qmax is hidden from every row and
+    // skipped; one whose largest code is at most qmin is visible to every
+    // row and runs without the predicate; any other tile is partial and
+    // runs the per-key predicate.  Each query wave reduces its rows with
+    // shuffles and leaves its range in LDS for the first barrier.
+    int qmin = 0, qmax = 0;
+    if (a.kind != 0) {
+        int mn = rv ? qcode : INT_MAX, mx = rv ? qcode : INT_MIN;
+        for (int o = 32; o >= 1; o >>= 1) {
+            mn = min(mn, __shfl_xor(mn, o));
+            mx = max(mx, __shfl_xor(mx, o));
+        }
+        if (kg == 0 && lane == 0) {
+            qrange_s[0][wq] = mn;
+            qrange_s[1][wq] = mx;
+        }
+    }
 
     bf16x8 qf[DK];
     {
@@ -306,6 +334,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
 
     const int k0 = split * a.split_keys;
     const int k1 = min(a.kv_len, k0 + a.split_keys);
+    int kbeg = k0, kend = k1;        // the split's live tiles (set after the first barrier)
     const uint16_t *kbase = a.ck + (long)bg * a.n_cap * D;
     const uint16_t *vbase = a.cv + (long)bg * a.n_cap * D;
     const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * ROWB);
@@ -323,11 +352,6 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         k_goff[u] = (kkey * D + ((lp ^ k_swz<D>(lr)) * 8)) * 2;
         v_goff[u] = (lr * D + ((lp ^ v_swz<D>(lr)) * 8)) * 2;
     }
-    auto dummy_row = [&](int n) -> bool {
-        if (n < a.P || n >= a.kv_len) return false;
-        const int s = (n - a.P) / a.bs;
-        return s >= a.n_slots || scode_s[s] == INT_MAX;
-    };
     // key_code from the slot codes staged in LDS: no global load, so the
     // only loads in flight in the tile loop are the tile loads themselves.
     auto key_code_lds = [&](int n) -> int {
@@ -337,31 +361,88 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         if (a.kind == 1) return sl;
         return sl < a.n_slots ? scode_s[sl] : INT_MAX;
     };
+    // Smallest and largest key code over keys [t0, t0 + len), keys at or
+    // past kv_len counting as INT_MAX, from the staged slot codes (uniform
+    // across the workgroup).  A group-mask range spanning more than eight
+    // slots reports the widest range, i.e. a partial tile.
+    auto key_range = [&](int t0, int len, int &kmn, int &kmx) {
+        const int hi = min(t0 + len, a.kv_len);
+        kmn = INT_MAX;
+        kmx = t0 + len > a.kv_len ? INT_MAX : INT_MIN;
+        if (t0 < hi) {
+            if (a.kind == 0 || t0 < a.P) kmn = INT_MIN;
+            const int lo = max(t0, a.P);
+            if (a.kind != 0 && lo < hi) {
+                const int s0 = (lo - a.P) / a.bs, s1 = (hi - 1 - a.P) / a.bs;
+                if (a.kind == 1) {
+                    kmn = min(kmn, s0);
+                    kmx = max(kmx, s1);
+                } else if (s1 - s0 >= 8) {
+                    kmn = INT_MIN;
+                    kmx = INT_MAX;
+                } else {
+                    for (int sl = s0; sl <= s1; ++sl) {
+                        const int c = sl < a.n_slots ? scode_s[sl] : INT_MAX;
+                        kmn = min(kmn, c);
+                        kmx = max(kmx, c);
+                    }
+                }
+            }
+        }
+        kmn = __builtin_amdgcn_readfirstlane(kmn);
+        kmx = __builtin_amdgcn_readfirstlane(kmx);
+    };
+    // Whether the tile at t0 is partial: not visible to every row of the
+    // workgroup (a ragged tail, or block-causal / group keys some row does
+    // not see).  Only partial tiles stage key codes for the predicate and
+    // check their rows.
+    auto partial_tile = [&](int t0) -> bool {
+        if (t0 + KT <= a.P) return false;
+        int kmn, kmx;
+        key_range(t0, KT, kmn, kmx);
+        return kmx > qmin;
+    };
     // Direct loads of the K (with its key codes) or V half of the tile at t0
-    // into LDS buffer buf.
-    auto issue_k = [&](int t0, int buf) {
+    // into LDS buffer buf.  In a partial block-causal or group tile, a row
+    // whose key is hidden from every row of the workgroup (a DUMMY slot, a
+    // later block or group) is not fetched: its out-of-range offset reads
+    // zeros, and the predicate masks it anyway.  Other tiles take the plain
+    // loop.
+    auto issue_k = [&](int t0, int buf, bool part) {
         uint16_t *ks = buf ? Ks1 : Ks0;
-        const bool group_tail = a.kind == 2 && t0 + KT > a.P;
-        for (int u = 0; u < NLD; ++u) {
-            int ko = k_goff[u] + t0 * ROWB;
-            if (group_tail) {
+        if (part && a.kind != 0) {
+            for (int u = 0; u < NLD; ++u) {
                 const int lr = ld_row[u];
                 const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));
-                if (dummy_row(t0 + kkey)) ko = OOB;
+                const int ko = key_code_lds(t0 + kkey) > qmax ? OOB : k_goff[u] + t0 * ROWB;
+                lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
             }
-            lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
+        } else {
+            // (the offsets are named variables: with the expression as the
+            // builtin's argument, the host pass drops the kernel's stub)
+            for (int u = 0; u < NLD; ++u) {
+                lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
+                const int ko = k_goff[u] + t0 * ROWB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
+            }
         }
-        if (tid < KT) kcode_s[buf][tid] = key_code_lds(t0 + tid);
+        if (part && tid < KT) kcode_s[buf][tid] = key_code_lds(t0 + tid);
     };
-    auto issue_v = [&](int t0, int buf) {
+    auto issue_v = [&](int t0, int buf, bool part) {
         uint16_t *vs = buf ? Vs1 : Vs0;
-        const bool group_tail = a.kind == 2 && t0 + KT > a.P;
-        for (int u = 0; u < NLD; ++u) {
-            int vo = v_goff[u] + t0 * ROWB;
-            if (group_tail && dummy_row(t0 + ld_row[u])) vo = OOB;
-            lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
+        if (part && a.kind != 0) {
+            for (int u = 0; u < NLD; ++u) {
+                const int vo = key_code_lds(t0 + ld_row[u]) > qmax ? OOB : v_goff[u] + t0 * ROWB;
+                lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
+            }
+        } else {
+            for (int u = 0; u < NLD; ++u) {
+                lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
+                const int vo = v_goff[u] + t0 * ROWB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
+            }
         }
     };
 
@@ -454,59 +535,101 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
             }
         }
     };
-    auto all_visible = [&](int t0) { return (a.kind == 0 && t0 + KT <= a.kv_len) || (t0 + KT <= a.P); };
 
-    // One tile: compute on LDS buffer BUF while tile t0 + KT streams
-    // into the other one.  BUF is a compile-time constant, so the
-    // compiler sees that the reads and the in-flight LDS loads touch
-    // different arrays and does not wait for the loads before reading.
-    // The PV products of sub-tile 0 are interleaved with the
-    // exponentials of sub-tile 1.
+    // One tile: compute on LDS buffer BUF while tile t0 + KT streams into
+    // the other one.  BUF is a compile-time constant, so the compiler sees
+    // that the reads and the in-flight LDS loads touch different arrays and
+    // does not wait for the loads before reading.  The PV products of
+    // sub-tile 0 are interleaved with the exponentials of sub-tile 1.
+    // Prefix tiles and whole in-range tiles of a full mask are visible to
+    // every row; any other tile is classified by this key group's 64 keys:
+    // skipped when hidden from every row, no predicate when visible to all.
     auto tile_step = [&](auto bufc, int t0) {
         constexpr int BUF = decltype(bufc)::value;
-        if (t0 + KT < k1) {
-            issue_k(t0 + KT, BUF ^ 1);
-            issue_v(t0 + KT, BUF ^ 1);
+        if (t0 + KT < kend) {
+            const bool part = partial_tile(t0 + KT);
+            issue_k(t0 + KT, BUF ^ 1, part);
+            issue_v(t0 + KT, BUF ^ 1, part);
         }
-        const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
-        const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
-        f32x16 s0, s1;
-        qk(ks, s0, s1);
-        float u0[16], u1[16];
-        prep(s0, s1, kcode_s[BUF] + kofs, all_visible(t0), u0, u1);
-        float psum = 0.f;
-        bf16x8 p0[2], p1[2];
-        for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(u0[i]);
-            psum += p;
-            p0[i >> 3][i & 7] = (__bf16)p;
+        bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
+        bool live = true;
+        if (!vis) {
+            int kmn, kmx;
+            key_range(t0 + kofs, 64, kmn, kmx);
+            live = kmn <= qmax;
+            vis = kmx <= qmin;
         }
-        constexpr int PER = 16 / (2 * DT);   // exps of sub-tile 1 per PV product
-        for (int q = 0; q < 2 * DT; ++q) {
-            pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
-            for (int e = 0; e < PER; ++e) {
-                const int i = q * PER + e;
-                const float p = fast_exp2(u1[i]);
+        if (live) {
+            const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
+            const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
+            f32x16 s0, s1;
+            qk(ks, s0, s1);
+            float u0[16], u1[16];
+            prep(s0, s1, kcode_s[BUF] + kofs, vis, u0, u1);
+            float psum = 0.f;
+            bf16x8 p0[2], p1[2];
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(u0[i]);
                 psum += p;
-                p1[i >> 3][i & 7] = (__bf16)p;
+                p0[i >> 3][i & 7] = (__bf16)p;
             }
+            constexpr int PER = 16 / (2 * DT);   // exps of sub-tile 1 per PV product
+            for (int q = 0; q < 2 * DT; ++q) {
+                pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
+                for (int e = 0; e < PER; ++e) {
+                    const int i = q * PER + e;
+                    const float p = fast_exp2(u1[i]);
+                    psum += p;
+                    p1[i >> 3][i & 7] = (__bf16)p;
+                }
+            }
+            l_run += psum;
+            for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
         }
-        l_run += psum;
-        for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
         __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile landed
         __syncthreads();
     };
 
-    __syncthreads();   // slot codes and zeroed tiles visible
-    if (k0 < k1) {
-        issue_k(k0, 0);
-        issue_v(k0, 0);
+    __syncthreads();   // slot codes, zeroed tiles and the query waves' code ranges visible
+    if (a.kind != 0) {
+        qmin = INT_MAX;
+        qmax = INT_MIN;
+        for (int w = 0; w < QW; ++w) {
+            qmin = min(qmin, qrange_s[0][w]);
+            qmax = max(qmax, qrange_s[1][w]);
+        }
+        qmin = __builtin_amdgcn_readfirstlane(qmin);
+        qmax = __builtin_amdgcn_readfirstlane(qmax);
+    }
+    // Leading and trailing tiles of the split that are hidden from every
+    // row (later blocks or groups, DUMMY slots past the last live one) are
+    // never visited: no loads, no MFMAs.  A hidden tile between live ones
+    // is visited, but its rows are not fetched and its MFMAs are skipped.
+    if (a.kind != 0) {
+        int kmn, kmx;
+        for (; kbeg < kend; kbeg += KT) {
+            key_range(kbeg, KT, kmn, kmx);
+            if (kmn <= qmax) break;
+        }
+        while (kend > kbeg) {
+            const int tl = kbeg + (kend - 1 - kbeg) / KT * KT;   // start of the last tile
+            key_range(tl, KT, kmn, kmx);
+            if (kmn <= qmax) break;
+            kend = tl;
+        }
+        kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+        kend = __builtin_amdgcn_readfirstlane(kend);
+    }
+    if (kbeg < kend) {
+        const bool part = partial_tile(kbeg);
+        issue_k(kbeg, 0, part);
+        issue_v(kbeg, 0, part);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t0 = k0; t0 < k1; t0 += 2 * KT) {
+    for (int t0 = kbeg; t0 < kend; t0 += 2 * KT) {
         tile_step(std::integral_constant<int, 0>{}, t0);
-        if (t0 + KT < k1) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
+        if (t0 + KT < kend) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
     }
 
     // Finish the rows: with two key groups, the groups first merge their
@@ -665,9 +788,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
 // as one sequence, double-buffered in LDS (tile t+1 is loaded straight into
 // LDS while tile t is used), and writes one partial column sum per (q-head,
 // row split).
-// Rows past the slice or with lse = -inf get lse = +inf (weight 0).  The
-// visibility test is only evaluated when the mask can hide a key of the
-// block from a counted row.
+// Rows past the slice or with lse = -inf get lse = +inf (weight 0).  Mask
+// tiles: a wave whose 64 keys are hidden from every weighted row of a query
+// tile skips the tile; one whose keys are visible to all of them adds
+// without the predicate; otherwise the per-element predicate runs.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
@@ -681,6 +805,7 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(1024))) uint16_t Qs1[kCsRows * D];
     __shared__ __attribute__((aligned(16))) float lse2_s[2][kCsRows];
     __shared__ int qcode_s[2][kCsRows];
+    __shared__ int qr_s[2][2];                     // each query tile's smallest / largest code
     __shared__ int range_s[2];
     __shared__ int grp_s[kMaxSlots];               // GROUP: slot -> group id
     __shared__ int kcs_s[kMaxSlots];               // GROUP: slot -> key code (INT_MAX: DUMMY)
@@ -759,6 +884,24 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
         }
         kc[ct] = c;
     }
+    // This wave's key-code range (keys past kv_len are never written, so
+    // they do not count): a query tile whose largest code is below it sees
+    // none of the wave's keys (the wave skips the tile); one whose smallest
+    // code is at least its top sees all of them (no predicate).
+    int wkmin = INT_MAX, wkmax = INT_MIN;
+    if (need_mask) {
+        for (int ct = 0; ct < 2; ++ct)
+            if (key[ct] < a.kv_len) {
+                wkmin = min(wkmin, kc[ct]);
+                wkmax = max(wkmax, kc[ct]);
+            }
+        for (int o = 32; o >= 1; o >>= 1) {
+            wkmin = min(wkmin, __shfl_xor(wkmin, o));
+            wkmax = max(wkmax, __shfl_xor(wkmax, o));
+        }
+        wkmin = __builtin_amdgcn_readfirstlane(wkmin);
+        wkmax = __builtin_amdgcn_readfirstlane(wkmax);
+    }
     const int j_lo = range_s[0], j_hi = range_s[1];
     const int cnt = max(0, j_hi - j_lo);
     const int per = ((cnt + a.n_rsplit - 1) / a.n_rsplit + kCsRows - 1) / kCsRows * kCsRows;
@@ -801,17 +944,32 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
         }
     };
     // lse in log2 units, +inf (weight 0) for a row past the slice or
-    // without a visible key; the row's mask code from the staged slot table.
+    // without a visible key; the row's mask code from the staged slot table,
+    // and the code range of the tile's weighted rows (wave 0; its lanes past
+    // kCsRows hold no row).
     auto store_rows = [&](int buf) {
-        if (tid < kCsRows) {
+        if (wid == 0) {
             const bool ok = lraw != -INFINITY;
             int qc = 0;
             if (need_mask) {
                 const int sl = (praw - a.P) / a.bs;
                 qc = a.kind == 1 ? sl : (sl >= 0 && sl < a.n_slots ? grp_s[sl] : INT_MIN);
             }
-            lse2_s[buf][tid] = ok ? lraw * kLog2e : INFINITY;
-            qcode_s[buf][tid] = ok ? qc : INT_MIN;
+            if (tid < kCsRows) {
+                lse2_s[buf][tid] = ok ? lraw * kLog2e : INFINITY;
+                qcode_s[buf][tid] = ok ? qc : INT_MIN;
+            }
+            if (need_mask) {
+                int mn = ok ? qc : INT_MAX, mx = ok ? qc : INT_MIN;
+                for (int o = 32; o >= 1; o >>= 1) {
+                    mn = min(mn, __shfl_xor(mn, o));
+                    mx = max(mx, __shfl_xor(mx, o));
+                }
+                if (lane == 0) {
+                    qr_s[buf][0] = mn;
+                    qr_s[buf][1] = mx;
+                }
+            }
         }
     };
     int q_rd[DK];                                        // Q chunk 2kk+hh of row l32
@@ -826,28 +984,35 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
         const bool more = t + 1 < n_tiles;
         if (more) issue_q(t + 1, BUF ^ 1);
         const uint16_t *qs = BUF ? Qs1 : Qs0;
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
-        for (int kk = 0; kk < DK; ++kk) {
-            const bf16x8 qa = lds_frag(qs + q_rd[kk]);
-            s0 = mfma32(qa, kf[0][kk], s0);
-            s1 = mfma32(qa, kf[1][kk], s1);
+        bool run = true, masked = false;
+        if (need_mask) {
+            run = wkmin <= __builtin_amdgcn_readfirstlane(qr_s[BUF][1]);
+            masked = wkmax > __builtin_amdgcn_readfirstlane(qr_s[BUF][0]);
         }
-        // element i of this lane is query row 8*(i/4) + 4*hh + i%4 of the tile
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 l2 = *reinterpret_cast<const float4 *>(&lse2_s[BUF][8 * q4 + 4 * hh]);
-            const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
-            if (!need_mask) {
-                for (int e = 0; e < 4; ++e) {
-                    acc[0] += fast_exp2(fmaf(s0[q4 * 4 + e], a.scale_log2, -lv[e]));
-                    acc[1] += fast_exp2(fmaf(s1[q4 * 4 + e], a.scale_log2, -lv[e]));
-                }
-            } else {
-                for (int e = 0; e < 4; ++e) {
-                    const int qc = qcode_s[BUF][8 * q4 + 4 * hh + e];
-                    const float p0 = fast_exp2(fmaf(s0[q4 * 4 + e], a.scale_log2, -lv[e]));
-                    const float p1 = fast_exp2(fmaf(s1[q4 * 4 + e], a.scale_log2, -lv[e]));
-                    acc[0] += kc[0] <= qc ? p0 : 0.f;
-                    acc[1] += kc[1] <= qc ? p1 : 0.f;
+        if (run) {
+            f32x16 s0 = f32x16{}, s1 = f32x16{};
+            for (int kk = 0; kk < DK; ++kk) {
+                const bf16x8 qa = lds_frag(qs + q_rd[kk]);
+                s0 = mfma32(qa, kf[0][kk], s0);
+                s1 = mfma32(qa, kf[1][kk], s1);
+            }
+            // element i of this lane is query row 8*(i/4) + 4*hh + i%4 of the tile
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 l2 = *reinterpret_cast<const float4 *>(&lse2_s[BUF][8 * q4 + 4 * hh]);
+                const float lv[4] = {l2.x, l2.y, l2.z, l2.w};
+                if (!masked) {
+                    for (int e = 0; e < 4; ++e) {
+                        acc[0] += fast_exp2(fmaf(s0[q4 * 4 + e], a.scale_log2, -lv[e]));
+                        acc[1] += fast_exp2(fmaf(s1[q4 * 4 + e], a.scale_log2, -lv[e]));
+                    }
+                } else {
+                    for (int e = 0; e < 4; ++e) {
+                        const int qc = qcode_s[BUF][8 * q4 + 4 * hh + e];
+                        const float p0 = fast_exp2(fmaf(s0[q4 * 4 + e], a.scale_log2, -lv[e]));
+                        const float p1 = fast_exp2(fmaf(s1[q4 * 4 + e], a.scale_log2, -lv[e]));
+                        acc[0] += kc[0] <= qc ? p0 : 0.f;
+                        acc[1] += kc[1] <= qc ? p1 : 0.f;
+                    }
                 }
             }
         }

@@ -172,6 +172,70 @@ def test_both_pass1_workgroup_shapes(kgroups, case, monkeypatch):
     full_check(w)
 
 
+def mask_tiles_case(name, seed=0):
+    """Shapes whose key tiles fall in each of the three mask classes:
+    hidden from every row of a workgroup (skipped), visible to all of them
+    (no predicate), partial.  Hidden cache rows hold large-variance garbage,
+    so reading one into a sum would show."""
+    B, Hq, Hkv, D = 2, 4, 2, 64
+    garbage = None
+    if name == "bc_early":
+        # block-causal, rows in blocks 0-1 only: blocks 2-9 are hidden from every row
+        P, bs, n_slots = 100, 32, 10
+        act = np.tile(np.arange(P, P + 2 * bs, dtype=np.int32), (B, 1))
+        state = np.full((B, n_slots), W.SLOT_ACTIVE, np.uint8)
+        group = np.zeros((B, n_slots), np.int32)
+        kind = W.MASK_BLOCK_CAUSAL
+        garbage = np.zeros((B, P + n_slots * bs), bool)
+        garbage[:, P + 2 * bs:] = True
+    elif name == "group_split":
+        # groups 0,0,1,1,2,2,2,2; rows in slots 0-2, slot 3 committed: group 2 is hidden
+        P, bs, n_slots = 64, 32, 8
+        act = np.tile(np.arange(P, P + 3 * bs, dtype=np.int32), (B, 1))
+        state = np.full((B, n_slots), W.SLOT_ACTIVE, np.uint8)
+        state[:, 3] = W.SLOT_IN_CACHE
+        group = np.tile(np.array([0, 0, 1, 1, 2, 2, 2, 2], np.int32), (B, 1))
+        kind = W.MASK_GROUP
+        garbage = np.zeros((B, P + n_slots * bs), bool)
+        garbage[:, P + 4 * bs:] = True
+    elif name == "group_one_block":
+        # one 256-position block, every position a row: every tile visible to all
+        B, Hq, Hkv, D = 1, 4, 4, 128
+        P, bs, n_slots = 0, 256, 1
+        act = np.arange(bs, dtype=np.int32)[None]
+        state = np.full((B, n_slots), W.SLOT_ACTIVE, np.uint8)
+        group = np.zeros((B, n_slots), np.int32)
+        kind = W.MASK_GROUP
+    else:
+        raise KeyError(name)
+    kv_len = P + n_slots * bs
+    M = act.shape[1]
+    a = W.make_attn("mask_tiles_" + name, B=B, Hq=Hq, Hkv=Hkv, D=D, kv_len=kv_len, prefix_len=P,
+                    active_idx=act, kind=kind, block_size=bs, n_slots=n_slots, slot_state=state,
+                    slot_group=group, cs_lo=0, cs_hi=kv_len, garbage_rows=garbage, seed=seed)
+    p = W.make_post(a.name, R=B * M, V=4096, logit_std=3.0, noise_std=0.1, eps=1e-3,
+                    mode=W.SEL_TOPK_CONF, k=4, group_rows=32, seed=seed)
+    return W.Workload(a, p, "mask tiles " + name)
+
+
+@pytest.mark.parametrize("kgroups", ["1", "2"])
+@pytest.mark.parametrize("case", ["bc_early", "group_split", "group_one_block"])
+def test_mask_tile_classes(kgroups, case, monkeypatch):
+    """Tiles hidden from a whole workgroup are skipped, tiles visible to all
+    its rows run without the predicate, the rest run it: all three against
+    the oracle, with both pass-1 workgroup shapes.  Hidden columns get
+    exactly zero column sums."""
+    monkeypatch.setenv("DLM_ATTN_KGROUPS", kgroups)
+    _say(f"DLM_ATTN_KGROUPS={kgroups}")
+    w = mask_tiles_case(case)
+    _, g, ora = full_check(w)
+    if case != "group_one_block":
+        a = w.attn
+        first_hidden = a.prefix_len + (2 if case == "bc_early" else 4) * a.block_size
+        assert np.all(g["colsum"][:, first_hidden:] == 0)
+        assert np.all(ora["colsum"][:, first_hidden:] == 0)
+
+
 @pytest.mark.parametrize("case", ["llada_dynamic", "long_topk_score"])
 def test_overlapped_step_equals_serial(case):
     """The overlapped schedule (posterior on a second stream, its selection
