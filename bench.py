@@ -107,15 +107,9 @@ def _summary_fields(path: str) -> dict:
 
 def stored_traffic(workload: str):
     """HBM bytes per pass-1 launch from the committed counter summary
-    (profiles/attn_fwd_<workload>_hbm_traffic.md), or None when there is
-    none or the kernel sources changed since the counters were taken."""
-    fields = _summary_fields(os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_traffic.md"))
-    if fields.get("source_sha256") != source_digest("attn_fwd"):
-        return None
-    try:
-        return int(fields["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    (profiles/attn_fwd_<workload>_counters.md), or None when there is none
+    or the kernel sources changed since the counters were taken."""
+    return (stored_counters("attn_fwd", workload) or {}).get("traffic_bytes_per_launch")
 
 
 def stored_counters(tag: str, workload: str):
@@ -615,11 +609,16 @@ def measure_workload(name, args, loops=LOOPS, with_cpu=False, spread=True):
             "target": POST_TARGET, "target_met": g / PEAK_HBM_GBS >= POST_TARGET,
             "per_launch_bytes": post_bytes, "avg_launch_us": ms["posterior"] * 1e3,
             "counters": stored_counters("posterior", name)}
-    # executed MFMA FLOPs per launch (profiler counter) over the live time
-    for key, ms_key in (("attention_pass1", "pass1"), ("attention_passes_1_2", "passes12")):
-        c = (rec.get(key) or {}).get("counters")
-        if c and "executed_mfma_flops_per_launch" in c:
-            t = c["executed_mfma_flops_per_launch"] / (ms[ms_key] * 1e-3) / 1e12
+    # executed bf16 MFMA FLOPs per call (profiler counters) over the live time
+    c1 = (rec.get("attention_pass1") or {}).get("counters") or {}
+    c2 = (rec.get("attention_passes_1_2") or {}).get("counters") or {}
+    f1 = c1.get("executed_mfma_flops_per_launch")
+    f2 = c2.get("executed_mfma_flops_per_launch")
+    for key, ms_key, flops in (("attention_pass1", "pass1", f1),
+                               ("attention_passes_1_2", "passes12", f1 + f2 if f1 and f2 else None)):
+        if key in rec and flops:
+            t = flops / (ms[ms_key] * 1e-3) / 1e12
+            rec[key]["executed_mfma_flops"] = flops
             rec[key]["executed_tflops"] = t
             rec[key]["executed_frac"] = t / PEAK_BF16_TFLOPS
     if with_cpu:
@@ -647,6 +646,67 @@ def dominant_roofline(rec) -> dict:
     return r
 
 
+def _pmc_per_dispatch(path, kernel_re):
+    """{(kernel, dispatch): {counter: value summed over instances}} of the
+    dispatches whose kernel name matches kernel_re."""
+    import re
+    per = {}
+    for r in _read_csv(path):
+        if not re.search(kernel_re, r["Kernel_Name"]):
+            continue
+        d = per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def _per_launch(per, counter):
+    """Per launch: the median over dispatches of each matching kernel, summed
+    over the kernels (a launch of the posterior is its stream and finish)."""
+    import statistics
+    by = {}
+    for (k, _), c in per.items():
+        if counter in c:
+            by.setdefault(k, []).append(c[counter])
+    return sum(statistics.median(v) for v in by.values())
+
+
+def counter_fields(tag, kernel_re, sq=None, fetch=None, write=None, copy_fetch=None, copy_write=None,
+                   copy_bytes=256 << 20) -> str:
+    """The machine-read lines of a profiles/<tag>_<workload>_counters.md
+    summary from rocprofv3 counter_collection.csv files: executed bf16 MFMA
+    FLOPs (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), MFMA-busy cycles, VALU
+    instructions per MFMA, co-issue and dependency-wait shares (one SQ pass);
+    HBM bytes from FETCH_SIZE and WRITE_SIZE (KiB), each scaled by what it
+    reads for a plain device copy of copy_bytes."""
+    lines = [f"- source_sha256: `{source_digest(tag)}`"]
+    if sq:
+        per = _pmc_per_dispatch(sq, kernel_re)
+        lines.append("- kernel: `" + "`, `".join(sorted({k for k, _ in per})) + "`")
+        mops = _per_launch(per, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        busy = _per_launch(per, "SQ_VALU_MFMA_BUSY_CYCLES")
+        mfma = _per_launch(per, "SQ_INSTS_MFMA")
+        valu = _per_launch(per, "SQ_INSTS_VALU")
+        lines += [f"- executed_mfma_flops_per_launch: {int(round(mops * 512))}",
+                  f"- mfma_busy_cycles_per_launch: {int(round(busy))}",
+                  # busy cycles spread over the 1024 SIMDs at the 2.4 GHz nameplate clock
+                  f"- mfma_busy_us_at_nameplate: {busy / 1024 / 2.4e3:.2f}",
+                  f"- valu_per_mfma: {valu / mfma:.3f}",
+                  f"- coexec_frac_of_mfma_busy: "
+                  f"{_per_launch(per, 'SQ_VALU_MFMA_COEXEC_CYCLES') / busy:.3f}",
+                  f"- wait_frac_of_wave_cycles: "
+                  f"{_per_launch(per, 'SQ_WAIT_INST_ANY') / _per_launch(per, 'SQ_WAVE_CYCLES'):.3f}"]
+    if fetch and write and copy_fetch and copy_write:
+        kib = copy_bytes / 1024
+        fs = kib / _per_launch(_pmc_per_dispatch(copy_fetch, "copyBuffer"), "FETCH_SIZE")
+        ws = kib / _per_launch(_pmc_per_dispatch(copy_write, "copyBuffer"), "WRITE_SIZE")
+        f_kib = _per_launch(_pmc_per_dispatch(fetch, kernel_re), "FETCH_SIZE")
+        w_kib = _per_launch(_pmc_per_dispatch(write, kernel_re), "WRITE_SIZE")
+        lines += [f"- fetch_scale: {fs:.4f}", f"- write_scale: {ws:.4f}",
+                  f"- fetch_kib_per_launch: {f_kib:.0f}", f"- write_kib_per_launch: {w_kib:.0f}",
+                  f"- traffic_bytes_per_launch: {int(round((f_kib * fs + w_kib * ws) * 1024))}"]
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -665,6 +725,9 @@ def main():
                     help="summarise a rocprofv3 kernel_trace.csv (per-kernel mean / median) and exit")
     ap.add_argument("--summarize-pmc", metavar="CSV",
                     help="summarise a rocprofv3 counter_collection.csv (per kernel and counter) and exit")
+    ap.add_argument("--counter-fields", nargs="+", metavar="ARG",
+                    help="TAG KERNEL_RE [sq=CSV] [fetch=CSV write=CSV copy_fetch=CSV copy_write=CSV]: print "
+                         "the machine-read lines of a counter summary and exit")
     ap.add_argument("--loop", action="store_true",
                     help="time a whole multi-step SureLock run instead (its own JSON line)")
     ap.add_argument("--layer", action="store_true",
@@ -681,6 +744,10 @@ def main():
         return
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc))
+        return
+    if args.counter_fields:
+        tag, kre, *kv = args.counter_fields
+        print(counter_fields(tag, kre, **dict(x.split("=", 1) for x in kv)))
         return
     if args.copy_probe:
         copy_probe()

@@ -15,6 +15,9 @@ from . import (KVCache, MaskDesc, Select, dlm_posterior, dlm_posterior_workspace
                dlm_step_attn, dlm_step_attn_workspace_bytes)
 
 
+_SIDE_STREAMS = {}
+
+
 def bf16_to_device(bits: np.ndarray, device) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16))
     return t.to(device).view(torch.bfloat16)
@@ -114,7 +117,11 @@ class DeviceStep:
             return
         main = stream if stream is not None else torch.cuda.current_stream()
         if not hasattr(self, "_side"):
-            self._side = torch.cuda.Stream()
+            # one side stream per device, shared by every step object: many
+            # streams would spread over the few hardware queues
+            if main.device not in _SIDE_STREAMS:
+                _SIDE_STREAMS[main.device] = torch.cuda.Stream(device=main.device)
+            self._side = _SIDE_STREAMS[main.device]
             self._ev_start, self._ev_cs, self._ev_post = (torch.cuda.Event() for _ in range(3))
         self._ev_start.record(main)
         self._side.wait_event(self._ev_start)      # prior work on the calling stream first

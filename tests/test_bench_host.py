@@ -84,8 +84,8 @@ def test_stored_traffic_is_dropped_when_the_pass1_sources_change(tmp_path, monke
         f.write_text("source " + rel + "\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     (tmp_path / "profiles").mkdir()
-    summary = tmp_path / "profiles" / "attn_fwd_w_hbm_traffic.md"
-    summary.write_text("# counters\n\n- kernel: `k`\n- workload: `w`\n"
+    summary = tmp_path / "profiles" / "attn_fwd_w_counters.md"
+    summary.write_text("# counters\n\n- kernel: `k`\n"
                        f"- source_sha256: `{bench.source_digest()}`\n"
                        "- traffic_bytes_per_launch: 12345\n")
     assert bench.stored_traffic("w") == 12345
