@@ -191,6 +191,12 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(AttnArgs a)
 // ---------------------------------------------------------------------------
 constexpr float kRescaleLog2 = 8.f;
 
+// Ping-pong schedule of the one-key-group pass-1 shape (see the tile loop).
+#ifndef DLM_ATTN_PINGPONG
+#define DLM_ATTN_PINGPONG 1
+#endif
+constexpr bool kPingPong = DLM_ATTN_PINGPONG != 0;
+
 // Query waves of a one-key-group pass-1 workgroup (32 rows each).
 #ifndef DLM_ATTN_QW1
 #define DLM_ATTN_QW1 8
@@ -227,6 +233,8 @@ __device__ __forceinline__ int v_swz(int r)
     return D == 128 ? (4 * i) ^ (2 * par) : D == 64 ? 2 * i : 2 * par;
 }
 
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 // Max over the two half-waves (lanes l and l ^ 32 hold the same query):
 // v_permlane32_swap hands each half the other's values without LDS.
 __device__ __forceinline__ float half_swap_max(float v)
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(1024))) uint16_t Ks1[KT * D];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs0[KT * D];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs1[KT * D];
-    __shared__ int kcode_s[2][KT];
+    __shared__ int kcode_s[NG == 1 && kPingPong ? 4 : 2][KT];   // key codes of partial tiles
     __shared__ int scode_s[kMaxSlots];
     __shared__ int qrange_s[2][QW];                    // each query wave's smallest / largest code
     __shared__ float ml_s[NG == 2 ? 4 * 4 * 64 : 1];   // each key group's running max and sum
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     // later block or group) is not fetched: its out-of-range offset reads
     // zeros, and the predicate masks it anyway.  Other tiles take the plain
     // loop.
-    auto issue_k = [&](int t0, int buf, bool part) {
+    auto issue_k = [&](int t0, int buf, bool part, int kslot) {
         uint16_t *ks = buf ? Ks1 : Ks0;
         if (part && a.kind != 0) {
             for (int u = 0; u < NLD; ++u) {
@@ -427,7 +435,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
             }
         }
-        if (part && tid < KT) kcode_s[buf][tid] = key_code_lds(t0 + tid);
+        if (part && tid < KT) kcode_s[kslot][tid] = key_code_lds(t0 + tid);
     };
     auto issue_v = [&](int t0, int buf, bool part) {
         uint16_t *vs = buf ? Vs1 : Vs0;
@@ -457,7 +465,11 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         v_rd[dt] = row * D + ((chunk ^ v_swz<D>(row)) * 8) + (s16 & 1) * 4;
     }
 
-    float m_run = -INFINITY, l_run = 0.f;
+    // Running max and sum; m_use is the exponent offset (the running max,
+    // 0 before the lane's first visible key) and g_thr how far a tile's
+    // max may pass it before O and l are rescaled (any finite max at the
+    // first visible key, kRescaleLog2 afterwards).
+    float m_run = -INFINITY, l_run = 0.f, m_use = 0.f, g_thr = -INFINITY;
     f32x16 o[DT];
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
@@ -499,14 +511,13 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         __builtin_amdgcn_sched_group_barrier(0x008, DK >= 2 ? 4 : 2, 0);
     };
 
-    // Mask, then the exponent arguments u = s * scale * log2(e) - m_use (the
-    // running max, 0 before the first visible key) and their max: taking
-    // the max of FMA results rather than raw MFMA outputs spares the NaN
-    // canonicalisation of every input.  The running max moves only when
-    // the tile's max exceeds it by more than kRescaleLog2, or at the lane's
-    // first visible key; then O and l are rescaled and u shifted.
-    auto prep = [&](f32x16 &s0, f32x16 &s1, const int *kc, bool all_vis, float (&u0)[16],
-                    float (&u1)[16]) {
+    // Mask, then the exponent arguments u = s * scale * log2(e) - m_use
+    // (written over the scores) and their max: taking the max of FMA results rather than raw MFMA outputs
+    // spares the NaN canonicalisation of every input.  The running max
+    // moves only when the tile's max exceeds g_thr (more than kRescaleLog2
+    // above it, or any visible key at the lane's first); then O and l are
+    // rescaled and u shifted.
+    auto prep = [&](f32x16 &s0, f32x16 &s1, const int *kc, bool all_vis) {
         if (!all_vis) {
             for (int i = 0; i < 16; ++i) {
                 const int key = 16 * (i >> 3) + 8 * hh + (i & 7);
@@ -514,21 +525,33 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
                 if (kc[32 + key] > qcode) s1[i] = -INFINITY;
             }
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        f32x16 &u0 = s0, &u1 = s1;       // the arguments replace the scores in place
         for (int i = 0; i < 16; ++i) {
             u0[i] = fmaf(s0[i], c2, -m_use);
             u1[i] = fmaf(s1[i], c2, -m_use);
         }
-        float tmax = fmaxf(u0[0], u1[0]);
-        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, fmaxf(u0[i], u1[i]));
-        tmax = half_swap_max(tmax);
-        const bool grow = m_run == -INFINITY ? tmax != -INFINITY : tmax > kRescaleLog2;
+        // the max of the 32 arguments as a tree of 3-input maxima (16 ops)
+        float t1[12];
+        for (int k = 0; k < 5; ++k) {
+            t1[k] = max3f(u0[3 * k], u0[3 * k + 1], u0[3 * k + 2]);
+            t1[5 + k] = max3f(u1[3 * k], u1[3 * k + 1], u1[3 * k + 2]);
+        }
+        t1[10] = u0[15];
+        t1[11] = u1[15];
+        const float t2[4] = {max3f(t1[0], t1[1], t1[2]), max3f(t1[3], t1[4], t1[5]), max3f(t1[6], t1[7], t1[8]),
+                             max3f(t1[9], t1[10], t1[11])};
+        const float tmax = half_swap_max(fmaxf(max3f(t2[0], t2[1], t2[2]), t2[3]));
+        const bool grow = tmax > g_thr;
         if (__any(grow)) {
             const float d = grow ? tmax : 0.f;                 // new max - m_use
             const float alpha = grow ? fast_exp2(m_run - (m_use + d)) : 1.f;   // 0 when m_run = -inf
             for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
             l_run *= alpha;
-            if (grow) m_run = m_use + d;
+            if (grow) {
+                m_run = m_use + d;
+                m_use = m_run;
+                g_thr = kRescaleLog2;
+            }
             for (int i = 0; i < 16; ++i) {
                 u0[i] -= d;
                 u1[i] -= d;
@@ -548,7 +571,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         constexpr int BUF = decltype(bufc)::value;
         if (t0 + KT < kend) {
             const bool part = partial_tile(t0 + KT);
-            issue_k(t0 + KT, BUF ^ 1, part);
+            issue_k(t0 + KT, BUF ^ 1, part, BUF ^ 1);
             issue_v(t0 + KT, BUF ^ 1, part);
         }
         bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
@@ -564,8 +587,8 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
             const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
             f32x16 s0, s1;
             qk(ks, s0, s1);
-            float u0[16], u1[16];
-            prep(s0, s1, kcode_s[BUF] + kofs, vis, u0, u1);
+            prep(s0, s1, kcode_s[BUF] + kofs, vis);
+            const f32x16 &u0 = s0, &u1 = s1;
             float psum = 0.f;
             bf16x8 p0[2], p1[2];
             for (int i = 0; i < 16; ++i) {
@@ -620,16 +643,131 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         kbeg = __builtin_amdgcn_readfirstlane(kbeg);
         kend = __builtin_amdgcn_readfirstlane(kend);
     }
-    if (kbeg < kend) {
-        const bool part = partial_tile(kbeg);
-        issue_k(kbeg, 0, part);
-        issue_v(kbeg, 0, part);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int t0 = kbeg; t0 < kend; t0 += 2 * KT) {
-        tile_step(std::integral_constant<int, 0>{}, t0);
-        if (t0 + KT < kend) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
+    if constexpr (NG == 1 && kPingPong) {
+        // Ping-pong.  Waves [0, QW/2) (group A) and [QW/2, QW) (group B) run
+        // the same sequence of tiles one phase apart.  A phase is either all
+        // MFMA (PV of tile j - 1 and QK of tile j) or all VALU (the softmax of
+        // tile j), so on every SIMD one wave's matrix work overlaps the other
+        // wave's vector work.  LDS slot j (buffer j % 2) holds K(j) and
+        // V(j - 1): group A uses it in phase 2j, group B in phase 2j + 1;
+        // slot j + 2 is loaded from the start of phase 2j + 2 and waited for
+        // at the end of phase 2j + 3.  Key codes of partial tiles go to a
+        // ring of four (tile j's are read up to phase 2j + 2).
+        const int grp = wid >= QW / 2 ? 1 : 0;
+        const int T = (kend - kbeg + KT - 1) / KT;
+        f32x16 s0 = f32x16{}, s1 = f32x16{};   // S^T of the tile between its QK and softmax phases
+        bf16x8 p0[2], p1[2];                   // P of the tile between its softmax and PV phases
+        auto load_slot = [&](auto bufc, int js) __attribute__((always_inline)) {
+            constexpr int SB = decltype(bufc)::value;
+            if (js < T) {
+                const int t0 = kbeg + js * KT;
+                issue_k(t0, SB, partial_tile(t0), js & 3);
+            }
+            if (js >= 1 && js <= T) {
+                const int t0 = kbeg + (js - 1) * KT;
+                issue_v(t0, SB, partial_tile(t0));
+            }
+        };
+        auto mfma_phase = [&](auto bufc, int jq) __attribute__((always_inline)) {   // PV of tile jq - 1, QK of tile jq (slot jq)
+            constexpr int SB = decltype(bufc)::value;
+            const uint16_t *ks = SB ? Ks1 : Ks0;
+            const uint16_t *vs = SB ? Vs1 : Vs0;
+            if (jq >= 1 && jq <= T) {
+                for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
+                for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
+            }
+            if (jq < T) qk(ks, s0, s1);
+        };
+        auto softmax_phase = [&](int jq) __attribute__((always_inline)) {           // tile jq: P and the running max and sum
+            if (jq >= T) return;
+            const int t0 = kbeg + jq * KT;
+            bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
+            if (!vis) {
+                int kmn, kmx;
+                key_range(t0, KT, kmn, kmx);
+                vis = kmx <= qmin;
+            }
+            prep(s0, s1, kcode_s[jq & 3], vis);
+            float psum = 0.f;
+            for (int i = 0; i < 16; ++i) {
+                const float e = fast_exp2(s0[i]);
+                psum += e;
+                p0[i >> 3][i & 7] = (__bf16)e;
+            }
+            for (int i = 0; i < 16; ++i) {
+                const float e = fast_exp2(s1[i]);
+                psum += e;
+                p1[i >> 3][i & 7] = (__bf16)e;
+            }
+            l_run += psum;
+        };
+        // Barriers ending a phase: after an even (global) phase the slot loads
+        // issued at its start stay in flight; after an odd one they have
+        // landed.
+        auto bar_nowait = [&]() __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        auto bar_wait = [&]() __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        load_slot(std::integral_constant<int, 0>{}, 0);
+        load_slot(std::integral_constant<int, 1>{}, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // Each group runs its own loop over local phases 2jq (MFMA, slot jq)
+        // and 2jq + 1 (softmax of tile jq); group B is one phase behind, so
+        // global phase p is A's phase p and B's phase p - 1.  Global phase
+        // 2s - 2 (s >= 2) issues slot s: A at the start of its MFMA phase
+        // s - 1, B at the start of its softmax phase s - 2.  Both groups end
+        // after 2T + 2 barriers.  Unrolled by two tiles so every LDS buffer
+        // index is a constant.
+        if (grp == 0) {
+            for (int jq = 0; jq <= T; jq += 2) {
+                if (jq >= 1) load_slot(std::integral_constant<int, 1>{}, jq + 1);
+                mfma_phase(std::integral_constant<int, 0>{}, jq);
+                bar_nowait();
+                softmax_phase(jq);
+                bar_wait();
+                if (jq + 1 > T) break;
+                load_slot(std::integral_constant<int, 0>{}, jq + 2);
+                mfma_phase(std::integral_constant<int, 1>{}, jq + 1);
+                bar_nowait();
+                softmax_phase(jq + 1);
+                bar_wait();
+            }
+        } else {
+            bar_nowait();   // global phase 0
+            for (int jq = 0; jq <= T; jq += 2) {
+                mfma_phase(std::integral_constant<int, 0>{}, jq);
+                bar_wait();
+                if (jq == T) break;
+                load_slot(std::integral_constant<int, 0>{}, jq + 2);
+                softmax_phase(jq);
+                bar_nowait();
+                mfma_phase(std::integral_constant<int, 1>{}, jq + 1);
+                bar_wait();
+                if (jq + 1 == T) break;
+                load_slot(std::integral_constant<int, 1>{}, jq + 3);
+                softmax_phase(jq + 1);
+                bar_nowait();
+            }
+        }
+    } else {
+        if (kbeg < kend) {
+            const bool part = partial_tile(kbeg);
+            issue_k(kbeg, 0, part, 0);
+            issue_v(kbeg, 0, part);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int t0 = kbeg; t0 < kend; t0 += 2 * KT) {
+            tile_step(std::integral_constant<int, 0>{}, t0);
+            if (t0 + KT < kend) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
+        }
     }
 
     // Finish the rows: with two key groups, the groups first merge their
