@@ -243,7 +243,7 @@ __device__ __forceinline__ float half_swap_max(float v)
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, int NG, int QW>
+template <int D, int NG, int QW, bool DYN>
 __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
 {
     constexpr int KT = 64 * NG;          // keys per LDS tile; key group kg takes [64kg, 64kg + 64)
@@ -272,592 +272,626 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
     const int wq = NG == 2 ? wid & 3 : wid;  // query wave
     const int kofs = 64 * kg;                // this group's first key in a tile
 
-    int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt = L % a.n_qtiles;
-    L /= a.n_qtiles;
-    const int split = L % a.n_split;
-    const int bg = L / a.n_split;
-    const int b = bg / a.Hkv, g = bg % a.Hkv;
-    // With a device row count, a tile past the valid rows has nothing to do
-    // (the whole workgroup leaves before its first barrier).
-    const int Mv = valid_rows(a, b);
-    if (qt * (32 * QW) >= a.G * Mv) return;
-
-    const uint8_t *st = a.kind == 2 ? a.slot_state + (long)b * a.n_slots : nullptr;
-    const int32_t *gr = a.kind == 2 ? a.slot_group + (long)b * a.n_slots : nullptr;
-    if (a.kind == 2) {
-        for (int s = tid; s < a.n_slots; s += NT) scode_s[s] = st[s] == 0 ? INT_MAX : gr[s];
-    }
-    // Zero the tiles once, so no LDS byte a tile does not overwrite can
-    // ever be a non-finite value times a zero weight.  Only a ragged last
-    // tile (rows past kv_len) or rows hidden from the whole workgroup
-    // (block-causal and group masks) take the out-of-range path; split
-    // boundaries are whole tiles, so otherwise every row of every tile is
-    // loaded.
-    const bool ragged = a.kv_len % KT != 0 || a.kind != 0;
-    for (int i = tid; ragged && i < KT * D / 8; i += NT) {
-        reinterpret_cast<uint4 *>(Ks0)[i] = uint4{0, 0, 0, 0};
-        reinterpret_cast<uint4 *>(Ks1)[i] = uint4{0, 0, 0, 0};
-        reinterpret_cast<uint4 *>(Vs0)[i] = uint4{0, 0, 0, 0};
-        reinterpret_cast<uint4 *>(Vs1)[i] = uint4{0, 0, 0, 0};
-    }
-
-    // This lane's query: packed row r = hl * Mv + j over the Mv valid rows
-    // (the row stride in memory stays M).
-    const int rows_bg = a.G * Mv;
-    const int r = qt * (32 * QW) + wq * 32 + l32;
-    const bool rv = r < rows_bg;
-    const int hl = rv ? r / Mv : 0;
-    const int j = rv ? r - hl * Mv : 0;
-    const int h = g * a.G + hl;
-    const int pos = a.active_idx[(long)b * a.M + j];
-    const int qcode = rv ? query_code(a, gr, pos) : INT_MIN;
-    // The workgroup's query-code range over its valid rows: a key tile
-    // whose smallest code exceeds qmax is hidden from every row and
-    // skipped; one whose largest code is at most qmin is visible to every
-    // row and runs without the predicate; any other tile is partial and
-    // runs the per-key predicate.  Each query wave reduces its rows with
-    // shuffles and leaves its range in LDS for the first barrier.
-    int qmin = 0, qmax = 0;
-    if (a.kind != 0) {
-        int mn = rv ? qcode : INT_MAX, mx = rv ? qcode : INT_MIN;
-        for (int o = 32; o >= 1; o >>= 1) {
-            mn = min(mn, __shfl_xor(mn, o));
-            mx = max(mx, __shfl_xor(mx, o));
+    // Work items: (query tile, key split, batch entry, kv-head).  A planned
+    // launch runs one item per workgroup, ordered so that the workgroups
+    // sharing K/V run on one XCD.  With a device-decided split the grid is
+    // one workgroup per CU, and each walks the active items of every batch
+    // entry (their query tiles and splits follow the device row counts), so
+    // no workgroup is dispatched for a tile or split that is not used.
+    // (DYN is a template parameter: a planned launch compiles to one pass
+    // through the body.)
+    for (int it = 0, item = blockIdx.x; DYN || it == 0; ++it, item += gridDim.x) {
+        int qt = 0, split = 0, b = 0, g = 0;
+        if constexpr (!DYN) {
+            int L = xcd_remap(item, gridDim.x);
+            qt = L % a.n_qtiles;
+            L /= a.n_qtiles;
+            split = L % a.n_split;
+            L /= a.n_split;
+            b = L / a.Hkv;
+            g = L % a.Hkv;
+        } else {
+            int rem = item;
+            for (; b < a.B; ++b) {
+                const int qtb = (a.G * valid_rows(a, b) + 32 * QW - 1) / (32 * QW);
+                const int nsb = splits_for(a, b);
+                if (rem < a.Hkv * qtb * nsb) {
+                    qt = rem % qtb;
+                    rem /= qtb;
+                    split = rem % nsb;
+                    g = rem / nsb;
+                    break;
+                }
+                rem -= a.Hkv * qtb * nsb;
+            }
+            if (b == a.B) break;
         }
-        if (kg == 0 && lane == 0) {
-            qrange_s[0][wq] = mn;
-            qrange_s[1][wq] = mx;
+        const int bg = b * a.Hkv + g;
+        // With a device row count, a tile past the valid rows, or a split this
+        // batch entry does not use, has nothing to do.
+        const int Mv = valid_rows(a, b);
+        const int ns = splits_for(a, b);
+        if (qt * (32 * QW) >= a.G * Mv || split >= ns) continue;
+        const int split_keys = ns == a.n_split ? a.split_keys : (a.kv_len + 64 * NG * ns - 1) / (64 * NG * ns) * 64 * NG;
+
+        const uint8_t *st = a.kind == 2 ? a.slot_state + (long)b * a.n_slots : nullptr;
+        const int32_t *gr = a.kind == 2 ? a.slot_group + (long)b * a.n_slots : nullptr;
+        if (a.kind == 2) {
+            for (int s = tid; s < a.n_slots; s += NT) scode_s[s] = st[s] == 0 ? INT_MAX : gr[s];
         }
-    }
-
-    bf16x8 qf[DK];
-    {
-        const uint16_t *qrow = a.q + ((long)(b * a.Hq + h) * a.M + j) * D;
-        for (int kk = 0; kk < DK; ++kk) {
-            if (rv) qf[kk] = *reinterpret_cast<const bf16x8 *>(qrow + kk * 16 + hh * 8);
-            else qf[kk] = bf16x8{};
+        // Zero the tiles once, so no LDS byte a tile does not overwrite can
+        // ever be a non-finite value times a zero weight.  Only a ragged last
+        // tile (rows past kv_len) or rows hidden from the whole workgroup
+        // (block-causal and group masks) take the out-of-range path; split
+        // boundaries are whole tiles, so otherwise every row of every tile is
+        // loaded.
+        const bool ragged = a.kv_len % KT != 0 || a.kind != 0;
+        for (int i = tid; ragged && i < KT * D / 8; i += NT) {
+            reinterpret_cast<uint4 *>(Ks0)[i] = uint4{0, 0, 0, 0};
+            reinterpret_cast<uint4 *>(Ks1)[i] = uint4{0, 0, 0, 0};
+            reinterpret_cast<uint4 *>(Vs0)[i] = uint4{0, 0, 0, 0};
+            reinterpret_cast<uint4 *>(Vs1)[i] = uint4{0, 0, 0, 0};
         }
-    }
 
-    const int k0 = split * a.split_keys;
-    const int k1 = min(a.kv_len, k0 + a.split_keys);
-    int kbeg = k0, kend = k1;        // the split's live tiles (set after the first barrier)
-    const uint16_t *kbase = a.ck + (long)bg * a.n_cap * D;
-    const uint16_t *vbase = a.cv + (long)bg * a.n_cap * D;
-    const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * ROWB);
-    const __amdgpu_buffer_rsrc_t vrs = buffer_view(vbase, a.kv_len * ROWB);
-    const float c2 = a.scale_log2;
+        // This lane's query: packed row r = hl * Mv + j over the Mv valid rows
+        // (the row stride in memory stays M).
+        const int rows_bg = a.G * Mv;
+        const int r = qt * (32 * QW) + wq * 32 + l32;
+        const bool rv = r < rows_bg;
+        const int hl = rv ? r / Mv : 0;
+        const int j = rv ? r - hl * Mv : 0;
+        const int h = g * a.G + hl;
+        const int pos = a.active_idx[(long)b * a.M + j];
+        const int qcode = rv ? query_code(a, gr, pos) : INT_MIN;
+        // The workgroup's query-code range over its valid rows: a key tile
+        // whose smallest code exceeds qmax is hidden from every row and
+        // skipped; one whose largest code is at most qmin is visible to every
+        // row and runs without the predicate; any other tile is partial and
+        // runs the per-key predicate.  Each query wave reduces its rows with
+        // shuffles and leaves its range in LDS for the first barrier.
+        int qmin = 0, qmax = 0;
+        if (a.kind != 0) {
+            int mn = rv ? qcode : INT_MAX, mx = rv ? qcode : INT_MIN;
+            for (int o = 32; o >= 1; o >>= 1) {
+                mn = min(mn, __shfl_xor(mn, o));
+                mx = max(mx, __shfl_xor(mx, o));
+            }
+            if (kg == 0 && lane == 0) {
+                qrange_s[0][wq] = mn;
+                qrange_s[1][wq] = mx;
+            }
+        }
 
-    // Direct-load geometry of this thread: load u writes 16 bytes at LDS
-    // byte (wid*NLD + u)*1024 + lane*16 of a tile, i.e. row lr, position lp.
-    int ld_row[NLD], k_goff[NLD], v_goff[NLD];
-    for (int u = 0; u < NLD; ++u) {
-        const int byte = (wid * NLD + u) * 1024 + lane * 16;
-        const int lr = byte / ROWB, lp = (byte % ROWB) / 16;
-        ld_row[u] = lr;
-        const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));   // sigma(lr)
-        k_goff[u] = (kkey * D + ((lp ^ k_swz<D>(lr)) * 8)) * 2;
-        v_goff[u] = (lr * D + ((lp ^ v_swz<D>(lr)) * 8)) * 2;
-    }
-    // key_code from the slot codes staged in LDS: no global load, so the
-    // only loads in flight in the tile loop are the tile loads themselves.
-    auto key_code_lds = [&](int n) -> int {
-        if (n >= a.kv_len) return INT_MAX;
-        if (a.kind == 0 || n < a.P) return INT_MIN;
-        const int sl = (n - a.P) / a.bs;
-        if (a.kind == 1) return sl;
-        return sl < a.n_slots ? scode_s[sl] : INT_MAX;
-    };
-    // Smallest and largest key code over keys [t0, t0 + len), keys at or
-    // past kv_len counting as INT_MAX, from the staged slot codes (uniform
-    // across the workgroup).  A group-mask range spanning more than eight
-    // slots reports the widest range, i.e. a partial tile.
-    auto key_range = [&](int t0, int len, int &kmn, int &kmx) {
-        const int hi = min(t0 + len, a.kv_len);
-        kmn = INT_MAX;
-        kmx = t0 + len > a.kv_len ? INT_MAX : INT_MIN;
-        if (t0 < hi) {
-            if (a.kind == 0 || t0 < a.P) kmn = INT_MIN;
-            const int lo = max(t0, a.P);
-            if (a.kind != 0 && lo < hi) {
-                const int s0 = (lo - a.P) / a.bs, s1 = (hi - 1 - a.P) / a.bs;
-                if (a.kind == 1) {
-                    kmn = min(kmn, s0);
-                    kmx = max(kmx, s1);
-                } else if (s1 - s0 >= 8) {
-                    kmn = INT_MIN;
-                    kmx = INT_MAX;
-                } else {
-                    for (int sl = s0; sl <= s1; ++sl) {
-                        const int c = sl < a.n_slots ? scode_s[sl] : INT_MAX;
-                        kmn = min(kmn, c);
-                        kmx = max(kmx, c);
+        bf16x8 qf[DK];
+        {
+            const uint16_t *qrow = a.q + ((long)(b * a.Hq + h) * a.M + j) * D;
+            for (int kk = 0; kk < DK; ++kk) {
+                if (rv) qf[kk] = *reinterpret_cast<const bf16x8 *>(qrow + kk * 16 + hh * 8);
+                else qf[kk] = bf16x8{};
+            }
+        }
+
+        const int k0 = split * split_keys;
+        const int k1 = min(a.kv_len, k0 + split_keys);
+        int kbeg = k0, kend = k1;        // the split's live tiles (set after the first barrier)
+        const uint16_t *kbase = a.ck + (long)bg * a.n_cap * D;
+        const uint16_t *vbase = a.cv + (long)bg * a.n_cap * D;
+        const __amdgpu_buffer_rsrc_t krs = buffer_view(kbase, a.kv_len * ROWB);
+        const __amdgpu_buffer_rsrc_t vrs = buffer_view(vbase, a.kv_len * ROWB);
+        const float c2 = a.scale_log2;
+
+        // Direct-load geometry of this thread: load u writes 16 bytes at LDS
+        // byte (wid*NLD + u)*1024 + lane*16 of a tile, i.e. row lr, position lp.
+        int ld_row[NLD], k_goff[NLD], v_goff[NLD];
+        for (int u = 0; u < NLD; ++u) {
+            const int byte = (wid * NLD + u) * 1024 + lane * 16;
+            const int lr = byte / ROWB, lp = (byte % ROWB) / 16;
+            ld_row[u] = lr;
+            const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));   // sigma(lr)
+            k_goff[u] = (kkey * D + ((lp ^ k_swz<D>(lr)) * 8)) * 2;
+            v_goff[u] = (lr * D + ((lp ^ v_swz<D>(lr)) * 8)) * 2;
+        }
+        // key_code from the slot codes staged in LDS: no global load, so the
+        // only loads in flight in the tile loop are the tile loads themselves.
+        auto key_code_lds = [&](int n) -> int {
+            if (n >= a.kv_len) return INT_MAX;
+            if (a.kind == 0 || n < a.P) return INT_MIN;
+            const int sl = (n - a.P) / a.bs;
+            if (a.kind == 1) return sl;
+            return sl < a.n_slots ? scode_s[sl] : INT_MAX;
+        };
+        // Smallest and largest key code over keys [t0, t0 + len), keys at or
+        // past kv_len counting as INT_MAX, from the staged slot codes (uniform
+        // across the workgroup).  A group-mask range spanning more than eight
+        // slots reports the widest range, i.e. a partial tile.
+        auto key_range = [&](int t0, int len, int &kmn, int &kmx) {
+            const int hi = min(t0 + len, a.kv_len);
+            kmn = INT_MAX;
+            kmx = t0 + len > a.kv_len ? INT_MAX : INT_MIN;
+            if (t0 < hi) {
+                if (a.kind == 0 || t0 < a.P) kmn = INT_MIN;
+                const int lo = max(t0, a.P);
+                if (a.kind != 0 && lo < hi) {
+                    const int s0 = (lo - a.P) / a.bs, s1 = (hi - 1 - a.P) / a.bs;
+                    if (a.kind == 1) {
+                        kmn = min(kmn, s0);
+                        kmx = max(kmx, s1);
+                    } else if (s1 - s0 >= 8) {
+                        kmn = INT_MIN;
+                        kmx = INT_MAX;
+                    } else {
+                        for (int sl = s0; sl <= s1; ++sl) {
+                            const int c = sl < a.n_slots ? scode_s[sl] : INT_MAX;
+                            kmn = min(kmn, c);
+                            kmx = max(kmx, c);
+                        }
                     }
                 }
             }
-        }
-        kmn = __builtin_amdgcn_readfirstlane(kmn);
-        kmx = __builtin_amdgcn_readfirstlane(kmx);
-    };
-    // Whether the tile at t0 is partial: not visible to every row of the
-    // workgroup (a ragged tail, or block-causal / group keys some row does
-    // not see).  Only partial tiles stage key codes for the predicate and
-    // check their rows.
-    auto partial_tile = [&](int t0) -> bool {
-        if (t0 + KT <= a.P) return false;
-        int kmn, kmx;
-        key_range(t0, KT, kmn, kmx);
-        return kmx > qmin;
-    };
-    // Direct loads of the K (with its key codes) or V half of the tile at t0
-    // into LDS buffer buf.  In a partial block-causal or group tile, a row
-    // whose key is hidden from every row of the workgroup (a DUMMY slot, a
-    // later block or group) is not fetched: its out-of-range offset reads
-    // zeros, and the predicate masks it anyway.  Other tiles take the plain
-    // loop.
-    auto issue_k = [&](int t0, int buf, bool part, int kslot) {
-        uint16_t *ks = buf ? Ks1 : Ks0;
-        if (part && a.kind != 0) {
-            for (int u = 0; u < NLD; ++u) {
-                const int lr = ld_row[u];
-                const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));
-                const int ko = key_code_lds(t0 + kkey) > qmax ? OOB : k_goff[u] + t0 * ROWB;
-                lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
-            }
-        } else {
-            // (the offsets are named variables: with the expression as the
-            // builtin's argument, the host pass drops the kernel's stub)
-            for (int u = 0; u < NLD; ++u) {
-                lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
-                const int ko = k_goff[u] + t0 * ROWB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
-            }
-        }
-        if (part && tid < KT) kcode_s[kslot][tid] = key_code_lds(t0 + tid);
-    };
-    auto issue_v = [&](int t0, int buf, bool part) {
-        uint16_t *vs = buf ? Vs1 : Vs0;
-        if (part && a.kind != 0) {
-            for (int u = 0; u < NLD; ++u) {
-                const int vo = key_code_lds(t0 + ld_row[u]) > qmax ? OOB : v_goff[u] + t0 * ROWB;
-                lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
-            }
-        } else {
-            for (int u = 0; u < NLD; ++u) {
-                lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
-                const int vo = v_goff[u] + t0 * ROWB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
-            }
-        }
-    };
-
-    // Loop-invariant LDS read offsets (elements) of this lane.
-    int k_rd[DK];                                          // K chunk 2kk+hh of row l32
-    for (int kk = 0; kk < DK; ++kk) k_rd[kk] = l32 * D + (((2 * kk + hh) ^ k_swz<D>(l32)) * 8);
-    const int s16 = lane & 15, g16 = lane >> 4;
-    int v_rd[DT];                                          // column tile dt, first row of the group
-    for (int dt = 0; dt < DT; ++dt) {
-        const int chunk = 4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1);
-        const int row = 8 * (g16 >> 1) + (s16 >> 2);      // row mod 4 = s16 / 4
-        v_rd[dt] = row * D + ((chunk ^ v_swz<D>(row)) * 8) + (s16 & 1) * 4;
-    }
-
-    // Running max and sum; m_use is the exponent offset (the running max,
-    // 0 before the lane's first visible key) and g_thr how far a tile's
-    // max may pass it before O and l are rescaled (any finite max at the
-    // first visible key, kRescaleLog2 afterwards).
-    float m_run = -INFINITY, l_run = 0.f, m_use = 0.f, g_thr = -INFINITY;
-    f32x16 o[DT];
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
-
-    // O^T += V^T P^T over one 32-key sub-tile at vt: two transposed reads
-    // give keys 16t + 8hh + (0..7) of column 32dt + l32 (operand A).
-    auto pv_mfma = [&](const uint16_t *vt, int t, int dt, const bf16x8 &p) {
-        const uint16_t *vp = vt + 16 * t * D + v_rd[dt];
-        const s16x4 lo = lds_read_tr(vp);
-        const s16x4 hi = lds_read_tr(vp + 4 * D);
-        const s16x4 v8[2] = {lo, hi};
-        o[dt] = mfma32(*reinterpret_cast<const bf16x8 *>(v8), p, o[dt]);
-    };
-
-    // S^T of this group's two 32-key sub-tiles of a tile (K at ks), the two
-    // MFMA chains interleaved and the K fragments read two k-steps ahead.
-    auto qk = [&](const uint16_t *ks, f32x16 &s0, f32x16 &s1) {
-        s0 = f32x16{};
-        s1 = f32x16{};
-        bf16x8 r0[2], r1[2];
-        for (int kk = 0; kk < 2 && kk < DK; ++kk) {
-            r0[kk] = lds_frag(ks + k_rd[kk]);
-            r1[kk] = lds_frag(ks + 32 * D + k_rd[kk]);
-        }
-        for (int kk = 0; kk < DK; ++kk) {
-            const bf16x8 a0 = r0[kk & 1], a1 = r1[kk & 1];
-            if (kk + 2 < DK) {
-                r0[kk & 1] = lds_frag(ks + k_rd[kk + 2]);
-                r1[kk & 1] = lds_frag(ks + 32 * D + k_rd[kk + 2]);
-            }
-            s0 = mfma32(a0, qf[kk], s0);
-            s1 = mfma32(a1, qf[kk], s1);
-        }
-        // keep that order: 4 reads, then (2 MFMAs, 2 reads) ..., 4 MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, DK >= 2 ? 4 : 2, 0);
-        for (int kk = 0; kk + 2 < DK; ++kk) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, DK >= 2 ? 4 : 2, 0);
-    };
-
-    // Mask, then the exponent arguments u = s * scale * log2(e) - m_use
-    // (written over the scores) and their max: taking the max of FMA results rather than raw MFMA outputs
-    // spares the NaN canonicalisation of every input.  The running max
-    // moves only when the tile's max exceeds g_thr (more than kRescaleLog2
-    // above it, or any visible key at the lane's first); then O and l are
-    // rescaled and u shifted.
-    auto prep = [&](f32x16 &s0, f32x16 &s1, const int *kc, bool all_vis) {
-        if (!all_vis) {
-            for (int i = 0; i < 16; ++i) {
-                const int key = 16 * (i >> 3) + 8 * hh + (i & 7);
-                if (kc[key] > qcode) s0[i] = -INFINITY;
-                if (kc[32 + key] > qcode) s1[i] = -INFINITY;
-            }
-        }
-        f32x16 &u0 = s0, &u1 = s1;       // the arguments replace the scores in place
-        for (int i = 0; i < 16; ++i) {
-            u0[i] = fmaf(s0[i], c2, -m_use);
-            u1[i] = fmaf(s1[i], c2, -m_use);
-        }
-        // the max of the 32 arguments as a tree of 3-input maxima (16 ops)
-        float t1[12];
-        for (int k = 0; k < 5; ++k) {
-            t1[k] = max3f(u0[3 * k], u0[3 * k + 1], u0[3 * k + 2]);
-            t1[5 + k] = max3f(u1[3 * k], u1[3 * k + 1], u1[3 * k + 2]);
-        }
-        t1[10] = u0[15];
-        t1[11] = u1[15];
-        const float t2[4] = {max3f(t1[0], t1[1], t1[2]), max3f(t1[3], t1[4], t1[5]), max3f(t1[6], t1[7], t1[8]),
-                             max3f(t1[9], t1[10], t1[11])};
-        const float tmax = half_swap_max(fmaxf(max3f(t2[0], t2[1], t2[2]), t2[3]));
-        const bool grow = tmax > g_thr;
-        if (__any(grow)) {
-            const float d = grow ? tmax : 0.f;                 // new max - m_use
-            const float alpha = grow ? fast_exp2(m_run - (m_use + d)) : 1.f;   // 0 when m_run = -inf
-            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-            l_run *= alpha;
-            if (grow) {
-                m_run = m_use + d;
-                m_use = m_run;
-                g_thr = kRescaleLog2;
-            }
-            for (int i = 0; i < 16; ++i) {
-                u0[i] -= d;
-                u1[i] -= d;
-            }
-        }
-    };
-
-    // One tile: compute on LDS buffer BUF while tile t0 + KT streams into
-    // the other one.  BUF is a compile-time constant, so the compiler sees
-    // that the reads and the in-flight LDS loads touch different arrays and
-    // does not wait for the loads before reading.  The PV products of
-    // sub-tile 0 are interleaved with the exponentials of sub-tile 1.
-    // Prefix tiles and whole in-range tiles of a full mask are visible to
-    // every row; any other tile is classified by this key group's 64 keys:
-    // skipped when hidden from every row, no predicate when visible to all.
-    auto tile_step = [&](auto bufc, int t0) {
-        constexpr int BUF = decltype(bufc)::value;
-        if (t0 + KT < kend) {
-            const bool part = partial_tile(t0 + KT);
-            issue_k(t0 + KT, BUF ^ 1, part, BUF ^ 1);
-            issue_v(t0 + KT, BUF ^ 1, part);
-        }
-        bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
-        bool live = true;
-        if (!vis) {
+            kmn = __builtin_amdgcn_readfirstlane(kmn);
+            kmx = __builtin_amdgcn_readfirstlane(kmx);
+        };
+        // Whether the tile at t0 is partial: not visible to every row of the
+        // workgroup (a ragged tail, or block-causal / group keys some row does
+        // not see).  Only partial tiles stage key codes for the predicate and
+        // check their rows.
+        auto partial_tile = [&](int t0) -> bool {
+            if (t0 + KT <= a.P) return false;
             int kmn, kmx;
-            key_range(t0 + kofs, 64, kmn, kmx);
-            live = kmn <= qmax;
-            vis = kmx <= qmin;
-        }
-        if (live) {
-            const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
-            const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
-            f32x16 s0, s1;
-            qk(ks, s0, s1);
-            prep(s0, s1, kcode_s[BUF] + kofs, vis);
-            const f32x16 &u0 = s0, &u1 = s1;
-            float psum = 0.f;
-            bf16x8 p0[2], p1[2];
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(u0[i]);
-                psum += p;
-                p0[i >> 3][i & 7] = (__bf16)p;
-            }
-            constexpr int PER = 16 / (2 * DT);   // exps of sub-tile 1 per PV product
-            for (int q = 0; q < 2 * DT; ++q) {
-                pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
-                for (int e = 0; e < PER; ++e) {
-                    const int i = q * PER + e;
-                    const float p = fast_exp2(u1[i]);
-                    psum += p;
-                    p1[i >> 3][i & 7] = (__bf16)p;
+            key_range(t0, KT, kmn, kmx);
+            return kmx > qmin;
+        };
+        // Direct loads of the K (with its key codes) or V half of the tile at t0
+        // into LDS buffer buf.  In a partial block-causal or group tile, a row
+        // whose key is hidden from every row of the workgroup (a DUMMY slot, a
+        // later block or group) is not fetched: its out-of-range offset reads
+        // zeros, and the predicate masks it anyway.  Other tiles take the plain
+        // loop.
+        auto issue_k = [&](int t0, int buf, bool part, int kslot) {
+            uint16_t *ks = buf ? Ks1 : Ks0;
+            if (part && a.kind != 0) {
+                for (int u = 0; u < NLD; ++u) {
+                    const int lr = ld_row[u];
+                    const int kkey = (lr & ~31) | ((lr & 19) | ((lr & 4) << 1) | ((lr & 8) >> 1));
+                    const int ko = key_code_lds(t0 + kkey) > qmax ? OOB : k_goff[u] + t0 * ROWB;
+                    lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
+                }
+            } else {
+                // (the offsets are named variables: with the expression as the
+                // builtin's argument, the host pass drops the kernel's stub)
+                for (int u = 0; u < NLD; ++u) {
+                    lds_void *kd = (lds_void *)(ks + (wid * NLD + u) * 512);
+                    const int ko = k_goff[u] + t0 * ROWB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, kd, 16, ko, 0, 0, 0);
                 }
             }
-            l_run += psum;
-            for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile landed
-        __syncthreads();
-    };
+            if (part && tid < KT) kcode_s[kslot][tid] = key_code_lds(t0 + tid);
+        };
+        auto issue_v = [&](int t0, int buf, bool part) {
+            uint16_t *vs = buf ? Vs1 : Vs0;
+            if (part && a.kind != 0) {
+                for (int u = 0; u < NLD; ++u) {
+                    const int vo = key_code_lds(t0 + ld_row[u]) > qmax ? OOB : v_goff[u] + t0 * ROWB;
+                    lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
+                }
+            } else {
+                for (int u = 0; u < NLD; ++u) {
+                    lds_void *vd = (lds_void *)(vs + (wid * NLD + u) * 512);
+                    const int vo = v_goff[u] + t0 * ROWB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, vd, 16, vo, 0, 0, 0);
+                }
+            }
+        };
 
-    __syncthreads();   // slot codes, zeroed tiles and the query waves' code ranges visible
-    if (a.kind != 0) {
-        qmin = INT_MAX;
-        qmax = INT_MIN;
-        for (int w = 0; w < QW; ++w) {
-            qmin = min(qmin, qrange_s[0][w]);
-            qmax = max(qmax, qrange_s[1][w]);
+        // Loop-invariant LDS read offsets (elements) of this lane.
+        int k_rd[DK];                                          // K chunk 2kk+hh of row l32
+        for (int kk = 0; kk < DK; ++kk) k_rd[kk] = l32 * D + (((2 * kk + hh) ^ k_swz<D>(l32)) * 8);
+        const int s16 = lane & 15, g16 = lane >> 4;
+        int v_rd[DT];                                          // column tile dt, first row of the group
+        for (int dt = 0; dt < DT; ++dt) {
+            const int chunk = 4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+            const int row = 8 * (g16 >> 1) + (s16 >> 2);      // row mod 4 = s16 / 4
+            v_rd[dt] = row * D + ((chunk ^ v_swz<D>(row)) * 8) + (s16 & 1) * 4;
         }
-        qmin = __builtin_amdgcn_readfirstlane(qmin);
-        qmax = __builtin_amdgcn_readfirstlane(qmax);
-    }
-    // Leading and trailing tiles of the split that are hidden from every
-    // row (later blocks or groups, DUMMY slots past the last live one) are
-    // never visited: no loads, no MFMAs.  A hidden tile between live ones
-    // is visited, but its rows are not fetched and its MFMAs are skipped.
-    if (a.kind != 0) {
-        int kmn, kmx;
-        for (; kbeg < kend; kbeg += KT) {
-            key_range(kbeg, KT, kmn, kmx);
-            if (kmn <= qmax) break;
-        }
-        while (kend > kbeg) {
-            const int tl = kbeg + (kend - 1 - kbeg) / KT * KT;   // start of the last tile
-            key_range(tl, KT, kmn, kmx);
-            if (kmn <= qmax) break;
-            kend = tl;
-        }
-        kbeg = __builtin_amdgcn_readfirstlane(kbeg);
-        kend = __builtin_amdgcn_readfirstlane(kend);
-    }
-    if constexpr (NG == 1 && kPingPong) {
-        // Ping-pong.  Waves [0, QW/2) (group A) and [QW/2, QW) (group B) run
-        // the same sequence of tiles one phase apart.  A phase is either all
-        // MFMA (PV of tile j - 1 and QK of tile j) or all VALU (the softmax of
-        // tile j), so on every SIMD one wave's matrix work overlaps the other
-        // wave's vector work.  LDS slot j (buffer j % 2) holds K(j) and
-        // V(j - 1): group A uses it in phase 2j, group B in phase 2j + 1;
-        // slot j + 2 is loaded from the start of phase 2j + 2 and waited for
-        // at the end of phase 2j + 3.  Key codes of partial tiles go to a
-        // ring of four (tile j's are read up to phase 2j + 2).
-        const int grp = wid >= QW / 2 ? 1 : 0;
-        const int T = (kend - kbeg + KT - 1) / KT;
-        f32x16 s0 = f32x16{}, s1 = f32x16{};   // S^T of the tile between its QK and softmax phases
-        bf16x8 p0[2], p1[2];                   // P of the tile between its softmax and PV phases
-        auto load_slot = [&](auto bufc, int js) __attribute__((always_inline)) {
-            constexpr int SB = decltype(bufc)::value;
-            if (js < T) {
-                const int t0 = kbeg + js * KT;
-                issue_k(t0, SB, partial_tile(t0), js & 3);
+
+        // Running max and sum; m_use is the exponent offset (the running max,
+        // 0 before the lane's first visible key) and g_thr how far a tile's
+        // max may pass it before O and l are rescaled (any finite max at the
+        // first visible key, kRescaleLog2 afterwards).
+        float m_run = -INFINITY, l_run = 0.f, m_use = 0.f, g_thr = -INFINITY;
+        f32x16 o[DT];
+        for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+
+        // O^T += V^T P^T over one 32-key sub-tile at vt: two transposed reads
+        // give keys 16t + 8hh + (0..7) of column 32dt + l32 (operand A).
+        auto pv_mfma = [&](const uint16_t *vt, int t, int dt, const bf16x8 &p) {
+            const uint16_t *vp = vt + 16 * t * D + v_rd[dt];
+            const s16x4 lo = lds_read_tr(vp);
+            const s16x4 hi = lds_read_tr(vp + 4 * D);
+            const s16x4 v8[2] = {lo, hi};
+            o[dt] = mfma32(*reinterpret_cast<const bf16x8 *>(v8), p, o[dt]);
+        };
+
+        // S^T of this group's two 32-key sub-tiles of a tile (K at ks), the two
+        // MFMA chains interleaved and the K fragments read two k-steps ahead.
+        auto qk = [&](const uint16_t *ks, f32x16 &s0, f32x16 &s1) {
+            s0 = f32x16{};
+            s1 = f32x16{};
+            bf16x8 r0[2], r1[2];
+            for (int kk = 0; kk < 2 && kk < DK; ++kk) {
+                r0[kk] = lds_frag(ks + k_rd[kk]);
+                r1[kk] = lds_frag(ks + 32 * D + k_rd[kk]);
             }
-            if (js >= 1 && js <= T) {
-                const int t0 = kbeg + (js - 1) * KT;
-                issue_v(t0, SB, partial_tile(t0));
+            for (int kk = 0; kk < DK; ++kk) {
+                const bf16x8 a0 = r0[kk & 1], a1 = r1[kk & 1];
+                if (kk + 2 < DK) {
+                    r0[kk & 1] = lds_frag(ks + k_rd[kk + 2]);
+                    r1[kk & 1] = lds_frag(ks + 32 * D + k_rd[kk + 2]);
+                }
+                s0 = mfma32(a0, qf[kk], s0);
+                s1 = mfma32(a1, qf[kk], s1);
+            }
+            // keep that order: 4 reads, then (2 MFMAs, 2 reads) ..., 4 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, DK >= 2 ? 4 : 2, 0);
+            for (int kk = 0; kk + 2 < DK; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, DK >= 2 ? 4 : 2, 0);
+        };
+
+        // Mask, then the exponent arguments u = s * scale * log2(e) - m_use
+        // (written over the scores) and their max: taking the max of FMA results rather than raw MFMA outputs
+        // spares the NaN canonicalisation of every input.  The running max
+        // moves only when the tile's max exceeds g_thr (more than kRescaleLog2
+        // above it, or any visible key at the lane's first); then O and l are
+        // rescaled and u shifted.
+        auto prep = [&](f32x16 &s0, f32x16 &s1, const int *kc, bool all_vis) {
+            if (!all_vis) {
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 16 * (i >> 3) + 8 * hh + (i & 7);
+                    if (kc[key] > qcode) s0[i] = -INFINITY;
+                    if (kc[32 + key] > qcode) s1[i] = -INFINITY;
+                }
+            }
+            f32x16 &u0 = s0, &u1 = s1;       // the arguments replace the scores in place
+            for (int i = 0; i < 16; ++i) {
+                u0[i] = fmaf(s0[i], c2, -m_use);
+                u1[i] = fmaf(s1[i], c2, -m_use);
+            }
+            // the max of the 32 arguments as a tree of 3-input maxima (16 ops)
+            float t1[12];
+            for (int k = 0; k < 5; ++k) {
+                t1[k] = max3f(u0[3 * k], u0[3 * k + 1], u0[3 * k + 2]);
+                t1[5 + k] = max3f(u1[3 * k], u1[3 * k + 1], u1[3 * k + 2]);
+            }
+            t1[10] = u0[15];
+            t1[11] = u1[15];
+            const float t2[4] = {max3f(t1[0], t1[1], t1[2]), max3f(t1[3], t1[4], t1[5]), max3f(t1[6], t1[7], t1[8]),
+                                 max3f(t1[9], t1[10], t1[11])};
+            const float tmax = half_swap_max(fmaxf(max3f(t2[0], t2[1], t2[2]), t2[3]));
+            const bool grow = tmax > g_thr;
+            if (__any(grow)) {
+                const float d = grow ? tmax : 0.f;                 // new max - m_use
+                const float alpha = grow ? fast_exp2(m_run - (m_use + d)) : 1.f;   // 0 when m_run = -inf
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+                l_run *= alpha;
+                if (grow) {
+                    m_run = m_use + d;
+                    m_use = m_run;
+                    g_thr = kRescaleLog2;
+                }
+                for (int i = 0; i < 16; ++i) {
+                    u0[i] -= d;
+                    u1[i] -= d;
+                }
             }
         };
-        auto mfma_phase = [&](auto bufc, int jq) __attribute__((always_inline)) {   // PV of tile jq - 1, QK of tile jq (slot jq)
-            constexpr int SB = decltype(bufc)::value;
-            const uint16_t *ks = SB ? Ks1 : Ks0;
-            const uint16_t *vs = SB ? Vs1 : Vs0;
-            if (jq >= 1 && jq <= T) {
-                for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
-                for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
+
+        // One tile: compute on LDS buffer BUF while tile t0 + KT streams into
+        // the other one.  BUF is a compile-time constant, so the compiler sees
+        // that the reads and the in-flight LDS loads touch different arrays and
+        // does not wait for the loads before reading.  The PV products of
+        // sub-tile 0 are interleaved with the exponentials of sub-tile 1.
+        // Prefix tiles and whole in-range tiles of a full mask are visible to
+        // every row; any other tile is classified by this key group's 64 keys:
+        // skipped when hidden from every row, no predicate when visible to all.
+        auto tile_step = [&](auto bufc, int t0) {
+            constexpr int BUF = decltype(bufc)::value;
+            if (t0 + KT < kend) {
+                const bool part = partial_tile(t0 + KT);
+                issue_k(t0 + KT, BUF ^ 1, part, BUF ^ 1);
+                issue_v(t0 + KT, BUF ^ 1, part);
             }
-            if (jq < T) qk(ks, s0, s1);
-        };
-        auto softmax_phase = [&](int jq) __attribute__((always_inline)) {           // tile jq: P and the running max and sum
-            if (jq >= T) return;
-            const int t0 = kbeg + jq * KT;
             bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
+            bool live = true;
             if (!vis) {
                 int kmn, kmx;
-                key_range(t0, KT, kmn, kmx);
+                key_range(t0 + kofs, 64, kmn, kmx);
+                live = kmn <= qmax;
                 vis = kmx <= qmin;
             }
-            prep(s0, s1, kcode_s[jq & 3], vis);
-            float psum = 0.f;
-            for (int i = 0; i < 16; ++i) {
-                const float e = fast_exp2(s0[i]);
-                psum += e;
-                p0[i >> 3][i & 7] = (__bf16)e;
+            if (live) {
+                const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
+                const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
+                f32x16 s0, s1;
+                qk(ks, s0, s1);
+                prep(s0, s1, kcode_s[BUF] + kofs, vis);
+                const f32x16 &u0 = s0, &u1 = s1;
+                float psum = 0.f;
+                bf16x8 p0[2], p1[2];
+                for (int i = 0; i < 16; ++i) {
+                    const float p = fast_exp2(u0[i]);
+                    psum += p;
+                    p0[i >> 3][i & 7] = (__bf16)p;
+                }
+                constexpr int PER = 16 / (2 * DT);   // exps of sub-tile 1 per PV product
+                for (int q = 0; q < 2 * DT; ++q) {
+                    pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
+                    for (int e = 0; e < PER; ++e) {
+                        const int i = q * PER + e;
+                        const float p = fast_exp2(u1[i]);
+                        psum += p;
+                        p1[i >> 3][i & 7] = (__bf16)p;
+                    }
+                }
+                l_run += psum;
+                for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
             }
-            for (int i = 0; i < 16; ++i) {
-                const float e = fast_exp2(s1[i]);
-                psum += e;
-                p1[i >> 3][i & 7] = (__bf16)e;
-            }
-            l_run += psum;
-        };
-        // Barriers ending a phase: after an even (global) phase the slot loads
-        // issued at its start stay in flight; after an odd one they have
-        // landed.
-        auto bar_nowait = [&]() __attribute__((always_inline)) {
-            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-        };
-        auto bar_wait = [&]() __attribute__((always_inline)) {
-            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_waitcnt(0);   // this thread's loads of the next tile landed
             __syncthreads();
         };
-        load_slot(std::integral_constant<int, 0>{}, 0);
-        load_slot(std::integral_constant<int, 1>{}, 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // Each group runs its own loop over local phases 2jq (MFMA, slot jq)
-        // and 2jq + 1 (softmax of tile jq); group B is one phase behind, so
-        // global phase p is A's phase p and B's phase p - 1.  Global phase
-        // 2s - 2 (s >= 2) issues slot s: A at the start of its MFMA phase
-        // s - 1, B at the start of its softmax phase s - 2.  Both groups end
-        // after 2T + 2 barriers.  Unrolled by two tiles so every LDS buffer
-        // index is a constant.
-        if (grp == 0) {
-            for (int jq = 0; jq <= T; jq += 2) {
-                if (jq >= 1) load_slot(std::integral_constant<int, 1>{}, jq + 1);
-                mfma_phase(std::integral_constant<int, 0>{}, jq);
-                bar_nowait();
-                softmax_phase(jq);
-                bar_wait();
-                if (jq + 1 > T) break;
-                load_slot(std::integral_constant<int, 0>{}, jq + 2);
-                mfma_phase(std::integral_constant<int, 1>{}, jq + 1);
-                bar_nowait();
-                softmax_phase(jq + 1);
-                bar_wait();
-            }
-        } else {
-            bar_nowait();   // global phase 0
-            for (int jq = 0; jq <= T; jq += 2) {
-                mfma_phase(std::integral_constant<int, 0>{}, jq);
-                bar_wait();
-                if (jq == T) break;
-                load_slot(std::integral_constant<int, 0>{}, jq + 2);
-                softmax_phase(jq);
-                bar_nowait();
-                mfma_phase(std::integral_constant<int, 1>{}, jq + 1);
-                bar_wait();
-                if (jq + 1 == T) break;
-                load_slot(std::integral_constant<int, 1>{}, jq + 3);
-                softmax_phase(jq + 1);
-                bar_nowait();
-            }
-        }
-    } else {
-        if (kbeg < kend) {
-            const bool part = partial_tile(kbeg);
-            issue_k(kbeg, 0, part, 0);
-            issue_v(kbeg, 0, part);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        for (int t0 = kbeg; t0 < kend; t0 += 2 * KT) {
-            tile_step(std::integral_constant<int, 0>{}, t0);
-            if (t0 + KT < kend) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
-        }
-    }
 
-    // Finish the rows: with two key groups, the groups first merge their
-    // (max, sum, O) through LDS, each then finishing half of every row's
-    // columns -- group KG takes the lane's accumulator elements [KG H,
-    // (KG + 1) H), H = 8 DT (whole groups of four: output column blocks)
-    // and hands its other half to its partner.  Both evaluate the merge in
-    // one operand order (group 0's term first), so their halves agree with
-    // each other bitwise.  (The last tile step ended with a barrier and
-    // issued no loads, so the tiles are free for the exchange.)  Then
-    // normalise and write out/lse, or the split partial.
-    const long rows_total = (long)a.B * a.Hq * a.M;
-    constexpr int H = NG == 2 ? DT * 8 : DT * 16;     // elements a group finishes
-    constexpr int Q4 = H / 4;                          // float4 per lane per half
-    // Group KG hands the partner's half of O, and its (max, sum), to LDS.
-    auto give = [&](auto kgc) {
-        constexpr int KG = decltype(kgc)::value;
-        constexpr int G0 = (1 - KG) * H;               // the partner's half
-        float4 *dst = reinterpret_cast<float4 *>(KG == 0 ? Ks1 : Ks0) + wq * Q4 * 64;
-        for (int e4 = 0; e4 < Q4; ++e4) {
-            const int f = G0 + 4 * e4;
-            const f32x16 &od = o[f / 16];
-            dst[e4 * 64 + lane] = float4{od[f % 16], od[f % 16 + 1], od[f % 16 + 2], od[f % 16 + 3]};
+        __syncthreads();   // slot codes, zeroed tiles and the query waves' code ranges visible
+        if (a.kind != 0) {
+            qmin = INT_MAX;
+            qmax = INT_MIN;
+            for (int w = 0; w < QW; ++w) {
+                qmin = min(qmin, qrange_s[0][w]);
+                qmax = max(qmax, qrange_s[1][w]);
+            }
+            qmin = __builtin_amdgcn_readfirstlane(qmin);
+            qmax = __builtin_amdgcn_readfirstlane(qmax);
         }
-        ml_s[((KG * 2 + 0) * 4 + wq) * 64 + lane] = m_run;
-        ml_s[((KG * 2 + 1) * 4 + wq) * 64 + lane] = l_run;
-    };
-    auto finish = [&](auto kgc) {
-        constexpr int KG = decltype(kgc)::value;
-        constexpr int E0 = KG * H, E1 = E0 + H;
-        if constexpr (NG == 2) {
-            const float4 *src = reinterpret_cast<const float4 *>(KG == 0 ? Ks0 : Ks1) + wq * Q4 * 64;
-            const float mo = ml_s[(((1 - KG) * 2 + 0) * 4 + wq) * 64 + lane];
-            const float lo = ml_s[(((1 - KG) * 2 + 1) * 4 + wq) * 64 + lane];
-            const float mg0 = KG == 0 ? m_run : mo, mg1 = KG == 0 ? mo : m_run;   // group 0's, group 1's
-            const float lg0 = KG == 0 ? l_run : lo, lg1 = KG == 0 ? lo : l_run;
-            const float m = fmaxf(mg0, mg1);
-            // a side whose max is the merged one (also both -inf) keeps scale 1
-            const float a0 = mg0 == m ? 1.f : fast_exp2(mg0 - m);
-            const float a1 = mg1 == m ? 1.f : fast_exp2(mg1 - m);
-            for (int e4 = 0; e4 < Q4; ++e4) {
-                const float4 t = src[e4 * 64 + lane];
-                const float tv[4] = {t.x, t.y, t.z, t.w};
-                for (int c = 0; c < 4; ++c) {
-                    const int f = E0 + 4 * e4 + c;
-                    const float x = o[f / 16][f % 16];
-                    o[f / 16][f % 16] = KG == 0 ? fmaf(x, a0, tv[c] * a1) : fmaf(tv[c], a0, x * a1);
+        // Leading and trailing tiles of the split that are hidden from every
+        // row (later blocks or groups, DUMMY slots past the last live one) are
+        // never visited: no loads, no MFMAs.  A hidden tile between live ones
+        // is visited, but its rows are not fetched and its MFMAs are skipped.
+        if (a.kind != 0) {
+            int kmn, kmx;
+            for (; kbeg < kend; kbeg += KT) {
+                key_range(kbeg, KT, kmn, kmx);
+                if (kmn <= qmax) break;
+            }
+            while (kend > kbeg) {
+                const int tl = kbeg + (kend - 1 - kbeg) / KT * KT;   // start of the last tile
+                key_range(tl, KT, kmn, kmx);
+                if (kmn <= qmax) break;
+                kend = tl;
+            }
+            kbeg = __builtin_amdgcn_readfirstlane(kbeg);
+            kend = __builtin_amdgcn_readfirstlane(kend);
+        }
+        if constexpr (NG == 1 && kPingPong) {
+            // Ping-pong.  Waves [0, QW/2) (group A) and [QW/2, QW) (group B) run
+            // the same sequence of tiles one phase apart.  A phase is either all
+            // MFMA (PV of tile j - 1 and QK of tile j) or all VALU (the softmax of
+            // tile j), so on every SIMD one wave's matrix work overlaps the other
+            // wave's vector work.  LDS slot j (buffer j % 2) holds K(j) and
+            // V(j - 1): group A uses it in phase 2j, group B in phase 2j + 1;
+            // slot j + 2 is loaded from the start of phase 2j + 2 and waited for
+            // at the end of phase 2j + 3.  Key codes of partial tiles go to a
+            // ring of four (tile j's are read up to phase 2j + 2).
+            const int grp = wid >= QW / 2 ? 1 : 0;
+            const int T = (kend - kbeg + KT - 1) / KT;
+            f32x16 s0 = f32x16{}, s1 = f32x16{};   // S^T of the tile between its QK and softmax phases
+            bf16x8 p0[2], p1[2];                   // P of the tile between its softmax and PV phases
+            auto load_slot = [&](auto bufc, int js) __attribute__((always_inline)) {
+                constexpr int SB = decltype(bufc)::value;
+                if (js < T) {
+                    const int t0 = kbeg + js * KT;
+                    issue_k(t0, SB, partial_tile(t0), js & 3);
+                }
+                if (js >= 1 && js <= T) {
+                    const int t0 = kbeg + (js - 1) * KT;
+                    issue_v(t0, SB, partial_tile(t0));
+                }
+            };
+            auto mfma_phase = [&](auto bufc, int jq) __attribute__((always_inline)) {   // PV of tile jq - 1, QK of tile jq (slot jq)
+                constexpr int SB = decltype(bufc)::value;
+                const uint16_t *ks = SB ? Ks1 : Ks0;
+                const uint16_t *vs = SB ? Vs1 : Vs0;
+                if (jq >= 1 && jq <= T) {
+                    for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs, q / DT, q % DT, p0[q / DT]);
+                    for (int q = 0; q < 2 * DT; ++q) pv_mfma(vs + 32 * D, q / DT, q % DT, p1[q / DT]);
+                }
+                if (jq < T) qk(ks, s0, s1);
+            };
+            auto softmax_phase = [&](int jq) __attribute__((always_inline)) {           // tile jq: P and the running max and sum
+                if (jq >= T) return;
+                const int t0 = kbeg + jq * KT;
+                bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
+                if (!vis) {
+                    int kmn, kmx;
+                    key_range(t0, KT, kmn, kmx);
+                    vis = kmx <= qmin;
+                }
+                prep(s0, s1, kcode_s[jq & 3], vis);
+                float psum = 0.f;
+                for (int i = 0; i < 16; ++i) {
+                    const float e = fast_exp2(s0[i]);
+                    psum += e;
+                    p0[i >> 3][i & 7] = (__bf16)e;
+                }
+                for (int i = 0; i < 16; ++i) {
+                    const float e = fast_exp2(s1[i]);
+                    psum += e;
+                    p1[i >> 3][i & 7] = (__bf16)e;
+                }
+                l_run += psum;
+            };
+            // Barriers ending a phase: after an even (global) phase the slot loads
+            // issued at its start stay in flight; after an odd one they have
+            // landed.
+            auto bar_nowait = [&]() __attribute__((always_inline)) {
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            };
+            auto bar_wait = [&]() __attribute__((always_inline)) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            };
+            load_slot(std::integral_constant<int, 0>{}, 0);
+            load_slot(std::integral_constant<int, 1>{}, 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            // Each group runs its own loop over local phases 2jq (MFMA, slot jq)
+            // and 2jq + 1 (softmax of tile jq); group B is one phase behind, so
+            // global phase p is A's phase p and B's phase p - 1.  Global phase
+            // 2s - 2 (s >= 2) issues slot s: A at the start of its MFMA phase
+            // s - 1, B at the start of its softmax phase s - 2.  Both groups end
+            // after 2T + 2 barriers.  Unrolled by two tiles so every LDS buffer
+            // index is a constant.
+            if (grp == 0) {
+                for (int jq = 0; jq <= T; jq += 2) {
+                    if (jq >= 1) load_slot(std::integral_constant<int, 1>{}, jq + 1);
+                    mfma_phase(std::integral_constant<int, 0>{}, jq);
+                    bar_nowait();
+                    softmax_phase(jq);
+                    bar_wait();
+                    if (jq + 1 > T) break;
+                    load_slot(std::integral_constant<int, 0>{}, jq + 2);
+                    mfma_phase(std::integral_constant<int, 1>{}, jq + 1);
+                    bar_nowait();
+                    softmax_phase(jq + 1);
+                    bar_wait();
+                }
+            } else {
+                bar_nowait();   // global phase 0
+                for (int jq = 0; jq <= T; jq += 2) {
+                    mfma_phase(std::integral_constant<int, 0>{}, jq);
+                    bar_wait();
+                    if (jq == T) break;
+                    load_slot(std::integral_constant<int, 0>{}, jq + 2);
+                    softmax_phase(jq);
+                    bar_nowait();
+                    mfma_phase(std::integral_constant<int, 1>{}, jq + 1);
+                    bar_wait();
+                    if (jq + 1 == T) break;
+                    load_slot(std::integral_constant<int, 1>{}, jq + 3);
+                    softmax_phase(jq + 1);
+                    bar_nowait();
                 }
             }
-            l_run = fmaf(lg0, a0, lg1 * a1);
-            m_run = m;
-        }
-        const float l_tot = l_run + __shfl_xor(l_run, 32);
-        if (!rv) return;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        const float row_lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-        const long row_flat = (long)(b * a.Hq + h) * a.M + j;
-        if (a.n_split == 1) {
-            uint16_t *orow = a.out + row_flat * D;
-            for (int dt = 0; dt < DT; ++dt)
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    if (dt * 16 + q4 * 4 < E0 || dt * 16 + q4 * 4 >= E1) continue;
-                    __bf16 v4[4];
-                    for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[dt][q4 * 4 + c] * inv);
-                    *reinterpret_cast<uint2 *>(orow + dt * 32 + q4 * 8 + hh * 4) =
-                        *reinterpret_cast<const uint2 *>(v4);
-                }
-            if (KG == 0 && hh == 0) a.lse[row_flat] = row_lse;
         } else {
-            float *orow = a.ws_o + ((long)split * rows_total + row_flat) * D;
-            for (int dt = 0; dt < DT; ++dt)
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    if (dt * 16 + q4 * 4 < E0 || dt * 16 + q4 * 4 >= E1) continue;
-                    float4 v;
-                    v.x = o[dt][q4 * 4 + 0] * inv;
-                    v.y = o[dt][q4 * 4 + 1] * inv;
-                    v.z = o[dt][q4 * 4 + 2] * inv;
-                    v.w = o[dt][q4 * 4 + 3] * inv;
-                    *reinterpret_cast<float4 *>(orow + dt * 32 + q4 * 8 + hh * 4) = v;
-                }
-            if (KG == 0 && hh == 0) a.ws_l[(long)split * rows_total + row_flat] = row_lse;
+            if (kbeg < kend) {
+                const bool part = partial_tile(kbeg);
+                issue_k(kbeg, 0, part, 0);
+                issue_v(kbeg, 0, part);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            for (int t0 = kbeg; t0 < kend; t0 += 2 * KT) {
+                tile_step(std::integral_constant<int, 0>{}, t0);
+                if (t0 + KT < kend) tile_step(std::integral_constant<int, 1>{}, t0 + KT);
+            }
         }
-    };
-    if constexpr (NG == 2) {
-        if (kg == 0) give(std::integral_constant<int, 0>{});
-        else give(std::integral_constant<int, 1>{});
-        __syncthreads();
+
+        // Finish the rows: with two key groups, the groups first merge their
+        // (max, sum, O) through LDS, each then finishing half of every row's
+        // columns -- group KG takes the lane's accumulator elements [KG H,
+        // (KG + 1) H), H = 8 DT (whole groups of four: output column blocks)
+        // and hands its other half to its partner.  Both evaluate the merge in
+        // one operand order (group 0's term first), so their halves agree with
+        // each other bitwise.  (The last tile step ended with a barrier and
+        // issued no loads, so the tiles are free for the exchange.)  Then
+        // normalise and write out/lse, or the split partial.
+        const long rows_total = (long)a.B * a.Hq * a.M;
+        constexpr int H = NG == 2 ? DT * 8 : DT * 16;     // elements a group finishes
+        constexpr int Q4 = H / 4;                          // float4 per lane per half
+        // Group KG hands the partner's half of O, and its (max, sum), to LDS.
+        auto give = [&](auto kgc) {
+            constexpr int KG = decltype(kgc)::value;
+            constexpr int G0 = (1 - KG) * H;               // the partner's half
+            float4 *dst = reinterpret_cast<float4 *>(KG == 0 ? Ks1 : Ks0) + wq * Q4 * 64;
+            for (int e4 = 0; e4 < Q4; ++e4) {
+                const int f = G0 + 4 * e4;
+                const f32x16 &od = o[f / 16];
+                dst[e4 * 64 + lane] = float4{od[f % 16], od[f % 16 + 1], od[f % 16 + 2], od[f % 16 + 3]};
+            }
+            ml_s[((KG * 2 + 0) * 4 + wq) * 64 + lane] = m_run;
+            ml_s[((KG * 2 + 1) * 4 + wq) * 64 + lane] = l_run;
+        };
+        auto finish = [&](auto kgc) {
+            constexpr int KG = decltype(kgc)::value;
+            constexpr int E0 = KG * H, E1 = E0 + H;
+            if constexpr (NG == 2) {
+                const float4 *src = reinterpret_cast<const float4 *>(KG == 0 ? Ks0 : Ks1) + wq * Q4 * 64;
+                const float mo = ml_s[(((1 - KG) * 2 + 0) * 4 + wq) * 64 + lane];
+                const float lo = ml_s[(((1 - KG) * 2 + 1) * 4 + wq) * 64 + lane];
+                const float mg0 = KG == 0 ? m_run : mo, mg1 = KG == 0 ? mo : m_run;   // group 0's, group 1's
+                const float lg0 = KG == 0 ? l_run : lo, lg1 = KG == 0 ? lo : l_run;
+                const float m = fmaxf(mg0, mg1);
+                // a side whose max is the merged one (also both -inf) keeps scale 1
+                const float a0 = mg0 == m ? 1.f : fast_exp2(mg0 - m);
+                const float a1 = mg1 == m ? 1.f : fast_exp2(mg1 - m);
+                for (int e4 = 0; e4 < Q4; ++e4) {
+                    const float4 t = src[e4 * 64 + lane];
+                    const float tv[4] = {t.x, t.y, t.z, t.w};
+                    for (int c = 0; c < 4; ++c) {
+                        const int f = E0 + 4 * e4 + c;
+                        const float x = o[f / 16][f % 16];
+                        o[f / 16][f % 16] = KG == 0 ? fmaf(x, a0, tv[c] * a1) : fmaf(tv[c], a0, x * a1);
+                    }
+                }
+                l_run = fmaf(lg0, a0, lg1 * a1);
+                m_run = m;
+            }
+            const float l_tot = l_run + __shfl_xor(l_run, 32);
+            if (!rv) return;
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const float row_lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+            const long row_flat = (long)(b * a.Hq + h) * a.M + j;
+            if (ns == 1) {
+                uint16_t *orow = a.out + row_flat * D;
+                for (int dt = 0; dt < DT; ++dt)
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        if (dt * 16 + q4 * 4 < E0 || dt * 16 + q4 * 4 >= E1) continue;
+                        __bf16 v4[4];
+                        for (int c = 0; c < 4; ++c) v4[c] = (__bf16)(o[dt][q4 * 4 + c] * inv);
+                        *reinterpret_cast<uint2 *>(orow + dt * 32 + q4 * 8 + hh * 4) =
+                            *reinterpret_cast<const uint2 *>(v4);
+                    }
+                if (KG == 0 && hh == 0) a.lse[row_flat] = row_lse;
+            } else {
+                float *orow = a.ws_o + ((long)split * rows_total + row_flat) * D;
+                for (int dt = 0; dt < DT; ++dt)
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        if (dt * 16 + q4 * 4 < E0 || dt * 16 + q4 * 4 >= E1) continue;
+                        float4 v;
+                        v.x = o[dt][q4 * 4 + 0] * inv;
+                        v.y = o[dt][q4 * 4 + 1] * inv;
+                        v.z = o[dt][q4 * 4 + 2] * inv;
+                        v.w = o[dt][q4 * 4 + 3] * inv;
+                        *reinterpret_cast<float4 *>(orow + dt * 32 + q4 * 8 + hh * 4) = v;
+                    }
+                if (KG == 0 && hh == 0) a.ws_l[(long)split * rows_total + row_flat] = row_lse;
+            }
+        };
+        if constexpr (NG == 2) {
+            if (kg == 0) give(std::integral_constant<int, 0>{});
+            else give(std::integral_constant<int, 1>{});
+            __syncthreads();
+        }
+        if (kg == 0) finish(std::integral_constant<int, 0>{});
+        else if constexpr (NG == 2) finish(std::integral_constant<int, 1>{});
+
+    __syncthreads();   // the LDS is free for the next item
     }
-    if (kg == 0) finish(std::integral_constant<int, 0>{});
-    else if constexpr (NG == 2) finish(std::integral_constant<int, 1>{});
 }
 
 // Merge the key splits of each row in split order:
@@ -878,8 +912,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     const long row = (long)blockIdx.x * RPB + threadIdx.x / PER_ROW;
     const int d4 = threadIdx.x % PER_ROW;
     if (row >= rows_total) return;
-    if (a.m_valid && (int)(row % a.M) >= valid_rows(a, (int)(row / ((long)a.Hq * a.M)))) return;
-    const int ns = a.n_split;
+    const int b = (int)(row / ((long)a.Hq * a.M));
+    if (a.m_valid && (int)(row % a.M) >= valid_rows(a, b)) return;
+    const int ns = splits_for(a, b);
+    if (ns == 1) return;   // pass 1 wrote this row directly
     const float *ls = a.ws_l + row;
     const float4 *os = reinterpret_cast<const float4 *>(a.ws_o + row * D) + d4;
     const long ostride = rows_total * PER_ROW;     // float4 between splits
@@ -1263,10 +1299,18 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
     }
     {
         long nwg = (long)a.B * a.Hkv * a.n_split * a.n_qtiles;
-        if (a.n_kgroups == 2)
-            attn_fwd_kernel<D, 2, 4><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
-        else
-            attn_fwd_kernel<D, 1, qwaves1(D)><<<dim3((unsigned)nwg), dim3(64 * qwaves1(D)), 0, stream>>>(a);
+        if (a.dyn_split) {
+            // persistent: one workgroup per CU walks the items the row counts ask for
+            nwg = min(nwg, (long)kNumCU);
+            if (a.n_kgroups == 2)
+                attn_fwd_kernel<D, 2, 4, true><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
+            else
+                attn_fwd_kernel<D, 1, qwaves1(D), true><<<dim3((unsigned)nwg), dim3(64 * qwaves1(D)), 0, stream>>>(a);
+        } else if (a.n_kgroups == 2) {
+            attn_fwd_kernel<D, 2, 4, false><<<dim3((unsigned)nwg), dim3(512), 0, stream>>>(a);
+        } else {
+            attn_fwd_kernel<D, 1, qwaves1(D), false><<<dim3((unsigned)nwg), dim3(64 * qwaves1(D)), 0, stream>>>(a);
+        }
     }
     if (a.n_split > 1) {
         const long rows = (long)a.B * a.Hq * a.M;
@@ -1298,7 +1342,7 @@ hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream)
     }
 }
 
-AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap)
+AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap, bool dyn)
 {
     AttnPlan p{};
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.D = D; p.M = M;
@@ -1330,9 +1374,18 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap)
         split = (int)((kAttnWgTarget + base - 1) / base);
         split = min(split, max(1, key_tiles / (1024 / tile)));
     }
+    // With a device row count the launch is sized for the most splits a
+    // batch entry may take (one key tile each, at most kMaxDynSplit) and
+    // each workgroup derives its entry's count from the row count
+    // (splits_for): workgroups of unused splits leave at once, so the
+    // launch shape stays static (graph capture) while pass 1 follows M_t.
+    p.dyn_split = dyn && split == 1 && key_tiles > 1 ? 1 : 0;
+    if (p.dyn_split) split = min(key_tiles, kMaxDynSplit);
     int tiles_per = (key_tiles + split - 1) / split;
     p.split_keys = max(1, tiles_per) * tile;
     p.n_split = max(1, (kv_len + p.split_keys - 1) / p.split_keys);
+    if (p.dyn_split && p.n_split == 1) p.dyn_split = 0;
+    p.rows_wg = p.n_kgroups == 2 ? kAttnRows : 32 * qwaves1(D);
     p.n_kblocks = (kv_len + kCsKeys - 1) / kCsKeys;
     const long cs_base = (long)B * Hkv * p.n_kblocks;
     int rsplit = 1;

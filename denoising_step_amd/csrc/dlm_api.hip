@@ -143,7 +143,7 @@ int dlm_step_attn_workspace_bytes(const dlm_kv_cache *kv_cache, const dlm_mask_d
     int rc = check_attn_scalars(kv_cache, mask_desc);
     if (rc != DLM_OK) return rc;
     dlm::AttnPlan p = dlm::plan_attn(kv_cache->B, mask_desc->Hq, kv_cache->Hkv, kv_cache->D,
-                                     mask_desc->M, mask_desc->kv_len, kv_cache->n_cap);
+                                     mask_desc->M, mask_desc->kv_len, kv_cache->n_cap, mask_desc->m_active != nullptr);
     *bytes = p.ws_total;
     return DLM_OK;
 }
@@ -165,7 +165,8 @@ int dlm_step_attn(const void *q, const void *k, const void *v, const dlm_kv_cach
     if ((md->M > 0 && (!aligned16(q) || !aligned16(out))) || !aligned16(kc->k) || !aligned16(kc->v) ||
         (k && !aligned16(k)) || (v && !aligned16(v)))
         return fail(DLM_E_SHAPE, "bf16 tensors must be 16-byte aligned");
-    dlm::AttnPlan p = dlm::plan_attn(kc->B, md->Hq, kc->Hkv, kc->D, md->M, md->kv_len, kc->n_cap);
+    dlm::AttnPlan p = dlm::plan_attn(kc->B, md->Hq, kc->Hkv, kc->D, md->M, md->kv_len, kc->n_cap,
+                                     md->m_active != nullptr);
     const size_t need = p.ws_total;
     if (need > 0 && (md->workspace == nullptr || md->workspace_bytes < need))
         return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -202,6 +203,7 @@ int dlm_step_attn(const void *q, const void *k, const void *v, const dlm_kv_cach
     a.scale_log2 = scale * 1.4426950408889634f;
     a.n_qtiles = p.n_qtiles; a.n_kgroups = p.n_kgroups; a.n_split = p.n_split; a.split_keys = p.split_keys;
     a.n_kblocks = p.n_kblocks; a.n_rsplit = p.n_rsplit;
+    a.dyn_split = p.dyn_split; a.rows_wg = p.rows_wg;
 
     hipError_t e = dlm::launch_step_attn(a, stream);
     if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -19,6 +19,7 @@ constexpr int kAttnRows = 128;       // query rows per pass-1 workgroup (4 query
 #define DLM_ATTN_WG_TARGET 256
 #endif
 constexpr long kAttnWgTarget = DLM_ATTN_WG_TARGET;  // 8-wave pass-1 workgroups wanted (1 per CU)
+constexpr int kMaxDynSplit = 8;      // key splits pass 1 may take with a device row count
 constexpr int kCsKeys = 256;         // keys per column-sum workgroup (4 waves x 64)
 constexpr int kCsRows = 32;          // query rows per column-sum tile
 constexpr int kMaxSlots = 1024;      // GROUP: slots per batch entry
@@ -31,7 +32,9 @@ struct AttnPlan {
     int B, Hq, Hkv, G, D, M, kv_len, n_cap;
     int n_qtiles;       // query tiles of kAttnRows packed rows per (b, kv-head)
     int n_kgroups;      // key groups per pass-1 workgroup (1: 4 waves, 2: 8 waves)
-    int n_split;        // key splits of pass 1
+    int n_split;        // key splits of pass 1 (with dyn: the most a batch entry may use)
+    int dyn_split;      // 1: the split count follows the device row count
+    int rows_wg;        // packed query rows per pass-1 workgroup
     int split_keys;     // keys per split (multiple of the 64 * n_kgroups key tile)
     int n_kblocks;      // column-sum key blocks of kCsKeys
     int n_rsplit;       // column-sum row splits
@@ -40,7 +43,9 @@ struct AttnPlan {
     size_t ws_colsum;   // bytes of column-sum partials (fp32)
     size_t ws_total;
 };
-AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap);
+// dyn: a device row count (m_active) is given; pass 1 then plans for the
+// largest key split and picks each batch entry's split count on the device.
+AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap, bool dyn = false);
 
 // Per-row partial state of the posterior stream over one vocabulary chunk
 // (48 bytes: staged through LDS in 16-byte pieces).
@@ -80,6 +85,7 @@ struct AttnArgs {
     int cs_lo, cs_hi, per_head, accumulate;
     float scale_log2;               // softmax scale * log2(e)
     int n_qtiles, n_kgroups, n_split, split_keys, n_kblocks, n_rsplit;
+    int dyn_split, rows_wg;         // device-decided key split (see plan_attn)
 };
 
 struct PostArgs {
@@ -144,6 +150,18 @@ struct R2LArgs {
 __device__ __forceinline__ int valid_rows(const AttnArgs &a, int b)
 {
     return a.m_valid ? min(max(a.m_valid[b], 0), a.M) : a.M;
+}
+
+// Key splits pass 1 uses for batch entry b: the planned count, or with a
+// device row count, enough splits (at most the planned n_split) that the
+// workgroups of a batch like this one would number about kAttnWgTarget.
+// Pass 1 and the split merge evaluate the same function.
+__device__ __forceinline__ int splits_for(const AttnArgs &a, int b)
+{
+    if (!a.dyn_split) return a.n_split;
+    const long wgs = (long)a.B * a.Hkv * ((a.G * valid_rows(a, b) + a.rows_wg - 1) / a.rows_wg);
+    if (wgs >= kAttnWgTarget) return 1;
+    return (int)min((long)a.n_split, (kAttnWgTarget + max(wgs, 1L) - 1) / max(wgs, 1L));
 }
 
 // Enqueue the kernels of one call (arguments already validated).

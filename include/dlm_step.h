@@ -121,7 +121,11 @@ typedef struct {
                                     capacity.  With it a step whose row count is decided
                                     on the device (dlm_block_buffer_advance) keeps the
                                     same launch shapes, e.g. inside a captured HIP graph
-                                    (SureLock page, sec. 2: M_t rows are computed). */
+                                    (SureLock page, sec. 2: M_t rows are computed).
+                                    Pass 1 then also splits the keys by the row count, on
+                                    the device, so its cost follows M_t: query the
+                                    workspace with m_active set (the size depends on
+                                    whether it is). */
 } dlm_mask_desc;
 
 /*

@@ -157,6 +157,10 @@ def test_attention_device_row_count(which, counts, kgroups, monkeypatch):
                                   mode=W.SEL_NONE), "row count")
     ds = DeviceStep(w, with_posterior=False)
     ds.md.m_active = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    # with a device row count pass 1 may split keys on the device: the
+    # workspace is sized for the descriptor that carries the count
+    ds.md.workspace = torch.empty(max(1, dlm.dlm_step_attn_workspace_bytes(ds.kv, ds.md)), dtype=torch.uint8,
+                                  device="cuda")
     sentinel_out = torch.full_like(ds.out, 3.0)
     ds.out.copy_(sentinel_out)
     ds.lse.fill_(777.0)
