@@ -489,7 +489,7 @@ def r2l_bench(args):
 HEADLINE = "surelock_sparse"
 EXTRAS = ("llada_bidirectional", "mbd_multiblock", "long_prefix_sampler")
 ATTN_TARGET, POST_TARGET = 0.5, 0.7
-LOOPS = ("step", "step_two_streams", "pass1", "passes12", "posterior")
+LOOPS = ("step", "step_two_streams", "step_after_pass1", "pass1", "passes12", "posterior")
 
 
 def _nbytes(*ts) -> int:
@@ -503,7 +503,7 @@ def loop_footprints(ds) -> dict:
     pass1 = _nbytes(ds.q, ds.cache_k, ds.cache_v, ds.out, ds.lse)
     post = _nbytes(ds.logits, ds.prev, ds.locked, ds.sel, ds.kl, ds.conf, ds.post_ws)
     step = pass1 + _nbytes(ds.k, ds.v, ds.colsum) + attn_ws + post
-    return {"step": step, "step_two_streams": step, "pass1": pass1,
+    return {"step": step, "step_two_streams": step, "step_after_pass1": step, "pass1": pass1,
             "passes12": pass1 + _nbytes(ds.colsum) + attn_ws, "posterior": post}
 
 
@@ -542,6 +542,9 @@ def measure_workload(name, args, loops=LOOPS, with_cpu=False, spread=True):
     def step_two_streams(i):
         sets[i].run(stream, locked=fresh_lock(), overlap=True)
 
+    def step_after_pass1(i):   # the posterior on a second stream from the end of pass 1
+        sets[i].run(stream, locked=fresh_lock(), overlap="pass1")
+
     def pass1(i):              # no fresh K/V (already in the cache), no column sums
         ds = sets[i]
         dlm.dlm_step_attn(ds.q, None, None, ds.kv, ds.active_idx, ds.md, ds.out, ds.lse, None, stream)
@@ -553,7 +556,7 @@ def measure_workload(name, args, loops=LOOPS, with_cpu=False, spread=True):
     def posterior(i):
         sets[i].run_posterior(stream, locked=fresh_lock())
 
-    fns = {"step": step, "step_two_streams": step_two_streams, "pass1": pass1,
+    fns = {"step": step, "step_two_streams": step_two_streams, "step_after_pass1": step_after_pass1, "pass1": pass1,
            "passes12": passes12, "posterior": posterior}
     ms = {}
     for k in loops:
@@ -584,6 +587,8 @@ def measure_workload(name, args, loops=LOOPS, with_cpu=False, spread=True):
             rec["step_ms_p10_p50_p90"] = [float(x) for x in np.percentile(np.array(step_ms), [10, 50, 90])]
     if "step_two_streams" in ms:
         rec["ms_per_step_two_streams"] = ms["step_two_streams"]
+    if "step_after_pass1" in ms:
+        rec["ms_per_step_posterior_after_pass1"] = ms["step_after_pass1"]
     if "pass1" in ms:
         t = alg_flops / (ms["pass1"] * 1e-3) / 1e12
         rec["attention_pass1"] = {

@@ -80,7 +80,8 @@ class _MaskDesc(ctypes.Structure):
                 ("cs_lo", ctypes.c_int32), ("cs_hi", ctypes.c_int32),
                 ("colsum_per_head", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("colsum_accumulate", ctypes.c_int32), ("m_active", ctypes.c_void_p)]
+                ("colsum_accumulate", ctypes.c_int32), ("m_active", ctypes.c_void_p),
+                ("pass1_done", ctypes.c_void_p)]
 
 
 class _Select(ctypes.Structure):
@@ -197,6 +198,7 @@ class MaskDesc:
     workspace_bytes: Optional[int] = None
     colsum_accumulate: int = 0  # 1: colsum += this call's sums (e.g. over layers)
     m_active: object = None     # optional int32 [B] device row counts
+    pass1_done: object = None   # optional torch.cuda.Event (recorded once) or raw hipEvent_t
 
 
 @dataclasses.dataclass
@@ -274,12 +276,21 @@ def _c_kv(kv: KVCache) -> _KVCache:
     return _KVCache(_ptr(kv.k), _ptr(kv.v), kv.B, kv.Hkv, kv.n_cap, kv.D)
 
 
+def _event_handle(ev, what):
+    if ev is None or isinstance(ev, int):
+        return ev or None
+    h = ev.cuda_event
+    if not h:
+        raise DlmError(-1, f"{what}: the event has not been created (record it once)")
+    return h
+
+
 def _c_mask(md: MaskDesc) -> _MaskDesc:
     wb = md.workspace_bytes if md.workspace_bytes is not None else _nbytes(md.workspace)
     return _MaskDesc(md.kind, md.Hq, md.M, md.kv_len, md.prefix_len, md.block_size, md.n_slots,
                      _ptr(md.slot_state), _ptr(md.slot_group), md.cs_lo, md.cs_hi,
                      md.colsum_per_head, md.scale, _ptr(md.workspace), wb, md.colsum_accumulate,
-                     _ptr(md.m_active))
+                     _ptr(md.m_active), _event_handle(md.pass1_done, "mask_desc.pass1_done"))
 
 
 def _c_sel(s: Select) -> _Select:

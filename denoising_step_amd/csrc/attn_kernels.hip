@@ -1283,7 +1283,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, long n)
 }
 
 template <int D>
-hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
+hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream, hipEvent_t pass1_done)
 {
     if (a.M > 0 && a.k != nullptr) {
         const long nblk = ((long)a.M * (D / 8) + 255) / 256 * a.B * a.Hkv;
@@ -1291,6 +1291,10 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
         kv_scatter_kernel<D><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(a);
     }
     if (a.M == 0) {
+        if (pass1_done) {
+            const hipError_t e = hipEventRecord(pass1_done, stream);
+            if (e != hipSuccess) return e;
+        }
         if (a.colsum && !a.accumulate) {
             long n = (long)a.B * (a.per_head ? a.Hq : 1) * a.kv_len;
             fill_zero_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(a.colsum, n);
@@ -1317,6 +1321,10 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
         constexpr int RPB = 256 / (D / 4);
         attn_combine_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(a);
     }
+    if (pass1_done) {
+        const hipError_t e = hipEventRecord(pass1_done, stream);
+        if (e != hipSuccess) return e;
+    }
     if (a.colsum) {
         long nwg = (long)a.B * a.Hkv * a.n_rsplit * a.n_kblocks;
         colsum_kernel<D><<<dim3((unsigned)nwg), dim3(256), 0, stream>>>(a);
@@ -1332,12 +1340,12 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream)
+hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream, hipEvent_t pass1_done)
 {
     switch (a.D) {
-    case 32: return launch_attn_d<32>(a, stream);
-    case 64: return launch_attn_d<64>(a, stream);
-    case 128: return launch_attn_d<128>(a, stream);
+    case 32: return launch_attn_d<32>(a, stream, pass1_done);
+    case 64: return launch_attn_d<64>(a, stream, pass1_done);
+    case 128: return launch_attn_d<128>(a, stream, pass1_done);
     default: return hipErrorInvalidValue;
     }
 }

@@ -205,7 +205,7 @@ int dlm_step_attn(const void *q, const void *k, const void *v, const dlm_kv_cach
     a.n_kblocks = p.n_kblocks; a.n_rsplit = p.n_rsplit;
     a.dyn_split = p.dyn_split; a.rows_wg = p.rows_wg;
 
-    hipError_t e = dlm::launch_step_attn(a, stream);
+    hipError_t e = dlm::launch_step_attn(a, stream, md->pass1_done);
     if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return DLM_OK;
 }

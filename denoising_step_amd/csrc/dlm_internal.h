@@ -165,7 +165,7 @@ __device__ __forceinline__ int splits_for(const AttnArgs &a, int b)
 }
 
 // Enqueue the kernels of one call (arguments already validated).
-hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream, hipEvent_t pass1_done);
 hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after);
 hipError_t launch_block_buffer(const BBArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);

@@ -106,10 +106,12 @@ class DeviceStep:
                       self.select, self.sel, self.kl, self.conf, p.R, p.V, stream)
 
     def run(self, stream=None, locked=None, overlap=False):
-        """One step.  With overlap, the posterior runs on a second stream:
-        its logit stream starts with the attention passes, and only its
-        selection waits for the column sums (select.score_ready); the
-        calling stream then waits for the posterior."""
+        """One step.  With overlap, the posterior runs on a second stream and
+        only its selection waits for the column sums (select.score_ready);
+        the calling stream then waits for the posterior.  overlap=True
+        starts its logit stream with the attention passes; overlap="pass1"
+        starts it once pass 1 is done (mask_desc.pass1_done), beside the
+        column-sum pass only."""
         if not (overlap and self.with_posterior):
             self.run_attn(stream)
             if self.with_posterior:
@@ -122,10 +124,19 @@ class DeviceStep:
             if main.device not in _SIDE_STREAMS:
                 _SIDE_STREAMS[main.device] = torch.cuda.Stream(device=main.device)
             self._side = _SIDE_STREAMS[main.device]
-            self._ev_start, self._ev_cs, self._ev_post = (torch.cuda.Event() for _ in range(3))
-        self._ev_start.record(main)
-        self._side.wait_event(self._ev_start)      # prior work on the calling stream first
-        self.run_attn(main)
+            self._ev_start, self._ev_cs, self._ev_post, self._ev_p1 = (torch.cuda.Event() for _ in range(4))
+            self._ev_p1.record(main)                   # created once; the library records it
+        if overlap == "pass1":
+            self.md.pass1_done = self._ev_p1
+            try:
+                self.run_attn(main)
+            finally:
+                self.md.pass1_done = None
+            self._side.wait_event(self._ev_p1)     # out / lse final; the column sums still running
+        else:
+            self._ev_start.record(main)
+            self._side.wait_event(self._ev_start)  # prior work on the calling stream first
+            self.run_attn(main)
         self._ev_cs.record(main)                   # column sums ready
         self.select.score_ready = self._ev_cs
         try:

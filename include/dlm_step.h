@@ -126,6 +126,12 @@ typedef struct {
                                     the device, so its cost follows M_t: query the
                                     workspace with m_active set (the size depends on
                                     whether it is). */
+    hipEvent_t pass1_done;       /* optional (NULL: none).  Recorded on `stream` once pass 1
+                                    (and its split merge) is enqueued, before the column-sum
+                                    pass: out and lse are final when it completes.  A caller
+                                    can start work that does not need the column sums (the
+                                    posterior's logit stream) on a second stream from this
+                                    event, beside the column-sum pass. */
 } dlm_mask_desc;
 
 /*

@@ -236,20 +236,22 @@ def test_mask_tile_classes(kgroups, case, monkeypatch):
         assert np.all(ora["colsum"][:, first_hidden:] == 0)
 
 
+@pytest.mark.parametrize("mode", [True, "pass1"])
 @pytest.mark.parametrize("case", ["llada_dynamic", "long_topk_score"])
-def test_overlapped_step_equals_serial(case):
-    """The overlapped schedule (posterior on a second stream, its selection
-    waiting for the column sums through select.score_ready) gives the same
-    bits as the serial one, for both selection modes that read the score."""
+def test_overlapped_step_equals_serial(case, mode):
+    """The overlapped schedules (posterior on a second stream from the start
+    of the step, or from mask_desc.pass1_done; its selection waiting for
+    the column sums through select.score_ready) give the same bits as the
+    serial one, for both selection modes that read the score."""
     w = small_llada(spread=True, seed=4) if case == "llada_dynamic" else small_long(seed=5)
-    _say(f"case: overlap {case}")
+    _say(f"case: overlap {case} ({mode})")
     ds = _device_step(w)
     ds.run()
     r1 = ds.results()
     for rep in range(3):
         ds.reset()
         ds.colsum.fill_(float("nan"))      # a read before the sums are ready would show
-        ds.run(overlap=True)
+        ds.run(overlap=mode)
         r2 = ds.results()
         for k in ("out", "lse", "colsum", "kl", "conf", "sel", "locked", "cache_k", "cache_v"):
             assert np.array_equal(r1[k], r2[k], equal_nan=False), (rep, k)
