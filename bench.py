@@ -383,8 +383,10 @@ def layer_bench(args):
     layer (width 4096, 32 heads of 128, SwiGLU width 12288, B=1, 2048
     positions) for a range of active-row counts M_t: each call timed alone
     with HIP events, against the bf16 MFMA peak (2 M N K flops) and the
-    weight bytes read (the bound at small M_t).  Two sets of weights rotate
-    so their footprint exceeds the 256 MB MALL.  Prints one JSON line."""
+    weight bytes read (the bound at small M_t), with the weights in the
+    packed layout (dlm_pack_weights, what a server keeps resident) and
+    row-major.  Two sets of weights rotate so their footprint exceeds the
+    256 MB MALL.  Prints one JSON line."""
     import torch
 
     import denoising_step_amd as dlm
@@ -400,40 +402,46 @@ def layer_bench(args):
 
     sets = [dict(qkv=w(((Hq + 2 * Hkv) * D, d), d), o=w((d, Hq * D), Hq * D), g=w((F, d), d),
                  u=w((F, d), d), dn=w((d, F), F)) for _ in range(2)]
+    packed = [{k: dlm.dlm_pack_weights(t) for k, t in s_.items()} for s_ in sets]
     x = torch.randn((1, n_pos, d), generator=gen, device=dev).to(torch.bfloat16)
     res = []
-    for M in (1024, 512, 256, 128, 64, 16):
+    for M in (1024, 512, 256, 128, 64, 32, 16):
         act = torch.sort(torch.randperm(n_pos, generator=gen, device=dev)[:M])[0].to(torch.int32)[None]
-        L = dlm.LayerDesc(B=1, n_pos=n_pos, d=d, M=M, active_idx=act, Hq=Hq, Hkv=Hkv, D=D, F=F)
         q = torch.empty((1, Hq, M, D), dtype=torch.bfloat16, device=dev)
         k = torch.empty((1, Hkv, M, D), dtype=torch.bfloat16, device=dev)
         v = torch.empty_like(k)
         ao = torch.randn((1, Hq, M, D), generator=gen, device=dev).to(torch.bfloat16)
         h = torch.empty((1, M, d), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(max(1, dlm.dlm_layer_workspace_bytes(L)), dtype=torch.uint8, device=dev)
-        calls = {
-            "qkv": (lambda i: dlm.dlm_proj_qkv(L, x, sets[i]["qkv"], q, k, v, ws),
-                    (Hq + 2 * Hkv) * D, d),
-            "out": (lambda i: dlm.dlm_proj_out(L, x, ao, sets[i]["o"], h, ws), d, Hq * D),
-            "ffn": (lambda i: dlm.dlm_ffn(L, h, sets[i]["g"], sets[i]["u"], sets[i]["dn"], x, ws),
-                    None, None),
-        }
         row = {"M_t": M}
-        for name, (fn, N, K) in calls.items():
-            ms = time_loop(fn, 2, args.steps, args.warmup)
-            if name == "ffn":
-                flops = 2.0 * M * (2 * F * d + d * F)
-                wbytes = 3.0 * F * d * 2
-            else:
-                flops = 2.0 * M * N * K
-                wbytes = 2.0 * N * K
-            row[name] = {"us": round(ms * 1e3, 2), "tflops": round(flops / ms / 1e9, 1),
-                         "mfma_frac": round(flops / ms / 1e9 / 2500.0, 3),
-                         "weight_gbs": round(wbytes / ms / 1e6, 0),
-                         "hbm_frac": round(wbytes / ms / 1e6 / 8000.0, 3)}
+        for layout, ws_ in (("packed", packed), ("row_major", sets)):
+            L = dlm.LayerDesc(B=1, n_pos=n_pos, d=d, M=M, active_idx=act, Hq=Hq, Hkv=Hkv, D=D, F=F,
+                              weights_packed=layout == "packed")
+            ws = torch.empty(max(1, dlm.dlm_layer_workspace_bytes(L)), dtype=torch.uint8, device=dev)
+            calls = {
+                "qkv": (lambda i: dlm.dlm_proj_qkv(L, x, ws_[i]["qkv"], q, k, v, ws),
+                        (Hq + 2 * Hkv) * D, d),
+                "out": (lambda i: dlm.dlm_proj_out(L, x, ao, ws_[i]["o"], h, ws), d, Hq * D),
+                "ffn": (lambda i: dlm.dlm_ffn(L, h, ws_[i]["g"], ws_[i]["u"], ws_[i]["dn"], x, ws),
+                        None, None),
+            }
+            r = {}
+            for name, (fn, N, K) in calls.items():
+                ms = time_loop(fn, 2, args.steps, args.warmup)
+                if name == "ffn":
+                    flops = 2.0 * M * (2 * F * d + d * F)
+                    wbytes = 3.0 * F * d * 2
+                else:
+                    flops = 2.0 * M * N * K
+                    wbytes = 2.0 * N * K
+                r[name] = {"us": round(ms * 1e3, 2), "tflops": round(flops / ms / 1e9, 1),
+                           "mfma_frac": round(flops / ms / 1e9 / 2500.0, 3),
+                           "weight_gbs": round(wbytes / ms / 1e6, 0),
+                           "hbm_frac": round(wbytes / ms / 1e6 / 8000.0, 3)}
+            row[layout] = r
+            print(f"layer M_t={M} {layout}: " + " ".join(
+                f"{n}={r[n]['us']}us/{r[n]['tflops']}TF/{r[n]['weight_gbs'] / 1000:.2f}TB/s" for n in calls),
+                file=sys.stderr, flush=True)
         res.append(row)
-        print(f"layer M_t={M}: " + " ".join(f"{n}={row[n]['us']}us/{row[n]['tflops']}TF"
-                                           for n in calls), file=sys.stderr, flush=True)
     line = {"metric": "active-row projections and feed-forward of one layer", "unit": "us",
             "n_gpus": 1, "dtype": "bf16", "data": "synthetic (random weights drawn on the device)",
             "config": {"workload": "layer_llada", "d": d, "Hq": Hq, "Hkv": Hkv, "D": D, "F": F,

@@ -31,7 +31,8 @@ ROW_SELECT, ROW_LOCK = 1, 2
 
 EXPORTS = ("dlm_step_attn", "dlm_step_attn_workspace_bytes", "dlm_posterior",
            "dlm_posterior_workspace_bytes", "dlm_posterior_noalloc", "dlm_block_buffer_init", "dlm_block_buffer_advance",
-           "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_layer_workspace_bytes", "dlm_r2l_scan",
+           "dlm_proj_qkv", "dlm_proj_out", "dlm_ffn", "dlm_layer_workspace_bytes", "dlm_pack_weights",
+           "dlm_r2l_scan",
            "dlm_last_error")
 
 if not os.path.exists(LIB_PATH):
@@ -97,7 +98,7 @@ class _LayerDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("n_pos", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("M", ctypes.c_int32), ("active_idx", ctypes.c_void_p), ("m_active", ctypes.c_void_p),
                 ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
-                ("F", ctypes.c_int32)]
+                ("F", ctypes.c_int32), ("weights_packed", ctypes.c_int32)]
 
 
 class _BlockBuffer(ctypes.Structure):
@@ -146,6 +147,8 @@ lib.dlm_ffn.argtypes = [_LP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 lib.dlm_ffn.restype = ctypes.c_int
 lib.dlm_layer_workspace_bytes.argtypes = [_LP, ctypes.POINTER(ctypes.c_size_t)]
 lib.dlm_layer_workspace_bytes.restype = ctypes.c_int
+lib.dlm_pack_weights.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, _P]
+lib.dlm_pack_weights.restype = ctypes.c_int
 lib.dlm_last_error.argtypes = []
 lib.dlm_last_error.restype = ctypes.c_char_p
 
@@ -230,6 +233,7 @@ class LayerDesc:
     Hkv: int = 1
     D: int = 64
     F: int = 64
+    weights_packed: bool = False   # weights in the layout of dlm_pack_weights (same shapes)
 
 
 @dataclasses.dataclass
@@ -305,7 +309,8 @@ def _c_sel(s: Select) -> _Select:
 
 
 def _c_layer(L: LayerDesc) -> _LayerDesc:
-    return _LayerDesc(L.B, L.n_pos, L.d, L.M, _ptr(L.active_idx), _ptr(L.m_active), L.Hq, L.Hkv, L.D, L.F)
+    return _LayerDesc(L.B, L.n_pos, L.d, L.M, _ptr(L.active_idx), _ptr(L.m_active), L.Hq, L.Hkv, L.D, L.F,
+                      int(bool(L.weights_packed)))
 
 
 def _c_bb(bb: BlockBuffer) -> _BlockBuffer:
@@ -478,6 +483,21 @@ def dlm_layer_workspace_bytes(layer: LayerDesc) -> int:
     c = _c_layer(layer)
     _check(lib.dlm_layer_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
     return n.value
+
+
+def dlm_pack_weights(w, packed=None, stream=None):
+    """A bf16 weight [N, K] in the fragment-packed layout of the layer calls
+    (see dlm_step.h), returned as a tensor of the same shape."""
+    if w is None or w.dim() != 2:
+        raise DlmError(DLM_E_SHAPE, "w must be a 2-d bf16 tensor")
+    N, K = w.shape
+    _expect(w, "w", (N, K), "torch.bfloat16")
+    if packed is None:
+        import torch
+        packed = torch.empty_like(w)
+    _expect(packed, "packed", (N, K), "torch.bfloat16")
+    _check(lib.dlm_pack_weights(_ptr(w), _ptr(packed), N, K, _stream(stream)))
+    return packed
 
 
 def dlm_ffn(layer: LayerDesc, h, w_gate, w_up, w_down, x, workspace, stream=None) -> None:

@@ -365,6 +365,8 @@ static int check_layer(const dlm_layer_desc *L)
         rows * wq * 2 > big || wq * L->d * 2 > big || (long)L->F * L->d * 2 > big || (long)L->Hq * L->D * L->d * 2 > big)
         return fail(DLM_E_SHAPE, "a tensor of the layer exceeds 2 GiB");
     if (L->M > 0 && !L->active_idx) return fail(DLM_E_NULL, "active_idx is NULL");
+    if (L->weights_packed != 0 && L->weights_packed != 1)
+        return fail(DLM_E_DESC, "weights_packed=%d must be 0 or 1", L->weights_packed);
     return DLM_OK;
 }
 
@@ -373,7 +375,26 @@ static dlm::GemmArgs gemm_base(const dlm_layer_desc *L)
     dlm::GemmArgs a{};
     a.act = L->active_idx; a.m_valid = L->m_active;
     a.B = L->B; a.M = L->M; a.n_pos = L->n_pos; a.Hq = L->Hq; a.Hkv = L->Hkv; a.D = L->D;
+    a.w_packed = L->weights_packed;
     return a;
+}
+
+int dlm_pack_weights(const void *w, void *packed, int32_t N, int32_t K, hipStream_t stream)
+{
+    g_err[0] = 0;
+    if (N < 0 || K < 0) return fail(DLM_E_SHAPE, "N=%d K=%d out of range", N, K);
+    if (N % 16 != 0 || K % 32 != 0)
+        return fail(DLM_E_UNSUPPORTED, "N=%d must be a multiple of 16 and K=%d of 32", N, K);
+    if ((long)N * K * 2 > (1L << 31) - 1) return fail(DLM_E_SHAPE, "N*K=%ld exceeds 2 GiB of bf16", (long)N * K);
+    if ((long)N * K == 0) return DLM_OK;
+    if (!w || !packed) return fail(DLM_E_NULL, "w and packed must be non-NULL");
+    const char *a = static_cast<const char *>(w), *b = static_cast<const char *>(packed);
+    const long bytes = (long)N * K * 2;
+    if (a < b + bytes && b < a + bytes) return fail(DLM_E_DESC, "w and packed overlap");
+    hipError_t e = dlm::launch_pack_weights(static_cast<const uint16_t *>(w), static_cast<uint16_t *>(packed), N, K,
+                                            stream);
+    if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return DLM_OK;
 }
 
 static int run_gemm(const dlm::GemmArgs &a, hipStream_t stream)
@@ -420,6 +441,7 @@ static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 struct LayerPlans {
     dlm::GemmPlan qkv, out, gu, down;
     size_t g_bytes;        // gated hidden rows (bf16)
+    size_t xp_bytes;       // weight-streaming products: the packed rows of x[act] and of h
     size_t total;
 };
 static LayerPlans plan_layer(const dlm_layer_desc *L)
@@ -430,9 +452,14 @@ static LayerPlans plan_layer(const dlm_layer_desc *L)
     p.out = dlm::plan_gemm(rows, L->d, L->Hq * L->D, false);
     p.gu = dlm::plan_gemm(rows, L->F, L->d, true);
     p.down = dlm::plan_gemm(rows, L->d, L->F, false);
-    p.g_bytes = al256((size_t)rows * L->F * 2);
+    // gated hidden rows: row-major, or (weight-streaming kernel) one packed
+    // 16-row operand block
+    p.g_bytes = al256((size_t)(dlm::gemm_skinny(rows) ? 16 : rows) * L->F * 2);
+    p.xp_bytes = dlm::gemm_skinny(rows) ? al256((size_t)16 * L->d * 2) : 0;
     size_t t = p.qkv.part_bytes > p.out.part_bytes ? p.qkv.part_bytes : p.out.part_bytes;
-    const size_t f = p.g_bytes + (p.gu.part_bytes > p.down.part_bytes ? p.gu.part_bytes : p.down.part_bytes);
+    if (p.xp_bytes > t) t = p.xp_bytes;
+    const size_t f = p.g_bytes + p.xp_bytes +
+                     (p.gu.part_bytes > p.down.part_bytes ? p.gu.part_bytes : p.down.part_bytes);
     p.total = t > f ? t : f;
     return p;
 }
@@ -470,13 +497,19 @@ int dlm_proj_qkv(const dlm_layer_desc *L, const void *x, const void *w_qkv, void
     if (!x || !w_qkv || (L->M > 0 && (!q || !k || !v))) return fail(DLM_E_NULL, "x, w_qkv, q, k and v must be non-NULL");
     if (L->M == 0) return DLM_OK;
     const LayerPlans P = plan_layer(L);
-    rc = check_ws(workspace, workspace_bytes, P.qkv.part_bytes);
+    rc = check_ws(workspace, workspace_bytes, P.qkv.part_bytes > P.xp_bytes ? P.qkv.part_bytes : P.xp_bytes);
     if (rc != DLM_OK) return rc;
     dlm::GemmArgs a = gemm_base(L);
     a.a = static_cast<const uint16_t *>(x);
     a.a_bytes = (long)L->B * L->n_pos * L->d * 2;
     a.a_mode = 1; a.ep_mode = 1;
     a.K = L->d; a.N = (L->Hq + 2 * L->Hkv) * L->D;
+    if (P.xp_bytes) {   // gather the active rows once, as packed fragments
+        hipError_t e = dlm::launch_pack_rows(a, static_cast<uint16_t *>(workspace), stream);
+        if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        a.a = static_cast<const uint16_t *>(workspace);
+        a.a_mode = 3;
+    }
     a.w0 = static_cast<const uint16_t *>(w_qkv);
     a.out = static_cast<uint16_t *>(q); a.out_k = static_cast<uint16_t *>(k); a.out_v = static_cast<uint16_t *>(v);
     set_plan(a, P.qkv, workspace);
@@ -517,7 +550,7 @@ int dlm_ffn(const dlm_layer_desc *L, const void *h, const void *w_gate, const vo
         return fail(DLM_E_NULL, "h, w_gate, w_up, w_down and x must be non-NULL");
     if (L->M == 0) return DLM_OK;
     const LayerPlans P = plan_layer(L);
-    const size_t need = P.g_bytes + (P.gu.part_bytes > P.down.part_bytes ? P.gu.part_bytes : P.down.part_bytes);
+    const size_t need = P.g_bytes + P.xp_bytes + (P.gu.part_bytes > P.down.part_bytes ? P.gu.part_bytes : P.down.part_bytes);
     rc = check_ws(workspace, workspace_bytes, need);
     if (rc != DLM_OK) return rc;
     char *ws = static_cast<char *>(workspace);
@@ -528,18 +561,25 @@ int dlm_ffn(const dlm_layer_desc *L, const void *h, const void *w_gate, const vo
     g.K = L->d; g.N = L->F;
     g.w0 = static_cast<const uint16_t *>(w_gate); g.w1 = static_cast<const uint16_t *>(w_up);
     g.out = reinterpret_cast<uint16_t *>(ws);
-    set_plan(g, P.gu, ws + P.g_bytes);
+    g.out_packed = dlm::gemm_skinny(L->B * L->M);   // the down projection then reads packed fragments
+    set_plan(g, P.gu, ws + P.g_bytes + P.xp_bytes);
+    if (P.xp_bytes) {   // h as packed fragments
+        hipError_t e = dlm::launch_pack_rows(g, reinterpret_cast<uint16_t *>(ws + P.g_bytes), stream);
+        if (e != hipSuccess) return fail(DLM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+        g.a = reinterpret_cast<const uint16_t *>(ws + P.g_bytes);
+        g.a_mode = 3;
+    }
     rc = run_gemm(g, stream);
     if (rc != DLM_OK) return rc;
     dlm::GemmArgs d = gemm_base(L);      // down projection + residual, back to x's active rows
     d.a = reinterpret_cast<const uint16_t *>(ws);
     d.a_bytes = (long)L->B * L->M * L->F * 2;
-    d.a_mode = 0; d.ep_mode = 3; d.resid_gather = 0;
+    d.a_mode = g.out_packed ? 3 : 0; d.ep_mode = 3; d.resid_gather = 0;
     d.K = L->F; d.N = L->d;
     d.w0 = static_cast<const uint16_t *>(w_down);
     d.resid = static_cast<const uint16_t *>(h);
     d.out = static_cast<uint16_t *>(x);
-    set_plan(d, P.down, ws + P.g_bytes);
+    set_plan(d, P.down, ws + P.g_bytes + P.xp_bytes);
     return run_gemm(d, stream);
 }
 

@@ -121,11 +121,14 @@ struct GemmArgs {
     const int32_t *act;             // active_idx [B, M] (gather modes)
     const int32_t *m_valid;         // optional device [B] row counts
     const uint16_t *w0, *w1;        // W [N, K]; w1: the up matrix of SwiGLU (else nullptr)
+    int w_packed;                   // 1: W in the fragment-packed layout of dlm_pack_weights
     uint16_t *out, *out_k, *out_v;  // outputs (QKV: q, k, v)
     const uint16_t *resid;          // residual rows (EP_RESID, EP_SCATTER)
-    int a_mode;                     // 0 plain [B*M, K], 1 gather x[b, act, :], 2 heads out[b, h, j, d]
+    int a_mode;                     // 0 plain [B*M, K], 1 gather x[b, act, :], 2 heads out[b, h, j, d],
+                                    // 3 packed 16-row operand fragments (at most 16 rows)
     int ep_mode;                    // 0 plain / SwiGLU, 1 QKV, 2 residual to compact rows, 3 residual scattered to x
     int resid_gather;               // residual row: 1 x[b, act[b, j]], 0 resid[b * M + j]
+    int out_packed;                 // SwiGLU, at most 16 rows: write the gated rows as packed fragments
     int B, M, K, N, n_pos, Hq, Hkv, D;
     int splits, kc;                 // K splits of kc columns each (1: one pass, fused epilogue)
     float *part;                    // splits > 1: fp32 partial sums [splits, B*M, N (2N for SwiGLU)]
@@ -135,6 +138,9 @@ struct GemmPlan {
     size_t part_bytes;
 };
 GemmPlan plan_gemm(int rows, int N, int K, bool swiglu);
+bool gemm_skinny(int rows);         // rows handled by the weight-streaming kernel (a_mode 3 / out_packed)
+// The A rows of a skinny product (a_mode 0-2) as packed fragments: 16 K bf16 at dst.
+hipError_t launch_pack_rows(const GemmArgs &a, uint16_t *dst, hipStream_t stream);
 
 // The right-to-left selective scan of one step (r2l_kernels.hip).
 struct R2LArgs {
@@ -169,6 +175,8 @@ hipError_t launch_step_attn(const AttnArgs &a, hipStream_t stream, hipEvent_t pa
 hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after);
 hipError_t launch_block_buffer(const BBArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
+// Row-major bf16 W [N, K] -> the fragment-packed layout (N % 16 == 0, K % 32 == 0).
+hipError_t launch_pack_weights(const uint16_t *w, uint16_t *packed, int N, int K, hipStream_t stream);
 hipError_t launch_r2l(const R2LArgs &a, hipStream_t stream);
 
 // ---- direct global-to-LDS loads ------------------------------------------

@@ -28,6 +28,15 @@
 // conflicts.
 // Workgroups are ordered weight-tile major and dealt so that the row tiles
 // sharing a weight tile run on one XCD (one L2).
+//
+// Weights may also come fragment-packed (dlm_pack_weights): for each tile
+// of 16 rows and each step of 32 columns, 1 KB holding the tile's 16 x 32
+// block in the register order of an MFMA operand (64 lanes x 8 bf16, lane
+// l: row l % 16, columns 8 (l / 16) .. + 7).  One wave load then reads 1 KB
+// of contiguous memory and hands every lane its fragment; with row-major
+// weights the same load touches 64 bytes in each of 16 rows, which streams
+// markedly slower from HBM (measured on MI355X: about 6.3 against 5.4 TB/s
+// for a bare read, 24 against 34 us for the 16-row q/k/v product).
 #include "dlm_internal.h"
 
 #include <math.h>
@@ -192,11 +201,18 @@ gemm_kernel(GemmArgs a)
     const i32x4 w1 = dma_view(SWIGLU ? a.w1 : a.w0, (long)a.N * a.K * 2);
     int woff[NB];
     for (int u = 0; u < NB; ++u) {
+        if (a.w_packed) {
+            // 1 KB fragment g of the tile: 16-row group g / (BK / 32), 32-column step g % (BK / 32)
+            const int g = 4 * u + wid, n16 = n0 / 16 + g / (BK / 32);
+            woff[u] = 16 * n16 < a.N ? ((n16 * (a.K / 32) + g % (BK / 32)) * 512 + lane * 8) * 2 : -1;
+            continue;
+        }
         const int byte = (4 * u + wid) * 1024 + lane * 16;
         const int row = byte / (2 * BK), sl = (byte >> 4) % CH;
         const int n = n0 + row;
         woff[u] = n < a.N ? (n * a.K + (sl ^ gswz<BK>(row)) * 8) * 2 : -1;
     }
+    const int wk = a.w_packed ? 32 : 2;      // weight bytes per column step (k0 a multiple of 32)
 
     // Load the K step at k0 into a slot; a step past this split's end
     // (k0 >= kend) loads zeros, so every stage issues the same loads.
@@ -213,7 +229,7 @@ gemm_kernel(GemmArgs a)
         }
         uint16_t *ws = slot + kBM * BK;
         for (int u = 0; u < NB; ++u) {
-            const int off = (woff[u] < 0 || !live) ? kOOB : woff[u] + k0 * 2;
+            const int off = (woff[u] < 0 || !live) ? kOOB : woff[u] + k0 * wk;
             dma16(w0, off, ws + (4 * u + wid) * 512);
             if (SWIGLU) dma16(w1, off, ws + kBN * BK + (4 * u + wid) * 512);
         }
@@ -228,8 +244,9 @@ gemm_kernel(GemmArgs a)
             ard[i][kk] = ra * BK + (((2 * kk + hh) ^ gswz<BK>(ra)) * 8);
         }
         for (int j = 0; j < TJ; ++j) {
-            const int rw = wn * 32 * TJ + 32 * j + l32;
-            wrd[j][kk] = kBM * BK + rw * BK + (((2 * kk + hh) ^ gswz<BK>(rw)) * 8);
+            const int rw = wn * 32 * TJ + 32 * j + l32, c = 2 * kk + hh;
+            wrd[j][kk] = kBM * BK + (a.w_packed ? ((rw / 16) * (BK / 32) + c / 4) * 512 + ((c % 4) * 16 + rw % 16) * 8
+                                                : rw * BK + ((c ^ gswz<BK>(rw)) * 8));
         }
     }
 
@@ -308,6 +325,133 @@ gemm_kernel(GemmArgs a)
         }
 }
 
+// Skinny products: at most 16 rows (late denoising steps, small M_t),
+// where the work is streaming the weights once.  A workgroup owns 16 weight
+// rows over the whole K (so no K-split partials and no second kernel); its
+// KW waves take a KW-th of K each, and their sums are added in LDS in a
+// fixed order.  KW is chosen per launch so that all waves of the grid are
+// resident at once (a second, partly filled round of workgroups would
+// leave the stream without enough loads in flight).  C^T = W A^T with
+// v_mfma_f32_16x16x32_bf16: operand A is 16 weight rows x 32 k, lane l
+// holding row l % 16, k = 8 (l / 16) .. + 7 (one packed fragment, or 64
+// bytes per weight row of a row-major matrix), loaded straight into
+// registers (non-temporal: each weight is read once); operand B is 32 k x
+// 16 activation rows in the same lane order, read from L2 (every workgroup
+// reads the same activation rows), as one 1 KB fragment per k step when
+// they come packed (a_mode 3).  U k steps of loads are issued a buffer
+// ahead of their MFMAs (about 12 16-byte loads per lane per buffer, two
+// buffers).  With more than 16 rows the tiled kernel is faster (measured on
+// MI355X with packed weights: 28 against 37 us for q/k/v at 32 rows).
+constexpr int kSkinnyRows = 16;
+
+// Packed position of element (r, n) of a 16-row activation block (the
+// operand order above): k step n / 32, lane (n % 32) / 8 * 16 + r.
+__device__ __forceinline__ long packed_act(int r, int n)
+{
+    return ((long)(n >> 5) * 64 + ((n & 31) >> 3) * 16 + r) * 8 + (n & 7);
+}
+
+template <bool SWIGLU, int KW>
+__global__ __launch_bounds__(64 * KW) void skinny_kernel(GemmArgs a)
+{
+    constexpr int NW = SWIGLU ? 2 : 1;
+    constexpr int U = SWIGLU ? 3 : 6;            // k steps (of 32) per register buffer
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    __shared__ float red_s[KW][NW][16][17];      // each wave's sums [row][n], padded
+
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int ksteps = a.K / 32;
+    const int per = (ksteps + KW - 1) / KW;
+    const int sb = min(ksteps, wid * per), se = min(ksteps, sb + per);
+
+    // this lane's weight fragment at k step 0, and the distance of k steps
+    // (in 16-byte units): packed, the tile's steps are 1 KB apart; row-major,
+    // rows past N read row 0 (their sums are never stored)
+    const long wbase = a.w_packed ? (long)blockIdx.x * ksteps * 512 + 8 * lane
+                                  : (long)(n0 + l16 < a.N ? n0 + l16 : 0) * a.K + 8 * q4;
+    const int wstep = a.w_packed ? 64 : 4;
+    const v4u *wp[NW];
+    wp[0] = reinterpret_cast<const v4u *>(a.w0 + wbase);
+    if (SWIGLU) wp[NW - 1] = reinterpret_cast<const v4u *>(a.w1 + wbase);
+    // activation row l16: element offset of this lane's first k (rows past
+    // the end read row 0; their sums are never stored, and an activation row
+    // only feeds its own output column)
+    const int r = row_valid(a, l16) ? l16 : 0;
+    const int rb = r / a.M, rj = r - rb * a.M;
+    const long abase = a.a_mode == 3 ? 8L * lane
+                     : (a.a_mode == 1 ? ((long)rb * a.n_pos + a.act[rb * a.M + rj]) * a.K
+                      : a.a_mode == 2 ? ((long)rb * a.Hq * a.M + rj) * a.D
+                                      : (long)r * a.K) + 8 * q4;
+    // offset of k step st (32 columns; in mode 2 a step never straddles two
+    // heads, D being a multiple of 32): the same for every lane of the wave
+    auto a_step = [&](int st) -> long {
+        const int kk = 32 * st;
+        return a.a_mode == 3 ? 16L * kk : a.a_mode == 2 ? (long)(kk / a.D) * a.M * a.D + kk % a.D : (long)kk;
+    };
+
+    f32x4 acc[NW];
+    for (int w = 0; w < NW; ++w) acc[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Two register buffers of U k steps: the loads of the next U steps are
+    // issued before the MFMAs of the current ones.  Every load is
+    // unconditional (a predicated load would make the compiler wait for it
+    // before the zero of the other branch): steps past the wave's range
+    // reload its last step and are not multiplied.
+    v4u wv[2][NW][U], av[2][U];
+    auto load = [&](int bi, int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int st = min(s + u, se - 1);
+            for (int w = 0; w < NW; ++w) wv[bi][w][u] = __builtin_nontemporal_load(wp[w] + wstep * st);
+            av[bi][u] = *reinterpret_cast<const v4u *>(a.a + abase + a_step(st));
+        }
+    };
+    auto mult = [&](int bi, int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s + u < se) {
+                for (int w = 0; w < NW; ++w)
+                    acc[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        *reinterpret_cast<const bf16x8 *>(&wv[bi][w][u]),
+                        *reinterpret_cast<const bf16x8 *>(&av[bi][u]), acc[w], 0, 0, 0);
+            }
+        }
+    };
+    if (sb < se) {
+        load(0, sb);
+        for (int s = sb; s < se; s += 2 * U) {
+            if (s + U < se) load(1, s + U);
+            mult(0, s);
+            if (s + U >= se) break;
+            if (s + 2 * U < se) load(0, s + 2 * U);
+            mult(1, s + U);
+        }
+    }
+    // lane (l16, q4) holds rows (weight) 4 q4 + i of column (activation row) l16
+    for (int w = 0; w < NW; ++w)
+        for (int i = 0; i < 4; ++i) red_s[wid][w][l16][4 * q4 + i] = acc[w][i];
+    __syncthreads();
+    for (int idx = tid; idx < 16 * 16; idx += 64 * KW) {
+        const int nl = idx % 16, rr = idx / 16;
+        const int nn = n0 + nl;
+        if (nn >= a.N || !row_valid(a, rr)) continue;
+        float v[NW];
+        for (int w = 0; w < NW; ++w) {
+            float t[KW];
+            for (int q = 0; q < KW; ++q) t[q] = red_s[q][w][rr][nl];
+            for (int h = KW / 2; h >= 1; h >>= 1)   // fixed tree order
+                for (int q = 0; q < h; ++q) t[q] += t[q + h];
+            v[w] = t[0];
+        }
+        if (SWIGLU && a.out_packed)   // gated rows straight into the down projection's operand order
+            a.out[packed_act(rr, nn)] = to_bf16(v[0] / (1.f + __expf(-v[0])) * v[NW - 1]);
+        else
+            store_out(a, SWIGLU, rr, nn, v[0], v[NW - 1]);
+    }
+}
+
 // Sum the K splits of each valid element in split order (deterministic)
 // and apply the epilogue.  One thread per element.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, int swiglu)
@@ -327,11 +471,71 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, int swiglu
     store_out(a, swiglu != 0, r, n, v, up);
 }
 
+// The activation rows of a skinny product (at most 16, a_mode 0, 1 or 2)
+// as packed operand fragments: one thread per 16-byte chunk o, k step
+// o / 64, lane o % 64 (row lane % 16, columns 32 step + 8 (lane / 16) ..
+// + 7); rows that are not valid are written as zeros.  One read of the rows
+// here saves every workgroup of the product a 16-row gather per k step.
+__global__ __launch_bounds__(256) void pack_rows_kernel(GemmArgs a, uint16_t *dst)
+{
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= a.K / 32 * 64) return;
+    const int lane = o % 64, r = lane % 16, k = (o / 64) * 32 + (lane / 16) * 8;
+    v4u v = v4u{0u, 0u, 0u, 0u};
+    if (row_valid(a, r)) {
+        const int b = r / a.M, j = r - b * a.M;
+        const long src = a.a_mode == 1 ? ((long)b * a.n_pos + a.act[b * a.M + j]) * a.K + k
+                       : a.a_mode == 2 ? ((long)b * a.Hq * a.M + j) * a.D + (long)(k / a.D) * a.M * a.D + k % a.D
+                                       : (long)r * a.K + k;
+        v = *reinterpret_cast<const v4u *>(a.a + src);
+    }
+    reinterpret_cast<v4u *>(dst)[o] = v;
+}
+
+// One thread per 16-byte chunk of the packed layout: chunk o is lane
+// o % 64 of fragment o / 64 (16-row group f / (K/32), 32-column step
+// f % (K/32)); the lane holds row 16 group + lane % 16, columns
+// 32 step + 8 (lane / 16) .. + 7.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *w, uint16_t *p, int N, int K)
+{
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    const long o = (long)blockIdx.x * 256 + threadIdx.x;
+    if (o >= (long)N * K / 8) return;
+    const long f = o / 64;
+    const int lane = (int)(o % 64), ks = K / 32;
+    const long row = (f / ks) * 16 + lane % 16;
+    const int col = (int)(f % ks) * 32 + (lane / 16) * 8;
+    reinterpret_cast<v4u *>(p)[o] = *reinterpret_cast<const v4u *>(w + row * K + col);
+}
+
 }  // namespace
+
+hipError_t launch_pack_rows(const GemmArgs &a, uint16_t *dst, hipStream_t stream)
+{
+    if (!gemm_skinny(a.B * a.M) || a.a_mode == 3) return hipErrorInvalidValue;
+    const int chunks = a.K / 32 * 64;
+    pack_rows_kernel<<<(chunks + 255) / 256, 256, 0, stream>>>(a, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(const uint16_t *w, uint16_t *packed, int N, int K, hipStream_t stream)
+{
+    const long chunks = (long)N * K / 8;
+    if (chunks == 0) return hipSuccess;
+    pack_weights_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(w, packed, N, K);
+    return hipGetLastError();
+}
 
 GemmPlan plan_gemm(int rows, int N, int K, bool swiglu)
 {
     GemmPlan p{};
+    if (gemm_skinny(rows)) {   // skinny_kernel: whole K per workgroup, no partials
+        p.kc = K;
+        p.splits = 1;
+        p.part_bytes = 0;
+        return p;
+    }
     const int bm = gemm_bm(rows);
     const long tiles = (long)((rows + bm - 1) / bm) * ((N + kBN - 1) / kBN);
     // Too few output tiles to fill the chip: split K (at least 256 columns
@@ -355,8 +559,31 @@ GemmPlan plan_gemm(int rows, int N, int K, bool swiglu)
     return p;
 }
 
+bool gemm_skinny(int rows) { return rows <= kSkinnyRows; }
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 {
+    const int rows = a.B * a.M;
+    if (rows == 0) return hipSuccess;
+    if ((a.a_mode == 3 || a.out_packed) && !gemm_skinny(rows)) return hipErrorInvalidValue;
+    if (gemm_skinny(rows)) {
+        const int tiles = (a.N + 15) / 16;
+        // four waves per SIMD fit at this kernel's register use: the widest
+        // K split whose grid still fits in one round (up to 8 for the SwiGLU
+        // pair, whose sums take twice the LDS)
+        const long slots = 4L * kNumCU * 4;
+        const int kw = !a.w1 && tiles * 16L <= slots ? 16 : tiles * 8L <= slots ? 8 : 4;
+        const dim3 grid((unsigned)tiles), block(64 * kw);
+        if (a.w1) {
+            if (kw == 8) skinny_kernel<true, 8><<<grid, block, 0, stream>>>(a);
+            else skinny_kernel<true, 4><<<grid, block, 0, stream>>>(a);
+        } else {
+            if (kw == 16) skinny_kernel<false, 16><<<grid, block, 0, stream>>>(a);
+            else if (kw == 8) skinny_kernel<false, 8><<<grid, block, 0, stream>>>(a);
+            else skinny_kernel<false, 4><<<grid, block, 0, stream>>>(a);
+        }
+        return hipGetLastError();
+    }
     const int bm = gemm_bm(a.B * a.M);
     const long tiles = (long)((a.B * a.M + bm - 1) / bm) * ((a.N + kBN - 1) / kBN) * a.splits;
     if (tiles == 0) return hipSuccess;

@@ -395,7 +395,23 @@ typedef struct {
     const int32_t *m_active;    /* optional device int32 [B] (NULL: all M rows) */
     int32_t Hq, Hkv, D;         /* attention heads (Hq % Hkv == 0) and head width */
     int32_t F;                  /* feed-forward width, a multiple of 64 */
+    int32_t weights_packed;     /* 0: every weight argument row-major as stated below;
+                                   1: every one in the layout of dlm_pack_weights */
 } dlm_layer_desc;
+
+/* Repack a bf16 weight matrix for the layer calls (weights_packed = 1): the
+ * same products, bit for bit, from a layout that streams from HBM faster
+ * when few rows are active (each 1 KB of it is one MFMA operand).  For each
+ * group of 16 rows g and each step of 32 columns s (s < K/32), 1 KB at
+ * element offset (g K/32 + s) * 512 holds 64 lanes of 8 bf16: lane l has
+ * row 16 g + l % 16, columns 32 s + 8 (l / 16) .. + 7.
+ *   w       bf16 [N, K] row-major (device), read
+ *   packed  bf16, N * K elements (device), written; must not overlap w
+ * N a multiple of 16, K of 32 (every layer weight qualifies: its dimensions
+ * are multiples of 64).  Done once per weight, e.g. at load time.  One
+ * kernel on `stream`.  Errors: DLM_E_NULL, DLM_E_SHAPE, DLM_E_UNSUPPORTED,
+ * DLM_E_DESC (overlap), DLM_E_HIP. */
+int dlm_pack_weights(const void *w, void *packed, int32_t N, int32_t K, hipStream_t stream);
 
 /* Every call takes a device workspace of at least dlm_layer_workspace_bytes()
  * (fp32 partial sums when a product has too few output tiles to fill the chip

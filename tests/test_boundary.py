@@ -313,14 +313,34 @@ def test_layer_call_specific_checks():
     c = dlm._c_layer(L)
     rc = dlm.lib.dlm_ffn(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None)
     assert rc == dlm.DLM_E_WORKSPACE
-    # few output tiles and a long K: K is split and the projections need partial sums too
-    c = dlm._c_layer(_layer(d=1024, M=8))
+    # over 16 rows, few output tiles and a long K: K is split and the
+    # projections need partial sums too (up to 16 rows one workgroup takes
+    # the whole K: no partials, only the gated rows and the packed rows of h)
+    assert dlm.dlm_layer_workspace_bytes(_layer(d=1024, M=8)) == 16 * 384 * 2 + 16 * 1024 * 2
+    c = dlm._c_layer(_layer(d=1024, M=40))
     assert dlm.lib.dlm_proj_qkv(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == \
         dlm.DLM_E_WORKSPACE
-    c = dlm._c_layer(_layer(Hq=16, Hkv=2, M=8))          # K = Hq D = 1024
+    c = dlm._c_layer(_layer(Hq=16, Hkv=2, M=40))         # K = Hq D = 1024
     assert dlm.lib.dlm_proj_out(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == \
         dlm.DLM_E_WORKSPACE
     assert dlm.lib.dlm_proj_qkv(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == dlm.DLM_E_NULL
+
+
+def test_pack_weights_rejects():
+    lib = dlm.lib
+    assert lib.dlm_pack_weights(FAKE, FAKE + (1 << 24), 24, 64, None) == dlm.DLM_E_UNSUPPORTED   # N % 16
+    assert lib.dlm_pack_weights(FAKE, FAKE + (1 << 24), 32, 48, None) == dlm.DLM_E_UNSUPPORTED   # K % 32
+    assert lib.dlm_pack_weights(FAKE, FAKE + (1 << 24), -16, 64, None) == dlm.DLM_E_SHAPE
+    assert lib.dlm_pack_weights(FAKE, FAKE + (1 << 24), 1 << 16, 1 << 15, None) == dlm.DLM_E_SHAPE
+    assert lib.dlm_pack_weights(None, FAKE, 32, 64, None) == dlm.DLM_E_NULL
+    assert lib.dlm_pack_weights(FAKE, FAKE + 1024, 32, 64, None) == dlm.DLM_E_DESC             # overlap
+    assert lib.dlm_pack_weights(None, None, 0, 64, None) == dlm.DLM_OK                           # nothing to do
+    assert dlm.dlm_layer_workspace_bytes(_layer(weights_packed=True)) == dlm.dlm_layer_workspace_bytes(_layer())
+    c = dlm._c_layer(_layer())
+    c.weights_packed = 2
+    n = __import__("ctypes").c_size_t(0)
+    assert lib.dlm_layer_workspace_bytes(__import__("ctypes").byref(c), __import__("ctypes").byref(n)) == \
+        dlm.DLM_E_DESC
 
 
 def test_posterior_rejects_nan_gate():

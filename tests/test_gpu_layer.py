@@ -68,12 +68,19 @@ CASES = {
     "rows_cut": dict(B=2, n_pos=260, d=320, Hq=4, Hkv=4, D=64, F=192, M=257, m=[0, 129]),
     # few rows, long K: every product splits K (partial sums and the reduction)
     "split_k": dict(B=2, n_pos=64, d=1024, Hq=16, Hkv=4, D=64, F=1024, M=40, m=[33, 40]),
-    # up to 64 rows in all: the 32- and 64-row tiles with their deep stage
+    # 17 to 64 rows in all: the 32- and 64-row tiles with their deep stage
     # rings; K splits, ragged column tiles, several batch entries sharing
     # one row tile, an entry with no rows
-    "skinny32_split_k": dict(B=1, n_pos=100, d=1024, Hq=16, Hkv=4, D=64, F=1024, M=24, m=[17]),
-    "skinny32_batches": dict(B=4, n_pos=40, d=256, Hq=4, Hkv=2, D=64, F=384, M=8, m=[8, 0, 5, 8]),
-    "skinny64_ragged": dict(B=2, n_pos=70, d=320, Hq=4, Hkv=4, D=64, F=192, M=30, m=[30, 11]),
+    "rows32_split_k": dict(B=1, n_pos=100, d=1024, Hq=16, Hkv=4, D=64, F=1024, M=24, m=[17]),
+    "rows32_batches": dict(B=4, n_pos=40, d=256, Hq=4, Hkv=2, D=64, F=384, M=8, m=[8, 0, 5, 8]),
+    "rows64_ragged": dict(B=2, n_pos=70, d=320, Hq=4, Hkv=4, D=64, F=192, M=30, m=[30, 11]),
+    # at most 16 rows: the weight-streaming kernel (whole K per workgroup,
+    # K split over its waves, the gated rows handed on packed); batch
+    # entries sharing the 16 rows with one empty, five rows with waves
+    # that get no K step, and 384 column tiles (eight-way K splits)
+    "skinny16_batches": dict(B=4, n_pos=40, d=256, Hq=4, Hkv=2, D=64, F=384, M=4, m=[4, 0, 3, 4]),
+    "skinny_rows5": dict(B=1, n_pos=70, d=320, Hq=4, Hkv=4, D=64, F=192, M=5, m=[5]),
+    "skinny_kw8": dict(B=1, n_pos=64, d=512, Hq=32, Hkv=8, D=128, F=6144, M=16, m=[16]),
 }
 
 
@@ -115,19 +122,21 @@ def check_layer(c, qg, kg, vg, hg, yg):
     return worst
 
 
-def _run_layer(c, m_dev, sentinel=5.0):
+def _run_layer(c, m_dev, sentinel=5.0, packed=False):
     import denoising_step_amd as dlm
     L = _layer_desc(c, m_dev)
+    L.weights_packed = packed
+    wt = (lambda bits: dlm.dlm_pack_weights(_dev(bits))) if packed else _dev
     x = _dev(c.x)
     q = torch.full((c.B, c.Hq, c.M, c.D), sentinel, dtype=torch.bfloat16, device="cuda")
     k = torch.full((c.B, c.Hkv, c.M, c.D), sentinel, dtype=torch.bfloat16, device="cuda")
     v = torch.full_like(k, sentinel)
     h = torch.full((c.B, c.M, c.d), sentinel, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(max(1, dlm.dlm_layer_workspace_bytes(L)), dtype=torch.uint8, device="cuda")
-    dlm.dlm_proj_qkv(L, x, _dev(c.w_qkv), q, k, v, ws)
-    dlm.dlm_proj_out(L, x, _dev(c.attn_out), _dev(c.w_o), h, ws)
+    dlm.dlm_proj_qkv(L, x, wt(c.w_qkv), q, k, v, ws)
+    dlm.dlm_proj_out(L, x, _dev(c.attn_out), wt(c.w_o), h, ws)
     x2 = x.clone()
-    dlm.dlm_ffn(L, _dev(c.h), _dev(c.w_gate), _dev(c.w_up), _dev(c.w_down), x2, ws)
+    dlm.dlm_ffn(L, _dev(c.h), wt(c.w_gate), wt(c.w_up), wt(c.w_down), x2, ws)
     torch.cuda.synchronize()
     return _host(q), _host(k), _host(v), _host(h), _host(x2)
 
@@ -158,8 +167,9 @@ def test_layer_calls_match_oracle(name):
 def test_layer_full_size_sampled(M):
     """The LLaDA-8B-shaped layer (width 4096, 32 heads of 128, feed-forward
     12288) with M of 2048 positions active (128-row tiles two to a CU; up
-    to 256 rows, the one-per-CU deep-ring tiles of 128, 64 and 32 rows with
-    K splits): sampled rows against the oracle, each element against the
+    to 256 rows, the one-per-CU deep-ring tiles with K splits; up to 16,
+    the weight-streaming kernel with four- and sixteen-way K splits in the
+    workgroup): sampled rows against the oracle, each element against the
     same bound."""
     c = W.layer_llada(M=M, n_pos=2048)
     _say(f"layer llada full size M={M}")
@@ -171,6 +181,58 @@ def test_layer_full_size_sampled(M):
     yg = xg[:, c.active_idx[0, rows]]
     worst = check_layer(sub, qg[:, :, rows], kg[:, :, rows], vg[:, :, rows], hg[:, rows], yg)
     _say(f"  worst error / bound = {worst:.3f}")
+
+
+def test_pack_weights_layout():
+    """dlm_pack_weights against the layout as the header states it: element
+    (n, k) at ((n / 16) (K / 32) + k / 32) 512 + ((k % 32) / 8 16 + n % 16) 8
+    + k % 8, bit for bit."""
+    import denoising_step_amd as dlm
+    rng = np.random.default_rng(3)
+    for N, K in ((16, 32), (48, 96), (4096, 4096)):
+        w = rng.integers(0, 1 << 16, size=(N, K), dtype=np.uint16)
+        got = dlm.dlm_pack_weights(_dev(w))
+        torch.cuda.synchronize()
+        from denoising_step_amd.runner import bf16_to_host
+        g = bf16_to_host(got).reshape(-1)
+        n, k = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+        pos = ((n // 16) * (K // 32) + k // 32) * 512 + ((k % 32) // 8 * 16 + n % 16) * 8 + k % 8
+        want = np.empty(N * K, np.uint16)
+        want[pos.reshape(-1)] = w.reshape(-1)
+        assert np.array_equal(g, want), (N, K)
+
+
+PACKED_CASES = ["skinny16_batches", "skinny_rows5", "skinny_kw8", "rows32_batches", "rows64_ragged",
+                "rows32_split_k", "split_k", "d256_gqa_ragged", "rows_cut"]
+
+
+@pytest.mark.parametrize("name", PACKED_CASES)
+def test_packed_weights_bit_exact(name):
+    """Weights in the packed layout give the row-major results bit for bit
+    (each MFMA sees the same operands in the same order), on both product
+    kernels: the weight-streaming one (up to 64 rows) and the tiled one."""
+    kw = dict(CASES[name])
+    m_list = kw.pop("m")
+    c = W.make_layer(name, m=m_list, seed=11, **kw)
+    _say(f"layer packed {name}")
+    m_dev = None if m_list is None else torch.tensor(m_list, dtype=torch.int32, device="cuda")
+    ref = _run_layer(c, m_dev)
+    got = _run_layer(c, m_dev, packed=True)
+    for r, g, nm in zip(ref, got, ("q", "k", "v", "h", "x")):
+        assert np.array_equal(r, g), nm
+
+
+@pytest.mark.parametrize("M", [16, 48, 200])
+def test_packed_weights_full_size(M):
+    """The LLaDA-8B-shaped layer with packed weights: bit for bit the
+    row-major results (16 rows: the weight-streaming kernel with its four-
+    and sixteen-way K splits; 48 and 200: the deep-ring tiles)."""
+    c = W.layer_llada(M=M, n_pos=2048)
+    _say(f"layer llada packed M={M}")
+    ref = _run_layer(c, None)
+    got = _run_layer(c, None, packed=True)
+    for r, g, nm in zip(ref, got, ("q", "k", "v", "h", "x")):
+        assert np.array_equal(r, g), nm
 
 
 def test_confidence_gate():
