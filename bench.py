@@ -29,6 +29,7 @@ import math
 import os
 import sys
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -139,12 +140,16 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_trace(path: str) -> str:
-    """Markdown table of a rocprofv3 kernel_trace.csv: per kernel, the
-    dispatch count and the mean, median, min and max duration in us."""
+def summarize_trace(path: str, kernel_re: Optional[str] = None) -> str:
+    """Markdown table of a rocprofv3 kernel_trace.csv: per kernel (those
+    whose name matches kernel_re, if given), the dispatch count and the
+    mean, median, min and max duration in us."""
+    import re
     import statistics
     by = {}
     for r in _read_csv(path):
+        if kernel_re and not re.search(kernel_re, r["Kernel_Name"]):
+            continue
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         by.setdefault(r["Kernel_Name"], []).append(d)
     lines = ["| kernel | calls | mean us | median us | min us | max us | total us |",
@@ -153,6 +158,70 @@ def summarize_trace(path: str) -> str:
         lines.append(f"| `{k}` | {len(v)} | {statistics.fmean(v):.2f} | {statistics.median(v):.2f} | "
                      f"{min(v):.2f} | {max(v):.2f} | {sum(v):.1f} |")
     return "\n".join(lines)
+
+
+LOOP_KERNELS = ("kv_scatter_kernel", "attn_fwd_kernel", "attn_combine_kernel", "colsum_kernel",
+                "colsum_reduce_kernel", "posterior_stream_kernel", "posterior_finish_kernel",
+                "block_buffer_kernel")
+
+
+def summarize_loop_trace(path: str) -> str:
+    """Per-step table of the last run in a kernel trace of `bench.py --loop`
+    (the graph replays), plus, per run, the gaps on the GPU around each
+    step: from the stand-in model's last kernel to the step's first, and
+    from the step's last kernel to the next kernel."""
+    import statistics
+
+    def short(n):
+        return n.split("(dlm")[0].split("::")[-1].split("<")[0].split("(")[0]
+
+    rows = sorted(_read_csv(path), key=lambda r: int(r["Start_Timestamp"]))
+    ks = [(short(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    segs, i = [], 0                       # maximal runs of step kernels: one step each
+    while i < len(ks):
+        if ks[i][0] in LOOP_KERNELS:
+            j = i
+            while j + 1 < len(ks) and ks[j + 1][0] in LOOP_KERNELS:
+                j += 1
+            segs.append((i, j))
+            i = j + 1
+        else:
+            i += 1
+    # runs: a Block Buffer initialisation (a lone block_buffer segment) starts each
+    runs, cur = [], []
+    for a, b in segs:
+        if a == b and ks[a][0] == "block_buffer_kernel":
+            if cur:
+                runs.append(cur)
+            cur = []
+        else:
+            cur.append((a, b))
+    if cur:
+        runs.append(cur)
+    cols = [c for c in LOOP_KERNELS]
+    out = ["| step | " + " | ".join(c.replace("_kernel", "") for c in cols) + " | sum |",
+           "|---" * (len(cols) + 2) + "|"]
+    for si, (a, b) in enumerate(runs[-1]):
+        d = {c: 0.0 for c in cols}
+        for n, t0, t1 in ks[a:b + 1]:
+            d[n] += (t1 - t0) / 1e3
+        out.append(f"| {si + 1} | " + " | ".join(f"{d[c]:.1f}" for c in cols) + f" | {sum(d.values()):.1f} |")
+    out += ["", "| run | steps | kernel time ms | gaps inside steps us | entry gap median us | exit gap median us |",
+            "|---|---|---|---|---|---|"]
+    for ri, run in enumerate(runs):
+        busy = inside = 0.0
+        ent, ext = [], []
+        for a, b in run:
+            busy += sum(t1 - t0 for _, t0, t1 in ks[a:b + 1]) / 1e3
+            inside += ((ks[b][2] - ks[a][1]) - sum(t1 - t0 for _, t0, t1 in ks[a:b + 1])) / 1e3
+            if a > 0:
+                ent.append((ks[a][1] - ks[a - 1][2]) / 1e3)
+            if b + 1 < len(ks):
+                ext.append((ks[b + 1][1] - ks[b][2]) / 1e3)
+        out.append(f"| {ri + 1} | {len(run)} | {busy / 1e3:.3f} | {inside:.1f} | "
+                   f"{statistics.median(ent) if ent else float('nan'):.2f} | "
+                   f"{statistics.median(ext) if ext else float('nan'):.2f} |")
+    return "\n".join(out)
 
 
 def summarize_pmc(path: str) -> str:
@@ -405,7 +474,11 @@ def layer_bench(args):
     packed = [{k: dlm.dlm_pack_weights(t) for k, t in s_.items()} for s_ in sets]
     x = torch.randn((1, n_pos, d), generator=gen, device=dev).to(torch.bfloat16)
     res = []
-    for M in (1024, 512, 256, 128, 64, 32, 16):
+    m_list = [int(v) for v in args.layer_m.split(",")] if args.layer_m else [1024, 512, 256, 128, 64, 32, 16]
+    layouts = [("packed", packed), ("row_major", sets)]
+    if args.layer_layout != "both":
+        layouts = [lw for lw in layouts if lw[0] == args.layer_layout]
+    for M in m_list:
         act = torch.sort(torch.randperm(n_pos, generator=gen, device=dev)[:M])[0].to(torch.int32)[None]
         q = torch.empty((1, Hq, M, D), dtype=torch.bfloat16, device=dev)
         k = torch.empty((1, Hkv, M, D), dtype=torch.bfloat16, device=dev)
@@ -413,7 +486,7 @@ def layer_bench(args):
         ao = torch.randn((1, Hq, M, D), generator=gen, device=dev).to(torch.bfloat16)
         h = torch.empty((1, M, d), dtype=torch.bfloat16, device=dev)
         row = {"M_t": M}
-        for layout, ws_ in (("packed", packed), ("row_major", sets)):
+        for layout, ws_ in layouts:
             L = dlm.LayerDesc(B=1, n_pos=n_pos, d=d, M=M, active_idx=act, Hq=Hq, Hkv=Hkv, D=D, F=F,
                               weights_packed=layout == "packed")
             ws = torch.empty(max(1, dlm.dlm_layer_workspace_bytes(L)), dtype=torch.uint8, device=dev)
@@ -734,8 +807,11 @@ def main():
                     help="run only this loop on --config (profiler runs) and print its record")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration) and exit")
-    ap.add_argument("--summarize-trace", metavar="CSV",
-                    help="summarise a rocprofv3 kernel_trace.csv (per-kernel mean / median) and exit")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="CSV [REGEX]",
+                    help="summarise a rocprofv3 kernel_trace.csv (per-kernel mean / median; only the "
+                         "kernels matching REGEX if given) and exit")
+    ap.add_argument("--summarize-loop-trace", metavar="CSV",
+                    help="per-step table and step gaps of a kernel trace of --loop, and exit")
     ap.add_argument("--summarize-pmc", metavar="CSV",
                     help="summarise a rocprofv3 counter_collection.csv (per kernel and counter) and exit")
     ap.add_argument("--counter-fields", nargs="+", metavar="ARG",
@@ -745,6 +821,10 @@ def main():
                     help="time a whole multi-step SureLock run instead (its own JSON line)")
     ap.add_argument("--layer", action="store_true",
                     help="time a layer's active-row projections and feed-forward instead")
+    ap.add_argument("--layer-m", metavar="M,M,...",
+                    help="with --layer: only these active-row counts")
+    ap.add_argument("--layer-layout", choices=("both", "packed", "row_major"), default="both",
+                    help="with --layer: the weight layouts to time")
     ap.add_argument("--r2l", action="store_true",
                     help="time the R2LM right-to-left scan instead")
     args = ap.parse_args()
@@ -753,10 +833,13 @@ def main():
               "the multi-GPU sharding is a design, not a build", file=sys.stderr)
         sys.exit(2)
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace))
+        print(summarize_trace(*args.summarize_trace[:2]))
         return
     if args.summarize_pmc:
         print(summarize_pmc(args.summarize_pmc))
+        return
+    if args.summarize_loop_trace:
+        print(summarize_loop_trace(args.summarize_loop_trace))
         return
     if args.counter_fields:
         tag, kre, *kv = args.counter_fields

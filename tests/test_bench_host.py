@@ -113,6 +113,30 @@ def test_trace_and_counter_summaries(tmp_path):
     assert "| `kB` | FETCH_SIZE | 1 | 7 |" in s
 
 
+def test_loop_trace_summary(tmp_path):
+    """The --loop trace summariser: runs split at the Block Buffer
+    initialisations, per-step kernel sums of the last run, and the gaps
+    around and inside each step (in microseconds)."""
+    K = "void dlm::(anonymous namespace)::{}(dlm::X)"
+    ev = [("block_buffer_kernel", 0, 1000),                      # run 1: initialisation
+          ("feed", 2000, 3000),
+          ("attn_fwd_kernel", 4000, 6000), ("posterior_stream_kernel", 6000, 9000),
+          ("block_buffer_kernel", 9500, 10500),                  # step 1 of run 1 (0.5 us inside)
+          ("feed", 11500, 12000),
+          ("block_buffer_kernel", 13000, 14000),                 # run 2: initialisation
+          ("feed", 15000, 16000),
+          ("attn_fwd_kernel", 18000, 19000), ("posterior_finish_kernel", 19000, 21000),
+          ("block_buffer_kernel", 21000, 22000),                 # step 1 of run 2
+          ("feed", 30000, 31000)]
+    trace = tmp_path / "kernel_trace.csv"
+    trace.write_text("Kernel_Name,Start_Timestamp,End_Timestamp\n" +
+                     "".join(f"\"{K.format(n)}\",{a},{b}\n" for n, a, b in ev))
+    t = bench.summarize_loop_trace(str(trace))
+    assert "| 1 | 0.0 | 1.0 | 0.0 | 0.0 | 0.0 | 0.0 | 2.0 | 1.0 | 4.0 |" in t
+    assert "| 1 | 1 | 0.006 | 0.5 | 1.00 | 1.00 |" in t
+    assert "| 2 | 1 | 0.004 | 0.0 | 2.00 | 8.00 |" in t
+
+
 def test_stored_counters_follow_the_kernel_sources(tmp_path, monkeypatch):
     for tag in bench.COUNTER_SOURCES:
         for rel in bench.COUNTER_SOURCES[tag]:
