@@ -279,7 +279,7 @@ def time_loop(fn, n_sets, steps, warmup, per_step=False):
     return mean, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
-def cpu_baseline(w, budget_heads=None, budget_rows=512):
+def cpu_baseline(w, budget_heads=None, budget_rows=1024):
     """Time the oracle, as it stands, on a bounded sample of the workload and
     scale to the metric's unit (rows/s of a whole step): attention and
     column sums on a few whole GQA groups of q-heads (the per-head work is
@@ -287,7 +287,7 @@ def cpu_baseline(w, budget_heads=None, budget_rows=512):
     import oracle
     from workloads import AttnCase
     a, p = w.attn, w.post
-    H = budget_heads or max(1, min(a.Hq, 4))
+    H = budget_heads or max(1, min(a.Hq, 8))
     # keep whole GQA groups so the sample has the workload's structure
     H = max(a.G, (H // a.G) * a.G)
     sub = AttnCase(**{**a.__dict__, "Hq": H, "Hkv": H // a.G, "q": a.q[:, :H],

@@ -319,19 +319,11 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         if (a.kind == 2) {
             for (int s = tid; s < a.n_slots; s += NT) scode_s[s] = st[s] == 0 ? INT_MAX : gr[s];
         }
-        // Zero the tiles once, so no LDS byte a tile does not overwrite can
-        // ever be a non-finite value times a zero weight.  Only a ragged last
-        // tile (rows past kv_len) or rows hidden from the whole workgroup
-        // (block-causal and group masks) take the out-of-range path; split
-        // boundaries are whole tiles, so otherwise every row of every tile is
-        // loaded.
-        const bool ragged = a.kv_len % KT != 0 || a.kind != 0;
-        for (int i = tid; ragged && i < KT * D / 8; i += NT) {
-            reinterpret_cast<uint4 *>(Ks0)[i] = uint4{0, 0, 0, 0};
-            reinterpret_cast<uint4 *>(Ks1)[i] = uint4{0, 0, 0, 0};
-            reinterpret_cast<uint4 *>(Vs0)[i] = uint4{0, 0, 0, 0};
-            reinterpret_cast<uint4 *>(Vs1)[i] = uint4{0, 0, 0, 0};
-        }
+        // The tiles need no clearing: every load of a tile writes its 16
+        // bytes, and a row past kv_len or hidden from the whole workgroup is
+        // given an offset past the buffer's range, for which the load writes
+        // zeros (measured on MI355X), so no LDS byte read as part of a tile
+        // is left over from before.
 
         // This lane's query: packed row r = hl * Mv + j over the Mv valid rows
         // (the row stride in memory stays M).
@@ -644,7 +636,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
             __syncthreads();
         };
 
-        __syncthreads();   // slot codes, zeroed tiles and the query waves' code ranges visible
+        __syncthreads();   // slot codes and the query waves' code ranges visible
         if (a.kind != 0) {
             qmin = INT_MAX;
             qmax = INT_MIN;
