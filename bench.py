@@ -4,9 +4,11 @@
 A step is the whole hot path on one batch of seeded synthetic input:
 K/V scatter + sparse-query attention (pass 1) + column sums (pass 2) +
 posterior / KL lock test / unmask selection, through the two C-ABI calls
-on one stream.  The same step with dlm_posterior on a second stream (its
-selection waiting for the column sums through select.score_ready) is
-reported for reference ("ms_per_step_two_streams").
+on one stream (its time is "value").  Two schedules of the same step with
+dlm_posterior on a second stream are reported beside it: its logit stream
+from the start of the step ("ms_per_step_two_streams") and from the end of
+pass 1 (mask_desc.pass1_done, "ms_per_step_posterior_after_pass1"); in both
+its selection waits for the column sums through select.score_ready.
 Inputs are resident in HBM before timing starts.  Each timed loop (the
 whole step, pass 1 alone, both attention passes, the posterior alone)
 rotates over enough copies of its inputs that the bytes it touches total at
@@ -887,7 +889,7 @@ def main():
         "roofline": dominant_roofline(head),
     }
     for k in ("attention_pass1", "attention_passes_1_2", "posterior_roofline", "step_ms_p10_p50_p90",
-              "ms_per_step_two_streams", "timing"):
+              "ms_per_step_two_streams", "ms_per_step_posterior_after_pass1", "timing"):
         res[k] = head[k]
     if "cpu_baseline" in head:
         res["cpu_baseline"] = head["cpu_baseline"]
@@ -901,6 +903,7 @@ def main():
                 "config": rec["config"], "rows_per_s": rec["rows_per_s"], "ms_per_step": rec["ms_per_step"],
                 "step_ms_p10_p50_p90": rec["step_ms_p10_p50_p90"],
                 "ms_per_step_two_streams": rec["ms_per_step_two_streams"],
+                "ms_per_step_posterior_after_pass1": rec["ms_per_step_posterior_after_pass1"],
                 "attention_pass1": rec["attention_pass1"], "attention_passes_1_2": rec["attention_passes_1_2"],
                 "posterior_roofline": rec["posterior_roofline"], "timing": rec["timing"]}
     print(json.dumps(res), flush=True)

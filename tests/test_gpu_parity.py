@@ -542,6 +542,12 @@ def test_full_llada_bidirectional_spread():
     full_check(W.llada_bidirectional(spread=True))
 
 
+def test_full_llada_group():
+    """The same layer under a one-block GROUP mask: every tile classified
+    visible, the results those of the FULL mask's path."""
+    full_check(W.llada_group())
+
+
 @pytest.mark.parametrize("variant", ["group", "dummy", "block_causal", "two_groups"])
 def test_full_mbd_multiblock(variant):
     w = W.mbd_multiblock(variant=variant)

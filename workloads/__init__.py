@@ -593,8 +593,22 @@ def r2l_bifocal(seed=0) -> R2LCase:
     return make_r2l("r2l_bifocal", B=8, L=256, E=2048, N=16, config_id=98, seed=seed)
 
 
+def llada_group(seed=0) -> Workload:
+    """The LLaDA-like layer's inputs under a one-block GROUP mask over the
+    whole sequence (the multi-step run's mask shape at M_t = 1024): every
+    key visible to every query, so it isolates what the GROUP mask itself
+    costs against the FULL mask on the same shape."""
+    w = llada_bidirectional(seed)
+    a = w.attn
+    a2 = AttnCase(**{**a.__dict__, "kind": MASK_GROUP, "prefix_len": 0, "block_size": a.kv_len,
+                     "n_slots": 1, "slot_state": np.full((a.B, 1), SLOT_ACTIVE, np.uint8),
+                     "slot_group": np.zeros((a.B, 1), np.int32)})
+    return Workload(a2, w.post, "LLaDA-like layer under a one-block group mask")
+
+
 CONFIGS = {
     "tiny": tiny,
+    "llada_group": llada_group,
     "llada_bidirectional": llada_bidirectional,
     "llada_bidirectional_spread": lambda seed=0: llada_bidirectional(seed, spread=True),
     "mbd_multiblock": mbd_multiblock,
