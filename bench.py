@@ -259,6 +259,27 @@ def copy_probe(n_bytes: int = 256 << 20, reps: int = 5):
     print(json.dumps({"copy_probe_bytes": n_bytes, "reps": reps}), flush=True)
 
 
+def hbm_ceilings(gib: int = 2, reps: int = 10) -> dict:
+    """Measured streaming ceilings of this GPU, for context beside the 8 TB/s
+    nameplate: a device-to-device copy (read + write bytes per second) and a
+    read-only full reduction (torch.sum), each over GiB-sized buffers that
+    rotate past the MALL, timed with HIP events."""
+    import torch
+    n = (gib << 30) // 4
+    bufs = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    dst = torch.empty_like(bufs[0])
+    out = {}
+    for name, fn, bytes_per in (("copy_gbs", lambda i: dst.copy_(bufs[i % 2]), 8 * n),
+                                ("read_gbs", lambda i: torch.sum(bufs[i % 2]), 4 * n)):
+        ms = time_loop(fn, 2, reps, 3)
+        out[name] = round(bytes_per / ms / 1e6, 0)
+    out["method"] = (f"{gib} GiB fp32 buffers, two rotating; copy = torch copy_ (read + write bytes), "
+                     "read = torch.sum (read bytes); HIP events over 10 calls after 3 warm-up")
+    del bufs, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_loop(fn, n_sets, steps, warmup, per_step=False):
     """ms per call over `steps` timed calls after `warmup` untimed ones,
     bracketed by synchronisations; with per_step, also every call's own
@@ -888,6 +909,10 @@ def main():
         "config": head["config"],
         "roofline": dominant_roofline(head),
     }
+    ceil = hbm_ceilings()
+    res["hbm_ceilings"] = ceil
+    pr = head["posterior_roofline"]
+    pr["frac_of_measured_read"] = round(pr["achieved"] / ceil["read_gbs"], 3) if ceil.get("read_gbs") else None
     for k in ("attention_pass1", "attention_passes_1_2", "posterior_roofline", "step_ms_p10_p50_p90",
               "ms_per_step_two_streams", "ms_per_step_posterior_after_pass1", "timing"):
         res[k] = head[k]

@@ -901,50 +901,68 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a)
     constexpr int RPB = 256 / PER_ROW;  // rows per block
     constexpr int NB = kCombineBatch;
     const long rows_total = (long)a.B * a.Hq * a.M;
-    const long row = (long)blockIdx.x * RPB + threadIdx.x / PER_ROW;
     const int d4 = threadIdx.x % PER_ROW;
-    if (row >= rows_total) return;
-    const int b = (int)(row / ((long)a.Hq * a.M));
-    if (a.m_valid && (int)(row % a.M) >= valid_rows(a, b)) return;
-    const int ns = splits_for(a, b);
-    if (ns == 1) return;   // pass 1 wrote this row directly
-    const float *ls = a.ws_l + row;
-    const float4 *os = reinterpret_cast<const float4 *>(a.ws_o + row * D) + d4;
-    const long ostride = rows_total * PER_ROW;     // float4 between splits
-    float lv[NB];
-    float4 ov[NB];
-    for (int s = 0; s < NB; ++s) {
-        if (s < ns) {
-            lv[s] = ls[s * rows_total];
-            ov[s] = os[s * ostride];
+    // Merge the ns key splits of one row (fixed split order).
+    auto combine_row = [&](long row, int ns) {
+        const float *ls = a.ws_l + row;
+        const float4 *os = reinterpret_cast<const float4 *>(a.ws_o + row * D) + d4;
+        const long ostride = rows_total * PER_ROW;     // float4 between splits
+        float lv[NB];
+        float4 ov[NB];
+        for (int s = 0; s < NB; ++s) {
+            if (s < ns) {
+                lv[s] = ls[s * rows_total];
+                ov[s] = os[s * ostride];
+            }
+        }
+        float m = -INFINITY;
+        for (int s = 0; s < NB; ++s)
+            if (s < ns) m = fmaxf(m, lv[s]);
+        for (int s = NB; s < ns; ++s) m = fmaxf(m, ls[s * rows_total]);
+        float4 res = {0.f, 0.f, 0.f, 0.f};
+        float L = -INFINITY;
+        if (m != -INFINITY) {
+            float sum = 0.f;
+            for (int s = 0; s < NB; ++s)
+                if (s < ns) sum += fast_exp2((lv[s] - m) * kLog2e);
+            for (int s = NB; s < ns; ++s) sum += fast_exp2((ls[s * rows_total] - m) * kLog2e);
+            L = m + logf(sum);
+            auto add = [&](float l, const float4 &v) {
+                const float w = fast_exp2((l - L) * kLog2e);
+                res.x = fmaf(w, v.x, res.x);
+                res.y = fmaf(w, v.y, res.y);
+                res.z = fmaf(w, v.z, res.z);
+                res.w = fmaf(w, v.w, res.w);
+            };
+            for (int s = 0; s < NB; ++s)
+                if (s < ns) add(lv[s], ov[s]);
+            for (int s = NB; s < ns; ++s) add(ls[s * rows_total], os[s * ostride]);
+        }
+        __bf16 bv[4] = {(__bf16)res.x, (__bf16)res.y, (__bf16)res.z, (__bf16)res.w};
+        reinterpret_cast<uint2 *>(a.out + row * D)[d4] = *reinterpret_cast<const uint2 *>(bv);
+        if (d4 == 0) a.lse[row] = L;
+    };
+    if (!a.dyn_split) {   // planned split: one row per RPB-th of a workgroup
+        const long row = (long)blockIdx.x * RPB + threadIdx.x / PER_ROW;
+        if (row >= rows_total) return;
+        const int b = (int)(row / ((long)a.Hq * a.M));
+        if (a.m_valid && (int)(row % a.M) >= valid_rows(a, b)) return;
+        const int ns = splits_for(a, b);
+        if (ns > 1) combine_row(row, ns);   // with one split pass 1 wrote the row directly
+        return;
+    }
+    // Device-decided split: a capped grid walks only the valid rows of the
+    // batch entries that split (the same count pass 1 used), so the launch
+    // shape stays static without a workgroup per row of the capacity.
+    for (int b = 0; b < a.B; ++b) {
+        const int ns = splits_for(a, b);
+        const int mv = valid_rows(a, b);
+        const long nb = ns > 1 ? (long)a.Hq * mv : 0;
+        for (long i = (long)blockIdx.x * RPB + threadIdx.x / PER_ROW; i < nb; i += (long)gridDim.x * RPB) {
+            const int h = (int)(i / mv), j = (int)(i - (long)h * mv);
+            combine_row(((long)b * a.Hq + h) * a.M + j, ns);
         }
     }
-    float m = -INFINITY;
-    for (int s = 0; s < NB; ++s)
-        if (s < ns) m = fmaxf(m, lv[s]);
-    for (int s = NB; s < ns; ++s) m = fmaxf(m, ls[s * rows_total]);
-    float4 res = {0.f, 0.f, 0.f, 0.f};
-    float L = -INFINITY;
-    if (m != -INFINITY) {
-        float sum = 0.f;
-        for (int s = 0; s < NB; ++s)
-            if (s < ns) sum += fast_exp2((lv[s] - m) * kLog2e);
-        for (int s = NB; s < ns; ++s) sum += fast_exp2((ls[s * rows_total] - m) * kLog2e);
-        L = m + logf(sum);
-        auto add = [&](float l, const float4 &v) {
-            const float w = fast_exp2((l - L) * kLog2e);
-            res.x = fmaf(w, v.x, res.x);
-            res.y = fmaf(w, v.y, res.y);
-            res.z = fmaf(w, v.z, res.z);
-            res.w = fmaf(w, v.w, res.w);
-        };
-        for (int s = 0; s < NB; ++s)
-            if (s < ns) add(lv[s], ov[s]);
-        for (int s = NB; s < ns; ++s) add(ls[s * rows_total], os[s * ostride]);
-    }
-    __bf16 bv[4] = {(__bf16)res.x, (__bf16)res.y, (__bf16)res.z, (__bf16)res.w};
-    reinterpret_cast<uint2 *>(a.out + row * D)[d4] = *reinterpret_cast<const uint2 *>(bv);
-    if (d4 == 0) a.lse[row] = L;
 }
 
 // ---------------------------------------------------------------------------
@@ -1311,7 +1329,9 @@ hipError_t launch_attn_d(const AttnArgs &a, hipStream_t stream, hipEvent_t pass1
     if (a.n_split > 1) {
         const long rows = (long)a.B * a.Hq * a.M;
         constexpr int RPB = 256 / (D / 4);
-        attn_combine_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(a);
+        long nblk = (rows + RPB - 1) / RPB;
+        if (a.dyn_split && nblk > 2L * kNumCU) nblk = 2L * kNumCU;   // the walk covers the rest
+        attn_combine_kernel<D><<<dim3((unsigned)nblk), dim3(256), 0, stream>>>(a);
     }
     if (pass1_done) {
         const hipError_t e = hipEventRecord(pass1_done, stream);
