@@ -91,7 +91,8 @@ class _Select(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("score_ready", ctypes.c_void_p), ("margin", ctypes.c_void_p),
                 ("entropy", ctypes.c_void_p), ("row_flags", ctypes.c_void_p),
-                ("conf_gate", ctypes.c_float)]
+                ("conf_gate", ctypes.c_float), ("live_rows", ctypes.c_void_p),
+                ("n_live", ctypes.c_void_p), ("live_offset", ctypes.c_int32)]
 
 
 class _LayerDesc(ctypes.Structure):
@@ -218,6 +219,9 @@ class Select:
     entropy: object = None      # optional fp32 [R] output
     row_flags: object = None    # optional uint8 [R]: ROW_SELECT | ROW_LOCK per row
     conf_gate: float = 0.0      # lock only if also conf >= conf_gate (0: no gate)
+    live_rows: object = None    # optional int32 [>= n]: rows that may arrive unlocked (+ live_offset)
+    n_live: object = None       # int32 [1] on the device: the list's length (with live_rows)
+    live_offset: int = 0        # subtracted from every live_rows entry
 
 
 @dataclasses.dataclass
@@ -305,7 +309,8 @@ def _c_sel(s: Select) -> _Select:
         if not ev:
             raise DlmError(-1, "select.score_ready: the event has not been recorded")
     return _Select(s.mode, s.k, s.group_rows, s.tau, _ptr(s.score), _ptr(s.workspace), wb, ev or None,
-                   _ptr(s.margin), _ptr(s.entropy), _ptr(s.row_flags), s.conf_gate)
+                   _ptr(s.margin), _ptr(s.entropy), _ptr(s.row_flags), s.conf_gate, _ptr(s.live_rows),
+                   _ptr(s.n_live), int(s.live_offset))
 
 
 def _c_layer(L: LayerDesc) -> _LayerDesc:
@@ -401,6 +406,12 @@ def _post_args(logits, prev_logits, locked, select, sel, kl, conf, R, V):
         _expect(select.entropy, "select.entropy", (R,), "torch.float32")
     if select.row_flags is not None:
         _expect(select.row_flags, "select.row_flags", (R,), "torch.uint8")
+    if select.live_rows is not None:
+        # R entries: the device reads at most min(n_live, R) of them
+        _expect(select.live_rows, "select.live_rows", (R,), "torch.int32")
+        if select.n_live is None:
+            raise DlmError(DLM_E_NULL, "select.live_rows needs select.n_live")
+        _expect(select.n_live, "select.n_live", (1,), "torch.int32")
 
 
 def dlm_posterior(logits, prev_logits, locked, eps: float, select: Select, sel, kl, conf,

@@ -235,7 +235,7 @@ int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select
     if (!bytes) return fail(DLM_E_NULL, "bytes is NULL");
     int rc = check_post_scalars(R, V, select);
     if (rc != DLM_OK) return rc;
-    *bytes = dlm::plan_post(R, V, select->mode, select->group_rows).ws_total;
+    *bytes = dlm::plan_post(R, V, select->mode, select->group_rows, select->live_rows != nullptr).ws_total;
     return DLM_OK;
 }
 
@@ -245,7 +245,7 @@ static int posterior_with(const float *logits, const float *prev_logits, uint8_t
                           const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R,
                           int32_t V, hipStream_t stream, void *ws, size_t ws_bytes)
 {
-    dlm::PostPlan p = dlm::plan_post(R, V, select->mode, select->group_rows);
+    dlm::PostPlan p = dlm::plan_post(R, V, select->mode, select->group_rows, select->live_rows != nullptr);
     if (p.ws_total > 0 && (ws == nullptr || ws_bytes < p.ws_total))
         return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_total,
                     ws ? ws_bytes : (size_t)0);
@@ -257,6 +257,8 @@ static int posterior_with(const float *logits, const float *prev_logits, uint8_t
     a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
     a.eps = eps; a.tau = select->tau; a.conf_gate = select->conf_gate;
     a.n_chunks = p.n_chunks; a.chunk = p.chunk;
+    a.live_rows = select->live_rows; a.n_live = select->n_live;
+    a.live_offset = select->live_offset; a.nc_cap = p.n_chunks;
     hipError_t e = dlm::launch_posterior(a, stream, select->score_ready);
     if (e != hipSuccess) return fail(DLM_E_HIP, "launch or event wait failed: %s", hipGetErrorString(e));
     return DLM_OK;
@@ -272,6 +274,7 @@ static int check_post_call(const float *logits, const float *prev_logits, uint8_
         return fail(DLM_E_NULL, "logits, prev_logits, locked, sel, kl and conf must be non-NULL");
     if ((select->mode == DLM_SEL_ATTN_DYNAMIC || select->mode == DLM_SEL_TOPK_SCORE) && !select->score)
         return fail(DLM_E_NULL, "selection by score needs select->score");
+    if (select->live_rows && !select->n_live) return fail(DLM_E_NULL, "live_rows needs n_live");
     if (isnan(eps)) return fail(DLM_E_DESC, "eps is NaN");
     if ((V & 3) == 0 && (!aligned16(logits) || !aligned16(prev_logits)))
         return fail(DLM_E_SHAPE, "logits must be 16-byte aligned");
@@ -336,7 +339,7 @@ int dlm_posterior_noalloc(const float *logits, const float *prev_logits, uint8_t
     g_err[0] = 0;
     int rc = check_post_call(logits, prev_logits, locked, eps, select, sel, kl, conf, R, V);
     if (rc != DLM_OK) return rc;
-    const size_t need = dlm::plan_post(R, V, select->mode, select->group_rows).ws_total;
+    const size_t need = dlm::plan_post(R, V, select->mode, select->group_rows, select->live_rows != nullptr).ws_total;
     if (need > (size_t)DLM_NOALLOC_SCRATCH_BYTES)
         return fail(DLM_E_WORKSPACE, "R=%d V=%d needs %zu bytes of partials; the allocation-free entry "
                     "point holds %zu (use dlm_posterior with a workspace)", R, V, need,

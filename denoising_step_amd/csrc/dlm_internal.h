@@ -69,7 +69,9 @@ struct PostPlan {
     int group_rows;     // rows per finishing workgroup
     size_t ws_total;
 };
-PostPlan plan_post(int R, int V, int mode, int group_rows);
+// live: with a device live-row list (dlm_select.live_rows); the plan then
+// sizes the partials for the largest split and n_chunks is that cap.
+PostPlan plan_post(int R, int V, int mode, int group_rows, bool live = false);
 
 struct AttnArgs {
     const uint16_t *q, *k, *v;      // bf16 bit patterns
@@ -100,6 +102,11 @@ struct PostArgs {
     int R, V, mode, k, group_rows;
     float eps, tau, conf_gate;
     int n_chunks, chunk;
+    // optional live-row list: live_rows[i] - live_offset for i < *n_live
+    // are the rows that may arrive unlocked; the split of the vocabulary is
+    // then chosen on the device from the count (at most nc_cap chunks)
+    const int32_t *live_rows, *n_live;
+    int live_offset, nc_cap;
 };
 
 // Block Buffer state of a multi-step run (device arrays, see dlm_step.h).

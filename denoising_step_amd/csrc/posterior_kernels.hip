@@ -152,6 +152,60 @@ __device__ __forceinline__ void rs_fold_masked(RowState &s, const float (&x)[N],
 
 constexpr int kStageBytes = 48 * 1024;   // 1024 partials of 48 bytes
 
+#ifndef DLM_POST_WGS_PER_CU
+#define DLM_POST_WGS_PER_CU 16
+#endif
+// Least chunks per row for a selection group of more than 256 rows.
+#ifndef DLM_POST_BIG_CHUNKS
+#define DLM_POST_BIG_CHUNKS 4
+#endif
+
+// The split of each row's vocabulary into chunks: about sixteen streaming
+// workgroups per CU over the `live` rows to stream (measured: shorter
+// chunks balance the end of the stream better than four long ones per CU),
+// chunks of whole streaming steps (4096 elements), capped for the
+// finishing kernel by the size of the selection groups of the R rows: a
+// group of up to 256 rows stages its partials in LDS in one round
+// (measured best: its rows are all live); a larger group (a whole block of
+// a multi-step run, most of whose rows are locked late) merges from global
+// memory and keeps at least four chunks per live row.  cap > 0 bounds the
+// chunk count (the partials a live-row call was sized for).  The host plan
+// and, with a live-row list, both kernels evaluate this same function.
+__host__ __device__ inline void post_split(long live, int R, int V, int mode, int group_rows, int cap,
+                                           int &n_chunks, int &chunk)
+{
+    int chunks = 1;
+    if (R > 0) {
+        const long target = (long)DLM_POST_WGS_PER_CU * kNumCU;
+        const long lv = live < 1 ? 1 : live;
+        if (lv < target) chunks = (int)((target + lv - 1) / lv);
+        const int max_chunks = max(1, (V + kPostThreads * kPostVec - 1) / (kPostThreads * kPostVec));
+        chunks = min(chunks, max_chunks);
+        const int g = min(R, mode == 0 ? 256 : group_rows);
+        if (g <= 256) chunks = min(chunks, max(1, (kStageBytes / (int)sizeof(PostPartial)) / max(1, g)));
+        else chunks = min(max_chunks, max(chunks, DLM_POST_BIG_CHUNKS));
+        if (cap > 0) chunks = min(chunks, cap);
+    }
+    int ch = (V + chunks - 1) / chunks;
+    // A split row gets chunks of whole streaming steps (4 float4 per array
+    // per thread), so a chunk is one round of loads per step.
+    constexpr int kStep = kPostThreads * kPostVec;
+    ch = chunks > 1 ? (ch + kStep - 1) / kStep * kStep : (ch + 3) / 4 * 4;
+    chunk = max(4, ch);
+    n_chunks = max(1, (V + chunk - 1) / chunk);
+}
+
+// Workgroups per CU of the stream kernel's grid with a live-row list.
+constexpr int kPostLiveGridPerCU = 16;
+
+// With a live-row list, the split this call uses (from the device count).
+__device__ __forceinline__ void live_split(PostArgs &a)
+{
+    if (!a.live_rows) return;
+    const int n = min(max(*a.n_live, 0), a.R);
+    post_split(n, a.R, a.V, a.mode, a.group_rows, a.nc_cap, a.n_chunks, a.chunk);
+}
+
 // Where partial (row, chunk) lives.  The partials of selection group
 // [g0, g0 + n) fill the block [g0 nc, (g0 + n) nc) of the array.  A group
 // whose partials fit one LDS staging round keeps its block row-major; a
@@ -168,12 +222,30 @@ __device__ __forceinline__ long part_index(const PostArgs &a, int row, int ch)
     return per_round < n ? (long)g0 * nc + (long)ch * n + (row - g0) : (long)row * nc + ch;
 }
 
-template <bool VEC4, bool SC>
-__global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs a)
+// One workgroup per (row, chunk); with a live-row list (LIVE), a fixed
+// grid walks the (listed row, chunk) items of the device-chosen split, so
+// the workgroups follow the live rows while the launch shape stays fixed.
+template <bool VEC4, bool SC, bool LIVE>
+__global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs a0)
 {
-    const int row = blockIdx.x / a.n_chunks;
-    const int ch = blockIdx.x % a.n_chunks;
-    if (a.locked[row]) return;      // a locked row is never read
+    __shared__ RowState red[kPostThreads / 64];
+    PostArgs a = a0;
+    int items = 1;
+    if constexpr (LIVE) {
+        live_split(a);
+        items = min(max(*a.n_live, 0), a.R) * a.n_chunks;
+    }
+    for (int it = 0, item = blockIdx.x; LIVE ? item < items : it == 0; ++it, item += gridDim.x) {
+    int row, ch;
+    if constexpr (LIVE) {
+        row = a.live_rows[item / a.n_chunks] - a.live_offset;
+        ch = item % a.n_chunks;
+        if (row < 0 || row >= a.R) continue;
+    } else {
+        row = blockIdx.x / a.n_chunks;
+        ch = blockIdx.x % a.n_chunks;
+    }
+    if (a.locked[row]) continue;    // a locked row is never read
     const int tid = threadIdx.x;
     const long base = (long)row * a.V;
     const float *x = a.x + base, *y = a.y + base;
@@ -230,7 +302,6 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
 
     // Wave, then workgroup reduction (fixed shape: deterministic).
     for (int m = 32; m >= 1; m >>= 1) rs_merge<SC>(s, rs_shfl_xor<SC>(s, m));
-    __shared__ RowState red[kPostThreads / 64];
     const int wid = tid >> 6;
     if ((tid & 63) == 0) red[wid] = s;
     __syncthreads();
@@ -242,6 +313,8 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
         p.av = t.av; p.a2 = t.a2; p.ex = t.ex; p.ai = t.ai;
         p.pad[0] = p.pad[1] = p.pad[2] = 0;
         a.part[part_index(a, row, ch)] = p;
+    }
+    if constexpr (LIVE) __syncthreads();   // red is rewritten by the next item
     }
 }
 
@@ -316,8 +389,10 @@ __device__ __forceinline__ RowState rs_load(const PostPartial &p)
     return s;
 }
 
-__global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
+__global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
 {
+    PostArgs a = a0;
+    live_split(a);   // with a live-row list, the split the stream kernel used
     __shared__ __attribute__((aligned(16))) float key_s[kMaxGroupRows];
     __shared__ float conf_s[kMaxGroupRows];
     __shared__ int tok_s[kMaxGroupRows];
@@ -330,6 +405,8 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
     constexpr int kSmallK = 32;                 // up to this k, a tournament instead of radix select
     __shared__ unsigned long long cand_s[4 * kSmallK + 1];
     __shared__ float red_s[4];
+    __shared__ int lrow_s[kMaxGroupRows];       // live-row list: the group's live rows, ascending
+    __shared__ int lcnt_s[4][4];                // live-row list: live rows per (round, wave)
 
     const int tid = threadIdx.x;
     const int g0 = blockIdx.x * a.group_rows;
@@ -393,7 +470,67 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
             }
         }
     };
-    if (rows_per_round < n) {
+    if (rows_per_round < n && a.live_rows) {
+        // A group of more than 256 rows under a live-row list: few rows are
+        // live late in a run, each split into up to nc_cap chunks.  The live
+        // rows of the group are compacted (ascending) into LDS, and `lanes`
+        // threads merge each one, lane k taking chunks k, k + lanes, ... in
+        // order (up to kDirect loads in flight), then a fixed butterfly over
+        // the lanes; rows locked on entry get their outputs afterwards.
+        constexpr int kDirect = 16;
+        const int nc = a.n_chunks;
+        set_flags();
+        lds_barrier();
+        const int lane = tid & 63, wid = tid >> 6;
+        unsigned long long bal[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = tid + 256 * k;
+            bal[k] = __ballot(t < n && (rowf_s[t] & 1));
+            if (lane == 0) lcnt_s[k][wid] = __popcll(bal[k]);
+        }
+        lds_barrier();
+        int L = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int before = L;
+            for (int w = 0; w < 4; ++w) {
+                if (w < wid) before += lcnt_s[k][w];
+                L += lcnt_s[k][w];
+            }
+            const int t = tid + 256 * k;
+            if ((bal[k] >> lane) & 1ull) lrow_s[before + __popcll(bal[k] & ((1ull << lane) - 1))] = t;
+        }
+        lds_barrier();
+        int lanes = 1;
+        while (lanes < 32 && lanes * 2 * L <= 256 && lanes * 2 <= nc) lanes *= 2;
+        const int per_pass = 256 / lanes;
+        for (int t0 = 0; t0 < L; t0 += per_pass) {
+            const int t = t0 + tid / lanes, sub = tid % lanes;
+            RowState s;
+            rs_init(s);
+            const int gt = t < L ? lrow_s[t] : 0;
+            for (int c0 = sub; t < L && c0 < nc; c0 += lanes * kDirect) {
+                PostPartial q[kDirect];
+#pragma unroll
+                for (int u = 0; u < kDirect; ++u) {
+                    const int c = c0 + u * lanes;
+                    if (c < nc) q[u] = a.part[(long)g0 * nc + (long)c * n + gt];
+                }
+#pragma unroll
+                for (int u = 0; u < kDirect; ++u)
+                    if (c0 + u * lanes < nc) rs_merge(s, rs_load(q[u]));
+            }
+            for (int m = lanes / 2; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
+            if (t < L && sub == 0) finish_row(gt, s, false);
+        }
+        for (int gt = tid; gt < n; gt += 256) {
+            if (rowf_s[gt] & 1) continue;
+            RowState s;
+            rs_init(s);
+            finish_row(gt, s, true);
+        }
+    } else if (rows_per_round < n) {
         // A group of more than 256 rows with split rows: its partials would
         // take several staging rounds, so each thread merges its rows
         // (gt = tid, tid + 256, ...) straight from global memory, issuing
@@ -664,17 +801,23 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a)
 hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t finish_after)
 {
     if (a.R == 0) return hipSuccess;
-    const long nwg = (long)a.R * a.n_chunks;
+    long nwg = (long)a.R * a.n_chunks;
     // margin / entropy: only when an output or the selection needs them
     const bool sc = a.margin || a.entropy || a.mode == 5 || a.mode == 6;
+    const bool live = a.live_rows != nullptr;
+    if (live && nwg > (long)kPostLiveGridPerCU * kNumCU) nwg = (long)kPostLiveGridPerCU * kNumCU;
     const dim3 grid((unsigned)nwg), block(kPostThreads);
+#define DLM_POST_STREAM(V4, SC_)                                                              \
+    (live ? (posterior_stream_kernel<V4, SC_, true><<<grid, block, 0, stream>>>(a), 0)       \
+          : (posterior_stream_kernel<V4, SC_, false><<<grid, block, 0, stream>>>(a), 0))
     if ((a.V & 3) == 0) {
-        if (sc) posterior_stream_kernel<true, true><<<grid, block, 0, stream>>>(a);
-        else posterior_stream_kernel<true, false><<<grid, block, 0, stream>>>(a);
+        if (sc) DLM_POST_STREAM(true, true);
+        else DLM_POST_STREAM(true, false);
     } else {
-        if (sc) posterior_stream_kernel<false, true><<<grid, block, 0, stream>>>(a);
-        else posterior_stream_kernel<false, false><<<grid, block, 0, stream>>>(a);
+        if (sc) DLM_POST_STREAM(false, true);
+        else DLM_POST_STREAM(false, false);
     }
+#undef DLM_POST_STREAM
     if (finish_after) {
         const hipError_t e = hipStreamWaitEvent(stream, finish_after, 0);
         if (e != hipSuccess) return e;
@@ -684,42 +827,13 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t fi
     return hipGetLastError();
 }
 
-#ifndef DLM_POST_WGS_PER_CU
-#define DLM_POST_WGS_PER_CU 16
-#endif
-// Least chunks per row for a selection group of more than 256 rows.
-#ifndef DLM_POST_BIG_CHUNKS
-#define DLM_POST_BIG_CHUNKS 4
-#endif
-
-PostPlan plan_post(int R, int V, int mode, int group_rows)
+PostPlan plan_post(int R, int V, int mode, int group_rows, bool live)
 {
     PostPlan p{};
-    // About sixteen streaming workgroups per CU (measured: shorter chunks
-    // balance the end of the stream better than four long ones per CU),
-    // chunks of at least one streaming step (4096 elements).
-    int chunks = 1;
-    if (R > 0) {
-        const long target = (long)DLM_POST_WGS_PER_CU * kNumCU;
-        if (R < target) chunks = (int)((target + R - 1) / R);
-        const int max_chunks = max(1, (V + kPostThreads * kPostVec - 1) / (kPostThreads * kPostVec));
-        chunks = min(chunks, max_chunks);
-        // A finishing group of up to 256 rows stages its partials in LDS in
-        // one round (measured best: its rows are all live), which caps the
-        // chunks; a larger group (the radix-selection regime of a whole
-        // block, most of whose rows are locked late in a run) merges from
-        // global memory, so its live rows keep several chunks each.
-        const int g = min(R, mode == 0 ? 256 : group_rows);
-        if (g <= 256) chunks = min(chunks, max(1, (kStageBytes / (int)sizeof(PostPartial)) / max(1, g)));
-        else chunks = min(max_chunks, max(chunks, DLM_POST_BIG_CHUNKS));
-    }
-    int chunk = (V + chunks - 1) / chunks;
-    // A split row gets chunks of whole streaming steps (4 float4 per array
-    // per thread), so a chunk is one round of loads per step.
-    constexpr int kStep = kPostThreads * kPostVec;
-    chunk = chunks > 1 ? (chunk + kStep - 1) / kStep * kStep : (chunk + 3) / 4 * 4;
-    p.chunk = max(4, chunk);
-    p.n_chunks = max(1, (V + p.chunk - 1) / p.chunk);
+    // With a live-row list the partials are sized for the largest split a
+    // call can choose (one live row), and the kernels pick the split from
+    // the device count.
+    post_split(live ? 1 : R, R, V, mode, group_rows, 0, p.n_chunks, p.chunk);
     p.group_rows = mode == 0 ? 256 : group_rows;
     p.ws_total = (size_t)R * p.n_chunks * sizeof(PostPartial);
     return p;

@@ -98,11 +98,16 @@ class DeviceLoop:
                            m_active=self.bb.m_active)
         self.attn_ws = z((max(1, dlm_step_attn_workspace_bytes(self.kv, self.md)),), torch.uint8)
         self.md.workspace = self.attn_ws
-        probe = Select(mode=case.mode, k=case.k, group_rows=bs, tau=case.tau)
-        self.post_ws = z((max(1, dlm_posterior_workspace_bytes(n_gen, V, probe)),), torch.uint8)
+        # The posterior streams only the step's rows: the buffer's compacted
+        # active rows (every other row arrives with skip set), their count on
+        # the device, so the vocabulary split follows M_t in the captured step.
         self.sels = [Select(mode=case.mode, k=case.k, group_rows=bs, tau=case.tau,
-                            score=self.colsum[b, P:P + n_gen], workspace=self.post_ws,
-                            row_flags=self.bb.row_flags[b]) for b in range(B)]
+                            score=self.colsum[b, P:P + n_gen], row_flags=self.bb.row_flags[b],
+                            live_rows=self.bb.active_idx[b], n_live=self.bb.m_active[b:b + 1],
+                            live_offset=P) for b in range(B)]
+        self.post_ws = z((max(1, dlm_posterior_workspace_bytes(n_gen, V, self.sels[0])),), torch.uint8)
+        for sl in self.sels:
+            sl.workspace = self.post_ws
 
     def start(self, stream=None):
         """Restore the cache and the unmasked set, clear the per-step buffers

@@ -238,6 +238,22 @@ typedef struct {
     float conf_gate;         /* the optional confidence gate of the lock test (SureLock
                                 page, sec. 2: a peaked posterior): a row locks only if
                                 also conf >= conf_gate.  0 (no gate) or any finite value. */
+    const int32_t *live_rows;    /* optional device int32 [*n_live] (NULL: none): the rows
+                                that may arrive unlocked, as live_rows[i] - live_offset
+                                (entries outside [0, R) are ignored; a listed row that
+                                arrives locked is skipped).  Every row NOT listed must
+                                arrive locked: it is not read, as any locked row.  With
+                                the list, the split of each row's vocabulary into chunks
+                                is chosen on the device from the count, so the logit
+                                stream's parallelism follows the live rows late in a
+                                run (SureLock page, sec. 2: only the M_t active rows are
+                                computed) while the launch shapes stay fixed for graph
+                                capture.  The workspace size depends on whether a list
+                                is given (set it before dlm_posterior_workspace_bytes).
+                                Outputs are those of the call without the list up to
+                                the fp32 summation order of the chunks. */
+    const int32_t *n_live;       /* device int32 [1], required with live_rows: list length (<= R) */
+    int32_t live_offset;         /* subtracted from every live_rows entry */
 } dlm_select;
 
 /* Bits of dlm_select.row_flags. */

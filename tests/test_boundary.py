@@ -66,6 +66,11 @@ def test_workspace_queries():
     s = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=4, group_rows=16)
     assert dlm.dlm_posterior_workspace_bytes(16, 512, s) >= 16 * 32
     assert dlm.dlm_posterior_workspace_bytes(0, 512, s) == 0
+    # a live-row list sizes the partials for the largest split any count can choose
+    big = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=16, group_rows=1024)
+    live = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=16, group_rows=1024, live_rows=FAKE, n_live=FAKE)
+    assert dlm.dlm_posterior_workspace_bytes(1024, 126464, big) == 1024 * 4 * 48
+    assert dlm.dlm_posterior_workspace_bytes(1024, 126464, live) == 1024 * 31 * 48
 
 
 @pytest.mark.parametrize("case,code", [
@@ -341,6 +346,14 @@ def test_pack_weights_rejects():
     n = __import__("ctypes").c_size_t(0)
     assert lib.dlm_layer_workspace_bytes(__import__("ctypes").byref(c), __import__("ctypes").byref(n)) == \
         dlm.DLM_E_DESC
+
+
+def test_posterior_live_rows_need_a_count():
+    import ctypes
+    s = dlm._c_sel(dlm.Select(mode=dlm.SEL_TOPK_CONF, k=4, group_rows=16, live_rows=FAKE))
+    s.workspace, s.workspace_bytes = FAKE, 1 << 20
+    rc = dlm.lib.dlm_posterior(FAKE, FAKE, FAKE, 1e-3, ctypes.byref(s), FAKE, FAKE, FAKE, 16, 512, None)
+    assert rc == dlm.DLM_E_NULL
 
 
 def test_posterior_rejects_nan_gate():

@@ -414,6 +414,66 @@ def test_large_selection_groups(g, V):
         assert (sel_o >= 0).sum() > 0
 
 
+@pytest.mark.parametrize("g,V,n_live", [(100, 40000, 30), (100, 600, 150), (700, 40000, 9), (700, 40000, 1200),
+                                         (1024, 40000, 0), (1024, 126464, 16)])
+def test_live_row_list(g, V, n_live):
+    """A live-row list (dlm_select.live_rows / n_live / live_offset): only the
+    listed rows are streamed, with the vocabulary split chosen on the device
+    from the count (more chunks for fewer rows), and the finishing kernel
+    merging with that same split.  Every unlisted row arrives locked; listed
+    rows may arrive locked too; entries outside [0, R) (after the offset)
+    and entries past the count are ignored.  Checked against the oracle on
+    every row, for a staged (100-row) and a global-memory (700, 1024-row)
+    merge, with no live row and with more entries than rows."""
+    import denoising_step_amd as dlm
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(90 + g + n_live)
+    R = 2 * g + 77 if g < 1024 else 1024
+    x = (rng.standard_normal((R, V)) * rng.uniform(0.5, 4.0, R)[:, None]).astype(np.float32)
+    y = (x + rng.standard_normal((R, V)) * 0.1).astype(np.float32)
+    live = np.sort(rng.choice(R, size=min(n_live, R), replace=False)).astype(np.int32)
+    locked = np.ones(R, np.uint8)
+    locked[live] = (rng.random(len(live)) < 0.2).astype(np.uint8)    # a listed row may arrive locked
+    flags = np.where(rng.random(R) < 0.1, 2, 3).astype(np.uint8)
+    off = 100
+    entries = list(live + off)
+    if n_live >= 9:
+        entries[3:3] = [-5, R + off + 7]            # outside [0, R) after the offset: ignored
+    count = min(len(entries), R)
+    lst = np.full(R, -1, np.int32)
+    lst[:count] = np.array(entries[:count], np.int32)
+    # rows that the count cuts off must arrive locked (the list's contract)
+    kept = lst[:count] - off
+    kept = kept[(kept >= 0) & (kept < R)]
+    locked[np.setdiff1d(np.arange(R), kept)] = 1
+    ora = oracle.posterior(x, y, locked, 1e-3, flags=flags)
+    for mode, k, tau in [(W.SEL_TOPK_CONF, 7, 0.0), (W.SEL_THRESH_CONF, 0, 0.99)]:
+        _say(f"case: live rows g={g} V={V} n_live={n_live} mode={mode}")
+        mg = torch.empty(R, device=dev)
+        en = torch.empty(R, device=dev)
+        s = dlm.Select(mode=mode, k=k, group_rows=g, tau=tau, margin=mg, entropy=en,
+                       row_flags=torch.from_numpy(flags).to(dev),
+                       live_rows=torch.from_numpy(lst).to(dev),
+                       n_live=torch.tensor([count], dtype=torch.int32, device=dev), live_offset=off)
+        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
+                                  device=dev)
+        lk = torch.from_numpy(locked.copy()).to(dev)
+        sel = torch.empty(R, dtype=torch.int32, device=dev)
+        kl = torch.empty(R, dtype=torch.float32, device=dev)
+        conf = torch.empty(R, dtype=torch.float32, device=dev)
+        dlm.dlm_posterior(torch.from_numpy(x).to(dev), torch.from_numpy(y).to(dev), lk, 1e-3, s,
+                          sel, kl, conf, R, V)
+        torch.cuda.synchronize()
+        check_posterior(kl.cpu().numpy(), conf.cpu().numpy(), lk.cpu().numpy(), ora["kl"], ora["conf"],
+                        ora["locked"], 1e-3, locked)
+        sel_o = oracle.select(mode, k, g, tau, np.zeros(R), ora["conf"], ora["tok"], locked,
+                              ora["margin"], ora["entropy"], flags=flags)
+        inelig = ((locked != 0) | ((flags & 1) == 0)).astype(np.uint8)
+        check_selection(sel.cpu().numpy(), sel_o, mode, g, tau, ora["conf"], np.zeros(R),
+                        inelig, x, ora["margin"], ora["entropy"])
+        check_scores(mg.cpu().numpy(), en.cpu().numpy(), ora["margin"], ora["entropy"], locked)
+
+
 @pytest.mark.parametrize("V", [1, 1003, 6000])
 def test_margin_entropy_samplers(V):
     """Margin and entropy of p_t and the two token-level samplers that rank
