@@ -329,6 +329,11 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
 // row per thread.
 // The selection uses block-wide reductions, not a serial scan.
 constexpr int kMergeLanes = 8;
+#ifndef DLM_FINISH_WIDE_THREADS
+#define DLM_FINISH_WIDE_THREADS 512
+#endif
+// Threads of the finishing workgroup of a group of more than 256 rows.
+constexpr int kFinishWideThreads = DLM_FINISH_WIDE_THREADS;
 
 // Workgroup barrier for data exchanged through LDS only: this wave's LDS
 // operations are complete, then s_barrier.  Unlike __syncthreads() it does
@@ -371,6 +376,7 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
            (unsigned long long)(unsigned)__builtin_amdgcn_readlane(lo, 63);
 }
 
+template <int NW>
 __device__ __forceinline__ float block_max(float v, float *red)
 {
     for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
@@ -378,7 +384,9 @@ __device__ __forceinline__ float block_max(float v, float *red)
     lds_barrier();
     if ((threadIdx.x & 63) == 0) red[wid] = v;
     lds_barrier();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float r = red[0];
+    for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w]);
+    return r;
 }
 
 __device__ __forceinline__ RowState rs_load(const PostPartial &p)
@@ -389,8 +397,11 @@ __device__ __forceinline__ RowState rs_load(const PostPartial &p)
     return s;
 }
 
-__global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
+template <int NT>
+__global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
 {
+    constexpr int NW = NT / 64;                 // waves
+    constexpr int KR = kMaxGroupRows / NT;      // rows per thread of the largest group
     PostArgs a = a0;
     live_split(a);   // with a live-row list, the split the stream kernel used
     __shared__ __attribute__((aligned(16))) float key_s[kMaxGroupRows];
@@ -403,10 +414,10 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
     __shared__ int hist_s[256];
     __shared__ int pick_s[2];                   // radix select: digit found, count still to go
     constexpr int kSmallK = 32;                 // up to this k, a tournament instead of radix select
-    __shared__ unsigned long long cand_s[4 * kSmallK + 1];
-    __shared__ float red_s[4];
+    __shared__ unsigned long long cand_s[NW * kSmallK + 1];
+    __shared__ float red_s[NW];
     __shared__ int lrow_s[kMaxGroupRows];       // live-row list: the group's live rows, ascending
-    __shared__ int lcnt_s[4][4];                // live-row list: live rows per (round, wave)
+    __shared__ int lcnt_s[KR][NW];              // live-row list: live rows per (round, wave)
 
     const int tid = threadIdx.x;
     const int g0 = blockIdx.x * a.group_rows;
@@ -420,17 +431,17 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
     // merge order is fixed.
     int lanes = 1;
     if (a.n_chunks > 1)
-        while (lanes < kMergeLanes && n * lanes * 2 <= 256) lanes *= 2;
+        while (lanes < kMergeLanes && n * lanes * 2 <= NT) lanes *= 2;
     const bool wide = lanes > 1;
 
     // Issue the lock-flag and score loads together with the staging loads
     // of the partials (when they fit one round); nothing waits until the
     // barrier.
-    uint8_t lk[4], fl[4];
-    float sc[4];
+    uint8_t lk[KR], fl[KR];
+    float sc[KR];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int t = tid + 256 * k;
+    for (int k = 0; k < KR; ++k) {
+        const int t = tid + NT * k;
         lk[k] = t < n ? a.locked[g0 + t] : 1;
         fl[k] = (a.flags && t < n) ? a.flags[g0 + t] : 3;
         sc[k] = (by_score && t < n) ? a.score[g0 + t] : 0.f;
@@ -461,8 +472,8 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
     };
     auto set_flags = [&]() {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t = tid + 256 * k;
+        for (int k = 0; k < KR; ++k) {
+            const int t = tid + NT * k;
             if (t < n) {
                 elig_s[t] = (lk[k] == 0 && (fl[k] & 1)) ? 1 : 0;
                 rowf_s[t] = (lk[k] == 0 ? 1 : 0) | ((fl[k] & 2) << 1);
@@ -482,29 +493,29 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
         set_flags();
         lds_barrier();
         const int lane = tid & 63, wid = tid >> 6;
-        unsigned long long bal[4];
+        unsigned long long bal[KR];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int t = tid + 256 * k;
+        for (int k = 0; k < KR; ++k) {
+            const int t = tid + NT * k;
             bal[k] = __ballot(t < n && (rowf_s[t] & 1));
             if (lane == 0) lcnt_s[k][wid] = __popcll(bal[k]);
         }
         lds_barrier();
         int L = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < KR; ++k) {
             int before = L;
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 if (w < wid) before += lcnt_s[k][w];
                 L += lcnt_s[k][w];
             }
-            const int t = tid + 256 * k;
+            const int t = tid + NT * k;
             if ((bal[k] >> lane) & 1ull) lrow_s[before + __popcll(bal[k] & ((1ull << lane) - 1))] = t;
         }
         lds_barrier();
         int lanes = 1;
-        while (lanes < 32 && lanes * 2 * L <= 256 && lanes * 2 <= nc) lanes *= 2;
-        const int per_pass = 256 / lanes;
+        while (lanes < 32 && lanes * 2 * L <= NT && lanes * 2 <= nc) lanes *= 2;
+        const int per_pass = NT / lanes;
         for (int t0 = 0; t0 < L; t0 += per_pass) {
             const int t = t0 + tid / lanes, sub = tid % lanes;
             RowState s;
@@ -524,7 +535,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
             for (int m = lanes / 2; m >= 1; m >>= 1) rs_merge(s, rs_shfl_xor(s, m));
             if (t < L && sub == 0) finish_row(gt, s, false);
         }
-        for (int gt = tid; gt < n; gt += 256) {
+        for (int gt = tid; gt < n; gt += NT) {
             if (rowf_s[gt] & 1) continue;
             RowState s;
             rs_init(s);
@@ -546,7 +557,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
             auto load_batch = [&](int gt0) {
 #pragma unroll
                 for (int u = 0; u < kDirect; ++u) {
-                    const int i = u / nc, c = u - i * nc, gt = gt0 + 256 * i;
+                    const int i = u / nc, c = u - i * nc, gt = gt0 + NT * i;
                     if (i < rpb && gt < n) q[u] = a.part[(long)g0 * nc + (long)c * n + gt];
                 }
             };
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
                 rs_init(s);
 #pragma unroll
                 for (int u = 0; u < kDirect; ++u) {
-                    const int i = u / nc, c = u - i * nc, gt = gt0 + 256 * i;
+                    const int i = u / nc, c = u - i * nc, gt = gt0 + NT * i;
                     if (i < rpb && gt < n) {
                         const bool live = rowf_s[gt] & 1;   // a locked row's slots are never read
                         if (c == 0) rs_init(s);
@@ -569,14 +580,14 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
             set_flags();
             lds_barrier();
             merge_batch(tid);
-            for (int gt0 = tid + 256 * rpb; gt0 < n; gt0 += 256 * rpb) {
+            for (int gt0 = tid + NT * rpb; gt0 < n; gt0 += NT * rpb) {
                 load_batch(gt0);
                 merge_batch(gt0);
             }
         } else {
             set_flags();
             lds_barrier();
-            for (int gt = tid; gt < n; gt += 256) {
+            for (int gt = tid; gt < n; gt += NT) {
                 const bool live = rowf_s[gt] & 1;
                 RowState s;
                 rs_init(s);
@@ -602,22 +613,22 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
         v4u *dst = reinterpret_cast<v4u *>(stage_s);
         const int n16 = nr * a.n_chunks * (int)(sizeof(PostPartial) / 16);
         // up to twelve 16-byte loads in flight per thread (one round: the stage is 3072)
-        for (int i0 = 0; i0 < n16; i0 += 256 * 12) {
+        for (int i0 = 0; i0 < n16; i0 += NT * 12) {
             v4u v[12];
 #pragma unroll
             for (int u = 0; u < 12; ++u) {
-                const int i = i0 + u * 256 + tid;
+                const int i = i0 + u * NT + tid;
                 v[u] = i < n16 ? src[i] : v4u{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < 12; ++u) {
-                const int i = i0 + u * 256 + tid;
+                const int i = i0 + u * NT + tid;
                 if (i < n16) dst[i] = v[u];
             }
         }
         set_flags();
         lds_barrier();
-        for (int t0 = 0; t0 < nr; t0 += 256 / lanes) {
+        for (int t0 = 0; t0 < nr; t0 += NT / lanes) {
             const int t = t0 + tid / lanes;
             const int sub = tid % lanes;
             const bool row_ok = t < nr;
@@ -635,7 +646,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
         }
     }
     if (a.mode == 0) {
-        for (int t = tid; t < n; t += 256) a.sel[g0 + t] = -1;
+        for (int t = tid; t < n; t += NT) a.sel[g0 + t] = -1;
         return;
     }
     lds_barrier();   // row results (LDS) visible
@@ -643,12 +654,12 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
     float thr = -INFINITY;
     if (a.mode == 3) {
         float v = -INFINITY;
-        for (int t = tid; t < n; t += 256)
+        for (int t = tid; t < n; t += NT)
             if (elig_s[t] && !(conf_s[t] > a.tau)) v = fmaxf(v, key_s[t]);
-        thr = block_max(v, red_s);
+        thr = block_max<NW>(v, red_s);
     }
     int mine = 0;
-    for (int t = tid; t < n; t += 256) {
+    for (int t = tid; t < n; t += NT) {
         if (!elig_s[t]) continue;
         if (a.mode == 2 && conf_s[t] > a.tau) mine = 1;
         if (a.mode == 3 && conf_s[t] > a.tau && key_s[t] > thr) mine = 1;
@@ -677,12 +688,12 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
     constexpr int kCountMax = 256;
     const bool counted = n <= kCountMax;
     lds_barrier();
-    for (int t = tid; t < n; t += 256) {
+    for (int t = tid; t < n; t += NT) {
         const unsigned bits = __float_as_uint(elig_s[t] ? key_s[t] : -INFINITY);
         const unsigned ord = bits ^ ((unsigned)((int)bits >> 31) | 0x80000000u);
         ord_s[t] = ((unsigned long long)ord << 32) | (0xffffffffu - (unsigned)t);
     }
-    for (int t = n + tid; t < ((n + 1) & ~1); t += 256) ord_s[t] = 0;   // even count
+    for (int t = n + tid; t < ((n + 1) & ~1); t += NT) ord_s[t] = 0;   // even count
     lds_barrier();
     // the kk-th largest packed value (kk in [1, n]); block-uniform call
     auto kth_largest = [&](int kk) -> unsigned long long {
@@ -690,9 +701,9 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
         int krem = kk;
         for (int pass = 7; pass >= 0; --pass) {
             const int shift = pass * 8;
-            hist_s[tid] = 0;
+            if (tid < 256) hist_s[tid] = 0;
             lds_barrier();
-            for (int i = tid; i < n; i += 256) {
+            for (int i = tid; i < n; i += NT) {
                 const unsigned long long v = ord_s[i];
                 if (pass == 7 || (v >> (shift + 8)) == prefix) atomicAdd(&hist_s[(v >> shift) & 255], 1);
             }
@@ -729,35 +740,37 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
         return prefix;
     };
     // The kk-th largest packed value for kk <= kSmallK (block-uniform
-    // call): each wave takes the kk largest of its rows (up to four per
-    // lane) by repeated 64-bit wave maxima (DPP steps), the one lane that
-    // holds a maximum dropping it (the values are distinct; padding is 0,
-    // below any packed value); the global kk largest are among these 4 kk
+    // call): each wave takes the kk largest of its rows (KR per lane) by
+    // repeated 64-bit wave maxima (DPP steps), the one lane that holds a
+    // maximum dropping it (the values are distinct; padding is 0, below any
+    // packed value); the global kk largest are among these NW kk
     // candidates, and the one with exactly kk - 1 candidates above it is
     // the answer.  No atomics, three barriers.
     auto kth_small = [&](int kk) -> unsigned long long {
         const int lane = tid & 63, wid = tid >> 6;
-        unsigned long long v[4];
-        for (int j = 0; j < 4; ++j) {
-            const int t = wid * 64 + lane + 256 * j;
+        unsigned long long v[KR];
+        for (int j = 0; j < KR; ++j) {
+            const int t = wid * 64 + lane + NT * j;
             v[j] = t < n ? ord_s[t] : 0ull;
         }
         for (int it = 0; it < kk; ++it) {
-            const unsigned long long m = wave_max_u64(max(max(v[0], v[1]), max(v[2], v[3])));
-            for (int j = 0; j < 4; ++j)
+            unsigned long long mx = v[0];
+            for (int j = 1; j < KR; ++j) mx = max(mx, v[j]);
+            const unsigned long long m = wave_max_u64(mx);
+            for (int j = 0; j < KR; ++j)
                 if (v[j] == m) v[j] = 0ull;
-            if (lane == 0) cand_s[wid * kk + it] = m;    // the 4 kk candidates, packed
+            if (lane == 0) cand_s[wid * kk + it] = m;    // the NW kk candidates, packed
         }
         lds_barrier();
-        if (tid < 4 * kk) {
+        if (tid < NW * kk) {
             const unsigned long long mine = cand_s[tid];
             int above = 0;
 #pragma unroll 8
-            for (int u = 0; u < 4 * kk; ++u) above += cand_s[u] > mine ? 1 : 0;
-            if (above == kk - 1) cand_s[4 * kSmallK] = mine;
+            for (int u = 0; u < NW * kk; ++u) above += cand_s[u] > mine ? 1 : 0;
+            if (above == kk - 1) cand_s[NW * kSmallK] = mine;
         }
         lds_barrier();
-        return cand_s[4 * kSmallK];
+        return cand_s[NW * kSmallK];
     };
     const bool topk = a.mode == 1 || a.mode == 4 || a.mode == 5 || a.mode == 6;
     unsigned long long kth = 0;                 // picked iff eligible and value >= kth
@@ -765,7 +778,7 @@ __global__ __launch_bounds__(256) void posterior_finish_kernel(PostArgs a0)
         if (topk) kth = a.k <= 0 ? ~0ull : a.k >= n ? 0ull : a.k <= kSmallK ? kth_small(a.k) : kth_largest(a.k);
         else if (!any) kth = kth_small(1);
     }
-    for (int t = tid; t < n; t += 256) {
+    for (int t = tid; t < n; t += NT) {
         int out = -1;
         if (elig_s[t]) {
             const float kt = key_s[t];
@@ -823,7 +836,11 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t fi
         if (e != hipSuccess) return e;
     }
     const int groups = (a.R + a.group_rows - 1) / a.group_rows;
-    posterior_finish_kernel<<<dim3((unsigned)groups), dim3(256), 0, stream>>>(a);
+    // groups of more than 256 rows: a workgroup of kFinishWideThreads
+    if (a.group_rows > 256)
+        posterior_finish_kernel<kFinishWideThreads><<<dim3((unsigned)groups), dim3(kFinishWideThreads), 0, stream>>>(a);
+    else
+        posterior_finish_kernel<256><<<dim3((unsigned)groups), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
