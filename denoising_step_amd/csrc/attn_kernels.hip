@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         // past kv_len counting as INT_MAX, from the staged slot codes (uniform
         // across the workgroup).  A group-mask range spanning more than eight
         // slots reports the widest range, i.e. a partial tile.
-        auto key_range = [&](int t0, int len, int &kmn, int &kmx) {
+        auto key_range_lane = [&](int t0, int len, int &kmn, int &kmx) {
             const int hi = min(t0 + len, a.kv_len);
             kmn = INT_MAX;
             kmx = t0 + len > a.kv_len ? INT_MAX : INT_MIN;
@@ -420,18 +420,11 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
                     }
                 }
             }
+        };
+        auto key_range = [&](int t0, int len, int &kmn, int &kmx) {
+            key_range_lane(t0, len, kmn, kmx);
             kmn = __builtin_amdgcn_readfirstlane(kmn);
             kmx = __builtin_amdgcn_readfirstlane(kmx);
-        };
-        // Whether the tile at t0 is partial: not visible to every row of the
-        // workgroup (a ragged tail, or block-causal / group keys some row does
-        // not see).  Only partial tiles stage key codes for the predicate and
-        // check their rows.
-        auto partial_tile = [&](int t0) -> bool {
-            if (t0 + KT <= a.P) return false;
-            int kmn, kmx;
-            key_range(t0, KT, kmn, kmx);
-            return kmx > qmin;
         };
         // Direct loads of the K (with its key codes) or V half of the tile at t0
         // into LDS buffer buf.  In a partial block-causal or group tile, a row
@@ -582,6 +575,46 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
             }
         };
 
+        // The classes of the split's tiles (read once kbeg and kend are final),
+        // 64 tiles at a time with one tile per lane: the slot-code reads run in
+        // parallel and outside the tile pipeline, where a uniform LDS read would
+        // wait for every LDS read in flight.  Bit i of window w, tile
+        // kbeg + (64 w + i) KT: cls_part, partial for the workgroup (its loads
+        // check rows); cls_vis / cls_live, this wave's keys of the tile are
+        // visible to every row / to some row.  A tile is partial when it is not
+        // visible to every row of the workgroup (a ragged tail, or block-causal
+        // / group keys some row does not see): only partial tiles stage key
+        // codes for the predicate and check their rows.
+        unsigned long long cls_part = 0, cls_vis = 0, cls_live = 0;
+        int cls_win = -1;
+        auto tile_class = [&](int j, bool &part, bool &vis, bool &live) {
+            const int w = j >> 6;
+            if (w != cls_win) {
+                const int t0 = kbeg + (64 * w + lane) * KT;
+                bool pt = false, vs = true, lv = true;
+                if (t0 < kend) {
+                    int kmn, kmx;
+                    key_range_lane(t0, KT, kmn, kmx);
+                    pt = t0 + KT > a.P && kmx > qmin;
+                    if (NG == 2) key_range_lane(t0 + kofs, 64, kmn, kmx);
+                    const bool v0 = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
+                    vs = v0 || kmx <= qmin;
+                    lv = v0 || kmn <= qmax;
+                }
+                cls_part = __ballot(pt);
+                cls_vis = __ballot(vs);
+                cls_live = __ballot(lv);
+                cls_win = w;
+            }
+            part = (cls_part >> (j & 63)) & 1;
+            vis = (cls_vis >> (j & 63)) & 1;
+            live = (cls_live >> (j & 63)) & 1;
+        };
+        auto tile_part = [&](int j) -> bool {
+            bool p, v, l;
+            tile_class(j, p, v, l);
+            return p;
+        };
         // One tile: compute on LDS buffer BUF while tile t0 + KT streams into
         // the other one.  BUF is a compile-time constant, so the compiler sees
         // that the reads and the in-flight LDS loads touch different arrays and
@@ -592,19 +625,14 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
         // skipped when hidden from every row, no predicate when visible to all.
         auto tile_step = [&](auto bufc, int t0) {
             constexpr int BUF = decltype(bufc)::value;
+            const int j = (t0 - kbeg) / KT;
             if (t0 + KT < kend) {
-                const bool part = partial_tile(t0 + KT);
+                const bool part = tile_part(j + 1);
                 issue_k(t0 + KT, BUF ^ 1, part, BUF ^ 1);
                 issue_v(t0 + KT, BUF ^ 1, part);
             }
-            bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
-            bool live = true;
-            if (!vis) {
-                int kmn, kmx;
-                key_range(t0 + kofs, 64, kmn, kmx);
-                live = kmn <= qmax;
-                vis = kmx <= qmin;
-            }
+            bool part_, vis, live;
+            tile_class(j, part_, vis, live);
             if (live) {
                 const uint16_t *ks = (BUF ? Ks1 : Ks0) + kofs * D;
                 const uint16_t *vs = (BUF ? Vs1 : Vs0) + kofs * D;
@@ -684,11 +712,11 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
                 constexpr int SB = decltype(bufc)::value;
                 if (js < T) {
                     const int t0 = kbeg + js * KT;
-                    issue_k(t0, SB, partial_tile(t0), js & 3);
+                    issue_k(t0, SB, tile_part(js), js & 3);
                 }
                 if (js >= 1 && js <= T) {
                     const int t0 = kbeg + (js - 1) * KT;
-                    issue_v(t0, SB, partial_tile(t0));
+                    issue_v(t0, SB, tile_part(js - 1));
                 }
             };
             auto mfma_phase = [&](auto bufc, int jq) __attribute__((always_inline)) {   // PV of tile jq - 1, QK of tile jq (slot jq)
@@ -703,13 +731,8 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
             };
             auto softmax_phase = [&](int jq) __attribute__((always_inline)) {           // tile jq: P and the running max and sum
                 if (jq >= T) return;
-                const int t0 = kbeg + jq * KT;
-                bool vis = (a.kind == 0 && t0 + KT <= a.kv_len) || t0 + KT <= a.P;
-                if (!vis) {
-                    int kmn, kmx;
-                    key_range(t0, KT, kmn, kmx);
-                    vis = kmx <= qmin;
-                }
+                bool part, vis, live;
+                tile_class(jq, part, vis, live);
                 prep(s0, s1, kcode_s[jq & 3], vis);
                 float psum = 0.f;
                 for (int i = 0; i < 16; ++i) {
@@ -781,7 +804,7 @@ __global__ __launch_bounds__(64 * QW * NG, 2) void attn_fwd_kernel(AttnArgs a)
             }
         } else {
             if (kbeg < kend) {
-                const bool part = partial_tile(kbeg);
+                const bool part = tile_part(0);
                 issue_k(kbeg, 0, part, 0);
                 issue_v(kbeg, 0, part);
             }

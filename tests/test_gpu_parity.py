@@ -198,6 +198,25 @@ def mask_tiles_case(name, seed=0):
         kind = W.MASK_GROUP
         garbage = np.zeros((B, P + n_slots * bs), bool)
         garbage[:, P + 4 * bs:] = True
+    elif name == "bc_odd":
+        # block-causal with 37-position blocks after a 45-position prefix: block
+        # boundaries fall inside key tiles at every offset
+        P, bs, n_slots = 45, 37, 9
+        act = np.tile(np.arange(P + 20, P + 20 + 5 * bs, dtype=np.int32), (B, 1))
+        state = np.full((B, n_slots), W.SLOT_ACTIVE, np.uint8)
+        group = np.zeros((B, n_slots), np.int32)
+        kind = W.MASK_BLOCK_CAUSAL
+    elif name == "group_odd":
+        # 23-position slots, groups 0,0,1,1,1,2,2 and a DUMMY slot: slot boundaries
+        # and group changes inside tiles
+        P, bs, n_slots = 70, 23, 8
+        act = np.tile(np.arange(P, P + 6 * bs, dtype=np.int32), (B, 1))
+        state = np.full((B, n_slots), W.SLOT_ACTIVE, np.uint8)
+        state[:, 7] = W.SLOT_DUMMY
+        group = np.tile(np.array([0, 0, 1, 1, 1, 2, 2, 3], np.int32), (B, 1))
+        kind = W.MASK_GROUP
+        garbage = np.zeros((B, P + n_slots * bs), bool)
+        garbage[:, P + 7 * bs:] = True
     elif name == "group_one_block":
         # one 256-position block, every position a row: every tile visible to all
         B, Hq, Hkv, D = 1, 4, 4, 128
@@ -219,7 +238,7 @@ def mask_tiles_case(name, seed=0):
 
 
 @pytest.mark.parametrize("kgroups", ["1", "2"])
-@pytest.mark.parametrize("case", ["bc_early", "group_split", "group_one_block"])
+@pytest.mark.parametrize("case", ["bc_early", "group_split", "group_one_block", "bc_odd", "group_odd"])
 def test_mask_tile_classes(kgroups, case, monkeypatch):
     """Tiles hidden from a whole workgroup are skipped, tiles visible to all
     its rows run without the predicate, the rest run it: all three against
@@ -231,7 +250,8 @@ def test_mask_tile_classes(kgroups, case, monkeypatch):
     _, g, ora = full_check(w)
     if case != "group_one_block":
         a = w.attn
-        first_hidden = a.prefix_len + (2 if case == "bc_early" else 4) * a.block_size
+        first_block = {"bc_early": 2, "group_split": 4, "bc_odd": 6, "group_odd": 7}[case]
+        first_hidden = a.prefix_len + first_block * a.block_size
         assert np.all(g["colsum"][:, first_hidden:] == 0)
         assert np.all(ora["colsum"][:, first_hidden:] == 0)
 
