@@ -481,6 +481,7 @@ __global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
             }
         }
     };
+    int n_lrow = -1;   // the group's compacted live rows in lrow_s (live-row path only)
     if (rows_per_round < n && a.live_rows) {
         // A group of more than 256 rows under a live-row list: few rows are
         // live late in a run, each split into up to nc_cap chunks.  The live
@@ -512,6 +513,7 @@ __global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
             const int t = tid + NT * k;
             if ((bal[k] >> lane) & 1ull) lrow_s[before + __popcll(bal[k] & ((1ull << lane) - 1))] = t;
         }
+        n_lrow = L;
         lds_barrier();
         int lanes = 1;
         while (lanes < 32 && lanes * 2 * L <= NT && lanes * 2 <= nc) lanes *= 2;
@@ -650,16 +652,27 @@ __global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
         return;
     }
     lds_barrier();   // row results (LDS) visible
+    // Only rows unlocked on entry can be eligible.  When the group's live
+    // rows were compacted (lrow_s) and are few, the selection runs over them
+    // alone (entry i stands for row lrow_s[i]); the others are never picked
+    // and order after every eligible row, so no rank changes.
+    constexpr int kCountMax = 256;
+    const bool lsel = n_lrow >= 0 && n_lrow <= kCountMax;
+    const int ns = lsel ? n_lrow : n;
+    auto row_of = [&](int i) { return lsel ? lrow_s[i] : i; };
     // Dynamic threshold: the largest score of an eligible non-candidate.
     float thr = -INFINITY;
     if (a.mode == 3) {
         float v = -INFINITY;
-        for (int t = tid; t < n; t += NT)
+        for (int i = tid; i < ns; i += NT) {
+            const int t = row_of(i);
             if (elig_s[t] && !(conf_s[t] > a.tau)) v = fmaxf(v, key_s[t]);
+        }
         thr = block_max<NW>(v, red_s);
     }
     int mine = 0;
-    for (int t = tid; t < n; t += NT) {
+    for (int i = tid; i < ns; i += NT) {
+        const int t = row_of(i);
         if (!elig_s[t]) continue;
         if (a.mode == 2 && conf_s[t] > a.tau) mine = 1;
         if (a.mode == 3 && conf_s[t] > a.tau && key_s[t] > thr) mine = 1;
@@ -685,17 +698,17 @@ __global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
     // found so far, then one wave scans the bins from the top for the one
     // that holds the k-th value.  Same cost for any k.
     typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-    constexpr int kCountMax = 256;
-    const bool counted = n <= kCountMax;
+    const bool counted = ns <= kCountMax;
     lds_barrier();
-    for (int t = tid; t < n; t += NT) {
+    for (int i = tid; i < ns; i += NT) {
+        const int t = row_of(i);
         const unsigned bits = __float_as_uint(elig_s[t] ? key_s[t] : -INFINITY);
         const unsigned ord = bits ^ ((unsigned)((int)bits >> 31) | 0x80000000u);
-        ord_s[t] = ((unsigned long long)ord << 32) | (0xffffffffu - (unsigned)t);
+        ord_s[i] = ((unsigned long long)ord << 32) | (0xffffffffu - (unsigned)t);
     }
-    for (int t = n + tid; t < ((n + 1) & ~1); t += NT) ord_s[t] = 0;   // even count
+    for (int i = ns + tid; i < ((ns + 1) & ~1); i += NT) ord_s[i] = 0;   // even count
     lds_barrier();
-    // the kk-th largest packed value (kk in [1, n]); block-uniform call
+    // the kk-th largest packed value (kk in [1, ns]); block-uniform call
     auto kth_largest = [&](int kk) -> unsigned long long {
         unsigned long long prefix = 0;
         int krem = kk;
@@ -703,7 +716,7 @@ __global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
             const int shift = pass * 8;
             if (tid < 256) hist_s[tid] = 0;
             lds_barrier();
-            for (int i = tid; i < n; i += NT) {
+            for (int i = tid; i < ns; i += NT) {
                 const unsigned long long v = ord_s[i];
                 if (pass == 7 || (v >> (shift + 8)) == prefix) atomicAdd(&hist_s[(v >> shift) & 255], 1);
             }
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
         unsigned long long v[KR];
         for (int j = 0; j < KR; ++j) {
             const int t = wid * 64 + lane + NT * j;
-            v[j] = t < n ? ord_s[t] : 0ull;
+            v[j] = t < ns ? ord_s[t] : 0ull;
         }
         for (int it = 0; it < kk; ++it) {
             unsigned long long mx = v[0];
@@ -775,21 +788,25 @@ __global__ __launch_bounds__(NT) void posterior_finish_kernel(PostArgs a0)
     const bool topk = a.mode == 1 || a.mode == 4 || a.mode == 5 || a.mode == 6;
     unsigned long long kth = 0;                 // picked iff eligible and value >= kth
     if (!counted) {
-        if (topk) kth = a.k <= 0 ? ~0ull : a.k >= n ? 0ull : a.k <= kSmallK ? kth_small(a.k) : kth_largest(a.k);
+        if (topk) kth = a.k <= 0 ? ~0ull : a.k >= ns ? 0ull : a.k <= kSmallK ? kth_small(a.k) : kth_largest(a.k);
         else if (!any) kth = kth_small(1);
     }
-    for (int t = tid; t < n; t += NT) {
+    if (lsel)
+        for (int t = tid; t < n; t += NT)
+            if (!(rowf_s[t] & 1)) a.sel[g0 + t] = -1;
+    for (int i = tid; i < ns; i += NT) {
+        const int t = row_of(i);
         int out = -1;
         if (elig_s[t]) {
             const float kt = key_s[t];
-            const unsigned long long mine = ord_s[t];
+            const unsigned long long mine = ord_s[i];
             bool first = false, in_topk = false;
             if (counted) {
                 int rank = 0;
                 // sixteen 16-byte LDS reads in flight (one wave per SIMD:
                 // nothing else hides their latency)
 #pragma unroll 16
-                for (int u = 0; u < n; u += 2) {
+                for (int u = 0; u < ns; u += 2) {
                     const u64x2 p = *reinterpret_cast<const u64x2 *>(&ord_s[u]);
                     rank += (p.x > mine ? 1 : 0) + (p.y > mine ? 1 : 0);
                 }

@@ -444,7 +444,9 @@ def test_live_row_list(g, V, n_live):
     rows may arrive locked too; entries outside [0, R) (after the offset)
     and entries past the count are ignored.  Checked against the oracle on
     every row, for a staged (100-row) and a global-memory (700, 1024-row)
-    merge, with no live row and with more entries than rows."""
+    merge, with no live row and with more entries than rows, under every
+    selection mode (groups with at most 256 live rows rank those alone, a
+    k past the live count included)."""
     import denoising_step_amd as dlm
     dev = torch.device("cuda")
     rng = np.random.default_rng(90 + g + n_live)
@@ -466,12 +468,17 @@ def test_live_row_list(g, V, n_live):
     kept = lst[:count] - off
     kept = kept[(kept >= 0) & (kept < R)]
     locked[np.setdiff1d(np.arange(R), kept)] = 1
+    score = rng.random(R).astype(np.float32)
     ora = oracle.posterior(x, y, locked, 1e-3, flags=flags)
-    for mode, k, tau in [(W.SEL_TOPK_CONF, 7, 0.0), (W.SEL_THRESH_CONF, 0, 0.99)]:
-        _say(f"case: live rows g={g} V={V} n_live={n_live} mode={mode}")
+    for mode, k, tau in [(W.SEL_TOPK_CONF, 7, 0.0), (W.SEL_THRESH_CONF, 0, 0.99),
+                         (W.SEL_TOPK_SCORE, 5, 0.0), (W.SEL_TOPK_MARGIN, 3, 0.0),
+                         (W.SEL_TOPK_LOW_ENTROPY, 1, 0.0), (W.SEL_ATTN_DYNAMIC, 0, 0.3),
+                         (W.SEL_TOPK_CONF, 300, 0.0)]:
+        _say(f"case: live rows g={g} V={V} n_live={n_live} mode={mode} k={k}")
         mg = torch.empty(R, device=dev)
         en = torch.empty(R, device=dev)
         s = dlm.Select(mode=mode, k=k, group_rows=g, tau=tau, margin=mg, entropy=en,
+                       score=torch.from_numpy(score).to(dev),
                        row_flags=torch.from_numpy(flags).to(dev),
                        live_rows=torch.from_numpy(lst).to(dev),
                        n_live=torch.tensor([count], dtype=torch.int32, device=dev), live_offset=off)
@@ -486,10 +493,10 @@ def test_live_row_list(g, V, n_live):
         torch.cuda.synchronize()
         check_posterior(kl.cpu().numpy(), conf.cpu().numpy(), lk.cpu().numpy(), ora["kl"], ora["conf"],
                         ora["locked"], 1e-3, locked)
-        sel_o = oracle.select(mode, k, g, tau, np.zeros(R), ora["conf"], ora["tok"], locked,
+        sel_o = oracle.select(mode, k, g, tau, score.astype(np.float64), ora["conf"], ora["tok"], locked,
                               ora["margin"], ora["entropy"], flags=flags)
         inelig = ((locked != 0) | ((flags & 1) == 0)).astype(np.uint8)
-        check_selection(sel.cpu().numpy(), sel_o, mode, g, tau, ora["conf"], np.zeros(R),
+        check_selection(sel.cpu().numpy(), sel_o, mode, g, tau, ora["conf"], score.astype(np.float64),
                         inelig, x, ora["margin"], ora["entropy"])
         check_scores(mg.cpu().numpy(), en.cpu().numpy(), ora["margin"], ora["entropy"], locked)
 
