@@ -200,7 +200,7 @@ def summarize_loop_trace(path: str) -> str:
             cur.append((a, b))
     if cur:
         runs.append(cur)
-    cols = [c for c in LOOP_KERNELS]
+    cols = [c for c in LOOP_KERNELS if any(k[0] == c for k in ks)]   # kernels the run launched
     out = ["| step | " + " | ".join(c.replace("_kernel", "") for c in cols) + " | sum |",
            "|---" * (len(cols) + 2) + "|"]
     for si, (a, b) in enumerate(runs[-1]):

@@ -5,7 +5,9 @@ per-step buffers, and runs one step as three C-ABI calls on one stream:
 
   1. ``dlm_step_attn`` over the rows the buffer chose (active_idx with its
      row count m_active on the device) under the group mask of the buffer's
-     slot tables, with column sums over every computed row;
+     slot tables, with column sums over every computed row when the
+     selection ranks by them (the Attn-Sampler modes; the other modes never
+     read them, so the pass that makes them is not run);
   2. ``dlm_posterior`` per batch entry over the generation region: rows
      outside active slots and locked rows are skipped, selection groups are
      the blocks, rows carry the buffer's select / lock flags, and the score
@@ -27,7 +29,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MASK_GROUP, BlockBuffer, KVCache, MaskDesc, Select, dlm_block_buffer_advance,
+from . import (MASK_GROUP, SEL_ATTN_DYNAMIC, SEL_TOPK_SCORE, BlockBuffer, KVCache, MaskDesc, Select,
+               dlm_block_buffer_advance,
                dlm_block_buffer_init, dlm_posterior, dlm_posterior_workspace_bytes,
                dlm_step_attn, dlm_step_attn_workspace_bytes)
 from .runner import bf16_to_device
@@ -86,7 +89,8 @@ class DeviceLoop:
         self.v = z((B, Hkv, n_gen, D), torch.bfloat16)
         self.out = z((B, Hq, n_gen, D), torch.bfloat16)
         self.lse = z((B, Hq, n_gen), torch.float32)
-        self.colsum = z((B, kv_len), torch.float32)
+        # column sums only for a selection that ranks by them
+        self.colsum = z((B, kv_len), torch.float32) if case.mode in (SEL_ATTN_DYNAMIC, SEL_TOPK_SCORE) else None
         self.x = z((B, n_gen, V), torch.float32)
         self.y = z((B, n_gen, V), torch.float32)
         self.sel = z((B, n_gen), torch.int32)
@@ -102,7 +106,8 @@ class DeviceLoop:
         # active rows (every other row arrives with skip set), their count on
         # the device, so the vocabulary split follows M_t in the captured step.
         self.sels = [Select(mode=case.mode, k=case.k, group_rows=bs, tau=case.tau,
-                            score=self.colsum[b, P:P + n_gen], row_flags=self.bb.row_flags[b],
+                            score=None if self.colsum is None else self.colsum[b, P:P + n_gen],
+                            row_flags=self.bb.row_flags[b],
                             live_rows=self.bb.active_idx[b], n_live=self.bb.m_active[b:b + 1],
                             live_offset=P) for b in range(B)]
         self.post_ws = z((max(1, dlm_posterior_workspace_bytes(n_gen, V, self.sels[0])),), torch.uint8)
@@ -116,7 +121,8 @@ class DeviceLoop:
         with torch.cuda.stream(stream or torch.cuda.current_stream()):
             for t in (self.q, self.k, self.v, self.out, self.lse, self.colsum, self.x, self.y,
                       self.sel, self.kl, self.conf):
-                t.zero_()
+                if t is not None:
+                    t.zero_()
             self.cache_k.copy_(self.cache_k0)
             self.cache_v.copy_(self.cache_v0)
             self.bb.decoded.copy_(self.decoded0)

@@ -115,8 +115,9 @@ def test_trace_and_counter_summaries(tmp_path):
 
 def test_loop_trace_summary(tmp_path):
     """The --loop trace summariser: runs split at the Block Buffer
-    initialisations, per-step kernel sums of the last run, and the gaps
-    around and inside each step (in microseconds)."""
+    initialisations, per-step kernel sums of the last run (a column for each
+    step kernel the trace holds), and the gaps around and inside each step
+    (in microseconds)."""
     K = "void dlm::(anonymous namespace)::{}(dlm::X)"
     ev = [("block_buffer_kernel", 0, 1000),                      # run 1: initialisation
           ("feed", 2000, 3000),
@@ -132,7 +133,10 @@ def test_loop_trace_summary(tmp_path):
     trace.write_text("Kernel_Name,Start_Timestamp,End_Timestamp\n" +
                      "".join(f"\"{K.format(n)}\",{a},{b}\n" for n, a, b in ev))
     t = bench.summarize_loop_trace(str(trace))
-    assert "| 1 | 0.0 | 1.0 | 0.0 | 0.0 | 0.0 | 0.0 | 2.0 | 1.0 | 4.0 |" in t
+    # columns: the step kernels the trace holds (attn_fwd, posterior_stream,
+    # posterior_finish, block_buffer)
+    assert "| step | attn_fwd | posterior_stream | posterior_finish | block_buffer | sum |" in t
+    assert "| 1 | 1.0 | 0.0 | 2.0 | 1.0 | 4.0 |" in t
     assert "| 1 | 1 | 0.006 | 0.5 | 1.00 | 1.00 |" in t
     assert "| 2 | 1 | 0.004 | 0.0 | 2.00 | 8.00 |" in t
 
