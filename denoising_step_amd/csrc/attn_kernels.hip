@@ -1018,7 +1018,7 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
     __shared__ int kcs_s[kMaxSlots];               // GROUP: slot -> key code (INT_MAX: DUMMY)
 
     const int tid = threadIdx.x;
-    const int wid = tid >> 6, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int l32 = lane & 31, hh = lane >> 5;
 
     int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -1132,17 +1132,28 @@ __global__ __launch_bounds__(256, 2) void colsum_kernel(AttnArgs a)
         rb = r0 + (t - hl * tiles_h) * kCsRows;
         hrow = ((long)b * a.Hq + g * a.G + hl) * a.M;
     };
+    // This thread's loads of a tile (load u = wid + 4 i): the tile row and
+    // its byte offset within the tile, fixed for the whole pass.
+    constexpr int NQW = (NQL + 3) / 4;
+    int q_lr[NQW], q_goff[NQW];
+    for (int i = 0; i < NQW; ++i) {
+        const int byte = (wid + 4 * i) * 1024 + lane * 16;
+        const int lr = byte / ROWB, lp = (byte % ROWB) / 16;
+        q_lr[i] = lr;
+        q_goff[i] = (lr * D + ((lp ^ k_swz<D>(lr)) * 8)) * 2;
+    }
     auto issue_q = [&](int t, int buf) {
         int rb;
         long hrow;
         tile_rows(t, rb, hrow);
         const __amdgpu_buffer_rsrc_t qrs = buffer_view(a.q + hrow * D, r1 * ROWB);
         uint16_t *qs = buf ? Qs1 : Qs0;
-        for (int u = wid; u < NQL; u += 4) {
-            const int byte = u * 1024 + lane * 16;
-            const int lr = byte / ROWB, lp = (byte % ROWB) / 16;
-            const int off = rb + lr < r1 ? ((rb + lr) * D + ((lp ^ k_swz<D>(lr)) * 8)) * 2 : OOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)(qs + u * 512), 16, off, 0, 0, 0);
+        for (int i = 0; i < NQW; ++i) {
+            const int u = wid + 4 * i;
+            if (u < NQL) {
+                const int off = rb + q_lr[i] < r1 ? rb * ROWB + q_goff[i] : OOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)(qs + u * 512), 16, off, 0, 0, 0);
+            }
         }
         if (tid < kCsRows) {
             const int jr = rb + tid;
