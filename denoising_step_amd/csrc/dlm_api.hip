@@ -235,7 +235,7 @@ int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select
     if (!bytes) return fail(DLM_E_NULL, "bytes is NULL");
     int rc = check_post_scalars(R, V, select);
     if (rc != DLM_OK) return rc;
-    *bytes = dlm::plan_post(R, V, select->mode, select->group_rows, select->live_rows != nullptr).ws_total;
+    *bytes = dlm::post_ws_bytes(R, V, select->mode, select->group_rows, select->live_rows != nullptr);
     return DLM_OK;
 }
 
@@ -245,20 +245,31 @@ static int posterior_with(const float *logits, const float *prev_logits, uint8_t
                           const dlm_select *select, int32_t *sel, float *kl, float *conf, int32_t R,
                           int32_t V, hipStream_t stream, void *ws, size_t ws_bytes)
 {
-    dlm::PostPlan p = dlm::plan_post(R, V, select->mode, select->group_rows, select->live_rows != nullptr);
-    if (p.ws_total > 0 && (ws == nullptr || ws_bytes < p.ws_total))
-        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_total,
+    const bool live = select->live_rows != nullptr;
+    // One launch unless the selection waits for an event (the two-launch
+    // path streams the logits before that wait).
+    const bool fused = select->score_ready == nullptr;
+    dlm::PostPlan p = dlm::plan_post(R, V, select->mode, select->group_rows, live, fused);
+    const size_t need = dlm::post_ws_bytes(R, V, select->mode, select->group_rows, live);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(DLM_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     ws ? ws_bytes : (size_t)0);
     dlm::PostArgs a{};
     a.x = logits; a.y = prev_logits; a.locked = locked; a.score = select->score;
     a.sel = sel; a.kl = kl; a.conf = conf; a.margin = select->margin; a.entropy = select->entropy;
     a.flags = select->row_flags;
-    a.part = static_cast<dlm::PostPartial *>(ws);
+    a.part = reinterpret_cast<dlm::PostPartial *>(static_cast<char *>(ws) + p.off_part);
     a.R = R; a.V = V; a.mode = select->mode; a.k = select->k; a.group_rows = p.group_rows;
     a.eps = eps; a.tau = select->tau; a.conf_gate = select->conf_gate;
     a.n_chunks = p.n_chunks; a.chunk = p.chunk;
     a.live_rows = select->live_rows; a.n_live = select->n_live;
     a.live_offset = select->live_offset; a.nc_cap = p.n_chunks;
+    if (p.fused) {
+        char *w = static_cast<char *>(ws);
+        a.rowres = reinterpret_cast<dlm::PostRowRes *>(w + p.off_rowres);
+        a.row_cnt = reinterpret_cast<unsigned *>(w + p.off_row_cnt);
+        a.grp_cnt = reinterpret_cast<unsigned *>(w + p.off_grp_cnt);
+    }
     hipError_t e = dlm::launch_posterior(a, stream, select->score_ready);
     if (e != hipSuccess) return fail(DLM_E_HIP, "launch or event wait failed: %s", hipGetErrorString(e));
     return DLM_OK;
@@ -339,7 +350,7 @@ int dlm_posterior_noalloc(const float *logits, const float *prev_logits, uint8_t
     g_err[0] = 0;
     int rc = check_post_call(logits, prev_logits, locked, eps, select, sel, kl, conf, R, V);
     if (rc != DLM_OK) return rc;
-    const size_t need = dlm::plan_post(R, V, select->mode, select->group_rows, select->live_rows != nullptr).ws_total;
+    const size_t need = dlm::post_ws_bytes(R, V, select->mode, select->group_rows, select->live_rows != nullptr);
     if (need > (size_t)DLM_NOALLOC_SCRATCH_BYTES)
         return fail(DLM_E_WORKSPACE, "R=%d V=%d needs %zu bytes of partials; the allocation-free entry "
                     "point holds %zu (use dlm_posterior with a workspace)", R, V, need,

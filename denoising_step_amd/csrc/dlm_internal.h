@@ -63,15 +63,35 @@ struct PostPartial {
 };
 static_assert(sizeof(PostPartial) % 16 == 0, "partials are staged in 16-byte pieces");
 
+// A row's results handed from the workgroup that finishes the row to the
+// one that runs its selection group (single-launch path).
+struct PostRowRes {
+    float key;  // ranking key: conf, margin or -entropy
+    float conf;
+    int tok;    // lowest argmax
+    int lock;   // the lock decision of this step
+};
+
 struct PostPlan {
     int n_chunks;       // vocabulary chunks per row
     int chunk;          // elements per chunk (multiple of 4)
     int group_rows;     // rows per finishing workgroup
+    int fused;          // 1: one launch (stream + row merge + selection)
+    size_t off_part;    // workspace offset of the partials
+    size_t off_rowres, off_row_cnt, off_grp_cnt;   // fused: workspace offsets
     size_t ws_total;
 };
+// The counter block at the start of every posterior workspace: row
+// counters, then selection-group counters, kPostMaxCounters of each.
+constexpr int kPostMaxCounters = 4096;
+constexpr size_t kPostCounterBytes = 2 * kPostMaxCounters * sizeof(unsigned);
 // live: with a device live-row list (dlm_select.live_rows); the plan then
 // sizes the partials for the largest split and n_chunks is that cap.
-PostPlan plan_post(int R, int V, int mode, int group_rows, bool live = false);
+// fused: the single-launch path when the shapes allow it (no live-row
+// list, selection groups of at most 256 rows).
+PostPlan plan_post(int R, int V, int mode, int group_rows, bool live = false, bool fused = false);
+// Workspace bytes a call needs: enough for either path.
+size_t post_ws_bytes(int R, int V, int mode, int group_rows, bool live);
 
 struct AttnArgs {
     const uint16_t *q, *k, *v;      // bf16 bit patterns
@@ -107,6 +127,10 @@ struct PostArgs {
     // then chosen on the device from the count (at most nc_cap chunks)
     const int32_t *live_rows, *n_live;
     int live_offset, nc_cap;
+    // single-launch path: per-row results and the arrival counters (zero
+    // between calls: the last arrival resets its counter)
+    PostRowRes *rowres;
+    unsigned *row_cnt, *grp_cnt;
 };
 
 // Block Buffer state of a multi-step run (device arrays, see dlm_step.h).

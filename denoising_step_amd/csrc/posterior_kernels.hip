@@ -19,6 +19,7 @@
 
 #include <limits.h>
 #include <math.h>
+#include <stdlib.h>
 
 namespace dlm {
 
@@ -197,6 +198,9 @@ __host__ __device__ inline void post_split(long live, int R, int V, int mode, in
 
 // Workgroups per CU of the stream kernel's grid with a live-row list.
 constexpr int kPostLiveGridPerCU = 16;
+// Resident workgroups per CU of the single-launch kernel (seven waves per
+// SIMD): its grid is one round when it has at most this many per CU.
+constexpr int kPostFusedWgsPerCU = 7;
 
 // With a live-row list, the split this call uses (from the device count).
 __device__ __forceinline__ void live_split(PostArgs &a)
@@ -222,30 +226,12 @@ __device__ __forceinline__ long part_index(const PostArgs &a, int row, int ch)
     return per_round < n ? (long)g0 * nc + (long)ch * n + (row - g0) : (long)row * nc + ch;
 }
 
-// One workgroup per (row, chunk); with a live-row list (LIVE), a fixed
-// grid walks the (listed row, chunk) items of the device-chosen split, so
-// the workgroups follow the live rows while the launch shape stays fixed.
-template <bool VEC4, bool SC, bool LIVE>
-__global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs a0)
+// Stream chunk ch of row r (elements [ch*chunk, min(V, (ch+1)*chunk))) with
+// the whole workgroup and reduce it: thread 0 returns the chunk's state
+// (other threads: unspecified).  Fixed reduction shape: deterministic.
+template <bool VEC4, bool SC>
+__device__ __forceinline__ RowState stream_chunk(const PostArgs &a, int row, int ch, RowState *red)
 {
-    __shared__ RowState red[kPostThreads / 64];
-    PostArgs a = a0;
-    int items = 1;
-    if constexpr (LIVE) {
-        live_split(a);
-        items = min(max(*a.n_live, 0), a.R) * a.n_chunks;
-    }
-    for (int it = 0, item = blockIdx.x; LIVE ? item < items : it == 0; ++it, item += gridDim.x) {
-    int row, ch;
-    if constexpr (LIVE) {
-        row = a.live_rows[item / a.n_chunks] - a.live_offset;
-        ch = item % a.n_chunks;
-        if (row < 0 || row >= a.R) continue;
-    } else {
-        row = blockIdx.x / a.n_chunks;
-        ch = blockIdx.x % a.n_chunks;
-    }
-    if (a.locked[row]) continue;    // a locked row is never read
     const int tid = threadIdx.x;
     const long base = (long)row * a.V;
     const float *x = a.x + base, *y = a.y + base;
@@ -305,16 +291,56 @@ __global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs
     const int wid = tid >> 6;
     if ((tid & 63) == 0) red[wid] = s;
     __syncthreads();
-    if (tid == 0) {
-        RowState t = red[0];
+    RowState t = red[0];
+    if (tid == 0)
         for (int w = 1; w < kPostThreads / 64; ++w) rs_merge<SC>(t, red[w]);
-        PostPartial p;
-        p.mx = t.mx; p.sx = t.sx; p.tx = t.tx; p.my = t.my; p.sy = t.sy;
-        p.av = t.av; p.a2 = t.a2; p.ex = t.ex; p.ai = t.ai;
-        p.pad[0] = p.pad[1] = p.pad[2] = 0;
-        a.part[part_index(a, row, ch)] = p;
+    return t;
+}
+
+__device__ __forceinline__ PostPartial to_partial(const RowState &t)
+{
+    PostPartial p;
+    p.mx = t.mx; p.sx = t.sx; p.tx = t.tx; p.my = t.my; p.sy = t.sy;
+    p.av = t.av; p.a2 = t.a2; p.ex = t.ex; p.ai = t.ai;
+    p.pad[0] = p.pad[1] = p.pad[2] = 0;
+    return p;
+}
+
+__device__ __forceinline__ RowState rs_load(const PostPartial &p)
+{
+    RowState s;
+    s.mx = p.mx; s.sx = p.sx; s.tx = p.tx; s.my = p.my; s.sy = p.sy; s.av = p.av; s.ai = p.ai;
+    s.a2 = p.a2; s.ex = p.ex;
+    return s;
+}
+
+// One workgroup per (row, chunk); with a live-row list (LIVE), a fixed
+// grid walks the (listed row, chunk) items of the device-chosen split, so
+// the workgroups follow the live rows while the launch shape stays fixed.
+template <bool VEC4, bool SC, bool LIVE>
+__global__ __launch_bounds__(kPostThreads) void posterior_stream_kernel(PostArgs a0)
+{
+    __shared__ RowState red[kPostThreads / 64];
+    PostArgs a = a0;
+    int items = 1;
+    if constexpr (LIVE) {
+        live_split(a);
+        items = min(max(*a.n_live, 0), a.R) * a.n_chunks;
     }
-    if constexpr (LIVE) __syncthreads();   // red is rewritten by the next item
+    for (int it = 0, item = blockIdx.x; LIVE ? item < items : it == 0; ++it, item += gridDim.x) {
+        int row, ch;
+        if constexpr (LIVE) {
+            row = a.live_rows[item / a.n_chunks] - a.live_offset;
+            ch = item % a.n_chunks;
+            if (row < 0 || row >= a.R) continue;
+        } else {
+            row = blockIdx.x / a.n_chunks;
+            ch = blockIdx.x % a.n_chunks;
+        }
+        if (a.locked[row]) continue;    // a locked row is never read
+        const RowState t = stream_chunk<VEC4, SC>(a, row, ch, red);
+        if (threadIdx.x == 0) a.part[part_index(a, row, ch)] = to_partial(t);
+        if constexpr (LIVE) __syncthreads();   // red is rewritten by the next item
     }
 }
 
@@ -389,12 +415,204 @@ __device__ __forceinline__ float block_max(float v, float *red)
     return r;
 }
 
-__device__ __forceinline__ RowState rs_load(const PostPartial &p)
+// Hand-over between workgroups of one launch without cache-wide fences.
+// The data are written with device-coherent stores (agent-scope atomic
+// stores: write-through past this XCD's L2) and read with device-coherent
+// loads; the writer waits until its stores are acknowledged before it
+// counts its arrival (an agent-scope atomic add), and the reader loads only
+// after it has seen the count.  This is the release / acquire sequence of
+// the memory model without its L2 write-back and invalidation (buffer_wbl2
+// / buffer_inv), which only plain stores and loads need and which cost
+// about a microsecond per workgroup, serialised within an XCD.
+__device__ __forceinline__ void st_dev(void *p, float v)
+{
+    __hip_atomic_store(static_cast<unsigned *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(void *p, int v)
+{
+    __hip_atomic_store(static_cast<unsigned *>(p), (unsigned)v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev_f(const void *p)
+{
+    return __uint_as_float(__hip_atomic_load(static_cast<const unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ int ld_dev_i(const void *p)
+{
+    return (int)__hip_atomic_load(static_cast<const unsigned *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// This wave's stores acknowledged (the "memory" clobber keeps the compiler
+// from moving memory accesses across).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned arrive(unsigned *cnt)
+{
+    wait_stores();
+    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void publish_partial(PostPartial *p, const RowState &t)
+{
+    st_dev(&p->mx, t.mx); st_dev(&p->sx, t.sx); st_dev(&p->tx, t.tx); st_dev(&p->my, t.my);
+    st_dev(&p->sy, t.sy); st_dev(&p->av, t.av); st_dev(&p->a2, t.a2); st_dev(&p->ex, t.ex);
+    st_dev(&p->ai, t.ai);
+}
+
+template <bool SC>
+__device__ __forceinline__ RowState fetch_partial(const PostPartial *p)
 {
     RowState s;
-    s.mx = p.mx; s.sx = p.sx; s.tx = p.tx; s.my = p.my; s.sy = p.sy; s.av = p.av; s.ai = p.ai;
-    s.a2 = p.a2; s.ex = p.ex;
+    s.mx = ld_dev_f(&p->mx); s.sx = ld_dev_f(&p->sx); s.tx = ld_dev_f(&p->tx); s.my = ld_dev_f(&p->my);
+    s.sy = ld_dev_f(&p->sy); s.av = ld_dev_f(&p->av); s.ai = ld_dev_i(&p->ai);
+    if constexpr (SC) {
+        s.a2 = ld_dev_f(&p->a2);
+        s.ex = ld_dev_f(&p->ex);
+    } else {
+        s.a2 = -INFINITY;
+        s.ex = 0.f;
+    }
     return s;
+}
+
+// The single launch: stream + row merge + selection.  Workgroup (row,
+// chunk) streams its chunk as above and publishes the partial; the
+// workgroup that arrives last at the row (an atomic count, no waiting)
+// merges the row's partials in chunk order, finishes KL / conf / tok and
+// the lock test, and hands the row's results on; the one that arrives last
+// at the selection group (at most 256 rows) reads them back, writes the
+// lock flags and runs the selection.  A row that arrives locked is handled
+// by its chunk-0 workgroup alone.  Every counter is reset by its last
+// arrival, so the workspace's counters are zero between calls.  Nothing
+// writes a lock flag of a group before every row of the group has read its
+// own: the eligibility of the selection sees the entry flags.
+template <bool VEC4, bool SC>
+__global__ __launch_bounds__(kPostThreads, SC ? 5 : 7) void posterior_fused_kernel(PostArgs a)
+{
+    __shared__ RowState red[kPostThreads / 64];
+    __shared__ int row_last_s, grp_last_s, any_s;
+    __shared__ float red_s[kPostThreads / 64];
+    __shared__ __attribute__((aligned(16))) unsigned long long ord_s[kPostThreads];
+
+    const int tid = threadIdx.x;
+    const int nc = a.n_chunks;
+    const int row = blockIdx.x / nc, ch = blockIdx.x - (blockIdx.x / nc) * nc;
+    const bool was_locked = a.locked[row] != 0;
+    if (was_locked && ch != 0) return;
+    RowState s;
+    rs_init(s);
+    if (!was_locked) {
+        s = stream_chunk<VEC4, SC>(a, row, ch, red);
+        if (nc > 1) {
+            if (tid == 0) {
+                publish_partial(&a.part[(long)row * nc + ch], s);
+                row_last_s = arrive(&a.row_cnt[row]) == (unsigned)(nc - 1);
+            }
+            __syncthreads();
+            if (!row_last_s) return;
+            if (tid < 64) {
+                // lane l merges chunks l, l + 64, ... in order, then a fixed
+                // butterfly over the wave
+                RowState m;
+                rs_init(m);
+                for (int c = tid; c < nc; c += 64) rs_merge<SC>(m, fetch_partial<SC>(&a.part[(long)row * nc + c]));
+                for (int k = 32; k >= 1; k >>= 1) rs_merge<SC>(m, rs_shfl_xor<SC>(m, k));
+                s = m;
+            }
+            if (tid == 0) __hip_atomic_store(&a.row_cnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (tid == 0) {
+        float klv = 0.f, cf = 0.f, mg = 0.f, en = 0.f;
+        int tok = -1, lock = 0;
+        if (!was_locked) {
+            // KL = t/sx - (mx + ln sx) + (my + ln sy)
+            klv = s.tx / s.sx - (s.mx - s.my) - (logf(s.sx) - logf(s.sy));
+            cf = 1.f / s.sx;
+            tok = s.ai;
+            const int fl = a.flags ? a.flags[row] : 3;
+            lock = (klv <= a.eps && (fl & 2) && cf >= a.conf_gate) ? 1 : 0;
+            // margin = conf * (1 - exp(a2 - mx)); entropy = ln sx - ex / sx
+            mg = cf * (1.f - fast_exp2((s.a2 - s.mx) * kLog2e));
+            en = logf(s.sx) - s.ex / s.sx;
+        }
+        a.kl[row] = klv;
+        a.conf[row] = cf;
+        if (a.margin) a.margin[row] = mg;
+        if (a.entropy) a.entropy[row] = en;
+        if (a.mode == 0) {
+            if (!was_locked) a.locked[row] = lock;
+            a.sel[row] = -1;
+        } else {
+            if (!was_locked) {
+                PostRowRes *rr = &a.rowres[row];
+                st_dev(&rr->key, a.mode == 5 ? mg : a.mode == 6 ? -en : cf);
+                st_dev(&rr->conf, cf);
+                st_dev(&rr->tok, tok);
+                st_dev(&rr->lock, lock);
+            }
+            const int gi = row / a.group_rows;
+            const int n = min(a.R - gi * a.group_rows, a.group_rows);
+            grp_last_s = arrive(&a.grp_cnt[gi]) == (unsigned)(n - 1);
+        }
+    }
+    if (a.mode == 0) return;
+    __syncthreads();
+    if (!grp_last_s) return;
+
+    // Selection over the group's n <= 256 rows, thread t for row g0 + t.
+    const int gi = row / a.group_rows;
+    const int g0 = gi * a.group_rows;
+    const int n = min(a.R - g0, a.group_rows);
+    const bool by_score = a.mode == 3 || a.mode == 4;
+    const int t = tid;
+    bool elig = false;
+    float key = -INFINITY, cf = 0.f;
+    int tok = -1;
+    if (t < n) {
+        const int r = g0 + t;
+        const bool lk = a.locked[r] != 0;                 // entry flag (see above)
+        const int fl = a.flags ? a.flags[r] : 3;
+        if (!lk) {
+            const PostRowRes *rr = &a.rowres[r];
+            cf = ld_dev_f(&rr->conf);
+            tok = ld_dev_i(&rr->tok);
+            key = by_score ? a.score[r] : ld_dev_f(&rr->key);
+            a.locked[r] = (uint8_t)ld_dev_i(&rr->lock);
+        }
+        elig = !lk && (fl & 1);
+    }
+    if (tid == 0) __hip_atomic_store(&a.grp_cnt[gi], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Dynamic threshold: the largest score of an eligible non-candidate.
+    float thr = -INFINITY;
+    if (a.mode == 3) thr = block_max<kPostThreads / 64>(elig && !(cf > a.tau) ? key : -INFINITY, red_s);
+    const bool mine = elig && ((a.mode == 2 && cf > a.tau) || (a.mode == 3 && cf > a.tau && key > thr));
+    if (tid == 0) any_s = 0;
+    lds_barrier();
+    if (mine) any_s = 1;                    // benign race: every writer stores 1
+    // (key desc, row asc) as one unsigned 64-bit order, as in the
+    // finishing kernel; ineligible rows take key -inf and sort last.
+    const unsigned bits = __float_as_uint(elig ? key : -INFINITY);
+    const unsigned ord = bits ^ ((unsigned)((int)bits >> 31) | 0x80000000u);
+    const unsigned long long me = ((unsigned long long)ord << 32) | (0xffffffffu - (unsigned)t);
+    ord_s[t] = t < n ? me : 0ull;
+    lds_barrier();
+    const int any = any_s;
+    if (t >= n) return;
+    int out = -1;
+    if (elig) {
+        typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+        int rank = 0;
+#pragma unroll 16
+        for (int u = 0; u < n; u += 2) {
+            const u64x2 p = *reinterpret_cast<const u64x2 *>(&ord_s[u]);
+            rank += (p.x > me ? 1 : 0) + (p.y > me ? 1 : 0);
+        }
+        const bool first = rank == 0;
+        bool pick = false;
+        if (a.mode == 1 || a.mode == 4 || a.mode == 5 || a.mode == 6) pick = rank < a.k;
+        else if (a.mode == 2) pick = any ? cf > a.tau : first;
+        else if (a.mode == 3) pick = any ? (cf > a.tau && key > thr) : first;
+        if (pick) out = tok;
+    }
+    a.sel[g0 + t] = out;
 }
 
 template <int NT>
@@ -837,6 +1055,16 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t fi
     const bool live = a.live_rows != nullptr;
     if (live && nwg > (long)kPostLiveGridPerCU * kNumCU) nwg = (long)kPostLiveGridPerCU * kNumCU;
     const dim3 grid((unsigned)nwg), block(kPostThreads);
+    if (a.rowres) {
+        if ((a.V & 3) == 0) {
+            if (sc) posterior_fused_kernel<true, true><<<grid, block, 0, stream>>>(a);
+            else posterior_fused_kernel<true, false><<<grid, block, 0, stream>>>(a);
+        } else {
+            if (sc) posterior_fused_kernel<false, true><<<grid, block, 0, stream>>>(a);
+            else posterior_fused_kernel<false, false><<<grid, block, 0, stream>>>(a);
+        }
+        return hipGetLastError();
+    }
 #define DLM_POST_STREAM(V4, SC_)                                                              \
     (live ? (posterior_stream_kernel<V4, SC_, true><<<grid, block, 0, stream>>>(a), 0)       \
           : (posterior_stream_kernel<V4, SC_, false><<<grid, block, 0, stream>>>(a), 0))
@@ -861,16 +1089,53 @@ hipError_t launch_posterior(const PostArgs &a, hipStream_t stream, hipEvent_t fi
     return hipGetLastError();
 }
 
-PostPlan plan_post(int R, int V, int mode, int group_rows, bool live)
+PostPlan plan_post(int R, int V, int mode, int group_rows, bool live, bool fused)
 {
     PostPlan p{};
+    p.group_rows = mode == 0 ? 256 : group_rows;
+    const long groups = mode == 0 ? 0 : ((long)R + p.group_rows - 1) / p.group_rows;
+    // The single launch: no live-row list, selection groups of at most 256
+    // rows (one thread per row in its selection) and counters that fit the
+    // workspace's fixed counter block; DLM_POST_FUSED=0 keeps the
+    // two-launch path (measurement).
     // With a live-row list the partials are sized for the largest split a
     // call can choose (one live row), and the kernels pick the split from
     // the device count.
     post_split(live ? 1 : R, R, V, mode, group_rows, 0, p.n_chunks, p.chunk);
-    p.group_rows = mode == 0 ? 256 : group_rows;
-    p.ws_total = (size_t)R * p.n_chunks * sizeof(PostPartial);
+    // ... and only when its grid is one round of resident workgroups: each
+    // workgroup's hand-over (an acknowledged store and an atomic round trip,
+    // 2-3 us) then overlaps the other workgroups' streaming, where with
+    // more rounds it adds up (measured on MI355X: 32 x 126464 and 256 x
+    // 151936 rows gain 1-3 us over the two launches, 1024 x 151936 in
+    // 4096 workgroups loses 6 %).
+    const long wgs = (long)R * p.n_chunks;
+    bool fz = fused && !live && p.group_rows <= kPostThreads && R > 0 && groups <= kPostMaxCounters &&
+              (p.n_chunks == 1 || R <= kPostMaxCounters) && wgs <= (long)kPostFusedWgsPerCU * kNumCU;
+    if (const char *e = getenv("DLM_POST_FUSED"))
+        if (e[0] == '0' && e[1] == 0) fz = false;
+    p.fused = fz ? 1 : 0;
+    if (R == 0) return p;
+    // Every layout starts with the counter block (row counters, then group
+    // counters), so calls of any shape and either path can share a
+    // workspace: only counters are ever written there, and every call
+    // leaves them zero.
+    size_t off = kPostCounterBytes;
+    p.off_row_cnt = 0;
+    p.off_grp_cnt = (size_t)kPostMaxCounters * sizeof(unsigned);
+    if (fz) {
+        p.off_rowres = off;
+        off += ((size_t)R * sizeof(PostRowRes) + 255) / 256 * 256;
+    }
+    p.off_part = off;
+    p.ws_total = off + (size_t)R * p.n_chunks * sizeof(PostPartial);
     return p;
+}
+
+size_t post_ws_bytes(int R, int V, int mode, int group_rows, bool live)
+{
+    const size_t a = plan_post(R, V, mode, group_rows, live, false).ws_total;
+    const size_t b = plan_post(R, V, mode, group_rows, live, true).ws_total;
+    return a > b ? a : b;
 }
 
 }  // namespace dlm

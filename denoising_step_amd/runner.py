@@ -86,7 +86,7 @@ class DeviceStep:
                                  margin=self.margin if scores else None,
                                  entropy=self.entropy if scores else None)
             ws = dlm_posterior_workspace_bytes(p.R, p.V, self.select)
-            self.post_ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+            self.post_ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)
             self.select.workspace = self.post_ws
 
     def reset(self):

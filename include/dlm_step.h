@@ -215,7 +215,12 @@ typedef struct {
     int32_t group_rows;      /* rows per selection group (consecutive rows), 1..1024 */
     float tau;               /* THRESH_CONF / ATTN_DYNAMIC confidence threshold */
     const float *score;      /* device fp32 [R]: ATTN_DYNAMIC / TOPK_SCORE ranking key */
-    void *workspace;         /* device scratch, >= dlm_posterior_workspace_bytes() */
+    void *workspace;         /* device scratch, >= dlm_posterior_workspace_bytes().
+                                Zero it once when it is allocated (hipMemset): it
+                                holds arrival counters that every call leaves at zero
+                                again, so a workspace reused by later calls needs no
+                                clearing (nor a memset node inside a captured graph).
+                                Any other use of its bytes between calls breaks this. */
     size_t workspace_bytes;
     hipEvent_t score_ready;  /* optional (NULL: none).  The selection stage, the only
                                 part that reads `score`, first waits for this event on
@@ -273,6 +278,14 @@ enum { DLM_ROW_SELECT = 1, DLM_ROW_LOCK = 2 };
  * A row that arrives locked is not read: kl = conf = 0, sel = -1, stays locked.
  * kl and conf are fp32; KL is computed in one pass as
  * E_p[x - y] - (logsumexp x - logsumexp y).
+ * Without a live-row list or a score_ready event, with selection groups of
+ * at most 256 rows, and when its (row, vocabulary chunk) workgroups fit one
+ * round on the GPU (1792), the call is one kernel launch: the workgroups
+ * of a row's chunks count their arrivals in the workspace, the last one
+ * merges the row, and the last row of a group runs its selection.
+ * Otherwise a second launch merges and selects.  Results are deterministic
+ * for given shapes on either path; the two paths merge a row's chunks in
+ * different fp32 orders.
  *
  * Arguments (device unless stated):
  *   logits       fp32 [R, V]   step-t logits
@@ -300,12 +313,13 @@ int dlm_posterior_workspace_bytes(int32_t R, int32_t V, const dlm_select *select
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Same arguments, outputs and errors as
  * dlm_posterior; select->workspace and workspace_bytes are ignored.  The
- * per-(row, vocabulary chunk) partials go to a file-scope device array of
- * DLM_NOALLOC_SCRATCH_BYTES, which each GPU the library runs on holds from
- * the first call on it until the process ends; its device address is
+ * per-(row, vocabulary chunk) partials and the arrival counters go to a
+ * file-scope device array of DLM_NOALLOC_SCRATCH_BYTES (zero when the module
+ * loads; every call leaves its counters zero), which each GPU the library
+ * runs on holds from the first call on it until the process ends; its device address is
  * fetched on that first call (the only call that may load the module's
  * globals), after which no call allocates or frees anything.
- * Limit: a problem whose partials (dlm_posterior_workspace_bytes) exceed
+ * Limit: a problem whose workspace (dlm_posterior_workspace_bytes) exceeds
  * DLM_NOALLOC_SCRATCH_BYTES returns DLM_E_WORKSPACE before any work is
  * enqueued.  Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race and give

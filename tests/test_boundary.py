@@ -69,8 +69,14 @@ def test_workspace_queries():
     # a live-row list sizes the partials for the largest split any count can choose
     big = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=16, group_rows=1024)
     live = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=16, group_rows=1024, live_rows=FAKE, n_live=FAKE)
-    assert dlm.dlm_posterior_workspace_bytes(1024, 126464, big) == 1024 * 4 * 48
-    assert dlm.dlm_posterior_workspace_bytes(1024, 126464, live) == 1024 * 31 * 48
+    # every layout starts with the 32 KiB block of arrival counters
+    ctr = 2 * 4096 * 4
+    assert dlm.dlm_posterior_workspace_bytes(1024, 126464, big) == ctr + 1024 * 4 * 48
+    assert dlm.dlm_posterior_workspace_bytes(1024, 126464, live) == ctr + 1024 * 31 * 48
+    # groups of at most 256 rows in one round of workgroups: room for the
+    # single launch's per-row results before the partials (4 chunks a row)
+    fz = dlm.Select(mode=dlm.SEL_TOPK_SCORE, k=16, group_rows=256, score=FAKE)
+    assert dlm.dlm_posterior_workspace_bytes(256, 151936, fz) == ctr + 256 * 16 + 256 * 4 * 48
 
 
 @pytest.mark.parametrize("case,code", [

@@ -247,7 +247,7 @@ def test_confidence_gate():
     o = oracle.posterior(x, y, locked, 1e-3, conf_gate=gate)
     assert (o["locked"] != o0["locked"]).any()
     s = dlm.Select(mode=dlm.SEL_NONE, conf_gate=gate)
-    s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device="cuda")
+    s.workspace = torch.zeros(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device="cuda")
     lk = torch.zeros(R, dtype=torch.uint8, device="cuda")
     sel = torch.empty(R, dtype=torch.int32, device="cuda")
     kl = torch.empty(R, device="cuda")

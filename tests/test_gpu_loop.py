@@ -208,7 +208,7 @@ def test_posterior_row_flags(mode, k, g, V):
     sel, kl, conf = (torch.empty(R, dtype=dt, device="cuda") for dt in (torch.int32, torch.float32,
                                                                        torch.float32))
     s = dlm.Select(mode=mode, k=k, group_rows=g, tau=p.tau, score=_t(p.score), row_flags=_t(flags))
-    s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
+    s.workspace = torch.zeros(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
                               device="cuda")
     dlm.dlm_posterior(_t(p.logits), _t(p.prev), locked, p.eps, s, sel, kl, conf, R, V)
     torch.cuda.synchronize()

@@ -258,23 +258,41 @@ def test_mask_tile_classes(kgroups, case, monkeypatch):
 
 @pytest.mark.parametrize("mode", [True, "pass1"])
 @pytest.mark.parametrize("case", ["llada_dynamic", "long_topk_score"])
-def test_overlapped_step_equals_serial(case, mode):
+def test_overlapped_step_equals_serial(case, mode, monkeypatch):
     """The overlapped schedules (posterior on a second stream from the start
     of the step, or from mask_desc.pass1_done; its selection waiting for
     the column sums through select.score_ready) give the same bits as the
-    serial one, for both selection modes that read the score."""
+    serial step on the same (two-launch) posterior kernels, for both
+    selection modes that read the score.  Against the serial step's
+    one-launch posterior, which merges the vocabulary chunks in another
+    fp32 order, the attention outputs are the same bits and the posterior
+    differs by rounding only."""
     w = small_llada(spread=True, seed=4) if case == "llada_dynamic" else small_long(seed=5)
     _say(f"case: overlap {case} ({mode})")
     ds = _device_step(w)
     ds.run()
     r1 = ds.results()
+    monkeypatch.setenv("DLM_POST_FUSED", "0")
+    ds.reset()
+    ds.run()
+    r0 = ds.results()
+    monkeypatch.delenv("DLM_POST_FUSED")
     for rep in range(3):
         ds.reset()
         ds.colsum.fill_(float("nan"))      # a read before the sums are ready would show
         ds.run(overlap=mode)
         r2 = ds.results()
         for k in ("out", "lse", "colsum", "kl", "conf", "sel", "locked", "cache_k", "cache_v"):
+            assert np.array_equal(r0[k], r2[k], equal_nan=False), (rep, k)
+        for k in ("out", "lse", "colsum", "cache_k", "cache_v"):
             assert np.array_equal(r1[k], r2[k], equal_nan=False), (rep, k)
+        assert np.abs(r1["kl"].astype(np.float64) - r2["kl"]).max() <= 2e-6
+        assert np.abs(r1["conf"].astype(np.float64) - r2["conf"]).max() <= 1e-6
+        near = np.abs(r2["kl"].astype(np.float64) - w.post.eps) <= 1e-5   # a lock decided by rounding
+        assert np.array_equal(r1["locked"][~near], r2["locked"][~near])
+        # a selection decided by rounding: a confidence within 1e-6 of tau
+        edge = np.abs(r2["conf"].astype(np.float64) - w.post.tau) <= 1e-6
+        assert np.array_equal(r1["sel"], r2["sel"]) or edge.any()
 
 
 def test_posterior_stream_variants_agree():
@@ -371,7 +389,7 @@ def test_posterior_edge_cases():
         _say(f"case: posterior edges mode={mode}")
         s = dlm.Select(mode=mode, k=k, group_rows=g, tau=tau,
                        score=torch.from_numpy(score).to(dev))
-        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device=dev)
+        s.workspace = torch.zeros(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device=dev)
         lk = torch.from_numpy(locked.copy()).to(dev)
         sel = torch.empty(R, dtype=torch.int32, device=dev)
         kl = torch.empty(R, dtype=torch.float32, device=dev)
@@ -386,6 +404,81 @@ def test_posterior_edge_cases():
                         locked, np.nan_to_num(x))
         assert kl.cpu().numpy()[5] == 0.0 or abs(kl.cpu().numpy()[5]) < 1e-6
         assert np.all(sel.cpu().numpy()[locked == 1] == -1)
+
+
+def test_single_launch_posterior_shares_one_workspace(monkeypatch):
+    """The one-launch posterior (arrival counters in the workspace, the last
+    chunk of a row merges it, the last row of a group selects; taken when
+    its grid is one round of workgroups) on a sequence of calls of
+    different shapes and both paths sharing one workspace that was zeroed
+    once: every call against the oracle, the counter block zero after every
+    call, a repeated call bitwise equal, and the two-launch path (a
+    score_ready event; DLM_POST_FUSED=0) on the same inputs also within the
+    parity bounds of the oracle."""
+    import denoising_step_amd as dlm
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(77)
+    cases = [
+        # R, V, mode, k, tau, group, margin/entropy, flags
+        (1, 151936, W.SEL_TOPK_CONF, 1, 0.0, 1, False, False),       # 38 chunks in one row
+        (150, 40000, W.SEL_TOPK_MARGIN, 3, 0.0, 7, True, True),      # ragged groups, margin path
+        (1024, 8192, W.SEL_TOPK_CONF, 4, 0.0, 32, False, False),     # 2048 workgroups: two launches
+        (64, 1003, W.SEL_THRESH_CONF, 0, 0.05, 64, False, False),    # V not a multiple of 4
+        (300, 9000, W.SEL_NONE, 0, 0.0, 1, False, True),             # no selection, 3 chunks
+        (256, 70000, W.SEL_TOPK_SCORE, 16, 0.0, 256, False, False),  # one 256-row group
+        (96, 20000, W.SEL_ATTN_DYNAMIC, 0, 0.3, 32, True, False),
+        (50, 8192, W.SEL_TOPK_LOW_ENTROPY, 2, 0.0, 10, True, False),  # every row locked below
+    ]
+    need = 0
+    for R, V, mode, k, tau, g, sc, fl in cases:
+        need = max(need, dlm.dlm_posterior_workspace_bytes(R, V, dlm.Select(mode=mode, k=k, group_rows=g)))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ctr = 2 * 4096 * 4
+    for ci, (R, V, mode, k, tau, g, sc, fl) in enumerate(cases):
+        x = (rng.standard_normal((R, V)) * rng.uniform(0.5, 4.0, R)[:, None]).astype(np.float32)
+        y = (x + rng.standard_normal((R, V)) * np.where(rng.random(R) < 0.4, 0.005, 0.1)[:, None]).astype(np.float32)
+        locked = np.ones(R, np.uint8) if ci == len(cases) - 1 else (rng.random(R) < 0.2).astype(np.uint8)
+        flags = np.where(rng.random(R) < 0.15, 2, 3).astype(np.uint8) if fl else None
+        score = rng.random(R).astype(np.float32)
+        ora = oracle.posterior(x, y, locked, 1e-3, flags=flags)
+        sel_o = oracle.select(mode, k, g, tau, score.astype(np.float64), ora["conf"], ora["tok"], locked,
+                              ora["margin"], ora["entropy"], flags=flags)
+        inelig = locked if flags is None else ((locked != 0) | ((flags & 1) == 0)).astype(np.uint8)
+        xd, yd, sd = (torch.from_numpy(a).to(dev) for a in (x, y, score))
+        fd = torch.from_numpy(flags).to(dev) if fl else None
+        runs = []
+        for path in ("fused", "fused", "event", "env"):
+            _say(f"case: one-launch posterior R={R} V={V} mode={mode} group={g} path={path}")
+            if path == "env":
+                monkeypatch.setenv("DLM_POST_FUSED", "0")
+            mg = torch.empty(R, device=dev) if sc else None
+            en = torch.empty(R, device=dev) if sc else None
+            s = dlm.Select(mode=mode, k=k, group_rows=g, tau=tau, score=sd, margin=mg, entropy=en, row_flags=fd)
+            s.workspace = ws
+            if path == "event":
+                ev = torch.cuda.Event()
+                ev.record()
+                s.score_ready = ev
+            lk = torch.from_numpy(locked.copy()).to(dev)
+            sel = torch.empty(R, dtype=torch.int32, device=dev)
+            kl = torch.empty(R, dtype=torch.float32, device=dev)
+            conf = torch.empty(R, dtype=torch.float32, device=dev)
+            dlm.dlm_posterior(xd, yd, lk, 1e-3, s, sel, kl, conf, R, V)
+            torch.cuda.synchronize()
+            monkeypatch.delenv("DLM_POST_FUSED", raising=False)
+            assert int(ws[:ctr].count_nonzero()) == 0, f"counters not left at zero after {path}"
+            r = dict(kl=kl.cpu().numpy(), conf=conf.cpu().numpy(), sel=sel.cpu().numpy(), locked=lk.cpu().numpy())
+            check_posterior(r["kl"], r["conf"], r["locked"], ora["kl"], ora["conf"], ora["locked"], 1e-3, locked)
+            check_selection(r["sel"], sel_o, mode, g, tau, ora["conf"], score.astype(np.float64), inelig, x,
+                            ora["margin"], ora["entropy"])
+            if sc:
+                check_scores(mg.cpu().numpy(), en.cpu().numpy(), ora["margin"], ora["entropy"], locked)
+            runs.append(r)
+        for key in ("kl", "conf", "sel", "locked"):
+            assert np.array_equal(runs[0][key], runs[1][key]), key   # deterministic
+            assert np.array_equal(runs[2][key], runs[3][key]), key   # the two-launch path, either way
+        if ci == len(cases) - 1:
+            assert np.all(runs[0]["sel"] == -1) and np.all(runs[0]["kl"] == 0)
 
 
 @pytest.mark.parametrize("g,V", [(200, 600), (257, 600), (700, 600), (1024, 600), (129, 33000), (300, 40000)])
@@ -415,7 +508,7 @@ def test_large_selection_groups(g, V):
         en = torch.empty(R, device=dev)
         s = dlm.Select(mode=mode, k=k, group_rows=g, tau=tau, score=torch.from_numpy(score).to(dev),
                        margin=mg, entropy=en, row_flags=torch.from_numpy(flags).to(dev))
-        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
+        s.workspace = torch.zeros(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
                                   device=dev)
         lk = torch.from_numpy(locked.copy()).to(dev)
         sel = torch.empty(R, dtype=torch.int32, device=dev)
@@ -482,7 +575,7 @@ def test_live_row_list(g, V, n_live):
                        row_flags=torch.from_numpy(flags).to(dev),
                        live_rows=torch.from_numpy(lst).to(dev),
                        n_live=torch.tensor([count], dtype=torch.int32, device=dev), live_offset=off)
-        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
+        s.workspace = torch.zeros(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8,
                                   device=dev)
         lk = torch.from_numpy(locked.copy()).to(dev)
         sel = torch.empty(R, dtype=torch.int32, device=dev)
@@ -525,7 +618,7 @@ def test_margin_entropy_samplers(V):
         mg = torch.full((R,), float("nan"), device=dev)
         en = torch.full((R,), float("nan"), device=dev)
         s = dlm.Select(mode=mode, k=k, group_rows=g, margin=mg, entropy=en)
-        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device=dev)
+        s.workspace = torch.zeros(max(1, dlm.dlm_posterior_workspace_bytes(R, V, s)), dtype=torch.uint8, device=dev)
         lk = torch.from_numpy(locked.copy()).to(dev)
         sel = torch.empty(R, dtype=torch.int32, device=dev)
         kl = torch.empty(R, dtype=torch.float32, device=dev)

@@ -47,7 +47,7 @@ def _run(dlm, p, fn, with_scores):
     s = dlm.Select(mode=p.mode, k=p.k, group_rows=p.group_rows, tau=p.tau, score=score,
                    margin=margin, entropy=entropy)
     if fn is dlm.dlm_posterior:
-        s.workspace = torch.empty(max(1, dlm.dlm_posterior_workspace_bytes(p.R, p.V, s)), dtype=torch.uint8,
+        s.workspace = torch.zeros(max(1, dlm.dlm_posterior_workspace_bytes(p.R, p.V, s)), dtype=torch.uint8,
                                   device=dev)
     fn(x, y, locked, p.eps, s, sel, kl, conf, p.R, p.V)
     torch.cuda.synchronize()
