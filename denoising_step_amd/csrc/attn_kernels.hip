@@ -1411,6 +1411,22 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap, 
     // shorter splits lose more to the split merge than they gain in
     // parallelism (measured on MI355X).
     p.n_kgroups = base >= 2L * kNumCU ? 1 : 2;
+    // A planned launch whose two-key-group shape would split the keys (so
+    // pays the split merge anyway) takes one key group of 32 * qwaves1 rows
+    // with about twice the splits when that gives at least as many
+    // workgroups: each K/V chunk is then read by half as many workgroups
+    // (measured on MI355X: the long-prefix pass 1, 256 rows over 16640 keys,
+    // 96 -> 90 us; the multi-block one, which needs no split, keeps two key
+    // groups).
+    if (!dyn && p.n_kgroups == 2 && qwaves1(D) != 4 && base > 0 && base < kAttnWgTarget) {
+        auto wgs_for = [&](long bs, int tl) {
+            const int kt = (kv_len + tl - 1) / tl;
+            const long sp = min((kAttnWgTarget + bs - 1) / bs, (long)max(1, kt / (1024 / tl)));
+            return bs * sp;
+        };
+        const long base1 = (long)B * Hkv * ((p.G * M + 32 * qwaves1(D) - 1) / (32 * qwaves1(D)));
+        if (wgs_for(base1, 64) >= wgs_for(base, 128)) p.n_kgroups = 1;
+    }
     // DLM_ATTN_KGROUPS=1 or 2 forces the workgroup shape (tests and tuning;
     // the workspace query must see the same setting as the call).
     if (const char *e = getenv("DLM_ATTN_KGROUPS")) {
@@ -1424,7 +1440,7 @@ AttnPlan plan_attn(int B, int Hq, int Hkv, int D, int M, int kv_len, int n_cap, 
     const int tile = 64 * p.n_kgroups;
     const int key_tiles = (kv_len + tile - 1) / tile;
     int split = 1;
-    if (p.n_kgroups == 2 && base > 0 && base < kAttnWgTarget) {
+    if (base > 0 && base < kAttnWgTarget) {
         split = (int)((kAttnWgTarget + base - 1) / base);
         split = min(split, max(1, key_tiles / (1024 / tile)));
     }
