@@ -427,6 +427,8 @@ def test_single_launch_posterior_shares_one_workspace(monkeypatch):
         (300, 9000, W.SEL_NONE, 0, 0.0, 1, False, True),             # no selection, 3 chunks
         (256, 70000, W.SEL_TOPK_SCORE, 16, 0.0, 256, False, False),  # one 256-row group
         (96, 20000, W.SEL_ATTN_DYNAMIC, 0, 0.3, 32, True, False),
+        (8, 9001, W.SEL_TOPK_CONF, 2, 0.0, 4, True, False),          # V % 4 != 0 with 3 chunks a row
+        (5, 1, W.SEL_TOPK_CONF, 2, 0.0, 5, False, False),            # V = 1
         (50, 8192, W.SEL_TOPK_LOW_ENTROPY, 2, 0.0, 10, True, False),  # every row locked below
     ]
     need = 0
@@ -479,6 +481,49 @@ def test_single_launch_posterior_shares_one_workspace(monkeypatch):
             assert np.array_equal(runs[2][key], runs[3][key]), key   # the two-launch path, either way
         if ci == len(cases) - 1:
             assert np.all(runs[0]["sel"] == -1) and np.all(runs[0]["kl"] == 0)
+
+
+def test_single_launch_posterior_graph_replays():
+    """The one-launch posterior captured in a HIP graph: its arrival counters
+    reset themselves (no memset node), so every replay, with eager work and
+    synchronisations between replays, gives the eager call's bits."""
+    import denoising_step_amd as dlm
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(91)
+    R, V, g = 64, 20000, 16
+    x = torch.from_numpy((rng.standard_normal((R, V)) * 3).astype(np.float32)).to(dev)
+    y = (x + torch.from_numpy((rng.standard_normal((R, V)) * 0.02).astype(np.float32)).to(dev)).contiguous()
+    locked0 = torch.from_numpy((rng.random(R) < 0.2).astype(np.uint8)).to(dev)
+    s = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=3, group_rows=g)
+    s.workspace = torch.zeros(dlm.dlm_posterior_workspace_bytes(R, V, s), dtype=torch.uint8, device=dev)
+    lk = locked0.clone()
+    sel = torch.empty(R, dtype=torch.int32, device=dev)
+    kl = torch.empty(R, dtype=torch.float32, device=dev)
+    conf = torch.empty(R, dtype=torch.float32, device=dev)
+    _say("case: one-launch posterior, eager")
+    dlm.dlm_posterior(x, y, lk, 1e-3, s, sel, kl, conf, R, V)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (sel, kl, conf, lk)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    lk.copy_(locked0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        dlm.dlm_posterior(x, y, lk, 1e-3, s, sel, kl, conf, R, V)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        _say(f"case: one-launch posterior, graph replay {rep}")
+        lk.copy_(locked0)
+        sel.fill_(-7)
+        kl.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want, name in zip((sel, kl, conf, lk), ref, ("sel", "kl", "conf", "locked")):
+            assert torch.equal(got, want), (rep, name)
+        assert int(s.workspace[:2 * 4096 * 4].count_nonzero()) == 0
+        _ = (x[:4] * 2).sum().item()   # eager work between replays
 
 
 @pytest.mark.parametrize("g,V", [(200, 600), (257, 600), (700, 600), (1024, 600), (129, 33000), (300, 40000)])
