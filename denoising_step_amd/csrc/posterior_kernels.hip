@@ -198,9 +198,10 @@ __host__ __device__ inline void post_split(long live, int R, int V, int mode, in
 
 // Workgroups per CU of the stream kernel's grid with a live-row list.
 constexpr int kPostLiveGridPerCU = 16;
-// Resident workgroups per CU of the single-launch kernel (seven waves per
-// SIMD): its grid is one round when it has at most this many per CU.
-constexpr int kPostFusedWgsPerCU = 7;
+// Resident workgroups per CU of the single-launch kernel: seven for the
+// plain variant, five for the one that also tracks margin and entropy (its
+// register use); with at most five per CU the grid is one round for both.
+constexpr int kPostFusedWgsPerCU = 5;
 
 // With a live-row list, the split this call uses (from the device count).
 __device__ __forceinline__ void live_split(PostArgs &a)

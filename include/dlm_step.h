@@ -280,7 +280,7 @@ enum { DLM_ROW_SELECT = 1, DLM_ROW_LOCK = 2 };
  * E_p[x - y] - (logsumexp x - logsumexp y).
  * Without a live-row list or a score_ready event, with selection groups of
  * at most 256 rows, and when its (row, vocabulary chunk) workgroups fit one
- * round on the GPU (1792) or, with DLM_SEL_NONE, each row is one workgroup,
+ * round on the GPU (1280) or, with DLM_SEL_NONE, each row is one workgroup,
  * the call is one kernel launch: the workgroups
  * of a row's chunks count their arrivals in the workspace, the last one
  * merges the row, and the last row of a group runs its selection.
