@@ -107,7 +107,8 @@ class DeviceStep:
 
     def run(self, stream=None, locked=None, overlap=False):
         """One step.  With overlap, the posterior runs on a second stream and
-        only its selection waits for the column sums (select.score_ready);
+        only its selection waits for the column sums (select.score_ready,
+        for the modes that rank by them);
         the calling stream then waits for the posterior.  overlap=True
         starts its logit stream with the attention passes; overlap="pass1"
         starts it once pass 1 is done (mask_desc.pass1_done), beside the
@@ -138,7 +139,10 @@ class DeviceStep:
             self._side.wait_event(self._ev_start)  # prior work on the calling stream first
             self.run_attn(main)
         self._ev_cs.record(main)                   # column sums ready
-        self.select.score_ready = self._ev_cs
+        # only a selection that ranks by the column sums waits for them (the
+        # others also keep the one-launch posterior where it applies)
+        by_score = self.workload.post.mode in (3, 4)
+        self.select.score_ready = self._ev_cs if by_score else None
         try:
             self.run_posterior(self._side, locked)
         finally:

@@ -257,7 +257,7 @@ def test_mask_tile_classes(kgroups, case, monkeypatch):
 
 
 @pytest.mark.parametrize("mode", [True, "pass1"])
-@pytest.mark.parametrize("case", ["llada_dynamic", "long_topk_score"])
+@pytest.mark.parametrize("case", ["llada_dynamic", "long_topk_score", "mbd_topk_conf"])
 def test_overlapped_step_equals_serial(case, mode, monkeypatch):
     """The overlapped schedules (posterior on a second stream from the start
     of the step, or from mask_desc.pass1_done; its selection waiting for
@@ -266,8 +266,12 @@ def test_overlapped_step_equals_serial(case, mode, monkeypatch):
     selection modes that read the score.  Against the serial step's
     one-launch posterior, which merges the vocabulary chunks in another
     fp32 order, the attention outputs are the same bits and the posterior
-    differs by rounding only."""
-    w = small_llada(spread=True, seed=4) if case == "llada_dynamic" else small_long(seed=5)
+    differs by rounding only.  A selection that does not rank by the column
+    sums does not wait for them and keeps the serial step's posterior
+    kernels: every output is the same bits."""
+    w = (small_llada(spread=True, seed=4) if case == "llada_dynamic" else
+         small_long(seed=5) if case == "long_topk_score" else small_mbd(seed=6))
+    by_score = w.post.mode in (W.SEL_ATTN_DYNAMIC, W.SEL_TOPK_SCORE)
     _say(f"case: overlap {case} ({mode})")
     ds = _device_step(w)
     ds.run()
@@ -283,7 +287,7 @@ def test_overlapped_step_equals_serial(case, mode, monkeypatch):
         ds.run(overlap=mode)
         r2 = ds.results()
         for k in ("out", "lse", "colsum", "kl", "conf", "sel", "locked", "cache_k", "cache_v"):
-            assert np.array_equal(r0[k], r2[k], equal_nan=False), (rep, k)
+            assert np.array_equal((r0 if by_score else r1)[k], r2[k], equal_nan=False), (rep, k)
         for k in ("out", "lse", "colsum", "cache_k", "cache_v"):
             assert np.array_equal(r1[k], r2[k], equal_nan=False), (rep, k)
         assert np.abs(r1["kl"].astype(np.float64) - r2["kl"]).max() <= 2e-6
