@@ -110,8 +110,18 @@ __device__ __forceinline__ void rs_fold(RowState &s, const float (&x)[N], const 
             eh = fmaf(ex, x[i] - mx, eh);
             if (x[i] > s.av) { s.a2 = s.av; s.av = x[i]; s.ai = idx[i]; }
             else s.a2 = fmaxf(s.a2, x[i]);
-        } else {
-            if (x[i] > s.av) { s.av = x[i]; s.ai = idx[i]; }
+        }
+    }
+    if constexpr (!SC) {
+        // A new maximum can only come from a batch whose maximum beats the
+        // running one; its index is the batch's lowest at that value (the
+        // indices increase with i), as the element-by-element update gives.
+        if (bx > s.av) {
+            int ai = idx[N - 1];
+            for (int i = N - 1; i >= 0; --i)
+                if (x[i] == bx) ai = idx[i];
+            s.av = bx;
+            s.ai = ai;
         }
     }
     s.mx = mx; s.my = my; s.sx = sx; s.tx = tx; s.sy = sy;
@@ -143,8 +153,15 @@ __device__ __forceinline__ void rs_fold_masked(RowState &s, const float (&x)[N],
             eh = fmaf(ex, x[i] - mx, eh);
             if (x[i] > s.av) { s.a2 = s.av; s.av = x[i]; s.ai = idx[i]; }
             else s.a2 = fmaxf(s.a2, x[i]);
-        } else {
-            if (x[i] > s.av) { s.av = x[i]; s.ai = idx[i]; }
+        }
+    }
+    if constexpr (!SC) {
+        if (bx > s.av) {           // as in rs_fold, over the valid elements
+            int ai = INT_MAX;
+            for (int i = N - 1; i >= 0; --i)
+                if (ok[i] && x[i] == bx) ai = idx[i];
+            s.av = bx;
+            s.ai = ai;
         }
     }
     s.mx = mx; s.my = my; s.sx = sx; s.tx = tx; s.sy = sy;
