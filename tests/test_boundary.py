@@ -79,6 +79,29 @@ def test_workspace_queries():
     assert dlm.dlm_posterior_workspace_bytes(256, 151936, fz) == ctr + 256 * 16 + 256 * 4 * 48
 
 
+def test_posterior_path_per_workload_shape():
+    """Which posterior path the plan takes for the bench shapes, read from
+    the workspace size (only the one-launch layout holds the 16-byte per-row
+    results, in a 256-byte aligned block before the partials)."""
+    ctr = 2 * 4096 * 4
+    res = lambda R: (R * 16 + 255) // 256 * 256
+    # LLaDA-like layer: 32 rows x 31 chunks = 992 workgroups, one round: one launch
+    s = dlm.Select(mode=dlm.SEL_ATTN_DYNAMIC, tau=0.9, group_rows=32, score=FAKE)
+    assert dlm.dlm_posterior_workspace_bytes(32, 126464, s) == ctr + res(32) + 32 * 31 * 48
+    # long-prefix sampler: 256 rows x 4 chunks = 1024 workgroups: one launch
+    s = dlm.Select(mode=dlm.SEL_TOPK_SCORE, k=16, group_rows=256, score=FAKE)
+    assert dlm.dlm_posterior_workspace_bytes(256, 151936, s) == ctr + res(256) + 256 * 4 * 48
+    # SureLock: 8192 whole rows, no selection, no hand-over: one launch
+    s = dlm.Select(mode=dlm.SEL_NONE)
+    assert dlm.dlm_posterior_workspace_bytes(8192, 126464, s) == ctr + res(8192) + 8192 * 48
+    # multi-block: 1024 rows x 4 chunks = 4096 workgroups, several rounds: two launches
+    s = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=8, group_rows=32)
+    assert dlm.dlm_posterior_workspace_bytes(1024, 151936, s) == ctr + 1024 * 4 * 48
+    # a group of more than 256 rows: two launches
+    s = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=8, group_rows=512)
+    assert dlm.dlm_posterior_workspace_bytes(512, 8192, s) == ctr + 512 * 2 * 48   # 2 chunks: V spans two steps
+
+
 @pytest.mark.parametrize("case,code", [
     (dict(kv=_kv(D=48)), dlm.DLM_E_UNSUPPORTED),
     (dict(md=_md(Hq=3)), dlm.DLM_E_UNSUPPORTED),
