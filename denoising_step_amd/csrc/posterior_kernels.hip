@@ -215,6 +215,8 @@ __host__ __device__ inline void post_split(long live, int R, int V, int mode, in
 
 // Workgroups per CU of the stream kernel's grid with a live-row list.
 constexpr int kPostLiveGridPerCU = 16;
+// Workgroups the single launch aims its vocabulary split at: two per CU.
+constexpr long kPostFusedTarget = 2L * kNumCU;
 // Resident workgroups per CU of the single-launch kernel: seven for the
 // plain variant, five for the one that also tracks margin and entropy (its
 // register use); with at most five per CU the grid is one round for both.
@@ -1120,22 +1122,37 @@ PostPlan plan_post(int R, int V, int mode, int group_rows, bool live, bool fused
     // call can choose (one live row), and the kernels pick the split from
     // the device count.
     post_split(live ? 1 : R, R, V, mode, group_rows, 0, p.n_chunks, p.chunk);
-    // ... and only when its grid is one round of resident workgroups: each
-    // workgroup's hand-over (an acknowledged store and an atomic round trip,
-    // 2-3 us) then overlaps the other workgroups' streaming, where with
-    // more rounds it adds up (measured on MI355X: 32 x 126464 and 256 x
-    // 151936 rows gain 1-3 us over the two launches, 1024 x 151936 in
-    // 4096 workgroups loses 6 %).
     // Without a selection and with whole rows per workgroup there is no
     // hand-over at all (each workgroup finishes its own row), so any grid
     // size goes (the SureLock posterior, 8192 rows: equal or 5 us faster).
-    const long wgs = (long)R * p.n_chunks;
-    const bool no_handover = mode == 0 && p.n_chunks == 1;
-    bool fz = fused && !live && p.group_rows <= kPostThreads && R > 0 && groups <= kPostMaxCounters &&
-              (p.n_chunks == 1 || R <= kPostMaxCounters) &&
-              (no_handover || wgs <= (long)kPostFusedWgsPerCU * kNumCU);
+    // Otherwise the single launch splits the rows into its own, fewer
+    // chunks, about kPostFusedTarget workgroups in all (each hand-over, an
+    // acknowledged store and an atomic round trip, costs 2-3 us, and a
+    // workgroup streaming several steps keeps its loads going), and is
+    // taken only when that grid is one round of resident workgroups, where
+    // the hand-overs overlap other workgroups' streaming.  Measured on
+    // MI355X: 32 x 126464 rows 22.1 us with the two-launch split (992
+    // workgroups), 17.8-18.2 us with 8-16 chunks a row; 256 x 151936 rows
+    // 61.0 us with 4 chunks, 59.8 with 2, 66.6 with 1.
+    const bool base_ok = fused && !live && p.group_rows <= kPostThreads && R > 0 && groups <= kPostMaxCounters;
+    bool fz = false;
+    if (base_ok && mode == 0 && p.n_chunks == 1) {
+        fz = true;
+    } else if (base_ok) {
+        constexpr int kStep = kPostThreads * kPostVec;
+        const int steps = max(1, (V + kStep - 1) / kStep);
+        const int c = (int)min((long)steps, max(1L, (kPostFusedTarget + R - 1) / R));
+        const int ch = c > 1 ? ((V + c - 1) / c + kStep - 1) / kStep * kStep : (V + 3) / 4 * 4;
+        const int nc = max(1, (V + max(4, ch) - 1) / max(4, ch));
+        if ((long)R * nc <= (long)kPostFusedWgsPerCU * kNumCU && (nc == 1 || R <= kPostMaxCounters)) {
+            fz = true;
+            p.chunk = max(4, ch);
+            p.n_chunks = nc;
+        }
+    }
     if (const char *e = getenv("DLM_POST_FUSED"))
         if (e[0] == '0' && e[1] == 0) fz = false;
+    if (!fz) post_split(live ? 1 : R, R, V, mode, group_rows, 0, p.n_chunks, p.chunk);
     p.fused = fz ? 1 : 0;
     if (R == 0) return p;
     // Every layout starts with the counter block (row counters, then group

@@ -73,33 +73,37 @@ def test_workspace_queries():
     ctr = 2 * 4096 * 4
     assert dlm.dlm_posterior_workspace_bytes(1024, 126464, big) == ctr + 1024 * 4 * 48
     assert dlm.dlm_posterior_workspace_bytes(1024, 126464, live) == ctr + 1024 * 31 * 48
-    # groups of at most 256 rows in one round of workgroups: room for the
-    # single launch's per-row results before the partials (4 chunks a row)
+    # groups of at most 256 rows: room for either path, here the two-launch
+    # layout (4 chunks a row) is the larger (the one-launch one: per-row
+    # results and 2 chunks a row)
     fz = dlm.Select(mode=dlm.SEL_TOPK_SCORE, k=16, group_rows=256, score=FAKE)
-    assert dlm.dlm_posterior_workspace_bytes(256, 151936, fz) == ctr + 256 * 16 + 256 * 4 * 48
+    assert dlm.dlm_posterior_workspace_bytes(256, 151936, fz) == max(ctr + 256 * 4 * 48, ctr + 256 * 16 + 256 * 2 * 48)
 
 
 def test_posterior_path_per_workload_shape():
-    """Which posterior path the plan takes for the bench shapes, read from
-    the workspace size (only the one-launch layout holds the 16-byte per-row
-    results, in a 256-byte aligned block before the partials)."""
+    """The posterior workspace covers both paths' layouts for the bench
+    shapes: the two-launch split (about sixteen workgroups per CU, capped
+    for LDS staging) and the one-launch split (about two workgroups per
+    CU, whole streaming steps, 16-byte per-row results before the
+    partials), both after the 32 KiB counter block."""
     ctr = 2 * 4096 * 4
     res = lambda R: (R * 16 + 255) // 256 * 256
-    # LLaDA-like layer: 32 rows x 31 chunks = 992 workgroups, one round: one launch
+    both = lambda R, nc2, nc1: max(ctr + R * nc2 * 48, ctr + res(R) + R * nc1 * 48)
+    # LLaDA-like layer: 31 chunks a row for two launches, 16 for one
     s = dlm.Select(mode=dlm.SEL_ATTN_DYNAMIC, tau=0.9, group_rows=32, score=FAKE)
-    assert dlm.dlm_posterior_workspace_bytes(32, 126464, s) == ctr + res(32) + 32 * 31 * 48
-    # long-prefix sampler: 256 rows x 4 chunks = 1024 workgroups: one launch
+    assert dlm.dlm_posterior_workspace_bytes(32, 126464, s) == both(32, 31, 16)
+    # long-prefix sampler: 4 chunks / 2 chunks
     s = dlm.Select(mode=dlm.SEL_TOPK_SCORE, k=16, group_rows=256, score=FAKE)
-    assert dlm.dlm_posterior_workspace_bytes(256, 151936, s) == ctr + res(256) + 256 * 4 * 48
-    # SureLock: 8192 whole rows, no selection, no hand-over: one launch
-    s = dlm.Select(mode=dlm.SEL_NONE)
-    assert dlm.dlm_posterior_workspace_bytes(8192, 126464, s) == ctr + res(8192) + 8192 * 48
-    # multi-block: 1024 rows x 4 chunks = 4096 workgroups, several rounds: two launches
+    assert dlm.dlm_posterior_workspace_bytes(256, 151936, s) == both(256, 4, 2)
+    # multi-block: 4 chunks / whole rows
     s = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=8, group_rows=32)
-    assert dlm.dlm_posterior_workspace_bytes(1024, 151936, s) == ctr + 1024 * 4 * 48
-    # a group of more than 256 rows: two launches
+    assert dlm.dlm_posterior_workspace_bytes(1024, 151936, s) == both(1024, 4, 1)
+    # SureLock: whole rows on both paths
+    s = dlm.Select(mode=dlm.SEL_NONE)
+    assert dlm.dlm_posterior_workspace_bytes(8192, 126464, s) == both(8192, 1, 1)
+    # a group of more than 256 rows: two launches only (2 chunks: V spans two steps)
     s = dlm.Select(mode=dlm.SEL_TOPK_CONF, k=8, group_rows=512)
-    assert dlm.dlm_posterior_workspace_bytes(512, 8192, s) == ctr + 512 * 2 * 48   # 2 chunks: V spans two steps
+    assert dlm.dlm_posterior_workspace_bytes(512, 8192, s) == ctr + 512 * 2 * 48
 
 
 @pytest.mark.parametrize("case,code", [

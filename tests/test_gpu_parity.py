@@ -426,7 +426,7 @@ def test_single_launch_posterior_shares_one_workspace(monkeypatch):
         # R, V, mode, k, tau, group, margin/entropy, flags
         (1, 151936, W.SEL_TOPK_CONF, 1, 0.0, 1, False, False),       # 38 chunks in one row
         (120, 40000, W.SEL_TOPK_MARGIN, 3, 0.0, 7, True, True),      # ragged groups, margin path
-        (1024, 8192, W.SEL_TOPK_CONF, 4, 0.0, 32, False, False),     # 2048 workgroups: two launches
+        (1600, 8192, W.SEL_TOPK_CONF, 4, 0.0, 32, False, False),     # 1600 whole rows, past one round: two launches
         (64, 1003, W.SEL_THRESH_CONF, 0, 0.05, 64, False, False),    # V not a multiple of 4
         (300, 9000, W.SEL_NONE, 0, 0.0, 1, False, True),             # no selection, 3 chunks
         (256, 70000, W.SEL_TOPK_SCORE, 16, 0.0, 256, False, False),  # one 256-row group
