@@ -278,12 +278,13 @@ enum { DLM_ROW_SELECT = 1, DLM_ROW_LOCK = 2 };
  * A row that arrives locked is not read: kl = conf = 0, sel = -1, stays locked.
  * kl and conf are fp32; KL is computed in one pass as
  * E_p[x - y] - (logsumexp x - logsumexp y).
- * Without a live-row list or a score_ready event, with selection groups of
- * at most 256 rows, and when its (row, vocabulary chunk) workgroups fit one
- * round on the GPU (1280) or, with DLM_SEL_NONE, each row is one workgroup,
- * the call is one kernel launch: the workgroups
- * of a row's chunks count their arrivals in the workspace, the last one
- * merges the row, and the last row of a group runs its selection.
+ * Without a live-row list or a score_ready event, and with selection groups
+ * of at most 256 rows, the call is one kernel launch when its own split of
+ * the rows into vocabulary chunks (about 512 workgroups in all) fits one
+ * round on the GPU (1280 workgroups), or with DLM_SEL_NONE when each row
+ * is one workgroup: the workgroups of a row's chunks count their arrivals
+ * in the workspace, the last one merges the row, and the last row of a
+ * group runs its selection.
  * Otherwise a second launch merges and selects.  Results are deterministic
  * for given shapes on either path; the two paths merge a row's chunks in
  * different fp32 orders.
